@@ -1,0 +1,197 @@
+"""CPU oracle for the Q4_G64_FP16 pure Linear op -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The library under
+``weight_only_bit_q4_amd`` never imports it and shares no code with it.
+
+The arithmetic lives in ``q4lin_oracle.c`` (plain C, binary64, one rounding to
+bfloat16 at the end); this module only builds that file with gcc and marshals
+numpy arrays to it.  What it computes, and where the pages define it, is stated
+in the C file's header:
+
+* "q4-linear.md", setup table: Q4_G64_FP16 weights (64 weights per FP16
+  scale, row-split), ``W[N,K] x X[K,T] -> Y[N,T]``, BF16 in and out;
+* "q4-linear.md", test paragraph: independent decode of codes and scales, an
+  FP64 matrix product as the oracle;
+* "linear-benchmark.md", section 4 table: 34 bytes per 64-weight group.
+
+Parity status: ``fp16_to_double``, ``bf16_to_double``, ``double_to_bf16``,
+``weight_bytes``, ``linear`` and ``linear_at`` are each pinned by the CPU
+test-suite (hand-worked examples, library special cases, invariants, exact
+rational brute force); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "q4lin_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libq4lin_oracle.so")
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc -O2 with OpenMP and without fast-math; atomic replace of ``out``."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=gnu11",
+           "-fno-fast-math", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle next to its source."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    return compile_source(SOURCE, LIB_PATH)
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, lib_path: str):
+        lib = ctypes.CDLL(lib_path)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        i64 = ctypes.c_int64
+        lib.q4o_fp16_to_double.argtypes = [ctypes.c_uint16]
+        lib.q4o_fp16_to_double.restype = ctypes.c_double
+        lib.q4o_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.q4o_bf16_to_double.restype = ctypes.c_double
+        lib.q4o_double_to_bf16.argtypes = [ctypes.c_double]
+        lib.q4o_double_to_bf16.restype = ctypes.c_uint16
+        lib.q4o_weight_bytes.argtypes = [i64, i64]
+        lib.q4o_weight_bytes.restype = i64
+        lib.q4o_linear.argtypes = [u16p, u8p, u16p, u16p, f64p, i64, i64, i64, ctypes.c_int]
+        lib.q4o_linear.restype = None
+        lib.q4o_linear_at.argtypes = [u16p, u8p, u16p, i64, i64, i64, i64p, i64p, i64,
+                                      u16p, f64p, ctypes.c_int]
+        lib.q4o_linear_at.restype = None
+        lib.q4o_max_threads.argtypes = []
+        lib.q4o_max_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = lib_path
+
+    # scalar helpers -------------------------------------------------------
+    def fp16_to_double(self, bits: int) -> float:
+        return self.lib.q4o_fp16_to_double(int(bits) & 0xFFFF)
+
+    def bf16_to_double(self, bits: int) -> float:
+        return self.lib.q4o_bf16_to_double(int(bits) & 0xFFFF)
+
+    def double_to_bf16(self, v: float) -> int:
+        return int(self.lib.q4o_double_to_bf16(float(v)))
+
+    def weight_bytes(self, n: int, k: int) -> int:
+        return int(self.lib.q4o_weight_bytes(int(n), int(k)))
+
+    def max_threads(self) -> int:
+        return int(self.lib.q4o_max_threads())
+
+    # the product ------------------------------------------------------------
+    @staticmethod
+    def _prep(x, codes, scales, n, k, t):
+        if k % 64 != 0 or k < 64:
+            raise ValueError("K must be a positive multiple of 64")
+        x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1)
+        codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
+        scales = np.ascontiguousarray(scales, dtype=np.uint16).reshape(-1)
+        if codes.size != n * k // 2 or scales.size != n * (k // 64) or x.size != k * t:
+            raise ValueError("array sizes do not match N, K, T")
+        return x, codes, scales
+
+    def linear(self, x, codes, scales, n: int, k: int, t: int,
+               threads: int = 0, with_acc: bool = False):
+        """Y = bf16(W . X).  ``x``: bf16 bits, token-major ``[T, K]``;
+        ``codes``: uint8 ``[N, K/2]``; ``scales``: fp16 bits ``[N, K/64]``.
+        Returns bf16 bits ``[T, N]`` (token-major) and, with ``with_acc``, the
+        unrounded binary64 sums in the same shape."""
+        x, codes, scales = self._prep(x, codes, scales, n, k, t)
+        y = np.zeros(t * n, dtype=np.uint16)
+        acc = np.zeros(t * n, dtype=np.float64) if with_acc else None
+        self.lib.q4o_linear(_ptr(x, ctypes.c_uint16), _ptr(codes, ctypes.c_uint8),
+                            _ptr(scales, ctypes.c_uint16), _ptr(y, ctypes.c_uint16),
+                            _ptr(acc, ctypes.c_double), n, k, t, int(threads))
+        y = y.reshape(t, n)
+        if with_acc:
+            return y, acc.reshape(t, n)
+        return y
+
+    def linear_at(self, x, codes, scales, n: int, k: int, t: int, ns, ts,
+                  threads: int = 0, with_acc: bool = False):
+        """Selected elements ``Y[ns[i], ts[i]]`` (bf16 bits), each summed alone."""
+        x, codes, scales = self._prep(x, codes, scales, n, k, t)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        ts = np.ascontiguousarray(ts, dtype=np.int64)
+        if ns.shape != ts.shape:
+            raise ValueError("ns and ts differ in shape")
+        if ns.size and (ns.min() < 0 or ns.max() >= n or ts.min() < 0 or ts.max() >= t):
+            raise ValueError("sample index out of range")
+        out = np.zeros(ns.size, dtype=np.uint16)
+        acc = np.zeros(ns.size, dtype=np.float64) if with_acc else None
+        self.lib.q4o_linear_at(_ptr(x, ctypes.c_uint16), _ptr(codes, ctypes.c_uint8),
+                               _ptr(scales, ctypes.c_uint16), n, k, t,
+                               _ptr(ns, ctypes.c_int64), _ptr(ts, ctypes.c_int64), ns.size,
+                               _ptr(out, ctypes.c_uint16), _ptr(acc, ctypes.c_double),
+                               int(threads))
+        if with_acc:
+            return out, acc
+        return out
+
+
+_lock = threading.Lock()
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``q4lin_oracle.c`` (compiled on first use if absent)."""
+    global _default
+    with _lock:
+        if _default is None:
+            if not os.path.exists(LIB_PATH):
+                build(force=True)
+            _default = Oracle(LIB_PATH)
+        return _default
+
+
+def fp16_to_double(bits):
+    return default().fp16_to_double(bits)
+
+
+def bf16_to_double(bits):
+    return default().bf16_to_double(bits)
+
+
+def double_to_bf16(v):
+    return default().double_to_bf16(v)
+
+
+def weight_bytes(n, k):
+    return default().weight_bytes(n, k)
+
+
+def linear(*args, **kw):
+    return default().linear(*args, **kw)
+
+
+def linear_at(*args, **kw):
+    return default().linear_at(*args, **kw)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> binary64 values (exact), for tolerance checks."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

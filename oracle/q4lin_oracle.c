@@ -1,0 +1,225 @@
+/*
+ * q4lin_oracle.c -- plain CPU reference for the Q4_G64_FP16 pure Linear op.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file: only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark do.  It shares no code, header or constant table with the HIP
+ * library.
+ *
+ * What it computes (the plain definition, written out):
+ *   Y[n,t] = bf16_rne( sum_k  W[n,k] * X[k,t] )
+ * where W[n,k] = (q[n,k] - 8) * scale[n, k/64]  (q a 4-bit code in 0..15),
+ * the sum is taken in IEEE binary64 in increasing k, and the result is rounded
+ * once, directly from binary64 to bfloat16 with round-to-nearest-even.
+ *
+ * Sources (the pages' text):
+ *  - "q4-linear.md" (NInferEZ-Engine maintainer example), setup table: W is
+ *    Q4_G64_FP16 with a row-split layout, 64 weights share one FP16 scale;
+ *    the math shape is W[N,K] x X[K,T] -> Y[N,T]; BF16 input and output.
+ *  - same page, test paragraph: the check decodes the packed codes and FP16
+ *    scales independently and uses an FP64 matrix product as the oracle.
+ *  - "linear-benchmark.md", section 4 (theoretical traffic), weight-format
+ *    table: a Q4G64_F16S group is 64 weights = 32 code bytes + 2 scale bytes,
+ *    34 bytes per group, weight bytes = groups * 34.
+ * Readings where the pages are silent (each listed in the design notes):
+ *  - code -> value is (q - 8) * scale;
+ *  - nibble order: byte j of a row holds k = 2j in its low nibble and
+ *    k = 2j+1 in its high nibble;
+ *  - planes: codes[N][K/2] row-major, scales[N][K/64] row-major (fp16 bits);
+ *  - X and Y are token-major: X(k,t) at x[t*K + k], Y(n,t) at y[t*N + n].
+ *
+ * Exactness: every weight (q-8)*s has at most 15 significant bits and every
+ * activation at most 8, so each product is exact in binary64; the binary64
+ * running sum has relative error at most about K * 2^-53, far below one bf16
+ * ulp, and the single final rounding is correctly rounded.
+ *
+ * Parity pins live in the CPU test-suite (hand-worked examples, library
+ * special cases, invariants, exact rational brute force).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* IEEE binary16 bits -> binary64, decoded by hand (sign, 5-bit exponent with
+ * bias 15, 10-bit fraction, subnormals, Inf/NaN). */
+double q4o_fp16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);            /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 bits -> binary64, decoded by hand (sign, 8-bit exponent with bias
+ * 127, 7-bit fraction, subnormals, Inf/NaN). */
+double q4o_bf16_to_double(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xFF;
+    int m = b & 0x7F;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -133);           /* subnormal: m * 2^-133 */
+    else if (e == 255)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 128), e - 134); /* (1 + m/128) * 2^(e-127) */
+    return sign ? -v : v;
+}
+
+/* binary64 -> bfloat16 bits, round to nearest, ties to even, done once from
+ * the binary64 value (no pass through binary32, which could round twice).
+ * bfloat16 keeps 8 significant bits; its quantum in the binade
+ * [2^e, 2^(e+1)) is 2^(e-7) for e >= -126 and 2^-133 below (subnormals).
+ * Magnitudes that round to 2^128 or more become Inf; NaN stays NaN. */
+uint16_t q4o_double_to_bf16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (isnan(v))
+        return 0x7FC0;
+    double a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7F80;
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);                 /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;                /* a in [2^e, 2^(e+1)) */
+    int qexp = (e < -126) ? -133 : e - 7;
+    double r = ldexp(a, -qexp);    /* a / quantum: exact power-of-two scaling */
+    double whole = floor(r);
+    double frac = r - whole;       /* exact: r has at most 53 significant bits */
+    if (frac > 0.5 || (frac == 0.5 && fmod(whole, 2.0) != 0.0))
+        whole += 1.0;
+    /* whole is an integer in [0, 256]; the value is whole * 2^qexp */
+    if (whole == 0.0)
+        return sign;
+    int exp_field;
+    int frac_field;
+    if (qexp == -133 && whole < 128.0) {      /* stays subnormal */
+        exp_field = 0;
+        frac_field = (int)whole;
+    } else {
+        int w = (int)whole;
+        int ee = qexp + 7;                    /* binade of the rounded value */
+        if (w == 256) {                       /* rounding carried into the next binade */
+            w = 128;
+            ee += 1;
+        }
+        if (ee > 127)
+            return sign | 0x7F80;             /* overflow -> Inf */
+        exp_field = ee + 127;
+        frac_field = w - 128;
+    }
+    return (uint16_t)(sign | (exp_field << 7) | frac_field);
+}
+
+/* Weight bytes of a Q4_G64_FP16 matrix, the pages' closed form
+ * ("linear-benchmark.md", section 4): groups * 34 with groups = N * K / 64
+ * (K a multiple of 64; every K used here is also a multiple of 128, so the
+ * pages' K_pad equals K). */
+int64_t q4o_weight_bytes(int64_t n, int64_t k)
+{
+    return n * (k / 64) * 34;
+}
+
+/* One weight value (q - 8) * scale, exact in binary64. */
+static double weight_value(const uint8_t *codes, const uint16_t *scales,
+                           int64_t K, int64_t n, int64_t k)
+{
+    uint8_t byte = codes[n * (K / 2) + k / 2];
+    int q = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    double s = q4o_fp16_to_double(scales[n * (K / 64) + k / 64]);
+    return (double)(q - 8) * s;
+}
+
+/* The binary64 sum for one output element, increasing k. */
+static double dot_one(const uint8_t *codes, const uint16_t *scales,
+                      const uint16_t *x, int64_t K, int64_t n, int64_t t)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += weight_value(codes, scales, K, n, k) * q4o_bf16_to_double(x[t * K + k]);
+    return acc;
+}
+
+/* Full product.  y[t*N + n] receives bf16 bits; acc (optional, may be NULL)
+ * receives the unrounded binary64 sums in the same order.  threads <= 0 uses
+ * the OpenMP default.  Rows are independent, so the row loop is split across
+ * threads; each sum is still taken sequentially in k. */
+void q4o_linear(const uint16_t *x, const uint8_t *codes, const uint16_t *scales,
+                uint16_t *y, double *acc, int64_t N, int64_t K, int64_t T,
+                int threads)
+{
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k)
+                w[k] = weight_value(codes, scales, K, n, k);
+            for (int64_t t = 0; t < T; ++t) {
+                double s = 0.0;
+                const uint16_t *xt = x + t * K;
+                for (int64_t k = 0; k < K; ++k)
+                    s += w[k] * q4o_bf16_to_double(xt[k]);
+                y[t * N + n] = q4o_double_to_bf16(s);
+                if (acc)
+                    acc[t * N + n] = s;
+            }
+        }
+        free(w);
+    }
+}
+
+/* Selected output elements only: out[i] = Y[ns[i], ts[i]] (bf16 bits), and
+ * acc[i] the binary64 sum (acc may be NULL).  Used where the full product
+ * would take too long on the CPU. */
+void q4o_linear_at(const uint16_t *x, const uint8_t *codes, const uint16_t *scales,
+                   int64_t N, int64_t K, int64_t T,
+                   const int64_t *ns, const int64_t *ts, int64_t count,
+                   uint16_t *out, double *acc, int threads)
+{
+    (void)N;
+    (void)T;
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < count; ++i) {
+        double s = dot_one(codes, scales, x, K, ns[i], ts[i]);
+        out[i] = q4o_double_to_bf16(s);
+        if (acc)
+            acc[i] = s;
+    }
+}
+
+/* Number of OpenMP threads a parallel region would use (for reporting). */
+int q4o_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
