@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q4_G64_FP16 Linear on one MI355X.
+
+Default run: the decode workload W[6144,5120] x X[5120,1] (T = 1), plus the
+prefill point T = 1024 on the same weight shape as a second object, printed as
+one JSON line.  Metrics follow the pages' definitions ("linear-benchmark.md"
+sections 4-5, "q4-linear.md" metric block):
+
+    model_bytes = N*K/64*34 + 2*K*T + 2*N*T     logical GB/s = model_bytes / s / 1e9
+    useful_flops = 2*N*K*T                      effective TFLOP/s = useful_flops / s / 1e12
+
+Timing.  Inputs are seeded synthetic data resident in HBM.  The weight (and
+activation/output) buffers rotate over enough copies that every call reads a
+weight nobody has touched for >= 1 GiB of traffic, so nothing is served from
+the 4 MB per-XCD L2s or the 256 MB Infinity Cache.  The K timed calls are
+captured in one HIP graph (host launch cost would otherwise exceed a ~3 us
+kernel) and bracketed by HIP events on the graph's stream, with a device
+synchronize on both sides; ms_per_step = elapsed / K.  Each step is one
+complete public call (for T = 1024 that is the activation-preparation kernel
+plus the tiled kernel).
+
+Other modes: ``--sweep 1:128`` (per-T table with step change between
+adjacent T), ``--n/--k/--t`` single points, ``--profile`` (one call after
+set-up, for profiler counter passes).  ``--gpus`` above 1 exits: this build
+measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix, published
+ROTATE_BYTES = 1 << 30         # traffic between two uses of one buffer set
+
+METRIC = "Q4 6144x5120: logical GB/s @T=1, eff. TFLOP/s @T=1024 (% of roofline)"
+
+
+# ---------------------------------------------------------------------------
+# the pages' metric definitions
+# ---------------------------------------------------------------------------
+def weight_bytes(n: int, k: int) -> int:
+    return n * k // 64 * 34
+
+
+def model_bytes(n: int, k: int, t: int) -> int:
+    return weight_bytes(n, k) + 2 * k * t + 2 * n * t
+
+
+def useful_flops(n: int, k: int, t: int) -> int:
+    return 2 * n * k * t
+
+
+def gbs(n, k, t, seconds):
+    return model_bytes(n, k, t) / seconds / 1e9
+
+
+def tflops(n, k, t, seconds):
+    return useful_flops(n, k, t) / seconds / 1e12
+
+
+def roof_fraction(n, k, t, seconds, hbm_gbs=HBM_PEAK_GBS, mfma_tflops=MFMA_PEAK_TFLOPS):
+    """Fraction of the roofline floor: max(memory floor, matrix floor) / time."""
+    floor = max(model_bytes(n, k, t) / (hbm_gbs * 1e9), useful_flops(n, k, t) / (mfma_tflops * 1e12))
+    return floor / seconds
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+class Point:
+    """Rotating buffer sets for one (N, K, T) and a graph of `steps` calls."""
+
+    def __init__(self, n, k, t, seed):
+        import torch
+        import weight_only_bit_q4_amd as q4
+        from weight_only_bit_q4_amd import inputs
+        self.n, self.k, self.t = n, k, t
+        self.q4 = q4
+        self.torch = torch
+        x, codes, scales = inputs.gen_problem(n, k, t, seed)
+        per_set = model_bytes(n, k, t) + max(q4.q4lin_workspace_bytes(n, k, t), 0)
+        self.nsets = max(2, int(math.ceil(ROTATE_BYTES / per_set)) + 1)
+        dev = torch.device("cuda")
+        xd = torch.from_numpy(x.view(np.int16).copy()).to(dev)
+        cd = torch.from_numpy(codes).to(dev)
+        sd = torch.from_numpy(scales.view(np.int16).copy()).to(dev)
+        self.ws_bytes = q4.q4lin_workspace_bytes(n, k, t)
+        self.sets = []
+        for _ in range(self.nsets):
+            ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+            y = torch.empty((t, n), dtype=torch.int16, device=dev)
+            self.sets.append((xd.clone(), cd.clone(), sd.clone(), y, ws))
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.Stream()
+
+    def call(self, i, stream_handle):
+        x, c, s, y, ws = self.sets[i % self.nsets]
+        st = self.q4.q4lin_linear(x.data_ptr(), c.data_ptr(), s.data_ptr(), y.data_ptr(),
+                                  self.n, self.k, self.t, ws.data_ptr() if self.ws_bytes else 0,
+                                  self.ws_bytes, stream_handle)
+        if st != 0:
+            raise RuntimeError("q4lin_linear: " + self.q4.q4lin_status_string(st))
+
+    def graph(self, steps, offset=0):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(g, stream=self.stream):
+                h = self.stream.cuda_stream
+                for i in range(steps):
+                    self.call(offset + i, h)
+        return g
+
+    def time(self, steps, warmup, repeats=1):
+        """Returns (list of seconds per call over `repeats` timed replays,
+        each replay = exactly `steps` calls)."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for i in range(min(warmup, 4 * self.nsets)):
+                self.call(i, self.stream.cuda_stream)
+        torch.cuda.synchronize()
+        g = self.graph(steps)
+        gw = self.graph(max(warmup, 1), offset=steps) if warmup > 0 else None
+        out = []
+        for _ in range(repeats):
+            if gw is not None:
+                gw.replay()
+            torch.cuda.synchronize()
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            start.record(self.stream)
+            g.replay()
+            end.record(self.stream)
+            torch.cuda.synchronize()
+            out.append(start.elapsed_time(end) / 1e3 / steps)
+        return out
+
+    def free(self):
+        self.sets = []
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def cpu_baseline_t1(n, k, seed, budget_s=10.0):
+    """The oracle, untuned, on the host cores: whole T=1 problems repeated
+    for about `budget_s` seconds; returns GB/s in the pages' metric."""
+    import oracle
+    from weight_only_bit_q4_amd import inputs
+    x, c, s = inputs.gen_problem(n, k, 1, seed)
+    o = oracle.default()
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or not times:
+        t0 = time.perf_counter()
+        o.linear(x, c, s, n, k, 1)
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
+    return {"value": round(gbs(n, k, 1, med), 4), "unit": "GB/s", "cores": o.max_threads(),
+            "kind": "oracle",
+            "sample": "%d full %dx%d T=1 problems, median %.1f ms each" % (len(times), n, k, med * 1e3)}
+
+
+def cpu_baseline_rows(n, k, t, seed, rows=48):
+    """The oracle on `rows` output rows of an N x K x T problem, scaled to the
+    whole problem; returns effective TFLOP/s."""
+    import oracle
+    from weight_only_bit_q4_amd import inputs
+    x, c, s = inputs.gen_problem(n, k, t, seed)
+    o = oracle.default()
+    ns = np.repeat(np.arange(rows), t)
+    ts = np.tile(np.arange(t), rows)
+    t0 = time.perf_counter()
+    o.linear_at(x, c, s, n, k, t, ns, ts)
+    el = time.perf_counter() - t0
+    full = el * n / rows
+    return {"value": round(tflops(n, k, t, full), 6), "unit": "TFLOP/s", "cores": o.max_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d output rows of %dx%d T=%d (%.1f s), scaled to all rows" % (rows, n, n, k, t, el)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000, help="timed calls at T=1 (T=1024 uses steps/20, >= 20)")
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--n", type=int, default=6144)
+    ap.add_argument("--k", type=int, default=5120)
+    ap.add_argument("--t", type=int, default=None, help="single point instead of the default pair")
+    ap.add_argument("--sweep", type=str, default=None, help="T range lo:hi[:step]")
+    ap.add_argument("--repeats", type=int, default=5, help="timed replays per sweep point (median)")
+    ap.add_argument("--profile", action="store_true", help="one call after set-up, then exit")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--csv", type=str, default=None)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only; --gpus %d is not supported (see the design notes "
+              "for how the op would shard over GPUs)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    from weight_only_bit_q4_amd import inputs
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 2
+    n, k = args.n, args.k
+    seed = inputs.workload_seed("decode_6144x5120_t1")
+
+    if args.profile:
+        t = args.t or 1
+        p = Point(n, k, t, seed)
+        with torch.cuda.stream(p.stream):
+            p.call(0, p.stream.cuda_stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": True, "n": n, "k": k, "t": t}))
+        return 0
+
+    if args.sweep:
+        parts = [int(v) for v in args.sweep.split(":")]
+        lo, hi = parts[0], parts[1]
+        step = parts[2] if len(parts) > 2 else 1
+        rows = []
+        prev = None
+        wl_seed = inputs.workload_seed("sweep_6144x5120_t1_128")
+        for t in range(lo, hi + 1, step):
+            p = Point(n, k, t, wl_seed)
+            steps = max(20, min(400, int(4e-3 / max(1e-6, 3e-6 * t))))
+            secs = p.time(steps, args.warmup, repeats=args.repeats)
+            p.free()
+            med = float(np.median(secs))
+            row = {"t": t, "us": med * 1e6, "min_us": min(secs) * 1e6, "gbs": gbs(n, k, t, med),
+                   "tflops": tflops(n, k, t, med), "hbm_frac": gbs(n, k, t, med) / HBM_PEAK_GBS,
+                   "mfma_frac": tflops(n, k, t, med) / MFMA_PEAK_TFLOPS,
+                   "roof_frac": roof_fraction(n, k, t, med),
+                   "delta_pct": None if prev is None else (med / prev - 1) * 100}
+            prev = med
+            rows.append(row)
+            print("T=%4d  %9.3f us  %8.1f GB/s (%5.1f%% HBM)  %8.2f TFLOP/s (%5.1f%% MFMA)  roof %5.1f%%  %s"
+                  % (t, row["us"], row["gbs"], 100 * row["hbm_frac"], row["tflops"], 100 * row["mfma_frac"],
+                     100 * row["roof_frac"], "" if row["delta_pct"] is None else "%+.1f%%" % row["delta_pct"]),
+                  flush=True)
+        if args.csv:
+            import csv
+            with open(args.csv, "w", newline="") as f:
+                w = csv.DictWriter(f, fieldnames=list(rows[0]))
+                w.writeheader()
+                w.writerows(rows)
+        return 0
+
+    if args.t is not None:
+        t = args.t
+        p = Point(n, k, t, seed)
+        secs = p.time(args.steps, args.warmup, repeats=1)[0]
+        print(json.dumps({"n": n, "k": k, "t": t, "us": secs * 1e6, "gbs": gbs(n, k, t, secs),
+                          "tflops": tflops(n, k, t, secs), "roof_frac": roof_fraction(n, k, t, secs)}))
+        return 0
+
+    # ---- default: the decode point (headline) + the prefill point ----------
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    p1 = Point(n, k, 1, seed)
+    s1 = p1.time(args.steps, args.warmup, repeats=1)[0]
+    p1.free()
+    steps2 = max(20, args.steps // 20)
+    p2 = Point(n, k, 1024, inputs.workload_seed("prefill_6144x5120_t1024"))
+    s2 = p2.time(steps2, max(5, args.warmup // 10), repeats=1)[0]
+    p2.free()
+
+    v1 = gbs(n, k, 1, s1)
+    v2 = tflops(n, k, 1024, s2)
+    line = {
+        "metric": METRIC,
+        "value": round(v1, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(s1 * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-products/f32-accumulate (bf16 in/out)",
+        "data": "synthetic",
+        "config": {"workload": "decode_6144x5120_t1", "n": n, "k": k, "t": 1,
+                   "weight_format": "Q4_G64_FP16", "cache": "cold (rotating %d buffer sets)" % 0},
+        "roofline": {"bound": "hbm", "achieved": round(v1, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(v1 / HBM_PEAK_GBS, 4), "traffic": None},
+        "prefill_t1024": {
+            "metric": "eff. TFLOP/s @T=1024", "value": round(v2, 2), "unit": "TFLOP/s",
+            "steps": steps2, "ms_per_step": round(s2 * 1e3, 6),
+            "roofline": {"bound": "mfma", "achieved": round(v2, 2), "peak": MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(v2 / MFMA_PEAK_TFLOPS, 4), "traffic": None},
+        },
+    }
+    line["config"]["cache"] = "cold (rotating buffer sets, >= 1 GiB between reuses)"
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_t1(n, k, seed)
+        line["prefill_t1024"]["cpu_baseline"] = cpu_baseline_rows(n, k, 1024,
+                                                                  inputs.workload_seed("prefill_6144x5120_t1024"))
+    line["wall_s"] = round(time.perf_counter() - t_wall0, 2)
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

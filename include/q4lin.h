@@ -1,0 +1,100 @@
+/*
+ * q4lin.h -- C ABI of the Q4_G64_FP16 weight-only Linear for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation ("q4-linear.md", setup table; "linear-benchmark.md", section 0,
+ * the public call linear(x, w, out, policy, workspace, stream)):
+ *
+ *     Y[N,T] = W[N,K] x X[K,T]
+ *
+ *   W   Q4_G64_FP16: every 64 consecutive weights of a row share one FP16
+ *       scale; a weight is (q - 8) * scale with q a 4-bit code in 0..15
+ *       ("linear-benchmark.md", section 4 table: 32 code bytes + 2 scale
+ *       bytes = 34 bytes per group).
+ *   X   bfloat16 activations, Y bfloat16 outputs; products are summed in
+ *       binary32 and Y is rounded to nearest even ("q4-linear.md", setup
+ *       table: BF16 input and output; the note under the metric definitions:
+ *       BF16 inputs with FP32 accumulation).  Only the A16 policy exists, so
+ *       the call carries no policy argument.
+ *
+ * Memory layout (all buffers are device memory owned by the caller):
+ *   codes   uint8  [N][K/2], row-major.  Byte j of a row holds the code of
+ *           k = 2j in its low nibble and of k = 2j+1 in its high nibble.
+ *           16-byte aligned.
+ *   scales  fp16   [N][K/64], row-major (IEEE binary16 bit patterns); scale g
+ *           of a row covers k in [64g, 64g+64).  2-byte aligned.
+ *   x       bf16   token-major [T][K]: element (k, t) at x[t*K + k].
+ *           16-byte aligned.
+ *   y       bf16   token-major [T][N]: element (n, t) at y[t*N + n].
+ *           2-byte aligned.  Fully overwritten; nothing outside it is written.
+ *   workspace  device scratch of at least q4lin_workspace_bytes(N, K, T)
+ *           bytes, 256-byte aligned; contents on entry are ignored and are not
+ *           preserved.  May be NULL when that size is 0.
+ *
+ * Shapes: N >= 0, T >= 0, K a positive multiple of 64.  N == 0 or T == 0 is an
+ * empty product: the call returns Q4LIN_OK and touches no memory (pointers may
+ * then be NULL).  The largest accepted values are N <= 2^24, T <= 2^21 and
+ * K <= 2^20, with every buffer under 2^40 bytes.
+ *
+ * Behaviour: the call only validates its arguments on the host and enqueues
+ * one or more kernels on `stream` (a hipStream_t; NULL is the null stream).  It
+ * never allocates, frees or synchronizes, keeps no pointer after it returns,
+ * and has no global mutable state, so it is thread-safe and may be captured in
+ * a HIP graph.  x, codes and scales are only read.  Every argument error is
+ * reported before anything is enqueued, leaving y untouched.  Calls that share
+ * a workspace must not overlap in time.
+ */
+#ifndef Q4LIN_H
+#define Q4LIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef Q4LIN_API
+#define Q4LIN_API __attribute__((visibility("default")))
+#endif
+
+/* Status codes. */
+#define Q4LIN_OK 0
+#define Q4LIN_E_NULL 1      /* a required pointer is NULL                         */
+#define Q4LIN_E_SHAPE 2     /* N, K or T out of contract (K % 64 != 0, sizes...)  */
+#define Q4LIN_E_ALIGN 3     /* a pointer is not aligned as stated above           */
+#define Q4LIN_E_WORKSPACE 4 /* workspace smaller than q4lin_workspace_bytes()     */
+#define Q4LIN_E_LAUNCH 5    /* the HIP runtime refused a kernel launch (e.g. the
+                               current device is not a gfx950 GPU)               */
+
+/* Bytes of workspace q4lin_linear needs for this shape (0 when none), or a
+ * negative status (-Q4LIN_E_SHAPE) for a shape outside the contract.  Pure
+ * host function; the pages ask for a public capacity query answered before
+ * any timed call ("linear-benchmark.md", section 1.1). */
+Q4LIN_API int64_t q4lin_workspace_bytes(int64_t n, int64_t k, int64_t t);
+
+/* Y = W x X as described above.  Returns Q4LIN_OK or a status code. */
+Q4LIN_API int q4lin_linear(const void *x, const void *codes, const void *scales, void *y,
+                 int64_t n, int64_t k, int64_t t,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+Q4LIN_API const char *q4lin_status_string(int status);
+
+/* Introspection for tests and reports: the kernel route the host dispatch
+ * picks for this shape (one of the Q4LIN_ROUTE_* values), or a negative status
+ * for a shape outside the contract.  The product call never needs it. */
+#define Q4LIN_ROUTE_NONE 0   /* empty product, nothing launched */
+#define Q4LIN_ROUTE_GEMV 1   /* few tokens: vector-ALU dot products            */
+#define Q4LIN_ROUTE_SKINNY 2 /* small T: W streamed once, matrix cores, K split */
+#define Q4LIN_ROUTE_TILED 3  /* large T: LDS-tiled matrix-core GEMM            */
+Q4LIN_API int q4lin_route(int64_t n, int64_t k, int64_t t);
+
+/* Library version as major*10000 + minor*100 + patch. */
+Q4LIN_API int q4lin_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4LIN_H */

@@ -1,0 +1,90 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, and rejects bad arguments before any HIP call (no GPU needed: every
+call here returns from host-side validation)."""
+import os
+import re
+
+import pytest
+
+import weight_only_bit_q4_amd as q
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "q4lin.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"Q4LIN_API\s+[\w\s\*]+?\b(q4lin_\w+)\s*\(", src)
+
+
+def test_header_declares_the_binding_names():
+    assert sorted(declared_functions()) == sorted(q.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = q.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for st in range(0, 6):
+        assert q.q4lin_status_string(st)
+    assert q.q4lin_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("n,k,t", [(8, 0, 1), (8, 32, 1), (8, 96, 1), (8, 100, 1), (-1, 64, 1),
+                                   (8, 64, -1), (1 << 25, 64, 1), (8, 64, (1 << 21) + 1),
+                                   (8, (1 << 20) + 64, 1)])
+def test_shape_rejected(n, k, t):
+    assert q.q4lin_workspace_bytes(n, k, t) == -q.Q4LIN_E_SHAPE
+    assert q.q4lin_route(n, k, t) == -q.Q4LIN_E_SHAPE
+    st = q.q4lin_linear(0x1000, 0x1000, 0x1000, 0x1000, n, k, t, 0x1000, 1 << 30, 0)
+    assert st == q.Q4LIN_E_SHAPE
+
+
+def test_empty_product_is_a_no_op():
+    for n, t in [(0, 5), (6, 0), (0, 0)]:
+        assert q.q4lin_route(n, 128, t) == q.Q4LIN_ROUTE_NONE
+        assert q.q4lin_workspace_bytes(n, 128, t) == 0
+        assert q.q4lin_linear(0, 0, 0, 0, n, 128, t, 0, 0, 0) == q.Q4LIN_OK
+
+
+@pytest.mark.parametrize("which", range(4))
+def test_null_pointer_rejected(which):
+    ptrs = [0x1000, 0x1000, 0x1000, 0x1000]
+    ptrs[which] = 0
+    assert q.q4lin_linear(*ptrs, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_NULL
+
+
+@pytest.mark.parametrize("which,addr", [(0, 0x1008), (1, 0x1004), (2, 0x1001), (3, 0x1001)])
+def test_misaligned_pointer_rejected(which, addr):
+    ptrs = [0x1000, 0x1000, 0x1000, 0x1000]
+    ptrs[which] = addr
+    assert q.q4lin_linear(*ptrs, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
+
+
+def test_workspace_checks():
+    n, k, t = 256, 512, 300
+    need = q.q4lin_workspace_bytes(n, k, t)
+    assert need > 0
+    p = 0x10000
+    assert q.q4lin_linear(p, p, p, p, n, k, t, p, need - 1, 0) == q.Q4LIN_E_WORKSPACE
+    assert q.q4lin_linear(p, p, p, p, n, k, t, 0, need, 0) == q.Q4LIN_E_NULL
+    assert q.q4lin_linear(p, p, p, p, n, k, t, p + 16, need, 0) == q.Q4LIN_E_ALIGN
+
+
+def test_routes_and_workspace_sizes():
+    # T = 1 is the few-token route, with no workspace
+    assert q.q4lin_route(6144, 5120, 1) == q.Q4LIN_ROUTE_GEMV
+    assert q.q4lin_workspace_bytes(6144, 5120, 1) == 0
+    for t in (1, 2, 3, 4, 5, 16, 64, 128, 512, 1024):
+        r = q.q4lin_route(6144, 5120, t)
+        assert r in (q.Q4LIN_ROUTE_GEMV, q.Q4LIN_ROUTE_SKINNY, q.Q4LIN_ROUTE_TILED)
+        ws = q.q4lin_workspace_bytes(6144, 5120, t)
+        if r == q.Q4LIN_ROUTE_TILED:
+            # float16 activations padded to 32 tokens plus one int32 per token
+            tp = (t + 31) // 32 * 32
+            assert ws >= tp * 5120 * 2 + tp * 4
+        else:
+            assert ws == 0
+    assert q.q4lin_route(6144, 5120, 1024) == q.Q4LIN_ROUTE_TILED

@@ -1,0 +1,254 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI, on the
+seeded workloads and the edge cases.  Needs an MI355X."""
+import hashlib
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+from gpu_util import (announce, assert_close, dev, host_bits, oracle_full, oracle_sampled,
+                      run_op, sample_indices, tolerance_violations, torch)
+from weight_only_bit_q4_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+# boundaries of the workgroup tiles (rows) and token tiles used by the kernels
+ROW_EDGES = [15, 16, 31, 32, 95, 96, 191, 192, 6143]
+TOK_EDGES = [1, 31, 32, 63, 64, 127, 128, 255, 256, 511, 512, 1023]
+
+
+def _problem(workload, n, k, t):
+    seed = inputs.workload_seed(workload)
+    return inputs.gen_problem(n, k, t, seed)
+
+
+# ---------------------------------------------------------------------------
+# hand-worked examples: exact in FP32 for every example except the ones whose
+# point is binary64 behaviour (single rounding from a sum below FP32
+# resolution, bf16 subnormal results), which are held to the tolerance.
+# ---------------------------------------------------------------------------
+FP32_INEXACT = {"E15_single_rounding_from_fp64", "E16_single_rounding_negative", "E17_subnormal_output_tie"}
+
+
+@pytest.mark.parametrize("replicate", [1, 40], ids=["as_is", "tokens_x40"])
+def test_worked_examples(replicate):
+    for ex in oracle_pins.load_examples():
+        x, codes, scales, want = oracle_pins.materialize(ex)
+        n, k, t = ex["n"], ex["k"], ex["t"]
+        # Replicating the tokens moves the example onto the many-token route;
+        # every copy must give the same column.
+        xr = np.tile(x, (replicate, 1))
+        got = run_op(xr, codes, scales, n, k, t * replicate, what=ex["name"])
+        want_r = np.tile(want.reshape(t, n), (replicate, 1))
+        if ex["name"] in FP32_INEXACT:
+            assert_close(got, want_r, what=ex["name"])
+        else:
+            assert np.array_equal(got.reshape(-1), want_r.reshape(-1)), (
+                ex["name"], [hex(v) for v in got.reshape(-1)[:8]], [hex(v) for v in want_r.reshape(-1)[:8]])
+
+
+# ---------------------------------------------------------------------------
+# the workloads
+# ---------------------------------------------------------------------------
+def test_small_512x1024_t4():
+    n, k, t = 512, 1024, 4
+    x, c, s = _problem("small_512x1024_t4", n, k, t)
+    got = run_op(x, c, s, n, k, t, what="small")
+    assert_close(got, oracle_full(x, c, s, n, k, t), what="512x1024 T=4")
+
+
+def test_decode_6144x5120_t1():
+    n, k, t = 6144, 5120, 1
+    x, c, s = _problem("decode_6144x5120_t1", n, k, t)
+    got = run_op(x, c, s, n, k, t, what="decode")
+    assert_close(got, oracle_full(x, c, s, n, k, t), what="6144x5120 T=1")
+
+
+def test_sweep_6144x5120_t1_to_128():
+    """Every T in 1..128 on the same weight, activations a prefix of one
+    128-token buffer; the oracle checks 600 sampled outputs per T (plus tile
+    boundaries) and every output at a few T."""
+    n, k, tmax = 6144, 5120, 128
+    seed = inputs.workload_seed("sweep_6144x5120_t1_128")
+    c = inputs.gen_codes(n, k, seed)
+    s = inputs.gen_scales(n, k, seed)
+    xall = inputs.gen_x(k, tmax, seed)
+    full_ts = {1, 2, 3, 4, 5, 16, 33}
+    for t in range(1, tmax + 1):
+        x = xall[:t]
+        got = run_op(x, c, s, n, k, t, what="sweep")
+        if t in full_ts:
+            assert_close(got, oracle_full(x, c, s, n, k, t), what="sweep T=%d full" % t)
+        else:
+            ns, ts = sample_indices(n, t, 600, seed + t, ROW_EDGES, TOK_EDGES)
+            ref = oracle_sampled(x, c, s, n, k, t, ns, ts)
+            assert_close(got[ts, ns], ref, what="sweep T=%d" % t)
+
+
+@pytest.mark.parametrize("t", [1024, 512, 384, 385, 640, 641])
+def test_prefill_6144x5120(t):
+    n, k = 6144, 5120
+    seed = inputs.workload_seed("prefill_6144x5120_t1024")
+    c = inputs.gen_codes(n, k, seed)
+    s = inputs.gen_scales(n, k, seed)
+    x = inputs.gen_x(k, t, seed)
+    got = run_op(x, c, s, n, k, t, what="prefill")
+    ns, ts = sample_indices(n, t, 3000, seed + t, ROW_EDGES, TOK_EDGES)
+    ref = oracle_sampled(x, c, s, n, k, t, ns, ts)
+    assert_close(got[ts, ns], ref, what="prefill T=%d" % t)
+    # column independence on the GPU: the first tokens alone give the same
+    # values up to the route's rounding
+    got8 = run_op(x[:8], c, s, n, k, 8, what="prefill prefix")
+    assert_close(got8, oracle_full(x[:8], c, s, n, k, 8), what="prefill prefix T=8")
+
+
+@pytest.mark.parametrize("shape", [(14336, 5120), (34816, 5120), (5120, 17408)], ids=lambda s: "%dx%d" % s)
+@pytest.mark.parametrize("t", [1, 1024])
+def test_large_shapes(shape, t):
+    n, k = shape
+    seed = inputs.workload_seed("large_shapes_t1_t1024") + n + k
+    c = inputs.gen_codes(n, k, seed)
+    s = inputs.gen_scales(n, k, seed)
+    x = inputs.gen_x(k, t, seed)
+    got = run_op(x, c, s, n, k, t, what="large")
+    if t == 1:
+        assert_close(got, oracle_full(x, c, s, n, k, t), what="%dx%d T=1" % shape)
+    else:
+        ns, ts = sample_indices(n, t, 3000, seed, ROW_EDGES + [n - 97, n - 96, n - 33, n - 32], TOK_EDGES)
+        ref = oracle_sampled(x, c, s, n, k, t, ns, ts)
+        assert_close(got[ts, ns], ref, what="%dx%d T=%d" % (shape + (t,)))
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,k,t", [
+    (1, 64, 1), (1, 64, 2), (7, 64, 3), (33, 128, 4), (97, 192, 5), (1, 64, 33), (17, 320, 31),
+    (200, 576, 129), (5, 1088, 257), (130, 4160, 70), (300, 2048, 1), (16, 64, 1000),
+])
+def test_ragged_shapes(n, k, t):
+    x, c, s = inputs.gen_problem(n, k, t, 1000 + n + k + t)
+    got = run_op(x, c, s, n, k, t, what="ragged")
+    assert_close(got, oracle_full(x, c, s, n, k, t), what="ragged %dx%d T=%d" % (n, k, t))
+
+
+@pytest.mark.parametrize("t", [1, 3, 40, 300])
+def test_all_code8_gives_exact_zeros(t):
+    n, k = 96, 640
+    x, c, s = inputs.gen_problem(n, k, t, 77)
+    c[:] = 0x88
+    got = run_op(x, c, s, n, k, t, what="all8")
+    assert np.all((got & 0x7FFF) == 0)
+
+
+@pytest.mark.parametrize("t", [1, 4, 48, 260])
+def test_wide_range_scales_and_activations(t):
+    """Scales over the whole FP16 range (subnormal, negative, zero) and
+    activations spread over many binades, with a few large outliers."""
+    n, k = 64, 1024
+    r = np.random.default_rng(5 + t)
+    c = r.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    sv = r.choice([-1, 1], size=(n, k // 64)) * np.ldexp(r.uniform(1, 2, (n, k // 64)),
+                                                         r.integers(-24, 15, (n, k // 64)))
+    sv[r.random((n, k // 64)) < 0.05] = 0.0
+    s = sv.astype(np.float16).view(np.uint16)
+    xv = (r.standard_normal((t, k)) * np.ldexp(1.0, r.integers(-30, 30, (t, k)))).astype(np.float32)
+    xv[:, 7] = 3.0e30
+    x = inputs.f32_to_bf16_bits(xv)
+    got = run_op(x, c, s, n, k, t, what="wide-range")
+    assert_close(got, oracle_full(x, c, s, n, k, t), what="wide range T=%d" % t)
+
+
+def test_extreme_magnitudes_finite_and_infinite():
+    """Largest finite activations and scales: results overflow to +-Inf
+    exactly where the exact sum does; nothing becomes NaN."""
+    n, k = 32, 128
+    for t in (1, 40):
+        r = np.random.default_rng(9)
+        c = r.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        s = np.full((n, k // 64), 0x7BFF, dtype=np.uint16)   # 65504
+        s[::2] = 0x0400                                       # 2^-14 on even rows
+        xv = np.full((t, k), 3.0e38, dtype=np.float32) * r.choice([-1, 1], size=(t, k))
+        x = inputs.f32_to_bf16_bits(xv)
+        got = run_op(x, c, s, n, k, t, what="extreme")
+        want = oracle_full(x, c, s, n, k, t)
+        assert not np.any(((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)), "NaN produced"
+        assert_close(got, want, what="extreme T=%d" % t)
+
+
+# ---------------------------------------------------------------------------
+# contract properties: inputs preserved, writes confined to y, graph replay,
+# determinism
+# ---------------------------------------------------------------------------
+def _digest(tensor):
+    return hashlib.sha256(tensor.detach().cpu().contiguous().view(torch().uint8).numpy().tobytes()).hexdigest()
+
+
+@pytest.mark.parametrize("t", [1, 3, 100])
+def test_inputs_preserved_and_output_guarded(t):
+    import weight_only_bit_q4_amd as q4
+    th = torch()
+    n, k = 400, 768
+    x, c, s = inputs.gen_problem(n, k, t, 4242)
+    xd, cd, sd = dev(x), dev(c), dev(s)
+    before = [_digest(v) for v in (xd, cd, sd)]
+    pad = 4096
+    canary = 0x5A5A
+    buf = th.full((t * n + 2 * pad,), canary, dtype=th.int16, device="cuda")
+    y = buf[pad:pad + t * n].view(t, n)
+    need = q4.q4lin_workspace_bytes(n, k, t)
+    ws = th.full((max(need, 1) + 2 * pad,), 0x33, dtype=th.uint8, device="cuda") if need else None
+    wsv = ws[pad:pad + need] if need else None
+    announce("guard q4lin_linear n=%d k=%d t=%d" % (n, k, t))
+    q4.linear(xd, cd, sd, y=y, workspace=wsv)
+    th.cuda.synchronize()
+    assert [_digest(v) for v in (xd, cd, sd)] == before
+    h = buf.cpu().numpy()
+    assert np.all(h[:pad] == canary) and np.all(h[pad + t * n:] == canary)
+    if need:
+        hw = ws.cpu().numpy()
+        assert np.all(hw[:pad] == 0x33) and np.all(hw[pad + need:] == 0x33)
+    assert_close(host_bits(y), oracle_full(x, c, s, n, k, t), what="guarded")
+
+
+@pytest.mark.parametrize("t", [1, 2, 96, 700])
+def test_graph_replay_with_changed_inputs(t):
+    """Capture one call in a HIP graph, then change the activations and the
+    weights in place and replay: every replay must match the oracle for the
+    inputs of that moment, and eager work between replays must not disturb it."""
+    import weight_only_bit_q4_amd as q4
+    th = torch()
+    n, k = 256, 1024
+    x0, c0, s0 = inputs.gen_problem(n, k, t, 51)
+    xd, cd, sd = dev(x0), dev(c0), dev(s0)
+    y = th.empty((t, n), dtype=th.bfloat16, device="cuda")
+    need = q4.q4lin_workspace_bytes(n, k, t)
+    ws = th.empty(max(need, 1), dtype=th.uint8, device="cuda")
+    q4.linear(xd, cd, sd, y=y, workspace=ws[:need] if need else None)   # warm-up outside capture
+    th.cuda.synchronize()
+    g = th.cuda.CUDAGraph()
+    announce("graph capture n=%d k=%d t=%d" % (n, k, t))
+    with th.cuda.graph(g):
+        q4.linear(xd, cd, sd, y=y, workspace=ws[:need] if need else None)
+    for rep in range(3):
+        x, c, s = inputs.gen_problem(n, k, t, 52 + rep)
+        xd.copy_(dev(x))
+        cd.copy_(dev(c))
+        sd.copy_(dev(s))
+        th.cuda.synchronize()
+        g.replay()
+        th.cuda.synchronize()
+        assert_close(host_bits(y), oracle_full(x, c, s, n, k, t), what="replay %d" % rep)
+        # unrelated eager work between replays
+        junk = th.randn(1 << 20, device="cuda")
+        junk.sum().item()
+
+
+@pytest.mark.parametrize("t", [1, 4, 64, 1024])
+def test_deterministic(t):
+    n, k = 6144, 5120
+    x, c, s = inputs.gen_problem(n, k, t, 99)
+    a = run_op(x, c, s, n, k, t, what="determinism a")
+    b = run_op(x, c, s, n, k, t, what="determinism b")
+    assert np.array_equal(a, b)

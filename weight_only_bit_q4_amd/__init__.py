@@ -1,0 +1,144 @@
+"""weight_only_bit_q4_amd -- the Q4_G64_FP16 weight-only Linear on MI355X.
+
+Python binding of the C ABI declared in ``include/q4lin.h``.  The functions
+carry the C names and only marshal arguments; every step of the op runs in the
+HIP kernels of ``libq4lin.so``.  The library is loaded on the first call
+(``load()``) and a missing library raises at once (build it with
+``python -m weight_only_bit_q4_amd.build``); there is no fallback path.  The
+seeded input generators in ``weight_only_bit_q4_amd.inputs`` import without
+it.
+
+``linear`` is a convenience over torch tensors (device memory and streams
+only): it checks dtypes/shapes, allocates the output and workspace when the
+caller does not pass them, and calls ``q4lin_linear`` on the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libq4lin.so")
+
+Q4LIN_OK = 0
+Q4LIN_E_NULL = 1
+Q4LIN_E_SHAPE = 2
+Q4LIN_E_ALIGN = 3
+Q4LIN_E_WORKSPACE = 4
+Q4LIN_E_LAUNCH = 5
+
+Q4LIN_ROUTE_NONE = 0
+Q4LIN_ROUTE_GEMV = 1
+Q4LIN_ROUTE_SKINNY = 2
+Q4LIN_ROUTE_TILED = 3
+
+EXPORTED = ("q4lin_workspace_bytes", "q4lin_linear", "q4lin_status_string", "q4lin_route",
+            "q4lin_version")
+
+
+class Q4LinError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__("q4lin: %s (status %d)" % (q4lin_status_string(status), status))
+
+
+def _load() -> ctypes.CDLL:
+    # Device memory and streams come from torch, which carries its own HIP
+    # runtime; import it first so libq4lin.so binds to that runtime instead of
+    # mapping a second one (pointers and streams are only valid in the runtime
+    # that made them).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libq4lin.so is not built: run `python -m weight_only_bit_q4_amd.build` "
+                          "(expected at %s)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    lib.q4lin_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.q4lin_workspace_bytes.restype = i64
+    lib.q4lin_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.q4lin_linear.restype = ctypes.c_int
+    lib.q4lin_status_string.argtypes = [ctypes.c_int]
+    lib.q4lin_status_string.restype = ctypes.c_char_p
+    lib.q4lin_route.argtypes = [i64, i64, i64]
+    lib.q4lin_route.restype = ctypes.c_int
+    lib.q4lin_version.argtypes = []
+    lib.q4lin_version.restype = ctypes.c_int
+    return lib
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libq4lin.so (once); raises ImportError when it is not built."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+# -- the C ABI, same names ---------------------------------------------------
+def q4lin_workspace_bytes(n: int, k: int, t: int) -> int:
+    return int(load().q4lin_workspace_bytes(int(n), int(k), int(t)))
+
+
+def q4lin_linear(x: int, codes: int, scales: int, y: int, n: int, k: int, t: int,
+                 workspace: int, workspace_bytes: int, stream: int) -> int:
+    """Raw call: device addresses as integers (0 for NULL); returns the status."""
+    return int(load().q4lin_linear(x or None, codes or None, scales or None, y or None,
+                                 int(n), int(k), int(t), workspace or None,
+                                 int(workspace_bytes), stream or None))
+
+
+def q4lin_status_string(status: int) -> str:
+    return load().q4lin_status_string(int(status)).decode()
+
+
+def q4lin_route(n: int, k: int, t: int) -> int:
+    return int(load().q4lin_route(int(n), int(k), int(t)))
+
+
+def q4lin_version() -> int:
+    return int(load().q4lin_version())
+
+
+# -- torch convenience (marshalling only) -------------------------------------
+def linear(x, codes, scales, y=None, workspace=None, stream=None):
+    """Y = W x X on torch device tensors.
+
+    ``x``: uint16/int16/bfloat16 ``[T, K]`` (bf16 bits, token-major);
+    ``codes``: uint8 ``[N, K/2]``; ``scales``: float16/int16/uint16 ``[N, K/64]``;
+    ``y``: optional bfloat16/int16/uint16 ``[T, N]`` output.  Returns ``y``.
+    """
+    import torch
+
+    t, k = x.shape
+    n = codes.shape[0]
+    if codes.shape[1] * 2 != k or tuple(scales.shape) != (n, k // 64):
+        raise ValueError("shape mismatch: x %s codes %s scales %s" % (tuple(x.shape), tuple(codes.shape),
+                                                                      tuple(scales.shape)))
+    for name, ten, size in (("x", x, 2), ("codes", codes, 1), ("scales", scales, 2)):
+        if not ten.is_contiguous() or ten.element_size() != size:
+            raise ValueError("%s must be contiguous with %d-byte elements" % (name, size))
+    if y is None:
+        y = torch.empty((t, n), dtype=torch.bfloat16, device=x.device)
+    if tuple(y.shape) != (t, n) or y.element_size() != 2 or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [T, N] tensor of 2-byte elements")
+    need = q4lin_workspace_bytes(n, k, t)
+    if need < 0:
+        raise Q4LinError(-need)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = q4lin_linear(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), y.data_ptr(), n, k, t,
+                      ws_ptr, ws_bytes, stream)
+    if st != Q4LIN_OK:
+        raise Q4LinError(st)
+    return y

@@ -1,0 +1,96 @@
+// q4lin_api.hip -- the C ABI: argument validation, route choice, launch.
+//
+// The contract follows the pages' public Linear call
+// linear(x, w, out, policy, workspace, stream) ("linear-benchmark.md",
+// section 0): the caller owns every buffer, the workspace size comes from a
+// capacity query answered before any timed call (same page, section 1.1),
+// and shapes the op does not support are rejected by the op itself (same
+// page, section 1.1, on numeric N/K points).  Only the A16 policy exists, so
+// there is no policy argument.
+#include <stdint.h>
+
+#include "../../include/q4lin.h"
+#include "q4lin_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxT = int64_t(1) << 21;
+constexpr int64_t kMaxK = int64_t(1) << 20;
+constexpr int64_t kMaxBytes = int64_t(1) << 40;
+constexpr size_t kGemvLdsLimit = 64 * 1024;
+
+bool shape_ok(int64_t n, int64_t k, int64_t t) {
+  if (n < 0 || t < 0 || k < 64 || (k % 64) != 0) return false;
+  if (n > kMaxN || t > kMaxT || k > kMaxK) return false;
+  if (n * (k / 2) >= kMaxBytes || t * k * 2 >= kMaxBytes || t * n * 2 >= kMaxBytes) return false;
+  return true;
+}
+
+int pick_route(int64_t n, int64_t k, int64_t t) {
+  if (n == 0 || t == 0) return Q4LIN_ROUTE_NONE;
+  if (t <= 4 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
+  return Q4LIN_ROUTE_TILED;
+}
+
+size_t route_workspace(int route, int64_t k, int64_t t) {
+  return route == Q4LIN_ROUTE_TILED ? q4lin::tiled_workspace_bytes(k, t) : 0;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t q4lin_workspace_bytes(int64_t n, int64_t k, int64_t t) {
+  if (!shape_ok(n, k, t)) return -Q4LIN_E_SHAPE;
+  return (int64_t)route_workspace(pick_route(n, k, t), k, t);
+}
+
+int q4lin_route(int64_t n, int64_t k, int64_t t) {
+  if (!shape_ok(n, k, t)) return -Q4LIN_E_SHAPE;
+  return pick_route(n, k, t);
+}
+
+int q4lin_linear(const void* x, const void* codes, const void* scales, void* y,
+                 int64_t n, int64_t k, int64_t t,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape_ok(n, k, t)) return Q4LIN_E_SHAPE;
+  const int route = pick_route(n, k, t);
+  if (route == Q4LIN_ROUTE_NONE) return Q4LIN_OK;
+  if (!x || !codes || !scales || !y) return Q4LIN_E_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(y, 2))
+    return Q4LIN_E_ALIGN;
+  const size_t need = route_workspace(route, k, t);
+  if (need > 0) {
+    if (workspace_bytes < need) return Q4LIN_E_WORKSPACE;
+    if (!workspace) return Q4LIN_E_NULL;
+    if (!aligned(workspace, 256)) return Q4LIN_E_ALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (route == Q4LIN_ROUTE_GEMV) {
+    e = q4lin::launch_gemv(q4lin::GemvArgs{x, codes, scales, y, n, k, t}, s);
+  } else {
+    q4lin::TiledArgs a{x, codes, scales, y, n, k, t, workspace, q4lin::tiled_pick_config(n, k, t)};
+    e = q4lin::launch_tiled(a, s);
+  }
+  return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+}
+
+const char* q4lin_status_string(int status) {
+  switch (status) {
+    case Q4LIN_OK: return "ok";
+    case Q4LIN_E_NULL: return "a required pointer is NULL";
+    case Q4LIN_E_SHAPE: return "shape outside the contract (K a positive multiple of 64, sizes within limits)";
+    case Q4LIN_E_ALIGN: return "pointer misaligned (x, codes: 16 B; scales, y: 2 B; workspace: 256 B)";
+    case Q4LIN_E_WORKSPACE: return "workspace smaller than q4lin_workspace_bytes()";
+    case Q4LIN_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int q4lin_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// q4lin_device.h -- device-side building blocks shared by the q4lin kernels
+// (gfx950 only).  Internal header: not part of the C ABI.
+//
+// Number formats (Q4_G64_FP16, "linear-benchmark.md" section 4 table; the
+// value of a code q is (q - 8) * scale):
+//   * a code dword holds 8 nibbles, k0..k7 from the least significant nibble
+//     up (even k in the low nibble of each byte);
+//   * the kernels pair nibble s with nibble s+4 of a dword, so one dword turns
+//     into the four pairs (k0,k4) (k1,k5) (k2,k6) (k3,k7).  Activations are
+//     staged in the same pair order, which leaves every dot product unchanged.
+//   * weights enter the arithmetic as exact float16 values q - 8; activations
+//     as float16 copies of the bf16 inputs scaled by a per-token power of two
+//     2^-e (exact for every value within 2^38 of the token's largest
+//     magnitude), undone in FP32 at the end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4lin {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+
+// float16 pair (q - 8) for the nibble pair (s, s+4): 0x6400 | q is 1024 + q
+// exactly (fp16 quantum in [1024, 2048) is 1); subtracting 1032 is exact too.
+__device__ __forceinline__ uint32_t f16_pair_q_minus_8(uint32_t w, int s) {
+  uint32_t m = ((w >> s) & 0x000F000Fu) | 0x64006400u;
+  f16x2_t v = __builtin_bit_cast(f16x2_t, m);
+  const f16x2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  v = v - off;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// binary32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+}  // namespace q4lin

@@ -1,0 +1,48 @@
+// q4lin_kernels.h -- host-side launchers of the q4lin kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4lin {
+
+struct GemvArgs {
+  const void* x;
+  const void* codes;
+  const void* scales;
+  void* y;
+  int64_t n, k, t;
+};
+
+// LDS bytes the few-token kernel needs: activations (bf16) plus one offset
+// sum per (token, 32-weight chunk).
+size_t gemv_lds_bytes(int64_t k, int64_t t);
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
+
+// Tiled matrix-core route.  Workspace layout (256-byte aligned pieces):
+//   x16   fp16 activations scaled by 2^-e[t], tile order (see q4lin_tiled.hip),
+//         tpad * k * 2 bytes with tpad = t rounded up to 32;
+//   texp  int32 e[t], tpad * 4 bytes.
+struct TiledConfig {
+  int ns;  // 32-row subtiles per wave
+  int ts;  // 32-token subtiles per wave
+  int wt;  // waves per workgroup (all share the workgroup's rows)
+};
+
+struct TiledArgs {
+  const void* x;
+  const void* codes;
+  const void* scales;
+  void* y;
+  int64_t n, k, t;
+  void* workspace;
+  TiledConfig cfg;
+};
+
+int64_t tiled_tpad(int64_t t);
+size_t tiled_workspace_bytes(int64_t k, int64_t t);
+TiledConfig tiled_pick_config(int64_t n, int64_t k, int64_t t);
+hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream);
+
+}  // namespace q4lin
