@@ -129,17 +129,19 @@ class Point:
         g = self.graph(steps)
         gw = self.graph(max(warmup, 1), offset=steps) if warmup > 0 else None
         out = []
-        for _ in range(repeats):
-            if gw is not None:
-                gw.replay()
-            torch.cuda.synchronize()
-            start = torch.cuda.Event(enable_timing=True)
-            end = torch.cuda.Event(enable_timing=True)
-            start.record(self.stream)
-            g.replay()
-            end.record(self.stream)
-            torch.cuda.synchronize()
-            out.append(start.elapsed_time(end) / 1e3 / steps)
+        # replay() launches on the current stream: make that the timed stream
+        with torch.cuda.stream(self.stream):
+            for _ in range(repeats):
+                if gw is not None:
+                    gw.replay()
+                torch.cuda.synchronize()
+                start = torch.cuda.Event(enable_timing=True)
+                end = torch.cuda.Event(enable_timing=True)
+                start.record(self.stream)
+                g.replay()
+                end.record(self.stream)
+                torch.cuda.synchronize()
+                out.append(start.elapsed_time(end) / 1e3 / steps)
         return out
 
     def free(self):

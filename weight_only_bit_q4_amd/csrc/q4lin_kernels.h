@@ -15,8 +15,11 @@ struct GemvArgs {
   int64_t n, k, t;
 };
 
-// LDS bytes the few-token kernel needs: activations (bf16) plus one offset
-// sum per (token, 32-weight chunk).
+// Few-token route.  Each of the 4 waves of a workgroup owns a quarter of the
+// 32-weight chunks of every row; gemv_chunks_per_wave is that quarter's
+// capacity (rounded up), gemv_lds_bytes the dynamic LDS the kernel needs:
+// float16 activations plus one all-8 chunk sum per (token, chunk).
+int64_t gemv_chunks_per_wave(int64_t k);
 size_t gemv_lds_bytes(int64_t k, int64_t t);
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 
