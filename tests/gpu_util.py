@@ -1,7 +1,7 @@
 """Helpers for the GPU parity tests: device transfer, one call of the op
 through the C ABI, and the parity tolerance.
 
-Tolerance (the workload statement of the benchmark spec): every output must
+Tolerance (the accuracy bound stated for this operation): every output must
 satisfy |y - y_o| <= 1e-2 * |y_o| + 1e-3 * rms(y_o), with y_o the oracle's
 bf16 output and rms over the oracle output tensor.  Where only sampled
 outputs are computed by the oracle, rms is taken over the sample (an unbiased

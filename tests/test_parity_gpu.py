@@ -133,6 +133,50 @@ def test_ragged_shapes(n, k, t):
     assert_close(got, oracle_full(x, c, s, n, k, t), what="ragged %dx%d T=%d" % (n, k, t))
 
 
+def test_k64_few_tokens_after_stale_lds():
+    """K = 64 leaves two of the few-token kernel's four K quarters empty.
+
+    A many-token call on all-0xFF codes first leaves float16 NaN bit patterns
+    in the LDS of every compute unit; the few-token calls that follow must not
+    pick any of them up (regression: an empty quarter once read stale LDS).
+    """
+    n0, k0, t0 = 6144, 512, 256
+    x, c, s = inputs.gen_problem(n0, k0, t0, 4242)
+    c[:] = 0xFF
+    run_op(x, c, s, n0, k0, t0, what="stale-lds fill")
+    for t in (1, 2, 3, 4):
+        n, k = 8192, 64
+        x, c, s = inputs.gen_problem(n, k, t, 4300 + t)
+        got = run_op(x, c, s, n, k, t, what="k64 after stale lds")
+        assert_close(got, oracle_full(x, c, s, n, k, t), what="k64 %dx%d T=%d" % (n, k, t))
+
+
+@pytest.mark.parametrize("n,k,t", [(97, 320, 1), (97, 320, 3), (97, 320, 40), (193, 576, 300)])
+def test_scales_and_output_only_2byte_aligned(n, k, t):
+    """Scales and y need only 2-byte alignment: run with both at an address 2 mod 4."""
+    import weight_only_bit_q4_amd as q4
+    th = torch()
+    x, c, s = inputs.gen_problem(n, k, t, 5000 + n + t)
+    announce("misaligned scales/y q4lin_linear n=%d k=%d t=%d" % (n, k, t))
+    xd = dev(x.reshape(t, k))
+    cd = dev(c.reshape(n, k // 2))
+    s_big = th.zeros(n * (k // 64) + 1, dtype=th.int16, device="cuda")
+    s_big[1:] = dev(s.reshape(-1))
+    sd = s_big[1:]
+    y_big = th.zeros(t * n + 1, dtype=th.int16, device="cuda")
+    yd = y_big[1:]
+    assert sd.data_ptr() % 4 == 2 and yd.data_ptr() % 4 == 2
+    ws_bytes = q4.q4lin_workspace_bytes(n, k, t)
+    ws = th.empty(max(ws_bytes, 1), dtype=th.uint8, device="cuda")
+    st = q4.q4lin_linear(xd.data_ptr(), cd.data_ptr(), sd.data_ptr(), yd.data_ptr(), n, k, t,
+                         ws.data_ptr(), ws_bytes, th.cuda.current_stream().cuda_stream)
+    assert st == 0, q4.q4lin_status_string(st)
+    th.cuda.synchronize()
+    got = host_bits(yd).reshape(t, n)
+    assert_close(got, oracle_full(x, c, s, n, k, t), what="misaligned %dx%d T=%d" % (n, k, t))
+    assert int(y_big[0].item()) == 0
+
+
 @pytest.mark.parametrize("t", [1, 3, 40, 300])
 def test_all_code8_gives_exact_zeros(t):
     n, k = 96, 640

@@ -189,6 +189,13 @@ gemv_kernel(const u32x4_t* __restrict__ x, const uint8_t* __restrict__ codes,
       for (int b = lane + 192; b < nb; b += 64)
         xq[(t * 4 + (b & 3)) * cq + (b >> 2)] = to_f16_pairs(x[(size_t)t * (K >> 3) + 4 * cw0 + b], e[t]);
   }
+  // An empty quarter (K = 64 has two chunks for four waves) still runs step 5
+  // at the clamped position 0 with zero scales; give that position finite
+  // zeros, since 0 times a stale NaN left in LDS would still be NaN.
+  if (cw == 0) {
+    if (lane < 4 * T) xq[lane * cq] = u32x4_t{0u, 0u, 0u, 0u};
+    if (lane < T) s8[lane * cq] = 0.0f;
+  }
   // 4. all-8 chunk sums, same dot2 chain as the rows use
   const u32x4_t k8 = kEights;
 #pragma unroll

@@ -30,7 +30,8 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 struct TiledConfig {
   int ns;  // 32-row subtiles per wave
   int ts;  // 32-token subtiles per wave
-  int wt;  // waves per workgroup (all share the workgroup's rows)
+  int wn;  // waves along the rows
+  int wt;  // waves along the tokens
 };
 
 struct TiledArgs {
