@@ -32,6 +32,8 @@
 // barrier per group publishes that tile and the ring stage to all waves.
 // Waits are explicit s_waitcnt vmcnt(n) with n the count of younger stages
 // still allowed in flight; the compiler's own fences would wait for all.
+#include <type_traits>
+
 #include "q4lin_device.h"
 #include "q4lin_kernels.h"
 
@@ -41,18 +43,11 @@ namespace {
 
 
 // ---------------------------------------------------------------------------
-// activation preparation: one wave per token
+// activation preparation
 // ---------------------------------------------------------------------------
-constexpr int kPrepWaves = 4;
-constexpr int kPrepRegBlocks = 12;  // 8-value blocks per lane kept in registers
-
 // Tile order: for token block tb (32 tokens) and group g, 4 KB laid out
 // [m 0..3][h 0..1][i 0..31][8 values]; the 8 values are k = 64g + 32h + 8m +
-// (0,4,1,5,2,6,3,7) (pair order), i the token inside the block.  Index in
-// 16-byte units.
-__device__ __forceinline__ size_t x16_index(int tb, int g, int G, int m, int h, int i) {
-  return ((size_t)tb * G + g) * 256 + (size_t)((m * 2 + h) * 32 + i);
-}
+// (0,4,1,5,2,6,3,7) (pair order), i the token inside the block.
 
 __device__ __forceinline__ uint32_t max_mag8(u32x4_t v) {
   uint32_t m = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
@@ -71,51 +66,76 @@ __device__ __forceinline__ u32x4_t to_f16_pairs(u32x4_t v, int e) {
   return u32x4_t{h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16), h[3] | (h[7] << 16)};
 }
 
-__global__ void __launch_bounds__(64 * kPrepWaves)
-prep_x_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, u32x4_t* __restrict__ x16,
-              int* __restrict__ texp) {
+// Per-token exponent e[t]: the token's largest magnitude times 2^-e lies in
+// [2^14, 2^15), so every bf16 value within 2^34 of it converts to float16
+// exactly; 0 for all-zero and padding tokens.  One wave per token.
+constexpr int kExpWaves = 4;
+__global__ void __launch_bounds__(64 * kExpWaves)
+prep_exp_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __restrict__ texp) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
+  const int t = blockIdx.x * kExpWaves + (threadIdx.x >> 6);
   if (t >= Tpad) return;
-  const int G = K >> 6;
-  const int nb = K >> 3;
-  const int tb = t >> 5, i = t & 31;
-  if (t >= T) {  // padding token: zeros, exponent 0
-    for (int b = lane; b < nb; b += 64) {
-      const int g = b >> 3, kb = b & 7;
-      x16[x16_index(tb, g, G, kb & 3, kb >> 2, i)] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-    if (lane == 0) texp[t] = 0;
-    return;
-  }
-  const u32x4_t* xt = x + (size_t)t * nb;
-  u32x4_t v[kPrepRegBlocks];
   uint32_t m = 0;
+  if (t < T) {
+    const int nb = K >> 3;
+    const u32x4_t* xt = x + (size_t)t * nb;
+    // sixteen independent loads in flight per lane (clamped, so no load is
+    // conditional: a load behind a branch would be waited for on its own)
+    for (int b0 = 0; b0 < nb; b0 += 1024) {
+      u32x4_t v[16];
 #pragma unroll
-  for (int j = 0; j < kPrepRegBlocks; ++j) {
-    const int b = lane + 64 * j;
-    v[j] = b < nb ? xt[b] : u32x4_t{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 16; ++j) v[j] = xt[min(b0 + lane + 64 * j, nb - 1)];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m = max(m, max_mag8(v[j]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
   }
-#pragma unroll
-  for (int j = 0; j < kPrepRegBlocks; ++j) m = max(m, max_mag8(v[j]));
-  for (int b = lane + 64 * kPrepRegBlocks; b < nb; b += 64) m = max(m, max_mag8(xt[b]));
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
   if (m >= 0x7F80u) m = 0x7F7Fu;  // Inf/NaN inputs are outside the contract
   int e = 0;
   if (m != 0u) e = ((m >= 0x80u) ? (int)(m >> 7) - 127 : (31 - __builtin_clz(m)) - 133) - 14;
   if (lane == 0) texp[t] = e;
+}
+
+// Float16 activations in tile order: one workgroup per (token block, eight
+// groups).  Reads are 128-byte runs of token rows, the LDS holds the 32 KB
+// chunk in tile order, and the writes are contiguous.  Padding tokens and
+// groups past the end give zeros / are skipped.
+constexpr int kPackGroups = 8;
+__global__ void __launch_bounds__(256)
+prep_pack_kernel(const u32x4_t* __restrict__ x, int K, int T, const int* __restrict__ texp,
+                 u32x4_t* __restrict__ x16) {
+  __shared__ u32x4_t tile[kPackGroups * 256];
+  const int G = K >> 6, nb = K >> 3;
+  const int tb = blockIdx.x, g0 = blockIdx.y * kPackGroups;
+  const int tid = threadIdx.x;
+  // All loads first, from clamped (valid) addresses; out-of-range values are
+  // zeroed afterwards.
+  u32x4_t v[kPackGroups];
+  int ev[kPackGroups];
 #pragma unroll
-  for (int j = 0; j < kPrepRegBlocks; ++j) {
-    const int b = lane + 64 * j;
-    if (b < nb) {
-      const int g = b >> 3, kb = b & 7;
-      x16[x16_index(tb, g, G, kb & 3, kb >> 2, i)] = to_f16_pairs(v[j], e);
-    }
+  for (int j = 0; j < kPackGroups; ++j) {
+    const int u = j * 256 + tid;
+    const int kb = u & 7, ilo = (u >> 3) & 7, gl = (u >> 6) & 7, ihi = u >> 9;
+    const int t = min(tb * 32 + ihi * 8 + ilo, T - 1), g = min(g0 + gl, G - 1);
+    v[j] = x[(size_t)t * nb + g * 8 + kb];
+    ev[j] = texp[t];
   }
-  for (int b = lane + 64 * kPrepRegBlocks; b < nb; b += 64) {
-    const int g = b >> 3, kb = b & 7;
-    x16[x16_index(tb, g, G, kb & 3, kb >> 2, i)] = to_f16_pairs(xt[b], e);
+#pragma unroll
+  for (int j = 0; j < kPackGroups; ++j) {
+    const int u = j * 256 + tid;
+    const int kb = u & 7, ilo = (u >> 3) & 7, gl = (u >> 6) & 7, ihi = u >> 9;
+    const int i = ihi * 8 + ilo;
+    const bool ok = tb * 32 + i < T && g0 + gl < G;
+    tile[gl * 256 + ((kb & 3) * 2 + (kb >> 2)) * 32 + i] = ok ? to_f16_pairs(v[j], ev[j]) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  const int ng = min(kPackGroups, G - g0);
+  u32x4_t* dst = x16 + ((size_t)tb * G + g0) * 256;
+#pragma unroll
+  for (int j = 0; j < kPackGroups; ++j) {
+    const int u = j * 256 + tid;
+    if ((u >> 8) < ng) dst[u] = tile[u];
   }
 }
 
@@ -141,13 +161,24 @@ __device__ __forceinline__ u32x4_t dequant_dword(uint32_t w) {
   return r;
 }
 
-// Direct-to-LDS loads: every lane of the wave sends `bytes` bytes from its own
-// global address to lds_base + lane * bytes (lds_base is wave-uniform).
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+// Direct-to-LDS buffer loads: every lane of the wave sends BYTES bytes from
+// base + voffset + soffset (voffset per lane, soffset wave-uniform) to
+// lds_base + lane * BYTES (lds_base wave-uniform).  Reads at or past the
+// resource's byte count return zeros.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+// raw (unformatted, stride 0) buffer over [base, base + bytes)
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_base, 4, 0, 0);
+
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voffset, uint32_t soffset, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, voffset,
+                                           soffset, 0, 0);
+}
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voffset, uint32_t soffset, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voffset,
+                                           soffset, 0, 0);
 }
 
 // s_waitcnt encoding for gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 =
@@ -159,37 +190,78 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
 }
 
-// Byte offset of 16-byte piece `pi` (0..7) of row r in a dequantized weight
-// tile: 128 bytes per row, pieces permuted per row so that the matrix-core
-// operand reads (32 rows, one piece each) and the dequantizer's writes hit
-// distinct LDS banks.
-__device__ __forceinline__ int wpiece(int r, int pi) { return r * 128 + ((pi ^ ((r ^ (r >> 3)) & 7)) << 4); }
+// 16-byte LDS read into accumulation registers (AGPRs), which the matrix
+// cores read as operands directly: a wave's next-group operands wait there
+// while its current ones (in the other AGPR set) are in use, without taking
+// ordinary VGPRs.  The compiler does not track this load: the caller waits
+// (s_waitcnt lgkmcnt) before the registers are read.
+template <int OFF>
+__device__ __forceinline__ void lds_read_agpr(f16x8_t& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=a"(v) : "v"(addr), "i"(OFF));
+}
 
-// Ring geometry: the activation ring has DX slots and is filled DX groups
-// ahead; the code/scale ring has DX slots and is filled DX+1 groups ahead
-// (a group's codes are dequantized two groups before its products).
-constexpr int DX = 4;
-constexpr int DC = DX + 1;
+// A dequantized weight tile holds 144 bytes per row: the row's 64 float16
+// values (eight 16-byte pieces) and 16 bytes of padding, which spreads the
+// matrix-core operand reads (32 rows, one piece each) over distinct banks.
+constexpr int kRowBytes = 144;
+
+// 16-byte buffer load into accumulation registers (AGPRs): the activation
+// fragments go straight from memory (L2) to the registers the matrix cores
+// read.  The compiler does not track this load either: the caller waits
+// (s_waitcnt vmcnt) before the registers are read.
+template <int OFF>
+__device__ __forceinline__ void buf_read_agpr(f16x8_t& v, u32x4_t rsrc, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4" : "=a"(v) : "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF));
+}
+
+// Buffer resource for the raw (stride 0) byte range [base, base + bytes),
+// built in scalar registers for the inline loads above.
+__device__ __forceinline__ u32x4_t make_rsrc_sgpr(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) & 0xFFFFu,
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+}
+
+template <int V>
+using Slot = std::integral_constant<int, V>;
+
+// Calls f(Slot<0>{}) ... f(Slot<N-1>{}).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Slot<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Ring geometry.  Codes and scales stream through an LDS ring of DS slots,
+// loaded DS+1 groups ahead (a group's codes are dequantized two groups
+// before its products); each wave's activation fragments stream through a
+// ring of DS register sets, loaded DS-1 groups ahead.
+constexpr int DS = 4;
+constexpr int DCODE = DS + 1;
+constexpr int DACT = DS - 1;
 
 template <int NS, int TS, int WN, int WT>
 struct TiledShape {
   static constexpr int NT = 64 * WN * WT;                 // threads
   static constexpr int BN = 32 * NS * WN;                 // rows per workgroup
   static constexpr int BT = 32 * TS * WT;                 // tokens per workgroup
-  static constexpr int CI = (2 * BN + NT - 1) / NT;       // code (and scale) loads per thread per batch
-  static constexpr int XI = BT * 8 / NT;                  // activation loads per thread per batch
-  static constexpr int L = 2 * CI + XI;                   // loads per thread per batch
-  static constexpr int CODE_B = CI * NT * 16;             // one code slot
-  static constexpr int SCALE_B = CI * NT * 4;             // one scale slot
-  static constexpr int X_B = BT * 128;                    // one activation slot
-  static constexpr int W_B = BN * 128;                    // one dequantized weight tile
-  static constexpr int OFF_C = DX * X_B;
-  static constexpr int OFF_S = OFF_C + DX * CODE_B;
-  static constexpr int OFF_W = OFF_S + DX * SCALE_B;
+  static constexpr int CD = BN * 8 / NT;                  // code dwords per thread per group
+  static constexpr int AI = TS * 4;                       // 16-byte activation loads per lane per group
+  static constexpr int L = CD + 1 + AI;                   // loads per thread per batch (one scale)
+  static constexpr int CODE_B = BN * 32;                  // one code slot
+  static constexpr int SCALE_B = NT * 4;                  // one scale slot (one dword per thread)
+  static constexpr int W_B = BN * kRowBytes;              // one dequantized weight tile
+  static constexpr int OFF_S = DS * CODE_B;
+  static constexpr int OFF_W = OFF_S + DS * SCALE_B;
   static constexpr int OFF_SB = OFF_W + 2 * W_B;
-  static constexpr int LDS_B = OFF_SB + 2 * BN * 4;
-  static_assert(BT * 8 % NT == 0, "activation tile must split evenly over the threads");
+  static constexpr int LDS_B = (OFF_SB + 2 * BN * 4 > BT * BN * 2) ? OFF_SB + 2 * BN * 4 : BT * BN * 2;
+  static_assert(BN * 8 % NT == 0, "code tiles must split evenly over the threads");
+  static_assert(NT >= BN, "one scale per row needs a thread per row");
   static_assert(LDS_B <= 160 * 1024, "LDS budget");
+  static_assert((DS - 2) * L <= 63, "the load counter holds 63");
 };
 
 template <int NS, int TS, int WN, int WT>
@@ -198,13 +270,13 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
              const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
              uint16_t* __restrict__ y, int N, int K, int T, int Tpad, int tiles_n, int tiles_t) {
   using Sh = TiledShape<NS, TS, WN, WT>;
-  constexpr int NT = Sh::NT, BN = Sh::BN, BT = Sh::BT, CI = Sh::CI, XI = Sh::XI, L = Sh::L;
+  constexpr int NT = Sh::NT, BN = Sh::BN, BT = Sh::BT, CD = Sh::CD, L = Sh::L;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  float* sbuf = reinterpret_cast<float*>(lds + Sh::OFF_SB);       // 2 x BN scales
 
   const int G = K >> 6;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int li = lane & 31, lh = lane >> 5;
   const int wn = wave % WN, wt = wave / WN;
 
@@ -219,79 +291,104 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
   const int tb0 = tile_t * (BT / 32);                 // first 32-token block
   const int tb_last = Tpad / 32 - 1;
 
-  // --- loads: codes and scales of group gc, activations of group gx --------
-  // Every thread issues exactly L loads per call; indexes are clamped to valid
-  // data, so the batches near the end simply repeat the last group.
-  auto issue = [&](int gc, int gx, bool with_x) __device__ {
+  // --- per-thread load offsets (32-bit, relative to per-group uniform offsets
+  // into buffers that start at the tile) ---------------------------------------
+  // Code dword task j = c*NT + tid: row j/8 of the tile, dword j%8 of the
+  // row's 32 bytes; rows past N repeat row N-1 (their outputs are dropped).
+  const uint8_t* codes_tile = codes + (size_t)n0 * (K >> 1);
+  const rsrc_t rc = make_rsrc(codes_tile, (uint32_t)min((int64_t)(N - n0) * (K >> 1), (int64_t)0x7FFFFFFF));
+  uint32_t coff[CD];
+#pragma unroll
+  for (int c = 0; c < CD; ++c) {
+    const int j = c * NT + tid;
+    coff[c] = (uint32_t)(min(j >> 3, N - 1 - n0) * (K >> 1) + (j & 7) * 4);
+  }
+  // Scale of row tid % BN: the naturally aligned dword around it (which never
+  // leaves the scale's page); the other half is ignored.  The buffer starts at
+  // the aligned dword below the tile's first scale; soff0 / soff1 are the
+  // lane's offsets for even / odd groups, to which 4 * (g / 2) is added.
+  const uintptr_t s_first = reinterpret_cast<uintptr_t>(scales + (size_t)n0 * G);
+  const uintptr_t s_base = s_first & ~(uintptr_t)3;
+  const rsrc_t rs = make_rsrc(reinterpret_cast<const void*>(s_base),
+                              (uint32_t)min((int64_t)(N - n0) * G * 2 + 4, (int64_t)0x7FFFFFFF));
+  const uint32_t s_lane = (uint32_t)(s_first - s_base) + (uint32_t)(min(tid % BN, N - 1 - n0) * G * 2);
+  const uint32_t soff0 = s_lane & ~3u, soff1 = (s_lane + 2) & ~3u;
+  const int s_row = tid % BN;
+  const bool s_odd_lane = (s_lane & 2) != 0;           // even groups sit in the high half
+  // Activation fragment (ts, m) of lane (li, lh): 16 bytes of token block
+  // tb0 + wt*TS + ts, group g, at ((m*2 + lh)*32 + li)*16 of its 4 KB block.
+  const uint8_t* x16_tile = reinterpret_cast<const uint8_t*>(x16) + (size_t)tb0 * G * 4096;
+  const u32x4_t rx = make_rsrc_sgpr(x16_tile, (uint32_t)min((int64_t)(tb_last + 1 - tb0) * G * 4096, (int64_t)0x7FFFFFFF));
+  uint32_t aoff[TS];
+#pragma unroll
+  for (int ts = 0; ts < TS; ++ts)
+    aoff[ts] = (uint32_t)(min(wt * TS + ts, tb_last - tb0) * G * 4096 + (lh * 32 + li) * 16);
+
+  // --- the matrix-core operand registers --------------------------------------
+  // Activations: DS sets, set g % DS holds group g.  Weights: two sets, set
+  // g & 1 holds group g.  All in AGPRs, filled by untracked loads.
+  f16x8_t act[DS][TS][4];
+  f16x8_t wgt[2][NS][4];
+  float scl[2][NS];
+
+  // --- one batch: codes and scales of group gc into code slot gc % DS, and
+  // this wave's activation fragments of group ga into set A (indexes clamped
+  // to the last group, so every batch has the same number of loads) --------
+  auto issue_codes = [&](int gc) __device__ {
     gc = min(gc, G - 1);
-    gx = min(gx, G - 1);
-    uint8_t* cs = lds + Sh::OFF_C + (gc % DX) * Sh::CODE_B;
-    uint8_t* ss = lds + Sh::OFF_S + (gc % DX) * Sh::SCALE_B;
-    uint8_t* xs = lds + (gx % DX) * Sh::X_B;
+    const int cs = gc % DS;
 #pragma unroll
-    for (int c = 0; c < CI; ++c) {
-      const int task = (c * NT + tid) % (2 * BN);     // tasks past 2*BN repeat valid ones
-      const int row = min(n0 + (task >> 1), N - 1);
-      dma16(codes + (size_t)row * (K >> 1) + (size_t)gc * 32 + (task & 1) * 16, cs + c * NT * 16 + wave * 1024);
-    }
-#pragma unroll
-    for (int c = 0; c < CI; ++c) {
-      const int task = (c * NT + tid) % (2 * BN);
-      const int row = min(n0 + (task >> 1), N - 1);
-      // The scale's naturally aligned dword: it never leaves the scale's own
-      // page, and the other half is ignored.
-      const uintptr_t sa = reinterpret_cast<uintptr_t>(scales + (size_t)row * G + gc) & ~(uintptr_t)3;
-      dma4(reinterpret_cast<const void*>(sa), ss + c * NT * 4 + wave * 256);
-    }
-    if (!with_x) return;
-#pragma unroll
-    for (int j = 0; j < XI; ++j) {
-      const int off = (j * NT + tid) * 16;             // byte offset inside the BT x 128 B slot
-      const int tb = min(tb0 + (off >> 12), tb_last);  // 4 KB per 32-token block
-      const uint8_t* src = reinterpret_cast<const uint8_t*>(x16) + (((size_t)tb * G + gx) << 12) + (off & 4095);
-      dma16(src, xs + j * NT * 16 + wave * 1024);
-    }
+    for (int c = 0; c < CD; ++c)
+      dma4(rc, coff[c], (uint32_t)gc * 32, lds + cs * Sh::CODE_B + c * NT * 4 + wave * 256);
+    dma4(rs, (gc & 1) ? soff1 : soff0, (uint32_t)(gc >> 1) * 4, lds + Sh::OFF_S + cs * Sh::SCALE_B + wave * 256);
+  };
+  auto issue_act = [&](int ga, f16x8_t (&a)[TS][4]) __device__ {
+    const uint32_t so = (uint32_t)min(ga, G - 1) * 4096;
+    static_for<TS * 4>([&](auto i) {
+      constexpr int ts = decltype(i)::value / 4, m = decltype(i)::value % 4;
+      buf_read_agpr<m * 1024>(a[ts][m], rx, aoff[ts], so);
+    });
   };
 
-  // --- dequantize this thread's own code pieces of group g into tile b -----
-  auto dequant = [&](int g, int b) __device__ {
-    const uint8_t* cs = lds + Sh::OFF_C + (g % DX) * Sh::CODE_B;
-    const uint8_t* ss = lds + Sh::OFF_S + (g % DX) * Sh::SCALE_B;
-    uint8_t* wb = lds + Sh::OFF_W + b * Sh::W_B;
+  // --- dequantization of group g into weight tile b, in two halves: the LDS
+  // reads of this thread's own code dwords and scale dword (dq_load), and the
+  // conversion and LDS writes (dq_store) -------------------------------------
+  const int dq_off = (tid >> 3) * kRowBytes + (tid & 7) * 16;   // + c*(NT/8)*kRowBytes
+  struct DqRegs {
+    uint32_t w[CD];
+    uint32_t sw;
+  };
+  auto dq_load = [&](int g, DqRegs& d) __device__ {
+    const uint8_t* cs = lds + (g % DS) * Sh::CODE_B + tid * 4;
 #pragma unroll
-    for (int c = 0; c < CI; ++c) {
-      const int task = c * NT + tid;
-      if (task < 2 * BN) {
-        const int r = task >> 1, hh = task & 1;
-        const u32x4_t cw = *reinterpret_cast<const u32x4_t*>(cs + c * NT * 16 + tid * 16);
+    for (int c = 0; c < CD; ++c) d.w[c] = *reinterpret_cast<const uint32_t*>(cs + c * NT * 4);
+    d.sw = *reinterpret_cast<const uint32_t*>(lds + Sh::OFF_S + (g % DS) * Sh::SCALE_B + tid * 4);
+  };
+  auto dq_store = [&](int g, int b, const DqRegs& d) __device__ {
+    uint8_t* wb = lds + Sh::OFF_W + b * Sh::W_B + dq_off;
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
-          *reinterpret_cast<u32x4_t*>(wb + wpiece(r, hh * 4 + d)) = dequant_dword(cw[d]);
-        if (hh == 0) {
-          const uint32_t sw = *reinterpret_cast<const uint32_t*>(ss + c * NT * 4 + tid * 4);
-          const int row = min(n0 + r, N - 1);
-          const bool hi = (reinterpret_cast<uintptr_t>(scales + (size_t)row * G + g) & 2) != 0;
-          sbuf[b * BN + r] = f16_bits_to_f32((uint16_t)(hi ? (sw >> 16) : (sw & 0xFFFFu)));
-        }
-      }
-    }
+    for (int c = 0; c < CD; ++c) *reinterpret_cast<u32x4_t*>(wb + c * (NT / 8) * kRowBytes) = dequant_dword(d.w[c]);
+    // Every thread converts the scale it loaded (row tid % BN); threads past
+    // BN write the same value as thread tid % BN, so no branch is needed.
+    const bool hi = s_odd_lane != ((g & 1) != 0);
+    reinterpret_cast<float*>(lds + Sh::OFF_SB)[b * BN + s_row] =
+        f16_bits_to_f32((uint16_t)(hi ? (d.sw >> 16) : (d.sw & 0xFFFFu)));
   };
 
-  // --- matrix-core operands of group g (activation slot, weight tile g & 1) -
-  auto read_a = [&](int g, f16x8_t (&a)[TS][4]) __device__ {
-    const uint8_t* xs = lds + (g % DX) * Sh::X_B;
+  // --- weight fragments and scales of group g (tile g & 1) --------------------
+  const int b_row = wn * NS * 32 + li;                                  // + ns*32
+  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+  auto read_wgt = [&](int g, f16x8_t (&b)[NS][4], float (&sc)[NS]) __device__ {
+    const uint32_t wb = lds_base + (uint32_t)(Sh::OFF_W + (g & 1) * Sh::W_B + b_row * kRowBytes + lh * 64);
+    static_for<NS * 4>([&](auto i) {
+      constexpr int ns = decltype(i)::value / 4, m = decltype(i)::value % 4;
+      lds_read_agpr<ns * 32 * kRowBytes + m * 16>(b[ns][m], wb);
+    });
 #pragma unroll
-    for (int ts = 0; ts < TS; ++ts)
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        a[ts][m] = *reinterpret_cast<const f16x8_t*>(xs + ((wt * TS + ts) << 12) + (((m * 2 + lh) * 32 + li) << 4));
-  };
-  auto read_b = [&](int g, int ns, f16x8_t (&b)[4], float& sc) __device__ {
-    const uint8_t* wb = lds + Sh::OFF_W + (g & 1) * Sh::W_B;
-    const int r = (wn * NS + ns) * 32 + li;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) b[m] = *reinterpret_cast<const f16x8_t*>(wb + wpiece(r, lh * 4 + m));
-    sc = sbuf[(g & 1) * BN + r];
+    for (int ns = 0; ns < NS; ++ns) {
+      const float v = reinterpret_cast<const float*>(lds + Sh::OFF_SB)[(g & 1) * BN + b_row + ns * 32];
+      sc[ns] = g < G ? v : 0.0f;  // groups past the end count zero
+    }
   };
 
   f32x16_t acc[TS][NS];
@@ -301,99 +398,152 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[ts][ns][r] = 0.0f;
-  // Operands of the group in flight: activation and weight fragments are
-  // each refilled with the next group's as soon as the last product that
-  // reads them has been issued.
-  f16x8_t aop[TS][4];
-  f16x8_t bop[NS][4];
-  float sc[NS], sn[NS];
 
-  // Step g: wait for the batch that carried group g+1's activations and group
-  // g+2's codes (issued three steps earlier), publish with a barrier, issue
-  // the next batch, run group g's products, refill the operands with group
-  // g+1's, and dequantize group g+2 in between.
-  auto step = [&](int g) __device__ {
+  // Before every barrier: this thread's batch from three steps back (it
+  // carried group g's activations and group g+2's codes) has landed, and its
+  // LDS reads and writes (also the untracked weight reads) are done.
+  auto sync = [&]() __device__ {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<(DX - 2) * L>();
+    wait_vm<(DS - 2) * L>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(g + DC, g + DX, true);
+  };
+
+  // Step g (SL = g % DS).  The products p hold group g-1's on entry: each
+  // chain's product is scaled into the accumulators (scales sp) just before
+  // the chain's first matrix-core instruction of group g overwrites it.  After
+  // the barrier: read the code dwords of group g+2 (their LDS latency then
+  // hides behind the matrix cores), issue the batch (codes of g+DCODE,
+  // activations of g+DACT), issue group g+1's weight reads, then the
+  // matrix-core instructions interleaved with the scaling and the
+  // dequantization of group g+2.  Past the last group the reads and the
+  // dequantization touch stale LDS (unused) and the loads repeat the last
+  // group, so the step is one basic block.
+  f32x16_t p[TS][NS];
+  float sp[NS];
+  auto step = [&](int g, auto slot) __device__ {
+    constexpr int SL = decltype(slot)::value;
+    sync();
+    DqRegs d;
+    dq_load(g + 2, d);
+    issue_codes(g + DCODE);
+    issue_act(g + DACT, act[(SL + DACT) % DS]);
+    read_wgt(g + 1, wgt[(SL + 1) & 1], scl[(SL + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
-    const bool more = g + 1 < G;
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      f32x16_t p[TS];
-#pragma unroll
-      for (int ts = 0; ts < TS; ++ts) {
-        p[ts] = f32x16_t{};
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          p[ts] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop[ts][m], bop[ns][m], p[ts], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) {
-        read_b(g + 1, ns, bop[ns], sn[ns]);
-        if (ns == NS - 1) read_a(g + 1, aop);
-      }
-      if (ns == 0 && g + 2 < G) dequant(g + 2, g & 1);
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[ts][ns][r] = __builtin_fmaf(sc[ns], p[ts][r], acc[ts][ns][r]);
-    }
+        for (int ns = 0; ns < NS; ++ns) {
+          if (m == 0) {
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) sc[ns] = sn[ns];
+            for (int r = 0; r < 16; ++r) acc[ts][ns][r] = __builtin_fmaf(sp[ns], p[ts][ns][r], acc[ts][ns][r]);
+            p[ts][ns] = f32x16_t{};
+          }
+          p[ts][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(act[SL][ts][m], wgt[SL & 1][ns][m], p[ts][ns], 0, 0, 0);
+        }
+    dq_store(g + 2, g & 1, d);
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) sp[ns] = scl[SL & 1][ns];
+    // one matrix-core instruction, then a share of the VALU work
+#pragma unroll
+    for (int i = 0; i < 4 * TS * NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+    }
   };
 
-  // Prologue: groups 0..DX-1 loaded, groups 0 and 1 dequantized, then the
-  // codes of group DX (whose slot group 0 used) in flight, and group 0's
-  // operands read.  Step 2 waits for those codes behind two full batches.
-  for (int j = 0; j < DX; ++j) issue(j, j, true);
+  // Prologue: codes of groups 0..DS-1 and activations of groups 0..DACT-1 in
+  // flight, then all landed; groups 0 and 1 dequantized; the codes of group
+  // DS (into the slot group 0 used) in flight; group 0's weights read.
+  static_assert(DS == 4, "the prologue and the step unrolling assume four slots");
+  issue_codes(0);
+  issue_codes(1);
+  issue_codes(2);
+  issue_codes(3);
+  issue_act(0, act[0]);
+  issue_act(1, act[1]);
+  issue_act(2, act[2]);
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();
   __builtin_amdgcn_sched_barrier(0);
-  dequant(0, 0);
-  if (G > 1) dequant(1, 1);
+  {
+    DqRegs d;
+    dq_load(0, d);
+    dq_store(0, 0, d);
+    dq_load(1, d);
+    dq_store(1, 1, d);
+  }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  issue(DX, 0, false);
+  issue_codes(DS);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_a(0, aop);
+  read_wgt(0, wgt[0], scl[0]);
+  // The first step scales an all-zero "group -1".
 #pragma unroll
-  for (int ns = 0; ns < NS; ++ns) read_b(0, ns, bop[ns], sc[ns]);
-  for (int g = 0; g < G; ++g) step(g);
+  for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) p[ts][ns] = f32x16_t{};
+#pragma unroll
+  for (int ns = 0; ns < NS; ++ns) sp[ns] = 0.0f;
+  // Steps run in fours (the register sets cycle with period four); up to
+  // three steps past the last group run on clamped, finite data with zero
+  // scales and so add exactly nothing.  (A tail of conditional steps would
+  // keep extra copies of the operand registers live.)
+  for (int g = 0; g < G; g += DS) {
+    step(g, Slot<0>{});
+    step(g + 1, Slot<1>{});
+    step(g + 2, Slot<2>{});
+    step(g + 3, Slot<3>{});
+  }
+  // the last group's products
+#pragma unroll
+  for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[ts][ns][r] = __builtin_fmaf(sp[ns], p[ts][ns][r], acc[ts][ns][r]);
+  // no load may still write this workgroup's LDS or registers after this
+  wait_vm<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
   // Epilogue: lane (li, lh) holds row n = n0 + 32 (wn*NS + ns) + li and tokens
-  // t = 32 (tb0 + wt*TS + ts) + 8 (r / 4) + 4 lh + r % 4.
-  // The exponents are loaded up front (texp has Tpad entries), so that the
-  // loads overlap instead of each waiting behind the previous store.
+  // t = 32 (tb0 + wt*TS + ts) + 8 (r / 4) + 4 lh + r % 4.  The bf16 results
+  // go through LDS ([token][row] order), so that the stores to y are whole
+  // 16-byte pieces of token rows.
+  static_assert(BT * BN * 2 <= Sh::LDS_B, "output tile must fit the LDS");
+  __syncthreads();
+  uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
   for (int ts = 0; ts < TS; ++ts) {
-    const int tbase = 32 * (tb0 + wt * TS + ts) + 4 * lh;
+    const int tl = (wt * TS + ts) * 32 + 4 * lh;
     int e[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = texp[min(tbase + 8 * (r >> 2) + (r & 3), Tpad - 1)];
-    // Scale every value before the first (masked) store: the empty asm pins
-    // the results here, so the stores below wait for no load.
+    for (int r = 0; r < 16; ++r) e[r] = texp[min(32 * tb0 + tl + 8 * (r >> 2) + (r & 3), Tpad - 1)];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) {
-        acc[ts][ns][r] = __builtin_ldexpf(acc[ts][ns][r], e[r]);
-        asm volatile("" : "+v"(acc[ts][ns][r]));
-      }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = tbase + 8 * (r >> 2) + (r & 3);
-      if (t < T) {
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-          const int n = n0 + 32 * (wn * NS + ns) + li;
-          if (n < N) y[(size_t)t * N + n] = f32_to_bf16_rne(acc[ts][ns][r]);
-        }
-      }
+      for (int ns = 0; ns < NS; ++ns)
+        otile[(tl + 8 * (r >> 2) + (r & 3)) * BN + (wn * NS + ns) * 32 + li] =
+            f32_to_bf16_rne(__builtin_ldexpf(acc[ts][ns][r], e[r]));
+  }
+  __syncthreads();
+  const int t0 = 32 * tb0;
+  if ((reinterpret_cast<uintptr_t>(y) & 15) == 0 && (N & 7) == 0 && n0 + BN <= N) {
+    constexpr int CPR = BN / 8;  // 16-byte pieces per token row of the tile
+    for (int c = tid; c < BT * CPR; c += NT) {
+      const int tl = c / CPR, cn = c - tl * CPR;
+      if (t0 + tl < T)
+        *reinterpret_cast<u32x4_t*>(y + (size_t)(t0 + tl) * N + n0 + cn * 8) =
+            *reinterpret_cast<const u32x4_t*>(otile + tl * BN + cn * 8);
+    }
+  } else {
+    for (int c = tid; c < BT * BN; c += NT) {
+      const int tl = c / BN, nl = c - tl * BN;
+      if (t0 + tl < T && n0 + nl < N) y[(size_t)(t0 + tl) * N + n0 + nl] = otile[c];
     }
   }
 }
@@ -427,7 +577,7 @@ size_t tiled_workspace_bytes(int64_t k, int64_t t) {
 TiledConfig tiled_pick_config(int64_t n, int64_t k, int64_t t) {
   (void)k;
   // 192 x 128 tiles where they fill the chip, else narrower token tiles
-  if (t > 96 && (n / 192) * ((t + 127) / 128) >= 192) return TiledConfig{3, 1, 2, 4};
+  if (t > 96 && (n / 192) * ((t + 127) / 128) >= 192) return TiledConfig{3, 2, 2, 2};
   if (t > 32) return TiledConfig{1, 1, 1, 4};
   return TiledConfig{1, 1, 1, 1};
 }
@@ -439,15 +589,16 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   {
     const u32x4_t* x = static_cast<const u32x4_t*>(a.x);
     int k = (int)a.k, t = (int)a.t, tpad = (int)tp;
-    void* args[] = {&x, &k, &t, &tpad, &x16, &texp};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(prep_x_kernel),
-                                   dim3((unsigned)((tp + kPrepWaves - 1) / kPrepWaves)), dim3(64 * kPrepWaves),
-                                   args, 0, stream);
+    prep_exp_kernel<<<dim3((unsigned)((tp + kExpWaves - 1) / kExpWaves)), dim3(64 * kExpWaves), 0, stream>>>(x, k, t, tpad,
+                                                                                                          texp);
+    prep_pack_kernel<<<dim3((unsigned)(tp / 32), (unsigned)((a.k / 64 + kPackGroups - 1) / kPackGroups)), dim3(256), 0,
+                       stream>>>(x, k, t, texp, x16);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int tpad = (int)tp;
   const TiledConfig c = a.cfg;
-  if (c.ns == 3 && c.ts == 1 && c.wn == 2 && c.wt == 4) return launch_cfg<3, 1, 2, 4>(a, x16, texp, tpad, stream);
+  if (c.ns == 3 && c.ts == 2 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 2, 2, 2>(a, x16, texp, tpad, stream);
   if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 4) return launch_cfg<1, 1, 1, 4>(a, x16, texp, tpad, stream);
   if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 1) return launch_cfg<1, 1, 1, 1>(a, x16, texp, tpad, stream);
   return hipErrorInvalidValue;
