@@ -169,22 +169,78 @@ def cpu_baseline_t1(n, k, seed, budget_s=10.0):
             "sample": "%d full %dx%d T=1 problems, median %.1f ms each" % (len(times), n, k, med * 1e3)}
 
 
-def cpu_baseline_rows(n, k, t, seed, rows=48):
-    """The oracle on `rows` output rows of an N x K x T problem, scaled to the
-    whole problem; returns effective TFLOP/s."""
+def cpu_baseline_rows(n, k, t, seed, budget_s=10.0):
+    """The oracle on whole output rows of an N x K x T problem (all T tokens),
+    as many rows as fit in about `budget_s` seconds, scaled to the whole
+    problem; returns effective TFLOP/s."""
     import oracle
     from weight_only_bit_q4_amd import inputs
     x, c, s = inputs.gen_problem(n, k, t, seed)
     o = oracle.default()
-    ns = np.repeat(np.arange(rows), t)
-    ts = np.tile(np.arange(t), rows)
-    t0 = time.perf_counter()
-    o.linear_at(x, c, s, n, k, t, ns, ts)
-    el = time.perf_counter() - t0
+
+    def run(rows):
+        ns = np.repeat(np.arange(rows), t)
+        ts = np.tile(np.arange(t), rows)
+        t0 = time.perf_counter()
+        o.linear_at(x, c, s, n, k, t, ns, ts)
+        return time.perf_counter() - t0
+
+    probe_rows = 16
+    el = run(probe_rows)
+    rows = int(min(n, max(probe_rows, probe_rows * budget_s / max(el, 1e-6))))
+    el = run(rows)
     full = el * n / rows
     return {"value": round(tflops(n, k, t, full), 6), "unit": "TFLOP/s", "cores": o.max_threads(),
             "kind": "oracle",
             "sample": "%d of %d output rows of %dx%d T=%d (%.1f s), scaled to all rows" % (rows, n, n, k, t, el)}
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from the committed counter summaries
+# ---------------------------------------------------------------------------
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = {
+    "gemv": "weight_only_bit_q4_amd/csrc/q4lin_gemv.hip",
+    "tiled": "weight_only_bit_q4_amd/csrc/q4lin_tiled.hip",
+}
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from profiles/traffic.txt
+    (FETCH_SIZE + WRITE_SIZE, each scaled by its copy-kernel factor), or None
+    when there is no entry or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        f = dict(kv.split("=", 1) for kv in line.split())
+        if f.get("kernel") == kernel and f.get("workload") == workload:
+            if f.get("source_sha256_16") != source_digest(kernel):
+                return None
+            return int(float(f["hbm_bytes_per_launch"]))
+    return None
+
+
+def copy_calibration(nbytes: int, reps: int = 5):
+    """A plain device copy of `nbytes` (torch's copy kernel), for scaling the
+    FETCH_SIZE / WRITE_SIZE counters: run under rocprofv3 --pmc."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": True, "bytes": nbytes, "reps": reps}))
 
 
 def main(argv=None):
@@ -200,6 +256,8 @@ def main(argv=None):
     ap.add_argument("--profile", action="store_true", help="one call after set-up, then exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--csv", type=str, default=None)
+    ap.add_argument("--copy-calibration", type=int, default=None, metavar="BYTES",
+                    help="run a plain copy of BYTES bytes (for scaling the byte counters), then exit")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -214,6 +272,10 @@ def main(argv=None):
         return 2
     n, k = args.n, args.k
     seed = inputs.workload_seed("decode_6144x5120_t1")
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
 
     if args.profile:
         t = args.t or 1
@@ -288,17 +350,23 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16-products/f32-accumulate (bf16 in/out)",
+        "dtype": "f16 (f32 accumulate; bf16 in/out)",
         "data": "synthetic",
         "config": {"workload": "decode_6144x5120_t1", "n": n, "k": k, "t": 1,
                    "weight_format": "Q4_G64_FP16", "cache": "cold (rotating %d buffer sets)" % 0},
+        # dominant kernel: the few-token kernel is the whole call at T=1; its
+        # algorithmic bytes per launch are model_bytes (W, X and Y once each)
         "roofline": {"bound": "hbm", "achieved": round(v1, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(v1 / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(v1 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles("gemv", "decode_6144x5120_t1"),
+                     "algorithmic_bytes": model_bytes(n, k, 1)},
         "prefill_t1024": {
             "metric": "eff. TFLOP/s @T=1024", "value": round(v2, 2), "unit": "TFLOP/s",
             "steps": steps2, "ms_per_step": round(s2 * 1e3, 6),
             "roofline": {"bound": "mfma", "achieved": round(v2, 2), "peak": MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(v2 / MFMA_PEAK_TFLOPS, 4), "traffic": None},
+                         "unit": "TFLOP/s", "frac": round(v2 / MFMA_PEAK_TFLOPS, 4),
+                         "traffic": traffic_from_profiles("tiled", "prefill_6144x5120_t1024"),
+                         "algorithmic_flops": useful_flops(n, k, 1024)},
         },
     }
     line["config"]["cache"] = "cold (rotating buffer sets, >= 1 GiB between reuses)"
