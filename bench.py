@@ -16,8 +16,11 @@ the 4 MB per-XCD L2s or the 256 MB Infinity Cache.  The K timed calls are
 captured in one HIP graph (host launch cost would otherwise exceed a ~3 us
 kernel) and bracketed by HIP events on the graph's stream, with a device
 synchronize on both sides; ms_per_step = elapsed / K.  Each step is one
-complete public call (for T = 1024 that is the activation-preparation kernel
-plus the tiled kernel).
+complete public call (for T = 1024 that is the activation-preparation kernels
+plus the tiled kernel).  Next to it the pages' own single-call contract
+("linear-benchmark.md" section 6: flush, then events around exactly one call;
+median, min and p95) is reported as ``single_call_cold``; on this platform an
+event pair around one launch adds a few microseconds of its own.
 
 Other modes: ``--sweep 1:128`` (per-T table with step change between
 adjacent T), ``--n/--k/--t`` single points, ``--profile`` (one call after
@@ -38,6 +41,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix, published
 ROTATE_BYTES = 1 << 30         # traffic between two uses of one buffer set
+FLUSH_BYTES = 1 << 30          # cache flush before every cold sample (L2s + 256 MB Infinity Cache)
 
 METRIC = "Q4 6144x5120: logical GB/s @T=1, eff. TFLOP/s @T=1024 (% of roofline)"
 
@@ -77,16 +81,16 @@ def roof_fraction(n, k, t, seconds, hbm_gbs=HBM_PEAK_GBS, mfma_tflops=MFMA_PEAK_
 class Point:
     """Rotating buffer sets for one (N, K, T) and a graph of `steps` calls."""
 
-    def __init__(self, n, k, t, seed):
+    def __init__(self, n, k, t, seed, rotate=True, data=None):
         import torch
         import weight_only_bit_q4_amd as q4
         from weight_only_bit_q4_amd import inputs
         self.n, self.k, self.t = n, k, t
         self.q4 = q4
         self.torch = torch
-        x, codes, scales = inputs.gen_problem(n, k, t, seed)
+        x, codes, scales = data if data is not None else inputs.gen_problem(n, k, t, seed)
         per_set = model_bytes(n, k, t) + max(q4.q4lin_workspace_bytes(n, k, t), 0)
-        self.nsets = max(2, int(math.ceil(ROTATE_BYTES / per_set)) + 1)
+        self.nsets = max(2, int(math.ceil(ROTATE_BYTES / per_set)) + 1) if rotate else 1
         dev = torch.device("cuda")
         xd = torch.from_numpy(x.view(np.int16).copy()).to(dev)
         cd = torch.from_numpy(codes).to(dev)
@@ -144,8 +148,35 @@ class Point:
                 out.append(start.elapsed_time(end) / 1e3 / steps)
         return out
 
+    def time_cold(self, samples, warmup, flush_bytes=FLUSH_BYTES):
+        """Per-call latencies with cold caches: before every sample a plain
+        copy between two flush_bytes/2 buffers evicts the per-XCD L2s and the
+        Infinity Cache; then one call, bracketed by HIP events recorded on the
+        call's stream.  Returns the `samples` timed latencies (seconds); the
+        first `warmup` samples are discarded."""
+        torch = self.torch
+        if not hasattr(self, "_flush"):
+            half = flush_bytes // 2
+            self._flush = (torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1),
+                           torch.empty(half, dtype=torch.uint8, device="cuda"))
+        fa, fb = self._flush
+        total = warmup + samples
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            h = self.stream.cuda_stream
+            for i in range(total):
+                fb.copy_(fa)
+                ev[i][0].record(self.stream)
+                self.call(0, h)
+                ev[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) / 1e3 for a, b in ev[warmup:]]
+
     def free(self):
         self.sets = []
+        if hasattr(self, "_flush"):
+            del self._flush
         self.torch.cuda.synchronize()
         self.torch.cuda.empty_cache()
 
@@ -252,7 +283,7 @@ def main(argv=None):
     ap.add_argument("--k", type=int, default=5120)
     ap.add_argument("--t", type=int, default=None, help="single point instead of the default pair")
     ap.add_argument("--sweep", type=str, default=None, help="T range lo:hi[:step]")
-    ap.add_argument("--repeats", type=int, default=5, help="timed replays per sweep point (median)")
+    ap.add_argument("--repeats", type=int, default=5, help="timed graph replays per sweep point (median)")
     ap.add_argument("--profile", action="store_true", help="one call after set-up, then exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--csv", type=str, default=None)
@@ -293,10 +324,13 @@ def main(argv=None):
         rows = []
         prev = None
         wl_seed = inputs.workload_seed("sweep_6144x5120_t1_128")
+        codes = inputs.gen_codes(n, k, wl_seed)
+        scales = inputs.gen_scales(n, k, wl_seed)
+        xall = inputs.gen_x(k, hi, wl_seed)
         for t in range(lo, hi + 1, step):
-            p = Point(n, k, t, wl_seed)
-            steps = max(20, min(400, int(4e-3 / max(1e-6, 3e-6 * t))))
-            secs = p.time(steps, args.warmup, repeats=args.repeats)
+            p = Point(n, k, t, wl_seed, data=(xall[:t], codes, scales))
+            steps = max(20, min(200, int(2e-3 / max(1e-6, 1e-6 * t))))
+            secs = p.time(steps, 5, repeats=args.repeats)
             p.free()
             med = float(np.median(secs))
             row = {"t": t, "us": med * 1e6, "min_us": min(secs) * 1e6, "gbs": gbs(n, k, t, med),
@@ -322,23 +356,48 @@ def main(argv=None):
         t = args.t
         p = Point(n, k, t, seed)
         secs = p.time(args.steps, args.warmup, repeats=1)[0]
-        print(json.dumps({"n": n, "k": k, "t": t, "us": secs * 1e6, "gbs": gbs(n, k, t, secs),
-                          "tflops": tflops(n, k, t, secs), "roof_frac": roof_fraction(n, k, t, secs)}))
+        p.free()
+        pc = Point(n, k, t, seed, rotate=False)
+        lat = pc.time_cold(30, 3)
+        pc.free()
+        print(json.dumps({"n": n, "k": k, "t": t, "us": secs * 1e6, "single_call_cold_median_us": float(np.median(lat)) * 1e6,
+                          "gbs": gbs(n, k, t, secs), "tflops": tflops(n, k, t, secs),
+                          "roof_frac": roof_fraction(n, k, t, secs)}))
         return 0
 
     # ---- default: the decode point (headline) + the prefill point ----------
+    # One step = one complete public call on one batch.  The K timed steps run
+    # back to back from one HIP graph over rotating buffer sets (every call
+    # reads a weight untouched for >= 1 GiB of traffic, so cold in the L2s and
+    # the Infinity Cache), bracketed by HIP events on the calls' stream and a
+    # device synchronize on both sides.  Beside it: the pages' single-call
+    # contract (cache flush, then events around one call; median, min, p95),
+    # which on this platform adds the event round trip to every sample.
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     p1 = Point(n, k, 1, seed)
     s1 = p1.time(args.steps, args.warmup, repeats=1)[0]
     p1.free()
+    p1c = Point(n, k, 1, seed, rotate=False)
+    lat1 = p1c.time_cold(100, 5)
+    p1c.free()
     steps2 = max(20, args.steps // 20)
-    p2 = Point(n, k, 1024, inputs.workload_seed("prefill_6144x5120_t1024"))
-    s2 = p2.time(steps2, max(5, args.warmup // 10), repeats=1)[0]
+    seed2 = inputs.workload_seed("prefill_6144x5120_t1024")
+    p2 = Point(n, k, 1024, seed2)
+    s2 = p2.time(steps2, max(3, args.warmup // 10), repeats=1)[0]
     p2.free()
+    p2c = Point(n, k, 1024, seed2, rotate=False)
+    lat2 = p2c.time_cold(30, 3)
+    p2c.free()
 
     v1 = gbs(n, k, 1, s1)
     v2 = tflops(n, k, 1024, s2)
+
+    def stats(lat):
+        a = np.asarray(lat) * 1e6
+        return {"median_us": round(float(np.median(a)), 3), "min_us": round(float(a.min()), 3),
+                "p95_us": round(float(np.percentile(a, 95)), 3)}
+
     line = {
         "metric": METRIC,
         "value": round(v1, 2),
@@ -353,23 +412,24 @@ def main(argv=None):
         "dtype": "f16 (f32 accumulate; bf16 in/out)",
         "data": "synthetic",
         "config": {"workload": "decode_6144x5120_t1", "n": n, "k": k, "t": 1,
-                   "weight_format": "Q4_G64_FP16", "cache": "cold (rotating %d buffer sets)" % 0},
-        # dominant kernel: the few-token kernel is the whole call at T=1; its
+                   "weight_format": "Q4_G64_FP16",
+                   "cache": "cold (rotating buffer sets, >= 1 GiB between reuses)"},
+        # dominant kernel: the few-token kernel is the whole call at T = 1; its
         # algorithmic bytes per launch are model_bytes (W, X and Y once each)
         "roofline": {"bound": "hbm", "achieved": round(v1, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(v1 / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles("gemv", "decode_6144x5120_t1"),
                      "algorithmic_bytes": model_bytes(n, k, 1)},
+        "single_call_cold": stats(lat1),
         "prefill_t1024": {
             "metric": "eff. TFLOP/s @T=1024", "value": round(v2, 2), "unit": "TFLOP/s",
-            "steps": steps2, "ms_per_step": round(s2 * 1e3, 6),
+            "steps": steps2, "ms_per_step": round(s2 * 1e3, 6), "single_call_cold": stats(lat2),
             "roofline": {"bound": "mfma", "achieved": round(v2, 2), "peak": MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(v2 / MFMA_PEAK_TFLOPS, 4),
                          "traffic": traffic_from_profiles("tiled", "prefill_6144x5120_t1024"),
                          "algorithmic_flops": useful_flops(n, k, 1024)},
         },
     }
-    line["config"]["cache"] = "cold (rotating buffer sets, >= 1 GiB between reuses)"
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_t1(n, k, seed)
         line["prefill_t1024"]["cpu_baseline"] = cpu_baseline_rows(n, k, 1024,
