@@ -29,6 +29,9 @@ bool shape_ok(int64_t n, int64_t k, int64_t t) {
 
 int pick_route(int64_t n, int64_t k, int64_t t) {
   if (n == 0 || t == 0) return Q4LIN_ROUTE_NONE;
+  if (t == 1 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
+  q4lin::SkinnyPlan sp;
+  if (q4lin::skinny_plan(n, k, t, &sp)) return Q4LIN_ROUTE_SKINNY;
   if (t <= 4 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
   return Q4LIN_ROUTE_TILED;
 }
@@ -72,6 +75,8 @@ int q4lin_linear(const void* x, const void* codes, const void* scales, void* y,
   hipError_t e = hipSuccess;
   if (route == Q4LIN_ROUTE_GEMV) {
     e = q4lin::launch_gemv(q4lin::GemvArgs{x, codes, scales, y, n, k, t}, s);
+  } else if (route == Q4LIN_ROUTE_SKINNY) {
+    e = q4lin::launch_skinny(q4lin::GemvArgs{x, codes, scales, y, n, k, t}, s);
   } else {
     q4lin::TiledArgs a{x, codes, scales, y, n, k, t, workspace, q4lin::tiled_pick_config(n, k, t)};
     e = q4lin::launch_tiled(a, s);

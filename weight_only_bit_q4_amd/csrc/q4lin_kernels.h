@@ -23,6 +23,20 @@ int64_t gemv_chunks_per_wave(int64_t k);
 size_t gemv_lds_bytes(int64_t k, int64_t t);
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 
+// Small-T route: one workgroup of eight waves per block of bn rows, K split
+// over the waves, no workspace.  skinny_plan() says whether the route takes
+// (n, k, t) and with which block shape; launch_skinny() uses the same plan.
+struct SkinnyPlan {
+  int bn;      // rows per workgroup
+  int ct;      // 16-row matrix-core column tiles per wave (bn <= 16 * ct)
+  int tt;      // 16-token tiles (t <= 16 * tt)
+  int blocks;  // workgroups
+  int off_codes, off_red;  // LDS byte offsets of the code staging / final sums
+  size_t lds_bytes;
+};
+bool skinny_plan(int64_t n, int64_t k, int64_t t, SkinnyPlan* p);
+hipError_t launch_skinny(const GemvArgs& a, hipStream_t stream);
+
 // Tiled matrix-core route.  Workspace layout (256-byte aligned pieces):
 //   x16   fp16 activations scaled by 2^-e[t], tile order (see q4lin_tiled.hip),
 //         tpad * k * 2 bytes with tpad = t rounded up to 32;
