@@ -186,7 +186,7 @@ def test_all_code8_gives_exact_zeros(t):
     assert np.all((got & 0x7FFF) == 0)
 
 
-@pytest.mark.parametrize("t", [1, 4, 48, 260])
+@pytest.mark.parametrize("t", [1, 4, 17, 48, 260])
 def test_wide_range_scales_and_activations(t):
     """Scales over the whole FP16 range (subnormal, negative, zero) and
     activations spread over many binades, with a few large outliers."""
@@ -206,9 +206,10 @@ def test_wide_range_scales_and_activations(t):
 
 def test_extreme_magnitudes_finite_and_infinite():
     """Largest finite activations and scales: results overflow to +-Inf
-    exactly where the exact sum does; nothing becomes NaN."""
+    exactly where the exact sum does; nothing becomes NaN.  T = 3 and 17 take
+    the small-T route's rescaled recomputation."""
     n, k = 32, 128
-    for t in (1, 40):
+    for t in (1, 3, 17, 40):
         r = np.random.default_rng(9)
         c = r.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
         s = np.full((n, k // 64), 0x7BFF, dtype=np.uint16)   # 65504

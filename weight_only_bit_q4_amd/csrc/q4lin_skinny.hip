@@ -60,6 +60,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voffset, uint32_t soffset, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, voffset,
+                                           soffset, 0, 0);
+}
+
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voffset, uint32_t soffset, void* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voffset,
                                            soffset, 0, 0);
@@ -72,10 +77,12 @@ constexpr int ring_depth(int ct) { return ct <= 2 ? 3 : 2; }
 
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
+// (a & m) | c in one instruction: gfx950's three-input bitwise operation with
+// truth table 0xEA.  A builtin rather than inline assembly, so the compiler
+// knows the instruction when it spaces matrix-core operand reads after
+// vector-ALU writes.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
-  return r;
+  return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
 }
 
 // (128 + q) bf16 operand values of one code dword, order k0 k4 k1 k5 k2 k6 k3 k7
@@ -129,20 +136,14 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
               int N, int K, int T, int BN, int off_codes, int off_red) {
   constexpr int BNP = 16 * CT;  // matrix-core columns (rows of W) per workgroup
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint16_t* s_lds = reinterpret_cast<uint16_t*>(lds);          // [BNP][G] fp16 scales, dead rows 0
+  // LDS: the block's scales (fp16 [BNP][G] from byte s_delta), then the
+  // waves' code rings; the final sums reuse the rings.
   const int G = K >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
   const int n0 = blockIdx.x * BN;
   const int rows = min(BN, N - n0);  // real rows of this block (>= 1)
-
-  // --- the block's scales into LDS (rows past the block or past N are 0) ----
-  for (int i = tid; i < BNP * G; i += kThreads) {
-    const int r = i / G;
-    s_lds[i] = r < rows ? scales[(size_t)(n0 + r) * G + (i - r * G)] : (uint16_t)0;
-  }
-  __syncthreads();
 
   // --- this wave's slice of K, in steps of four 64-groups -------------------
   // A step is 128 bytes of every row of the block: eight 16-byte pieces per
@@ -156,7 +157,12 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   const int ng = gh - gl;
   const int nsteps = (ng + kStepGroups - 1) / kStepGroups;
   constexpr int STEP_B = NL * 1024;  // LDS bytes per ring slot
-  uint8_t* cw = lds + off_codes + wave * DEPTH * STEP_B;
+  // the wave's LDS area: the code ring, then its own copy of the scales of
+  // its slice (SW dwords per row, enough for the slice at any alignment)
+  const int SW = (2 * ((G + kWaves - 1) / kWaves) + 3) / 4 + 1;
+  const int wave_b = DEPTH * STEP_B + ((BNP * SW * 4 + 255) & ~255);  // whole 64-lane copies
+  uint8_t* cw = lds + off_codes + wave * wave_b;
+  uint8_t* sw = cw + DEPTH * STEP_B;
   // Buffer over the whole code plane: slots past the block's rows use an
   // offset beyond it and read zeros without touching memory; pieces of
   // groups past the slice read a neighbour's codes (their scale is 0).
@@ -191,6 +197,15 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   for (int ct = 0; ct < CT; ++ct) {
     const int r = 16 * ct + li < BN ? 16 * ct + li : 0;
     rd_row[ct] = r;
+  }
+  // scale of (row 16 ct + li, group g) at s_row[ct] + 2 g (rows past the
+  // block hold other rows' scales or zeros; they are never stored)
+  const uint8_t* s_row[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int r = 16 * ct + li;
+    const uint32_t b = (uint32_t)(n0 + r) * (uint32_t)G * 2u + (uint32_t)gl * 2u;
+    s_row[ct] = sw + 4 * SW * r + (b & 3u) - 2 * gl;
   }
   auto rd_addr = [&](int st, int ct, int p) __device__ {
     const int r = rd_row[ct];
@@ -247,7 +262,7 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
         const uint32_t wa = h == 0 ? cp[ct].z : cp[ct].x;
         const uint32_t wb = h == 0 ? cp[ct].w : cp[ct].y;
         const bf16x8_t ba = bf16_codes(wa), bb = bf16_codes(wb);
-        const float sc = g < gh ? f16_bits_to_f32(s_lds[(16 * ct + li) * G + g]) : 0.0f;
+        const float sc = g < gh ? f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(s_row[ct] + 2 * g)) : 0.0f;
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
           f32x4_t pr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[0][tt], ba, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -265,13 +280,15 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     for (int p = 0; p < 2; ++p) load_x(gl + st * kStepGroups + 2 * p, xv[p]);
   };
 
-  // Step st.  Issue order per step: the activations of step st + 1 (8 TT
-  // loads), then the codes of step st + DEPTH (NL loads).  So when step st
-  // starts, the loads younger than its codes are at most the codes of the
-  // DEPTH - 1 later steps and the activations of step st: waiting until no
-  // more than NL (DEPTH - 1) + 8 TT loads are outstanding means its codes
-  // have landed.
-  auto step = [&](int st, bool scaled, const u32x4_t (&xcur)[2][2][2][TT], u32x4_t (&xnext)[2][2][2][TT]) __device__ {
+  // Step st issues the activations of step st + 1 (8 TT loads) and the codes
+  // of step st + DEPTH (NL loads; past the slice they read nothing).  So when step st starts, the loads younger
+  // than its codes that may still be in flight are the codes of the DEPTH - 1
+  // later steps and the activations of step st (older activations have been
+  // used, hence have landed): waiting until no more than NL (DEPTH - 1) +
+  // 8 TT loads are outstanding means its codes have landed.
+  // last: the slice's final step, which prefetches nothing.
+  auto step = [&](int st, bool scaled, bool last, const u32x4_t (&xcur)[2][2][2][TT],
+                  u32x4_t (&xnext)[2][2][2][TT]) __device__ {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (DEPTH - 1) + 8 * TT));
     __builtin_amdgcn_sched_barrier(0);
@@ -283,52 +300,97 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     // the slot is free once the reads are back; refill it with step st + DEPTH
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    load_xs(st + 1, xnext);
-    issue(st + DEPTH);
-    __builtin_amdgcn_sched_barrier(0);
-    if (st < nsteps) {
-      const int gs = gl + st * kStepGroups;
-#pragma unroll
-      for (int p = 0; p < kStepGroups / 2; ++p)
-        if (gs + 2 * p < gh) pair_products(gs + 2 * p, cp[p], scaled, xcur[p]);
+    if (!last) {
+      load_xs(st + 1, xnext);
+      issue(st + DEPTH);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const int gs = gl + st * kStepGroups;
+#pragma unroll
+    for (int p = 0; p < kStepGroups / 2; ++p)
+      if (gs + 2 * p < gh) pair_products(gs + 2 * p, cp[p], scaled, xcur[p]);
   };
 
-  // One pass over the slice.  scaled: activations times 2^-ex[tt].
-  auto run = [&](bool scaled) __device__ {
+  // The slice's first DEPTH code steps and first activations (issued
+  // before anything waits).
+  // Step 0's codes must be issued before step 0's activations (its wait
+  // counts the activations among the younger loads), so the scheduler may
+  // not move them across.
+  auto prologue = [&](u32x4_t (&xs)[2][2][2][TT]) __device__ {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(d);
+    __builtin_amdgcn_sched_barrier(0);
+    load_xs(0, xs);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One pass over the slice, prologue already issued.  scaled: activations
+  // times 2^-ex[tt].
+  auto run = [&](bool scaled, u32x4_t (&xs0)[2][2][2][TT]) __device__ {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) acc[ct][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (ng <= 0) return;
-    u32x4_t xs0[2][2][2][TT], xs1[2][2][2][TT];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d) issue(d);
-    load_xs(0, xs0);
-    issue(DEPTH - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int st = 0; st < nsteps; st += 2) {
-      step(st, scaled, xs0, xs1);
-      step(st + 1, scaled, xs1, xs0);
+    u32x4_t xs1[2][2][2][TT];
+    // steps in pairs (the two activation buffers alternate), the last one or
+    // two peeled so that nothing past the slice is fetched
+    int st = 0;
+    for (; st + 2 < nsteps; st += 2) {
+      step(st, scaled, false, xs0, xs1);
+      step(st + 1, scaled, false, xs1, xs0);
     }
-    // the trailing (empty) loads must land before the LDS is used otherwise
+    if (st + 2 == nsteps) {
+      step(st, scaled, false, xs0, xs1);
+      step(st + 1, scaled, true, xs1, xs0);
+    } else {
+      step(st, scaled, true, xs0, xs1);
+    }
+    // the trailing code copies (past the slice: zeros, no memory traffic)
+    // must land before the LDS is used otherwise
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // --- the scales of the wave's slice, then its first steps ------------------
+  // Each wave copies the dwords holding its slice's scales for the block's
+  // BNP rows (rows past N read zeros) into its own LDS area.  These copies are
+  // issued first, so step 0's wait covers them: no barrier, and no wave waits
+  // for another's memory traffic.
+  u32x4_t xs0[2][2][2][TT];
+  if (ng > 0) {
+    // the byte count rounded up to whole dwords: the copy moves aligned
+    // dwords, and the one holding the last scale must not read as zero (an
+    // aligned dword never leaves the page of its first byte)
+    const rsrc_t rs = make_rsrc(scales, (uint32_t)(((size_t)N * (size_t)G * 2 + 3) & ~(size_t)3));
+    const int nd = BNP * SW;
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; 64 * i < nd; ++i) {
+      const int d = min(64 * i + lane, nd - 1);
+      const int r = d / SW, j = d - r * SW;
+      const uint32_t b = ((uint32_t)(n0 + r) * (uint32_t)G * 2u + (uint32_t)gl * 2u) & ~3u;
+      dma4(rs, b + 4u * (uint32_t)j, 0u, sw + 256 * i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    prologue(xs0);
+  }
+
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) ex[tt] = 0;
-  run(false);
+  run(false, xs0);
 
   // Sums beyond the FP32 range: recompute this wave's slice with scaled tokens.
+  // (Only entries that are stored count: padding rows and tokens may hold
+  // anything.)
   bool bad = false;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bad |= !(__builtin_fabsf(acc[ct][tt][r]) <= 3.0e38f);
+      for (int r = 0; r < 4; ++r)
+        if (16 * ct + li < rows && 16 * tt + 4 * lq + r < T) bad |= !(__builtin_fabsf(acc[ct][tt][r]) <= 3.0e38f);
   const bool rerun = __builtin_amdgcn_ballot_w64(bad) != 0;
   if (rerun) {
     // exponent per token over this wave's slice: largest magnitude in [1, 2)
@@ -344,7 +406,8 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
       if (m >= 0x7F80u) m = 0x7F7Fu;  // Inf/NaN inputs are outside the contract
       ex[tt] = m >= 0x80u ? (int)(m >> 7) - 127 : 0;
     }
-    run(true);
+    if (ng > 0) prologue(xs0);
+    run(true, xs0);
   }
 
   // --- eight-way sum in binary64 ----------------------------------------------
@@ -406,8 +469,10 @@ bool skinny_plan(int64_t n, int64_t k, int64_t t, SkinnyPlan* p) {
   const int64_t ct = (bn + 15) / 16;
   const int64_t tt = t > 16 ? 2 : 1;
   if (ct * tt > 4) return false;  // accumulators and operands must fit the registers
-  const size_t sc = align16((size_t)(16 * ct) * (size_t)G * 2);
-  const size_t codes_b = (size_t)kWaves * (size_t)ring_depth((int)ct) * (size_t)(2 * ct) * 1024;
+  const int64_t sw = (2 * ((G + kWaves - 1) / kWaves) + 3) / 4 + 1;  // scale dwords per row and wave
+  const size_t wave_b = (size_t)ring_depth((int)ct) * (size_t)(2 * ct) * 1024 + (size_t)((16 * ct * sw * 4 + 255) & ~255);
+  const size_t codes_b = (size_t)kWaves * wave_b;
+  const size_t sc = 0;
   const size_t red_b = (size_t)kWaves * (size_t)t * (size_t)bn * 8 + (size_t)kWaves * 16 * 2 * 4;
   const size_t lds = sc + (codes_b > red_b ? codes_b : red_b);
   if (lds > 160 * 1024) return false;
