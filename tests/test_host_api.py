@@ -74,12 +74,12 @@ def test_workspace_checks():
 
 
 def test_routes_and_workspace_sizes():
-    # T = 1 is the few-token route, with no workspace
-    assert q.q4lin_route(6144, 5120, 1) == q.Q4LIN_ROUTE_GEMV
+    # T = 1 is the single-token route, with no workspace
+    assert q.q4lin_route(6144, 5120, 1) == q.Q4LIN_ROUTE_DECODE
     assert q.q4lin_workspace_bytes(6144, 5120, 1) == 0
     for t in (1, 2, 3, 4, 5, 16, 64, 128, 512, 1024):
         r = q.q4lin_route(6144, 5120, t)
-        assert r in (q.Q4LIN_ROUTE_GEMV, q.Q4LIN_ROUTE_SKINNY, q.Q4LIN_ROUTE_TILED)
+        assert r in (q.Q4LIN_ROUTE_DECODE, q.Q4LIN_ROUTE_GEMV, q.Q4LIN_ROUTE_SKINNY, q.Q4LIN_ROUTE_TILED)
         ws = q.q4lin_workspace_bytes(6144, 5120, t)
         if r == q.Q4LIN_ROUTE_TILED:
             # float16 activations padded to 32 tokens plus one int32 per token

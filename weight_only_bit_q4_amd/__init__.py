@@ -31,6 +31,7 @@ Q4LIN_ROUTE_NONE = 0
 Q4LIN_ROUTE_GEMV = 1
 Q4LIN_ROUTE_SKINNY = 2
 Q4LIN_ROUTE_TILED = 3
+Q4LIN_ROUTE_DECODE = 4
 
 EXPORTED = ("q4lin_workspace_bytes", "q4lin_linear", "q4lin_status_string", "q4lin_route",
             "q4lin_version")

@@ -29,6 +29,8 @@ bool shape_ok(int64_t n, int64_t k, int64_t t) {
 
 int pick_route(int64_t n, int64_t k, int64_t t) {
   if (n == 0 || t == 0) return Q4LIN_ROUTE_NONE;
+  q4lin::DecodePlan dp;
+  if (q4lin::decode_plan(n, k, t, &dp)) return Q4LIN_ROUTE_DECODE;
   if (t == 1 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
   q4lin::SkinnyPlan sp;
   if (q4lin::skinny_plan(n, k, t, &sp)) return Q4LIN_ROUTE_SKINNY;
@@ -75,6 +77,8 @@ int q4lin_linear(const void* x, const void* codes, const void* scales, void* y,
   hipError_t e = hipSuccess;
   if (route == Q4LIN_ROUTE_GEMV) {
     e = q4lin::launch_gemv(q4lin::GemvArgs{x, codes, scales, y, n, k, t}, s);
+  } else if (route == Q4LIN_ROUTE_DECODE) {
+    e = q4lin::launch_decode(q4lin::GemvArgs{x, codes, scales, y, n, k, t}, s);
   } else if (route == Q4LIN_ROUTE_SKINNY) {
     e = q4lin::launch_skinny(q4lin::GemvArgs{x, codes, scales, y, n, k, t}, s);
   } else {

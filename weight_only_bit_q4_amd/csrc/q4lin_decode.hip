@@ -1,0 +1,314 @@
+// q4lin_decode.hip -- the single-token route (T = 1): vector-ALU dot products,
+// one weight stream per CU.
+//
+// The pages' prior art for T = 1 is a dedicated single-token GEMV
+// ("q4-linear.md", notes under the result table); this is an MI355X design of
+// that step.
+//
+// Work mapping.  A workgroup of eight waves owns BN consecutive rows (about
+// N / (256 c) with c workgroups per CU) and the whole of K; wave w owns the
+// w-th eighth of the 64-groups.  Inside a wave the slice of every row is cut
+// into S slots of PL consecutive 16-byte pieces; lane l serves slot l % S of
+// rows l / S, l / S + R, ... (R = 64 / S row groups).  So a lane keeps one
+// fixed piece of the activations in registers for all its rows, each load
+// instruction reads R rows x 16 PL S contiguous bytes, and every load of a
+// lane is issued before the first wait.  The block's scales arrive by a
+// direct-to-LDS copy issued first.
+//
+// Arithmetic (as in the pages' "decode, FP32 accumulate" reading of the op):
+//   * Activations: float16 copies of the bf16 values times 2^-e, e from the
+//     wave slice's largest magnitude (every value within 2^34 of it converts
+//     exactly); odd-k values are further divided by 16.
+//   * Codes become float16 operands with one AND: w & 0x000F000F is the pair
+//     (q * 2^-24, q' * 2^-24) (subnormal, exact), w & 0x00F000F0 is 16 q * 2^-24
+//     for the odd k, which the /16 above cancels.
+//   * v_dot2_f32_f16 sums q * x; the offset enters as sum (q - 8) x =
+//     sum q x - sum 8 x, the second sum from the very same dot2 chain run on
+//     an all-8 code dword, so a piece of eight-codes contributes exactly 0.
+//     Each piece's difference is scaled by its group's scale in FP32.
+//   * Partials carry 2^-(e + 24) with a per-wave e; the eight waves' sums are
+//     combined in binary64 and rounded to bf16 once.
+#include "q4lin_device.h"
+#include "q4lin_kernels.h"
+
+namespace q4lin {
+
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct-to-LDS dword copy: lane l sends 4 bytes from base + voffset to
+// lds_base + 4 l; offsets at or past the resource's byte count read zeros.
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voffset, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, voffset, 0u, 0,
+                                           0);
+}
+
+// s_waitcnt immediate for gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 =
+// no wait), lgkmcnt 11:8 (15 = no wait).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// largest |x| over 8 bf16 values, as bf16 magnitude bits (monotone in the value)
+__device__ __forceinline__ uint32_t max_mag8(u32x4_t v) {
+  uint32_t m = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  return max(m, max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu)));
+}
+
+// e such that (largest magnitude) * 2^-e lies in [2^14, 2^15); 0 for all-zero input.
+__device__ __forceinline__ int exponent_for(uint32_t m) {
+  if (m >= 0x7F80u) m = 0x7F7Fu;  // Inf/NaN inputs are outside the contract
+  if (m == 0u) return 0;
+  const int lg = (m >= 0x80u) ? (int)(m >> 7) - 127 : (31 - __builtin_clz(m)) - 133;
+  return lg - 14;
+}
+
+// 8 bf16 values -> float16 pairs (k0,k4) (k1,k5) (k2,k6) (k3,k7), times 2^-e,
+// odd k times 2^-(e+4).
+__device__ __forceinline__ u32x4_t to_f16_pairs(u32x4_t v, int e) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t h[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    h[2 * q] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(bf16_bits_to_f32(w[q] & 0xFFFFu), -e));
+    h[2 * q + 1] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(bf16_bits_to_f32(w[q] >> 16), -e - 4));
+  }
+  return u32x4_t{h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16), h[3] | (h[7] << 16)};
+}
+
+// dot2 chain of one 16-byte code piece (32 weights) against its activations
+__device__ __forceinline__ float piece_dot(u32x4_t w, const u32x4_t (&xf)[4]) {
+  float c = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t wd = w[d];
+    const uint32_t w8 = wd >> 8;
+    c = dot2_f16(wd & 0x000F000Fu, xf[d].x, c);
+    c = dot2_f16(wd & 0x00F000F0u, xf[d].y, c);
+    c = dot2_f16(w8 & 0x000F000Fu, xf[d].z, c);
+    c = dot2_f16(w8 & 0x00F000F0u, xf[d].w, c);
+  }
+  return c;
+}
+
+// PL: consecutive 16-byte pieces per lane and row; MAXR: rows per lane, at most
+template <int PL, int MAXR>
+__global__ void __launch_bounds__(kThreads)
+decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+              uint16_t* __restrict__ y, int N, int K, int BN, int SW) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int G = K >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * BN;
+  const int rows = min(BN, N - n0);
+
+  // wave slice, slots and row groups (all wave-uniform but the lane's own)
+  const int gl = (G * wave) / kWaves, gh = (G * (wave + 1)) / kWaves;
+  const int ng = gh - gl;
+  const int P = 2 * ng;                          // pieces per row in the slice
+  const int S = max((P + PL - 1) / PL, 1);       // slots per row
+  const int R = 64 / S;                          // row groups per wave (>= 1)
+  const int grp_raw = lane / S;
+  // idle lanes (past R row groups) repeat the last group's addresses (no
+  // extra memory traffic); their sums are never read
+  const int grp = min(grp_raw, R - 1);
+  const int slot = lane - grp_raw * S;
+  const int pc0 = slot * PL;
+
+  // LDS: per wave, the scales of its slice ([BN][SW] dwords), then a scratch
+  // of 64 x MAXR floats; after them the waves' combined row sums (binary64).
+  const int sreg = (BN * SW * 4 + 255) & ~255;
+  uint8_t* wl = lds + wave * (sreg + 64 * MAXR * 4);
+  float* scratch = reinterpret_cast<float*>(wl + sreg);
+  double* rowsum = reinterpret_cast<double*>(lds + kWaves * (sreg + 64 * MAXR * 4));
+
+  // 1. scales of the slice for the block's rows, straight into LDS
+  if (ng > 0) {
+    const rsrc_t rs = make_rsrc(scales, (uint32_t)(((size_t)N * (size_t)G * 2 + 3) & ~(size_t)3));
+    const int nd = BN * SW;
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; 64 * i < nd; ++i) {
+      const int d = min(64 * i + lane, nd - 1);
+      const int r = d / SW, j = d - r * SW;
+      const uint32_t b = ((uint32_t)(n0 + r) * (uint32_t)G * 2u + (uint32_t)gl * 2u) & ~3u;
+      dma4(rs, b + 4u * (uint32_t)j, wl + 256 * i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // 2. the lane's activations (before the codes, so that waiting for them
+  //    does not wait for the codes)
+  u32x4_t xv[PL][4];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(x + 64 * gl + 32 * min(pc0 + i, max(P - 1, 0)));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) xv[i][d] = xp[d];
+  }
+  // 3. codes of the lane's rows (clamped addresses stay valid; the values of
+  //    rows past the block and pieces past the slice are never used)
+  u32x4_t w[MAXR][PL];
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const int row = n0 + min(grp + R * j, rows - 1);
+    const uint8_t* rp = codes + (size_t)row * (size_t)(K >> 1) + (size_t)gl * 32;
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+      w[j][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(rp + 16 * min(pc0 + i, max(P - 1, 0))));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 4. the slice's exponent (pieces past the slice repeat a valid piece)
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < PL; ++i)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) m = max(m, max_mag8(xv[i][d]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  const int e = exponent_for(m);
+  u32x4_t xf[PL][4];
+#pragma unroll
+  for (int i = 0; i < PL; ++i)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) xf[i][d] = to_f16_pairs(xv[i][d], e);
+
+  // 5. the eight-code sums of the lane's pieces, same chain as the rows use
+  const u32x4_t k8 = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+  float s8[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) s8[i] = piece_dot(k8, xf[i]);
+
+  // the scale copy was issued before every load of steps 2-3
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(MAXR * PL + 4 * PL));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 6. rows
+  float acc[MAXR];
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const int r = grp + R * j;
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int pc = pc0 + i;
+      const uint32_t b = (uint32_t)(n0 + min(r, rows - 1)) * (uint32_t)G * 2u + (uint32_t)gl * 2u;
+      const uint16_t sb =
+          *reinterpret_cast<const uint16_t*>(wl + 4 * SW * min(r, rows - 1) + (b & 3u) + 2 * (pc >> 1));
+      const float s = pc < P ? f16_bits_to_f32(sb) : 0.0f;
+      a = __builtin_fmaf(s, piece_dot(w[j][i], xf[i]) - s8[i], a);
+    }
+    acc[j] = a;
+  }
+
+  // 7. sums: the S slots of each row group inside the wave (LDS), then the
+  //    eight waves in binary64
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) scratch[j * 64 + lane] = acc[j];
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own writes are visible to it
+  // (four independent partial sums, so that the LDS reads overlap)
+  for (int q = lane; q < R * MAXR; q += 64) {
+    const int g = q % R, j = q / R;
+    const int r = g + R * j;
+    if (r < rows) {
+      const float* sp = scratch + j * 64 + g * S;
+      float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
+      int sl = 0;
+      for (; sl + 4 <= S; sl += 4) {
+        v0 += sp[sl];
+        v1 += sp[sl + 1];
+        v2 += sp[sl + 2];
+        v3 += sp[sl + 3];
+      }
+      for (; sl < S; ++sl) v0 += sp[sl];
+      rowsum[wave * BN + r] = __builtin_ldexp((double)((v0 + v1) + (v2 + v3)), e + 24);
+    }
+  }
+  // waves without groups contribute zero
+  if (ng <= 0)
+    for (int r = lane; r < rows; r += 64) rowsum[wave * BN + r] = 0.0;
+  __syncthreads();
+  for (int r = tid; r < rows; r += kThreads) {
+    double v = 0.0;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) v += rowsum[wv * BN + r];
+    y[n0 + r] = f32_to_bf16_rne((float)v);
+  }
+}
+
+size_t decode_lds(int bn, int sw, int maxr) {
+  return (size_t)kWaves * (size_t)(((bn * sw * 4 + 255) & ~255) + 64 * maxr * 4) + (size_t)kWaves * bn * 8;
+}
+
+template <int PL, int MAXR>
+hipError_t launch_pm(const DecodePlan& p, const GemvArgs& a, hipStream_t stream) {
+  auto kern = decode_kernel<PL, MAXR>;
+  const size_t lds = decode_lds(p.bn, p.sw, MAXR);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  kern<<<dim3((unsigned)p.blocks), dim3(kThreads), lds, stream>>>(
+      static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
+      static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, p.bn, p.sw);
+  return hipGetLastError();
+}
+
+// instantiated (pieces per lane, rows per lane) shapes
+constexpr int kShapes[][2] = {{1, 8}, {1, 16}, {2, 8}, {4, 4}};
+
+}  // namespace
+
+bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p) {
+  if (t != 1 || n < 1 || k < 64) return false;
+  if (n * (k / 2) >= (int64_t(1) << 31)) return false;  // 32-bit buffer offsets
+  const int64_t G = k / 64;
+  const int64_t pmax = 2 * ((G + kWaves - 1) / kWaves);
+  const int64_t pmin = 2 * (G / kWaves);
+  for (int64_t c = 1; c <= 3; ++c) {  // workgroups per CU
+    const int64_t bn = (n + 256 * c - 1) / (256 * c);
+    for (const auto& sh : kShapes) {
+      const int64_t pl = sh[0], maxr = sh[1];
+      const int64_t s = (pmax + pl - 1) / pl;
+      if (s > 64) continue;
+      // every wave, also one with the smaller slice, must cover bn rows
+      const int64_t smin = pmin > 0 ? (pmin + pl - 1) / pl : 1;
+      const int64_t rmin = 64 / (s > smin ? s : smin);
+      if ((bn + rmin - 1) / rmin > maxr) continue;
+      // fewer than half the lanes busy: leave the shape to the other route
+      if (2 * rmin * s < 64 && bn > rmin) continue;
+      const int64_t sw = (2 * ((G + kWaves - 1) / kWaves) + 3) / 4 + 1;
+      if (decode_lds((int)bn, (int)sw, (int)maxr) > 64 * 1024) continue;
+      p->bn = (int)bn;
+      p->sw = (int)sw;
+      p->pl = (int)pl;
+      p->maxr = (int)maxr;
+      p->blocks = (int)((n + bn - 1) / bn);
+      return true;
+    }
+  }
+  return false;
+}
+
+hipError_t launch_decode(const GemvArgs& a, hipStream_t stream) {
+  DecodePlan p;
+  if (!decode_plan(a.n, a.k, a.t, &p)) return hipErrorInvalidValue;
+  if (p.pl == 1 && p.maxr == 8) return launch_pm<1, 8>(p, a, stream);
+  if (p.pl == 1 && p.maxr == 16) return launch_pm<1, 16>(p, a, stream);
+  if (p.pl == 2 && p.maxr == 8) return launch_pm<2, 8>(p, a, stream);
+  if (p.pl == 4 && p.maxr == 4) return launch_pm<4, 4>(p, a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace q4lin

@@ -23,6 +23,18 @@ int64_t gemv_chunks_per_wave(int64_t k);
 size_t gemv_lds_bytes(int64_t k, int64_t t);
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 
+// Single-token route: a workgroup of eight waves per block of bn rows, K
+// split over the waves, activations in registers, no workspace.
+struct DecodePlan {
+  int bn;      // rows per workgroup
+  int sw;      // scale dwords per row copied by each wave
+  int pl;      // consecutive 16-byte pieces per lane and row
+  int maxr;    // rows per lane, at most
+  int blocks;  // workgroups
+};
+bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p);
+hipError_t launch_decode(const GemvArgs& a, hipStream_t stream);
+
 // Small-T route: one workgroup of eight waves per block of bn rows, K split
 // over the waves, no workspace.  skinny_plan() says whether the route takes
 // (n, k, t) and with which block shape; launch_skinny() uses the same plan.
