@@ -27,8 +27,9 @@ CFLAGS = [
     "-mcode-object-version=5",
     # packed FP32 vector instructions stay off in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # matrix-core results in ordinary VGPRs: the tiled kernel scales every
-    # product with VALU instructions, which cannot read accumulator registers
+    # matrix-core results in ordinary VGPRs: the small-T kernel scales every
+    # group's products with VALU instructions, which cannot read accumulator
+    # registers
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result", "-Wno-unknown-warning-option", "-Wno-cuda-compat",
     "-I", os.path.join(ROOT, "include"),

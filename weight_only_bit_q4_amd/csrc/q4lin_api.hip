@@ -38,8 +38,8 @@ int pick_route(int64_t n, int64_t k, int64_t t) {
   return Q4LIN_ROUTE_TILED;
 }
 
-size_t route_workspace(int route, int64_t k, int64_t t) {
-  return route == Q4LIN_ROUTE_TILED ? q4lin::tiled_workspace_bytes(k, t) : 0;
+size_t route_workspace(int route, int64_t n, int64_t k, int64_t t) {
+  return route == Q4LIN_ROUTE_TILED ? q4lin::tiled_workspace_bytes(n, k, t) : 0;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -50,7 +50,7 @@ extern "C" {
 
 int64_t q4lin_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   if (!shape_ok(n, k, t)) return -Q4LIN_E_SHAPE;
-  return (int64_t)route_workspace(pick_route(n, k, t), k, t);
+  return (int64_t)route_workspace(pick_route(n, k, t), n, k, t);
 }
 
 int q4lin_route(int64_t n, int64_t k, int64_t t) {
@@ -67,7 +67,7 @@ int q4lin_linear(const void* x, const void* codes, const void* scales, void* y,
   if (!x || !codes || !scales || !y) return Q4LIN_E_NULL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(y, 2))
     return Q4LIN_E_ALIGN;
-  const size_t need = route_workspace(route, k, t);
+  const size_t need = route_workspace(route, n, k, t);
   if (need > 0) {
     if (workspace_bytes < need) return Q4LIN_E_WORKSPACE;
     if (!workspace) return Q4LIN_E_NULL;

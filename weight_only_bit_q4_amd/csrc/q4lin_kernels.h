@@ -71,7 +71,7 @@ struct TiledArgs {
 };
 
 int64_t tiled_tpad(int64_t t);
-size_t tiled_workspace_bytes(int64_t k, int64_t t);
+size_t tiled_workspace_bytes(int64_t n, int64_t k, int64_t t);
 TiledConfig tiled_pick_config(int64_t n, int64_t k, int64_t t);
 hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream);
 

@@ -455,7 +455,6 @@ hipError_t launch_ct(const SkinnyPlan& p, const GemvArgs& a, hipStream_t stream)
   return hipGetLastError();
 }
 
-size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
 }  // namespace
 

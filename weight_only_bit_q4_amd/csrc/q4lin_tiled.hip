@@ -4,34 +4,33 @@
 // MMA with 32x32 to 64x128 output tiles ("q4-linear.md", notes under the
 // result table).  This is an MI355X design of the same step.
 //
-// Operands.  The 64-group scale must be applied to exact group sums
-// (rounding (q-8)*scale to a 16-bit float loses bits the tolerance needs), so
-// every group's partial product P = sum_k (q-8) x is formed by the matrix
-// cores from exact operands and then scaled in FP32: acc += scale * P.
-//   * Weights: a code dword gives four float16 pairs with two VALU operations
-//     each.  Masking with 0x000F000F and OR-ing 0x6400 builds 1024 + q for the
-//     nibbles at bits 0-3 of each half; masking with 0x00F000F0 builds
-//     1024 + 16 q for the nibbles at bits 4-7.  One packed subtraction
-//     (1032 resp. 1152) leaves q - 8 resp. 16 (q - 8), both exact in float16.
+// Operands.  The matrix cores take float16 on both sides and accumulate in
+// FP32 across all groups (v_mfma_f32_32x32x16_f16, A = activations, 32 tokens
+// x 16 k; B = weights, 16 k x 32 rows).
+//   * Weights are dequantized with their scale, as the pages' large-T path
+//     feeds its MMA 16-bit dequantized weights: (q - 8) * s' rounded once to
+//     float16 (11 significant bits, three more than bfloat16), with
+//     s' = s * 2^c[n] and c[n] a per-row power of two that puts the row's
+//     largest scale in [2^11, 2^12) (so nothing overflows float16 and small
+//     scales keep full precision).  A code dword gives four float16 pairs:
+//     v_bitop3 builds 1024 + q exactly, a packed subtraction of 1032 leaves
+//     q - 8, a packed multiply applies s'.
 //   * Activations: a preparation pass multiplies each token by a power of two
 //     2^-e[t] chosen from its largest magnitude (so every bf16 value within
-//     2^34 of it converts to float16 exactly), divides the odd-k values by a
-//     further 16 (cancelling the 16 above), and writes them in the order the
-//     matrix-core operand reads want.  The epilogue multiplies by 2^e[t].
-//   * v_mfma_f32_32x32x16_f16 with A = activations (32 tokens x 16 k) and
-//     B = weights (16 k x 32 rows): every lane's 16 accumulators share one
-//     weight row, so one scale per lane per group suffices.
+//     2^34 of it converts to float16 exactly) and writes them in the order the
+//     matrix-core operand reads want.
+//   * The epilogue multiplies by 2^(e[t] - c[n]) and rounds to bf16.
 //
 // Data movement.  A workgroup owns BN rows x BT tokens.  Per 64-group it
-// needs BN x 32 code bytes, BN scales and BT x 64 activations; these stream
-// into an S-stage LDS ring with gfx950 direct-to-LDS loads
-// (global_load_lds_dwordx4 / _dword), issued S-2 groups ahead, so the HBM
-// latency of the codes and the L2 latency of the activations are covered.
-// Each thread dequantizes exactly the code pieces it loaded itself (its own
-// load counter is enough), into a padded, double-buffered weight tile; one
-// barrier per group publishes that tile and the ring stage to all waves.
-// Waits are explicit s_waitcnt vmcnt(n) with n the count of younger stages
-// still allowed in flight; the compiler's own fences would wait for all.
+// needs BN x 32 code bytes and BN scales, which stream into a DS-slot LDS ring
+// with gfx950 direct-to-LDS loads issued DS+1 groups ahead (covering the HBM
+// latency), and BT x 64 activations, which each wave loads straight into the
+// matrix cores' operand registers (AGPRs) DS-1 groups ahead.  Each thread
+// dequantizes the code dwords it loaded itself, with the scale of their row
+// (loaded by another thread), into a padded, double-buffered weight tile; one
+// barrier per group publishes the tile and the ring slot to all waves.  Waits
+// are explicit s_waitcnt vmcnt(n) with n the count of younger loads still
+// allowed in flight; the compiler's own fences would wait for all.
 #include <type_traits>
 
 #include "q4lin_device.h"
@@ -54,24 +53,65 @@ __device__ __forceinline__ uint32_t max_mag8(u32x4_t v) {
   return max(m, max(max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu)));
 }
 
-// 8 bf16 values -> float16 in pair order, times 2^-e (odd k: 2^-(e+4)).
+// 8 bf16 values -> float16 in pair order, times 2^-e.
 __device__ __forceinline__ u32x4_t to_f16_pairs(u32x4_t v, int e) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t h[8];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     h[2 * q] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(bf16_bits_to_f32(w[q] & 0xFFFFu), -e));
-    h[2 * q + 1] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(bf16_bits_to_f32(w[q] >> 16), -e - 4));
+    h[2 * q + 1] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(bf16_bits_to_f32(w[q] >> 16), -e));
   }
   return u32x4_t{h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16), h[3] | (h[7] << 16)};
 }
 
+// Per-row exponent c[n]: the row's largest scale magnitude times 2^c lies in
+// [2^11, 2^12), clamped to c in [-4, 15] (so 2^c is a normal float16 and
+// every scaled weight (q - 8) s 2^c stays below 2^15 in magnitude; the
+// smallest float16 scale 2^-24 still scales to a normal 2^-9).  0 for a row
+// of zero scales.  32 rows per workgroup: the rows' scales are one contiguous
+// run, read coalesced, with an LDS maximum per row.
+constexpr int kRowsPerBlock = 32;
+__device__ void row_exponents(const uint16_t* __restrict__ scales, int N, int G, int r0, int* __restrict__ rexp) {
+  __shared__ uint32_t rmax[kRowsPerBlock];
+  const int tid = threadIdx.x;
+  if (tid < kRowsPerBlock) rmax[tid] = 0u;
+  __syncthreads();
+  const int rows = min(kRowsPerBlock, N - r0);
+  const int cnt = rows * G;  // <= 2^19
+  const uint16_t* s = scales + (int64_t)r0 * G;
+  for (int i0 = 0; i0 < cnt; i0 += 256 * 16) {
+    uint32_t v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = s[min(i0 + j * 256 + tid, cnt - 1)] & 0x7FFFu;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) atomicMax(&rmax[min(i0 + j * 256 + tid, cnt - 1) / G], v[j]);
+  }
+  __syncthreads();
+  if (tid < rows) {
+    uint32_t m = rmax[tid];
+    if (m >= 0x7C00u) m = 0x7BFFu;  // Inf/NaN scales are outside the contract
+    int c = 0;
+    if (m != 0u) {
+      const int lg = (m >= 0x400u) ? (int)(m >> 10) - 15 : (31 - __builtin_clz(m)) - 24;  // floor(log2 |s|)
+      c = min(max(11 - lg, -4), 15);
+    }
+    rexp[r0 + tid] = c;
+  }
+}
+
 // Per-token exponent e[t]: the token's largest magnitude times 2^-e lies in
 // [2^14, 2^15), so every bf16 value within 2^34 of it converts to float16
-// exactly; 0 for all-zero and padding tokens.  One wave per token.
+// exactly; 0 for all-zero and padding tokens.  One wave per token; the blocks
+// past the token blocks compute the row exponents.
 constexpr int kExpWaves = 4;
 __global__ void __launch_bounds__(64 * kExpWaves)
-prep_exp_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __restrict__ texp) {
+prep_exp_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __restrict__ texp,
+                const uint16_t* __restrict__ scales, int N, int* __restrict__ rexp, int tok_blocks) {
+  if ((int)blockIdx.x >= tok_blocks) {
+    row_exponents(scales, N, K >> 6, ((int)blockIdx.x - tok_blocks) * kRowsPerBlock, rexp);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kExpWaves + (threadIdx.x >> 6);
   if (t >= Tpad) return;
@@ -142,22 +182,25 @@ prep_pack_kernel(const u32x4_t* __restrict__ x, int K, int T, const int* __restr
 // ---------------------------------------------------------------------------
 // the tiled kernel
 // ---------------------------------------------------------------------------
+// (a & m) | c in one instruction (gfx950 three-input bitwise operation, truth
+// table 0xEA), as a builtin so that the compiler sees it when it spaces the
+// instructions around matrix-core operand reads.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
-  return r;
+  return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
 }
 
-// q - 8 (bits 0-3) and 16 (q - 8) (bits 4-7) as float16 pairs
-__device__ __forceinline__ u32x4_t dequant_dword(uint32_t w) {
+// Weights (q - 8) * s' as float16 pairs in the order (k0,k4) (k1,k5) (k2,k6)
+// (k3,k7) of a code dword: v_bitop3 builds 1024 + q exactly (fp16 spacing 1 on
+// [1024, 2048)), a packed subtraction of 1032 leaves q - 8 exactly, and a packed
+// multiply by the pair sp = (s', s') rounds (q - 8) * s' once to float16.
+__device__ __forceinline__ u32x4_t dequant_dword(uint32_t w, uint32_t sp) {
   const f16x2_t o1 = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const f16x2_t o16 = {(_Float16)1152.0f, (_Float16)1152.0f};
-  const uint32_t w8 = w >> 8;
+  const f16x2_t s2 = __builtin_bit_cast(f16x2_t, sp);
   u32x4_t r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, and_or(w, 0x000F000Fu, 0x64006400u)) - o1);
-  r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, and_or(w, 0x00F000F0u, 0x64006400u)) - o16);
-  r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, and_or(w8, 0x000F000Fu, 0x64006400u)) - o1);
-  r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, and_or(w8, 0x00F000F0u, 0x64006400u)) - o16);
+  r.x = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, and_or(w, 0x000F000Fu, 0x64006400u)) - o1) * s2);
+  r.y = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, and_or(w >> 4, 0x000F000Fu, 0x64006400u)) - o1) * s2);
+  r.z = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, and_or(w >> 8, 0x000F000Fu, 0x64006400u)) - o1) * s2);
+  r.w = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, and_or(w >> 12, 0x000F000Fu, 0x64006400u)) - o1) * s2);
   return r;
 }
 
@@ -174,10 +217,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 __device__ __forceinline__ void dma4(rsrc_t r, uint32_t voffset, uint32_t soffset, void* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, voffset,
-                                           soffset, 0, 0);
-}
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voffset, uint32_t soffset, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voffset,
                                            soffset, 0, 0);
 }
 
@@ -256,8 +295,7 @@ struct TiledShape {
   static constexpr int W_B = BN * kRowBytes;              // one dequantized weight tile
   static constexpr int OFF_S = DS * CODE_B;
   static constexpr int OFF_W = OFF_S + DS * SCALE_B;
-  static constexpr int OFF_SB = OFF_W + 2 * W_B;
-  static constexpr int LDS_B = (OFF_SB + 2 * BN * 4 > BT * BN * 2) ? OFF_SB + 2 * BN * 4 : BT * BN * 2;
+  static constexpr int LDS_B = (OFF_W + 2 * W_B > BT * BN * 2) ? OFF_W + 2 * W_B : BT * BN * 2;
   static_assert(BN * 8 % NT == 0, "code tiles must split evenly over the threads");
   static_assert(NT >= BN, "one scale per row needs a thread per row");
   static_assert(LDS_B <= 160 * 1024, "LDS budget");
@@ -266,7 +304,7 @@ struct TiledShape {
 
 template <int NS, int TS, int WN, int WT>
 __global__ void __launch_bounds__(64 * WN * WT)
-tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
+tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, const int* __restrict__ rexp,
              const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
              uint16_t* __restrict__ y, int N, int K, int T, int Tpad, int tiles_n, int tiles_t) {
   using Sh = TiledShape<NS, TS, WN, WT>;
@@ -313,8 +351,21 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
                               (uint32_t)min((int64_t)(N - n0) * G * 2 + 4, (int64_t)0x7FFFFFFF));
   const uint32_t s_lane = (uint32_t)(s_first - s_base) + (uint32_t)(min(tid % BN, N - 1 - n0) * G * 2);
   const uint32_t soff0 = s_lane & ~3u, soff1 = (s_lane + 2) & ~3u;
-  const int s_row = tid % BN;
-  const bool s_odd_lane = (s_lane & 2) != 0;           // even groups sit in the high half
+  // Code dword c of this thread belongs to tile row (c * NT + tid) / 8, whose
+  // scale sits in the dword loaded by the thread of that number, in its high
+  // half when (the scale's byte offset) / 2 is odd.  s_sel[c] is the byte
+  // selector that copies the row's scale of an even group into both halves;
+  // odd groups sit in the other half (selector ^ 0x02020202).  s_mul[c] is
+  // the float16 pair (2^c[row], 2^c[row]).
+  uint32_t s_sel[CD], s_mul[CD];
+#pragma unroll
+  for (int c = 0; c < CD; ++c) {
+    const int r = min((c * NT + tid) >> 3, N - 1 - n0);
+    const bool hi = ((((uint32_t)(s_first - s_base) >> 1) + (uint32_t)r * (uint32_t)G) & 1u) != 0;
+    s_sel[c] = hi ? 0x03020302u : 0x01000100u;
+    const uint32_t h = (uint32_t)(rexp[n0 + r] + 15) << 10;
+    s_mul[c] = h | (h << 16);
+  }
   // Activation fragment (ts, m) of lane (li, lh): 16 bytes of token block
   // tb0 + wt*TS + ts, group g, at ((m*2 + lh)*32 + li)*16 of its 4 KB block.
   const uint8_t* x16_tile = reinterpret_cast<const uint8_t*>(x16) + (size_t)tb0 * G * 4096;
@@ -329,7 +380,6 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
   // g & 1 holds group g.  All in AGPRs, filled by untracked loads.
   f16x8_t act[DS][TS][4];
   f16x8_t wgt[2][NS][4];
-  float scl[2][NS];
 
   // --- one batch: codes and scales of group gc into code slot gc % DS, and
   // this wave's activation fragments of group ga into set A (indexes clamped
@@ -356,39 +406,41 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
   const int dq_off = (tid >> 3) * kRowBytes + (tid & 7) * 16;   // + c*(NT/8)*kRowBytes
   struct DqRegs {
     uint32_t w[CD];
-    uint32_t sw;
+    uint32_t sw[CD];
   };
   auto dq_load = [&](int g, DqRegs& d) __device__ {
     const uint8_t* cs = lds + (g % DS) * Sh::CODE_B + tid * 4;
+    const uint8_t* ss = lds + Sh::OFF_S + (g % DS) * Sh::SCALE_B + (tid >> 3) * 4;
 #pragma unroll
-    for (int c = 0; c < CD; ++c) d.w[c] = *reinterpret_cast<const uint32_t*>(cs + c * NT * 4);
-    d.sw = *reinterpret_cast<const uint32_t*>(lds + Sh::OFF_S + (g % DS) * Sh::SCALE_B + tid * 4);
+    for (int c = 0; c < CD; ++c) {
+      d.w[c] = *reinterpret_cast<const uint32_t*>(cs + c * NT * 4);
+      d.sw[c] = *reinterpret_cast<const uint32_t*>(ss + c * (NT / 8) * 4);
+    }
   };
-  auto dq_store = [&](int g, int b, const DqRegs& d) __device__ {
+  // Group g (of parity ODD) into weight tile b with the scales s' = s 2^c[row]
+  // (exact unless s lies 2^25 or more below the row's largest scale); groups
+  // past the end get s' = 0 (the clamped loads repeat the last group).
+  auto dq_store = [&](int g, int b, const DqRegs& d, auto odd) __device__ {
     uint8_t* wb = lds + Sh::OFF_W + b * Sh::W_B + dq_off;
 #pragma unroll
-    for (int c = 0; c < CD; ++c) *reinterpret_cast<u32x4_t*>(wb + c * (NT / 8) * kRowBytes) = dequant_dword(d.w[c]);
-    // Every thread converts the scale it loaded (row tid % BN); threads past
-    // BN write the same value as thread tid % BN, so no branch is needed.
-    const bool hi = s_odd_lane != ((g & 1) != 0);
-    reinterpret_cast<float*>(lds + Sh::OFF_SB)[b * BN + s_row] =
-        f16_bits_to_f32((uint16_t)(hi ? (d.sw >> 16) : (d.sw & 0xFFFFu)));
+    for (int c = 0; c < CD; ++c) {
+      const uint32_t sel = decltype(odd)::value ? (s_sel[c] ^ 0x02020202u) : s_sel[c];
+      const f16x2_t s2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(d.sw[c], d.sw[c], sel));
+      uint32_t sp = __builtin_bit_cast(uint32_t, s2 * __builtin_bit_cast(f16x2_t, s_mul[c]));
+      sp = g < G ? sp : 0u;
+      *reinterpret_cast<u32x4_t*>(wb + c * (NT / 8) * kRowBytes) = dequant_dword(d.w[c], sp);
+    }
   };
 
   // --- weight fragments and scales of group g (tile g & 1) --------------------
   const int b_row = wn * NS * 32 + li;                                  // + ns*32
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
-  auto read_wgt = [&](int g, f16x8_t (&b)[NS][4], float (&sc)[NS]) __device__ {
+  auto read_wgt = [&](int g, f16x8_t (&b)[NS][4]) __device__ {
     const uint32_t wb = lds_base + (uint32_t)(Sh::OFF_W + (g & 1) * Sh::W_B + b_row * kRowBytes + lh * 64);
     static_for<NS * 4>([&](auto i) {
       constexpr int ns = decltype(i)::value / 4, m = decltype(i)::value % 4;
       lds_read_agpr<ns * 32 * kRowBytes + m * 16>(b[ns][m], wb);
     });
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      const float v = reinterpret_cast<const float*>(lds + Sh::OFF_SB)[(g & 1) * BN + b_row + ns * 32];
-      sc[ns] = g < G ? v : 0.0f;  // groups past the end count zero
-    }
   };
 
   f32x16_t acc[TS][NS];
@@ -410,18 +462,14 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Step g (SL = g % DS).  The products p hold group g-1's on entry: each
-  // chain's product is scaled into the accumulators (scales sp) just before
-  // the chain's first matrix-core instruction of group g overwrites it.  After
-  // the barrier: read the code dwords of group g+2 (their LDS latency then
-  // hides behind the matrix cores), issue the batch (codes of g+DCODE,
-  // activations of g+DACT), issue group g+1's weight reads, then the
-  // matrix-core instructions interleaved with the scaling and the
-  // dequantization of group g+2.  Past the last group the reads and the
-  // dequantization touch stale LDS (unused) and the loads repeat the last
-  // group, so the step is one basic block.
-  f32x16_t p[TS][NS];
-  float sp[NS];
+  // Step g (SL = g % DS, so g + 2 has the parity of SL).  After the barrier:
+  // read the code and scale dwords of group g+2 (their LDS latency then hides
+  // behind the matrix cores), issue the batch (codes of g+DCODE, activations
+  // of g+DACT), issue group g+1's weight reads, then group g's matrix-core
+  // instructions interleaved with the dequantization of group g+2.  Past the
+  // last group the reads and the dequantization touch stale LDS (unused) and
+  // the loads repeat the last group, so the step is one basic block.
+  constexpr int kValuPerMfma = (CD * 18 + 4 * TS * NS - 1) / (4 * TS * NS);
   auto step = [&](int g, auto slot) __device__ {
     constexpr int SL = decltype(slot)::value;
     sync();
@@ -429,29 +477,21 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
     dq_load(g + 2, d);
     issue_codes(g + DCODE);
     issue_act(g + DACT, act[(SL + DACT) % DS]);
-    read_wgt(g + 1, wgt[(SL + 1) & 1], scl[(SL + 1) & 1]);
+    read_wgt(g + 1, wgt[(SL + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-          if (m == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[ts][ns][r] = __builtin_fmaf(sp[ns], p[ts][ns][r], acc[ts][ns][r]);
-            p[ts][ns] = f32x16_t{};
-          }
-          p[ts][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(act[SL][ts][m], wgt[SL & 1][ns][m], p[ts][ns], 0, 0, 0);
-        }
-    dq_store(g + 2, g & 1, d);
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) sp[ns] = scl[SL & 1][ns];
+        for (int ns = 0; ns < NS; ++ns)
+          acc[ts][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(act[SL][ts][m], wgt[SL & 1][ns][m], acc[ts][ns], 0, 0, 0);
+    dq_store(g + 2, g & 1, d, std::integral_constant<bool, (SL & 1) != 0>{});
     // one matrix-core instruction, then a share of the VALU work
 #pragma unroll
     for (int i = 0; i < 4 * TS * NS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);   // VALU
     }
   };
 
@@ -466,46 +506,36 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
   issue_act(0, act[0]);
   issue_act(1, act[1]);
   issue_act(2, act[2]);
+  // A thread dequantizes its own code dwords but reads row scales that other
+  // waves loaded: a barrier after the waits publishes them, and a second one
+  // (which also publishes the weight tiles) orders every read of slot 0
+  // before the load of group DS into it.
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   {
     DqRegs d;
     dq_load(0, d);
-    dq_store(0, 0, d);
+    dq_store(0, 0, d, std::false_type{});
     dq_load(1, d);
-    dq_store(1, 1, d);
+    dq_store(1, 1, d, std::true_type{});
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  issue_codes(DS);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_wgt(0, wgt[0], scl[0]);
-  // The first step scales an all-zero "group -1".
-#pragma unroll
-  for (int ts = 0; ts < TS; ++ts)
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) p[ts][ns] = f32x16_t{};
-#pragma unroll
-  for (int ns = 0; ns < NS; ++ns) sp[ns] = 0.0f;
+  issue_codes(DS);
+  read_wgt(0, wgt[0]);
   // Steps run in fours (the register sets cycle with period four); up to
-  // three steps past the last group run on clamped, finite data with zero
-  // scales and so add exactly nothing.  (A tail of conditional steps would
-  // keep extra copies of the operand registers live.)
+  // three steps past the last group run on clamped, finite activations with
+  // zero weights and so add exactly nothing.  (A tail of conditional steps
+  // would keep extra copies of the operand registers live.)
   for (int g = 0; g < G; g += DS) {
     step(g, Slot<0>{});
     step(g + 1, Slot<1>{});
     step(g + 2, Slot<2>{});
     step(g + 3, Slot<3>{});
   }
-  // the last group's products
-#pragma unroll
-  for (int ts = 0; ts < TS; ++ts)
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[ts][ns][r] = __builtin_fmaf(sp[ns], p[ts][ns][r], acc[ts][ns][r]);
   // no load may still write this workgroup's LDS or registers after this
   wait_vm<0>();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -515,6 +545,9 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
   // go through LDS ([token][row] order), so that the stores to y are whole
   // 16-byte pieces of token rows.
   static_assert(BT * BN * 2 <= Sh::LDS_B, "output tile must fit the LDS");
+  int ce[NS];
+#pragma unroll
+  for (int ns = 0; ns < NS; ++ns) ce[ns] = rexp[min(n0 + (wn * NS + ns) * 32 + li, N - 1)];
   __syncthreads();
   uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
@@ -528,7 +561,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns)
         otile[(tl + 8 * (r >> 2) + (r & 3)) * BN + (wn * NS + ns) * 32 + li] =
-            f32_to_bf16_rne(__builtin_ldexpf(acc[ts][ns][r], e[r]));
+            f32_to_bf16_rne(__builtin_ldexpf(acc[ts][ns][r], e[r] - ce[ns]));
   }
   __syncthreads();
   const int t0 = 32 * tb0;
@@ -549,7 +582,8 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp,
 }
 
 template <int NS, int TS, int WN, int WT>
-hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, int tpad, hipStream_t stream) {
+hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, const int* rexp, int tpad,
+                      hipStream_t stream) {
   using Sh = TiledShape<NS, TS, WN, WT>;
   const int tiles_n = (int)((a.n + Sh::BN - 1) / Sh::BN);
   const int tiles_t = (int)((a.t + Sh::BT - 1) / Sh::BT);
@@ -558,7 +592,7 @@ hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, i
                                      hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS_B);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)(tiles_n * tiles_t)), dim3(Sh::NT), Sh::LDS_B, stream>>>(
-      x16, texp, static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
+      x16, texp, rexp, static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
       static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t);
   return hipGetLastError();
 }
@@ -569,9 +603,11 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int64_t tiled_tpad(int64_t t) { return (t + 31) / 32 * 32; }
 
-size_t tiled_workspace_bytes(int64_t k, int64_t t) {
+// Workspace: float16 activations in tile order, then the token exponents,
+// then the row exponents.
+size_t tiled_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   const int64_t tp = tiled_tpad(t);
-  return align256((size_t)(tp * k * 2)) + align256((size_t)(tp * 4));
+  return align256((size_t)(tp * k * 2)) + align256((size_t)(tp * 4)) + align256((size_t)(n * 4));
 }
 
 TiledConfig tiled_pick_config(int64_t n, int64_t k, int64_t t) {
@@ -586,11 +622,14 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   const int64_t tp = tiled_tpad(a.t);
   u32x4_t* x16 = static_cast<u32x4_t*>(a.workspace);
   int* texp = reinterpret_cast<int*>(static_cast<uint8_t*>(a.workspace) + align256((size_t)(tp * a.k * 2)));
+  int* rexp = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(texp) + align256((size_t)(tp * 4)));
   {
     const u32x4_t* x = static_cast<const u32x4_t*>(a.x);
-    int k = (int)a.k, t = (int)a.t, tpad = (int)tp;
-    prep_exp_kernel<<<dim3((unsigned)((tp + kExpWaves - 1) / kExpWaves)), dim3(64 * kExpWaves), 0, stream>>>(x, k, t, tpad,
-                                                                                                          texp);
+    int k = (int)a.k, t = (int)a.t, n = (int)a.n, tpad = (int)tp;
+    const int tok_blocks = (int)((tp + kExpWaves - 1) / kExpWaves);
+    const int row_blocks = (int)((a.n + kRowsPerBlock - 1) / kRowsPerBlock);
+    prep_exp_kernel<<<dim3((unsigned)(tok_blocks + row_blocks)), dim3(64 * kExpWaves), 0, stream>>>(
+        x, k, t, tpad, texp, static_cast<const uint16_t*>(a.scales), n, rexp, tok_blocks);
     prep_pack_kernel<<<dim3((unsigned)(tp / 32), (unsigned)((a.k / 64 + kPackGroups - 1) / kPackGroups)), dim3(256), 0,
                        stream>>>(x, k, t, texp, x16);
     hipError_t e = hipGetLastError();
@@ -598,9 +637,9 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   }
   const int tpad = (int)tp;
   const TiledConfig c = a.cfg;
-  if (c.ns == 3 && c.ts == 2 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 2, 2, 2>(a, x16, texp, tpad, stream);
-  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 4) return launch_cfg<1, 1, 1, 4>(a, x16, texp, tpad, stream);
-  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 1) return launch_cfg<1, 1, 1, 1>(a, x16, texp, tpad, stream);
+  if (c.ns == 3 && c.ts == 2 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 2, 2, 2>(a, x16, texp, rexp, tpad, stream);
+  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 4) return launch_cfg<1, 1, 1, 4>(a, x16, texp, rexp, tpad, stream);
+  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 1) return launch_cfg<1, 1, 1, 1>(a, x16, texp, rexp, tpad, stream);
   return hipErrorInvalidValue;
 }
 
