@@ -100,83 +100,85 @@ __device__ void row_exponents(const uint16_t* __restrict__ scales, int N, int G,
   }
 }
 
-// Per-token exponent e[t]: the token's largest magnitude times 2^-e lies in
-// [2^14, 2^15), so every bf16 value within 2^34 of it converts to float16
-// exactly; 0 for all-zero and padding tokens.  One wave per token; the blocks
+// Per-token exponent e[t] from the token's largest magnitude m (bf16 bits
+// without sign): m * 2^-e lies in [2^14, 2^15), so every bf16 value within
+// 2^34 of it converts to float16 exactly; 0 for an all-zero token.
+__device__ __forceinline__ int token_exponent(uint32_t m) {
+  if (m >= 0x7F80u) m = 0x7F7Fu;  // Inf/NaN inputs are outside the contract
+  if (m == 0u) return 0;
+  return ((m >= 0x80u) ? (int)(m >> 7) - 127 : (31 - __builtin_clz(m)) - 133) - 14;
+}
+
+// Piece p (values k = 8p .. 8p+7, in pair order) of token t into the tile
+// order described above.
+__device__ __forceinline__ void store_piece(u32x4_t* __restrict__ x16, int G, int t, int p, u32x4_t v) {
+  const int g = p >> 3, kb = p & 7;
+  x16[((size_t)(t >> 5) * G + g) * 256 + ((kb & 3) * 2 + (kb >> 2)) * 32 + (t & 31)] = v;
+}
+
+// Activation preparation, one pass: one wave per token of the padded token
+// range loads the token's values (16-byte pieces), takes the largest
+// magnitude, picks e[t] and writes the float16 values in tile order; padding
+// tokens write zeros.  Rows of up to 8192 values stay in registers between
+// the two steps; longer rows are read a second time (from L2).  The blocks
 // past the token blocks compute the row exponents.
-constexpr int kExpWaves = 4;
-__global__ void __launch_bounds__(64 * kExpWaves)
-prep_exp_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __restrict__ texp,
-                const uint16_t* __restrict__ scales, int N, int* __restrict__ rexp, int tok_blocks) {
+constexpr int kPrepWaves = 4;
+constexpr int kPieces = 16;
+__global__ void __launch_bounds__(64 * kPrepWaves)
+prep_act_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __restrict__ texp,
+                u32x4_t* __restrict__ x16, const uint16_t* __restrict__ scales, int N, int* __restrict__ rexp,
+                int tok_blocks) {
   if ((int)blockIdx.x >= tok_blocks) {
     row_exponents(scales, N, K >> 6, ((int)blockIdx.x - tok_blocks) * kRowsPerBlock, rexp);
     return;
   }
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kExpWaves + (threadIdx.x >> 6);
+  const int t = blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
   if (t >= Tpad) return;
+  const int nb = K >> 3, G = K >> 6;
+  if (t >= T) {
+    for (int p = lane; p < nb; p += 64) store_piece(x16, G, t, p, u32x4_t{0u, 0u, 0u, 0u});
+    if (lane == 0) texp[t] = 0;
+    return;
+  }
+  const u32x4_t* xt = x + (size_t)t * nb;
   uint32_t m = 0;
-  if (t < T) {
-    const int nb = K >> 3;
-    const u32x4_t* xt = x + (size_t)t * nb;
-    // sixteen independent loads in flight per lane (clamped, so no load is
-    // conditional: a load behind a branch would be waited for on its own)
-    for (int b0 = 0; b0 < nb; b0 += 1024) {
-      u32x4_t v[16];
+  int e;
+  // all loads of a round first, from clamped (valid) addresses: a load
+  // behind a branch would be waited for on its own
+  if (nb <= 64 * kPieces) {
+    u32x4_t v[kPieces];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = xt[min(b0 + lane + 64 * j, nb - 1)];
+    for (int j = 0; j < kPieces; ++j) v[j] = xt[min(lane + 64 * j, nb - 1)];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) m = max(m, max_mag8(v[j]));
+    for (int j = 0; j < kPieces; ++j) m = max(m, max_mag8(v[j]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    e = token_exponent(m);
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j)
+      if (lane + 64 * j < nb) store_piece(x16, G, t, lane + 64 * j, to_f16_pairs(v[j], e));
+  } else {
+    for (int b0 = 0; b0 < nb; b0 += 64 * kPieces) {
+      u32x4_t v[kPieces];
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j) v[j] = xt[min(b0 + lane + 64 * j, nb - 1)];
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j) m = max(m, max_mag8(v[j]));
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    e = token_exponent(m);
+    for (int b0 = 0; b0 < nb; b0 += 64 * kPieces) {
+      u32x4_t v[kPieces];
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j) v[j] = xt[min(b0 + lane + 64 * j, nb - 1)];
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j)
+        if (b0 + lane + 64 * j < nb) store_piece(x16, G, t, b0 + lane + 64 * j, to_f16_pairs(v[j], e));
+    }
   }
-  if (m >= 0x7F80u) m = 0x7F7Fu;  // Inf/NaN inputs are outside the contract
-  int e = 0;
-  if (m != 0u) e = ((m >= 0x80u) ? (int)(m >> 7) - 127 : (31 - __builtin_clz(m)) - 133) - 14;
   if (lane == 0) texp[t] = e;
-}
-
-// Float16 activations in tile order: one workgroup per (token block, eight
-// groups).  Reads are 128-byte runs of token rows, the LDS holds the 32 KB
-// chunk in tile order, and the writes are contiguous.  Padding tokens and
-// groups past the end give zeros / are skipped.
-constexpr int kPackGroups = 8;
-__global__ void __launch_bounds__(256)
-prep_pack_kernel(const u32x4_t* __restrict__ x, int K, int T, const int* __restrict__ texp,
-                 u32x4_t* __restrict__ x16) {
-  __shared__ u32x4_t tile[kPackGroups * 256];
-  const int G = K >> 6, nb = K >> 3;
-  const int tb = blockIdx.x, g0 = blockIdx.y * kPackGroups;
-  const int tid = threadIdx.x;
-  // All loads first, from clamped (valid) addresses; out-of-range values are
-  // zeroed afterwards.
-  u32x4_t v[kPackGroups];
-  int ev[kPackGroups];
-#pragma unroll
-  for (int j = 0; j < kPackGroups; ++j) {
-    const int u = j * 256 + tid;
-    const int kb = u & 7, ilo = (u >> 3) & 7, gl = (u >> 6) & 7, ihi = u >> 9;
-    const int t = min(tb * 32 + ihi * 8 + ilo, T - 1), g = min(g0 + gl, G - 1);
-    v[j] = x[(size_t)t * nb + g * 8 + kb];
-    ev[j] = texp[t];
-  }
-#pragma unroll
-  for (int j = 0; j < kPackGroups; ++j) {
-    const int u = j * 256 + tid;
-    const int kb = u & 7, ilo = (u >> 3) & 7, gl = (u >> 6) & 7, ihi = u >> 9;
-    const int i = ihi * 8 + ilo;
-    const bool ok = tb * 32 + i < T && g0 + gl < G;
-    tile[gl * 256 + ((kb & 3) * 2 + (kb >> 2)) * 32 + i] = ok ? to_f16_pairs(v[j], ev[j]) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-  __syncthreads();
-  const int ng = min(kPackGroups, G - g0);
-  u32x4_t* dst = x16 + ((size_t)tb * G + g0) * 256;
-#pragma unroll
-  for (int j = 0; j < kPackGroups; ++j) {
-    const int u = j * 256 + tid;
-    if ((u >> 8) < ng) dst[u] = tile[u];
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -229,14 +231,22 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
 }
 
+// s_waitcnt lgkmcnt(0) as a builtin, which the compiler's own counter
+// tracking sees (an inline-asm wait is opaque to it, and it would then add
+// waits of its own that count only the loads it knows).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4)); }
+
 // 16-byte LDS read into accumulation registers (AGPRs), which the matrix
 // cores read as operands directly: a wave's next-group operands wait there
 // while its current ones (in the other AGPR set) are in use, without taking
 // ordinary VGPRs.  The compiler does not track this load: the caller waits
-// (s_waitcnt lgkmcnt) before the registers are read.
+// (s_waitcnt lgkmcnt) before the registers are read.  The destination is
+// also an input ("+a"), so it stays the register set's own: the compiler may
+// not place it over an operand of a matrix-core instruction issued just
+// before, which could still be reading it when the load returns.
 template <int OFF>
 __device__ __forceinline__ void lds_read_agpr(f16x8_t& v, uint32_t addr) {
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=a"(v) : "v"(addr), "i"(OFF));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "+a"(v) : "v"(addr), "i"(OFF));
 }
 
 // A dequantized weight tile holds 144 bytes per row: the row's 64 float16
@@ -247,10 +257,10 @@ constexpr int kRowBytes = 144;
 // 16-byte buffer load into accumulation registers (AGPRs): the activation
 // fragments go straight from memory (L2) to the registers the matrix cores
 // read.  The compiler does not track this load either: the caller waits
-// (s_waitcnt vmcnt) before the registers are read.
+// (s_waitcnt vmcnt) before the registers are read.  "+a" as above.
 template <int OFF>
 __device__ __forceinline__ void buf_read_agpr(f16x8_t& v, u32x4_t rsrc, uint32_t voff, uint32_t soff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4" : "=a"(v) : "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF));
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4" : "+a"(v) : "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF));
 }
 
 // Buffer resource for the raw (stride 0) byte range [base, base + bytes),
@@ -277,10 +287,18 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Ring geometry.  Codes and scales stream through an LDS ring of DS slots,
 // loaded DS+1 groups ahead (a group's codes are dequantized two groups
 // before its products); each wave's activation fragments stream through a
-// ring of DS register sets, loaded DS-1 groups ahead.
-constexpr int DS = 4;
+// ring of DA register sets, loaded DA-1 groups ahead.  Before step g the
+// loads of group g's activations and group g+2's codes must have landed;
+// the NB = min(DS-2, DA-1) batches issued after the older of the two may
+// still be in flight.  The step code is unrolled over P steps, after which
+// every ring index repeats.
+constexpr int DS = 5;
+constexpr int DA = 5;
 constexpr int DCODE = DS + 1;
-constexpr int DACT = DS - 1;
+constexpr int DACT = DA - 1;
+constexpr int NB = (DS - 2 < DA - 1) ? DS - 2 : DA - 1;
+constexpr int P = 10;
+static_assert(P % DS == 0 && P % DA == 0 && P % 2 == 0, "the unrolled steps must cover every ring period");
 
 template <int NS, int TS, int WN, int WT>
 struct TiledShape {
@@ -299,7 +317,7 @@ struct TiledShape {
   static_assert(BN * 8 % NT == 0, "code tiles must split evenly over the threads");
   static_assert(NT >= BN, "one scale per row needs a thread per row");
   static_assert(LDS_B <= 160 * 1024, "LDS budget");
-  static_assert((DS - 2) * L <= 63, "the load counter holds 63");
+  static_assert(NB * L <= 63, "the load counter holds 63");
 };
 
 template <int NS, int TS, int WN, int WT>
@@ -318,13 +336,28 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   const int li = lane & 31, lh = lane >> 5;
   const int wn = wave % WN, wt = wave / WN;
 
-  // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
-  // give each XCD a contiguous run of tiles (same token tile, neighbouring row
-  // tiles) and let its L2 keep that activation tile.
+  // XCD-aware tile order.  Workgroups are dealt round-robin to the 8 XCDs,
+  // each with its own L2.  Where the tile grid allows, the grid is cut into a
+  // 4 x 2 (rows x tokens) block per XCD, so that each XCD's L2 fetches a
+  // quarter of W and half of the activations (W would otherwise be fetched by
+  // every XCD); else each XCD takes a contiguous run of tiles.  Inside an XCD
+  // the row tile varies fastest, so that workgroups close in time share an
+  // activation tile.
   const int nblk = tiles_n * tiles_t;
-  int lin = blockIdx.x;
-  if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-  const int tile_t = lin / tiles_n, tile_n = lin - tile_t * tiles_n;
+  int tile_t, tile_n;
+  {
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    if ((tiles_n & 3) == 0 && (tiles_t & 1) == 0) {
+      const int bn = tiles_n >> 2, bt = tiles_t >> 1;
+      const int lt = idx / bn;
+      tile_t = (xcd >> 2) * bt + lt;
+      tile_n = (xcd & 3) * bn + (idx - lt * bn);
+    } else {
+      const int lin = (nblk & 7) == 0 ? xcd * (nblk >> 3) + idx : (int)blockIdx.x;
+      tile_t = lin / tiles_n;
+      tile_n = lin - tile_t * tiles_n;
+    }
+  }
   const int n0 = tile_n * BN;
   const int tb0 = tile_t * (BT / 32);                 // first 32-token block
   const int tb_last = Tpad / 32 - 1;
@@ -376,28 +409,35 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     aoff[ts] = (uint32_t)(min(wt * TS + ts, tb_last - tb0) * G * 4096 + (lh * 32 + li) * 16);
 
   // --- the matrix-core operand registers --------------------------------------
-  // Activations: DS sets, set g % DS holds group g.  Weights: two sets, set
+  // Activations: DA sets, set g % DA holds group g.  Weights: two sets, set
   // g & 1 holds group g.  All in AGPRs, filled by untracked loads.
-  f16x8_t act[DS][TS][4];
+  f16x8_t act[DA][TS][4];
   f16x8_t wgt[2][NS][4];
 
   // --- one batch: codes and scales of group gc into code slot gc % DS, and
   // this wave's activation fragments of group ga into set A (indexes clamped
   // to the last group, so every batch has the same number of loads) --------
+  // Load v of a batch: v < CD a code dword, v == CD the scale dword, then
+  // the TS * 4 activation fragments.
+  constexpr int NV = CD + 1 + TS * 4;
+  auto issue_one = [&](int gc, int ga, f16x8_t (&a)[TS][4], auto vi) __device__ {
+    constexpr int v = decltype(vi)::value;
+    if constexpr (v < CD) {
+      dma4(rc, coff[v], (uint32_t)gc * 32, lds + (gc % DS) * Sh::CODE_B + v * NT * 4 + wave * 256);
+    } else if constexpr (v == CD) {
+      dma4(rs, (gc & 1) ? soff1 : soff0, (uint32_t)(gc >> 1) * 4, lds + Sh::OFF_S + (gc % DS) * Sh::SCALE_B + wave * 256);
+    } else {
+      constexpr int i = v - CD - 1, ts = i / 4, m = i % 4;
+      buf_read_agpr<m * 1024>(a[ts][m], rx, aoff[ts], (uint32_t)ga * 4096);
+    }
+  };
   auto issue_codes = [&](int gc) __device__ {
     gc = min(gc, G - 1);
-    const int cs = gc % DS;
-#pragma unroll
-    for (int c = 0; c < CD; ++c)
-      dma4(rc, coff[c], (uint32_t)gc * 32, lds + cs * Sh::CODE_B + c * NT * 4 + wave * 256);
-    dma4(rs, (gc & 1) ? soff1 : soff0, (uint32_t)(gc >> 1) * 4, lds + Sh::OFF_S + cs * Sh::SCALE_B + wave * 256);
+    static_for<CD + 1>([&](auto v) { issue_one(gc, 0, act[0], v); });
   };
   auto issue_act = [&](int ga, f16x8_t (&a)[TS][4]) __device__ {
-    const uint32_t so = (uint32_t)min(ga, G - 1) * 4096;
-    static_for<TS * 4>([&](auto i) {
-      constexpr int ts = decltype(i)::value / 4, m = decltype(i)::value % 4;
-      buf_read_agpr<m * 1024>(a[ts][m], rx, aoff[ts], so);
-    });
+    ga = min(ga, G - 1);
+    static_for<TS * 4>([&](auto i) { issue_one(0, ga, a, Slot<CD + 1 + decltype(i)::value>{}); });
   };
 
   // --- dequantization of group g into weight tile b, in two halves: the LDS
@@ -420,27 +460,29 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // Group g (of parity ODD) into weight tile b with the scales s' = s 2^c[row]
   // (exact unless s lies 2^25 or more below the row's largest scale); groups
   // past the end get s' = 0 (the clamped loads repeat the last group).
-  auto dq_store = [&](int g, int b, const DqRegs& d, auto odd) __device__ {
+  auto dq_store_one = [&](int g, int b, const DqRegs& d, auto odd, int c) __device__ {
     uint8_t* wb = lds + Sh::OFF_W + b * Sh::W_B + dq_off;
+    const uint32_t sel = decltype(odd)::value ? (s_sel[c] ^ 0x02020202u) : s_sel[c];
+    const f16x2_t s2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(d.sw[c], d.sw[c], sel));
+    uint32_t sp = __builtin_bit_cast(uint32_t, s2 * __builtin_bit_cast(f16x2_t, s_mul[c]));
+    sp = g < G ? sp : 0u;
+    *reinterpret_cast<u32x4_t*>(wb + c * (NT / 8) * kRowBytes) = dequant_dword(d.w[c], sp);
+  };
+  auto dq_store = [&](int g, int b, const DqRegs& d, auto odd) __device__ {
 #pragma unroll
-    for (int c = 0; c < CD; ++c) {
-      const uint32_t sel = decltype(odd)::value ? (s_sel[c] ^ 0x02020202u) : s_sel[c];
-      const f16x2_t s2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(d.sw[c], d.sw[c], sel));
-      uint32_t sp = __builtin_bit_cast(uint32_t, s2 * __builtin_bit_cast(f16x2_t, s_mul[c]));
-      sp = g < G ? sp : 0u;
-      *reinterpret_cast<u32x4_t*>(wb + c * (NT / 8) * kRowBytes) = dequant_dword(d.w[c], sp);
-    }
+    for (int c = 0; c < CD; ++c) dq_store_one(g, b, d, odd, c);
   };
 
   // --- weight fragments and scales of group g (tile g & 1) --------------------
   const int b_row = wn * NS * 32 + li;                                  // + ns*32
   const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
-  auto read_wgt = [&](int g, f16x8_t (&b)[NS][4]) __device__ {
+  auto read_wgt_one = [&](int g, f16x8_t (&b)[NS][4], auto ii) __device__ {
+    constexpr int ns = decltype(ii)::value / 4, m = decltype(ii)::value % 4;
     const uint32_t wb = lds_base + (uint32_t)(Sh::OFF_W + (g & 1) * Sh::W_B + b_row * kRowBytes + lh * 64);
-    static_for<NS * 4>([&](auto i) {
-      constexpr int ns = decltype(i)::value / 4, m = decltype(i)::value % 4;
-      lds_read_agpr<ns * 32 * kRowBytes + m * 16>(b[ns][m], wb);
-    });
+    lds_read_agpr<ns * 32 * kRowBytes + m * 16>(b[ns][m], wb);
+  };
+  auto read_wgt = [&](int g, f16x8_t (&b)[NS][4]) __device__ {
+    static_for<NS * 4>([&](auto i) { read_wgt_one(g, b, i); });
   };
 
   f32x16_t acc[TS][NS];
@@ -456,56 +498,77 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // LDS reads and writes (also the untracked weight reads) are done.
   auto sync = [&]() __device__ {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<(DS - 2) * L>();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wait_vm<NB * L>();
+    wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Step g (SL = g % DS, so g + 2 has the parity of SL).  After the barrier:
-  // read the code and scale dwords of group g+2 (their LDS latency then hides
-  // behind the matrix cores), issue the batch (codes of g+DCODE, activations
-  // of g+DACT), issue group g+1's weight reads, then group g's matrix-core
-  // instructions interleaved with the dequantization of group g+2.  Past the
-  // last group the reads and the dequantization touch stale LDS (unused) and
-  // the loads repeat the last group, so the step is one basic block.
-  constexpr int kValuPerMfma = (CD * 18 + 4 * TS * NS - 1) / (4 * TS * NS);
+  // Step g (SL = g % DS, so g + 2 has the parity of SL).  The memory and
+  // VALU work is spread between the matrix-core instructions, so that one
+  // wave per SIMD keeps the matrix core, the load path, the LDS and the VALU
+  // busy at once:
+  //   * after the barrier, read the code and scale dwords of group g+2;
+  //   * k-slice 0 of group g's products (no LDS data needed), each
+  //     instruction followed by its share of the batch's loads (codes of
+  //     g+DCODE, activations of g+DACT);
+  //   * wait for the dword reads;
+  //   * k-slices 1-3, each led by a third of group g+1's weight reads
+  //     (untracked loads, issued after the wait so that no wait of the
+  //     compiler counts them) and interleaved with the dequantization of a
+  //     third of this thread's dwords of group g+2.
+  // Past the last group the reads and the dequantization touch stale LDS
+  // (unused) and the loads repeat the last group, so the step is one basic
+  // block.
+  constexpr int NM = TS * NS;               // matrix-core instructions per k-slice
+  auto mfma_one = [&](int m, int j, auto slot) __device__ {
+    constexpr int SL = decltype(slot)::value;
+    const int ts = j / NS, ns = j % NS;
+    acc[ts][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(act[SL % DA][ts][m], wgt[SL & 1][ns][m], acc[ts][ns], 0, 0, 0);
+  };
   auto step = [&](int g, auto slot) __device__ {
     constexpr int SL = decltype(slot)::value;
     sync();
     DqRegs d;
     dq_load(g + 2, d);
-    issue_codes(g + DCODE);
-    issue_act(g + DACT, act[(SL + DACT) % DS]);
-    read_wgt(g + 1, wgt[(SL + 1) & 1]);
+    const int gc = min(g + DCODE, G - 1), ga = min(g + DACT, G - 1);
     __builtin_amdgcn_sched_barrier(0);
+    static_for<NM>([&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      mfma_one(0, j, slot);
+      static_for<(j + 1) * NV / NM - j * NV / NM>([&](auto u) {
+        issue_one(gc, ga, act[(SL + DACT) % DA], Slot<j * NV / NM + decltype(u)::value>{});
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    wait_lgkm0();
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<3>([&](auto ss) {
+      constexpr int sl = decltype(ss)::value;
+      constexpr int r0 = sl * NS * 4 / 3, r1 = (sl + 1) * NS * 4 / 3;
+      static_for<r1 - r0>([&](auto u) { read_wgt_one(g + 1, wgt[(SL + 1) & 1], Slot<r0 + decltype(u)::value>{}); });
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int c0 = sl * CD / 3, c1 = (sl + 1) * CD / 3;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int j = 0; j < NM; ++j) mfma_one(sl + 1, j, slot);
 #pragma unroll
-      for (int ts = 0; ts < TS; ++ts)
+      for (int c = c0; c < c1; ++c) dq_store_one(g + 2, g & 1, d, std::integral_constant<bool, (SL & 1) != 0>{}, c);
+      // one matrix-core instruction, then a share of the VALU work
+      constexpr int kValu = ((c1 - c0) * 18 + NM - 1) / NM;
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns)
-          acc[ts][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(act[SL][ts][m], wgt[SL & 1][ns][m], acc[ts][ns], 0, 0, 0);
-    dq_store(g + 2, g & 1, d, std::integral_constant<bool, (SL & 1) != 0>{});
-    // one matrix-core instruction, then a share of the VALU work
-#pragma unroll
-    for (int i = 0; i < 4 * TS * NS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);   // VALU
-    }
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);   // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   // Prologue: codes of groups 0..DS-1 and activations of groups 0..DACT-1 in
   // flight, then all landed; groups 0 and 1 dequantized; the codes of group
   // DS (into the slot group 0 used) in flight; group 0's weights read.
-  static_assert(DS == 4, "the prologue and the step unrolling assume four slots");
-  issue_codes(0);
-  issue_codes(1);
-  issue_codes(2);
-  issue_codes(3);
-  issue_act(0, act[0]);
-  issue_act(1, act[1]);
-  issue_act(2, act[2]);
+  static_for<DS>([&](auto i) { issue_codes(decltype(i)::value); });
+  static_for<DACT>([&](auto i) { issue_act(decltype(i)::value, act[decltype(i)::value]); });
   // A thread dequantizes its own code dwords but reads row scales that other
   // waves loaded: a barrier after the waits publishes them, and a second one
   // (which also publishes the weight tiles) orders every read of slot 0
@@ -521,24 +584,22 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     dq_load(1, d);
     dq_store(1, 1, d, std::true_type{});
   }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   issue_codes(DS);
   read_wgt(0, wgt[0]);
-  // Steps run in fours (the register sets cycle with period four); up to
-  // three steps past the last group run on clamped, finite activations with
-  // zero weights and so add exactly nothing.  (A tail of conditional steps
-  // would keep extra copies of the operand registers live.)
-  for (int g = 0; g < G; g += DS) {
-    step(g, Slot<0>{});
-    step(g + 1, Slot<1>{});
-    step(g + 2, Slot<2>{});
-    step(g + 3, Slot<3>{});
+  // Steps run in blocks of P (the ring indexes repeat with period P); the
+  // block stops after the last group.
+  for (int g0 = 0; g0 < G; g0 += P) {
+    static_for<P>([&](auto sl) {
+      constexpr int SL = decltype(sl)::value;
+      if (SL == 0 || g0 + SL < G) step(g0 + SL, sl);
+    });
   }
   // no load may still write this workgroup's LDS or registers after this
   wait_vm<0>();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wait_lgkm0();
 
   // Epilogue: lane (li, lh) holds row n = n0 + 32 (wn*NS + ns) + li and tokens
   // t = 32 (tb0 + wt*TS + ts) + 8 (r / 4) + 4 lh + r % 4.  The bf16 results
@@ -626,12 +687,10 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   {
     const u32x4_t* x = static_cast<const u32x4_t*>(a.x);
     int k = (int)a.k, t = (int)a.t, n = (int)a.n, tpad = (int)tp;
-    const int tok_blocks = (int)((tp + kExpWaves - 1) / kExpWaves);
+    const int tok_blocks = (int)((tp + kPrepWaves - 1) / kPrepWaves);
     const int row_blocks = (int)((a.n + kRowsPerBlock - 1) / kRowsPerBlock);
-    prep_exp_kernel<<<dim3((unsigned)(tok_blocks + row_blocks)), dim3(64 * kExpWaves), 0, stream>>>(
-        x, k, t, tpad, texp, static_cast<const uint16_t*>(a.scales), n, rexp, tok_blocks);
-    prep_pack_kernel<<<dim3((unsigned)(tp / 32), (unsigned)((a.k / 64 + kPackGroups - 1) / kPackGroups)), dim3(256), 0,
-                       stream>>>(x, k, t, texp, x16);
+    prep_act_kernel<<<dim3((unsigned)(tok_blocks + row_blocks)), dim3(64 * kPrepWaves), 0, stream>>>(
+        x, k, t, tpad, texp, x16, static_cast<const uint16_t*>(a.scales), n, rexp, tok_blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
