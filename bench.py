@@ -16,7 +16,7 @@ the 4 MB per-XCD L2s or the 256 MB Infinity Cache.  The K timed calls are
 captured in one HIP graph (host launch cost would otherwise exceed a ~3 us
 kernel) and bracketed by HIP events on the graph's stream, with a device
 synchronize on both sides; ms_per_step = elapsed / K.  Each step is one
-complete public call (for T = 1024 that is the activation-preparation kernels
+complete public call (for T = 1024 that is the activation-preparation kernel
 plus the tiled kernel).  Next to it the pages' own single-call contract
 ("linear-benchmark.md" section 6: flush, then events around exactly one call;
 median, min and p95) is reported as ``single_call_cold``; on this platform an
@@ -24,8 +24,8 @@ event pair around one launch adds a few microseconds of its own.
 
 Other modes: ``--sweep 1:128`` (per-T table with step change between
 adjacent T), ``--n/--k/--t`` single points, ``--profile`` (one call after
-set-up, for profiler counter passes).  ``--gpus`` above 1 exits: this build
-measures one GPU.
+set-up, for profiler counter passes).  ``--gpus`` above 1 exits: the
+benchmark covers one GPU.
 """
 from __future__ import annotations
 
@@ -231,7 +231,7 @@ def cpu_baseline_rows(n, k, t, seed, budget_s=10.0):
 # ---------------------------------------------------------------------------
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
-    "gemv": "weight_only_bit_q4_amd/csrc/q4lin_gemv.hip",
+    "decode": "weight_only_bit_q4_amd/csrc/q4lin_decode.hip",
     "tiled": "weight_only_bit_q4_amd/csrc/q4lin_tiled.hip",
 }
 
@@ -384,7 +384,7 @@ def main(argv=None):
     steps2 = max(20, args.steps // 20)
     seed2 = inputs.workload_seed("prefill_6144x5120_t1024")
     p2 = Point(n, k, 1024, seed2)
-    s2 = p2.time(steps2, max(3, args.warmup // 10), repeats=1)[0]
+    s2 = float(np.median(p2.time(steps2, max(20, args.warmup // 2), repeats=5)))
     p2.free()
     p2c = Point(n, k, 1024, seed2, rotate=False)
     lat2 = p2c.time_cold(30, 3)
@@ -414,11 +414,11 @@ def main(argv=None):
         "config": {"workload": "decode_6144x5120_t1", "n": n, "k": k, "t": 1,
                    "weight_format": "Q4_G64_FP16",
                    "cache": "cold (rotating buffer sets, >= 1 GiB between reuses)"},
-        # dominant kernel: the few-token kernel is the whole call at T = 1; its
-        # algorithmic bytes per launch are model_bytes (W, X and Y once each)
+        # dominant kernel: the single-token kernel is the whole call at T = 1;
+        # its algorithmic bytes per launch are model_bytes (W, X and Y once each)
         "roofline": {"bound": "hbm", "achieved": round(v1, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(v1 / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profiles("gemv", "decode_6144x5120_t1"),
+                     "traffic": traffic_from_profiles("decode", "decode_6144x5120_t1"),
                      "algorithmic_bytes": model_bytes(n, k, 1)},
         "single_call_cold": stats(lat1),
         "prefill_t1024": {
