@@ -16,7 +16,7 @@
 // region, and reads them back in matrix-core operand order.
 //
 // Arithmetic (v_mfma_f32_16x16x32_bf16, A = activations, B = weights).
-//   * Weights: v_and_or_b32 turns nibbles s and s+16 of a code dword into the
+//   * Weights: one (a & m) | c (v_bitop3) turns nibbles s and s+16 of a code dword into the
 //     bf16 pair (128 + q, 128 + q') exactly (bf16 has unit spacing on
 //     [128, 256)); four such operations give the 8 operand values of one
 //     dword in the order k0 k4 k1 k5 k2 k6 k3 k7.
