@@ -12,22 +12,28 @@
 // rows l / S, l / S + R, ... (R = 64 / S row groups).  So a lane keeps one
 // fixed piece of the activations in registers for all its rows, each load
 // instruction reads R rows x 16 PL S contiguous bytes, and every load of a
-// lane is issued before the first wait.  The block's scales arrive by a
-// direct-to-LDS copy issued first.
+// lane (activations, then its scales, then its codes row by row) is issued
+// before the first wait; each row is then processed as soon as its own codes
+// have arrived.
 //
 // Arithmetic (as in the pages' "decode, FP32 accumulate" reading of the op):
-//   * Activations: float16 copies of the bf16 values times 2^-e, e from the
-//     wave slice's largest magnitude (every value within 2^34 of it converts
-//     exactly); odd-k values are further divided by 16.
-//   * Codes become float16 operands with one AND: w & 0x000F000F is the pair
-//     (q * 2^-24, q' * 2^-24) (subnormal, exact), w & 0x00F000F0 is 16 q * 2^-24
-//     for the odd k, which the /16 above cancels.
-//   * v_dot2_f32_f16 sums q * x; the offset enters as sum (q - 8) x =
-//     sum q x - sum 8 x, the second sum from the very same dot2 chain run on
-//     an all-8 code dword, so a piece of eight-codes contributes exactly 0.
-//     Each piece's difference is scaled by its group's scale in FP32.
-//   * Partials carry 2^-(e + 24) with a per-wave e; the eight waves' sums are
-//     combined in binary64 and rounded to bf16 once.
+//   * The bf16 activations are used as they are, permuted into the pair
+//     order (k0,k4) (k1,k5) (k2,k6) (k3,k7) of a code dword's nibbles.
+//   * A code pair becomes the exact bf16 pair (128 + q, 128 + q') with one
+//     (a & m) | c (bf16 has unit spacing on [128, 256)); v_dot2_f32_bf16 sums
+//     (128 + q) x (products exact in FP32).  The offset enters as
+//     sum (q - 8) x = sum (128 + q) x - sum 136 x, the second sum from the
+//     very same dot chain run on an all-8 code dword, so a piece of
+//     eight-codes contributes exactly 0.  Each piece's difference is scaled
+//     by its group's scale in FP32.
+//   * Activations near the bf16 maximum can overflow those FP32 sums; a wave
+//     that sees a non-finite partial redoes its rows on float16 copies of
+//     the activations scaled by 2^-e (e from the slice's largest magnitude,
+//     every value within 2^34 of it exact; odd k further /16, cancelled by
+//     reading 16 q 2^-24 subnormals from the codes with one AND), and its
+//     partials carry 2^-(e + 24).
+//   * The eight waves' partials are combined in binary64 and rounded to bf16
+//     once.
 #include "q4lin_device.h"
 #include "q4lin_kernels.h"
 
@@ -37,19 +43,6 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Direct-to-LDS dword copy: lane l sends 4 bytes from base + voffset to
-// lds_base + 4 l; offsets at or past the resource's byte count read zeros.
-__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voffset, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, voffset, 0u, 0,
-                                           0);
-}
 
 // s_waitcnt immediate for gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 =
 // no wait), lgkmcnt 11:8 (15 = no wait).
@@ -86,7 +79,42 @@ __device__ __forceinline__ u32x4_t to_f16_pairs(u32x4_t v, int e) {
   return u32x4_t{h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16), h[3] | (h[7] << 16)};
 }
 
-// dot2 chain of one 16-byte code piece (32 weights) against its activations
+// 8 bf16 values (k0..k7 in memory order) -> the pairs (k0,k4) (k1,k5)
+// (k2,k6) (k3,k7), the order in which a code dword's nibbles pair up below
+__device__ __forceinline__ u32x4_t bf16_pairs(u32x4_t v) {
+  return u32x4_t{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                 __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// (a & m) | c in one instruction (gfx950 three-input bitwise operation)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
+}
+
+// bf16 dot2 chain of one 16-byte code piece (32 weights) against its
+// activations in pair order: the nibbles become the exact bf16 values 128 + q
+// (bf16 has unit spacing on [128, 256)), so the chain sums (128 + q) x; the
+// same chain over all-eight codes sums 136 x, and the difference is
+// sum (q - 8) x, exactly 0 for a piece of eight-codes.
+__device__ __forceinline__ float piece_dot_bf16(u32x4_t w, const u32x4_t (&xb)[4]) {
+  float c = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t wd = w[d];
+    c = dot2_bf16(and_or(wd, 0x000F000Fu, 0x43004300u), xb[d].x, c);
+    c = dot2_bf16(and_or(wd >> 4, 0x000F000Fu, 0x43004300u), xb[d].y, c);
+    c = dot2_bf16(and_or(wd >> 8, 0x000F000Fu, 0x43004300u), xb[d].z, c);
+    c = dot2_bf16(and_or(wd >> 12, 0x000F000Fu, 0x43004300u), xb[d].w, c);
+  }
+  return c;
+}
+
+// float16 dot2 chain of one 16-byte code piece (32 weights) against its
+// activations (the overflow path)
 __device__ __forceinline__ float piece_dot(u32x4_t w, const u32x4_t (&xf)[4]) {
   float c = 0.0f;
 #pragma unroll
@@ -105,7 +133,7 @@ __device__ __forceinline__ float piece_dot(u32x4_t w, const u32x4_t (&xf)[4]) {
 template <int PL, int MAXR>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-              uint16_t* __restrict__ y, int N, int K, int BN, int SW) {
+              uint16_t* __restrict__ y, int N, int K, int BN) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int G = K >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -126,29 +154,12 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   const int slot = lane - grp_raw * S;
   const int pc0 = slot * PL;
 
-  // LDS: per wave, the scales of its slice ([BN][SW] dwords), then a scratch
-  // of 64 x MAXR floats; after them the waves' combined row sums (binary64).
-  const int sreg = (BN * SW * 4 + 255) & ~255;
-  uint8_t* wl = lds + wave * (sreg + 64 * MAXR * 4);
-  float* scratch = reinterpret_cast<float*>(wl + sreg);
-  double* rowsum = reinterpret_cast<double*>(lds + kWaves * (sreg + 64 * MAXR * 4));
+  // LDS: per wave a scratch of 64 x MAXR floats; after them the waves'
+  // combined row sums (binary64).
+  float* scratch = reinterpret_cast<float*>(lds + wave * (64 * MAXR * 4));
+  double* rowsum = reinterpret_cast<double*>(lds + kWaves * (64 * MAXR * 4));
 
-  // 1. scales of the slice for the block's rows, straight into LDS
-  if (ng > 0) {
-    const rsrc_t rs = make_rsrc(scales, (uint32_t)(((size_t)N * (size_t)G * 2 + 3) & ~(size_t)3));
-    const int nd = BN * SW;
-    __builtin_amdgcn_sched_barrier(0);
-    for (int i = 0; 64 * i < nd; ++i) {
-      const int d = min(64 * i + lane, nd - 1);
-      const int r = d / SW, j = d - r * SW;
-      const uint32_t b = ((uint32_t)(n0 + r) * (uint32_t)G * 2u + (uint32_t)gl * 2u) & ~3u;
-      dma4(rs, b + 4u * (uint32_t)j, wl + 256 * i);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // 2. the lane's activations (before the codes, so that waiting for them
-  //    does not wait for the codes)
+  // 1. the lane's activations (first: waiting for them waits for nothing else)
   u32x4_t xv[PL][4];
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
@@ -156,8 +167,18 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 #pragma unroll
     for (int d = 0; d < 4; ++d) xv[i][d] = xp[d];
   }
-  // 3. codes of the lane's rows (clamped addresses stay valid; the values of
-  //    rows past the block and pieces past the slice are never used)
+  // 2. the scales of the lane's pieces (clamped rows and pieces stay valid)
+  uint16_t sbits[MAXR][PL];
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const uint16_t* sr = scales + (size_t)(n0 + min(grp + R * j, rows - 1)) * (size_t)G + gl;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) sbits[j][i] = sr[min(pc0 + i, max(P - 1, 0)) >> 1];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 3. codes of the lane's rows, in row order (the rows are waited for one by
+  //    one below; values of rows past the block and pieces past the slice are
+  //    never used)
   u32x4_t w[MAXR][PL];
 #pragma unroll
   for (int j = 0; j < MAXR; ++j) {
@@ -166,74 +187,114 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 #pragma unroll
     for (int i = 0; i < PL; ++i)
       w[j][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(rp + 16 * min(pc0 + i, max(P - 1, 0))));
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
 
-  // 4. the slice's exponent (pieces past the slice repeat a valid piece)
-  uint32_t m = 0;
+  // 4. activation pairs in the order of the code pairs, and the correction
+  //    sums of the all-eight codes through the very same dot chain
+  u32x4_t xb[PL][4];
 #pragma unroll
   for (int i = 0; i < PL; ++i)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) m = max(m, max_mag8(xv[i][d]));
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-  const int e = exponent_for(m);
-  u32x4_t xf[PL][4];
-#pragma unroll
-  for (int i = 0; i < PL; ++i)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) xf[i][d] = to_f16_pairs(xv[i][d], e);
-
-  // 5. the eight-code sums of the lane's pieces, same chain as the rows use
+    for (int d = 0; d < 4; ++d) xb[i][d] = bf16_pairs(xv[i][d]);
   const u32x4_t k8 = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-  float s8[PL];
+  float c8[PL];
 #pragma unroll
-  for (int i = 0; i < PL; ++i) s8[i] = piece_dot(k8, xf[i]);
+  for (int i = 0; i < PL; ++i) c8[i] = piece_dot_bf16(k8, xb[i]);
 
-  // the scale copy was issued before every load of steps 2-3
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(MAXR * PL + 4 * PL));
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 6. rows
+  // 5. rows, in the order their codes arrive: row j waits only for its own
+  //    loads (the (MAXR-1-j) PL younger ones may still be in flight)
   float acc[MAXR];
-#pragma unroll
-  for (int j = 0; j < MAXR; ++j) {
-    const int r = grp + R * j;
+  static_for<MAXR>([&](auto jj) {
+    constexpr int j = decltype(jj)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((MAXR - 1 - j) * PL));
+    __builtin_amdgcn_sched_barrier(0);
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
-      const int pc = pc0 + i;
-      const uint32_t b = (uint32_t)(n0 + min(r, rows - 1)) * (uint32_t)G * 2u + (uint32_t)gl * 2u;
-      const uint16_t sb =
-          *reinterpret_cast<const uint16_t*>(wl + 4 * SW * min(r, rows - 1) + (b & 3u) + 2 * (pc >> 1));
-      const float s = pc < P ? f16_bits_to_f32(sb) : 0.0f;
-      a = __builtin_fmaf(s, piece_dot(w[j][i], xf[i]) - s8[i], a);
+      const float sc = pc0 + i < P ? f16_bits_to_f32(sbits[j][i]) : 0.0f;
+      a = __builtin_fmaf(sc, piece_dot_bf16(w[j][i], xb[i]) - c8[i], a);
     }
     acc[j] = a;
+  });
+
+  // 6. activations near the bf16 maximum can overflow these FP32 sums: then
+  //    the wave redoes its rows on float16 copies of X scaled by 2^-e (e from
+  //    the slice's largest magnitude, so the sums stay in range) and its
+  //    partials carry 2^-(e+24)
+  int ew = 0;
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) bad |= !__builtin_isfinite(acc[j]);
+  if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) m = max(m, max_mag8(xv[i][d]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    const int e = exponent_for(m);
+    u32x4_t xf[PL][4];
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) xf[i][d] = to_f16_pairs(xv[i][d], e);
+    float s8[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) s8[i] = piece_dot(k8, xf[i]);
+#pragma unroll
+    for (int j = 0; j < MAXR; ++j) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const float sc = pc0 + i < P ? f16_bits_to_f32(sbits[j][i]) : 0.0f;
+        a = __builtin_fmaf(sc, piece_dot(w[j][i], xf[i]) - s8[i], a);
+      }
+      acc[j] = a;
+    }
+    ew = e + 24;
   }
 
-  // 7. sums: the S slots of each row group inside the wave (LDS), then the
+  // 8. sums: the S slots of each row group inside the wave (LDS), then the
   //    eight waves in binary64
 #pragma unroll
   for (int j = 0; j < MAXR; ++j) scratch[j * 64 + lane] = acc[j];
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own writes are visible to it
-  // (four independent partial sums, so that the LDS reads overlap)
+  // (S <= 64; for S a multiple of 4 all of a lane's reads are in flight
+  // together, as up to 16 clamped 16-byte pieces; else four independent
+  // partial sums keep four reads in flight)
   for (int q = lane; q < R * MAXR; q += 64) {
     const int g = q % R, j = q / R;
     const int r = g + R * j;
     if (r < rows) {
       const float* sp = scratch + j * 64 + g * S;
       float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
-      int sl = 0;
-      for (; sl + 4 <= S; sl += 4) {
-        v0 += sp[sl];
-        v1 += sp[sl + 1];
-        v2 += sp[sl + 2];
-        v3 += sp[sl + 3];
+      if ((S & 3) == 0) {
+        const int n4 = S >> 2;
+        f32x4_t t4[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) t4[u] = reinterpret_cast<const f32x4_t*>(sp)[min(u, n4 - 1)];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (u < n4) {
+            v0 += t4[u].x;
+            v1 += t4[u].y;
+            v2 += t4[u].z;
+            v3 += t4[u].w;
+          }
+      } else {
+        int sl = 0;
+        for (; sl + 4 <= S; sl += 4) {
+          v0 += sp[sl];
+          v1 += sp[sl + 1];
+          v2 += sp[sl + 2];
+          v3 += sp[sl + 3];
+        }
+        for (; sl < S; ++sl) v0 += sp[sl];
       }
-      for (; sl < S; ++sl) v0 += sp[sl];
-      rowsum[wave * BN + r] = __builtin_ldexp((double)((v0 + v1) + (v2 + v3)), e + 24);
+      rowsum[wave * BN + r] = __builtin_ldexp((double)((v0 + v1) + (v2 + v3)), ew);
     }
   }
   // waves without groups contribute zero
@@ -248,20 +309,20 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   }
 }
 
-size_t decode_lds(int bn, int sw, int maxr) {
-  return (size_t)kWaves * (size_t)(((bn * sw * 4 + 255) & ~255) + 64 * maxr * 4) + (size_t)kWaves * bn * 8;
+size_t decode_lds(int bn, int maxr) {
+  return (size_t)kWaves * (size_t)(64 * maxr * 4) + (size_t)kWaves * bn * 8;
 }
 
 template <int PL, int MAXR>
 hipError_t launch_pm(const DecodePlan& p, const GemvArgs& a, hipStream_t stream) {
   auto kern = decode_kernel<PL, MAXR>;
-  const size_t lds = decode_lds(p.bn, p.sw, MAXR);
+  const size_t lds = decode_lds(p.bn, MAXR);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)p.blocks), dim3(kThreads), lds, stream>>>(
       static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
-      static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, p.bn, p.sw);
+      static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, p.bn);
   return hipGetLastError();
 }
 
@@ -288,10 +349,8 @@ bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p) {
       if ((bn + rmin - 1) / rmin > maxr) continue;
       // fewer than half the lanes busy: leave the shape to the other route
       if (2 * rmin * s < 64 && bn > rmin) continue;
-      const int64_t sw = (2 * ((G + kWaves - 1) / kWaves) + 3) / 4 + 1;
-      if (decode_lds((int)bn, (int)sw, (int)maxr) > 64 * 1024) continue;
+      if (decode_lds((int)bn, (int)maxr) > 64 * 1024) continue;
       p->bn = (int)bn;
-      p->sw = (int)sw;
       p->pl = (int)pl;
       p->maxr = (int)maxr;
       p->blocks = (int)((n + bn - 1) / bn);

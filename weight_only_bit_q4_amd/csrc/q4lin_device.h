@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace q4lin {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -49,6 +51,18 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
 // binary32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+template <int V>
+using Slot = std::integral_constant<int, V>;
+
+// Calls f(Slot<0>{}) ... f(Slot<N-1>{}) (compile-time unrolled loop).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Slot<I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 }  // namespace q4lin

@@ -27,7 +27,6 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 // split over the waves, activations in registers, no workspace.
 struct DecodePlan {
   int bn;      // rows per workgroup
-  int sw;      // scale dwords per row copied by each wave
   int pl;      // consecutive 16-byte pieces per lane and row
   int maxr;    // rows per lane, at most
   int blocks;  // workgroups

@@ -272,18 +272,6 @@ __device__ __forceinline__ u32x4_t make_rsrc_sgpr(const void* base, uint32_t byt
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
 }
 
-template <int V>
-using Slot = std::integral_constant<int, V>;
-
-// Calls f(Slot<0>{}) ... f(Slot<N-1>{}).
-template <int N, int I = 0, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(Slot<I>{});
-    static_for<N, I + 1>(f);
-  }
-}
-
 // Ring geometry.  Codes and scales stream through an LDS ring of DS slots,
 // loaded DS+1 groups ahead (a group's codes are dequantized two groups
 // before its products); each wave's activation fragments stream through a
