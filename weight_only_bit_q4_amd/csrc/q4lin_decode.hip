@@ -43,6 +43,8 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+template <int MAXR>
+constexpr int kRegion = 64 * MAXR * 4 + 16;  // bytes of one wave's LDS scratch region
 
 // s_waitcnt immediate for gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 =
 // no wait), lgkmcnt 11:8 (15 = no wait).
@@ -154,10 +156,12 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   const int slot = lane - grp_raw * S;
   const int pc0 = slot * PL;
 
-  // LDS: per wave a scratch of 64 x MAXR floats; after them the waves'
-  // combined row sums (binary64).
-  float* scratch = reinterpret_cast<float*>(lds + wave * (64 * MAXR * 4));
-  double* rowsum = reinterpret_cast<double*>(lds + kWaves * (64 * MAXR * 4));
+  // LDS: per wave a scratch of 64 x MAXR floats (regions 16 bytes more than
+  // that apart, so that the eight threads of a row, which read the eight
+  // regions at the same offset, hit different banks), then the waves'
+  // exponents.
+  float* scratch = reinterpret_cast<float*>(lds + wave * kRegion<MAXR>);
+  int* wexp = reinterpret_cast<int*>(lds + kWaves * kRegion<MAXR>);
 
   // 1. the lane's activations (first: waiting for them waits for nothing else)
   u32x4_t xv[PL][4];
@@ -167,16 +171,7 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 #pragma unroll
     for (int d = 0; d < 4; ++d) xv[i][d] = xp[d];
   }
-  // 2. the scales of the lane's pieces (clamped rows and pieces stay valid)
-  uint16_t sbits[MAXR][PL];
-#pragma unroll
-  for (int j = 0; j < MAXR; ++j) {
-    const uint16_t* sr = scales + (size_t)(n0 + min(grp + R * j, rows - 1)) * (size_t)G + gl;
-#pragma unroll
-    for (int i = 0; i < PL; ++i) sbits[j][i] = sr[min(pc0 + i, max(P - 1, 0)) >> 1];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // 3. codes of the lane's rows, in row order (the rows are waited for one by
+  // 2. codes of the lane's rows, in row order (the rows are waited for one by
   //    one below; values of rows past the block and pieces past the slice are
   //    never used)
   u32x4_t w[MAXR][PL];
@@ -189,6 +184,16 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
       w[j][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(rp + 16 * min(pc0 + i, max(P - 1, 0))));
     __builtin_amdgcn_sched_barrier(0);
   }
+  // 3. the scales of the lane's pieces, last: they are needed only after
+  //    every row's dot products (clamped rows and pieces stay valid)
+  uint16_t sbits[MAXR][PL];
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const uint16_t* sr = scales + (size_t)(n0 + min(grp + R * j, rows - 1)) * (size_t)G + gl;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) sbits[j][i] = sr[min(pc0 + i, max(P - 1, 0)) >> 1];
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   // 4. activation pairs in the order of the code pairs, and the correction
   //    sums of the all-eight codes through the very same dot chain
@@ -202,31 +207,43 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 #pragma unroll
   for (int i = 0; i < PL; ++i) c8[i] = piece_dot_bf16(k8, xb[i]);
 
-  // 5. rows, in the order their codes arrive: row j waits only for its own
-  //    loads (the (MAXR-1-j) PL younger ones may still be in flight)
-  float acc[MAXR];
+  // 5. the pieces' sums (q - 8) x, row by row in the order the codes arrive:
+  //    row j waits only for its own loads (the younger code loads of later
+  //    rows and the scale loads may still be in flight)
+  float dp[MAXR][PL];
   static_for<MAXR>([&](auto jj) {
     constexpr int j = decltype(jj)::value;
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((MAXR - 1 - j) * PL));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((MAXR - 1 - j) * PL + MAXR * PL));
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < PL; ++i) dp[j][i] = piece_dot_bf16(w[j][i], xb[i]) - c8[i];
+  });
+  // 6. scales
+  float sc[MAXR][PL];
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j)
+#pragma unroll
+    for (int i = 0; i < PL; ++i) sc[j][i] = pc0 + i < P ? f16_bits_to_f32(sbits[j][i]) : 0.0f;
+  float acc[MAXR];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
-      const float sc = pc0 + i < P ? f16_bits_to_f32(sbits[j][i]) : 0.0f;
-      a = __builtin_fmaf(sc, piece_dot_bf16(w[j][i], xb[i]) - c8[i], a);
+      bad |= !__builtin_isfinite(dp[j][i]);
+      a = __builtin_fmaf(sc[j][i], dp[j][i], a);
     }
     acc[j] = a;
-  });
+    bad |= !__builtin_isfinite(a);
+  }
 
-  // 6. activations near the bf16 maximum can overflow these FP32 sums: then
+  // 7. activations near the bf16 maximum can overflow these FP32 sums: then
   //    the wave redoes its rows on float16 copies of X scaled by 2^-e (e from
   //    the slice's largest magnitude, so the sums stay in range) and its
   //    partials carry 2^-(e+24)
   int ew = 0;
-  bool bad = false;
-#pragma unroll
-  for (int j = 0; j < MAXR; ++j) bad |= !__builtin_isfinite(acc[j]);
   if (__builtin_amdgcn_ballot_w64(bad) != 0) {
     uint32_t m = 0;
 #pragma unroll
@@ -248,69 +265,67 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     for (int j = 0; j < MAXR; ++j) {
       float a = 0.0f;
 #pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        const float sc = pc0 + i < P ? f16_bits_to_f32(sbits[j][i]) : 0.0f;
-        a = __builtin_fmaf(sc, piece_dot(w[j][i], xf[i]) - s8[i], a);
-      }
+      for (int i = 0; i < PL; ++i) a = __builtin_fmaf(sc[j][i], piece_dot(w[j][i], xf[i]) - s8[i], a);
       acc[j] = a;
     }
     ew = e + 24;
   }
-
-  // 8. sums: the S slots of each row group inside the wave (LDS), then the
-  //    eight waves in binary64
-#pragma unroll
-  for (int j = 0; j < MAXR; ++j) scratch[j * 64 + lane] = acc[j];
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own writes are visible to it
-  // (S <= 64; for S a multiple of 4 all of a lane's reads are in flight
-  // together, as up to 16 clamped 16-byte pieces; else four independent
-  // partial sums keep four reads in flight)
-  for (int q = lane; q < R * MAXR; q += 64) {
-    const int g = q % R, j = q / R;
-    const int r = g + R * j;
-    if (r < rows) {
-      const float* sp = scratch + j * 64 + g * S;
-      float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
-      if ((S & 3) == 0) {
-        const int n4 = S >> 2;
-        f32x4_t t4[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) t4[u] = reinterpret_cast<const f32x4_t*>(sp)[min(u, n4 - 1)];
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (u < n4) {
-            v0 += t4[u].x;
-            v1 += t4[u].y;
-            v2 += t4[u].z;
-            v3 += t4[u].w;
-          }
-      } else {
-        int sl = 0;
-        for (; sl + 4 <= S; sl += 4) {
-          v0 += sp[sl];
-          v1 += sp[sl + 1];
-          v2 += sp[sl + 2];
-          v3 += sp[sl + 3];
-        }
-        for (; sl < S; ++sl) v0 += sp[sl];
-      }
-      rowsum[wave * BN + r] = __builtin_ldexp((double)((v0 + v1) + (v2 + v3)), ew);
-    }
-  }
   // waves without groups contribute zero
   if (ng <= 0)
-    for (int r = lane; r < rows; r += 64) rowsum[wave * BN + r] = 0.0;
-  __syncthreads();
-  for (int r = tid; r < rows; r += kThreads) {
-    double v = 0.0;
 #pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) v += rowsum[wv * BN + r];
-    y[n0 + r] = f32_to_bf16_rne((float)v);
+    for (int j = 0; j < MAXR; ++j) acc[j] = 0.0f;
+
+  // 8. sums: every lane's partials and every wave's exponent into LDS; then
+  //    eight threads per row each add one wave's S slots, scale by that
+  //    wave's 2^ew in binary64, and combine the eight by shuffles; the
+  //    row's first thread rounds to bf16 once and stores
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) scratch[j * 64 + lane] = acc[j];
+  if (lane == 0) wexp[wave] = ew;
+  __syncthreads();
+  for (int idx = tid; idx < rows * kWaves; idx += kThreads) {
+    const int r = idx / kWaves, wv = idx % kWaves;
+    const int glw = (G * wv) / kWaves, ngw = (G * (wv + 1)) / kWaves - glw;
+    const int Sw = max((2 * ngw + PL - 1) / PL, 1), Rw = 64 / Sw;
+    const int g = r % Rw, j = r / Rw;
+    const float* sp = reinterpret_cast<const float*>(lds + wv * kRegion<MAXR>) + j * 64 + g * Sw;
+    float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
+    if ((Sw & 3) == 0 && Sw <= 32) {
+      // all reads in flight together (at most 8 clamped 16-byte pieces)
+      const int n4 = Sw >> 2;
+      f32x4_t t4[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t4[u] = reinterpret_cast<const f32x4_t*>(sp)[min(u, n4 - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u < n4) {
+          v0 += t4[u].x;
+          v1 += t4[u].y;
+          v2 += t4[u].z;
+          v3 += t4[u].w;
+        }
+    } else {
+      int sl = 0;
+      for (; sl + 4 <= Sw; sl += 4) {
+        v0 += sp[sl];
+        v1 += sp[sl + 1];
+        v2 += sp[sl + 2];
+        v3 += sp[sl + 3];
+      }
+      for (; sl < Sw; ++sl) v0 += sp[sl];
+    }
+    double v = __builtin_ldexp((double)((v0 + v1) + (v2 + v3)), wexp[wv]);
+    // the eight threads of a row are eight consecutive lanes of one wave
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    if (wv == 0) y[n0 + r] = f32_to_bf16_rne((float)v);
   }
 }
 
 size_t decode_lds(int bn, int maxr) {
-  return (size_t)kWaves * (size_t)(64 * maxr * 4) + (size_t)kWaves * bn * 8;
+  (void)bn;
+  return (size_t)kWaves * (size_t)(64 * maxr * 4 + 16) + (size_t)kWaves * 4;
 }
 
 template <int PL, int MAXR>
