@@ -126,6 +126,10 @@ def test_large_shapes(shape, t):
 @pytest.mark.parametrize("n,k,t", [
     (1, 64, 1), (1, 64, 2), (7, 64, 3), (33, 128, 4), (97, 192, 5), (1, 64, 33), (17, 320, 31),
     (200, 576, 129), (5, 1088, 257), (130, 4160, 70), (300, 2048, 1), (16, 64, 1000),
+    # K split over several workgroups per tile: 8 splits of 10 groups with
+    # ragged rows; 2 splits of 13 and 14 groups (the second starts at an odd
+    # group, so its scales sit in the other halves of their dwords)
+    (1000, 5120, 40), (700, 1728, 60), (4000, 1344, 100),
 ])
 def test_ragged_shapes(n, k, t):
     x, c, s = inputs.gen_problem(n, k, t, 1000 + n + k + t)

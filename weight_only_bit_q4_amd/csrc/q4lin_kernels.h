@@ -57,6 +57,7 @@ struct TiledConfig {
   int ts;  // 32-token subtiles per wave
   int wn;  // waves along the rows
   int wt;  // waves along the tokens
+  int ks;  // K split into this many workgroup shares (1: none)
 };
 
 struct TiledArgs {

@@ -312,12 +312,19 @@ template <int NS, int TS, int WN, int WT>
 __global__ void __launch_bounds__(64 * WN * WT)
 tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, const int* __restrict__ rexp,
              const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-             uint16_t* __restrict__ y, int N, int K, int T, int Tpad, int tiles_n, int tiles_t) {
+             uint16_t* __restrict__ y, float* __restrict__ part, int N, int K, int T, int Tpad, int tiles_n,
+             int tiles_t, int KS) {
   using Sh = TiledShape<NS, TS, WN, WT>;
   constexpr int NT = Sh::NT, BN = Sh::BN, BT = Sh::BT, CD = Sh::CD, L = Sh::L;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int G = K >> 6;
+  // K split: the workgroup's share is the Gs groups from g0 (all of K when KS
+  // is 1); inside the kernel groups are counted from g0
+  const int nblk = tiles_n * tiles_t;
+  const int ks = blockIdx.x / nblk, bidx = blockIdx.x - ks * nblk;
+  const int g0 = (int)(((int64_t)G * ks) / KS);
+  const int Gs = (int)(((int64_t)G * (ks + 1)) / KS) - g0;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -331,17 +338,16 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // every XCD); else each XCD takes a contiguous run of tiles.  Inside an XCD
   // the row tile varies fastest, so that workgroups close in time share an
   // activation tile.
-  const int nblk = tiles_n * tiles_t;
   int tile_t, tile_n;
   {
-    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int xcd = bidx & 7, idx = bidx >> 3;
     if ((tiles_n & 3) == 0 && (tiles_t & 1) == 0) {
       const int bn = tiles_n >> 2, bt = tiles_t >> 1;
       const int lt = idx / bn;
       tile_t = (xcd >> 2) * bt + lt;
       tile_n = (xcd & 3) * bn + (idx - lt * bn);
     } else {
-      const int lin = (nblk & 7) == 0 ? xcd * (nblk >> 3) + idx : (int)blockIdx.x;
+      const int lin = (nblk & 7) == 0 ? xcd * (nblk >> 3) + idx : bidx;
       tile_t = lin / tiles_n;
       tile_n = lin - tile_t * tiles_n;
     }
@@ -382,7 +388,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
 #pragma unroll
   for (int c = 0; c < CD; ++c) {
     const int r = min((c * NT + tid) >> 3, N - 1 - n0);
-    const bool hi = ((((uint32_t)(s_first - s_base) >> 1) + (uint32_t)r * (uint32_t)G) & 1u) != 0;
+    const bool hi = ((((uint32_t)(s_first - s_base) >> 1) + (uint32_t)r * (uint32_t)G + (uint32_t)g0) & 1u) != 0;
     s_sel[c] = hi ? 0x03020302u : 0x01000100u;
     const uint32_t h = (uint32_t)(rexp[n0 + r] + 15) << 10;
     s_mul[c] = h | (h << 16);
@@ -411,20 +417,21 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   auto issue_one = [&](int gc, int ga, f16x8_t (&a)[TS][4], auto vi) __device__ {
     constexpr int v = decltype(vi)::value;
     if constexpr (v < CD) {
-      dma4(rc, coff[v], (uint32_t)gc * 32, lds + (gc % DS) * Sh::CODE_B + v * NT * 4 + wave * 256);
+      dma4(rc, coff[v], (uint32_t)(g0 + gc) * 32, lds + (gc % DS) * Sh::CODE_B + v * NT * 4 + wave * 256);
     } else if constexpr (v == CD) {
-      dma4(rs, (gc & 1) ? soff1 : soff0, (uint32_t)(gc >> 1) * 4, lds + Sh::OFF_S + (gc % DS) * Sh::SCALE_B + wave * 256);
+      dma4(rs, ((g0 + gc) & 1) ? soff1 : soff0, (uint32_t)((g0 + gc) >> 1) * 4,
+           lds + Sh::OFF_S + (gc % DS) * Sh::SCALE_B + wave * 256);
     } else {
       constexpr int i = v - CD - 1, ts = i / 4, m = i % 4;
-      buf_read_agpr<m * 1024>(a[ts][m], rx, aoff[ts], (uint32_t)ga * 4096);
+      buf_read_agpr<m * 1024>(a[ts][m], rx, aoff[ts], (uint32_t)(g0 + ga) * 4096);
     }
   };
   auto issue_codes = [&](int gc) __device__ {
-    gc = min(gc, G - 1);
+    gc = min(gc, Gs - 1);
     static_for<CD + 1>([&](auto v) { issue_one(gc, 0, act[0], v); });
   };
   auto issue_act = [&](int ga, f16x8_t (&a)[TS][4]) __device__ {
-    ga = min(ga, G - 1);
+    ga = min(ga, Gs - 1);
     static_for<TS * 4>([&](auto i) { issue_one(0, ga, a, Slot<CD + 1 + decltype(i)::value>{}); });
   };
 
@@ -453,7 +460,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     const uint32_t sel = decltype(odd)::value ? (s_sel[c] ^ 0x02020202u) : s_sel[c];
     const f16x2_t s2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(d.sw[c], d.sw[c], sel));
     uint32_t sp = __builtin_bit_cast(uint32_t, s2 * __builtin_bit_cast(f16x2_t, s_mul[c]));
-    sp = g < G ? sp : 0u;
+    sp = g < Gs ? sp : 0u;
     *reinterpret_cast<u32x4_t*>(wb + c * (NT / 8) * kRowBytes) = dequant_dword(d.w[c], sp);
   };
   auto dq_store = [&](int g, int b, const DqRegs& d, auto odd) __device__ {
@@ -519,7 +526,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     sync();
     DqRegs d;
     dq_load(g + 2, d);
-    const int gc = min(g + DCODE, G - 1), ga = min(g + DACT, G - 1);
+    const int gc = min(g + DCODE, Gs - 1), ga = min(g + DACT, Gs - 1);
     __builtin_amdgcn_sched_barrier(0);
     static_for<NM>([&](auto jj) {
       constexpr int j = decltype(jj)::value;
@@ -579,10 +586,10 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   read_wgt(0, wgt[0]);
   // Steps run in blocks of P (the ring indexes repeat with period P); the
   // block stops after the last group.
-  for (int g0 = 0; g0 < G; g0 += P) {
+  for (int gb = 0; gb < Gs; gb += P) {
     static_for<P>([&](auto sl) {
       constexpr int SL = decltype(sl)::value;
-      if (SL == 0 || g0 + SL < G) step(g0 + SL, sl);
+      if (SL == 0 || gb + SL < Gs) step(gb + SL, sl);
     });
   }
   // no load may still write this workgroup's LDS or registers after this
@@ -594,6 +601,24 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // go through LDS ([token][row] order), so that the stores to y are whole
   // 16-byte pieces of token rows.
   static_assert(BT * BN * 2 <= Sh::LDS_B, "output tile must fit the LDS");
+  if (part != nullptr) {
+    // K split: this split's raw FP32 sums (they carry 2^(c[n] - e[t])) into
+    // its slice of the partials, [split][token][row]; a second kernel adds
+    // the splits and finishes the outputs
+    float* pk = part + (size_t)ks * (size_t)Tpad * (size_t)N;
+#pragma unroll
+    for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const int n = n0 + (wn * NS + ns) * 32 + li;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * tb0 + (wt * TS + ts) * 32 + 4 * lh + 8 * (r >> 2) + (r & 3);
+          if (t < T && n < N) pk[(size_t)t * N + n] = acc[ts][ns][r];
+        }
+      }
+    return;
+  }
   int ce[NS];
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns) ce[ns] = rexp[min(n0 + (wn * NS + ns) * 32 + li, N - 1)];
@@ -630,9 +655,22 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   }
 }
 
+// The K-split outputs: y[t][n] = bf16(2^(e[t] - c[n]) * sum over splits of
+// the partials), the splits added in order.  One thread per output.
+__global__ void __launch_bounds__(256)
+tiled_reduce_kernel(const float* __restrict__ part, const int* __restrict__ texp, const int* __restrict__ rexp,
+                    uint16_t* __restrict__ y, int N, int Tpad, int KS) {
+  const int n = blockIdx.x * 256 + threadIdx.x, t = blockIdx.y;
+  if (n >= N) return;
+  const size_t i = (size_t)t * N + n, stride = (size_t)Tpad * N;
+  float v = 0.0f;
+  for (int k = 0; k < KS; ++k) v += part[k * stride + i];
+  y[i] = f32_to_bf16_rne(__builtin_ldexpf(v, texp[t] - rexp[n]));
+}
+
 template <int NS, int TS, int WN, int WT>
-hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, const int* rexp, int tpad,
-                      hipStream_t stream) {
+hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, const int* rexp, float* part,
+                      int tpad, hipStream_t stream) {
   using Sh = TiledShape<NS, TS, WN, WT>;
   const int tiles_n = (int)((a.n + Sh::BN - 1) / Sh::BN);
   const int tiles_t = (int)((a.t + Sh::BT - 1) / Sh::BT);
@@ -640,9 +678,14 @@ hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, c
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS_B);
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)(tiles_n * tiles_t)), dim3(Sh::NT), Sh::LDS_B, stream>>>(
+  const int ks = a.cfg.ks;
+  kern<<<dim3((unsigned)(tiles_n * tiles_t * ks)), dim3(Sh::NT), Sh::LDS_B, stream>>>(
       x16, texp, rexp, static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
-      static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t);
+      static_cast<uint16_t*>(a.y), ks > 1 ? part : nullptr, (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t, ks);
+  e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  tiled_reduce_kernel<<<dim3((unsigned)((a.n + 255) / 256), (unsigned)a.t), dim3(256), 0, stream>>>(
+      part, texp, rexp, static_cast<uint16_t*>(a.y), (int)a.n, tpad, ks);
   return hipGetLastError();
 }
 
@@ -652,19 +695,39 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int64_t tiled_tpad(int64_t t) { return (t + 31) / 32 * 32; }
 
-// Workspace: float16 activations in tile order, then the token exponents,
-// then the row exponents.
-size_t tiled_workspace_bytes(int64_t n, int64_t k, int64_t t) {
-  const int64_t tp = tiled_tpad(t);
-  return align256((size_t)(tp * k * 2)) + align256((size_t)(tp * 4)) + align256((size_t)(n * 4));
+// K split factor for a grid of `tiles` workgroup tiles: about `target`
+// workgroups in all, at most 8 splits, every split at least 10 groups.
+static int pick_ks(int64_t tiles, int64_t target, int64_t k, int64_t t) {
+  int64_t ks = target / tiles;
+  if (ks > 8) ks = 8;
+  if (ks > (k / 64) / 10) ks = (k / 64) / 10;
+  if (ks < 1 || t > 4096) ks = 1;
+  return (int)ks;
 }
 
 TiledConfig tiled_pick_config(int64_t n, int64_t k, int64_t t) {
-  (void)k;
-  // 192 x 128 tiles where they fill the chip, else narrower token tiles
-  if (t > 96 && (n / 192) * ((t + 127) / 128) >= 192) return TiledConfig{3, 2, 2, 2};
-  if (t > 32) return TiledConfig{1, 1, 1, 4};
-  return TiledConfig{1, 1, 1, 1};
+  if (t <= 32) return TiledConfig{1, 1, 1, 1, 1};
+  if (n >= 192) {
+    // 192-row tiles (every 32-row tile would read all the activations again),
+    // 64 or 128 tokens; with fewer tiles than CUs, K is split (one
+    // workgroup per CU: these tiles use most of a CU's registers)
+    const bool narrow_t = t <= 64;
+    const int64_t tiles = ((n + 191) / 192) * ((t + (narrow_t ? 63 : 127)) / (narrow_t ? 64 : 128));
+    const int ks = tiles >= 192 ? 1 : pick_ks(tiles, 256, k, t);
+    return narrow_t ? TiledConfig{3, 1, 2, 2, ks} : TiledConfig{3, 2, 2, 2, ks};
+  }
+  // few rows: 32 x 128 tiles, about three workgroups per CU
+  return TiledConfig{1, 1, 1, 4, pick_ks(((n + 31) / 32) * ((t + 127) / 128), 768, k, t)};
+}
+
+// Workspace: float16 activations in tile order, then the token exponents,
+// then the row exponents, then (K split only) the FP32 partial sums
+// [split][Tpad][N].
+size_t tiled_workspace_bytes(int64_t n, int64_t k, int64_t t) {
+  const int64_t tp = tiled_tpad(t);
+  const TiledConfig c = tiled_pick_config(n, k, t);
+  const size_t part = c.ks > 1 ? align256((size_t)c.ks * (size_t)tp * (size_t)n * 4) : 0;
+  return align256((size_t)(tp * k * 2)) + align256((size_t)(tp * 4)) + align256((size_t)(n * 4)) + part;
 }
 
 hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
@@ -672,6 +735,7 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   u32x4_t* x16 = static_cast<u32x4_t*>(a.workspace);
   int* texp = reinterpret_cast<int*>(static_cast<uint8_t*>(a.workspace) + align256((size_t)(tp * a.k * 2)));
   int* rexp = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(texp) + align256((size_t)(tp * 4)));
+  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(rexp) + align256((size_t)(a.n * 4)));
   {
     const u32x4_t* x = static_cast<const u32x4_t*>(a.x);
     int k = (int)a.k, t = (int)a.t, n = (int)a.n, tpad = (int)tp;
@@ -684,9 +748,10 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   }
   const int tpad = (int)tp;
   const TiledConfig c = a.cfg;
-  if (c.ns == 3 && c.ts == 2 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 2, 2, 2>(a, x16, texp, rexp, tpad, stream);
-  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 4) return launch_cfg<1, 1, 1, 4>(a, x16, texp, rexp, tpad, stream);
-  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 1) return launch_cfg<1, 1, 1, 1>(a, x16, texp, rexp, tpad, stream);
+  if (c.ns == 3 && c.ts == 2 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 2, 2, 2>(a, x16, texp, rexp, part, tpad, stream);
+  if (c.ns == 3 && c.ts == 1 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 1, 2, 2>(a, x16, texp, rexp, part, tpad, stream);
+  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 4) return launch_cfg<1, 1, 1, 4>(a, x16, texp, rexp, part, tpad, stream);
+  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 1) return launch_cfg<1, 1, 1, 1>(a, x16, texp, rexp, part, tpad, stream);
   return hipErrorInvalidValue;
 }
 
