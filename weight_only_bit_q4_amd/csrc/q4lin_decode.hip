@@ -342,25 +342,32 @@ hipError_t launch_pm(const DecodePlan& p, const GemvArgs& a, hipStream_t stream)
 }
 
 // instantiated (pieces per lane, rows per lane) shapes
-constexpr int kShapes[][2] = {{1, 8}, {1, 16}, {2, 8}, {4, 4}};
+// Lane shapes (PL, MAXR) in order of preference: the fewest registers first
+// (PL 1, MAXR 8 leaves room for two workgroups per CU), then more pieces per
+// lane, then more rows per lane.
+constexpr int kShapes[][2] = {{1, 8}, {2, 8}, {4, 4}, {1, 16}};
 
 }  // namespace
 
+// For each shape in turn, the fewest workgroups per CU (1..6, so blocks of
+// about N / (256 c) rows) whose rows the shape covers.  Measured on
+// 6144/14336/34816 x 5120 and 5120 x 17408: more, smaller blocks beat
+// more rows per lane.
 bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p) {
   if (t != 1 || n < 1 || k < 64) return false;
   if (n * (k / 2) >= (int64_t(1) << 31)) return false;  // 32-bit buffer offsets
   const int64_t G = k / 64;
   const int64_t pmax = 2 * ((G + kWaves - 1) / kWaves);
   const int64_t pmin = 2 * (G / kWaves);
-  for (int64_t c = 1; c <= 3; ++c) {  // workgroups per CU
-    const int64_t bn = (n + 256 * c - 1) / (256 * c);
-    for (const auto& sh : kShapes) {
-      const int64_t pl = sh[0], maxr = sh[1];
-      const int64_t s = (pmax + pl - 1) / pl;
-      if (s > 64) continue;
-      // every wave, also one with the smaller slice, must cover bn rows
-      const int64_t smin = pmin > 0 ? (pmin + pl - 1) / pl : 1;
-      const int64_t rmin = 64 / (s > smin ? s : smin);
+  for (const auto& sh : kShapes) {
+    const int64_t pl = sh[0], maxr = sh[1];
+    const int64_t s = (pmax + pl - 1) / pl;
+    if (s > 64) continue;
+    // every wave, also one with the smaller slice, must cover bn rows
+    const int64_t smin = pmin > 0 ? (pmin + pl - 1) / pl : 1;
+    const int64_t rmin = 64 / (s > smin ? s : smin);
+    for (int64_t c = 1; c <= 6; ++c) {  // workgroups per CU
+      const int64_t bn = (n + 256 * c - 1) / (256 * c);
       if ((bn + rmin - 1) / rmin > maxr) continue;
       // fewer than half the lanes busy: leave the shape to the other route
       if (2 * rmin * s < 64 && bn > rmin) continue;
