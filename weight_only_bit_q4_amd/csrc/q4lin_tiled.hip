@@ -21,16 +21,17 @@
 //     matrix-core operand reads want.
 //   * The epilogue multiplies by 2^(e[t] - c[n]) and rounds to bf16.
 //
-// Data movement.  A workgroup owns BN rows x BT tokens.  Per 64-group it
-// needs BN x 32 code bytes and BN scales, which stream into a DS-slot LDS ring
-// with gfx950 direct-to-LDS loads issued DS+1 groups ahead (covering the HBM
-// latency), and BT x 64 activations, which each wave loads straight into the
-// matrix cores' operand registers (AGPRs) DS-1 groups ahead.  Each thread
-// dequantizes the code dwords it loaded itself, with the scale of their row
-// (loaded by another thread), into a padded, double-buffered weight tile; one
-// barrier per group publishes the tile and the ring slot to all waves.  Waits
-// are explicit s_waitcnt vmcnt(n) with n the count of younger loads still
-// allowed in flight; the compiler's own fences would wait for all.
+// Data movement.  A workgroup owns BN rows x BT tokens (and, when K is split,
+// one share of the 64-groups).  Codes move in pairs of groups, 64 contiguous
+// bytes of every row per 16-byte direct-to-LDS load, into an LDS ring of
+// pair slots, with the pair's scales; activations go from L2 straight into
+// each wave's matrix-core operand registers (AGPRs), a ring of register sets
+// several groups ahead.  Each thread dequantizes its own share of a group's
+// code dwords, with the scale of their row (loaded by another thread), into a
+// padded, double-buffered weight tile; one barrier per group publishes the
+// tile and the ring slots to all waves.  Waits are explicit s_waitcnt
+// vmcnt(n) with n the count of younger loads still allowed in flight; the
+// compiler's own fences would wait for all.
 #include <type_traits>
 
 #include "q4lin_device.h"
@@ -222,6 +223,11 @@ __device__ __forceinline__ void dma4(rsrc_t r, uint32_t voffset, uint32_t soffse
                                            soffset, 0, 0);
 }
 
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voffset, uint32_t soffset, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voffset,
+                                           soffset, 0, 0);
+}
+
 // s_waitcnt encoding for gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7 =
 // no wait), lgkmcnt 11:8 (15 = no wait).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
@@ -272,40 +278,44 @@ __device__ __forceinline__ u32x4_t make_rsrc_sgpr(const void* base, uint32_t byt
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
 }
 
-// Ring geometry.  Codes and scales stream through an LDS ring of DS slots,
-// loaded DS+1 groups ahead (a group's codes are dequantized two groups
-// before its products); each wave's activation fragments stream through a
-// ring of DA register sets, loaded DA-1 groups ahead.  Before step g the
-// loads of group g's activations and group g+2's codes must have landed;
-// the NB = min(DS-2, DA-1) batches issued after the older of the two may
-// still be in flight.  The step code is unrolled over P steps, after which
-// every ring index repeats.
-constexpr int DS = 5;
+// Ring geometry.  Codes stream in pairs of groups (64 contiguous bytes of
+// every row, moved by 16-byte direct-to-LDS loads) through an LDS ring of NP
+// pair slots: even step s loads the pair of groups s+DC and s+DC+1 (a
+// group's codes are dequantized two groups before its products), and slot
+// reuse needs DC <= 2 NP.  The scales travel with their pair, one dword per
+// thread and group.  Each wave's activation fragments stream through a ring
+// of DA register sets, loaded DACT = DA-1 groups ahead, every step.  Before
+// step s the batch of step s-4, which carries group s's activations and
+// (s even) the codes of groups s+2 and s+3, must have landed; the batches of
+// steps s-3 .. s-1 may still be in flight.  The step code is unrolled over P
+// steps, after which every ring index repeats.
+constexpr int NP = 3;
+constexpr int DC = 6;
 constexpr int DA = 5;
-constexpr int DCODE = DS + 1;
 constexpr int DACT = DA - 1;
-constexpr int NB = (DS - 2 < DA - 1) ? DS - 2 : DA - 1;
 constexpr int P = 10;
-static_assert(P % DS == 0 && P % DA == 0 && P % 2 == 0, "the unrolled steps must cover every ring period");
+static_assert(DC <= 2 * NP && DC % 2 == 0 && DACT == 4 && DC - 2 == DACT, "ring geometry");
+static_assert(P % DA == 0 && P % 2 == 0, "the unrolled steps must cover every ring period");
 
 template <int NS, int TS, int WN, int WT>
 struct TiledShape {
   static constexpr int NT = 64 * WN * WT;                 // threads
   static constexpr int BN = 32 * NS * WN;                 // rows per workgroup
   static constexpr int BT = 32 * TS * WT;                 // tokens per workgroup
-  static constexpr int CD = BN * 8 / NT;                  // code dwords per thread per group
+  static constexpr int CD = BN * 8 / NT;                  // code dwords per thread per group (dequantization)
   static constexpr int AI = TS * 4;                       // 16-byte activation loads per lane per group
-  static constexpr int L = CD + 1 + AI;                   // loads per thread per batch (one scale)
-  static constexpr int CODE_B = BN * 32;                  // one code slot
+  static constexpr int CQ = (BN * 4 + NT - 1) / NT;       // 16-byte code loads per thread per pair
+  static constexpr int CP = CQ + 2;                       // loads per thread per pair (codes, two scales)
+  static constexpr int CODE_B = CQ * NT * 16;             // one pair slot ([row][64 bytes], then slack)
   static constexpr int SCALE_B = NT * 4;                  // one scale slot (one dword per thread)
   static constexpr int W_B = BN * kRowBytes;              // one dequantized weight tile
-  static constexpr int OFF_S = DS * CODE_B;
-  static constexpr int OFF_W = OFF_S + DS * SCALE_B;
+  static constexpr int OFF_S = NP * CODE_B;
+  static constexpr int OFF_W = OFF_S + 2 * NP * SCALE_B;
   static constexpr int LDS_B = (OFF_W + 2 * W_B > BT * BN * 2) ? OFF_W + 2 * W_B : BT * BN * 2;
   static_assert(BN * 8 % NT == 0, "code tiles must split evenly over the threads");
   static_assert(NT >= BN, "one scale per row needs a thread per row");
   static_assert(LDS_B <= 160 * 1024, "LDS budget");
-  static_assert(NB * L <= 63, "the load counter holds 63");
+  static_assert(3 * AI + 2 * CP <= 63, "the load counter holds 63");
 };
 
 template <int NS, int TS, int WN, int WT>
@@ -315,7 +325,8 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
              uint16_t* __restrict__ y, float* __restrict__ part, int N, int K, int T, int Tpad, int tiles_n,
              int tiles_t, int KS) {
   using Sh = TiledShape<NS, TS, WN, WT>;
-  constexpr int NT = Sh::NT, BN = Sh::BN, BT = Sh::BT, CD = Sh::CD, L = Sh::L;
+  constexpr int NT = Sh::NT, BN = Sh::BN, BT = Sh::BT, CD = Sh::CD, CQ = Sh::CQ, CP = Sh::CP, AI = Sh::AI;
+  constexpr int NW = WN * WT;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int G = K >> 6;
@@ -358,15 +369,18 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
 
   // --- per-thread load offsets (32-bit, relative to per-group uniform offsets
   // into buffers that start at the tile) ---------------------------------------
-  // Code dword task j = c*NT + tid: row j/8 of the tile, dword j%8 of the
-  // row's 32 bytes; rows past N repeat row N-1 (their outputs are dropped).
+  // Code load i of a pair: piece j = (i*NW + wave)*64 + lane, row j/4 of the
+  // tile, 16-byte quarter j%4 of the row's 64 bytes; it lands at byte 16 j
+  // of the pair slot, so the slot holds [row][64 bytes].  Pieces past the
+  // tile (when 4 BN is not a multiple of NT) repeat the last one into the
+  // slot's slack; rows past N repeat row N-1 (their outputs are dropped).
   const uint8_t* codes_tile = codes + (size_t)n0 * (K >> 1);
   const rsrc_t rc = make_rsrc(codes_tile, (uint32_t)min((int64_t)(N - n0) * (K >> 1), (int64_t)0x7FFFFFFF));
-  uint32_t coff[CD];
+  uint32_t coff[CQ];
 #pragma unroll
-  for (int c = 0; c < CD; ++c) {
-    const int j = c * NT + tid;
-    coff[c] = (uint32_t)(min(j >> 3, N - 1 - n0) * (K >> 1) + (j & 7) * 4);
+  for (int i = 0; i < CQ; ++i) {
+    const int j = min((i * NW + wave) * 64 + lane, 4 * BN - 1);
+    coff[i] = (uint32_t)(min(j >> 2, N - 1 - n0) * (K >> 1) + (j & 3) * 16);
   }
   // Scale of row tid % BN: the naturally aligned dword around it (which never
   // leaves the scale's page); the other half is ignored.  The buffer starts at
@@ -408,31 +422,35 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   f16x8_t act[DA][TS][4];
   f16x8_t wgt[2][NS][4];
 
-  // --- one batch: codes and scales of group gc into code slot gc % DS, and
+  // --- one batch: a code pair and its scales into their slots, and
   // this wave's activation fragments of group ga into set A (indexes clamped
   // to the last group, so every batch has the same number of loads) --------
-  // Load v of a batch: v < CD a code dword, v == CD the scale dword, then
-  // the TS * 4 activation fragments.
-  constexpr int NV = CD + 1 + TS * 4;
-  auto issue_one = [&](int gc, int ga, f16x8_t (&a)[TS][4], auto vi) __device__ {
+  // Load v of a batch: v < CQ a 16-byte code piece of pair q (groups 2q,
+  // 2q+1), v = CQ, CQ+1 the scale dwords of the two groups, then the TS * 4
+  // activation fragments of group ga.  Pair and group indexes are clamped to
+  // the last ones, so every batch of a kind has the same number of loads.
+  auto code_slot = [&](int q) __device__ { return lds + (q % NP) * Sh::CODE_B; };
+  auto scale_slot = [&](int g) __device__ { return lds + Sh::OFF_S + (((g >> 1) % NP) * 2 + (g & 1)) * Sh::SCALE_B; };
+  auto issue_one = [&](int q, int ga, f16x8_t (&a)[TS][4], auto vi) __device__ {
     constexpr int v = decltype(vi)::value;
-    if constexpr (v < CD) {
-      dma4(rc, coff[v], (uint32_t)(g0 + gc) * 32, lds + (gc % DS) * Sh::CODE_B + v * NT * 4 + wave * 256);
-    } else if constexpr (v == CD) {
-      dma4(rs, ((g0 + gc) & 1) ? soff1 : soff0, (uint32_t)((g0 + gc) >> 1) * 4,
-           lds + Sh::OFF_S + (gc % DS) * Sh::SCALE_B + wave * 256);
+    if constexpr (v < CQ) {
+      dma16(rc, coff[v], (uint32_t)(g0 + 2 * q) * 32, code_slot(q) + (v * NW + wave) * 1024);
+    } else if constexpr (v < CQ + 2) {
+      const int gs = min(2 * q + (v - CQ), Gs - 1);
+      dma4(rs, ((g0 + gs) & 1) ? soff1 : soff0, (uint32_t)((g0 + gs) >> 1) * 4, scale_slot(2 * q + (v - CQ)) + wave * 256);
     } else {
-      constexpr int i = v - CD - 1, ts = i / 4, m = i % 4;
+      constexpr int i = v - CQ - 2, ts = i / 4, m = i % 4;
       buf_read_agpr<m * 1024>(a[ts][m], rx, aoff[ts], (uint32_t)(g0 + ga) * 4096);
     }
   };
-  auto issue_codes = [&](int gc) __device__ {
-    gc = min(gc, Gs - 1);
-    static_for<CD + 1>([&](auto v) { issue_one(gc, 0, act[0], v); });
+  const int qlast = (Gs - 1) >> 1;
+  auto issue_codes = [&](int q) __device__ {
+    q = min(q, qlast);
+    static_for<CP>([&](auto v) { issue_one(q, 0, act[0], v); });
   };
   auto issue_act = [&](int ga, f16x8_t (&a)[TS][4]) __device__ {
     ga = min(ga, Gs - 1);
-    static_for<TS * 4>([&](auto i) { issue_one(0, ga, a, Slot<CD + 1 + decltype(i)::value>{}); });
+    static_for<TS * 4>([&](auto i) { issue_one(0, ga, a, Slot<CP + decltype(i)::value>{}); });
   };
 
   // --- dequantization of group g into weight tile b, in two halves: the LDS
@@ -443,12 +461,14 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     uint32_t w[CD];
     uint32_t sw[CD];
   };
+  // code dword c of this thread: row (c*NT + tid)/8, dword tid%8 of group
+  // g's 32 bytes in the row's 64-byte pair
   auto dq_load = [&](int g, DqRegs& d) __device__ {
-    const uint8_t* cs = lds + (g % DS) * Sh::CODE_B + tid * 4;
-    const uint8_t* ss = lds + Sh::OFF_S + (g % DS) * Sh::SCALE_B + (tid >> 3) * 4;
+    const uint8_t* cs = code_slot(g >> 1) + (tid >> 3) * 64 + (g & 1) * 32 + (tid & 7) * 4;
+    const uint8_t* ss = scale_slot(g) + (tid >> 3) * 4;
 #pragma unroll
     for (int c = 0; c < CD; ++c) {
-      d.w[c] = *reinterpret_cast<const uint32_t*>(cs + c * NT * 4);
+      d.w[c] = *reinterpret_cast<const uint32_t*>(cs + c * (NT / 8) * 64);
       d.sw[c] = *reinterpret_cast<const uint32_t*>(ss + c * (NT / 8) * 4);
     }
   };
@@ -488,25 +508,26 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[ts][ns][r] = 0.0f;
 
-  // Before every barrier: this thread's batch from three steps back (it
-  // carried group g's activations and group g+2's codes) has landed, and its
-  // LDS reads and writes (also the untracked weight reads) are done.
-  auto sync = [&]() __device__ {
+  // Before the barrier of step s: this thread's batch of step s-4 has landed
+  // (the three younger batches may still be in flight: 3 activation loads
+  // sets and one (s even) or two (s odd) code pairs), and its LDS reads and
+  // writes (also the untracked weight reads) are done.
+  auto sync = [&](auto odd) __device__ {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<NB * L>();
+    wait_vm<3 * AI + (decltype(odd)::value ? 2 : 1) * CP>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Step g (SL = g % DS, so g + 2 has the parity of SL).  The memory and
-  // VALU work is spread between the matrix-core instructions, so that one
-  // wave per SIMD keeps the matrix core, the load path, the LDS and the VALU
-  // busy at once:
+  // Step g (SL = g % P, so g has the parity of SL).  The memory and VALU
+  // work is spread between the matrix-core instructions, so that one wave
+  // per SIMD keeps the matrix core, the load path, the LDS and the VALU busy
+  // at once:
   //   * after the barrier, read the code and scale dwords of group g+2;
   //   * k-slice 0 of group g's products (no LDS data needed), each
-  //     instruction followed by its share of the batch's loads (codes of
-  //     g+DCODE, activations of g+DACT);
+  //     instruction followed by its share of the batch's loads (g even: the
+  //     code pair of groups g+DC, g+DC+1; activations of g+DACT);
   //   * wait for the dword reads;
   //   * k-slices 1-3, each led by a third of group g+1's weight reads
   //     (untracked loads, issued after the wait so that no wait of the
@@ -523,16 +544,19 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   };
   auto step = [&](int g, auto slot) __device__ {
     constexpr int SL = decltype(slot)::value;
-    sync();
+    constexpr bool EVEN = (SL & 1) == 0;
+    constexpr int V0 = EVEN ? 0 : CP;          // first load of this step's batch
+    constexpr int NV = CP + AI - V0;           // loads in this step's batch
+    sync(std::integral_constant<bool, !EVEN>{});
     DqRegs d;
     dq_load(g + 2, d);
-    const int gc = min(g + DCODE, Gs - 1), ga = min(g + DACT, Gs - 1);
+    const int q = min((g + DC) >> 1, qlast), ga = min(g + DACT, Gs - 1);
     __builtin_amdgcn_sched_barrier(0);
     static_for<NM>([&](auto jj) {
       constexpr int j = decltype(jj)::value;
       mfma_one(0, j, slot);
       static_for<(j + 1) * NV / NM - j * NV / NM>([&](auto u) {
-        issue_one(gc, ga, act[(SL + DACT) % DA], Slot<j * NV / NM + decltype(u)::value>{});
+        issue_one(q, ga, act[(SL + DACT) % DA], Slot<V0 + j * NV / NM + decltype(u)::value>{});
       });
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -559,15 +583,15 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     });
   };
 
-  // Prologue: codes of groups 0..DS-1 and activations of groups 0..DACT-1 in
-  // flight, then all landed; groups 0 and 1 dequantized; the codes of group
-  // DS (into the slot group 0 used) in flight; group 0's weights read.
-  static_for<DS>([&](auto i) { issue_codes(decltype(i)::value); });
+  // Prologue: code pairs 0..NP-1 (groups 0..2NP-1) and activations of groups
+  // 0..DACT-1 in flight, then all landed; groups 0 and 1 dequantized; group
+  // 0's weights read.
+  static_for<NP>([&](auto i) { issue_codes(decltype(i)::value); });
   static_for<DACT>([&](auto i) { issue_act(decltype(i)::value, act[decltype(i)::value]); });
   // A thread dequantizes its own code dwords but reads row scales that other
   // waves loaded: a barrier after the waits publishes them, and a second one
-  // (which also publishes the weight tiles) orders every read of slot 0
-  // before the load of group DS into it.
+  // (which also publishes the weight tiles) orders every read of pair slot 0
+  // before step 0 loads pair NP into it.
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
@@ -582,7 +606,6 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  issue_codes(DS);
   read_wgt(0, wgt[0]);
   // Steps run in blocks of P (the ring indexes repeat with period P); the
   // block stops after the last group.
