@@ -27,18 +27,23 @@ CFLAGS = [
     "-mcode-object-version=5",
     # packed FP32 vector instructions stay off in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # matrix-core results in ordinary VGPRs: the small-T kernel scales every
-    # group's products with VALU instructions, which cannot read accumulator
-    # registers
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result", "-Wno-unknown-warning-option", "-Wno-cuda-compat",
     "-I", os.path.join(ROOT, "include"),
 ]
 
 
+# Matrix-core results in ordinary VGPRs for every kernel but the tiled one:
+# the small-T kernel scales every group's products with VALU instructions,
+# which cannot read accumulator registers; the tiled kernel keeps its
+# accumulators in AGPRs, away from its VALU work.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_ACC_SOURCES = {"q4lin_tiled.hip"}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+    extra = [] if os.path.basename(src) in AGPR_ACC_SOURCES else VGPR_FORM
+    cmd = [HIPCC] + CFLAGS + extra + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only target feature; drop that note
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

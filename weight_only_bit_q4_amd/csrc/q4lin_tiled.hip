@@ -242,17 +242,19 @@ __device__ __forceinline__ void wait_vm() {
 // waits of its own that count only the loads it knows).
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4)); }
 
-// 16-byte LDS read into accumulation registers (AGPRs), which the matrix
-// cores read as operands directly: a wave's next-group operands wait there
-// while its current ones (in the other AGPR set) are in use, without taking
-// ordinary VGPRs.  The compiler does not track this load: the caller waits
-// (s_waitcnt lgkmcnt) before the registers are read.  The destination is
-// also an input ("+a"), so it stays the register set's own: the compiler may
-// not place it over an operand of a matrix-core instruction issued just
-// before, which could still be reading it when the load returns.
+// 16-byte LDS read of a weight fragment into VGPRs, for the matrix cores'
+// B operand: a wave's next-group fragments arrive there while its current
+// ones (the other register set) are in use.  (The accumulators live in
+// AGPRs, which the matrix cores read and write without the VGPR file, so the
+// dequantization's VALU work has the VGPRs to itself.)  The compiler does not
+// track this load: the caller waits (s_waitcnt lgkmcnt) before the registers
+// are read.  The destination is also an input ("+v"), so it stays the
+// register set's own: the compiler may not place it over an operand of a
+// matrix-core instruction issued just before, which could still be reading
+// it when the load returns.
 template <int OFF>
-__device__ __forceinline__ void lds_read_agpr(f16x8_t& v, uint32_t addr) {
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "+a"(v) : "v"(addr), "i"(OFF));
+__device__ __forceinline__ void lds_read_vgpr(f16x8_t& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "+v"(v) : "v"(addr), "i"(OFF));
 }
 
 // A dequantized weight tile holds 144 bytes per row: the row's 64 float16
@@ -263,7 +265,8 @@ constexpr int kRowBytes = 144;
 // 16-byte buffer load into accumulation registers (AGPRs): the activation
 // fragments go straight from memory (L2) to the registers the matrix cores
 // read.  The compiler does not track this load either: the caller waits
-// (s_waitcnt vmcnt) before the registers are read.  "+a" as above.
+// (s_waitcnt vmcnt) before the registers are read.  The destination is also
+// an input ("+a"), for the reason given above.
 template <int OFF>
 __device__ __forceinline__ void buf_read_agpr(f16x8_t& v, u32x4_t rsrc, uint32_t voff, uint32_t soff) {
   asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4" : "+a"(v) : "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF));
@@ -494,7 +497,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   auto read_wgt_one = [&](int g, f16x8_t (&b)[NS][4], auto ii) __device__ {
     constexpr int ns = decltype(ii)::value / 4, m = decltype(ii)::value % 4;
     const uint32_t wb = lds_base + (uint32_t)(Sh::OFF_W + (g & 1) * Sh::W_B + b_row * kRowBytes + lh * 64);
-    lds_read_agpr<ns * 32 * kRowBytes + m * 16>(b[ns][m], wb);
+    lds_read_vgpr<ns * 32 * kRowBytes + m * 16>(b[ns][m], wb);
   };
   auto read_wgt = [&](int g, f16x8_t (&b)[NS][4]) __device__ {
     static_for<NS * 4>([&](auto i) { read_wgt_one(g, b, i); });
@@ -730,6 +733,7 @@ static int pick_ks(int64_t tiles, int64_t target, int64_t k, int64_t t) {
 
 TiledConfig tiled_pick_config(int64_t n, int64_t k, int64_t t) {
   if (t <= 32) return TiledConfig{1, 1, 1, 1, 1};
+  if (n >= 96 && t > 128 && ((n + 95) / 96) * ((t + 255) / 256) >= 192) return TiledConfig{3, 2, 1, 4, 1};
   if (n >= 192) {
     // 192-row tiles (every 32-row tile would read all the activations again),
     // 64 or 128 tokens; with fewer tiles than CUs, K is split (one
@@ -773,6 +777,7 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   const TiledConfig c = a.cfg;
   if (c.ns == 3 && c.ts == 2 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 2, 2, 2>(a, x16, texp, rexp, part, tpad, stream);
   if (c.ns == 3 && c.ts == 1 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 1, 2, 2>(a, x16, texp, rexp, part, tpad, stream);
+  if (c.ns == 3 && c.ts == 2 && c.wn == 1 && c.wt == 4) return launch_cfg<3, 2, 1, 4>(a, x16, texp, rexp, part, tpad, stream);
   if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 4) return launch_cfg<1, 1, 1, 4>(a, x16, texp, rexp, part, tpad, stream);
   if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 1) return launch_cfg<1, 1, 1, 1>(a, x16, texp, rexp, part, tpad, stream);
   return hipErrorInvalidValue;
