@@ -528,14 +528,16 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // per SIMD keeps the matrix core, the load path, the LDS and the VALU busy
   // at once:
   //   * after the barrier, read the code and scale dwords of group g+2;
-  //   * k-slice 0 of group g's products (no LDS data needed), each
-  //     instruction followed by its share of the batch's loads (g even: the
-  //     code pair of groups g+DC, g+DC+1; activations of g+DACT);
+  //   * k-slice 0 of group g's products (no LDS data needed), with a quarter
+  //     of the batch's loads (g even: the code pair of groups g+DC, g+DC+1;
+  //     activations of g+DACT) between its instructions;
   //   * wait for the dword reads;
-  //   * k-slices 1-3, each led by a third of group g+1's weight reads
-  //     (untracked loads, issued after the wait so that no wait of the
-  //     compiler counts them) and interleaved with the dequantization of a
-  //     third of this thread's dwords of group g+2.
+  //   * k-slices 1-3, each led by a share of the batch's other loads and a
+  //     third of group g+1's weight reads (untracked loads, issued after the
+  //     wait so that no wait of the compiler counts them), interleaved with
+  //     the dequantization of a third of this thread's dwords of group g+2.
+  // (Issued in one burst, the loads of four waves stall their issue behind
+  // the load path for longer than a k-slice takes.)
   // Past the last group the reads and the dequantization touch stale LDS
   // (unused) and the loads repeat the last group, so the step is one basic
   // block.
@@ -555,11 +557,14 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     dq_load(g + 2, d);
     const int q = min((g + DC) >> 1, qlast), ga = min(g + DACT, Gs - 1);
     __builtin_amdgcn_sched_barrier(0);
+    // the batch's loads: a quarter in k-slice 0 (one or two after each
+    // matrix-core instruction), a quarter at the head of each other k-slice
+    constexpr int NV0 = NV / 4;
     static_for<NM>([&](auto jj) {
       constexpr int j = decltype(jj)::value;
       mfma_one(0, j, slot);
-      static_for<(j + 1) * NV / NM - j * NV / NM>([&](auto u) {
-        issue_one(q, ga, act[(SL + DACT) % DA], Slot<V0 + j * NV / NM + decltype(u)::value>{});
+      static_for<(j + 1) * NV0 / NM - j * NV0 / NM>([&](auto u) {
+        issue_one(q, ga, act[(SL + DACT) % DA], Slot<V0 + j * NV0 / NM + decltype(u)::value>{});
       });
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -568,6 +573,10 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     static_for<3>([&](auto ss) {
       constexpr int sl = decltype(ss)::value;
       constexpr int r0 = sl * NS * 4 / 3, r1 = (sl + 1) * NS * 4 / 3;
+      constexpr int u0 = NV0 + sl * (NV - NV0) / 3, u1 = NV0 + (sl + 1) * (NV - NV0) / 3;
+      static_for<u1 - u0>([&](auto u) {
+        issue_one(q, ga, act[(SL + DACT) % DA], Slot<V0 + u0 + decltype(u)::value>{});
+      });
       static_for<r1 - r0>([&](auto u) { read_wgt_one(g + 1, wgt[(SL + 1) & 1], Slot<r0 + decltype(u)::value>{}); });
       __builtin_amdgcn_sched_barrier(0);
       constexpr int c0 = sl * CD / 3, c1 = (sl + 1) * CD / 3;
