@@ -292,7 +292,7 @@ __device__ __forceinline__ u32x4_t make_rsrc_sgpr(const void* base, uint32_t byt
 // (s even) the codes of groups s+2 and s+3, must have landed; the batches of
 // steps s-3 .. s-1 may still be in flight.  The step code is unrolled over P
 // steps, after which every ring index repeats.
-constexpr int NP = 3;
+constexpr int NP = 4;
 constexpr int DC = 6;
 constexpr int DA = 5;
 constexpr int DACT = DA - 1;
@@ -432,8 +432,13 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // 2q+1), v = CQ, CQ+1 the scale dwords of the two groups, then the TS * 4
   // activation fragments of group ga.  Pair and group indexes are clamped to
   // the last ones, so every batch of a kind has the same number of loads.
-  auto code_slot = [&](int q) __device__ { return lds + (q % NP) * Sh::CODE_B; };
-  auto scale_slot = [&](int g) __device__ { return lds + Sh::OFF_S + (((g >> 1) % NP) * 2 + (g & 1)) * Sh::SCALE_B; };
+  // (slot indexes in unsigned arithmetic: NP is a power of two, so the
+  // remainders are masks)
+  static_assert((NP & (NP - 1)) == 0, "pair slots: a power of two");
+  auto code_slot = [&](int q) __device__ { return lds + ((uint32_t)q % NP) * Sh::CODE_B; };
+  auto scale_slot = [&](int g) __device__ {
+    return lds + Sh::OFF_S + ((((uint32_t)g >> 1) % NP) * 2 + ((uint32_t)g & 1)) * Sh::SCALE_B;
+  };
   auto issue_one = [&](int q, int ga, f16x8_t (&a)[TS][4], auto vi) __device__ {
     constexpr int v = decltype(vi)::value;
     if constexpr (v < CQ) {
