@@ -70,35 +70,47 @@ __device__ __forceinline__ u32x4_t to_f16_pairs(u32x4_t v, int e) {
 // [2^11, 2^12), clamped to c in [-4, 15] (so 2^c is a normal float16 and
 // every scaled weight (q - 8) s 2^c stays below 2^15 in magnitude; the
 // smallest float16 scale 2^-24 still scales to a normal 2^-9).  0 for a row
-// of zero scales.  32 rows per workgroup: the rows' scales are one contiguous
-// run, read coalesced, with an LDS maximum per row.
-constexpr int kRowsPerBlock = 32;
+// of zero scales.  64 rows per workgroup.
+constexpr int kRowsPerBlock = 64;
+__device__ __forceinline__ uint32_t max_mag_f16x8(u32x4_t v) {
+  const uint32_t a = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), b = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
+  const uint32_t c = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), d = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
+  return max(max(a, b), max(c, d));
+}
+// One lane per row (the block's first wave): the row's scales are read as
+// 16-byte pieces when the rows are 16-byte aligned (G a multiple of 8), else
+// one by one; eight loads in flight per round.
 __device__ void row_exponents(const uint16_t* __restrict__ scales, int N, int G, int r0, int* __restrict__ rexp) {
-  __shared__ uint32_t rmax[kRowsPerBlock];
-  const int tid = threadIdx.x;
-  if (tid < kRowsPerBlock) rmax[tid] = 0u;
-  __syncthreads();
-  const int rows = min(kRowsPerBlock, N - r0);
-  const int cnt = rows * G;  // <= 2^19
-  const uint16_t* s = scales + (int64_t)r0 * G;
-  for (int i0 = 0; i0 < cnt; i0 += 256 * 16) {
-    uint32_t v[16];
+  const int r = r0 + (int)threadIdx.x;
+  if (threadIdx.x >= kRowsPerBlock || r >= N) return;
+  const uint16_t* s = scales + (int64_t)r * G;
+  uint32_t m = 0;
+  if ((G & 7) == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) {
+    const int nv = G >> 3;
+    const u32x4_t* s4 = reinterpret_cast<const u32x4_t*>(s);
+    for (int c0 = 0; c0 < nv; c0 += 8) {
+      u32x4_t v[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = s[min(i0 + j * 256 + tid, cnt - 1)] & 0x7FFFu;
+      for (int i = 0; i < 8; ++i) v[i] = s4[min(c0 + i, nv - 1)];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) atomicMax(&rmax[min(i0 + j * 256 + tid, cnt - 1) / G], v[j]);
-  }
-  __syncthreads();
-  if (tid < rows) {
-    uint32_t m = rmax[tid];
-    if (m >= 0x7C00u) m = 0x7BFFu;  // Inf/NaN scales are outside the contract
-    int c = 0;
-    if (m != 0u) {
-      const int lg = (m >= 0x400u) ? (int)(m >> 10) - 15 : (31 - __builtin_clz(m)) - 24;  // floor(log2 |s|)
-      c = min(max(11 - lg, -4), 15);
+      for (int i = 0; i < 8; ++i) m = max(m, max_mag_f16x8(v[i]));
     }
-    rexp[r0 + tid] = c;
+  } else {
+    for (int c0 = 0; c0 < G; c0 += 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = s[min(c0 + i, G - 1)] & 0x7FFFu;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = max(m, v[i]);
+    }
   }
+  if (m >= 0x7C00u) m = 0x7BFFu;  // Inf/NaN scales are outside the contract
+  int c = 0;
+  if (m != 0u) {
+    const int lg = (m >= 0x400u) ? (int)(m >> 10) - 15 : (31 - __builtin_clz(m)) - 24;  // floor(log2 |s|)
+    c = min(max(11 - lg, -4), 15);
+  }
+  rexp[r] = c;
 }
 
 // Per-token exponent e[t] from the token's largest magnitude m (bf16 bits
@@ -117,15 +129,20 @@ __device__ __forceinline__ void store_piece(u32x4_t* __restrict__ x16, int G, in
   x16[((size_t)(t >> 5) * G + g) * 256 + ((kb & 3) * 2 + (kb >> 2)) * 32 + (t & 31)] = v;
 }
 
-// Activation preparation, one pass: one wave per token of the padded token
-// range loads the token's values (16-byte pieces), takes the largest
-// magnitude, picks e[t] and writes the float16 values in tile order; padding
-// tokens write zeros.  Rows of up to 8192 values stay in registers between
-// the two steps; longer rows are read a second time (from L2).  The blocks
-// past the token blocks compute the row exponents.
-constexpr int kPrepWaves = 4;
-constexpr int kPieces = 16;
-__global__ void __launch_bounds__(64 * kPrepWaves)
+// Activation preparation, one pass: a workgroup of sixteen waves takes eight
+// consecutive tokens of the padded token range, wave w the w-th sixteenth of
+// their 16-byte pieces; lane l serves token l % 8 and pieces l / 8 + 8 j of
+// the wave's share.  So every load instruction reads 128-byte runs of eight
+// token rows and every store writes whole 128-byte runs of the tile order
+// (eight consecutive tokens of a 32-token block).  The token's largest
+// magnitude is combined over the lanes and then, through LDS, over the
+// waves; the values wait in registers (up to MAXJ pieces per lane; longer
+// rows are read a second time, from L2).  Padding tokens write zeros.  The
+// blocks past the token blocks compute the row exponents.
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepTokens = 8;
+template <int MAXJ>
+__global__ void __launch_bounds__(kPrepThreads)
 prep_act_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __restrict__ texp,
                 u32x4_t* __restrict__ x16, const uint16_t* __restrict__ scales, int N, int* __restrict__ rexp,
                 int tok_blocks) {
@@ -133,53 +150,61 @@ prep_act_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __re
     row_exponents(scales, N, K >> 6, ((int)blockIdx.x - tok_blocks) * kRowsPerBlock, rexp);
     return;
   }
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
-  if (t >= Tpad) return;
+  __shared__ uint32_t wmax[kPrepThreads / 64][kPrepTokens];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i8 = lane & 7, sub = lane >> 3;
+  const int t = blockIdx.x * kPrepTokens + i8;          // < Tpad (a multiple of 32)
+  const bool real = t < T;
   const int nb = K >> 3, G = K >> 6;
-  if (t >= T) {
-    for (int p = lane; p < nb; p += 64) store_piece(x16, G, t, p, u32x4_t{0u, 0u, 0u, 0u});
-    if (lane == 0) texp[t] = 0;
-    return;
-  }
-  const u32x4_t* xt = x + (size_t)t * nb;
+  constexpr int NWV = kPrepThreads / 64;
+  const int pw = (nb + NWV - 1) / NWV;                  // pieces per wave
+  const int pb = wave * pw, pe = min(pb + pw, nb);
+  const int nj = (pw + 7) / 8;                          // pieces per lane
+  const u32x4_t* xt = x + (size_t)min(t, T - 1) * nb;  // padding tokens read a valid row
   uint32_t m = 0;
-  int e;
-  // all loads of a round first, from clamped (valid) addresses: a load
-  // behind a branch would be waited for on its own
-  if (nb <= 64 * kPieces) {
-    u32x4_t v[kPieces];
+  u32x4_t v[MAXJ];
+  if (nj <= MAXJ) {
 #pragma unroll
-    for (int j = 0; j < kPieces; ++j) v[j] = xt[min(lane + 64 * j, nb - 1)];
+    for (int j = 0; j < MAXJ; ++j) v[j] = xt[min(pb + sub + 8 * j, nb - 1)];
 #pragma unroll
-    for (int j = 0; j < kPieces; ++j) m = max(m, max_mag8(v[j]));
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    e = token_exponent(m);
-#pragma unroll
-    for (int j = 0; j < kPieces; ++j)
-      if (lane + 64 * j < nb) store_piece(x16, G, t, lane + 64 * j, to_f16_pairs(v[j], e));
+    for (int j = 0; j < MAXJ; ++j)
+      if (pb + sub + 8 * j < pe) m = max(m, max_mag8(v[j]));
   } else {
-    for (int b0 = 0; b0 < nb; b0 += 64 * kPieces) {
-      u32x4_t v[kPieces];
+    for (int b0 = pb; b0 < pe; b0 += 8 * MAXJ) {
 #pragma unroll
-      for (int j = 0; j < kPieces; ++j) v[j] = xt[min(b0 + lane + 64 * j, nb - 1)];
+      for (int j = 0; j < MAXJ; ++j) v[j] = xt[min(b0 + sub + 8 * j, nb - 1)];
 #pragma unroll
-      for (int j = 0; j < kPieces; ++j) m = max(m, max_mag8(v[j]));
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    e = token_exponent(m);
-    for (int b0 = 0; b0 < nb; b0 += 64 * kPieces) {
-      u32x4_t v[kPieces];
-#pragma unroll
-      for (int j = 0; j < kPieces; ++j) v[j] = xt[min(b0 + lane + 64 * j, nb - 1)];
-#pragma unroll
-      for (int j = 0; j < kPieces; ++j)
-        if (b0 + lane + 64 * j < nb) store_piece(x16, G, t, b0 + lane + 64 * j, to_f16_pairs(v[j], e));
+      for (int j = 0; j < MAXJ; ++j)
+        if (b0 + sub + 8 * j < pe) m = max(m, max_mag8(v[j]));
     }
   }
-  if (lane == 0) texp[t] = e;
+  // lanes of one token: l % 8 equal
+  m = max(m, (uint32_t)__shfl_xor((int)m, 8));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+  if (sub == 0) wmax[wave][i8] = m;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kPrepThreads / 64; ++w) m = max(m, wmax[w][i8]);
+  const int e = real ? token_exponent(m) : 0;
+  if (nj <= MAXJ) {
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int p = pb + sub + 8 * j;
+      if (p < pe) store_piece(x16, G, t, p, real ? to_f16_pairs(v[j], e) : u32x4_t{0u, 0u, 0u, 0u});
+    }
+  } else {
+    for (int b0 = pb; b0 < pe; b0 += 8 * MAXJ) {
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j) v[j] = xt[min(b0 + sub + 8 * j, nb - 1)];
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j) {
+        const int p = b0 + sub + 8 * j;
+        if (p < pe) store_piece(x16, G, t, p, real ? to_f16_pairs(v[j], e) : u32x4_t{0u, 0u, 0u, 0u});
+      }
+    }
+  }
+  if (wave == 0 && sub == 0) texp[t] = e;
 }
 
 // ---------------------------------------------------------------------------
@@ -780,10 +805,20 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   {
     const u32x4_t* x = static_cast<const u32x4_t*>(a.x);
     int k = (int)a.k, t = (int)a.t, n = (int)a.n, tpad = (int)tp;
-    const int tok_blocks = (int)((tp + kPrepWaves - 1) / kPrepWaves);
+    const int tok_blocks = (int)(tp / kPrepTokens);
     const int row_blocks = (int)((a.n + kRowsPerBlock - 1) / kRowsPerBlock);
-    prep_act_kernel<<<dim3((unsigned)(tok_blocks + row_blocks)), dim3(64 * kPrepWaves), 0, stream>>>(
-        x, k, t, tpad, texp, x16, static_cast<const uint16_t*>(a.scales), n, rexp, tok_blocks);
+    const int nwv = kPrepThreads / 64;
+    const int nj = (int)(((a.k / 8 + nwv - 1) / nwv + 7) / 8);  // pieces per lane
+    const dim3 grid((unsigned)(tok_blocks + row_blocks)), block(kPrepThreads);
+    const uint16_t* sc = static_cast<const uint16_t*>(a.scales);
+    if (nj <= 2)
+      prep_act_kernel<2><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
+    else if (nj <= 5)
+      prep_act_kernel<5><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
+    else if (nj <= 10)
+      prep_act_kernel<10><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
+    else
+      prep_act_kernel<16><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
