@@ -316,14 +316,17 @@ __device__ __forceinline__ u32x4_t make_rsrc_sgpr(const void* base, uint32_t byt
 // step s the batch of step s-4, which carries group s's activations and
 // (s even) the codes of groups s+2 and s+3, must have landed; the batches of
 // steps s-3 .. s-1 may still be in flight.  The step code is unrolled over P
-// steps, after which every ring index repeats.
-constexpr int NP = 4;
+// steps, a multiple of every ring period (2 NP groups for the pair slots, DA
+// for the register sets, 2 for the weight tiles), so that every slot, tile
+// and register set a step touches is fixed by its position in the block:
+// LDS addresses are immediates and no step computes an index.
+constexpr int NP = 5;
 constexpr int DC = 6;
 constexpr int DA = 5;
 constexpr int DACT = DA - 1;
 constexpr int P = 10;
 static_assert(DC <= 2 * NP && DC % 2 == 0 && DACT == 4 && DC - 2 == DACT, "ring geometry");
-static_assert(P % DA == 0 && P % 2 == 0, "the unrolled steps must cover every ring period");
+static_assert(P % DA == 0 && P % (2 * NP) == 0, "the unrolled steps must cover every ring period");
 
 template <int NS, int TS, int WN, int WT>
 struct TiledShape {
@@ -420,6 +423,8 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
                               (uint32_t)min((int64_t)(N - n0) * G * 2 + 4, (int64_t)0x7FFFFFFF));
   const uint32_t s_lane = (uint32_t)(s_first - s_base) + (uint32_t)(min(tid % BN, N - 1 - n0) * G * 2);
   const uint32_t soff0 = s_lane & ~3u, soff1 = (s_lane + 2) & ~3u;
+  // soffp[j]: the offset for groups 2q + j (parity of g0 + j)
+  const uint32_t soffp[2] = {(g0 & 1) ? soff1 : soff0, (g0 & 1) ? soff0 : soff1};
   // Code dword c of this thread belongs to tile row (c * NT + tid) / 8, whose
   // scale sits in the dword loaded by the thread of that number, in its high
   // half when (the scale's byte offset) / 2 is odd.  s_sel[c] is the byte
@@ -457,33 +462,37 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // 2q+1), v = CQ, CQ+1 the scale dwords of the two groups, then the TS * 4
   // activation fragments of group ga.  Pair and group indexes are clamped to
   // the last ones, so every batch of a kind has the same number of loads.
-  // (slot indexes in unsigned arithmetic: NP is a power of two, so the
-  // remainders are masks)
-  static_assert((NP & (NP - 1)) == 0, "pair slots: a power of two");
-  auto code_slot = [&](int q) __device__ { return lds + ((uint32_t)q % NP) * Sh::CODE_B; };
-  auto scale_slot = [&](int g) __device__ {
-    return lds + Sh::OFF_S + ((((uint32_t)g >> 1) % NP) * 2 + ((uint32_t)g & 1)) * Sh::SCALE_B;
+  // Slots are compile-time: pair p sits in slot p % NP, and QS below is a
+  // pair index whose remainder equals the real pair's (the real index may
+  // be clamped to the last pair: such a load lands in the slot of a pair
+  // past the end, which nothing reads).
+  auto code_slot = [&](auto qs) __device__ { return lds + (decltype(qs)::value % NP) * Sh::CODE_B; };
+  auto scale_slot = [&](auto qs, auto par) __device__ {
+    return lds + Sh::OFF_S + ((decltype(qs)::value % NP) * 2 + decltype(par)::value) * Sh::SCALE_B;
   };
-  auto issue_one = [&](int q, int ga, f16x8_t (&a)[TS][4], auto vi) __device__ {
+  auto issue_one = [&](int q, auto qs, int ga, f16x8_t (&a)[TS][4], auto vi) __device__ {
     constexpr int v = decltype(vi)::value;
     if constexpr (v < CQ) {
-      dma16(rc, coff[v], (uint32_t)(g0 + 2 * q) * 32, code_slot(q) + (v * NW + wave) * 1024);
+      dma16(rc, coff[v], (uint32_t)(g0 + 2 * q) * 32, code_slot(qs) + (v * NW + wave) * 1024);
     } else if constexpr (v < CQ + 2) {
+      // (a group clamped to the last one takes the other parity's offset:
+      // an in-bounds dword for a group past the end, which nothing reads)
       const int gs = min(2 * q + (v - CQ), Gs - 1);
-      dma4(rs, ((g0 + gs) & 1) ? soff1 : soff0, (uint32_t)((g0 + gs) >> 1) * 4, scale_slot(2 * q + (v - CQ)) + wave * 256);
+      dma4(rs, soffp[v - CQ], (uint32_t)((g0 + gs) >> 1) * 4,
+           scale_slot(qs, std::integral_constant<int, v - CQ>{}) + wave * 256);
     } else {
       constexpr int i = v - CQ - 2, ts = i / 4, m = i % 4;
       buf_read_agpr<m * 1024>(a[ts][m], rx, aoff[ts], (uint32_t)(g0 + ga) * 4096);
     }
   };
   const int qlast = (Gs - 1) >> 1;
-  auto issue_codes = [&](int q) __device__ {
-    q = min(q, qlast);
-    static_for<CP>([&](auto v) { issue_one(q, 0, act[0], v); });
+  auto issue_codes = [&](auto qs) __device__ {
+    const int q = min((int)decltype(qs)::value, qlast);
+    static_for<CP>([&](auto v) { issue_one(q, qs, 0, act[0], v); });
   };
   auto issue_act = [&](int ga, f16x8_t (&a)[TS][4]) __device__ {
     ga = min(ga, Gs - 1);
-    static_for<TS * 4>([&](auto i) { issue_one(0, ga, a, Slot<CP + decltype(i)::value>{}); });
+    static_for<TS * 4>([&](auto i) { issue_one(0, Slot<0>{}, ga, a, Slot<CP + decltype(i)::value>{}); });
   };
 
   // --- dequantization of group g into weight tile b, in two halves: the LDS
@@ -494,43 +503,43 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     uint32_t w[CD];
     uint32_t sw[CD];
   };
-  // code dword c of this thread: row (c*NT + tid)/8, dword tid%8 of group
-  // g's 32 bytes in the row's 64-byte pair
-  auto dq_load = [&](int g, DqRegs& d) __device__ {
-    const uint8_t* cs = code_slot(g >> 1) + (tid >> 3) * 64 + (g & 1) * 32 + (tid & 7) * 4;
-    const uint8_t* ss = scale_slot(g) + (tid >> 3) * 4;
+  // code dword c of this thread: row (c*NT + tid)/8, dword tid%8 of the
+  // group's 32 bytes in the row's 64-byte pair (pair slot of QS, group
+  // parity PAR)
+  auto dq_load = [&](auto qs, auto par, DqRegs& d) __device__ {
+    const uint8_t* cs = code_slot(qs) + (tid >> 3) * 64 + decltype(par)::value * 32 + (tid & 7) * 4;
+    const uint8_t* ss = scale_slot(qs, par) + (tid >> 3) * 4;
 #pragma unroll
     for (int c = 0; c < CD; ++c) {
       d.w[c] = *reinterpret_cast<const uint32_t*>(cs + c * (NT / 8) * 64);
       d.sw[c] = *reinterpret_cast<const uint32_t*>(ss + c * (NT / 8) * 4);
     }
   };
-  // Group g (of parity ODD) into weight tile b with the scales s' = s 2^c[row]
-  // (exact unless s lies 2^25 or more below the row's largest scale); groups
-  // past the end get s' = 0 (the clamped loads repeat the last group).
-  auto dq_store_one = [&](int g, int b, const DqRegs& d, auto odd, int c) __device__ {
-    uint8_t* wb = lds + Sh::OFF_W + b * Sh::W_B + dq_off;
+  // A group (of parity ODD) into weight tile B with the scales s' = s 2^c[row]
+  // (exact unless s lies 2^25 or more below the row's largest scale).  Tiles
+  // of groups past the end hold whatever the clamped loads brought; no
+  // matrix-core instruction reads them.
+  auto dq_store_one = [&](auto b, const DqRegs& d, auto odd, int c) __device__ {
+    uint8_t* wb = lds + Sh::OFF_W + decltype(b)::value * Sh::W_B + dq_off;
     const uint32_t sel = decltype(odd)::value ? (s_sel[c] ^ 0x02020202u) : s_sel[c];
     const f16x2_t s2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(d.sw[c], d.sw[c], sel));
-    uint32_t sp = __builtin_bit_cast(uint32_t, s2 * __builtin_bit_cast(f16x2_t, s_mul[c]));
-    sp = g < Gs ? sp : 0u;
+    const uint32_t sp = __builtin_bit_cast(uint32_t, s2 * __builtin_bit_cast(f16x2_t, s_mul[c]));
     *reinterpret_cast<u32x4_t*>(wb + c * (NT / 8) * kRowBytes) = dequant_dword(d.w[c], sp);
   };
-  auto dq_store = [&](int g, int b, const DqRegs& d, auto odd) __device__ {
+  auto dq_store = [&](auto b, const DqRegs& d, auto odd) __device__ {
 #pragma unroll
-    for (int c = 0; c < CD; ++c) dq_store_one(g, b, d, odd, c);
+    for (int c = 0; c < CD; ++c) dq_store_one(b, d, odd, c);
   };
 
-  // --- weight fragments and scales of group g (tile g & 1) --------------------
+  // --- weight fragments of the group in tile TB --------------------------------
   const int b_row = wn * NS * 32 + li;                                  // + ns*32
-  const uint32_t lds_base = (uint32_t)reinterpret_cast<uintptr_t>(lds);
-  auto read_wgt_one = [&](int g, f16x8_t (&b)[NS][4], auto ii) __device__ {
+  const uint32_t wrd = (uint32_t)reinterpret_cast<uintptr_t>(lds) + (uint32_t)(Sh::OFF_W + b_row * kRowBytes + lh * 64);
+  auto read_wgt_one = [&](auto tb, f16x8_t (&b)[NS][4], auto ii) __device__ {
     constexpr int ns = decltype(ii)::value / 4, m = decltype(ii)::value % 4;
-    const uint32_t wb = lds_base + (uint32_t)(Sh::OFF_W + (g & 1) * Sh::W_B + b_row * kRowBytes + lh * 64);
-    lds_read_vgpr<ns * 32 * kRowBytes + m * 16>(b[ns][m], wb);
+    lds_read_vgpr<decltype(tb)::value * Sh::W_B + ns * 32 * kRowBytes + m * 16>(b[ns][m], wrd);
   };
-  auto read_wgt = [&](int g, f16x8_t (&b)[NS][4]) __device__ {
-    static_for<NS * 4>([&](auto i) { read_wgt_one(g, b, i); });
+  auto read_wgt = [&](auto tb, f16x8_t (&b)[NS][4]) __device__ {
+    static_for<NS * 4>([&](auto i) { read_wgt_one(tb, b, i); });
   };
 
   f32x16_t acc[TS][NS];
@@ -568,9 +577,9 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   //     the dequantization of a third of this thread's dwords of group g+2.
   // (Issued in one burst, the loads of four waves stall their issue behind
   // the load path for longer than a k-slice takes.)
-  // Past the last group the reads and the dequantization touch stale LDS
-  // (unused) and the loads repeat the last group, so the step is one basic
-  // block.
+  // Near the last group the reads and the dequantization of groups past the
+  // end touch stale LDS (unused) and the loads repeat the last group, so the
+  // step is one basic block.
   constexpr int NM = TS * NS;               // matrix-core instructions per k-slice
   auto mfma_one = [&](int m, int j, auto slot) __device__ {
     constexpr int SL = decltype(slot)::value;
@@ -582,9 +591,13 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     constexpr bool EVEN = (SL & 1) == 0;
     constexpr int V0 = EVEN ? 0 : CP;          // first load of this step's batch
     constexpr int NV = CP + AI - V0;           // loads in this step's batch
+    // g = gb + SL with gb a multiple of P: the pair of group g+2 sits in
+    // slot ((SL + 2) >> 1) % NP, the pair this step loads in slot
+    // ((SL + DC) >> 1) % NP, and g, g+2 have the parity of SL
+    constexpr int QD = (SL + 2) >> 1, QL = (SL + DC) >> 1;
     sync(std::integral_constant<bool, !EVEN>{});
     DqRegs d;
-    dq_load(g + 2, d);
+    dq_load(Slot<QD>{}, std::integral_constant<int, SL & 1>{}, d);
     const int q = min((g + DC) >> 1, qlast), ga = min(g + DACT, Gs - 1);
     __builtin_amdgcn_sched_barrier(0);
     // the batch's loads: a quarter in k-slice 0 (one or two after each
@@ -594,7 +607,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
       constexpr int j = decltype(jj)::value;
       mfma_one(0, j, slot);
       static_for<(j + 1) * NV0 / NM - j * NV0 / NM>([&](auto u) {
-        issue_one(q, ga, act[(SL + DACT) % DA], Slot<V0 + j * NV0 / NM + decltype(u)::value>{});
+        issue_one(q, Slot<QL>{}, ga, act[(SL + DACT) % DA], Slot<V0 + j * NV0 / NM + decltype(u)::value>{});
       });
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -605,15 +618,17 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
       constexpr int r0 = sl * NS * 4 / 3, r1 = (sl + 1) * NS * 4 / 3;
       constexpr int u0 = NV0 + sl * (NV - NV0) / 3, u1 = NV0 + (sl + 1) * (NV - NV0) / 3;
       static_for<u1 - u0>([&](auto u) {
-        issue_one(q, ga, act[(SL + DACT) % DA], Slot<V0 + u0 + decltype(u)::value>{});
+        issue_one(q, Slot<QL>{}, ga, act[(SL + DACT) % DA], Slot<V0 + u0 + decltype(u)::value>{});
       });
-      static_for<r1 - r0>([&](auto u) { read_wgt_one(g + 1, wgt[(SL + 1) & 1], Slot<r0 + decltype(u)::value>{}); });
+      static_for<r1 - r0>([&](auto u) {
+        read_wgt_one(Slot<(SL + 1) & 1>{}, wgt[(SL + 1) & 1], Slot<r0 + decltype(u)::value>{});
+      });
       __builtin_amdgcn_sched_barrier(0);
       constexpr int c0 = sl * CD / 3, c1 = (sl + 1) * CD / 3;
 #pragma unroll
       for (int j = 0; j < NM; ++j) mfma_one(sl + 1, j, slot);
 #pragma unroll
-      for (int c = c0; c < c1; ++c) dq_store_one(g + 2, g & 1, d, std::integral_constant<bool, (SL & 1) != 0>{}, c);
+      for (int c = c0; c < c1; ++c) dq_store_one(Slot<SL & 1>{}, d, std::integral_constant<bool, (SL & 1) != 0>{}, c);
       // one matrix-core instruction, then a share of the VALU work
       constexpr int kValu = ((c1 - c0) * 18 + NM - 1) / NM;
 #pragma unroll
@@ -625,10 +640,10 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     });
   };
 
-  // Prologue: code pairs 0..NP-1 (groups 0..2NP-1) and activations of groups
-  // 0..DACT-1 in flight, then all landed; groups 0 and 1 dequantized; group
-  // 0's weights read.
-  static_for<NP>([&](auto i) { issue_codes(decltype(i)::value); });
+  // Prologue: code pairs 0..DC/2-1 (groups 0..DC-1; step 0 loads the next)
+  // and activations of groups 0..DACT-1 in flight, then all landed; groups 0
+  // and 1 dequantized; group 0's weights read.
+  static_for<DC / 2>([&](auto i) { issue_codes(i); });
   static_for<DACT>([&](auto i) { issue_act(decltype(i)::value, act[decltype(i)::value]); });
   // A thread dequantizes its own code dwords but reads row scales that other
   // waves loaded: a barrier after the waits publishes them, and a second one
@@ -640,18 +655,21 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   __builtin_amdgcn_sched_barrier(0);
   {
     DqRegs d;
-    dq_load(0, d);
-    dq_store(0, 0, d, std::false_type{});
-    dq_load(1, d);
-    dq_store(1, 1, d, std::true_type{});
+    dq_load(Slot<0>{}, std::integral_constant<int, 0>{}, d);
+    dq_store(Slot<0>{}, d, std::false_type{});
+    dq_load(Slot<0>{}, std::integral_constant<int, 1>{}, d);
+    dq_store(Slot<1>{}, d, std::true_type{});
   }
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_wgt(0, wgt[0]);
-  // Steps run in blocks of P (the ring indexes repeat with period P); the
-  // block stops after the last group.
-  for (int gb = 0; gb < Gs; gb += P) {
+  read_wgt(Slot<0>{}, wgt[0]);
+  // Steps run in blocks of P (the ring indexes repeat with period P): whole
+  // blocks without a test, then the last partial block, which stops after
+  // the last group.
+  int gb = 0;
+  for (; gb + P <= Gs; gb += P) static_for<P>([&](auto sl) { step(gb + decltype(sl)::value, sl); });
+  if (gb < Gs) {
     static_for<P>([&](auto sl) {
       constexpr int SL = decltype(sl)::value;
       if (SL == 0 || gb + SL < Gs) step(gb + SL, sl);
@@ -815,10 +833,8 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
       prep_act_kernel<2><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
     else if (nj <= 5)
       prep_act_kernel<5><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
-    else if (nj <= 10)
+    else  // longer rows (nj > 10) take the chunked two-pass form of the same kernel
       prep_act_kernel<10><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
-    else
-      prep_act_kernel<16><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
