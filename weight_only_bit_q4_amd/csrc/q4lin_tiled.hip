@@ -70,40 +70,46 @@ __device__ __forceinline__ u32x4_t to_f16_pairs(u32x4_t v, int e) {
 // [2^11, 2^12), clamped to c in [-4, 15] (so 2^c is a normal float16 and
 // every scaled weight (q - 8) s 2^c stays below 2^15 in magnitude; the
 // smallest float16 scale 2^-24 still scales to a normal 2^-9).  0 for a row
-// of zero scales.  64 rows per workgroup.
-constexpr int kRowsPerBlock = 64;
+// of zero scales.  Eight lanes per row, 128 rows per workgroup.
+constexpr int kRowLanes = 8;
 __device__ __forceinline__ uint32_t max_mag_f16x8(u32x4_t v) {
   const uint32_t a = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), b = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
   const uint32_t c = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu), d = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
   return max(max(a, b), max(c, d));
 }
-// One lane per row (the block's first wave): the row's scales are read as
-// 16-byte pieces when the rows are 16-byte aligned (G a multiple of 8), else
-// one by one; eight loads in flight per round.
+// Lane l of a row reads the row's 16-byte pieces l, l+8, ... when the rows
+// are 16-byte aligned (G a multiple of 8), else its scales l, l+8, ...; four
+// loads in flight per round (one round for rows of up to 32 pieces, K up to
+// 16384); the eight lanes then combine their maxima.
 __device__ void row_exponents(const uint16_t* __restrict__ scales, int N, int G, int r0, int* __restrict__ rexp) {
-  const int r = r0 + (int)threadIdx.x;
-  if (threadIdx.x >= kRowsPerBlock || r >= N) return;
-  const uint16_t* s = scales + (int64_t)r * G;
+  const int r = r0 + (int)threadIdx.x / kRowLanes, sub = (int)threadIdx.x % kRowLanes;
   uint32_t m = 0;
-  if ((G & 7) == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) {
-    const int nv = G >> 3;
-    const u32x4_t* s4 = reinterpret_cast<const u32x4_t*>(s);
-    for (int c0 = 0; c0 < nv; c0 += 8) {
-      u32x4_t v[8];
+  if (r < N) {
+    const uint16_t* s = scales + (int64_t)r * G;
+    if ((G & 7) == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) {
+      const int nv = G >> 3;
+      const u32x4_t* s4 = reinterpret_cast<const u32x4_t*>(s);
+      for (int c0 = sub; c0 < nv; c0 += 4 * kRowLanes) {
+        u32x4_t v[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = s4[min(c0 + i, nv - 1)];
+        for (int i = 0; i < 4; ++i) v[i] = s4[min(c0 + i * kRowLanes, nv - 1)];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, max_mag_f16x8(v[i]));
-    }
-  } else {
-    for (int c0 = 0; c0 < G; c0 += 8) {
-      uint32_t v[8];
+        for (int i = 0; i < 4; ++i) m = max(m, max_mag_f16x8(v[i]));
+      }
+    } else {
+      for (int c0 = sub; c0 < G; c0 += 4 * kRowLanes) {
+        uint32_t v[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = s[min(c0 + i, G - 1)] & 0x7FFFu;
+        for (int i = 0; i < 4; ++i) v[i] = s[min(c0 + i * kRowLanes, G - 1)] & 0x7FFFu;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, v[i]);
+        for (int i = 0; i < 4; ++i) m = max(m, v[i]);
+      }
     }
   }
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+  if (r >= N || sub != 0) return;
   if (m >= 0x7C00u) m = 0x7BFFu;  // Inf/NaN scales are outside the contract
   int c = 0;
   if (m != 0u) {
@@ -129,19 +135,22 @@ __device__ __forceinline__ void store_piece(u32x4_t* __restrict__ x16, int G, in
   x16[((size_t)(t >> 5) * G + g) * 256 + ((kb & 3) * 2 + (kb >> 2)) * 32 + (t & 31)] = v;
 }
 
-// Activation preparation, one pass: a workgroup of sixteen waves takes eight
-// consecutive tokens of the padded token range, wave w the w-th sixteenth of
-// their 16-byte pieces; lane l serves token l % 8 and pieces l / 8 + 8 j of
-// the wave's share.  So every load instruction reads 128-byte runs of eight
-// token rows and every store writes whole 128-byte runs of the tile order
-// (eight consecutive tokens of a 32-token block).  The token's largest
-// magnitude is combined over the lanes and then, through LDS, over the
-// waves; the values wait in registers (up to MAXJ pieces per lane; longer
-// rows are read a second time, from L2).  Padding tokens write zeros.  The
-// blocks past the token blocks compute the row exponents.
-constexpr int kPrepThreads = 1024;
-constexpr int kPrepTokens = 8;
-template <int MAXJ>
+// Activation preparation, one pass: a workgroup of eight waves takes TOK
+// consecutive tokens of the padded token range (2 for short prompts, so that
+// the few tokens still spread over many CUs; 4 for long ones), wave w the
+// w-th eighth of their 16-byte pieces; lane l serves token l % TOK and
+// pieces l / TOK + (64 / TOK) j of the wave's share.  So every load
+// instruction reads runs of 64 * 16 / TOK bytes of TOK token rows and every
+// store writes whole 16 TOK-byte runs of the tile order (TOK consecutive
+// tokens of a 32-token block).  The token's largest magnitude is combined
+// over the lanes and then, through LDS, over the waves; the values wait in
+// registers (up to MAXJ pieces per lane; longer rows are read a second time,
+// from L2).  Padding tokens write zeros.  The blocks past the token blocks
+// compute the row exponents.
+constexpr int kPrepThreads = 512;
+constexpr int kRowsPerBlock = kPrepThreads / kRowLanes;
+constexpr int prep_tokens(int64_t t) { return t <= 128 ? 2 : 4; }
+template <int MAXJ, int TOK>
 __global__ void __launch_bounds__(kPrepThreads)
 prep_act_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __restrict__ texp,
                 u32x4_t* __restrict__ x16, const uint16_t* __restrict__ scales, int N, int* __restrict__ rexp,
@@ -150,56 +159,56 @@ prep_act_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __re
     row_exponents(scales, N, K >> 6, ((int)blockIdx.x - tok_blocks) * kRowsPerBlock, rexp);
     return;
   }
-  __shared__ uint32_t wmax[kPrepThreads / 64][kPrepTokens];
+  constexpr int SUBS = 64 / TOK;                         // lanes per token in a wave
+  __shared__ uint32_t wmax[kPrepThreads / 64][TOK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i8 = lane & 7, sub = lane >> 3;
-  const int t = blockIdx.x * kPrepTokens + i8;          // < Tpad (a multiple of 32)
+  const int itok = lane % TOK, sub = lane / TOK;
+  const int t = blockIdx.x * TOK + itok;                // < Tpad (a multiple of 32)
   const bool real = t < T;
   const int nb = K >> 3, G = K >> 6;
   constexpr int NWV = kPrepThreads / 64;
   const int pw = (nb + NWV - 1) / NWV;                  // pieces per wave
   const int pb = wave * pw, pe = min(pb + pw, nb);
-  const int nj = (pw + 7) / 8;                          // pieces per lane
+  const int nj = (pw + SUBS - 1) / SUBS;                // pieces per lane
   const u32x4_t* xt = x + (size_t)min(t, T - 1) * nb;  // padding tokens read a valid row
   uint32_t m = 0;
   u32x4_t v[MAXJ];
   if (nj <= MAXJ) {
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) v[j] = xt[min(pb + sub + 8 * j, nb - 1)];
+    for (int j = 0; j < MAXJ; ++j) v[j] = xt[min(pb + sub + SUBS * j, nb - 1)];
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j)
-      if (pb + sub + 8 * j < pe) m = max(m, max_mag8(v[j]));
+      if (pb + sub + SUBS * j < pe) m = max(m, max_mag8(v[j]));
   } else {
-    for (int b0 = pb; b0 < pe; b0 += 8 * MAXJ) {
+    for (int b0 = pb; b0 < pe; b0 += SUBS * MAXJ) {
 #pragma unroll
-      for (int j = 0; j < MAXJ; ++j) v[j] = xt[min(b0 + sub + 8 * j, nb - 1)];
+      for (int j = 0; j < MAXJ; ++j) v[j] = xt[min(b0 + sub + SUBS * j, nb - 1)];
 #pragma unroll
       for (int j = 0; j < MAXJ; ++j)
-        if (b0 + sub + 8 * j < pe) m = max(m, max_mag8(v[j]));
+        if (b0 + sub + SUBS * j < pe) m = max(m, max_mag8(v[j]));
     }
   }
-  // lanes of one token: l % 8 equal
-  m = max(m, (uint32_t)__shfl_xor((int)m, 8));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 16));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 32));
-  if (sub == 0) wmax[wave][i8] = m;
+  // lanes of one token: l % TOK equal
+#pragma unroll
+  for (int o = TOK; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if (sub == 0) wmax[wave][itok] = m;
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < kPrepThreads / 64; ++w) m = max(m, wmax[w][i8]);
+  for (int w = 0; w < kPrepThreads / 64; ++w) m = max(m, wmax[w][itok]);
   const int e = real ? token_exponent(m) : 0;
   if (nj <= MAXJ) {
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
-      const int p = pb + sub + 8 * j;
+      const int p = pb + sub + SUBS * j;
       if (p < pe) store_piece(x16, G, t, p, real ? to_f16_pairs(v[j], e) : u32x4_t{0u, 0u, 0u, 0u});
     }
   } else {
-    for (int b0 = pb; b0 < pe; b0 += 8 * MAXJ) {
+    for (int b0 = pb; b0 < pe; b0 += SUBS * MAXJ) {
 #pragma unroll
-      for (int j = 0; j < MAXJ; ++j) v[j] = xt[min(b0 + sub + 8 * j, nb - 1)];
+      for (int j = 0; j < MAXJ; ++j) v[j] = xt[min(b0 + sub + SUBS * j, nb - 1)];
 #pragma unroll
       for (int j = 0; j < MAXJ; ++j) {
-        const int p = b0 + sub + 8 * j;
+        const int p = b0 + sub + SUBS * j;
         if (p < pe) store_piece(x16, G, t, p, real ? to_f16_pairs(v[j], e) : u32x4_t{0u, 0u, 0u, 0u});
       }
     }
@@ -739,15 +748,22 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
 }
 
 // The K-split outputs: y[t][n] = bf16(2^(e[t] - c[n]) * sum over splits of
-// the partials), the splits added in order.  One thread per output.
+// the partials), the splits added in order.  One thread per output; its (at
+// most kMaxSplits) partial loads are all issued before the sum.
+constexpr int kMaxSplits = 8;
 __global__ void __launch_bounds__(256)
 tiled_reduce_kernel(const float* __restrict__ part, const int* __restrict__ texp, const int* __restrict__ rexp,
                     uint16_t* __restrict__ y, int N, int Tpad, int KS) {
   const int n = blockIdx.x * 256 + threadIdx.x, t = blockIdx.y;
   if (n >= N) return;
   const size_t i = (size_t)t * N + n, stride = (size_t)Tpad * N;
+  float p[kMaxSplits];
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k) p[k] = k < KS ? part[k * stride + i] : 0.0f;
   float v = 0.0f;
-  for (int k = 0; k < KS; ++k) v += part[k * stride + i];
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k)
+    if (k < KS) v += p[k];
   y[i] = f32_to_bf16_rne(__builtin_ldexpf(v, texp[t] - rexp[n]));
 }
 
@@ -762,6 +778,7 @@ hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, c
                                      hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS_B);
   if (e != hipSuccess) return e;
   const int ks = a.cfg.ks;
+  if (ks < 1 || ks > kMaxSplits) return hipErrorInvalidValue;
   kern<<<dim3((unsigned)(tiles_n * tiles_t * ks)), dim3(Sh::NT), Sh::LDS_B, stream>>>(
       x16, texp, rexp, static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
       static_cast<uint16_t*>(a.y), ks > 1 ? part : nullptr, (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t, ks);
@@ -823,18 +840,25 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   {
     const u32x4_t* x = static_cast<const u32x4_t*>(a.x);
     int k = (int)a.k, t = (int)a.t, n = (int)a.n, tpad = (int)tp;
-    const int tok_blocks = (int)(tp / kPrepTokens);
+    const int tok = prep_tokens(a.t);
+    const int tok_blocks = (int)(tp / tok);
     const int row_blocks = (int)((a.n + kRowsPerBlock - 1) / kRowsPerBlock);
     const int nwv = kPrepThreads / 64;
-    const int nj = (int)(((a.k / 8 + nwv - 1) / nwv + 7) / 8);  // pieces per lane
+    const int nj = (int)(((a.k / 8 + nwv - 1) / nwv + 64 / tok - 1) / (64 / tok));  // pieces per lane
     const dim3 grid((unsigned)(tok_blocks + row_blocks)), block(kPrepThreads);
     const uint16_t* sc = static_cast<const uint16_t*>(a.scales);
-    if (nj <= 2)
-      prep_act_kernel<2><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
-    else if (nj <= 5)
-      prep_act_kernel<5><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
-    else  // longer rows (nj > 10) take the chunked two-pass form of the same kernel
-      prep_act_kernel<10><<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks);
+    // longer rows (nj > 10) take the chunked two-pass form of the kernel
+    const int mj = nj <= 2 ? 2 : nj <= 5 ? 5 : 10;
+    auto launch = [&](auto kern) { kern<<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks); };
+    if (tok == 2) {
+      if (mj == 2) launch(prep_act_kernel<2, 2>);
+      else if (mj == 5) launch(prep_act_kernel<5, 2>);
+      else launch(prep_act_kernel<10, 2>);
+    } else {
+      if (mj == 2) launch(prep_act_kernel<2, 4>);
+      else if (mj == 5) launch(prep_act_kernel<5, 4>);
+      else launch(prep_act_kernel<10, 4>);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
