@@ -23,7 +23,8 @@ median, min and p95) is reported as ``single_call_cold``; on this platform an
 event pair around one launch adds a few microseconds of its own.
 
 Other modes: ``--sweep 1:128`` (per-T table with step change between
-adjacent T), ``--n/--k/--t`` single points, ``--profile`` (one call after
+adjacent T), ``--suite`` (the prefill extra points T = 512, 384/385, 640/641
+and the large shapes at T = 1 and 1024), ``--n/--k/--t`` single points, ``--profile`` (one call after
 set-up, for profiler counter passes).  ``--gpus`` above 1 exits: the
 benchmark covers one GPU.
 """
@@ -283,6 +284,8 @@ def main(argv=None):
     ap.add_argument("--k", type=int, default=5120)
     ap.add_argument("--t", type=int, default=None, help="single point instead of the default pair")
     ap.add_argument("--sweep", type=str, default=None, help="T range lo:hi[:step]")
+    ap.add_argument("--suite", action="store_true",
+                    help="the prefill extra points and the large-shape set, one table (median of --repeats replays)")
     ap.add_argument("--repeats", type=int, default=5, help="timed graph replays per sweep point (median)")
     ap.add_argument("--profile", action="store_true", help="one call after set-up, then exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -344,6 +347,39 @@ def main(argv=None):
                   % (t, row["us"], row["gbs"], 100 * row["hbm_frac"], row["tflops"], 100 * row["mfma_frac"],
                      100 * row["roof_frac"], "" if row["delta_pct"] is None else "%+.1f%%" % row["delta_pct"]),
                   flush=True)
+        if args.csv:
+            import csv
+            with open(args.csv, "w", newline="") as f:
+                w = csv.DictWriter(f, fieldnames=list(rows[0]))
+                w.writeheader()
+                w.writerows(rows)
+        return 0
+
+    if args.suite:
+        # every (shape, T) point of the prefill and large-shape workloads; each
+        # point: rotating cold buffer sets, graph of `steps` calls, median of
+        # `repeats` replays
+        import weight_only_bit_q4_amd as q4
+        rows = []
+        for wl in ("prefill_6144x5120_t1024", "large_shapes_t1_t1024"):
+            spec = inputs.WORKLOADS[wl]
+            wl_seed = inputs.workload_seed(wl)
+            for (sn, sk) in spec["shapes"]:
+                for t in spec["ts"]:
+                    p = Point(sn, sk, t, wl_seed)
+                    steps = max(20, min(500, int(4e-3 / max(1e-6, model_bytes(sn, sk, t) / 4e12,
+                                                            useful_flops(sn, sk, t) / 1e15))))
+                    secs = p.time(steps, 10, repeats=args.repeats)
+                    p.free()
+                    med = float(np.median(secs))
+                    row = {"workload": wl, "n": sn, "k": sk, "t": t, "route": q4.q4lin_route(sn, sk, t),
+                           "steps": steps, "us": round(med * 1e6, 3), "min_us": round(min(secs) * 1e6, 3),
+                           "gbs": round(gbs(sn, sk, t, med), 1), "tflops": round(tflops(sn, sk, t, med), 2),
+                           "hbm_frac": round(gbs(sn, sk, t, med) / HBM_PEAK_GBS, 4),
+                           "mfma_frac": round(tflops(sn, sk, t, med) / MFMA_PEAK_TFLOPS, 4),
+                           "roof_frac": round(roof_fraction(sn, sk, t, med), 4)}
+                    rows.append(row)
+                    print(json.dumps(row), flush=True)
         if args.csv:
             import csv
             with open(args.csv, "w", newline="") as f:

@@ -302,8 +302,14 @@ constexpr int kRowBytes = 144;
 // (s_waitcnt vmcnt) before the registers are read.  The destination is also
 // an input ("+a"), for the reason given above.
 template <int OFF>
+// (The resource and the offset are wave-uniform; readfirstlane states it, so
+// that they stay in scalar registers wherever the compiler's uniformity
+// analysis loses track.)
 __device__ __forceinline__ void buf_read_agpr(f16x8_t& v, u32x4_t rsrc, uint32_t voff, uint32_t soff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4" : "+a"(v) : "v"(voff), "s"(rsrc), "s"(soff), "i"(OFF));
+  const u32x4_t r = {(uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc.x), (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc.y),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc.z), (uint32_t)__builtin_amdgcn_readfirstlane((int)rsrc.w)};
+  const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)soff);
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4" : "+a"(v) : "v"(voff), "s"(r), "s"(so), "i"(OFF));
 }
 
 // Buffer resource for the raw (stride 0) byte range [base, base + bytes),
@@ -322,9 +328,11 @@ __device__ __forceinline__ u32x4_t make_rsrc_sgpr(const void* base, uint32_t byt
 // reuse needs DC <= 2 NP.  The scales travel with their pair, one dword per
 // thread and group.  Each wave's activation fragments stream through a ring
 // of DA register sets, loaded DACT = DA-1 groups ahead, every step.  Before
-// step s the batch of step s-4, which carries group s's activations and
-// (s even) the codes of groups s+2 and s+3, must have landed; the batches of
-// steps s-3 .. s-1 may still be in flight.  The step code is unrolled over P
+// step s the batch of step s-4, which carries group s's activations, must have
+// landed (and with it every older load, among them the codes of groups s+2
+// and s+3, issued DC - 2 >= DACT groups ahead); the batches of steps
+// s-3 .. s-1 may still be in flight.  (Measured: loading the codes the whole
+// ring ahead, DC = 2 NP, gains nothing.)  The step code is unrolled over P
 // steps, a multiple of every ring period (2 NP groups for the pair slots, DA
 // for the register sets, 2 for the weight tiles), so that every slot, tile
 // and register set a step touches is fixed by its position in the block:
@@ -334,7 +342,7 @@ constexpr int DC = 6;
 constexpr int DA = 5;
 constexpr int DACT = DA - 1;
 constexpr int P = 10;
-static_assert(DC <= 2 * NP && DC % 2 == 0 && DACT == 4 && DC - 2 == DACT, "ring geometry");
+static_assert(DC <= 2 * NP && DC % 2 == 0 && DACT == 4 && DC - 2 >= DACT, "ring geometry");
 static_assert(P % DA == 0 && P % (2 * NP) == 0, "the unrolled steps must cover every ring period");
 
 template <int NS, int TS, int WN, int WT>
@@ -342,20 +350,22 @@ struct TiledShape {
   static constexpr int NT = 64 * WN * WT;                 // threads
   static constexpr int BN = 32 * NS * WN;                 // rows per workgroup
   static constexpr int BT = 32 * TS * WT;                 // tokens per workgroup
-  static constexpr int CD = BN * 8 / NT;                  // code dwords per thread per group (dequantization)
+  static constexpr int CD = (BN * 8 + NT - 1) / NT;      // code dwords per thread per group (dequantization)
+  static constexpr int CDF = BN * 8 / NT;                 // of which every thread has the first CDF
   static constexpr int AI = TS * 4;                       // 16-byte activation loads per lane per group
   static constexpr int CQ = (BN * 4 + NT - 1) / NT;       // 16-byte code loads per thread per pair
-  static constexpr int CP = CQ + 2;                       // loads per thread per pair (codes, two scales)
+  static constexpr int CP = CQ;                           // loads per thread per pair
   static constexpr int CODE_B = CQ * NT * 16;             // one pair slot ([row][64 bytes], then slack)
-  static constexpr int SCALE_B = NT * 4;                  // one scale slot (one dword per thread)
+  static constexpr int SQ = (BN * 3 + NT - 1) / NT;       // 16-byte loads per thread per scale strip
+  static constexpr int STRIP_B = SQ * NT * 16;            // one scale strip ([row][48 bytes], then slack)
   static constexpr int W_B = BN * kRowBytes;              // one dequantized weight tile
   static constexpr int OFF_S = NP * CODE_B;
-  static constexpr int OFF_W = OFF_S + 2 * NP * SCALE_B;
+  static constexpr int OFF_W = OFF_S + 2 * STRIP_B;
   static constexpr int LDS_B = (OFF_W + 2 * W_B > BT * BN * 2) ? OFF_W + 2 * W_B : BT * BN * 2;
-  static_assert(BN * 8 % NT == 0, "code tiles must split evenly over the threads");
-  static_assert(NT >= BN, "one scale per row needs a thread per row");
+  // a partial last dword round covers whole waves (64 lanes, 8 rows each)
+  static_assert(BN * 8 % 64 == 0, "code tiles must split into whole waves");
   static_assert(LDS_B <= 160 * 1024, "LDS budget");
-  static_assert(3 * AI + 2 * CP <= 63, "the load counter holds 63");
+  static_assert(3 * AI + 2 * CP + SQ <= 63, "the load counter holds 63");
 };
 
 template <int NS, int TS, int WN, int WT>
@@ -365,7 +375,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
              uint16_t* __restrict__ y, float* __restrict__ part, int N, int K, int T, int Tpad, int tiles_n,
              int tiles_t, int KS) {
   using Sh = TiledShape<NS, TS, WN, WT>;
-  constexpr int NT = Sh::NT, BN = Sh::BN, BT = Sh::BT, CD = Sh::CD, CQ = Sh::CQ, CP = Sh::CP, AI = Sh::AI;
+  constexpr int NT = Sh::NT, BN = Sh::BN, BT = Sh::BT, CD = Sh::CD, CQ = Sh::CQ, CP = Sh::CP, AI = Sh::AI, SQ = Sh::SQ;
   constexpr int NW = WN * WT;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -422,33 +432,65 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     const int j = min((i * NW + wave) * 64 + lane, 4 * BN - 1);
     coff[i] = (uint32_t)(min(j >> 2, N - 1 - n0) * (K >> 1) + (j & 3) * 16);
   }
-  // Scale of row tid % BN: the naturally aligned dword around it (which never
-  // leaves the scale's page); the other half is ignored.  The buffer starts at
-  // the aligned dword below the tile's first scale; soff0 / soff1 are the
-  // lane's offsets for even / odd groups, to which 4 * (g / 2) is added.
-  const uintptr_t s_first = reinterpret_cast<uintptr_t>(scales + (size_t)n0 * G);
-  const uintptr_t s_base = s_first & ~(uintptr_t)3;
+  // Scales move in strips of P groups (one strip per block of unrolled
+  // steps): strip b holds, for every row of the tile, the 48 bytes (three
+  // aligned 16-byte pieces) that cover the row's 2 P bytes of scales of
+  // groups g0 + P b .. g0 + P b + P - 1, as [row][48 bytes]; one 16-byte
+  // direct-to-LDS load per piece, so a strip costs about one memory request
+  // per row instead of one per row and group.  Piece p = i NT + tid of a
+  // strip is piece p % 3 of row p / 3 and lands at byte 16 p.  The buffer
+  // runs from the 16-byte boundary below the scale plane to the one above
+  // its end (an aligned 16-byte piece never leaves the page of its bytes, so
+  // the pieces that hold the first and the last scale are read whole; a
+  // piece cut by the buffer's end would read as zeros); pieces past it read
+  // zeros (they belong to groups past the last row's end, which nothing
+  // reads).  With o the byte offset of the row's
+  // scale of group g0 + P b, its scale of group g0 + P b + j sits at byte
+  // 48 r + (o & 15) + 2 j of the strip.
+  static_assert(2 * P + 14 <= 48, "a row's strip must fit three pieces");
+  const uintptr_t s_plane = reinterpret_cast<uintptr_t>(scales);
+  const uintptr_t s_base = s_plane & ~(uintptr_t)15;
   const rsrc_t rs = make_rsrc(reinterpret_cast<const void*>(s_base),
-                              (uint32_t)min((int64_t)(N - n0) * G * 2 + 4, (int64_t)0x7FFFFFFF));
-  const uint32_t s_lane = (uint32_t)(s_first - s_base) + (uint32_t)(min(tid % BN, N - 1 - n0) * G * 2);
-  const uint32_t soff0 = s_lane & ~3u, soff1 = (s_lane + 2) & ~3u;
-  // soffp[j]: the offset for groups 2q + j (parity of g0 + j)
-  const uint32_t soffp[2] = {(g0 & 1) ? soff1 : soff0, (g0 & 1) ? soff0 : soff1};
-  // Code dword c of this thread belongs to tile row (c * NT + tid) / 8, whose
-  // scale sits in the dword loaded by the thread of that number, in its high
-  // half when (the scale's byte offset) / 2 is odd.  s_sel[c] is the byte
-  // selector that copies the row's scale of an even group into both halves;
-  // odd groups sit in the other half (selector ^ 0x02020202).  s_mul[c] is
-  // the float16 pair (2^c[row], 2^c[row]).
-  uint32_t s_sel[CD], s_mul[CD];
+                              (uint32_t)min(((int64_t)(s_plane - s_base) + (int64_t)N * G * 2 + 15) & ~(int64_t)15,
+                                            (int64_t)0x7FFFFFF0));
+  uint32_t so_p[SQ];  // strip 0 offset o of the row of piece i, plus 16 (p % 3)
+#pragma unroll
+  for (int i = 0; i < SQ; ++i) {
+    const int p = min(i * NT + tid, 3 * BN - 1);
+    const int r = min(p / 3, N - 1 - n0);
+    so_p[i] = (uint32_t)(s_plane - s_base) + (uint32_t)((n0 + r) * G + g0) * 2u + (uint32_t)(p % 3) * 16u;
+  }
+  // Code dword c of this thread belongs to tile row (c * NT + tid) / 8;
+  // s_r48[c] = 48 r and s_o[c] the strip 0 offset o of that row.  s_mul[c] is
+  // the float16 pair (2^c[row], 2^c[row]), made from c[row] after the
+  // prologue's wait (a use before it would stall the prologue's loads behind
+  // the exponent loads).
+  uint32_t s_r48[CD], s_o[CD], s_mul[CD];
+  int rx_c[CD];
 #pragma unroll
   for (int c = 0; c < CD; ++c) {
-    const int r = min((c * NT + tid) >> 3, N - 1 - n0);
-    const bool hi = ((((uint32_t)(s_first - s_base) >> 1) + (uint32_t)r * (uint32_t)G + (uint32_t)g0) & 1u) != 0;
-    s_sel[c] = hi ? 0x03020302u : 0x01000100u;
-    const uint32_t h = (uint32_t)(rexp[n0 + r] + 15) << 10;
-    s_mul[c] = h | (h << 16);
+    const int r = min((c * NT + tid) >> 3, BN - 1);
+    const int rr = min(r, N - 1 - n0);
+    s_o[c] = (uint32_t)(s_plane - s_base) + (uint32_t)((n0 + rr) * G + g0) * 2u;
+    s_r48[c] = (uint32_t)r * 48u;
+    rx_c[c] = rexp[n0 + rr];
   }
+  // The epilogue's exponents, also loaded now: c[n] of the lane's rows and
+  // e[t] of its tokens (16 per 32-token block: t = tl + 8 (r / 4) + r % 4,
+  // tl a multiple of 4, as four 16-byte loads).  Not needed with a K split.
+  int ce[NS];
+  int4 ev[TS][4];
+  if (part == nullptr) {
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) ce[ns] = rexp[min(n0 + (wn * NS + ns) * 32 + li, N - 1)];
+#pragma unroll
+    for (int ts = 0; ts < TS; ++ts) {
+      const int tl = 32 * tb0 + (wt * TS + ts) * 32 + 4 * lh;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ev[ts][q] = *reinterpret_cast<const int4*>(texp + min(tl + 8 * q, Tpad - 4));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   // Activation fragment (ts, m) of lane (li, lh): 16 bytes of token block
   // tb0 + wt*TS + ts, group g, at ((m*2 + lh)*32 + li)*16 of its 4 KB block.
   const uint8_t* x16_tile = reinterpret_cast<const uint8_t*>(x16) + (size_t)tb0 * G * 4096;
@@ -476,22 +518,24 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // be clamped to the last pair: such a load lands in the slot of a pair
   // past the end, which nothing reads).
   auto code_slot = [&](auto qs) __device__ { return lds + (decltype(qs)::value % NP) * Sh::CODE_B; };
-  auto scale_slot = [&](auto qs, auto par) __device__ {
-    return lds + Sh::OFF_S + ((decltype(qs)::value % NP) * 2 + decltype(par)::value) * Sh::SCALE_B;
-  };
   auto issue_one = [&](int q, auto qs, int ga, f16x8_t (&a)[TS][4], auto vi) __device__ {
     constexpr int v = decltype(vi)::value;
     if constexpr (v < CQ) {
       dma16(rc, coff[v], (uint32_t)(g0 + 2 * q) * 32, code_slot(qs) + (v * NW + wave) * 1024);
-    } else if constexpr (v < CQ + 2) {
-      // (a group clamped to the last one takes the other parity's offset:
-      // an in-bounds dword for a group past the end, which nothing reads)
-      const int gs = min(2 * q + (v - CQ), Gs - 1);
-      dma4(rs, soffp[v - CQ], (uint32_t)((g0 + gs) >> 1) * 4,
-           scale_slot(qs, std::integral_constant<int, v - CQ>{}) + wave * 256);
     } else {
-      constexpr int i = v - CQ - 2, ts = i / 4, m = i % 4;
+      constexpr int i = v - CQ, ts = i / 4, m = i % 4;
       buf_read_agpr<m * 1024>(a[ts][m], rx, aoff[ts], (uint32_t)(g0 + ga) * 4096);
+    }
+  };
+  // scale strip b (of the workgroup's share) into strip buffer b & 1: piece
+  // k of a row starts at the 16-byte boundary below the row's first scale
+  // of the strip, plus 16 k
+  auto issue_strip = [&](int b) __device__ {
+    uint8_t* dst = lds + Sh::OFF_S + (b & 1) * Sh::STRIP_B;
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+      // (o + 16 k) & ~15 = (o & ~15) + 16 k, with o the row's strip offset
+      dma16(rs, (so_p[i] + (uint32_t)b * (2u * P)) & ~15u, 0u, dst + (i * NW + wave) * 1024);
     }
   };
   const int qlast = (Gs - 1) >> 1;
@@ -514,14 +558,16 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   };
   // code dword c of this thread: row (c*NT + tid)/8, dword tid%8 of the
   // group's 32 bytes in the row's 64-byte pair (pair slot of QS, group
-  // parity PAR)
-  auto dq_load = [&](auto qs, auto par, DqRegs& d) __device__ {
+  // parity PAR); its scale: group P b + J of the share, from strip b
+  auto dq_load = [&](auto qs, auto par, int b, auto jj, DqRegs& d) __device__ {
     const uint8_t* cs = code_slot(qs) + (tid >> 3) * 64 + decltype(par)::value * 32 + (tid & 7) * 4;
-    const uint8_t* ss = scale_slot(qs, par) + (tid >> 3) * 4;
+    const uint8_t* ss = lds + Sh::OFF_S + (b & 1) * Sh::STRIP_B + 2 * decltype(jj)::value;
 #pragma unroll
     for (int c = 0; c < CD; ++c) {
-      d.w[c] = *reinterpret_cast<const uint32_t*>(cs + c * (NT / 8) * 64);
-      d.sw[c] = *reinterpret_cast<const uint32_t*>(ss + c * (NT / 8) * 4);
+      if (c < Sh::CDF || c * NT + tid < BN * 8) {
+        d.w[c] = *reinterpret_cast<const uint32_t*>(cs + c * (NT / 8) * 64);
+        d.sw[c] = *reinterpret_cast<const uint16_t*>(ss + s_r48[c] + ((s_o[c] + (uint32_t)b * (2u * P)) & 15u));
+      }
     }
   };
   // A group (of parity ODD) into weight tile B with the scales s' = s 2^c[row]
@@ -529,9 +575,10 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // of groups past the end hold whatever the clamped loads brought; no
   // matrix-core instruction reads them.
   auto dq_store_one = [&](auto b, const DqRegs& d, auto odd, int c) __device__ {
+    if (c >= Sh::CDF && c * NT + tid >= BN * 8) return;  // past the tile (wave-uniform)
     uint8_t* wb = lds + Sh::OFF_W + decltype(b)::value * Sh::W_B + dq_off;
-    const uint32_t sel = decltype(odd)::value ? (s_sel[c] ^ 0x02020202u) : s_sel[c];
-    const f16x2_t s2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(d.sw[c], d.sw[c], sel));
+    (void)odd;
+    const f16x2_t s2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(d.sw[c], d.sw[c], 0x01000100u));
     const uint32_t sp = __builtin_bit_cast(uint32_t, s2 * __builtin_bit_cast(f16x2_t, s_mul[c]));
     *reinterpret_cast<u32x4_t*>(wb + c * (NT / 8) * kRowBytes) = dequant_dword(d.w[c], sp);
   };
@@ -563,9 +610,11 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // (the three younger batches may still be in flight: 3 activation loads
   // sets and one (s even) or two (s odd) code pairs), and its LDS reads and
   // writes (also the untracked weight reads) are done.
-  auto sync = [&](auto odd) __device__ {
+  // (STRIP: a scale strip was issued after batch s-4, so SQ more loads may
+  // be in flight)
+  auto sync = [&](auto odd, auto strip) __device__ {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<3 * AI + (decltype(odd)::value ? 2 : 1) * CP>();
+    wait_vm<3 * AI + (decltype(odd)::value ? 2 : 1) * CP + (decltype(strip)::value ? SQ : 0)>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -595,7 +644,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     const int ts = j / NS, ns = j % NS;
     acc[ts][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(act[SL % DA][ts][m], wgt[SL & 1][ns][m], acc[ts][ns], 0, 0, 0);
   };
-  auto step = [&](int g, auto slot) __device__ {
+  auto step = [&](int g, auto slot, int blk) __device__ {
     constexpr int SL = decltype(slot)::value;
     constexpr bool EVEN = (SL & 1) == 0;
     constexpr int V0 = EVEN ? 0 : CP;          // first load of this step's batch
@@ -604,9 +653,11 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     // slot ((SL + 2) >> 1) % NP, the pair this step loads in slot
     // ((SL + DC) >> 1) % NP, and g, g+2 have the parity of SL
     constexpr int QD = (SL + 2) >> 1, QL = (SL + DC) >> 1;
-    sync(std::integral_constant<bool, !EVEN>{});
+    // the scale strip of block blk is issued at the end of its step 8
+    static_assert(P == 10, "strip issue and waits assume blocks of 10 steps");
+    sync(std::integral_constant<bool, !EVEN>{}, std::integral_constant<bool, SL == 9 || SL <= 2>{});
     DqRegs d;
-    dq_load(Slot<QD>{}, std::integral_constant<int, SL & 1>{}, d);
+    dq_load(Slot<QD>{}, std::integral_constant<int, SL & 1>{}, blk + (SL + 2) / P, Slot<(SL + 2) % P>{}, d);
     const int q = min((g + DC) >> 1, qlast), ga = min(g + DACT, Gs - 1);
     __builtin_amdgcn_sched_barrier(0);
     // the batch's loads: a quarter in k-slice 0 (one or two after each
@@ -647,11 +698,19 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    // Step 8 of block blk comes after the barrier that ends the last read of
+    // strip blk (its group P blk + 9 was read at step 7): strip blk + 2 into
+    // the same buffer, ten steps before its first read.  (Past the last
+    // strip this reads unused scales or zeros.)
+    if constexpr (SL == 8) issue_strip(blk + 2);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Prologue: code pairs 0..DC/2-1 (groups 0..DC-1; step 0 loads the next)
-  // and activations of groups 0..DACT-1 in flight, then all landed; groups 0
-  // and 1 dequantized; group 0's weights read.
+  // Prologue: scale strips 0 and 1, code pairs 0..DC/2-1 (groups 0..DC-1;
+  // step 0 loads the next) and activations of groups 0..DACT-1 in flight,
+  // then all landed; groups 0 and 1 dequantized; group 0's weights read.
+  issue_strip(0);
+  issue_strip(1);
   static_for<DC / 2>([&](auto i) { issue_codes(i); });
   static_for<DACT>([&](auto i) { issue_act(decltype(i)::value, act[decltype(i)::value]); });
   // A thread dequantizes its own code dwords but reads row scales that other
@@ -662,11 +721,16 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < CD; ++c) {
+    const uint32_t h = (uint32_t)(rx_c[c] + 15) << 10;
+    s_mul[c] = h | (h << 16);
+  }
   {
     DqRegs d;
-    dq_load(Slot<0>{}, std::integral_constant<int, 0>{}, d);
+    dq_load(Slot<0>{}, std::integral_constant<int, 0>{}, 0, Slot<0>{}, d);
     dq_store(Slot<0>{}, d, std::false_type{});
-    dq_load(Slot<0>{}, std::integral_constant<int, 1>{}, d);
+    dq_load(Slot<0>{}, std::integral_constant<int, 1>{}, 0, Slot<1>{}, d);
     dq_store(Slot<1>{}, d, std::true_type{});
   }
   wait_lgkm0();
@@ -676,12 +740,12 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // Steps run in blocks of P (the ring indexes repeat with period P): whole
   // blocks without a test, then the last partial block, which stops after
   // the last group.
-  int gb = 0;
-  for (; gb + P <= Gs; gb += P) static_for<P>([&](auto sl) { step(gb + decltype(sl)::value, sl); });
+  int gb = 0, blk = 0;
+  for (; gb + P <= Gs; gb += P, ++blk) static_for<P>([&](auto sl) { step(gb + decltype(sl)::value, sl, blk); });
   if (gb < Gs) {
     static_for<P>([&](auto sl) {
       constexpr int SL = decltype(sl)::value;
-      if (SL == 0 || gb + SL < Gs) step(gb + SL, sl);
+      if (SL == 0 || gb + SL < Gs) step(gb + SL, sl, blk);
     });
   }
   // no load may still write this workgroup's LDS or registers after this
@@ -711,9 +775,6 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
       }
     return;
   }
-  int ce[NS];
-#pragma unroll
-  for (int ns = 0; ns < NS; ++ns) ce[ns] = rexp[min(n0 + (wn * NS + ns) * 32 + li, N - 1)];
   __syncthreads();
   uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
@@ -721,7 +782,12 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     const int tl = (wt * TS + ts) * 32 + 4 * lh;
     int e[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = texp[min(32 * tb0 + tl + 8 * (r >> 2) + (r & 3), Tpad - 1)];
+    for (int q = 0; q < 4; ++q) {
+      e[4 * q + 0] = ev[ts][q].x;
+      e[4 * q + 1] = ev[ts][q].y;
+      e[4 * q + 2] = ev[ts][q].z;
+      e[4 * q + 3] = ev[ts][q].w;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r)
 #pragma unroll
