@@ -275,6 +275,98 @@ def copy_calibration(nbytes: int, reps: int = 5):
     print(json.dumps({"copy_calibration": True, "bytes": nbytes, "reps": reps}))
 
 
+def _graph_period(torch, fn, steps, repeats=5):
+    """Median seconds per call of `steps` calls of fn(i, stream_handle) captured
+    in one graph (same method as Point.time)."""
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        for i in range(3):
+            fn(i, st.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for i in range(steps):
+                fn(i, st.cuda_stream)
+    out = []
+    with torch.cuda.stream(st):
+        for _ in range(repeats):
+            g.replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            g.replay()
+            b.record(st)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / 1e3 / steps)
+    return float(np.median(out))
+
+
+def ceilings():
+    """What this GPU itself reaches on the op's resources, measured like the
+    op (graphs of back-to-back calls, cold rotating buffers): the period of an
+    empty kernel, a plain streaming read of each workload's weight bytes (best
+    of a few launch shapes), back-to-back matrix-core instructions, and a dense
+    FP16/BF16 GEMM of the prefill shape through torch (hipBLASLt).  One JSON
+    line per measurement."""
+    import ctypes
+    import torch
+    from weight_only_bit_q4_amd import build as q4build
+    lib = ctypes.CDLL(q4build.PROBE_LIB)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.q4lin_probe_empty.argtypes = [vp, vp]
+    lib.q4lin_probe_read.argtypes = [vp, i64, vp, ci, ci, ci, vp]
+    lib.q4lin_probe_mfma.argtypes = [vp, ci, ci, vp]
+    out = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+
+    def check(r):
+        if r != 0:
+            raise RuntimeError("probe call failed: %d" % r)
+
+    t = _graph_period(torch, lambda i, h: check(lib.q4lin_probe_empty(out.data_ptr(), h)), 1000)
+    print(json.dumps({"ceiling": "empty_kernel_period", "us": round(t * 1e6, 3)}), flush=True)
+
+    for (n, k) in [(6144, 5120), (14336, 5120), (5120, 17408), (34816, 5120)]:
+        nb = weight_bytes(n, k) // 16 * 16
+        nsets = int(math.ceil(ROTATE_BYTES / nb)) + 1
+        bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+        best = None
+        for (grid, block, u) in [(256, 512, 8), (1024, 512, 2), (2048, 512, 1), (4096, 256, 1), (8192, 256, 1)]:
+            def f(i, h, grid=grid, block=block, u=u):
+                check(lib.q4lin_probe_read(bufs[i % nsets].data_ptr(), nb, out.data_ptr(), grid, block, u, h))
+            t = _graph_period(torch, f, 1000 if nb < 3e7 else 300)
+            if best is None or t < best[0]:
+                best = (t, grid, block, u)
+        t, grid, block, u = best
+        print(json.dumps({"ceiling": "streaming_read", "weight_shape": "%dx%d" % (n, k), "bytes": nb,
+                          "us": round(t * 1e6, 3), "gbs": round(nb / t / 1e9, 1),
+                          "frac_of_8000": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
+                          "launch": {"grid": grid, "block": block, "loads_per_lane": u}}), flush=True)
+        del bufs
+        torch.cuda.empty_cache()
+
+    outf = torch.zeros(1 << 16, dtype=torch.float32, device="cuda")
+    grid, iters = 1024, 1000
+    t = _graph_period(torch, lambda i, h: check(lib.q4lin_probe_mfma(outf.data_ptr(), grid, iters, h)), 10)
+    fl = grid * 4 * iters * 8 * 32768.0
+    print(json.dumps({"ceiling": "matrix_core_loop_f16", "tflops": round(fl / t / 1e12, 1),
+                      "frac_of_2500": round(fl / t / 1e12 / MFMA_PEAK_TFLOPS, 4)}), flush=True)
+
+    for dt in (torch.float16, torch.bfloat16):
+        m, n, k = 1024, 6144, 5120
+        a = torch.randn(m, k, device="cuda").to(dt)
+        bs = [torch.randn(n, k, device="cuda").to(dt) for _ in range(8)]  # 8 x 63 MB: beyond the 256 MB cache
+        c = torch.empty(m, n, device="cuda", dtype=dt)
+        t = _graph_period(torch, lambda i, h: torch.matmul(a, bs[i % 8].t(), out=c), 20)
+        print(json.dumps({"ceiling": "dense_gemm_torch", "dtype": str(dt).replace("torch.", ""),
+                          "shape": "[%d,%d] x [%d,%d]^T" % (m, k, n, k), "us": round(t * 1e6, 3),
+                          "tflops": round(2.0 * m * n * k / t / 1e12, 1),
+                          "frac_of_2500": round(2.0 * m * n * k / t / 1e12 / MFMA_PEAK_TFLOPS, 4)}), flush=True)
+        del bs
+        torch.cuda.empty_cache()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +376,8 @@ def main(argv=None):
     ap.add_argument("--k", type=int, default=5120)
     ap.add_argument("--t", type=int, default=None, help="single point instead of the default pair")
     ap.add_argument("--sweep", type=str, default=None, help="T range lo:hi[:step]")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="same-GPU ceilings: empty-launch period, streaming-read probe, matrix-core loop, dense GEMM")
     ap.add_argument("--suite", action="store_true",
                     help="the prefill extra points and the large-shape set, one table (median of --repeats replays)")
     ap.add_argument("--repeats", type=int, default=5, help="timed graph replays per sweep point (median)")
@@ -353,6 +447,10 @@ def main(argv=None):
                 w = csv.DictWriter(f, fieldnames=list(rows[0]))
                 w.writeheader()
                 w.writerows(rows)
+        return 0
+
+    if args.ceilings:
+        ceilings()
         return 0
 
     if args.suite:

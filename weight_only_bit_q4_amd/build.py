@@ -1,8 +1,10 @@
 """Build the q4lin HIP library (gfx950) in-tree.
 
 ``python -m weight_only_bit_q4_amd.build`` compiles every ``csrc/*.hip`` with
-hipcc for gfx950 and links ``weight_only_bit_q4_amd/libq4lin.so``.  Object
-files go to ``_build/`` at the repository root.
+hipcc for gfx950 and links ``weight_only_bit_q4_amd/libq4lin.so``, and the
+benchmark's ceiling probes (``csrc/probe/*.hip``, not part of the op) into
+``weight_only_bit_q4_amd/libq4lin_probe.so``.  Object files go to ``_build/``
+at the repository root.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq4lin.so")
+PROBE_LIB = os.path.join(PKG, "libq4lin_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -54,19 +57,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-mcode-object-version=5", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probe_srcs = sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
+        objs = list(ex.map(_compile, srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
         print("built", LIB)
+        print("built", PROBE_LIB)
     return LIB
 
 
