@@ -77,6 +77,8 @@ class Oracle:
         lib.q4o_weight_bytes.restype = i64
         lib.q4o_linear.argtypes = [u16p, u8p, u16p, u16p, f64p, i64, i64, i64, ctypes.c_int]
         lib.q4o_linear.restype = None
+        lib.q4o_linear_add.argtypes = [u16p, u8p, u16p, u16p, u16p, i64, i64, i64, ctypes.c_int]
+        lib.q4o_linear_add.restype = None
         lib.q4o_linear_at.argtypes = [u16p, u8p, u16p, i64, i64, i64, i64p, i64p, i64,
                                       u16p, f64p, ctypes.c_int]
         lib.q4o_linear_at.restype = None
@@ -129,6 +131,19 @@ class Oracle:
         if with_acc:
             return y, acc.reshape(t, n)
         return y
+
+    def linear_add(self, x, codes, scales, r, n: int, k: int, t: int, threads: int = 0):
+        """Y = bf16(W . X + R), rounded once.  ``r``: bf16 bits, token-major
+        ``[T, N]`` like the result.  Returns bf16 bits ``[T, N]``."""
+        x, codes, scales = self._prep(x, codes, scales, n, k, t)
+        r = np.ascontiguousarray(r, dtype=np.uint16).reshape(-1)
+        if r.size != t * n:
+            raise ValueError("residual size does not match T x N")
+        y = np.zeros(t * n, dtype=np.uint16)
+        self.lib.q4o_linear_add(_ptr(x, ctypes.c_uint16), _ptr(codes, ctypes.c_uint8),
+                                _ptr(scales, ctypes.c_uint16), _ptr(r, ctypes.c_uint16),
+                                _ptr(y, ctypes.c_uint16), n, k, t, int(threads))
+        return y.reshape(t, n)
 
     def linear_at(self, x, codes, scales, n: int, k: int, t: int, ns, ts,
                   threads: int = 0, with_acc: bool = False):
@@ -185,6 +200,10 @@ def weight_bytes(n, k):
 
 def linear(*args, **kw):
     return default().linear(*args, **kw)
+
+
+def linear_add(*args, **kw):
+    return default().linear_add(*args, **kw)
 
 
 def linear_at(*args, **kw):

@@ -189,6 +189,43 @@ void q4o_linear(const uint16_t *x, const uint8_t *codes, const uint16_t *scales,
     }
 }
 
+/* LinearAdd, the pages' fused variant with a residual ("q4-linear.md" and
+ * "linear-benchmark.md" name LinearAdd among the Linear variants without
+ * defining it; the plain reading taken here):
+ *   Y[n,t] = bf16_rne( sum_k W[n,k] * X[k,t]  +  R[n,t] )
+ * with R in bf16, token-major like Y (R(n,t) at r[t*N + n]); the residual
+ * (exact in binary64) joins the binary64 sum after the last k, and the
+ * result is rounded once. */
+void q4o_linear_add(const uint16_t *x, const uint8_t *codes, const uint16_t *scales,
+                    const uint16_t *r, uint16_t *y, int64_t N, int64_t K, int64_t T,
+                    int threads)
+{
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k)
+                w[k] = weight_value(codes, scales, K, n, k);
+            for (int64_t t = 0; t < T; ++t) {
+                double s = 0.0;
+                const uint16_t *xt = x + t * K;
+                for (int64_t k = 0; k < K; ++k)
+                    s += w[k] * q4o_bf16_to_double(xt[k]);
+                s += q4o_bf16_to_double(r[t * N + n]);
+                y[t * N + n] = q4o_double_to_bf16(s);
+            }
+        }
+        free(w);
+    }
+}
+
 /* Selected output elements only: out[i] = Y[ns[i], ts[i]] (bf16 bits), and
  * acc[i] the binary64 sum (acc may be NULL).  Used where the full product
  * would take too long on the CPU. */

@@ -126,6 +126,28 @@ def pin_worked_examples(o):
             ex["name"], [hex(v) for v in got], [hex(v) for v in want])
 
 
+GOLDEN_ADD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_examples_add.json")
+
+
+def load_add_examples():
+    with open(GOLDEN_ADD) as f:
+        return json.load(f)["examples"]
+
+
+def materialize_add(ex):
+    x, codes, scales, y = materialize(ex)
+    r = np.array([_h(v) for v in ex["r"]], dtype=np.uint16).reshape(ex["t"], ex["n"])
+    return x, codes, scales, r, y
+
+
+def pin_add_worked_examples(o):
+    for ex in load_add_examples():
+        x, codes, scales, r, want = materialize_add(ex)
+        got = o.linear_add(x, codes, scales, r, ex["n"], ex["k"], ex["t"]).reshape(-1)
+        assert np.array_equal(got, want), "%s: got %s want %s" % (
+            ex["name"], [hex(v) for v in got], [hex(v) for v in want])
+
+
 # --------------------------------------------------------------------------
 # number formats
 # --------------------------------------------------------------------------
@@ -288,6 +310,72 @@ def _exact_linear(x, codes, scales, n, k, t):
     return out
 
 
+def pin_add_exact_bruteforce(o, trials=6):
+    """LinearAdd against exact rationals: the exact sum plus the exact residual,
+    rounded once (round to nearest, ties to even)."""
+    r = np.random.default_rng(29)
+    for trial in range(trials):
+        n = int(r.integers(1, 5))
+        k = 64 * int(r.integers(1, 3))
+        t = int(r.integers(1, 4))
+        codes = r.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        sv = r.choice([-1, 1], size=(n, k // 64)) * np.ldexp(r.uniform(1, 2, (n, k // 64)),
+                                                             r.integers(-12, 4, (n, k // 64)))
+        scales = sv.astype(np.float16).view(np.uint16)
+        xv = (r.standard_normal((t, k)) * np.ldexp(1.0, r.integers(-6, 6, (t, k)))).astype(np.float32)
+        x = torch_f32_to_bf16_bits(xv)
+        res = torch_f32_to_bf16_bits((r.standard_normal((t, n)) * 4.0).astype(np.float32))
+        q = _int_weights(codes, n, k)
+        sc = [[fp16_exact(int(scales[i, g])) for g in range(k // 64)] for i in range(n)]
+        want = np.zeros((t, n), dtype=np.uint16)
+        for j in range(t):
+            for i in range(n):
+                acc = bf16_exact(int(res[j, i]))
+                for kk in range(k):
+                    if q[i, kk]:
+                        acc += int(q[i, kk]) * sc[i][kk // 64] * bf16_exact(int(x[j, kk]))
+                want[j, i] = frac_to_bf16_bits(acc)
+        got = o.linear_add(x, codes, scales, res, n, k, t)
+        assert np.array_equal(got, want), "trial %d (n=%d k=%d t=%d)" % (trial, n, k, t)
+
+
+def pin_add_all_code8_passes_residual(o):
+    """All-eight codes make every weight 0, so the result is the residual itself,
+    bit for bit (any finite bf16 residual, across the binades)."""
+    n, k, t = 24, 192, 3
+    x, codes, scales = _problem(n, k, t, 31)
+    codes[:] = 0x88
+    r = np.random.default_rng(31)
+    res = torch_f32_to_bf16_bits((r.standard_normal((t, n)) * np.ldexp(1.0, r.integers(-60, 60, (t, n))))
+                                 .astype(np.float32))
+    got = o.linear_add(x, codes, scales, res, n, k, t)
+    assert np.array_equal(got, res)
+
+
+def pin_add_zero_residual_and_shift(o):
+    """R = 0 leaves the plain Linear result; an R that is a multiple of the
+    result's own bf16 spacing and keeps its binade shifts it exactly."""
+    n, k, t = 16, 256, 2
+    x, codes, scales = _problem(n, k, t, 37)
+    plain = o.linear(x, codes, scales, n, k, t)
+    zero = np.zeros((t, n), dtype=np.uint16)
+    assert np.array_equal(o.linear_add(x, codes, scales, zero, n, k, t), plain)
+    # weights in {-1, 0, 1} (nibbles 7, 8, 9), unit scales and activations:
+    # the sum is an integer s with |s| <= 128, so s and s + 1 are bf16 values
+    # and R = 1 shifts the result exactly
+    k2 = 128
+    r = np.random.default_rng(37)
+    nib = r.integers(7, 10, size=(n, k2))
+    codes2 = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales2 = np.full((n, k2 // 64), 0x3C00, dtype=np.uint16)  # 1.0
+    x2 = np.full((t, k2), 0x3F80, dtype=np.uint16)              # 1.0
+    s = (nib - 8).sum(axis=1)
+    ones = np.full((t, n), 0x3F80, dtype=np.uint16)
+    got = o.linear_add(x2, codes2, scales2, ones, n, k2, t)
+    from oracle import bf16_bits_to_f64
+    assert np.array_equal(bf16_bits_to_f64(got), np.tile((s + 1).astype(np.float64), (t, 1)))
+
+
 def pin_exact_bruteforce(o, trials=6):
     """Exact rational sums with an exact round-to-nearest-even, on tiny shapes
     with wide-range scales (including subnormal and negative FP16) and
@@ -412,4 +500,6 @@ ALL_PINS = [
     pin_rounding_vs_torch, pin_weight_bytes, pin_unit_scales_integer_x, pin_unit_scales_matmul,
     pin_exact_bruteforce, pin_all_code8_zero, pin_pow2_scale_invariance, pin_locality,
     pin_token_independence, pin_group_permutation, pin_linear_at,
+    pin_add_worked_examples, pin_add_exact_bruteforce, pin_add_all_code8_passes_residual,
+    pin_add_zero_residual_and_shift,
 ]

@@ -34,6 +34,12 @@ MUTANTS = [
     ("binary32 accumulation", "double s = 0.0;\n                const uint16_t *xt",
      "float s = 0.0f;\n                const uint16_t *xt"),
     ("no bf16 subnormals", "int qexp = (e < -126) ? -133 : e - 7;", "int qexp = e - 7;"),
+    ("residual dropped", "s += q4o_bf16_to_double(r[t * N + n]);", "s += 0.0;"),
+    ("residual read n-major", "s += q4o_bf16_to_double(r[t * N + n]);",
+     "s += q4o_bf16_to_double(r[(n * T + t) % (N * T)]);"),
+    ("residual added after a first rounding", "s += q4o_bf16_to_double(r[t * N + n]);",
+     "s = q4o_bf16_to_double(q4o_double_to_bf16(s)) + q4o_bf16_to_double(r[t * N + n]);"),
+    ("residual subtracted", "s += q4o_bf16_to_double(r[t * N + n]);", "s -= q4o_bf16_to_double(r[t * N + n]);"),
     ("sampled path reads k-major",
      "acc += weight_value(codes, scales, K, n, k) * q4o_bf16_to_double(x[t * K + k]);",
      "acc += weight_value(codes, scales, K, n, k) * q4o_bf16_to_double(x[(k * 7 + t) % K]);"),
