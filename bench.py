@@ -82,7 +82,7 @@ def roof_fraction(n, k, t, seconds, hbm_gbs=HBM_PEAK_GBS, mfma_tflops=MFMA_PEAK_
 class Point:
     """Rotating buffer sets for one (N, K, T) and a graph of `steps` calls."""
 
-    def __init__(self, n, k, t, seed, rotate=True, data=None):
+    def __init__(self, n, k, t, seed, rotate=True, data=None, add=False):
         import torch
         import weight_only_bit_q4_amd as q4
         from weight_only_bit_q4_amd import inputs
@@ -90,26 +90,34 @@ class Point:
         self.q4 = q4
         self.torch = torch
         x, codes, scales = data if data is not None else inputs.gen_problem(n, k, t, seed)
-        per_set = model_bytes(n, k, t) + max(q4.q4lin_workspace_bytes(n, k, t), 0)
+        per_set = model_bytes(n, k, t) + max(q4.q4lin_workspace_bytes(n, k, t), 0) + (2 * n * t if add else 0)
         self.nsets = max(2, int(math.ceil(ROTATE_BYTES / per_set)) + 1) if rotate else 1
         dev = torch.device("cuda")
         xd = torch.from_numpy(x.view(np.int16).copy()).to(dev)
         cd = torch.from_numpy(codes).to(dev)
         sd = torch.from_numpy(scales.view(np.int16).copy()).to(dev)
         self.ws_bytes = q4.q4lin_workspace_bytes(n, k, t)
+        self.add = add
         self.sets = []
         for _ in range(self.nsets):
             ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
             y = torch.empty((t, n), dtype=torch.int16, device=dev)
-            self.sets.append((xd.clone(), cd.clone(), sd.clone(), y, ws))
+            # LinearAdd: a residual per set (bf16 N(0,1)), read once per call
+            r = torch.randn((t, n), device=dev).to(torch.bfloat16).view(torch.int16) if add else None
+            self.sets.append((xd.clone(), cd.clone(), sd.clone(), y, ws, r))
         torch.cuda.synchronize()
         self.stream = torch.cuda.Stream()
 
     def call(self, i, stream_handle):
-        x, c, s, y, ws = self.sets[i % self.nsets]
-        st = self.q4.q4lin_linear(x.data_ptr(), c.data_ptr(), s.data_ptr(), y.data_ptr(),
-                                  self.n, self.k, self.t, ws.data_ptr() if self.ws_bytes else 0,
-                                  self.ws_bytes, stream_handle)
+        x, c, s, y, ws, r = self.sets[i % self.nsets]
+        if self.add:
+            st = self.q4.q4lin_linear_add(x.data_ptr(), c.data_ptr(), s.data_ptr(), r.data_ptr(), y.data_ptr(),
+                                          self.n, self.k, self.t, ws.data_ptr() if self.ws_bytes else 0,
+                                          self.ws_bytes, stream_handle)
+        else:
+            st = self.q4.q4lin_linear(x.data_ptr(), c.data_ptr(), s.data_ptr(), y.data_ptr(),
+                                      self.n, self.k, self.t, ws.data_ptr() if self.ws_bytes else 0,
+                                      self.ws_bytes, stream_handle)
         if st != 0:
             raise RuntimeError("q4lin_linear: " + self.q4.q4lin_status_string(st))
 
@@ -382,6 +390,8 @@ def main(argv=None):
                     help="the prefill extra points and the large-shape set, one table (median of --repeats replays)")
     ap.add_argument("--repeats", type=int, default=5, help="timed graph replays per sweep point (median)")
     ap.add_argument("--profile", action="store_true", help="one call after set-up, then exit")
+    ap.add_argument("--add", action="store_true",
+                    help="with --t: time the LinearAdd entry point (Y = W x X + R; R adds 2NT bytes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--csv", type=str, default=None)
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="BYTES",
@@ -488,14 +498,16 @@ def main(argv=None):
 
     if args.t is not None:
         t = args.t
-        p = Point(n, k, t, seed)
-        secs = p.time(args.steps, args.warmup, repeats=1)[0]
+        p = Point(n, k, t, seed, add=args.add)
+        secs = float(np.median(p.time(max(20, args.steps // (20 if t >= 512 else 1)), args.warmup, repeats=5)))
         p.free()
-        pc = Point(n, k, t, seed, rotate=False)
+        pc = Point(n, k, t, seed, rotate=False, add=args.add)
         lat = pc.time_cold(30, 3)
         pc.free()
-        print(json.dumps({"n": n, "k": k, "t": t, "us": secs * 1e6, "single_call_cold_median_us": float(np.median(lat)) * 1e6,
-                          "gbs": gbs(n, k, t, secs), "tflops": tflops(n, k, t, secs),
+        extra = 2 * n * t if args.add else 0   # the residual read
+        print(json.dumps({"op": "linear_add" if args.add else "linear", "n": n, "k": k, "t": t, "us": secs * 1e6,
+                          "single_call_cold_median_us": float(np.median(lat)) * 1e6,
+                          "gbs": (model_bytes(n, k, t) + extra) / secs / 1e9, "tflops": tflops(n, k, t, secs),
                           "roof_frac": roof_fraction(n, k, t, secs)}))
         return 0
 

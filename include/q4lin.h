@@ -78,6 +78,24 @@ Q4LIN_API int q4lin_linear(const void *x, const void *codes, const void *scales,
                  int64_t n, int64_t k, int64_t t,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* LinearAdd, the pages' fused Linear variant with a residual ("q4-linear.md"
+ * and "linear-benchmark.md" name LinearAdd beside LinearSwiGLU and LinearPair
+ * without defining it; the plain reading taken here):
+ *
+ *     Y[N,T] = W[N,K] x X[K,T] + R[N,T]
+ *
+ * with the residual R in bfloat16, token-major like Y (element (n, t) at
+ * residual[t*N + n]), 2-byte aligned.  R joins the binary32 result before
+ * its single rounding to bfloat16, so the sum is rounded once (not the
+ * product first).  residual may be the same buffer as y (in place, element
+ * for element); any other overlap with y is outside the contract.  Every
+ * other argument, the workspace size (q4lin_workspace_bytes), the routes and
+ * the errors are those of q4lin_linear; residual NULL with a non-empty
+ * product is Q4LIN_E_NULL. */
+Q4LIN_API int q4lin_linear_add(const void *x, const void *codes, const void *scales, const void *residual,
+                     void *y, int64_t n, int64_t k, int64_t t,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 Q4LIN_API const char *q4lin_status_string(int status);
 

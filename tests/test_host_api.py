@@ -88,3 +88,31 @@ def test_routes_and_workspace_sizes():
         else:
             assert ws == 0
     assert q.q4lin_route(6144, 5120, 1024) == q.Q4LIN_ROUTE_TILED
+
+
+# -- LinearAdd: same contract plus the residual --------------------------------
+def test_linear_add_empty_product_is_a_no_op():
+    for n, t in [(0, 5), (6, 0)]:
+        assert q.q4lin_linear_add(0, 0, 0, 0, 0, n, 128, t, 0, 0, 0) == q.Q4LIN_OK
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_linear_add_null_pointer_rejected(which):
+    ptrs = [0x1000] * 5
+    ptrs[which] = 0
+    assert q.q4lin_linear_add(*ptrs, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_NULL
+
+
+@pytest.mark.parametrize("which,addr", [(0, 0x1008), (1, 0x1004), (2, 0x1001), (3, 0x1001), (4, 0x1001)])
+def test_linear_add_misaligned_pointer_rejected(which, addr):
+    ptrs = [0x1000] * 5
+    ptrs[which] = addr
+    assert q.q4lin_linear_add(*ptrs, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
+
+
+def test_linear_add_shape_and_workspace_checks():
+    p = 0x10000
+    assert q.q4lin_linear_add(p, p, p, p, p, 8, 96, 1, 0, 0, 0) == q.Q4LIN_E_SHAPE
+    n, k, t = 256, 512, 300
+    need = q.q4lin_workspace_bytes(n, k, t)
+    assert q.q4lin_linear_add(p, p, p, p, p, n, k, t, p, need - 1, 0) == q.Q4LIN_E_WORKSPACE

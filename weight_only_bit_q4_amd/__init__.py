@@ -33,7 +33,7 @@ Q4LIN_ROUTE_SKINNY = 2
 Q4LIN_ROUTE_TILED = 3
 Q4LIN_ROUTE_DECODE = 4
 
-EXPORTED = ("q4lin_workspace_bytes", "q4lin_linear", "q4lin_status_string", "q4lin_route",
+EXPORTED = ("q4lin_workspace_bytes", "q4lin_linear", "q4lin_linear_add", "q4lin_status_string", "q4lin_route",
             "q4lin_version")
 
 
@@ -62,6 +62,8 @@ def _load() -> ctypes.CDLL:
     lib.q4lin_workspace_bytes.restype = i64
     lib.q4lin_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.q4lin_linear.restype = ctypes.c_int
+    lib.q4lin_linear_add.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.q4lin_linear_add.restype = ctypes.c_int
     lib.q4lin_status_string.argtypes = [ctypes.c_int]
     lib.q4lin_status_string.restype = ctypes.c_char_p
     lib.q4lin_route.argtypes = [i64, i64, i64]
@@ -95,6 +97,14 @@ def q4lin_linear(x: int, codes: int, scales: int, y: int, n: int, k: int, t: int
                                  int(workspace_bytes), stream or None))
 
 
+def q4lin_linear_add(x: int, codes: int, scales: int, residual: int, y: int, n: int, k: int, t: int,
+                     workspace: int, workspace_bytes: int, stream: int) -> int:
+    """Raw call of the LinearAdd entry point (Y = W x X + R); returns the status."""
+    return int(load().q4lin_linear_add(x or None, codes or None, scales or None, residual or None, y or None,
+                                       int(n), int(k), int(t), workspace or None,
+                                       int(workspace_bytes), stream or None))
+
+
 def q4lin_status_string(status: int) -> str:
     return load().q4lin_status_string(int(status)).decode()
 
@@ -108,12 +118,14 @@ def q4lin_version() -> int:
 
 
 # -- torch convenience (marshalling only) -------------------------------------
-def linear(x, codes, scales, y=None, workspace=None, stream=None):
-    """Y = W x X on torch device tensors.
+def linear(x, codes, scales, y=None, workspace=None, stream=None, residual=None):
+    """Y = W x X (or, with ``residual``, the LinearAdd Y = W x X + R) on torch
+    device tensors.
 
     ``x``: uint16/int16/bfloat16 ``[T, K]`` (bf16 bits, token-major);
     ``codes``: uint8 ``[N, K/2]``; ``scales``: float16/int16/uint16 ``[N, K/64]``;
-    ``y``: optional bfloat16/int16/uint16 ``[T, N]`` output.  Returns ``y``.
+    ``y``: optional bfloat16/int16/uint16 ``[T, N]`` output; ``residual``:
+    optional ``[T, N]`` bf16 bits (may be ``y`` itself).  Returns ``y``.
     """
     import torch
 
@@ -138,8 +150,14 @@ def linear(x, codes, scales, y=None, workspace=None, stream=None):
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    st = q4lin_linear(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), y.data_ptr(), n, k, t,
-                      ws_ptr, ws_bytes, stream)
+    if residual is None:
+        st = q4lin_linear(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), y.data_ptr(), n, k, t,
+                          ws_ptr, ws_bytes, stream)
+    else:
+        if tuple(residual.shape) != (t, n) or residual.element_size() != 2 or not residual.is_contiguous():
+            raise ValueError("residual must be a contiguous [T, N] tensor of 2-byte elements")
+        st = q4lin_linear_add(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), residual.data_ptr(),
+                              y.data_ptr(), n, k, t, ws_ptr, ws_bytes, stream)
     if st != Q4LIN_OK:
         raise Q4LinError(st)
     return y

@@ -44,6 +44,37 @@ size_t route_workspace(int route, int64_t n, int64_t k, int64_t t) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// The op, with an optional residual (LinearAdd when res is not null).
+int run_linear(const void* x, const void* codes, const void* scales, const void* res, void* y,
+               int64_t n, int64_t k, int64_t t, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape_ok(n, k, t)) return Q4LIN_E_SHAPE;
+  const int route = pick_route(n, k, t);
+  if (route == Q4LIN_ROUTE_NONE) return Q4LIN_OK;
+  if (!x || !codes || !scales || !y) return Q4LIN_E_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(y, 2) || !aligned(res, 2))
+    return Q4LIN_E_ALIGN;
+  const size_t need = route_workspace(route, n, k, t);
+  if (need > 0) {
+    if (workspace_bytes < need) return Q4LIN_E_WORKSPACE;
+    if (!workspace) return Q4LIN_E_NULL;
+    if (!aligned(workspace, 256)) return Q4LIN_E_ALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  const q4lin::GemvArgs ga{x, codes, scales, y, n, k, t, res};
+  if (route == Q4LIN_ROUTE_GEMV) {
+    e = q4lin::launch_gemv(ga, s);
+  } else if (route == Q4LIN_ROUTE_DECODE) {
+    e = q4lin::launch_decode(ga, s);
+  } else if (route == Q4LIN_ROUTE_SKINNY) {
+    e = q4lin::launch_skinny(ga, s);
+  } else {
+    q4lin::TiledArgs a{x, codes, scales, y, n, k, t, workspace, q4lin::tiled_pick_config(n, k, t), res};
+    e = q4lin::launch_tiled(a, s);
+  }
+  return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -61,31 +92,14 @@ int q4lin_route(int64_t n, int64_t k, int64_t t) {
 int q4lin_linear(const void* x, const void* codes, const void* scales, void* y,
                  int64_t n, int64_t k, int64_t t,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  if (!shape_ok(n, k, t)) return Q4LIN_E_SHAPE;
-  const int route = pick_route(n, k, t);
-  if (route == Q4LIN_ROUTE_NONE) return Q4LIN_OK;
-  if (!x || !codes || !scales || !y) return Q4LIN_E_NULL;
-  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(y, 2))
-    return Q4LIN_E_ALIGN;
-  const size_t need = route_workspace(route, n, k, t);
-  if (need > 0) {
-    if (workspace_bytes < need) return Q4LIN_E_WORKSPACE;
-    if (!workspace) return Q4LIN_E_NULL;
-    if (!aligned(workspace, 256)) return Q4LIN_E_ALIGN;
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  if (route == Q4LIN_ROUTE_GEMV) {
-    e = q4lin::launch_gemv(q4lin::GemvArgs{x, codes, scales, y, n, k, t}, s);
-  } else if (route == Q4LIN_ROUTE_DECODE) {
-    e = q4lin::launch_decode(q4lin::GemvArgs{x, codes, scales, y, n, k, t}, s);
-  } else if (route == Q4LIN_ROUTE_SKINNY) {
-    e = q4lin::launch_skinny(q4lin::GemvArgs{x, codes, scales, y, n, k, t}, s);
-  } else {
-    q4lin::TiledArgs a{x, codes, scales, y, n, k, t, workspace, q4lin::tiled_pick_config(n, k, t)};
-    e = q4lin::launch_tiled(a, s);
-  }
-  return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+  return run_linear(x, codes, scales, nullptr, y, n, k, t, workspace, workspace_bytes, stream);
+}
+
+int q4lin_linear_add(const void* x, const void* codes, const void* scales, const void* residual, void* y,
+                     int64_t n, int64_t k, int64_t t,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (shape_ok(n, k, t) && n > 0 && t > 0 && !residual) return Q4LIN_E_NULL;
+  return run_linear(x, codes, scales, residual, y, n, k, t, workspace, workspace_bytes, stream);
 }
 
 const char* q4lin_status_string(int status) {
@@ -93,13 +107,13 @@ const char* q4lin_status_string(int status) {
     case Q4LIN_OK: return "ok";
     case Q4LIN_E_NULL: return "a required pointer is NULL";
     case Q4LIN_E_SHAPE: return "shape outside the contract (K a positive multiple of 64, sizes within limits)";
-    case Q4LIN_E_ALIGN: return "pointer misaligned (x, codes: 16 B; scales, y: 2 B; workspace: 256 B)";
+    case Q4LIN_E_ALIGN: return "pointer misaligned (x, codes: 16 B; scales, y, residual: 2 B; workspace: 256 B)";
     case Q4LIN_E_WORKSPACE: return "workspace smaller than q4lin_workspace_bytes()";
     case Q4LIN_E_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
 }
 
-int q4lin_version(void) { return 100; }
+int q4lin_version(void) { return 200; }
 
 }  // extern "C"

@@ -135,7 +135,7 @@ __device__ __forceinline__ float piece_dot(u32x4_t w, const u32x4_t (&xf)[4]) {
 template <int PL, int MAXR>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-              uint16_t* __restrict__ y, int N, int K, int BN) {
+              uint16_t* y, int N, int K, int BN, const uint16_t* res) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int G = K >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -319,7 +319,10 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     v += __shfl_xor(v, 1);
     v += __shfl_xor(v, 2);
     v += __shfl_xor(v, 4);
-    if (wv == 0) y[n0 + r] = f32_to_bf16_rne((float)v);
+    if (wv == 0) {
+      if (res != nullptr) v += (double)bf16_bits_to_f32(res[n0 + r]);  // LinearAdd
+      y[n0 + r] = f32_to_bf16_rne((float)v);
+    }
   }
 }
 
@@ -337,7 +340,7 @@ hipError_t launch_pm(const DecodePlan& p, const GemvArgs& a, hipStream_t stream)
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)p.blocks), dim3(kThreads), lds, stream>>>(
       static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
-      static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, p.bn);
+      static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, p.bn, static_cast<const uint16_t*>(a.res));
   return hipGetLastError();
 }
 

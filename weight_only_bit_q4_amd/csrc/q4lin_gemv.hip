@@ -98,8 +98,8 @@ __device__ __forceinline__ float chunk_dot(u32x4_t w, const u32x4_t* xs, int pla
 template <int T, bool ONE>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(const u32x4_t* __restrict__ x, const uint8_t* __restrict__ codes,
-            const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
-            int N, int K, int cq) {
+            const uint16_t* __restrict__ scales, uint16_t* y,
+            int N, int K, int cq, const uint16_t* res) {
   // Dynamic LDS per wave: activations [T][4 planes][cq] (16 B each), then the
   // all-8 sums [T][cq] (4 B each).  cq = ceil(C / 4) chunk slots per wave.
   extern __shared__ u32x4_t lds[];
@@ -270,6 +270,7 @@ gemv_kernel(const u32x4_t* __restrict__ x, const uint8_t* __restrict__ codes,
       double v = 0.0;
 #pragma unroll
       for (int q = 0; q < kWaves; ++q) v += __builtin_ldexp((double)lds_part[q][r][t], lds_e[q][t] + 24);
+      if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + row]);  // LinearAdd
       y[(size_t)t * N + row] = f32_to_bf16_rne((float)v);
     }
   }
@@ -287,7 +288,8 @@ hipError_t launch_t(const GemvArgs& a, hipStream_t stream) {
   const uint16_t* scales = static_cast<const uint16_t*>(a.scales);
   uint16_t* y = static_cast<uint16_t*>(a.y);
   int n = (int)a.n, k = (int)a.k;
-  void* args[] = {&x, &codes, &scales, &y, &n, &k, (void*)&cq};
+  const uint16_t* res = static_cast<const uint16_t*>(a.res);
+  void* args[] = {&x, &codes, &scales, &y, &n, &k, (void*)&cq, &res};
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, dim3(kThreads), args, lds, stream);
 }
 

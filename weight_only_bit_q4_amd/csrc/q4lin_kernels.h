@@ -13,6 +13,7 @@ struct GemvArgs {
   const void* scales;
   void* y;
   int64_t n, k, t;
+  const void* res = nullptr;  // LinearAdd residual, bf16 [T][N] like y (nullptr: plain Linear)
 };
 
 // Few-token route.  Each of the 4 waves of a workgroup owns a quarter of the
@@ -68,6 +69,7 @@ struct TiledArgs {
   int64_t n, k, t;
   void* workspace;
   TiledConfig cfg;
+  const void* res = nullptr;  // LinearAdd residual, bf16 [T][N] like y (nullptr: plain Linear)
 };
 
 int64_t tiled_tpad(int64_t t);

@@ -132,8 +132,8 @@ __device__ __forceinline__ int dword_b(int q) { return dword_a(q) + 1; }
 template <int CT, int TT, int NL, int DEPTH>
 __global__ void __launch_bounds__(kThreads, 1)
 skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
-              const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
-              int N, int K, int T, int BN, int off_codes, int off_red) {
+              const uint16_t* __restrict__ scales, uint16_t* y,
+              int N, int K, int T, int BN, int off_codes, int off_red, const uint16_t* res) {
   constexpr int BNP = 16 * CT;  // matrix-core columns (rows of W) per workgroup
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   // LDS: the block's scales (fp16 [BNP][G] from byte s_delta), then the
@@ -438,6 +438,7 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     double v = 0.0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) v += red[(w * T + t) * BN + col];
+    if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + n0 + col]);  // LinearAdd
     y[(size_t)t * N + n0 + col] = f32_to_bf16_rne((float)v);
   }
 }
@@ -451,7 +452,7 @@ hipError_t launch_ct(const SkinnyPlan& p, const GemvArgs& a, hipStream_t stream)
   kern<<<dim3((unsigned)p.blocks), dim3(kThreads), p.lds_bytes, stream>>>(
       static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes),
       static_cast<const uint16_t*>(a.scales), static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, (int)a.t,
-      p.bn, p.off_codes, p.off_red);
+      p.bn, p.off_codes, p.off_red, static_cast<const uint16_t*>(a.res));
   return hipGetLastError();
 }
 

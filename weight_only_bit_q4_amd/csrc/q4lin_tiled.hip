@@ -368,12 +368,14 @@ struct TiledShape {
   static_assert(3 * AI + 2 * CP + SQ <= 63, "the load counter holds 63");
 };
 
-template <int NS, int TS, int WN, int WT>
+// ADD: the LinearAdd form (a residual joins the results); the plain form
+// carries none of its code.
+template <int NS, int TS, int WN, int WT, bool ADD>
 __global__ void __launch_bounds__(64 * WN * WT)
 tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, const int* __restrict__ rexp,
              const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-             uint16_t* __restrict__ y, float* __restrict__ part, int N, int K, int T, int Tpad, int tiles_n,
-             int tiles_t, int KS) {
+             uint16_t* y, float* __restrict__ part, int N, int K, int T, int Tpad, int tiles_n,
+             int tiles_t, int KS, const uint16_t* res) {
   using Sh = TiledShape<NS, TS, WN, WT>;
   constexpr int NT = Sh::NT, BN = Sh::BN, BT = Sh::BT, CD = Sh::CD, CQ = Sh::CQ, CP = Sh::CP, AI = Sh::AI, SQ = Sh::SQ;
   constexpr int NW = WN * WT;
@@ -775,6 +777,23 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
       }
     return;
   }
+  // LinearAdd: the tile's residual values, all loaded before the first use
+  // (one round trip: the loads are unconditional, at clamped indices, so no
+  // branch separates them), so each joins its FP32 result before the one
+  // rounding.  Values of padding tokens and rows are never stored.
+  uint16_t rr[TS][NS][16];
+  if constexpr (ADD) {
+#pragma unroll
+    for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = min(32 * tb0 + (wt * TS + ts) * 32 + 4 * lh + 8 * (r >> 2) + (r & 3), T - 1);
+          const int n = min(n0 + (wn * NS + ns) * 32 + li, N - 1);
+          rr[ts][ns][r] = res[(size_t)t * N + n];
+        }
+  }
   __syncthreads();
   uint16_t* otile = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
@@ -791,9 +810,11 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
 #pragma unroll
     for (int r = 0; r < 16; ++r)
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-        otile[(tl + 8 * (r >> 2) + (r & 3)) * BN + (wn * NS + ns) * 32 + li] =
-            f32_to_bf16_rne(__builtin_ldexpf(acc[ts][ns][r], e[r] - ce[ns]));
+      for (int ns = 0; ns < NS; ++ns) {
+        float v = __builtin_ldexpf(acc[ts][ns][r], e[r] - ce[ns]);
+        if constexpr (ADD) v += bf16_bits_to_f32(rr[ts][ns][r]);
+        otile[(tl + 8 * (r >> 2) + (r & 3)) * BN + (wn * NS + ns) * 32 + li] = f32_to_bf16_rne(v);
+      }
   }
   __syncthreads();
   const int t0 = 32 * tb0;
@@ -819,7 +840,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
 constexpr int kMaxSplits = 8;
 __global__ void __launch_bounds__(256)
 tiled_reduce_kernel(const float* __restrict__ part, const int* __restrict__ texp, const int* __restrict__ rexp,
-                    uint16_t* __restrict__ y, int N, int Tpad, int KS) {
+                    uint16_t* y, int N, int Tpad, int KS, const uint16_t* res) {
   const int n = blockIdx.x * 256 + threadIdx.x, t = blockIdx.y;
   if (n >= N) return;
   const size_t i = (size_t)t * N + n, stride = (size_t)Tpad * N;
@@ -830,7 +851,9 @@ tiled_reduce_kernel(const float* __restrict__ part, const int* __restrict__ texp
 #pragma unroll
   for (int k = 0; k < kMaxSplits; ++k)
     if (k < KS) v += p[k];
-  y[i] = f32_to_bf16_rne(__builtin_ldexpf(v, texp[t] - rexp[n]));
+  v = __builtin_ldexpf(v, texp[t] - rexp[n]);
+  if (res != nullptr) v += bf16_bits_to_f32(res[i]);  // LinearAdd
+  y[i] = f32_to_bf16_rne(v);
 }
 
 template <int NS, int TS, int WN, int WT>
@@ -839,7 +862,7 @@ hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, c
   using Sh = TiledShape<NS, TS, WN, WT>;
   const int tiles_n = (int)((a.n + Sh::BN - 1) / Sh::BN);
   const int tiles_t = (int)((a.t + Sh::BT - 1) / Sh::BT);
-  auto kern = tiled_kernel<NS, TS, WN, WT>;
+  auto kern = a.res != nullptr ? tiled_kernel<NS, TS, WN, WT, true> : tiled_kernel<NS, TS, WN, WT, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS_B);
   if (e != hipSuccess) return e;
@@ -847,11 +870,12 @@ hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, c
   if (ks < 1 || ks > kMaxSplits) return hipErrorInvalidValue;
   kern<<<dim3((unsigned)(tiles_n * tiles_t * ks)), dim3(Sh::NT), Sh::LDS_B, stream>>>(
       x16, texp, rexp, static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
-      static_cast<uint16_t*>(a.y), ks > 1 ? part : nullptr, (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t, ks);
+      static_cast<uint16_t*>(a.y), ks > 1 ? part : nullptr, (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t, ks,
+      static_cast<const uint16_t*>(a.res));
   e = hipGetLastError();
   if (e != hipSuccess || ks == 1) return e;
   tiled_reduce_kernel<<<dim3((unsigned)((a.n + 255) / 256), (unsigned)a.t), dim3(256), 0, stream>>>(
-      part, texp, rexp, static_cast<uint16_t*>(a.y), (int)a.n, tpad, ks);
+      part, texp, rexp, static_cast<uint16_t*>(a.y), (int)a.n, tpad, ks, static_cast<const uint16_t*>(a.res));
   return hipGetLastError();
 }
 
