@@ -131,8 +131,38 @@ __device__ __forceinline__ float piece_dot(u32x4_t w, const u32x4_t (&xf)[4]) {
   return c;
 }
 
-// PL: consecutive 16-byte pieces per lane and row; MAXR: rows per lane, at most
-template <int PL, int MAXR>
+// (128 + q) bf16 pairs of one 16-byte code piece, in the order of
+// piece_dot_bf16's chain, for reuse against several tokens
+__device__ __forceinline__ void piece_codes_bf16(u32x4_t w, uint32_t (&c)[16]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t wd = w[d];
+    c[4 * d + 0] = and_or(wd, 0x000F000Fu, 0x43004300u);
+    c[4 * d + 1] = and_or(wd >> 4, 0x000F000Fu, 0x43004300u);
+    c[4 * d + 2] = and_or(wd >> 8, 0x000F000Fu, 0x43004300u);
+    c[4 * d + 3] = and_or(wd >> 12, 0x000F000Fu, 0x43004300u);
+  }
+}
+
+// the chain of piece_dot_bf16 on pre-converted codes (same order, same sum)
+__device__ __forceinline__ float piece_dot_pre(const uint32_t (&c)[16], const u32x4_t (&xb)[4]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    a = dot2_bf16(c[4 * d + 0], xb[d].x, a);
+    a = dot2_bf16(c[4 * d + 1], xb[d].y, a);
+    a = dot2_bf16(c[4 * d + 2], xb[d].z, a);
+    a = dot2_bf16(c[4 * d + 3], xb[d].w, a);
+  }
+  return a;
+}
+
+// PL: consecutive 16-byte pieces per lane and row; MAXR: rows per lane, at
+// most; NT: tokens (1..4).  With several tokens every lane keeps each token's
+// piece of X, converts each code piece once and runs one dot chain per token
+// (vector-ALU work grows with NT, the weight stream does not: a few tokens
+// cost little more than one).
+template <int PL, int MAXR, int NT>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
               uint16_t* y, int N, int K, int BN, const uint16_t* res) {
@@ -156,21 +186,23 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   const int slot = lane - grp_raw * S;
   const int pc0 = slot * PL;
 
-  // LDS: per wave a scratch of 64 x MAXR floats (regions 16 bytes more than
-  // that apart, so that the eight threads of a row, which read the eight
-  // regions at the same offset, hit different banks), then the waves'
-  // exponents.
-  float* scratch = reinterpret_cast<float*>(lds + wave * kRegion<MAXR>);
-  int* wexp = reinterpret_cast<int*>(lds + kWaves * kRegion<MAXR>);
+  // LDS: per wave and token a scratch of 64 x MAXR floats (regions 16 bytes
+  // more than that apart, so that the eight threads of a row, which read the
+  // eight regions at the same offset, hit different banks), then the waves'
+  // per-token exponents.
+  int* wexp = reinterpret_cast<int*>(lds + kWaves * NT * kRegion<MAXR>);
 
   // 1. the lane's activations (first: waiting for them waits for nothing else)
-  u32x4_t xv[PL][4];
+  u32x4_t xv[NT][PL][4];
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(x + 64 * gl + 32 * min(pc0 + i, max(P - 1, 0)));
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) xv[i][d] = xp[d];
-  }
+    for (int i = 0; i < PL; ++i) {
+      const u32x4_t* xp =
+          reinterpret_cast<const u32x4_t*>(x + (size_t)t * K + 64 * gl + 32 * min(pc0 + i, max(P - 1, 0)));
+#pragma unroll
+      for (int d = 0; d < 4; ++d) xv[t][i][d] = xp[d];
+    }
   // 2. codes of the lane's rows, in row order (the rows are waited for one by
   //    one below; values of rows past the block and pieces past the slice are
   //    never used)
@@ -197,27 +229,40 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 
   // 4. activation pairs in the order of the code pairs, and the correction
   //    sums of the all-eight codes through the very same dot chain
-  u32x4_t xb[PL][4];
+  u32x4_t xb[NT][PL][4];
 #pragma unroll
-  for (int i = 0; i < PL; ++i)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) xb[i][d] = bf16_pairs(xv[i][d]);
+    for (int i = 0; i < PL; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) xb[t][i][d] = bf16_pairs(xv[t][i][d]);
   const u32x4_t k8 = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-  float c8[PL];
+  float c8[NT][PL];
 #pragma unroll
-  for (int i = 0; i < PL; ++i) c8[i] = piece_dot_bf16(k8, xb[i]);
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < PL; ++i) c8[t][i] = piece_dot_bf16(k8, xb[t][i]);
 
   // 5. the pieces' sums (q - 8) x, row by row in the order the codes arrive:
   //    row j waits only for its own loads (the younger code loads of later
   //    rows and the scale loads may still be in flight)
-  float dp[MAXR][PL];
+  float dp[MAXR][NT][PL];
   static_for<MAXR>([&](auto jj) {
     constexpr int j = decltype(jj)::value;
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((MAXR - 1 - j) * PL + MAXR * PL));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < PL; ++i) dp[j][i] = piece_dot_bf16(w[j][i], xb[i]) - c8[i];
+    for (int i = 0; i < PL; ++i) {
+      if constexpr (NT == 1) {
+        dp[j][0][i] = piece_dot_bf16(w[j][i], xb[0][i]) - c8[0][i];  // converts as it goes (fewer registers)
+      } else {
+        uint32_t c[16];
+        piece_codes_bf16(w[j][i], c);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) dp[j][t][i] = piece_dot_pre(c, xb[t][i]) - c8[t][i];
+      }
+    }
   });
   // 6. scales
   float sc[MAXR][PL];
@@ -225,70 +270,86 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   for (int j = 0; j < MAXR; ++j)
 #pragma unroll
     for (int i = 0; i < PL; ++i) sc[j][i] = pc0 + i < P ? f16_bits_to_f32(sbits[j][i]) : 0.0f;
-  float acc[MAXR];
+  float acc[NT][MAXR];
   bool bad = false;
 #pragma unroll
-  for (int j = 0; j < MAXR; ++j) {
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      bad |= !__builtin_isfinite(dp[j][i]);
-      a = __builtin_fmaf(sc[j][i], dp[j][i], a);
-    }
-    acc[j] = a;
-    bad |= !__builtin_isfinite(a);
-  }
-
-  // 7. activations near the bf16 maximum can overflow these FP32 sums: then
-  //    the wave redoes its rows on float16 copies of X scaled by 2^-e (e from
-  //    the slice's largest magnitude, so the sums stay in range) and its
-  //    partials carry 2^-(e+24)
-  int ew = 0;
-  if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < PL; ++i)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) m = max(m, max_mag8(xv[i][d]));
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    const int e = exponent_for(m);
-    u32x4_t xf[PL][4];
-#pragma unroll
-    for (int i = 0; i < PL; ++i)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) xf[i][d] = to_f16_pairs(xv[i][d], e);
-    float s8[PL];
-#pragma unroll
-    for (int i = 0; i < PL; ++i) s8[i] = piece_dot(k8, xf[i]);
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int j = 0; j < MAXR; ++j) {
       float a = 0.0f;
 #pragma unroll
-      for (int i = 0; i < PL; ++i) a = __builtin_fmaf(sc[j][i], piece_dot(w[j][i], xf[i]) - s8[i], a);
-      acc[j] = a;
+      for (int i = 0; i < PL; ++i) {
+        bad |= !__builtin_isfinite(dp[j][t][i]);
+        a = __builtin_fmaf(sc[j][i], dp[j][t][i], a);
+      }
+      acc[t][j] = a;
+      bad |= !__builtin_isfinite(a);
     }
-    ew = e + 24;
+
+  // 7. activations near the bf16 maximum can overflow these FP32 sums: then
+  //    the wave redoes its rows on float16 copies of X scaled by 2^-e (e per
+  //    token from its slice's largest magnitude, so the sums stay in range)
+  //    and its partials carry 2^-(e+24)
+  int ew[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ew[t] = 0;
+  if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) m = max(m, max_mag8(xv[t][i][d]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+      const int e = exponent_for(m);
+      u32x4_t xf[PL][4];
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) xf[i][d] = to_f16_pairs(xv[t][i][d], e);
+      float s8[PL];
+#pragma unroll
+      for (int i = 0; i < PL; ++i) s8[i] = piece_dot(k8, xf[i]);
+#pragma unroll
+      for (int j = 0; j < MAXR; ++j) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) a = __builtin_fmaf(sc[j][i], piece_dot(w[j][i], xf[i]) - s8[i], a);
+        acc[t][j] = a;
+      }
+      ew[t] = e + 24;
+    }
   }
   // waves without groups contribute zero
   if (ng <= 0)
 #pragma unroll
-    for (int j = 0; j < MAXR; ++j) acc[j] = 0.0f;
-
-  // 8. sums: every lane's partials and every wave's exponent into LDS; then
-  //    eight threads per row each add one wave's S slots, scale by that
-  //    wave's 2^ew in binary64, and combine the eight by shuffles; the
-  //    row's first thread rounds to bf16 once and stores
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-  for (int j = 0; j < MAXR; ++j) scratch[j * 64 + lane] = acc[j];
-  if (lane == 0) wexp[wave] = ew;
+      for (int j = 0; j < MAXR; ++j) acc[t][j] = 0.0f;
+
+  // 8. sums: every lane's partials and every wave's exponents into LDS; then
+  //    eight threads per (row, token) each add one wave's S slots, scale by
+  //    that wave's 2^ew in binary64, and combine the eight by shuffles; the
+  //    first of them rounds to bf16 once and stores
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float* scratch = reinterpret_cast<float*>(lds + (wave * NT + t) * kRegion<MAXR>);
+#pragma unroll
+    for (int j = 0; j < MAXR; ++j) scratch[j * 64 + lane] = acc[t][j];
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) wexp[wave * NT + t] = ew[t];
   __syncthreads();
-  for (int idx = tid; idx < rows * kWaves; idx += kThreads) {
-    const int r = idx / kWaves, wv = idx % kWaves;
+  for (int idx = tid; idx < NT * rows * kWaves; idx += kThreads) {
+    const int wv = idx % kWaves, rt = idx / kWaves;
+    const int t = rt / rows, r = rt - t * rows;
     const int glw = (G * wv) / kWaves, ngw = (G * (wv + 1)) / kWaves - glw;
     const int Sw = max((2 * ngw + PL - 1) / PL, 1), Rw = 64 / Sw;
     const int g = r % Rw, j = r / Rw;
-    const float* sp = reinterpret_cast<const float*>(lds + wv * kRegion<MAXR>) + j * 64 + g * Sw;
+    const float* sp = reinterpret_cast<const float*>(lds + (wv * NT + t) * kRegion<MAXR>) + j * 64 + g * Sw;
     float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
     if ((Sw & 3) == 0 && Sw <= 32) {
       // all reads in flight together (at most 8 clamped 16-byte pieces)
@@ -314,27 +375,26 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
       }
       for (; sl < Sw; ++sl) v0 += sp[sl];
     }
-    double v = __builtin_ldexp((double)((v0 + v1) + (v2 + v3)), wexp[wv]);
-    // the eight threads of a row are eight consecutive lanes of one wave
+    double v = __builtin_ldexp((double)((v0 + v1) + (v2 + v3)), wexp[wv * NT + t]);
+    // the eight threads of a (row, token) are eight consecutive lanes of one wave
     v += __shfl_xor(v, 1);
     v += __shfl_xor(v, 2);
     v += __shfl_xor(v, 4);
     if (wv == 0) {
-      if (res != nullptr) v += (double)bf16_bits_to_f32(res[n0 + r]);  // LinearAdd
-      y[n0 + r] = f32_to_bf16_rne((float)v);
+      if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + n0 + r]);  // LinearAdd
+      y[(size_t)t * N + n0 + r] = f32_to_bf16_rne((float)v);
     }
   }
 }
 
-size_t decode_lds(int bn, int maxr) {
-  (void)bn;
-  return (size_t)kWaves * (size_t)(64 * maxr * 4 + 16) + (size_t)kWaves * 4;
+size_t decode_lds(int maxr, int nt) {
+  return (size_t)kWaves * (size_t)nt * (size_t)(64 * maxr * 4 + 16) + (size_t)kWaves * (size_t)nt * 4;
 }
 
-template <int PL, int MAXR>
+template <int PL, int MAXR, int NT>
 hipError_t launch_pm(const DecodePlan& p, const GemvArgs& a, hipStream_t stream) {
-  auto kern = decode_kernel<PL, MAXR>;
-  const size_t lds = decode_lds(p.bn, MAXR);
+  auto kern = decode_kernel<PL, MAXR, NT>;
+  const size_t lds = decode_lds(MAXR, NT);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -355,26 +415,33 @@ constexpr int kShapes[][2] = {{1, 8}, {2, 8}, {4, 4}, {1, 16}};
 // For each shape in turn, the fewest workgroups per CU (1..6, so blocks of
 // about N / (256 c) rows) whose rows the shape covers.  Measured on
 // 6144/14336/34816 x 5120 and 5120 x 17408: more, smaller blocks beat
-// more rows per lane.
+// more rows per lane.  Two to four tokens take the first shape only (their
+// activations and sums need the registers the other shapes use for codes).
+constexpr int kMaxDecodeTokens = 4;
 bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p) {
-  if (t != 1 || n < 1 || k < 64) return false;
+  if (t < 1 || t > kMaxDecodeTokens || n < 1 || k < 64) return false;
   if (n * (k / 2) >= (int64_t(1) << 31)) return false;  // 32-bit buffer offsets
   const int64_t G = k / 64;
   const int64_t pmax = 2 * ((G + kWaves - 1) / kWaves);
   const int64_t pmin = 2 * (G / kWaves);
   for (const auto& sh : kShapes) {
     const int64_t pl = sh[0], maxr = sh[1];
+    if (t > 1 && !(pl == 1 && maxr == 8)) continue;
     const int64_t s = (pmax + pl - 1) / pl;
     if (s > 64) continue;
     // every wave, also one with the smaller slice, must cover bn rows
     const int64_t smin = pmin > 0 ? (pmin + pl - 1) / pl : 1;
     const int64_t rmin = 64 / (s > smin ? s : smin);
-    for (int64_t c = 1; c <= 6; ++c) {  // workgroups per CU
+    // (with several tokens a workgroup takes every register a CU's SIMDs
+    // hold for two waves each: one workgroup per CU, c = 1 only; measured, a
+    // second round of workgroups costs more than the small-T route)
+    for (int64_t c = 1; c <= (t > 1 ? 1 : 6); ++c) {  // workgroups per CU
       const int64_t bn = (n + 256 * c - 1) / (256 * c);
       if ((bn + rmin - 1) / rmin > maxr) continue;
       // fewer than half the lanes busy: leave the shape to the other route
       if (2 * rmin * s < 64 && bn > rmin) continue;
-      if (decode_lds((int)bn, (int)maxr) > 64 * 1024) continue;
+      // c workgroups of this size must fit one CU's 160 KB of LDS
+      if (decode_lds((int)maxr, (int)t) * (size_t)c > 160 * 1024) continue;
       p->bn = (int)bn;
       p->pl = (int)pl;
       p->maxr = (int)maxr;
@@ -388,10 +455,18 @@ bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p) {
 hipError_t launch_decode(const GemvArgs& a, hipStream_t stream) {
   DecodePlan p;
   if (!decode_plan(a.n, a.k, a.t, &p)) return hipErrorInvalidValue;
-  if (p.pl == 1 && p.maxr == 8) return launch_pm<1, 8>(p, a, stream);
-  if (p.pl == 1 && p.maxr == 16) return launch_pm<1, 16>(p, a, stream);
-  if (p.pl == 2 && p.maxr == 8) return launch_pm<2, 8>(p, a, stream);
-  if (p.pl == 4 && p.maxr == 4) return launch_pm<4, 4>(p, a, stream);
+  if (p.pl == 1 && p.maxr == 8) {
+    switch (a.t) {
+      case 1: return launch_pm<1, 8, 1>(p, a, stream);
+      case 2: return launch_pm<1, 8, 2>(p, a, stream);
+      case 3: return launch_pm<1, 8, 3>(p, a, stream);
+      case 4: return launch_pm<1, 8, 4>(p, a, stream);
+    }
+  }
+  if (a.t != 1) return hipErrorInvalidValue;
+  if (p.pl == 1 && p.maxr == 16) return launch_pm<1, 16, 1>(p, a, stream);
+  if (p.pl == 2 && p.maxr == 8) return launch_pm<2, 8, 1>(p, a, stream);
+  if (p.pl == 4 && p.maxr == 4) return launch_pm<4, 4, 1>(p, a, stream);
   return hipErrorInvalidValue;
 }
 
