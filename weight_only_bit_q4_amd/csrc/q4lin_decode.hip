@@ -345,7 +345,7 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   __syncthreads();
   for (int idx = tid; idx < NT * rows * kWaves; idx += kThreads) {
     const int wv = idx % kWaves, rt = idx / kWaves;
-    const int t = rt / rows, r = rt - t * rows;
+    const int t = NT == 1 ? 0 : rt / rows, r = rt - t * rows;
     const int glw = (G * wv) / kWaves, ngw = (G * (wv + 1)) / kWaves - glw;
     const int Sw = max((2 * ngw + PL - 1) / PL, 1), Rw = 64 / Sw;
     const int g = r % Rw, j = r / Rw;
