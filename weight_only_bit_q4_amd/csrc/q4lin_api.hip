@@ -30,9 +30,16 @@ bool shape_ok(int64_t n, int64_t k, int64_t t) {
 int pick_route(int64_t n, int64_t k, int64_t t) {
   if (n == 0 || t == 0) return Q4LIN_ROUTE_NONE;
   q4lin::DecodePlan dp;
-  if (q4lin::decode_plan(n, k, t, &dp)) return Q4LIN_ROUTE_DECODE;
-  if (t == 1 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
   q4lin::SkinnyPlan sp;
+  if (q4lin::decode_plan(n, k, t, &dp)) {
+    // The single-token route streams best with one 16-byte piece per lane
+    // and row; where a wave's slice is longer than 64 pieces (K > 16384) the
+    // small-T route beats its wider lane shapes (5120 x 17408: 19.8 against
+    // 23.3 us)
+    if (dp.pl == 1 || !q4lin::skinny_plan(n, k, t, &sp)) return Q4LIN_ROUTE_DECODE;
+    return Q4LIN_ROUTE_SKINNY;
+  }
+  if (t == 1 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
   if (q4lin::skinny_plan(n, k, t, &sp)) return Q4LIN_ROUTE_SKINNY;
   if (t <= 4 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
   return Q4LIN_ROUTE_TILED;
