@@ -392,6 +392,8 @@ def main(argv=None):
     ap.add_argument("--profile", action="store_true", help="one call after set-up, then exit")
     ap.add_argument("--add", action="store_true",
                     help="with --t: time the LinearAdd entry point (Y = W x X + R; R adds 2NT bytes)")
+    ap.add_argument("--pair", type=int, default=None, metavar="N2",
+                    help="LinearPair: --n rows and N2 rows over one X, against two separate calls (--t)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--csv", type=str, default=None)
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="BYTES",
@@ -494,6 +496,37 @@ def main(argv=None):
                 w = csv.DictWriter(f, fieldnames=list(rows[0]))
                 w.writeheader()
                 w.writerows(rows)
+        return 0
+
+    if args.pair is not None:
+        # LinearPair against the same two weights called one after the other:
+        # rotating sets as in Point, the pair reading set i's x for both.
+        import weight_only_bit_q4_amd as q4
+        t = args.t if args.t is not None else 1
+        n2 = args.pair
+        p1, p2 = Point(n, k, t, seed), Point(n2, k, t, seed + 1)
+        nsets = min(p1.nsets, p2.nsets)
+        ws_pair = max(q4.q4lin_pair_workspace_bytes(n, n2, k, t), 256)
+        wsp = [torch.empty(ws_pair, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+
+        def pair(i, h):
+            x, c1, s1, y1, _, _ = p1.sets[i % nsets]
+            _, c2, s2, y2, _, _ = p2.sets[i % nsets]
+            st = q4.q4lin_linear_pair(x.data_ptr(), c1.data_ptr(), s1.data_ptr(), y1.data_ptr(), n,
+                                      c2.data_ptr(), s2.data_ptr(), y2.data_ptr(), n2, k, t,
+                                      wsp[i % nsets].data_ptr(), ws_pair, h)
+            if st != 0:
+                raise RuntimeError("q4lin_linear_pair: " + q4.q4lin_status_string(st))
+
+        def two(i, h):
+            p1.call(i % nsets, h)
+            p2.call(i % nsets, h)
+
+        steps = max(20, args.steps // (20 if t >= 512 else 1))
+        sp, s2c = _graph_period(torch, pair, steps), _graph_period(torch, two, steps)
+        byts = model_bytes(n, k, t) + model_bytes(n2, k, t) - 2 * k * t
+        print(json.dumps({"op": "linear_pair", "n1": n, "n2": n2, "k": k, "t": t, "route": q4.q4lin_route(n + n2, k, t),
+                          "pair_us": sp * 1e6, "two_calls_us": s2c * 1e6, "pair_gbs": byts / sp / 1e9}))
         return 0
 
     if args.t is not None:

@@ -96,6 +96,29 @@ Q4LIN_API int q4lin_linear_add(const void *x, const void *codes, const void *sca
                      void *y, int64_t n, int64_t k, int64_t t,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* LinearPair, the third fused Linear variant the pages name beside LinearAdd
+ * and LinearSwiGLU ("q4-linear.md" and "linear-benchmark.md", without a
+ * definition; the plain reading taken here): two weights of the same K over
+ * one activation X, two outputs,
+ *
+ *     Y1[N1,T] = W1[N1,K] x X[K,T]      Y2[N2,T] = W2[N2,K] x X[K,T]
+ *
+ * each element equal to what q4lin_linear gives for that weight alone.  Each
+ * (codes, scales, y) triple follows q4lin_linear's layout and alignment with
+ * its own row count.  The one- to four-token and small-T routes (chosen for
+ * N1 + N2 rows) run both weights in a single launch; the other routes run one
+ * launch sequence per weight, one after the other on `stream`.  workspace
+ * must hold q4lin_pair_workspace_bytes(n1, n2, k, t) bytes.  N1 or N2 = 0
+ * reduces to q4lin_linear on the other weight (whose pointers alone are then
+ * checked).  y1 and y2 must not overlap each other or any input. */
+Q4LIN_API int q4lin_linear_pair(const void *x, const void *codes1, const void *scales1, void *y1, int64_t n1,
+                      const void *codes2, const void *scales2, void *y2, int64_t n2, int64_t k, int64_t t,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace q4lin_linear_pair needs (0 when none), or
+ * -Q4LIN_E_SHAPE for a shape outside the contract.  Pure host function. */
+Q4LIN_API int64_t q4lin_pair_workspace_bytes(int64_t n1, int64_t n2, int64_t k, int64_t t);
+
 /* Static, human-readable text for a status code (never NULL). */
 Q4LIN_API const char *q4lin_status_string(int status);
 

@@ -116,3 +116,45 @@ def test_linear_add_shape_and_workspace_checks():
     n, k, t = 256, 512, 300
     need = q.q4lin_workspace_bytes(n, k, t)
     assert q.q4lin_linear_add(p, p, p, p, p, n, k, t, p, need - 1, 0) == q.Q4LIN_E_WORKSPACE
+
+
+# -- LinearPair: two weights over one X ----------------------------------------
+def test_linear_pair_empty_and_one_plane():
+    assert q.q4lin_linear_pair(0, 0, 0, 0, 0, 0, 0, 0, 0, 128, 5, 0, 0, 0) == q.Q4LIN_OK
+    assert q.q4lin_linear_pair(0, 0, 0, 0, 6, 0, 0, 0, 7, 128, 0, 0, 0, 0) == q.Q4LIN_OK
+    p = 0x10000
+    # one plane empty: only the other weight's pointers are checked (a
+    # misaligned output stops the call before any launch)
+    assert q.q4lin_linear_pair(p, p, p, p + 1, 64, 0, 0, 0, 0, 128, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
+    assert q.q4lin_linear_pair(p, 0, 0, 0, 0, p, p, p + 1, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
+    assert q.q4lin_linear_pair(p, p, p, 0, 64, 0, 0, 0, 0, 128, 1, 0, 0, 0) == q.Q4LIN_E_NULL
+
+
+@pytest.mark.parametrize("which", [0, 1, 2, 3, 5, 6, 7])
+def test_linear_pair_null_pointer_rejected(which):
+    args = [0x1000, 0x1000, 0x1000, 0x1000, 64, 0x1000, 0x1000, 0x1000, 64, 128, 1, 0, 0, 0]
+    args[which] = 0
+    assert q.q4lin_linear_pair(*args) == q.Q4LIN_E_NULL
+
+
+@pytest.mark.parametrize("which,addr", [(0, 0x1008), (1, 0x1004), (2, 0x1001), (3, 0x1001), (5, 0x1004),
+                                        (6, 0x1001), (7, 0x1001)])
+def test_linear_pair_misaligned_pointer_rejected(which, addr):
+    args = [0x1000, 0x1000, 0x1000, 0x1000, 64, 0x1000, 0x1000, 0x1000, 64, 128, 1, 0, 0, 0]
+    args[which] = addr
+    assert q.q4lin_linear_pair(*args) == q.Q4LIN_E_ALIGN
+
+
+def test_linear_pair_shapes_and_workspace():
+    p = 0x10000
+    assert q.q4lin_linear_pair(p, p, p, p, 8, p, p, p, 8, 96, 1, 0, 0, 0) == q.Q4LIN_E_SHAPE
+    assert q.q4lin_linear_pair(p, p, p, p, -1, p, p, p, 8, 128, 1, 0, 0, 0) == q.Q4LIN_E_SHAPE
+    assert q.q4lin_pair_workspace_bytes(8, 8, 96, 1) == -q.Q4LIN_E_SHAPE
+    # fused routes need none; the many-token route needs the larger weight's
+    assert q.q4lin_pair_workspace_bytes(3072, 3072, 5120, 1) == 0
+    assert q.q4lin_pair_workspace_bytes(1000, 700, 2048, 20) == 0
+    n1, n2, k, t = 768, 256, 1024, 100
+    need = q.q4lin_pair_workspace_bytes(n1, n2, k, t)
+    assert need == max(q.q4lin_workspace_bytes(n1, k, t), q.q4lin_workspace_bytes(n2, k, t)) > 0
+    assert q.q4lin_linear_pair(p, p, p, p, n1, p, p, p, n2, k, t, p, need - 1, 0) == q.Q4LIN_E_WORKSPACE
+    assert q.q4lin_pair_workspace_bytes(0, 512, 1024, 300) == q.q4lin_workspace_bytes(512, 1024, 300)

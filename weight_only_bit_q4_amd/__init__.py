@@ -33,8 +33,8 @@ Q4LIN_ROUTE_SKINNY = 2
 Q4LIN_ROUTE_TILED = 3
 Q4LIN_ROUTE_DECODE = 4
 
-EXPORTED = ("q4lin_workspace_bytes", "q4lin_linear", "q4lin_linear_add", "q4lin_status_string", "q4lin_route",
-            "q4lin_version")
+EXPORTED = ("q4lin_workspace_bytes", "q4lin_linear", "q4lin_linear_add", "q4lin_linear_pair",
+            "q4lin_pair_workspace_bytes", "q4lin_status_string", "q4lin_route", "q4lin_version")
 
 
 class Q4LinError(RuntimeError):
@@ -64,6 +64,10 @@ def _load() -> ctypes.CDLL:
     lib.q4lin_linear.restype = ctypes.c_int
     lib.q4lin_linear_add.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.q4lin_linear_add.restype = ctypes.c_int
+    lib.q4lin_linear_pair.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.q4lin_linear_pair.restype = ctypes.c_int
+    lib.q4lin_pair_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.q4lin_pair_workspace_bytes.restype = i64
     lib.q4lin_status_string.argtypes = [ctypes.c_int]
     lib.q4lin_status_string.restype = ctypes.c_char_p
     lib.q4lin_route.argtypes = [i64, i64, i64]
@@ -103,6 +107,18 @@ def q4lin_linear_add(x: int, codes: int, scales: int, residual: int, y: int, n: 
     return int(load().q4lin_linear_add(x or None, codes or None, scales or None, residual or None, y or None,
                                        int(n), int(k), int(t), workspace or None,
                                        int(workspace_bytes), stream or None))
+
+
+def q4lin_linear_pair(x: int, codes1: int, scales1: int, y1: int, n1: int, codes2: int, scales2: int, y2: int,
+                      n2: int, k: int, t: int, workspace: int, workspace_bytes: int, stream: int) -> int:
+    """Raw call of the LinearPair entry point (Y1 = W1 x X, Y2 = W2 x X); returns the status."""
+    return int(load().q4lin_linear_pair(x or None, codes1 or None, scales1 or None, y1 or None, int(n1),
+                                        codes2 or None, scales2 or None, y2 or None, int(n2), int(k), int(t),
+                                        workspace or None, int(workspace_bytes), stream or None))
+
+
+def q4lin_pair_workspace_bytes(n1: int, n2: int, k: int, t: int) -> int:
+    return int(load().q4lin_pair_workspace_bytes(int(n1), int(n2), int(k), int(t)))
 
 
 def q4lin_status_string(status: int) -> str:
@@ -161,3 +177,44 @@ def linear(x, codes, scales, y=None, workspace=None, stream=None, residual=None)
     if st != Q4LIN_OK:
         raise Q4LinError(st)
     return y
+
+
+def linear_pair(x, codes1, scales1, codes2, scales2, y1=None, y2=None, workspace=None, stream=None):
+    """LinearPair on torch device tensors: ``(W1 x X, W2 x X)`` for two weights
+    of the same K over one ``x`` (layouts as in ``linear``).  Returns
+    ``(y1, y2)``."""
+    import torch
+
+    t, k = x.shape
+    n1, n2 = codes1.shape[0], codes2.shape[0]
+    for i, (c, sc) in enumerate(((codes1, scales1), (codes2, scales2)), 1):
+        n = c.shape[0]
+        if c.shape[1] * 2 != k or tuple(sc.shape) != (n, k // 64):
+            raise ValueError("shape mismatch: x %s codes%d %s scales%d %s" % (tuple(x.shape), i, tuple(c.shape),
+                                                                           i, tuple(sc.shape)))
+    for name, ten, size in (("x", x, 2), ("codes1", codes1, 1), ("scales1", scales1, 2), ("codes2", codes2, 1),
+                            ("scales2", scales2, 2)):
+        if not ten.is_contiguous() or ten.element_size() != size:
+            raise ValueError("%s must be contiguous with %d-byte elements" % (name, size))
+    outs = []
+    for y, n in ((y1, n1), (y2, n2)):
+        if y is None:
+            y = torch.empty((t, n), dtype=torch.bfloat16, device=x.device)
+        if tuple(y.shape) != (t, n) or y.element_size() != 2 or not y.is_contiguous():
+            raise ValueError("outputs must be contiguous [T, N] tensors of 2-byte elements")
+        outs.append(y)
+    need = q4lin_pair_workspace_bytes(n1, n2, k, t)
+    if need < 0:
+        raise Q4LinError(-need)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = q4lin_linear_pair(x.data_ptr(), codes1.data_ptr(), scales1.data_ptr(), outs[0].data_ptr(), n1,
+                           codes2.data_ptr(), scales2.data_ptr(), outs[1].data_ptr(), n2, k, t,
+                           ws_ptr, ws_bytes, stream)
+    if st != Q4LIN_OK:
+        raise Q4LinError(st)
+    return outs[0], outs[1]

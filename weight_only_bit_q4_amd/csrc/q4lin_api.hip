@@ -102,6 +102,44 @@ int q4lin_linear(const void* x, const void* codes, const void* scales, void* y,
   return run_linear(x, codes, scales, nullptr, y, n, k, t, workspace, workspace_bytes, stream);
 }
 
+int q4lin_linear_pair(const void* x, const void* codes1, const void* scales1, void* y1, int64_t n1,
+                      const void* codes2, const void* scales2, void* y2, int64_t n2, int64_t k, int64_t t,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape_ok(n1, k, t) || !shape_ok(n2, k, t) || !shape_ok(n1 + n2, k, t)) return Q4LIN_E_SHAPE;
+  if (n1 == 0 || n2 == 0 || t == 0) {  // one plane or none: the plain op
+    return n2 == 0 ? run_linear(x, codes1, scales1, nullptr, y1, n1, k, t, workspace, workspace_bytes, stream)
+                   : run_linear(x, codes2, scales2, nullptr, y2, n2, k, t, workspace, workspace_bytes, stream);
+  }
+  const int route = pick_route(n1 + n2, k, t);
+  if (route != Q4LIN_ROUTE_DECODE && route != Q4LIN_ROUTE_SKINNY) {
+    // the many-token and wide-K routes: one launch sequence per weight
+    const int s1 = run_linear(x, codes1, scales1, nullptr, y1, n1, k, t, workspace, workspace_bytes, stream);
+    if (s1 != Q4LIN_OK) return s1;
+    return run_linear(x, codes2, scales2, nullptr, y2, n2, k, t, workspace, workspace_bytes, stream);
+  }
+  if (!x || !codes1 || !scales1 || !y1 || !codes2 || !scales2 || !y2) return Q4LIN_E_NULL;
+  if (!aligned(x, 16) || !aligned(codes1, 16) || !aligned(scales1, 2) || !aligned(y1, 2) ||
+      !aligned(codes2, 16) || !aligned(scales2, 2) || !aligned(y2, 2))
+    return Q4LIN_E_ALIGN;
+  q4lin::GemvArgs ga{x, codes1, scales1, y1, n1, k, t};
+  ga.codes2 = codes2;
+  ga.scales2 = scales2;
+  ga.y2 = y2;
+  ga.n2 = n2;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = route == Q4LIN_ROUTE_DECODE ? q4lin::launch_decode(ga, s) : q4lin::launch_skinny(ga, s);
+  return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+}
+
+int64_t q4lin_pair_workspace_bytes(int64_t n1, int64_t n2, int64_t k, int64_t t) {
+  if (!shape_ok(n1, k, t) || !shape_ok(n2, k, t) || !shape_ok(n1 + n2, k, t)) return -Q4LIN_E_SHAPE;
+  const int route = pick_route(n1 + n2, k, t);
+  if (n1 > 0 && n2 > 0 && (route == Q4LIN_ROUTE_DECODE || route == Q4LIN_ROUTE_SKINNY)) return 0;
+  const size_t w1 = route_workspace(pick_route(n1, k, t), n1, k, t);
+  const size_t w2 = route_workspace(pick_route(n2, k, t), n2, k, t);
+  return (int64_t)(w1 > w2 ? w1 : w2);
+}
+
 int q4lin_linear_add(const void* x, const void* codes, const void* scales, const void* residual, void* y,
                      int64_t n, int64_t k, int64_t t,
                      void* workspace, size_t workspace_bytes, void* stream) {
@@ -121,6 +159,6 @@ const char* q4lin_status_string(int status) {
   }
 }
 
-int q4lin_version(void) { return 200; }
+int q4lin_version(void) { return 210; }
 
 }  // extern "C"

@@ -165,12 +165,21 @@ __device__ __forceinline__ float piece_dot_pre(const uint32_t (&c)[16], const u3
 template <int PL, int MAXR, int NT>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-              uint16_t* y, int N, int K, int BN, const uint16_t* res) {
+              uint16_t* y, int N, int K, int BN, const uint16_t* res, SecondPlane p2) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int G = K >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = blockIdx.x * BN;
+  int bid = blockIdx.x;
+  if (p2.n > 0 && bid >= p2.first) {  // LinearPair: the second weight
+    codes = p2.codes;
+    scales = p2.scales;
+    y = p2.y;
+    N = p2.n;
+    res = nullptr;  // a pair carries no residual
+    bid -= p2.first;
+  }
+  const int n0 = bid * BN;
   const int rows = min(BN, N - n0);
 
   // wave slice, slots and row groups (all wave-uniform but the lane's own)
@@ -398,9 +407,11 @@ hipError_t launch_pm(const DecodePlan& p, const GemvArgs& a, hipStream_t stream)
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)p.blocks), dim3(kThreads), lds, stream>>>(
+  const int blocks1 = (int)((a.n + p.bn - 1) / p.bn), blocks2 = (int)((a.n2 + p.bn - 1) / p.bn);
+  kern<<<dim3((unsigned)(blocks1 + blocks2)), dim3(kThreads), lds, stream>>>(
       static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
-      static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, p.bn, static_cast<const uint16_t*>(a.res));
+      static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, p.bn, static_cast<const uint16_t*>(a.res),
+      second_plane(a, blocks1));
   return hipGetLastError();
 }
 
@@ -454,7 +465,7 @@ bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p) {
 
 hipError_t launch_decode(const GemvArgs& a, hipStream_t stream) {
   DecodePlan p;
-  if (!decode_plan(a.n, a.k, a.t, &p)) return hipErrorInvalidValue;
+  if (!decode_plan(a.n + a.n2, a.k, a.t, &p)) return hipErrorInvalidValue;
   if (p.pl == 1 && p.maxr == 8) {
     switch (a.t) {
       case 1: return launch_pm<1, 8, 1>(p, a, stream);

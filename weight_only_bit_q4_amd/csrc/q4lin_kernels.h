@@ -14,7 +14,26 @@ struct GemvArgs {
   void* y;
   int64_t n, k, t;
   const void* res = nullptr;  // LinearAdd residual, bf16 [T][N] like y (nullptr: plain Linear)
+  // LinearPair: a second weight (n2 rows, same K) and its output; n2 == 0: none
+  const void* codes2 = nullptr;
+  const void* scales2 = nullptr;
+  void* y2 = nullptr;
+  int64_t n2 = 0;
 };
+
+// The second plane of a LinearPair as the kernels see it: the workgroups from
+// `first` on serve it (their block index counted from there).
+struct SecondPlane {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  uint16_t* y;
+  int n;      // rows (0: no second plane)
+  int first;  // its first workgroup
+};
+inline SecondPlane second_plane(const GemvArgs& a, int first) {
+  return SecondPlane{static_cast<const uint8_t*>(a.codes2), static_cast<const uint16_t*>(a.scales2),
+                     static_cast<uint16_t*>(a.y2), (int)a.n2, first};
+}
 
 // Few-token route.  Each of the 4 waves of a workgroup owns a quarter of the
 // 32-weight chunks of every row; gemv_chunks_per_wave is that quarter's
@@ -70,6 +89,11 @@ struct TiledArgs {
   void* workspace;
   TiledConfig cfg;
   const void* res = nullptr;  // LinearAdd residual, bf16 [T][N] like y (nullptr: plain Linear)
+  // LinearPair: a second weight (n2 rows, same K) and its output; n2 == 0: none
+  const void* codes2 = nullptr;
+  const void* scales2 = nullptr;
+  void* y2 = nullptr;
+  int64_t n2 = 0;
 };
 
 int64_t tiled_tpad(int64_t t);

@@ -133,7 +133,7 @@ template <int CT, int TT, int NL, int DEPTH>
 __global__ void __launch_bounds__(kThreads, 1)
 skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
               const uint16_t* __restrict__ scales, uint16_t* y,
-              int N, int K, int T, int BN, int off_codes, int off_red, const uint16_t* res) {
+              int N, int K, int T, int BN, int off_codes, int off_red, const uint16_t* res, SecondPlane p2) {
   constexpr int BNP = 16 * CT;  // matrix-core columns (rows of W) per workgroup
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   // LDS: the block's scales (fp16 [BNP][G] from byte s_delta), then the
@@ -142,7 +142,16 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
-  const int n0 = blockIdx.x * BN;
+  int bid = blockIdx.x;
+  if (p2.n > 0 && bid >= p2.first) {  // LinearPair: the second weight
+    codes = p2.codes;
+    scales = p2.scales;
+    y = p2.y;
+    N = p2.n;
+    res = nullptr;  // a pair carries no residual
+    bid -= p2.first;
+  }
+  const int n0 = bid * BN;
   const int rows = min(BN, N - n0);  // real rows of this block (>= 1)
 
   // --- this wave's slice of K, in steps of four 64-groups -------------------
@@ -449,10 +458,11 @@ hipError_t launch_ct(const SkinnyPlan& p, const GemvArgs& a, hipStream_t stream)
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)p.blocks), dim3(kThreads), p.lds_bytes, stream>>>(
+  const int blocks1 = (int)((a.n + p.bn - 1) / p.bn), blocks2 = (int)((a.n2 + p.bn - 1) / p.bn);
+  kern<<<dim3((unsigned)(blocks1 + blocks2)), dim3(kThreads), p.lds_bytes, stream>>>(
       static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes),
       static_cast<const uint16_t*>(a.scales), static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, (int)a.t,
-      p.bn, p.off_codes, p.off_red, static_cast<const uint16_t*>(a.res));
+      p.bn, p.off_codes, p.off_red, static_cast<const uint16_t*>(a.res), second_plane(a, blocks1));
   return hipGetLastError();
 }
 
@@ -488,7 +498,7 @@ bool skinny_plan(int64_t n, int64_t k, int64_t t, SkinnyPlan* p) {
 
 hipError_t launch_skinny(const GemvArgs& a, hipStream_t stream) {
   SkinnyPlan p;
-  if (!skinny_plan(a.n, a.k, a.t, &p)) return hipErrorInvalidValue;
+  if (!skinny_plan(a.n + a.n2, a.k, a.t, &p)) return hipErrorInvalidValue;
   if (p.tt == 1) {
     switch (p.ct) {
       case 1: return launch_ct<1, 1>(p, a, stream);
