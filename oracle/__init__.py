@@ -82,6 +82,8 @@ class Oracle:
         lib.q4o_linear_at.argtypes = [u16p, u8p, u16p, i64, i64, i64, i64p, i64p, i64,
                                       u16p, f64p, ctypes.c_int]
         lib.q4o_linear_at.restype = None
+        lib.q4o_swiglu.argtypes = [f64p, f64p, u16p, i64]
+        lib.q4o_swiglu.restype = None
         lib.q4o_max_threads.argtypes = []
         lib.q4o_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -145,6 +147,23 @@ class Oracle:
                                 _ptr(y, ctypes.c_uint16), n, k, t, int(threads))
         return y.reshape(t, n)
 
+    def swiglu(self, g, u):
+        """bf16(silu(g) * u) element by element, g and u binary64 sums."""
+        g = np.ascontiguousarray(g, dtype=np.float64).reshape(-1)
+        u = np.ascontiguousarray(u, dtype=np.float64).reshape(-1)
+        if g.size != u.size:
+            raise ValueError("gate and up sizes differ")
+        y = np.zeros(g.size, dtype=np.uint16)
+        self.lib.q4o_swiglu(_ptr(g, ctypes.c_double), _ptr(u, ctypes.c_double), _ptr(y, ctypes.c_uint16), g.size)
+        return y
+
+    def linear_swiglu(self, x, codes_g, scales_g, codes_u, scales_u, n: int, k: int, t: int, threads: int = 0):
+        """Y = bf16(silu(Wg . X) * (Wu . X)), both sums in binary64 and one
+        rounding.  Returns bf16 bits ``[T, N]``."""
+        _, g = self.linear(x, codes_g, scales_g, n, k, t, threads=threads, with_acc=True)
+        _, u = self.linear(x, codes_u, scales_u, n, k, t, threads=threads, with_acc=True)
+        return self.swiglu(g, u).reshape(t, n)
+
     def linear_at(self, x, codes, scales, n: int, k: int, t: int, ns, ts,
                   threads: int = 0, with_acc: bool = False):
         """Selected elements ``Y[ns[i], ts[i]]`` (bf16 bits), each summed alone."""
@@ -204,6 +223,14 @@ def linear(*args, **kw):
 
 def linear_add(*args, **kw):
     return default().linear_add(*args, **kw)
+
+
+def swiglu(*args, **kw):
+    return default().swiglu(*args, **kw)
+
+
+def linear_swiglu(*args, **kw):
+    return default().linear_swiglu(*args, **kw)
 
 
 def linear_at(*args, **kw):

@@ -226,6 +226,23 @@ void q4o_linear_add(const uint16_t *x, const uint8_t *codes, const uint16_t *sca
     }
 }
 
+/* LinearSwiGLU, the pages' fused gate/up variant ("q4-linear.md" and
+ * "linear-benchmark.md" name LinearSwiGLU among the Linear variants without
+ * defining it; the plain reading taken here, the gated linear unit with the
+ * SiLU (swish) gate):
+ *   Y[n,t] = bf16_rne( silu(G[n,t]) * U[n,t] ),   silu(g) = g / (1 + e^-g)
+ * where G and U are the unrounded binary64 sums of the gate and up weights
+ * over the same X (q4o_linear's acc).  The gate, its product with U and the
+ * single rounding are all taken in binary64 (exp from the C library).
+ * g and u hold `count` sums each; y receives `count` bf16 values. */
+void q4o_swiglu(const double *g, const double *u, uint16_t *y, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        const double silu = g[i] / (1.0 + exp(-g[i]));
+        y[i] = q4o_double_to_bf16(silu * u[i]);
+    }
+}
+
 /* Selected output elements only: out[i] = Y[ns[i], ts[i]] (bf16 bits), and
  * acc[i] the binary64 sum (acc may be NULL).  Used where the full product
  * would take too long on the CPU. */

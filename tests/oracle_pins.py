@@ -295,18 +295,28 @@ def pin_unit_scales_matmul(o):
     assert np.array_equal(got, want)
 
 
-def _exact_linear(x, codes, scales, n, k, t):
+def _exact_sums(x, codes, scales, n, k, t):
+    """The exact rational sums W . X, [t][n] lists of Fractions."""
     q = _int_weights(codes, n, k)
     sc = [[fp16_exact(int(scales[i, g])) for g in range(k // 64)] for i in range(n)]
     xs = [[bf16_exact(int(x[j, kk])) for kk in range(k)] for j in range(t)]
-    out = np.zeros((t, n), dtype=np.uint16)
+    out = [[Fraction(0)] * n for _ in range(t)]
     for j in range(t):
         for i in range(n):
             acc = Fraction(0)
             for kk in range(k):
                 if q[i, kk]:
                     acc += int(q[i, kk]) * sc[i][kk // 64] * xs[j][kk]
-            out[j, i] = frac_to_bf16_bits(acc)
+            out[j][i] = acc
+    return out
+
+
+def _exact_linear(x, codes, scales, n, k, t):
+    sums = _exact_sums(x, codes, scales, n, k, t)
+    out = np.zeros((t, n), dtype=np.uint16)
+    for j in range(t):
+        for i in range(n):
+            out[j, i] = frac_to_bf16_bits(sums[j][i])
     return out
 
 
@@ -495,6 +505,106 @@ def pin_linear_at(o):
     assert np.array_equal(got, y[ts, ns])
 
 
+# -- LinearSwiGLU: Y = bf16(silu(G) * U), G and U the sums of two weights -----
+def pin_swiglu_zero_gate_or_up(o):
+    """silu(0) = 0: an all-eight gate gives zeros signed like U; an all-eight
+    up weight gives zeros of either sign."""
+    n, k, t = 24, 256, 3
+    x, cg, sg = _problem(n, k, t, 91)
+    _, cu, su = _problem(n, k, t, 92)
+    zero = np.full_like(cg, 0x88)
+    _, u = o.linear(x, cu, su, n, k, t, with_acc=True)
+    y = o.linear_swiglu(x, zero, sg, cu, su, n, k, t)
+    assert np.array_equal(y, np.where(u < 0, 0x8000, 0x0000).astype(np.uint16))
+    y = o.linear_swiglu(x, cg, sg, zero, su, n, k, t)
+    assert np.all((y & 0x7FFF) == 0)
+
+
+def pin_swiglu_saturated_gate(o):
+    """For G >= 64, silu(G) = G (1 - e^-G) is G to far below bf16 resolution
+    (e^-64 < 2^-92), so Y = bf16(G U) from the exact rationals, except where
+    G U is itself a bf16 tie (skipped: the e^-G term decides those); for
+    G <= -64, silu(G) < 64 e^-64 < 2^-86 and |Y| underflows to zero for the
+    |U| < 2^10 used here."""
+    n, k, t = 6, 128, 2
+    r = np.random.default_rng(93)
+    x = np.full((t, k), 0x3F80, dtype=np.uint16)              # X = 1
+    sg = np.full((n, k // 64), 0x3C00, dtype=np.uint16)        # scale 1
+    cg = np.full((n, k // 2), 0x99, dtype=np.uint8)            # G = K = 128
+    cg[n // 2:] = 0x77                                         # G = -128
+    _, cu, su = _problem(n, k, t, 94)
+    su = (r.integers(0x2C00, 0x3400, size=su.shape)).astype(np.uint16)   # |s| in [2^-4, 2^-2)
+    y = o.linear_swiglu(x, cg, sg, cu, su, n, k, t)
+    G = _exact_sums(x, cg, sg, n, k, t)
+    U = _exact_sums(x, cu, su, n, k, t)
+    checked = 0
+    for j in range(t):
+        for i in range(n):
+            assert abs(U[j][i]) < 2 ** 10
+            if G[j][i] > 0:
+                prod = G[j][i] * U[j][i]
+                lo = bf16_exact(frac_to_bf16_bits(prod))
+                if prod != lo and 2 * prod == lo + bf16_exact(frac_to_bf16_bits(2 * prod - lo)):
+                    continue  # a tie
+                assert int(y[j, i]) == frac_to_bf16_bits(prod), (i, j)
+                checked += 1
+            else:
+                assert int(y[j, i]) & 0x7FFF == 0, (i, j)
+    assert checked >= n * t // 2 - 1
+
+
+def pin_swiglu_single_rounding(o):
+    """Worked example: X = 1 at k = 0 and 64, 2^-6 at k = 128, zero elsewhere.
+    Gate: code 0 at k = 0 with scale -16, all other codes 8, so G = 128 and
+    silu(G) = 128 in binary64 (e^-128 < 2^-184).  Up: code 9 at k = 0, 64,
+    128 with scales 1, 2^-8, 2^-24 (the fp16 subnormal 0x0001), so
+    U = 1 + 2^-8 + 2^-30.  G U = 128.5 + 2^-23 lies just above the bf16
+    midpoint between 128 and 129 (spacing 1 there): one rounding gives 129
+    (0x4301); rounding U to binary32 first would leave the tie 128.5, which
+    goes to the even 128 (0x4300).  A negative up weight mirrors it."""
+    n, k, t = 2, 192, 1
+    x = np.zeros((t, k), dtype=np.uint16)
+    x[0, 0] = x[0, 64] = 0x3F80
+    x[0, 128] = 0x3C80
+    cg = np.full((n, k // 2), 0x88, dtype=np.uint8)
+    cg[:, 0] = 0x80
+    sg = np.array([[0xCC00, 0x3C00, 0x3C00]] * n, dtype=np.uint16)
+    cu = np.full((n, k // 2), 0x88, dtype=np.uint8)
+    cu[0, [0, 32, 64]] = 0x89
+    cu[1, [0, 32, 64]] = 0x87
+    su = np.array([[0x3C00, 0x1C00, 0x0001]] * n, dtype=np.uint16)
+    y = o.linear_swiglu(x, cg, sg, cu, su, n, k, t)
+    assert [int(v) for v in y.reshape(-1)] == [0x4301, 0xC301], [hex(int(v)) for v in y.reshape(-1)]
+
+
+def pin_swiglu_bruteforce(o, trials=4):
+    """Exact rational sums for G and U, the gate from the logistic function
+    through its tanh form, sigma(g) = (1 + tanh(g / 2)) / 2, a second route
+    to silu(g) = g sigma(g); the two agree to a few binary64 ulps, so the bf16
+    results agree except where the value lies within that of a rounding
+    boundary (at most one bf16 ulp apart, and rarely)."""
+    import math
+    total = off = 0
+    for trial in range(trials):
+        n, k, t = 5, 128, 2
+        x, cg, sg = _problem(n, k, t, 100 + trial)
+        _, cu, su = _problem(n, k, t, 200 + trial)
+        y = o.linear_swiglu(x, cg, sg, cu, su, n, k, t)
+        G = _exact_sums(x, cg, sg, n, k, t)
+        U = _exact_sums(x, cu, su, n, k, t)
+        for j in range(t):
+            for i in range(n):
+                g = float(G[j][i])
+                v = Fraction(g * (1.0 + math.tanh(g / 2.0)) / 2.0) * U[j][i]
+                want = frac_to_bf16_bits(v)
+                got = int(y[j, i])
+                total += 1
+                if got != want:
+                    off += 1
+                    assert abs(bf16_exact(got) - bf16_exact(want)) <= abs(bf16_exact(want)) * Fraction(1, 128)
+    assert off <= max(1, total // 50), (off, total)
+
+
 ALL_PINS = [
     pin_worked_examples, pin_fp16_decode, pin_bf16_decode, pin_rounding_nearest_even,
     pin_rounding_vs_torch, pin_weight_bytes, pin_unit_scales_integer_x, pin_unit_scales_matmul,
@@ -502,4 +612,5 @@ ALL_PINS = [
     pin_token_independence, pin_group_permutation, pin_linear_at,
     pin_add_worked_examples, pin_add_exact_bruteforce, pin_add_all_code8_passes_residual,
     pin_add_zero_residual_and_shift,
+    pin_swiglu_zero_gate_or_up, pin_swiglu_saturated_gate, pin_swiglu_single_rounding, pin_swiglu_bruteforce,
 ]

@@ -39,6 +39,12 @@ MUTANTS = [
      "s += q4o_bf16_to_double(r[(n * T + t) % (N * T)]);"),
     ("residual added after a first rounding", "s += q4o_bf16_to_double(r[t * N + n]);",
      "s = q4o_bf16_to_double(q4o_double_to_bf16(s)) + q4o_bf16_to_double(r[t * N + n]);"),
+    ("swiglu gate sign", "g[i] / (1.0 + exp(-g[i]))", "g[i] / (1.0 + exp(g[i]))"),
+    ("swiglu sigmoid without the g factor", "g[i] / (1.0 + exp(-g[i]))", "1.0 / (1.0 + exp(-g[i]))"),
+    ("swiglu gate and up swapped", "g[i] / (1.0 + exp(-g[i]));\n        y[i] = q4o_double_to_bf16(silu * u[i]);",
+     "u[i] / (1.0 + exp(-u[i]));\n        y[i] = q4o_double_to_bf16(silu * g[i]);"),
+    ("swiglu gate rounded to binary32 first", "y[i] = q4o_double_to_bf16(silu * u[i]);",
+     "y[i] = q4o_double_to_bf16((double)(float)silu * (double)(float)u[i]);"),
     ("residual subtracted", "s += q4o_bf16_to_double(r[t * N + n]);", "s -= q4o_bf16_to_double(r[t * N + n]);"),
     ("sampled path reads k-major",
      "acc += weight_value(codes, scales, K, n, k) * q4o_bf16_to_double(x[t * K + k]);",
