@@ -394,6 +394,8 @@ def main(argv=None):
                     help="with --t: time the LinearAdd entry point (Y = W x X + R; R adds 2NT bytes)")
     ap.add_argument("--pair", type=int, default=None, metavar="N2",
                     help="LinearPair: --n rows and N2 rows over one X, against two separate calls (--t)")
+    ap.add_argument("--swiglu", action="store_true",
+                    help="LinearSwiGLU (gate and up of --n rows) against two plain calls (--t)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--csv", type=str, default=None)
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="BYTES",
@@ -496,6 +498,34 @@ def main(argv=None):
                 w = csv.DictWriter(f, fieldnames=list(rows[0]))
                 w.writeheader()
                 w.writerows(rows)
+        return 0
+
+    if args.swiglu:
+        # LinearSwiGLU against the same two weights through two plain calls
+        import weight_only_bit_q4_amd as q4
+        t = args.t if args.t is not None else 1
+        p1, p2 = Point(n, k, t, seed), Point(n, k, t, seed + 1)
+        nsets = min(p1.nsets, p2.nsets)
+        wsb = q4.q4lin_swiglu_workspace_bytes(n, k, t)
+        wss = [torch.empty(wsb, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+
+        def swiglu(i, h):
+            x, cg, sg, y, _, _ = p1.sets[i % nsets]
+            _, cu, su, _, _, _ = p2.sets[i % nsets]
+            st = q4.q4lin_linear_swiglu(x.data_ptr(), cg.data_ptr(), sg.data_ptr(), cu.data_ptr(), su.data_ptr(),
+                                        y.data_ptr(), n, k, t, wss[i % nsets].data_ptr(), wsb, h)
+            if st != 0:
+                raise RuntimeError("q4lin_linear_swiglu: " + q4.q4lin_status_string(st))
+
+        def two(i, h):
+            p1.call(i % nsets, h)
+            p2.call(i % nsets, h)
+
+        steps = max(20, args.steps // (20 if t >= 512 else 1))
+        ss, s2c = _graph_period(torch, swiglu, steps), _graph_period(torch, two, steps)
+        print(json.dumps({"op": "linear_swiglu", "n": n, "k": k, "t": t, "swiglu_us": ss * 1e6,
+                          "two_plain_calls_us": s2c * 1e6, "weights_gbs": 2 * weight_bytes(n, k) / ss / 1e9,
+                          "tflops": 2 * useful_flops(n, k, t) / ss / 1e12}))
         return 0
 
     if args.pair is not None:

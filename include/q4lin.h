@@ -119,6 +119,29 @@ Q4LIN_API int q4lin_linear_pair(const void *x, const void *codes1, const void *s
  * -Q4LIN_E_SHAPE for a shape outside the contract.  Pure host function. */
 Q4LIN_API int64_t q4lin_pair_workspace_bytes(int64_t n1, int64_t n2, int64_t k, int64_t t);
 
+/* LinearSwiGLU, the gate/up variant the pages name beside LinearAdd and
+ * LinearPair ("q4-linear.md" and "linear-benchmark.md", without a
+ * definition; the plain reading taken here, the gated linear unit with the
+ * SiLU gate):
+ *
+ *     Y[N,T] = silu(Wg[N,K] x X[K,T]) * (Wu[N,K] x X[K,T]),  silu(g) = g / (1 + e^-g)
+ *
+ * elementwise, both products taken as unrounded sums (binary32 on the GPU,
+ * never bf16), the gate formed in binary64 and the result rounded once to
+ * bfloat16.  The gate weight (codes_gate, scales_gate) and the up weight
+ * (codes_up, scales_up) both have N rows and q4lin_linear's layout and
+ * alignment; y is bf16 [T][N] like q4lin_linear's.  workspace must hold
+ * q4lin_swiglu_workspace_bytes(n, k, t) bytes (never 0 for a non-empty
+ * product: the two sums pass through it), 256-byte aligned.  y must not
+ * overlap any input or the workspace.  Errors as for q4lin_linear. */
+Q4LIN_API int q4lin_linear_swiglu(const void *x, const void *codes_gate, const void *scales_gate,
+                      const void *codes_up, const void *scales_up, void *y, int64_t n, int64_t k, int64_t t,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace q4lin_linear_swiglu needs (0 for an empty product), or
+ * -Q4LIN_E_SHAPE for a shape outside the contract.  Pure host function. */
+Q4LIN_API int64_t q4lin_swiglu_workspace_bytes(int64_t n, int64_t k, int64_t t);
+
 /* Static, human-readable text for a status code (never NULL). */
 Q4LIN_API const char *q4lin_status_string(int status);
 

@@ -158,3 +158,34 @@ def test_linear_pair_shapes_and_workspace():
     assert need == max(q.q4lin_workspace_bytes(n1, k, t), q.q4lin_workspace_bytes(n2, k, t)) > 0
     assert q.q4lin_linear_pair(p, p, p, p, n1, p, p, p, n2, k, t, p, need - 1, 0) == q.Q4LIN_E_WORKSPACE
     assert q.q4lin_pair_workspace_bytes(0, 512, 1024, 300) == q.q4lin_workspace_bytes(512, 1024, 300)
+
+
+# -- LinearSwiGLU: silu(gate sums) * (up sums) ---------------------------------
+def test_linear_swiglu_checks():
+    p = 0x10000
+    assert q.q4lin_linear_swiglu(0, 0, 0, 0, 0, 0, 0, 128, 5, 0, 0, 0) == q.Q4LIN_OK
+    assert q.q4lin_linear_swiglu(0, 0, 0, 0, 0, 0, 6, 128, 0, 0, 0, 0) == q.Q4LIN_OK
+    assert q.q4lin_swiglu_workspace_bytes(0, 128, 5) == 0
+    assert q.q4lin_linear_swiglu(p, p, p, p, p, p, 8, 96, 1, 0, 0, 0) == q.Q4LIN_E_SHAPE
+    assert q.q4lin_swiglu_workspace_bytes(8, 96, 1) == -q.Q4LIN_E_SHAPE
+    for n, k, t in [(6144, 5120, 1), (1000, 2048, 20), (768, 1024, 100), (128, 20480, 3)]:
+        need = q.q4lin_swiglu_workspace_bytes(n, k, t)
+        assert need >= 2 * n * t * 4 and need % 256 == 0
+        assert q.q4lin_linear_swiglu(p, p, p, p, p, p, n, k, t, p, need - 1, 0) == q.Q4LIN_E_WORKSPACE
+        assert q.q4lin_linear_swiglu(p, p, p, p, p, p, n, k, t, 0, need, 0) == q.Q4LIN_E_NULL
+        assert q.q4lin_linear_swiglu(p, p, p, p, p, p, n, k, t, p + 16, need, 0) == q.Q4LIN_E_ALIGN
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_linear_swiglu_null_pointer_rejected(which):
+    ptrs = [0x1000] * 6
+    ptrs[which] = 0
+    assert q.q4lin_linear_swiglu(*ptrs, 64, 128, 1, 0x1000, 1 << 20, 0) == q.Q4LIN_E_NULL
+
+
+@pytest.mark.parametrize("which,addr", [(0, 0x1008), (1, 0x1004), (2, 0x1001), (3, 0x1004), (4, 0x1001),
+                                        (5, 0x1001)])
+def test_linear_swiglu_misaligned_pointer_rejected(which, addr):
+    ptrs = [0x1000] * 6
+    ptrs[which] = addr
+    assert q.q4lin_linear_swiglu(*ptrs, 64, 128, 1, 0x1000, 1 << 20, 0) == q.Q4LIN_E_ALIGN

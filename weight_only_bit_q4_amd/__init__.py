@@ -34,7 +34,8 @@ Q4LIN_ROUTE_TILED = 3
 Q4LIN_ROUTE_DECODE = 4
 
 EXPORTED = ("q4lin_workspace_bytes", "q4lin_linear", "q4lin_linear_add", "q4lin_linear_pair",
-            "q4lin_pair_workspace_bytes", "q4lin_status_string", "q4lin_route", "q4lin_version")
+            "q4lin_pair_workspace_bytes", "q4lin_linear_swiglu", "q4lin_swiglu_workspace_bytes",
+            "q4lin_status_string", "q4lin_route", "q4lin_version")
 
 
 class Q4LinError(RuntimeError):
@@ -68,6 +69,10 @@ def _load() -> ctypes.CDLL:
     lib.q4lin_linear_pair.restype = ctypes.c_int
     lib.q4lin_pair_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.q4lin_pair_workspace_bytes.restype = i64
+    lib.q4lin_linear_swiglu.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.q4lin_linear_swiglu.restype = ctypes.c_int
+    lib.q4lin_swiglu_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.q4lin_swiglu_workspace_bytes.restype = i64
     lib.q4lin_status_string.argtypes = [ctypes.c_int]
     lib.q4lin_status_string.restype = ctypes.c_char_p
     lib.q4lin_route.argtypes = [i64, i64, i64]
@@ -119,6 +124,18 @@ def q4lin_linear_pair(x: int, codes1: int, scales1: int, y1: int, n1: int, codes
 
 def q4lin_pair_workspace_bytes(n1: int, n2: int, k: int, t: int) -> int:
     return int(load().q4lin_pair_workspace_bytes(int(n1), int(n2), int(k), int(t)))
+
+
+def q4lin_linear_swiglu(x: int, codes_gate: int, scales_gate: int, codes_up: int, scales_up: int, y: int,
+                        n: int, k: int, t: int, workspace: int, workspace_bytes: int, stream: int) -> int:
+    """Raw call of the LinearSwiGLU entry point (Y = silu(Wg x X) * (Wu x X)); returns the status."""
+    return int(load().q4lin_linear_swiglu(x or None, codes_gate or None, scales_gate or None, codes_up or None,
+                                          scales_up or None, y or None, int(n), int(k), int(t),
+                                          workspace or None, int(workspace_bytes), stream or None))
+
+
+def q4lin_swiglu_workspace_bytes(n: int, k: int, t: int) -> int:
+    return int(load().q4lin_swiglu_workspace_bytes(int(n), int(k), int(t)))
 
 
 def q4lin_status_string(status: int) -> str:
@@ -218,3 +235,38 @@ def linear_pair(x, codes1, scales1, codes2, scales2, y1=None, y2=None, workspace
     if st != Q4LIN_OK:
         raise Q4LinError(st)
     return outs[0], outs[1]
+
+
+def linear_swiglu(x, codes_gate, scales_gate, codes_up, scales_up, y=None, workspace=None, stream=None):
+    """LinearSwiGLU on torch device tensors: ``silu(Wg x X) * (Wu x X)``, both
+    weights with ``linear``'s layouts and the same shape.  Returns ``y``."""
+    import torch
+
+    t, k = x.shape
+    n = codes_gate.shape[0]
+    for name, c, sc in (("gate", codes_gate, scales_gate), ("up", codes_up, scales_up)):
+        if tuple(c.shape) != (n, k // 2) or tuple(sc.shape) != (n, k // 64):
+            raise ValueError("shape mismatch: x %s %s codes %s scales %s" % (tuple(x.shape), name, tuple(c.shape),
+                                                                          tuple(sc.shape)))
+    for name, ten, size in (("x", x, 2), ("codes_gate", codes_gate, 1), ("scales_gate", scales_gate, 2),
+                            ("codes_up", codes_up, 1), ("scales_up", scales_up, 2)):
+        if not ten.is_contiguous() or ten.element_size() != size:
+            raise ValueError("%s must be contiguous with %d-byte elements" % (name, size))
+    if y is None:
+        y = torch.empty((t, n), dtype=torch.bfloat16, device=x.device)
+    if tuple(y.shape) != (t, n) or y.element_size() != 2 or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [T, N] tensor of 2-byte elements")
+    need = q4lin_swiglu_workspace_bytes(n, k, t)
+    if need < 0:
+        raise Q4LinError(-need)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = q4lin_linear_swiglu(x.data_ptr(), codes_gate.data_ptr(), scales_gate.data_ptr(), codes_up.data_ptr(),
+                             scales_up.data_ptr(), y.data_ptr(), n, k, t, ws_ptr, ws_bytes, stream)
+    if st != Q4LIN_OK:
+        raise Q4LinError(st)
+    return y

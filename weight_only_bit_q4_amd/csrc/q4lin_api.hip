@@ -82,9 +82,103 @@ int run_linear(const void* x, const void* codes, const void* scales, const void*
   return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
 }
 
+size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// LinearSwiGLU's plan: how the gate and up sums are made, and the workspace.
+//   FUSED: both weights in one launch of the one-to-four-token or small-T
+//          route (chosen for 2N rows), binary32 sums into the workspace;
+//   SPLIT: one launch per weight on the route chosen for N rows;
+//   TILED: the many-token route per weight, its raw sums left in the
+//          partials of a workspace half each.
+enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3 };
+struct SwigluPlan {
+  int mode;
+  int route;
+  size_t half;  // bytes of each weight's half of the workspace
+};
+
+bool swiglu_plan(int64_t n, int64_t k, int64_t t, SwigluPlan* p) {
+  if (!shape_ok(n, k, t) || !shape_ok(2 * n, k, t) || !shape_ok(n, k, 2 * t)) return false;
+  const int r2 = pick_route(2 * n, k, t);
+  if (r2 == Q4LIN_ROUTE_DECODE || r2 == Q4LIN_ROUTE_SKINNY) {
+    *p = SwigluPlan{SW_FUSED, r2, al256((size_t)(n * t * 4))};
+    return true;
+  }
+  const int r1 = pick_route(n, k, t);
+  if (r1 == Q4LIN_ROUTE_TILED) {
+    *p = SwigluPlan{SW_TILED, r1, al256(q4lin::tiled_workspace_bytes_f32(n, k, t))};
+  } else {
+    *p = SwigluPlan{SW_SPLIT, r1, al256((size_t)(n * t * 4))};
+  }
+  return true;
+}
+
+hipError_t launch_sums(int route, const q4lin::GemvArgs& a, hipStream_t s) {
+  if (route == Q4LIN_ROUTE_DECODE) return q4lin::launch_decode(a, s);
+  if (route == Q4LIN_ROUTE_SKINNY) return q4lin::launch_skinny(a, s);
+  return q4lin::launch_gemv(a, s);
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t q4lin_swiglu_workspace_bytes(int64_t n, int64_t k, int64_t t) {
+  SwigluPlan p;
+  if (!swiglu_plan(n, k, t, &p)) return -Q4LIN_E_SHAPE;
+  if (n == 0 || t == 0) return 0;
+  return (int64_t)(2 * p.half);
+}
+
+int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scales_gate, const void* codes_up,
+                        const void* scales_up, void* y, int64_t n, int64_t k, int64_t t,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  SwigluPlan p;
+  if (!swiglu_plan(n, k, t, &p)) return Q4LIN_E_SHAPE;
+  if (n == 0 || t == 0) return Q4LIN_OK;
+  if (!x || !codes_gate || !scales_gate || !codes_up || !scales_up || !y) return Q4LIN_E_NULL;
+  if (!aligned(x, 16) || !aligned(codes_gate, 16) || !aligned(scales_gate, 2) || !aligned(codes_up, 16) ||
+      !aligned(scales_up, 2) || !aligned(y, 2))
+    return Q4LIN_E_ALIGN;
+  if (workspace_bytes < 2 * p.half) return Q4LIN_E_WORKSPACE;
+  if (!workspace) return Q4LIN_E_NULL;
+  if (!aligned(workspace, 256)) return Q4LIN_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* w0 = static_cast<uint8_t*>(workspace);
+  uint8_t* w1 = w0 + p.half;
+  q4lin::SumSource sg{reinterpret_cast<const float*>(w0), nullptr, nullptr, 1, 0};
+  q4lin::SumSource su{reinterpret_cast<const float*>(w1), nullptr, nullptr, 1, 0};
+  hipError_t e = hipSuccess;
+  if (p.mode == SW_FUSED) {
+    q4lin::GemvArgs a{x, codes_gate, scales_gate, w0, n, k, t};
+    a.codes2 = codes_up;
+    a.scales2 = scales_up;
+    a.y2 = w1;
+    a.n2 = n;
+    a.f32 = true;
+    e = launch_sums(p.route, a, s);
+  } else if (p.mode == SW_SPLIT) {
+    q4lin::GemvArgs a{x, codes_gate, scales_gate, w0, n, k, t};
+    a.f32 = true;
+    e = launch_sums(p.route, a, s);
+    if (e == hipSuccess) {
+      q4lin::GemvArgs b{x, codes_up, scales_up, w1, n, k, t};
+      b.f32 = true;
+      e = launch_sums(p.route, b, s);
+    }
+  } else {
+    const q4lin::TiledConfig cfg = q4lin::tiled_pick_config(n, k, t);
+    q4lin::TiledArgs a{x, codes_gate, scales_gate, y, n, k, t, w0, cfg};
+    e = q4lin::launch_tiled_f32(a, &sg, s);
+    if (e == hipSuccess) {
+      q4lin::TiledArgs b{x, codes_up, scales_up, y, n, k, t, w1, cfg};
+      e = q4lin::launch_tiled_f32(b, &su, s);
+    }
+  }
+  if (e == hipSuccess) e = q4lin::launch_swiglu_combine(sg, su, y, n, t, s);
+  return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+}
+
 
 int64_t q4lin_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   if (!shape_ok(n, k, t)) return -Q4LIN_E_SHAPE;
@@ -159,6 +253,6 @@ const char* q4lin_status_string(int status) {
   }
 }
 
-int q4lin_version(void) { return 210; }
+int q4lin_version(void) { return 220; }
 
 }  // extern "C"

@@ -391,7 +391,8 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     v += __shfl_xor(v, 4);
     if (wv == 0) {
       if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + n0 + r]);  // LinearAdd
-      y[(size_t)t * N + n0 + r] = f32_to_bf16_rne((float)v);
+      if (p2.f32) reinterpret_cast<float*>(y)[(size_t)t * N + n0 + r] = (float)v;  // LinearSwiGLU sums
+      else y[(size_t)t * N + n0 + r] = f32_to_bf16_rne((float)v);
     }
   }
 }

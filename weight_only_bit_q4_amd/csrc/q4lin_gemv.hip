@@ -99,7 +99,7 @@ template <int T, bool ONE>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(const u32x4_t* __restrict__ x, const uint8_t* __restrict__ codes,
             const uint16_t* __restrict__ scales, uint16_t* y,
-            int N, int K, int cq, const uint16_t* res) {
+            int N, int K, int cq, const uint16_t* res, int f32) {
   // Dynamic LDS per wave: activations [T][4 planes][cq] (16 B each), then the
   // all-8 sums [T][cq] (4 B each).  cq = ceil(C / 4) chunk slots per wave.
   extern __shared__ u32x4_t lds[];
@@ -271,7 +271,8 @@ gemv_kernel(const u32x4_t* __restrict__ x, const uint8_t* __restrict__ codes,
 #pragma unroll
       for (int q = 0; q < kWaves; ++q) v += __builtin_ldexp((double)lds_part[q][r][t], lds_e[q][t] + 24);
       if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + row]);  // LinearAdd
-      y[(size_t)t * N + row] = f32_to_bf16_rne((float)v);
+      if (f32) reinterpret_cast<float*>(y)[(size_t)t * N + row] = (float)v;  // LinearSwiGLU sums
+      else y[(size_t)t * N + row] = f32_to_bf16_rne((float)v);
     }
   }
 }
@@ -289,7 +290,8 @@ hipError_t launch_t(const GemvArgs& a, hipStream_t stream) {
   uint16_t* y = static_cast<uint16_t*>(a.y);
   int n = (int)a.n, k = (int)a.k;
   const uint16_t* res = static_cast<const uint16_t*>(a.res);
-  void* args[] = {&x, &codes, &scales, &y, &n, &k, (void*)&cq, &res};
+  int f32 = a.f32 ? 1 : 0;
+  void* args[] = {&x, &codes, &scales, &y, &n, &k, (void*)&cq, &res, &f32};
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, dim3(kThreads), args, lds, stream);
 }
 

@@ -19,6 +19,7 @@ struct GemvArgs {
   const void* scales2 = nullptr;
   void* y2 = nullptr;
   int64_t n2 = 0;
+  bool f32 = false;  // outputs as binary32 [T][N] (LinearSwiGLU's gate and up sums), not bf16
 };
 
 // The second plane of a LinearPair as the kernels see it: the workgroups from
@@ -29,10 +30,11 @@ struct SecondPlane {
   uint16_t* y;
   int n;      // rows (0: no second plane)
   int first;  // its first workgroup
+  int f32;    // every output stored as binary32 [T][N] instead of bf16
 };
 inline SecondPlane second_plane(const GemvArgs& a, int first) {
   return SecondPlane{static_cast<const uint8_t*>(a.codes2), static_cast<const uint16_t*>(a.scales2),
-                     static_cast<uint16_t*>(a.y2), (int)a.n2, first};
+                     static_cast<uint16_t*>(a.y2), (int)a.n2, first, a.f32 ? 1 : 0};
 }
 
 // Few-token route.  Each of the 4 waves of a workgroup owns a quarter of the
@@ -89,16 +91,31 @@ struct TiledArgs {
   void* workspace;
   TiledConfig cfg;
   const void* res = nullptr;  // LinearAdd residual, bf16 [T][N] like y (nullptr: plain Linear)
-  // LinearPair: a second weight (n2 rows, same K) and its output; n2 == 0: none
-  const void* codes2 = nullptr;
-  const void* scales2 = nullptr;
-  void* y2 = nullptr;
-  int64_t n2 = 0;
+  bool f32 = false;  // the raw FP32 sums go to the partials for a later pass (LinearSwiGLU)
+};
+
+// A binary32 source of sums for the LinearSwiGLU combine: element (t, n) is
+// 2^(texp[t] - rexp[n]) * (sum over ks slices of part[s * stride + t*N + n]),
+// the exponents omitted when texp is null.
+struct SumSource {
+  const float* part;
+  const int* texp;
+  const int* rexp;
+  int ks;
+  size_t stride;
 };
 
 int64_t tiled_tpad(int64_t t);
 size_t tiled_workspace_bytes(int64_t n, int64_t k, int64_t t);
 TiledConfig tiled_pick_config(int64_t n, int64_t k, int64_t t);
 hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream);
+// LinearSwiGLU's many-token leg: the tiled kernel with its raw FP32 sums left
+// in the workspace's partials (no bf16 pass); *src then describes them.  The
+// workspace must hold tiled_workspace_bytes_f32(n, k, t).
+size_t tiled_workspace_bytes_f32(int64_t n, int64_t k, int64_t t);
+hipError_t launch_tiled_f32(const TiledArgs& a, SumSource* src, hipStream_t stream);
+// y[t][n] = bf16(silu(G) * U), G and U from the two sources ([T][N] each).
+hipError_t launch_swiglu_combine(const SumSource& g, const SumSource& u, void* y, int64_t n, int64_t t,
+                                 hipStream_t stream);
 
 }  // namespace q4lin

@@ -448,7 +448,8 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) v += red[(w * T + t) * BN + col];
     if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + n0 + col]);  // LinearAdd
-    y[(size_t)t * N + n0 + col] = f32_to_bf16_rne((float)v);
+    if (p2.f32) reinterpret_cast<float*>(y)[(size_t)t * N + n0 + col] = (float)v;  // LinearSwiGLU sums
+    else y[(size_t)t * N + n0 + col] = f32_to_bf16_rne((float)v);
   }
 }
 

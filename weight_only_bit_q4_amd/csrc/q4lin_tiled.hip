@@ -870,10 +870,10 @@ hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, c
   if (ks < 1 || ks > kMaxSplits) return hipErrorInvalidValue;
   kern<<<dim3((unsigned)(tiles_n * tiles_t * ks)), dim3(Sh::NT), Sh::LDS_B, stream>>>(
       x16, texp, rexp, static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
-      static_cast<uint16_t*>(a.y), ks > 1 ? part : nullptr, (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t, ks,
+      static_cast<uint16_t*>(a.y), (ks > 1 || a.f32) ? part : nullptr, (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t, ks,
       static_cast<const uint16_t*>(a.res));
   e = hipGetLastError();
-  if (e != hipSuccess || ks == 1) return e;
+  if (e != hipSuccess || ks == 1 || a.f32) return e;
   tiled_reduce_kernel<<<dim3((unsigned)((a.n + 255) / 256), (unsigned)a.t), dim3(256), 0, stream>>>(
       part, texp, rexp, static_cast<uint16_t*>(a.y), (int)a.n, tpad, ks, static_cast<const uint16_t*>(a.res));
   return hipGetLastError();
@@ -919,6 +919,26 @@ size_t tiled_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   const TiledConfig c = tiled_pick_config(n, k, t);
   const size_t part = c.ks > 1 ? align256((size_t)c.ks * (size_t)tp * (size_t)n * 4) : 0;
   return align256((size_t)(tp * k * 2)) + align256((size_t)(tp * 4)) + align256((size_t)(n * 4)) + part;
+}
+
+size_t tiled_workspace_bytes_f32(int64_t n, int64_t k, int64_t t) {
+  const int64_t tp = tiled_tpad(t);
+  const TiledConfig c = tiled_pick_config(n, k, t);
+  return align256((size_t)(tp * k * 2)) + align256((size_t)(tp * 4)) + align256((size_t)(n * 4)) +
+         align256((size_t)c.ks * (size_t)tp * (size_t)n * 4);
+}
+
+hipError_t launch_tiled_f32(const TiledArgs& a, SumSource* src, hipStream_t stream) {
+  TiledArgs b = a;
+  b.f32 = true;
+  b.res = nullptr;
+  const int64_t tp = tiled_tpad(a.t);
+  uint8_t* w = static_cast<uint8_t*>(a.workspace);
+  const int* texp = reinterpret_cast<const int*>(w + align256((size_t)(tp * a.k * 2)));
+  const int* rexp = reinterpret_cast<const int*>(reinterpret_cast<const uint8_t*>(texp) + align256((size_t)(tp * 4)));
+  const float* part = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(rexp) + align256((size_t)(a.n * 4)));
+  *src = SumSource{part, texp, rexp, a.cfg.ks, (size_t)tp * (size_t)a.n};
+  return launch_tiled(b, stream);
 }
 
 hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
