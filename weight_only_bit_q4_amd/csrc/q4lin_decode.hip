@@ -467,6 +467,17 @@ bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p) {
 hipError_t launch_decode(const GemvArgs& a, hipStream_t stream) {
   DecodePlan p;
   if (!decode_plan(a.n + a.n2, a.k, a.t, &p)) return hipErrorInvalidValue;
+  // Two weights: each ends in its own partial workgroup, which can push the
+  // grid one past a round of the CUs (6144 + 1024 rows: 220 + 37 of 28 rows
+  // against 256).  Plan for a few more rows (bn grows by one) until the two
+  // grids together fit what the plan sized for one.
+  for (int64_t extra = p.bn, i = 0; a.n2 > 0 && i < 4; extra += p.bn, ++i) {
+    const int64_t b = (a.n + p.bn - 1) / p.bn + (a.n2 + p.bn - 1) / p.bn;
+    DecodePlan q;
+    if (b <= p.blocks || !decode_plan(a.n + a.n2 + extra, a.k, a.t, &q)) break;
+    if (q.pl != p.pl || q.maxr != p.maxr) break;  // keep the kernel shape
+    p = q;
+  }
   if (p.pl == 1 && p.maxr == 8) {
     switch (a.t) {
       case 1: return launch_pm<1, 8, 1>(p, a, stream);
