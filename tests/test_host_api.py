@@ -42,6 +42,20 @@ def test_shape_rejected(n, k, t):
     assert st == q.Q4LIN_E_SHAPE
 
 
+@pytest.mark.parametrize("n,k,t", [
+    (64, 1 << 20, 1024),        # float16 activation copy 2 GiB: past the tiled kernels' 32-bit offsets
+    (1 << 24, 4096, 64),        # scale plane n * k / 32 = 2 GiB
+])
+def test_tiled_route_rejects_shapes_past_32bit_offsets(n, k, t):
+    # the shapes pass the general limits and would take the many-token route
+    assert q.q4lin_route(n, k, t) == q.Q4LIN_ROUTE_TILED
+    assert q.q4lin_workspace_bytes(n, k, t) == -q.Q4LIN_E_SHAPE
+    st = q.q4lin_linear(0x1000, 0x1000, 0x1000, 0x1000, n, k, t, 0x1000, 1 << 40, 0)
+    assert st == q.Q4LIN_E_SHAPE
+    # just inside both bounds the query answers with a size
+    assert q.q4lin_workspace_bytes(64, 1 << 19, 1024) > 0
+
+
 def test_empty_product_is_a_no_op():
     for n, t in [(0, 5), (6, 0), (0, 0)]:
         assert q.q4lin_route(n, 128, t) == q.Q4LIN_ROUTE_NONE

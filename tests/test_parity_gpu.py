@@ -74,7 +74,7 @@ def test_sweep_6144x5120_t1_to_128():
     c = inputs.gen_codes(n, k, seed)
     s = inputs.gen_scales(n, k, seed)
     xall = inputs.gen_x(k, tmax, seed)
-    full_ts = {1, 2, 3, 4, 5, 16, 33}
+    full_ts = {1, 2, 3, 4, 5, 8, 16, 17, 24, 32, 33, 48, 64, 65, 96, 128}
     for t in range(1, tmax + 1):
         x = xall[:t]
         got = run_op(x, c, s, n, k, t, what="sweep")
@@ -101,6 +101,34 @@ def test_prefill_6144x5120(t):
     # values up to the route's rounding
     got8 = run_op(x[:8], c, s, n, k, 8, what="prefill prefix")
     assert_close(got8, oracle_full(x[:8], c, s, n, k, 8), what="prefill prefix T=8")
+
+
+@pytest.mark.parametrize("n,k,t", [
+    (6144, 256, 1024),   # 64 x 4 tiles of 96 x 256, each XCD a 16 x 2 block of them
+    (6100, 320, 1000),   # ragged rows and tokens, an odd number of groups (5)
+    (6000, 256, 777),    # 63 x 4 tiles: the plain round-robin tile order
+])
+def test_tiled_96x256_full_tensor(n, k, t):
+    """Every output of shapes that select the 96-row x 256-token tiles (the
+    T = 1024 configuration), against the oracle."""
+    import weight_only_bit_q4_amd as q4
+    x, c, s = inputs.gen_problem(n, k, t, 7000 + n + k + t)
+    assert q4.q4lin_route(n, k, t) == q4.Q4LIN_ROUTE_TILED
+    got = run_op(x, c, s, n, k, t, what="96x256 full")
+    assert_close(got, oracle_full(x, c, s, n, k, t), what="96x256 %dx%d T=%d" % (n, k, t))
+
+
+def test_prefill_6144x5120_t1024_full_tensor():
+    """All 6,291,456 outputs of the prefill workload at T = 1024 against the
+    oracle (about 25 s of oracle time on 16 host cores)."""
+    n, k, t = 6144, 5120, 1024
+    seed = inputs.workload_seed("prefill_6144x5120_t1024")
+    c = inputs.gen_codes(n, k, seed)
+    s = inputs.gen_scales(n, k, seed)
+    x = inputs.gen_x(k, t, seed)
+    got = run_op(x, c, s, n, k, t, what="prefill full")
+    announce("oracle 6144x5120 T=1024 (full)")
+    assert_close(got, oracle_full(x, c, s, n, k, t), what="prefill T=1024 full")
 
 
 @pytest.mark.parametrize("shape", [(14336, 5120), (34816, 5120), (5120, 17408)], ids=lambda s: "%dx%d" % s)
@@ -208,21 +236,25 @@ def test_wide_range_scales_and_activations(t):
     assert_close(got, oracle_full(x, c, s, n, k, t), what="wide range T=%d" % t)
 
 
-def test_extreme_magnitudes_finite_and_infinite():
+@pytest.mark.parametrize("n,k,ts", [(32, 128, (1, 3, 17, 40)), (200, 1280, (40,))],
+                         ids=["one_split", "k_split"])
+def test_extreme_magnitudes_finite_and_infinite(n, k, ts):
     """Largest finite activations and scales: results overflow to +-Inf
-    exactly where the exact sum does; nothing becomes NaN.  T = 3 and 17 take
-    the small-T route's rescaled recomputation.
+    exactly where the exact sum does; nothing becomes NaN; every other output
+    meets the tolerance.  T = 3 and 17 take the small-T route's rescaled
+    recomputation.
 
-    On the odd rows every term is near 1e44 and a few outputs are exact
-    cancellations (exact value 0).  The one- and few-token routes form exact
-    group sums and return 0 there.  The many-token route (T = 40) feeds the
-    matrix cores 16-bit weights, (q - 8) * scale rounded once to float16, as
-    the pages' large-T path does with its 16-bit MMA inputs; a relative
-    rounding of 2^-12 on terms near 1e44 cannot cancel to 0, so on that route
-    those outputs are only required to be free of NaN."""
+    On the odd rows every term is near 1e44 (all activations have the same
+    magnitude), so an output is either an exact cancellation (value 0) or
+    overflows; a few are cancellations.  The one- and few-token routes form
+    exact group sums and return 0 there.  The many-token route (T = 40) feeds
+    the matrix cores float16 weights, whose roundings do not cancel, so those
+    outputs first come out as +-Inf; the route forms every non-finite output
+    again exactly, so they too must match.  The second shape splits K over
+    two workgroups per tile (about ten cancellations among its 4000 odd-row
+    outputs), so the same repair runs in the split-sum pass."""
     import weight_only_bit_q4_amd as q4
-    n, k = 32, 128
-    for t in (1, 3, 17, 40):
+    for t in ts:
         r = np.random.default_rng(9)
         c = r.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
         s = np.full((n, k // 64), 0x7BFF, dtype=np.uint16)   # 65504
@@ -232,12 +264,9 @@ def test_extreme_magnitudes_finite_and_infinite():
         got = run_op(x, c, s, n, k, t, what="extreme")
         want = oracle_full(x, c, s, n, k, t)
         assert not np.any(((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)), "NaN produced"
-        keep = np.ones(want.shape, dtype=bool)
-        if q4.q4lin_route(n, k, t) == q4.Q4LIN_ROUTE_TILED:
-            keep = (want & 0x7FFF) != 0          # drop the exact cancellations
-            keep[:, 0::2] = True                 # even rows: small terms, all kept
-            assert (~keep).sum() <= 8
-        assert_close(got[keep], want[keep], what="extreme T=%d" % t)
+        if k == 1280:
+            assert q4.q4lin_route(n, k, t) == q4.Q4LIN_ROUTE_TILED
+        assert_close(got, want, what="extreme %dx%d T=%d" % (n, k, t))
 
 
 # ---------------------------------------------------------------------------

@@ -9,8 +9,30 @@
 // there is no policy argument.
 #include <stdint.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "../../include/q4lin.h"
 #include "q4lin_kernels.h"
+
+namespace q4lin {
+
+hipError_t allow_full_lds(const void* kern) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> done;  // (kernel, device) pairs already raised
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& d : done)
+    if (d.first == kern && d.second == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.emplace_back(kern, dev);
+  return e;
+}
+
+}  // namespace q4lin
 
 namespace {
 
@@ -57,6 +79,7 @@ int run_linear(const void* x, const void* codes, const void* scales, const void*
   if (!shape_ok(n, k, t)) return Q4LIN_E_SHAPE;
   const int route = pick_route(n, k, t);
   if (route == Q4LIN_ROUTE_NONE) return Q4LIN_OK;
+  if (route == Q4LIN_ROUTE_TILED && !q4lin::tiled_shape_ok(n, k, t)) return Q4LIN_E_SHAPE;
   if (!x || !codes || !scales || !y) return Q4LIN_E_NULL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(y, 2) || !aligned(res, 2))
     return Q4LIN_E_ALIGN;
@@ -105,6 +128,7 @@ bool swiglu_plan(int64_t n, int64_t k, int64_t t, SwigluPlan* p) {
     return true;
   }
   const int r1 = pick_route(n, k, t);
+  if (r1 == Q4LIN_ROUTE_TILED && !q4lin::tiled_shape_ok(n, k, t)) return false;
   if (r1 == Q4LIN_ROUTE_TILED) {
     *p = SwigluPlan{SW_TILED, r1, al256(q4lin::tiled_workspace_bytes_f32(n, k, t))};
   } else {
@@ -182,7 +206,9 @@ int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scale
 
 int64_t q4lin_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   if (!shape_ok(n, k, t)) return -Q4LIN_E_SHAPE;
-  return (int64_t)route_workspace(pick_route(n, k, t), n, k, t);
+  const int route = pick_route(n, k, t);
+  if (route == Q4LIN_ROUTE_TILED && !q4lin::tiled_shape_ok(n, k, t)) return -Q4LIN_E_SHAPE;
+  return (int64_t)route_workspace(route, n, k, t);
 }
 
 int q4lin_route(int64_t n, int64_t k, int64_t t) {

@@ -405,8 +405,7 @@ template <int PL, int MAXR, int NT>
 hipError_t launch_pm(const DecodePlan& p, const GemvArgs& a, hipStream_t stream) {
   auto kern = decode_kernel<PL, MAXR, NT>;
   const size_t lds = decode_lds(MAXR, NT);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
   const int blocks1 = (int)((a.n + p.bn - 1) / p.bn), blocks2 = (int)((a.n2 + p.bn - 1) / p.bn);
   kern<<<dim3((unsigned)(blocks1 + blocks2)), dim3(kThreads), lds, stream>>>(

@@ -7,6 +7,11 @@
 
 namespace q4lin {
 
+// Lets `kern` take up to the whole 160 KiB of a gfx950 CU's LDS as dynamic
+// LDS.  Only the first call per (kernel, device) reaches the runtime; later
+// calls return the recorded result (thread-safe).
+hipError_t allow_full_lds(const void* kern);
+
 struct GemvArgs {
   const void* x;
   const void* codes;
@@ -106,6 +111,10 @@ struct SumSource {
 };
 
 int64_t tiled_tpad(int64_t t);
+// Whether the tiled kernels can address (n, k, t): their buffer offsets are
+// 32-bit, so the float16 activation copy (tpad * k * 2 bytes) and the scale
+// plane (n * k / 32 bytes) must each stay below 2 GiB.
+bool tiled_shape_ok(int64_t n, int64_t k, int64_t t);
 size_t tiled_workspace_bytes(int64_t n, int64_t k, int64_t t);
 TiledConfig tiled_pick_config(int64_t n, int64_t k, int64_t t);
 hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream);

@@ -456,8 +456,7 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 template <int CT, int TT>
 hipError_t launch_ct(const SkinnyPlan& p, const GemvArgs& a, hipStream_t stream) {
   auto kern = skinny_kernel<CT, TT, 2 * CT, ring_depth(CT)>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
   const int blocks1 = (int)((a.n + p.bn - 1) / p.bn), blocks2 = (int)((a.n2 + p.bn - 1) / p.bn);
   kern<<<dim3((unsigned)(blocks1 + blocks2)), dim3(kThreads), p.lds_bytes, stream>>>(

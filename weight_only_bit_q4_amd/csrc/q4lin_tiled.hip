@@ -217,6 +217,53 @@ prep_act_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __re
 }
 
 // ---------------------------------------------------------------------------
+// exact recomputation of one output
+// ---------------------------------------------------------------------------
+// The matrix cores see each weight rounded once to float16.  Where that
+// rounding matters beyond the stated accuracy, the result comes out of range:
+// terms near the top of the binary32 range that cancel exactly (their float16
+// roundings do not), or a running FP32 sum that overflows although the exact
+// sum does not.  Every output that rounds to a non-finite bf16 value is
+// therefore formed again from the inputs, one thread per output: per 64-group
+// the exact sum of (q - 8) x in binary64 (each product exact), times the
+// group's scale, summed over the groups in binary64 (with the residual of
+// LinearAdd), then rounded to bf16 -- the plain definition of the op.  An
+// output whose exact value overflows bf16 comes out as the same infinity
+// again.  Finite outputs never take this path, so it costs one bit test per
+// 16-byte store.
+__device__ __attribute__((noinline)) uint16_t exact_output(const uint16_t* __restrict__ x,
+                                                           const uint8_t* __restrict__ codes,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint16_t* res, int N, int K, int n, int t) {
+  const int G = K >> 6;
+  const uint8_t* cr = codes + (size_t)n * (size_t)(K >> 1);
+  const uint16_t* xr = x + (size_t)t * (size_t)K;
+  double acc = 0.0;
+  for (int g = 0; g < G; ++g) {
+    double p = 0.0;
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t b = cr[32 * g + j];
+      p += (double)((int)(b & 15u) - 8) * (double)bf16_bits_to_f32(xr[64 * g + 2 * j]);
+      p += (double)((int)(b >> 4) - 8) * (double)bf16_bits_to_f32(xr[64 * g + 2 * j + 1]);
+    }
+    acc += (double)f16_bits_to_f32(scales[(size_t)n * (size_t)G + g]) * p;
+  }
+  if (res != nullptr) acc += (double)bf16_bits_to_f32(res[(size_t)t * (size_t)N + n]);
+  return f32_to_bf16_rne((float)acc);
+}
+
+// bit i of the result: bf16 value i of the 8 in v is Inf or NaN
+__device__ __forceinline__ uint32_t nonfinite8(u32x4_t v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m |= ((v[i] & 0x7F80u) == 0x7F80u ? 1u : 0u) << (2 * i);
+    m |= ((v[i] & 0x7F800000u) == 0x7F800000u ? 1u : 0u) << (2 * i + 1);
+  }
+  return m;
+}
+
+// ---------------------------------------------------------------------------
 // the tiled kernel
 // ---------------------------------------------------------------------------
 // (a & m) | c in one instruction (gfx950 three-input bitwise operation, truth
@@ -373,7 +420,7 @@ struct TiledShape {
 template <int NS, int TS, int WN, int WT, bool ADD>
 __global__ void __launch_bounds__(64 * WN * WT)
 tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, const int* __restrict__ rexp,
-             const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+             const uint16_t* __restrict__ xraw, const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
              uint16_t* y, float* __restrict__ part, int N, int K, int T, int Tpad, int tiles_n,
              int tiles_t, int KS, const uint16_t* res) {
   using Sh = TiledShape<NS, TS, WN, WT>;
@@ -822,14 +869,26 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     constexpr int CPR = BN / 8;  // 16-byte pieces per token row of the tile
     for (int c = tid; c < BT * CPR; c += NT) {
       const int tl = c / CPR, cn = c - tl * CPR;
-      if (t0 + tl < T)
-        *reinterpret_cast<u32x4_t*>(y + (size_t)(t0 + tl) * N + n0 + cn * 8) =
-            *reinterpret_cast<const u32x4_t*>(otile + tl * BN + cn * 8);
+      if (t0 + tl < T) {
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(otile + tl * BN + cn * 8);
+        uint32_t bad = nonfinite8(v);
+        while (bad != 0u) {  // rare: recompute exactly (see exact_output)
+          const int i = __builtin_ctz(bad);
+          bad &= bad - 1u;
+          const uint32_t h = exact_output(xraw, codes, scales, ADD ? res : nullptr, N, K, n0 + cn * 8 + i, t0 + tl);
+          v[i >> 1] = (i & 1) ? ((v[i >> 1] & 0xFFFFu) | (h << 16)) : ((v[i >> 1] & 0xFFFF0000u) | h);
+        }
+        *reinterpret_cast<u32x4_t*>(y + (size_t)(t0 + tl) * N + n0 + cn * 8) = v;
+      }
     }
   } else {
     for (int c = tid; c < BT * BN; c += NT) {
       const int tl = c / BN, nl = c - tl * BN;
-      if (t0 + tl < T && n0 + nl < N) y[(size_t)(t0 + tl) * N + n0 + nl] = otile[c];
+      if (t0 + tl < T && n0 + nl < N) {
+        uint16_t v = otile[c];
+        if ((v & 0x7F80u) == 0x7F80u) v = exact_output(xraw, codes, scales, ADD ? res : nullptr, N, K, n0 + nl, t0 + tl);
+        y[(size_t)(t0 + tl) * N + n0 + nl] = v;
+      }
     }
   }
 }
@@ -840,7 +899,8 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
 constexpr int kMaxSplits = 8;
 __global__ void __launch_bounds__(256)
 tiled_reduce_kernel(const float* __restrict__ part, const int* __restrict__ texp, const int* __restrict__ rexp,
-                    uint16_t* y, int N, int Tpad, int KS, const uint16_t* res) {
+                    uint16_t* y, int N, int Tpad, int KS, const uint16_t* res, const uint16_t* __restrict__ xraw,
+                    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int K) {
   const int n = blockIdx.x * 256 + threadIdx.x, t = blockIdx.y;
   if (n >= N) return;
   const size_t i = (size_t)t * N + n, stride = (size_t)Tpad * N;
@@ -853,7 +913,9 @@ tiled_reduce_kernel(const float* __restrict__ part, const int* __restrict__ texp
     if (k < KS) v += p[k];
   v = __builtin_ldexpf(v, texp[t] - rexp[n]);
   if (res != nullptr) v += bf16_bits_to_f32(res[i]);  // LinearAdd
-  y[i] = f32_to_bf16_rne(v);
+  uint16_t h = f32_to_bf16_rne(v);
+  if ((h & 0x7F80u) == 0x7F80u) h = exact_output(xraw, codes, scales, res, N, K, n, t);  // rare
+  y[i] = h;
 }
 
 template <int NS, int TS, int WN, int WT>
@@ -863,19 +925,21 @@ hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, c
   const int tiles_n = (int)((a.n + Sh::BN - 1) / Sh::BN);
   const int tiles_t = (int)((a.t + Sh::BT - 1) / Sh::BT);
   auto kern = a.res != nullptr ? tiled_kernel<NS, TS, WN, WT, true> : tiled_kernel<NS, TS, WN, WT, false>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS_B);
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
   const int ks = a.cfg.ks;
   if (ks < 1 || ks > kMaxSplits) return hipErrorInvalidValue;
   kern<<<dim3((unsigned)(tiles_n * tiles_t * ks)), dim3(Sh::NT), Sh::LDS_B, stream>>>(
-      x16, texp, rexp, static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
+      x16, texp, rexp, static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes),
+      static_cast<const uint16_t*>(a.scales),
       static_cast<uint16_t*>(a.y), (ks > 1 || a.f32) ? part : nullptr, (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t, ks,
       static_cast<const uint16_t*>(a.res));
   e = hipGetLastError();
   if (e != hipSuccess || ks == 1 || a.f32) return e;
   tiled_reduce_kernel<<<dim3((unsigned)((a.n + 255) / 256), (unsigned)a.t), dim3(256), 0, stream>>>(
-      part, texp, rexp, static_cast<uint16_t*>(a.y), (int)a.n, tpad, ks, static_cast<const uint16_t*>(a.res));
+      part, texp, rexp, static_cast<uint16_t*>(a.y), (int)a.n, tpad, ks, static_cast<const uint16_t*>(a.res),
+      static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
+      (int)a.k);
   return hipGetLastError();
 }
 
@@ -884,6 +948,11 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
 int64_t tiled_tpad(int64_t t) { return (t + 31) / 32 * 32; }
+
+bool tiled_shape_ok(int64_t n, int64_t k, int64_t t) {
+  const int64_t lim = (int64_t(1) << 31) - 256;
+  return tiled_tpad(t) * k * 2 < lim && n * (k / 64) * 2 < lim;
+}
 
 // K split factor for a grid of `tiles` workgroup tiles: about `target`
 // workgroups in all, at most 8 splits, every split at least 10 groups.
