@@ -39,10 +39,13 @@
  * Behaviour: the call only validates its arguments on the host and enqueues
  * one or more kernels on `stream` (a hipStream_t; NULL is the null stream).  It
  * never allocates, frees or synchronizes, keeps no pointer after it returns,
- * and has no global mutable state, so it is thread-safe and may be captured in
- * a HIP graph.  x, codes and scales are only read.  Every argument error is
- * reported before anything is enqueued, leaving y untouched.  Calls that share
- * a workspace must not overlap in time.
+ * and keeps no state between calls (the library's only process-wide records
+ * are set once per kernel and device -- the dynamic-LDS limit -- and, for
+ * q4lin_linear_noalloc, the scratch array's address per device, both behind
+ * a lock), so it is thread-safe and may be captured in a HIP graph.  x,
+ * codes and scales are only read.  Every argument error is reported before
+ * anything is enqueued, leaving y untouched.  Calls that share a workspace
+ * must not overlap in time.
  */
 #ifndef Q4LIN_H
 #define Q4LIN_H
@@ -141,6 +144,29 @@ Q4LIN_API int q4lin_linear_swiglu(const void *x, const void *codes_gate, const v
 /* Bytes of workspace q4lin_linear_swiglu needs (0 for an empty product), or
  * -Q4LIN_E_SHAPE for a shape outside the contract.  Pure host function. */
 Q4LIN_API int64_t q4lin_swiglu_workspace_bytes(int64_t n, int64_t k, int64_t t);
+
+/* The op without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Y = W x X with every argument, layout, route and
+ * error of q4lin_linear; where the route needs scratch memory it uses a
+ * static array inside the library instead of a caller's workspace.  Each GPU
+ * the library runs on holds its own copy of that array
+ * (q4lin_noalloc_scratch_bytes() bytes) from the first call that needs it
+ * until the process ends; the call looks up its address once per device
+ * (with that device current) and never calls hipMalloc, hipFree or any
+ * allocating routine.  A shape whose route needs more scratch than the array
+ * holds returns Q4LIN_E_WORKSPACE before anything is enqueued.  Every call on
+ * one GPU shares that GPU's array and leaves its contents behind (the kernels
+ * write every scratch byte they later read, so nothing needs clearing): calls
+ * that overlap in time on one GPU -- on different streams, or from different
+ * threads -- race on it and must be serialized by the caller. */
+Q4LIN_API int q4lin_linear_noalloc(const void *x, const void *codes, const void *scales, void *y,
+                 int64_t n, int64_t k, int64_t t, void *stream);
+
+/* Size in bytes of the static scratch array q4lin_linear_noalloc uses
+ * (64 MiB): the largest q4lin_workspace_bytes() it accepts.  Pure host
+ * function. */
+Q4LIN_API int64_t q4lin_noalloc_scratch_bytes(void);
 
 /* Static, human-readable text for a status code (never NULL). */
 Q4LIN_API const char *q4lin_status_string(int status);

@@ -203,3 +203,24 @@ def test_linear_swiglu_misaligned_pointer_rejected(which, addr):
     ptrs = [0x1000] * 6
     ptrs[which] = addr
     assert q.q4lin_linear_swiglu(*ptrs, 64, 128, 1, 0x1000, 1 << 20, 0) == q.Q4LIN_E_ALIGN
+
+
+# -- the no-allocation entry point: host-side checks only ---------------------
+def test_noalloc_scratch_size_and_rejections():
+    cap = q.q4lin_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    p = 0x10000
+    # empty product, shape, NULL and alignment errors as q4lin_linear
+    assert q.q4lin_linear_noalloc(0, 0, 0, 0, 0, 128, 5, 0) == q.Q4LIN_OK
+    assert q.q4lin_linear_noalloc(p, p, p, p, 8, 100, 1, 0) == q.Q4LIN_E_SHAPE
+    assert q.q4lin_linear_noalloc(p, 0, p, p, 64, 128, 1, 0) == q.Q4LIN_E_NULL
+    assert q.q4lin_linear_noalloc(p + 8, p, p, p, 64, 128, 1, 0) == q.Q4LIN_E_ALIGN
+    # a many-token shape whose workspace exceeds the array: rejected before
+    # anything touches a device
+    n, k, t = 6144, 5120, 8192
+    assert q.q4lin_workspace_bytes(n, k, t) > cap
+    assert q.q4lin_linear_noalloc(p, p, p, p, n, k, t, 0) == q.Q4LIN_E_WORKSPACE
+    # the benchmarked workloads fit
+    for (n, k, t) in [(6144, 5120, 1024), (6144, 5120, 128), (14336, 5120, 1024), (34816, 5120, 1024),
+                      (5120, 17408, 1024)]:
+        assert 0 <= q.q4lin_workspace_bytes(n, k, t) <= cap, (n, k, t)

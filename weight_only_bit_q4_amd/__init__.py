@@ -35,7 +35,8 @@ Q4LIN_ROUTE_DECODE = 4
 
 EXPORTED = ("q4lin_workspace_bytes", "q4lin_linear", "q4lin_linear_add", "q4lin_linear_pair",
             "q4lin_pair_workspace_bytes", "q4lin_linear_swiglu", "q4lin_swiglu_workspace_bytes",
-            "q4lin_status_string", "q4lin_route", "q4lin_version")
+            "q4lin_status_string", "q4lin_route", "q4lin_version", "q4lin_linear_noalloc",
+            "q4lin_noalloc_scratch_bytes")
 
 
 class Q4LinError(RuntimeError):
@@ -79,6 +80,10 @@ def _load() -> ctypes.CDLL:
     lib.q4lin_route.restype = ctypes.c_int
     lib.q4lin_version.argtypes = []
     lib.q4lin_version.restype = ctypes.c_int
+    lib.q4lin_linear_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.q4lin_linear_noalloc.restype = ctypes.c_int
+    lib.q4lin_noalloc_scratch_bytes.argtypes = []
+    lib.q4lin_noalloc_scratch_bytes.restype = i64
     return lib
 
 
@@ -136,6 +141,16 @@ def q4lin_linear_swiglu(x: int, codes_gate: int, scales_gate: int, codes_up: int
 
 def q4lin_swiglu_workspace_bytes(n: int, k: int, t: int) -> int:
     return int(load().q4lin_swiglu_workspace_bytes(int(n), int(k), int(t)))
+
+
+def q4lin_linear_noalloc(x: int, codes: int, scales: int, y: int, n: int, k: int, t: int, stream: int) -> int:
+    """Raw call of the no-allocation entry point (scratch inside the library); returns the status."""
+    return int(load().q4lin_linear_noalloc(x or None, codes or None, scales or None, y or None,
+                                           int(n), int(k), int(t), stream or None))
+
+
+def q4lin_noalloc_scratch_bytes() -> int:
+    return int(load().q4lin_noalloc_scratch_bytes())
 
 
 def q4lin_status_string(status: int) -> str:

@@ -73,16 +73,28 @@ size_t route_workspace(int route, int64_t n, int64_t k, int64_t t) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// The op, with an optional residual (LinearAdd when res is not null).
-int run_linear(const void* x, const void* codes, const void* scales, const void* res, void* y,
-               int64_t n, int64_t k, int64_t t, void* workspace, size_t workspace_bytes, void* stream) {
+// Host-side checks of the op's arguments other than the workspace: the
+// status, and in *route the route for a valid non-empty product.
+int check_linear(const void* x, const void* codes, const void* scales, const void* res, const void* y,
+                 int64_t n, int64_t k, int64_t t, int* route) {
+  *route = Q4LIN_ROUTE_NONE;
   if (!shape_ok(n, k, t)) return Q4LIN_E_SHAPE;
-  const int route = pick_route(n, k, t);
-  if (route == Q4LIN_ROUTE_NONE) return Q4LIN_OK;
-  if (route == Q4LIN_ROUTE_TILED && !q4lin::tiled_shape_ok(n, k, t)) return Q4LIN_E_SHAPE;
+  const int r = pick_route(n, k, t);
+  if (r == Q4LIN_ROUTE_NONE) return Q4LIN_OK;
+  if (r == Q4LIN_ROUTE_TILED && !q4lin::tiled_shape_ok(n, k, t)) return Q4LIN_E_SHAPE;
   if (!x || !codes || !scales || !y) return Q4LIN_E_NULL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(y, 2) || !aligned(res, 2))
     return Q4LIN_E_ALIGN;
+  *route = r;
+  return Q4LIN_OK;
+}
+
+// The op, with an optional residual (LinearAdd when res is not null).
+int run_linear(const void* x, const void* codes, const void* scales, const void* res, void* y,
+               int64_t n, int64_t k, int64_t t, void* workspace, size_t workspace_bytes, void* stream) {
+  int route = Q4LIN_ROUTE_NONE;
+  const int st = check_linear(x, codes, scales, res, y, n, k, t, &route);
+  if (st != Q4LIN_OK || route == Q4LIN_ROUTE_NONE) return st;
   const size_t need = route_workspace(route, n, k, t);
   if (need > 0) {
     if (workspace_bytes < need) return Q4LIN_E_WORKSPACE;
@@ -143,9 +155,53 @@ hipError_t launch_sums(int route, const q4lin::GemvArgs& a, hipStream_t s) {
   return q4lin::launch_gemv(a, s);
 }
 
+// ---------------------------------------------------------------------------
+// The no-allocation variant's scratch: a static device array (each GPU the
+// library runs on holds its own copy until the process ends).  Host code
+// never uses the array's name as an address: the device address is fetched
+// once per device with hipGetSymbolAddress and kept in scratch_dev.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];  // device address of `scratch` per device, null until first needed
+
+// The current device's address of the scratch array (looked up on the first
+// call on that device, with that device current).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q4LIN_E_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return Q4LIN_E_LAUNCH;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return Q4LIN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t q4lin_noalloc_scratch_bytes(void) { return (int64_t)kScratchBytes; }
+
+int q4lin_linear_noalloc(const void* x, const void* codes, const void* scales, void* y,
+                         int64_t n, int64_t k, int64_t t, void* stream) {
+  int route = Q4LIN_ROUTE_NONE;
+  const int st = check_linear(x, codes, scales, nullptr, y, n, k, t, &route);
+  if (st != Q4LIN_OK || route == Q4LIN_ROUTE_NONE) return st;
+  const size_t need = route_workspace(route, n, k, t);
+  if (need > kScratchBytes) return Q4LIN_E_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int sa = scratch_address(&ws);
+    if (sa != Q4LIN_OK) return sa;
+  }
+  return run_linear(x, codes, scales, nullptr, y, n, k, t, ws, need, stream);
+}
 
 int64_t q4lin_swiglu_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   SwigluPlan p;
