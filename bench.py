@@ -132,24 +132,35 @@ class Point:
         return g
 
     def time(self, steps, warmup, repeats=1):
-        """Returns (list of seconds per call over `repeats` timed replays,
-        each replay = exactly `steps` calls)."""
+        """Returns the list of seconds per call of `repeats` timed replays,
+        each replay exactly `steps` calls.
+
+        Each replay: device synchronize; a graph of max(warmup, 8) untimed
+        calls; then, queued behind it on the same stream with no host
+        round-trip, the start event, the graph of the `steps` timed calls and
+        the end event; device synchronize.  The timed graph's launch is thus
+        processed while the warm-up calls run, so the events measure the
+        calls themselves, back to back, and the per-call period does not
+        depend on `steps` (a graph launch costs tens of microseconds of
+        host and queue time, which would otherwise be divided by `steps`)."""
         torch = self.torch
         with torch.cuda.stream(self.stream):
             for i in range(min(warmup, 4 * self.nsets)):
                 self.call(i, self.stream.cuda_stream)
         torch.cuda.synchronize()
         g = self.graph(steps)
-        gw = self.graph(max(warmup, 1), offset=steps) if warmup > 0 else None
+        # the warm-up calls take the buffer sets just before set 0 in the
+        # rotation, so the first timed calls still find cold buffers
+        w = max(warmup, 8)
+        gw = self.graph(w, offset=(self.nsets - w % self.nsets) % self.nsets)
         out = []
         # replay() launches on the current stream: make that the timed stream
         with torch.cuda.stream(self.stream):
             for _ in range(repeats):
-                if gw is not None:
-                    gw.replay()
                 torch.cuda.synchronize()
                 start = torch.cuda.Event(enable_timing=True)
                 end = torch.cuda.Event(enable_timing=True)
+                gw.replay()
                 start.record(self.stream)
                 g.replay()
                 end.record(self.stream)
@@ -190,23 +201,46 @@ class Point:
         self.torch.cuda.empty_cache()
 
 
-def cpu_baseline_t1(n, k, seed, budget_s=10.0):
+def host_cpu_model() -> str:
+    """The host CPU's model name (first 'model name' of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_t1(n, k, seed, budget_s=10.0, budget_1t_s=4.0):
     """The oracle, untuned, on the host cores: whole T=1 problems repeated
-    for about `budget_s` seconds; returns GB/s in the pages' metric."""
+    for about `budget_s` seconds with all cores (OpenMP over rows), then for
+    about `budget_1t_s` seconds on one thread; returns GB/s in the pages'
+    metric (median per problem) for both."""
     import oracle
     from weight_only_bit_q4_amd import inputs
     x, c, s = inputs.gen_problem(n, k, 1, seed)
     o = oracle.default()
-    times = []
-    t_end = time.perf_counter() + budget_s
-    while time.perf_counter() < t_end or not times:
-        t0 = time.perf_counter()
-        o.linear(x, c, s, n, k, 1)
-        times.append(time.perf_counter() - t0)
-    med = float(np.median(times))
-    return {"value": round(gbs(n, k, 1, med), 4), "unit": "GB/s", "cores": o.max_threads(),
-            "kind": "oracle",
-            "sample": "%d full %dx%d T=1 problems, median %.1f ms each" % (len(times), n, k, med * 1e3)}
+    cores = o.max_threads()
+
+    def run(threads, budget):
+        times = []
+        t_end = time.perf_counter() + budget
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            o.linear(x, c, s, n, k, 1, threads=threads)
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times)), len(times)
+
+    med, cnt = run(cores, budget_s)
+    med1, cnt1 = run(1, budget_1t_s)
+    o.linear(x, c[:0], s[:0], 0, k, 1, threads=cores)  # leave the thread count as found
+    return {"value": round(gbs(n, k, 1, med), 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "cpu_model": host_cpu_model(),
+            "sample": "%d full %dx%d T=1 problems, median %.1f ms each" % (cnt, n, k, med * 1e3),
+            "one_thread": {"value": round(gbs(n, k, 1, med1), 4), "unit": "GB/s", "cores": 1,
+                           "sample": "%d full problems, median %.1f ms each" % (cnt1, med1 * 1e3)}}
 
 
 def cpu_baseline_rows(n, k, t, seed, budget_s=10.0):
@@ -217,12 +251,13 @@ def cpu_baseline_rows(n, k, t, seed, budget_s=10.0):
     from weight_only_bit_q4_amd import inputs
     x, c, s = inputs.gen_problem(n, k, t, seed)
     o = oracle.default()
+    cores = o.max_threads()
 
     def run(rows):
         ns = np.repeat(np.arange(rows), t)
         ts = np.tile(np.arange(t), rows)
         t0 = time.perf_counter()
-        o.linear_at(x, c, s, n, k, t, ns, ts)
+        o.linear_at(x, c, s, n, k, t, ns, ts, threads=cores)
         return time.perf_counter() - t0
 
     probe_rows = 16
@@ -230,8 +265,8 @@ def cpu_baseline_rows(n, k, t, seed, budget_s=10.0):
     rows = int(min(n, max(probe_rows, probe_rows * budget_s / max(el, 1e-6))))
     el = run(rows)
     full = el * n / rows
-    return {"value": round(tflops(n, k, t, full), 6), "unit": "TFLOP/s", "cores": o.max_threads(),
-            "kind": "oracle",
+    return {"value": round(tflops(n, k, t, full), 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "cpu_model": host_cpu_model(),
             "sample": "%d of %d output rows of %dx%d T=%d (%.1f s), scaled to all rows" % (rows, n, n, k, t, el)}
 
 
@@ -283,32 +318,71 @@ def copy_calibration(nbytes: int, reps: int = 5):
     print(json.dumps({"copy_calibration": True, "bytes": nbytes, "reps": reps}))
 
 
-def _graph_period(torch, fn, steps, repeats=5):
+def _graph_period(torch, fn, steps, repeats=5, warm=8):
     """Median seconds per call of `steps` calls of fn(i, stream_handle) captured
-    in one graph (same method as Point.time)."""
+    in one graph, each timed replay queued behind a graph of `warm` untimed
+    calls (same method as Point.time)."""
     st = torch.cuda.Stream()
     with torch.cuda.stream(st):
         for i in range(3):
             fn(i, st.cuda_stream)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(st):
-        with torch.cuda.graph(g, stream=st):
-            for i in range(steps):
-                fn(i, st.cuda_stream)
+
+    def capture(count, offset):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for i in range(count):
+                    fn(offset + i, st.cuda_stream)
+        return g
+
+    g = capture(steps, 0)
+    gw = capture(warm, steps)
     out = []
     with torch.cuda.stream(st):
         for _ in range(repeats):
-            g.replay()
             torch.cuda.synchronize()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
+            gw.replay()
             a.record(st)
             g.replay()
             b.record(st)
             torch.cuda.synchronize()
             out.append(a.elapsed_time(b) / 1e3 / steps)
     return float(np.median(out))
+
+
+PROBE_SHAPES = [(256, 512, 8), (512, 512, 4), (1024, 512, 2), (1024, 256, 4), (2048, 512, 1), (2048, 256, 2),
+                (4096, 256, 1), (8192, 256, 1)]
+
+
+def read_ceiling(torch, nbytes, steps=200, repeats=5):
+    """The same-GPU sustained-read ceiling for a cold stream of `nbytes`: the
+    streaming-read probe (every lane several 16-byte loads in flight) over
+    rotating buffers, best of a few launch shapes, timed like the op.
+    Returns (seconds per read, launch shape)."""
+    import ctypes
+    from weight_only_bit_q4_amd import build as q4build
+    lib = ctypes.CDLL(q4build.PROBE_LIB)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.q4lin_probe_read.argtypes = [vp, i64, vp, ci, ci, ci, vp]
+    nb = nbytes // 16 * 16
+    nsets = int(math.ceil(ROTATE_BYTES / nb)) + 1
+    bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    out = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    best = None
+    for (grid, block, u) in PROBE_SHAPES:
+        def f(i, h, grid=grid, block=block, u=u):
+            r = lib.q4lin_probe_read(bufs[i % nsets].data_ptr(), nb, out.data_ptr(), grid, block, u, h)
+            if r != 0:
+                raise RuntimeError("probe call failed: %d" % r)
+        t = _graph_period(torch, f, steps, repeats)
+        if best is None or t < best[0]:
+            best = (t, {"grid": grid, "block": block, "loads_per_lane": u})
+    del bufs
+    torch.cuda.empty_cache()
+    return best
 
 
 def ceilings():
@@ -340,7 +414,7 @@ def ceilings():
         nsets = int(math.ceil(ROTATE_BYTES / nb)) + 1
         bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
         best = None
-        for (grid, block, u) in [(256, 512, 8), (1024, 512, 2), (2048, 512, 1), (4096, 256, 1), (8192, 256, 1)]:
+        for (grid, block, u) in PROBE_SHAPES:
             def f(i, h, grid=grid, block=block, u=u):
                 check(lib.q4lin_probe_read(bufs[i % nsets].data_ptr(), nb, out.data_ptr(), grid, block, u, h))
             t = _graph_period(torch, f, 1000 if nb < 3e7 else 300)
@@ -375,6 +449,36 @@ def ceilings():
         torch.cuda.empty_cache()
 
 
+def trace_summary(path):
+    """Per-kernel durations from a rocprofv3 kernel-trace CSV, split by
+    population: calls that follow another call of the op back to back
+    ('back_to_back': graph replays) and calls that follow any other kernel
+    ('after_other': the cold single calls behind a cache flush, and the first
+    call of each replay).  Prints one markdown table row per (kernel,
+    population) with count, median, min, p95 and mean in ns."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    groups = {}
+    prev = None
+    for (a, b, name) in rows:
+        pop = "back_to_back" if prev is not None and prev.startswith("q4lin") else "after_other"
+        short = name.split("(")[0]
+        groups.setdefault((short, pop), []).append(b - a)
+        prev = short
+    print("| kernel | population | calls | median ns | min ns | p95 ns | mean ns |")
+    print("|---|---|---|---|---|---|---|")
+    for (name, pop), d in sorted(groups.items(), key=lambda kv: (-len(kv[1]), kv[0])):
+        if not name.startswith("q4lin"):
+            continue
+        a = np.asarray(d, dtype=np.float64)
+        print("| %s | %s | %d | %.0f | %.0f | %.0f | %.1f |" % (name, pop, a.size, np.median(a), a.min(),
+                                                             np.percentile(a, 95), a.mean()))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,7 +504,13 @@ def main(argv=None):
     ap.add_argument("--csv", type=str, default=None)
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="BYTES",
                     help="run a plain copy of BYTES bytes (for scaling the byte counters), then exit")
+    ap.add_argument("--trace-summary", type=str, default=None, metavar="CSV",
+                    help="summarize a rocprofv3 kernel_trace.csv (per kernel and population), then exit")
     args = ap.parse_args(argv)
+
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return 0
 
     if args.gpus != 1:
         print("bench.py measures one GPU only; --gpus %d is not supported (see the design notes "
@@ -438,6 +548,10 @@ def main(argv=None):
         codes = inputs.gen_codes(n, k, wl_seed)
         scales = inputs.gen_scales(n, k, wl_seed)
         xall = inputs.gen_x(k, hi, wl_seed)
+        rc_s, _ = read_ceiling(torch, weight_bytes(n, k))
+        rc_gbs = weight_bytes(n, k) // 16 * 16 / rc_s / 1e9
+        print("read ceiling (streaming read of the %d weight bytes): %.3f us, %.1f GB/s"
+              % (weight_bytes(n, k), rc_s * 1e6, rc_gbs), flush=True)
         for t in range(lo, hi + 1, step):
             p = Point(n, k, t, wl_seed, data=(xall[:t], codes, scales))
             steps = max(20, min(200, int(2e-3 / max(1e-6, 1e-6 * t))))
@@ -447,13 +561,15 @@ def main(argv=None):
             row = {"t": t, "us": med * 1e6, "min_us": min(secs) * 1e6, "gbs": gbs(n, k, t, med),
                    "tflops": tflops(n, k, t, med), "hbm_frac": gbs(n, k, t, med) / HBM_PEAK_GBS,
                    "mfma_frac": tflops(n, k, t, med) / MFMA_PEAK_TFLOPS,
-                   "roof_frac": roof_fraction(n, k, t, med),
+                   "roof_frac": roof_fraction(n, k, t, med), "read_pct": 100.0 * gbs(n, k, t, med) / rc_gbs,
                    "delta_pct": None if prev is None else (med / prev - 1) * 100}
             prev = med
             rows.append(row)
-            print("T=%4d  %9.3f us  %8.1f GB/s (%5.1f%% HBM)  %8.2f TFLOP/s (%5.1f%% MFMA)  roof %5.1f%%  %s"
-                  % (t, row["us"], row["gbs"], 100 * row["hbm_frac"], row["tflops"], 100 * row["mfma_frac"],
-                     100 * row["roof_frac"], "" if row["delta_pct"] is None else "%+.1f%%" % row["delta_pct"]),
+            print("T=%4d  %9.3f us  %8.1f GB/s (%5.1f%% HBM, %5.1f%% READ)  %8.2f TFLOP/s (%5.1f%% MFMA)  "
+                  "roof %5.1f%%  %s"
+                  % (t, row["us"], row["gbs"], 100 * row["hbm_frac"], row["read_pct"], row["tflops"],
+                     100 * row["mfma_frac"], 100 * row["roof_frac"],
+                     "" if row["delta_pct"] is None else "%+.1f%%" % row["delta_pct"]),
                   flush=True)
         if args.csv:
             import csv
@@ -585,8 +701,10 @@ def main(argv=None):
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     p1 = Point(n, k, 1, seed)
-    s1 = p1.time(args.steps, args.warmup, repeats=1)[0]
+    reps1 = p1.time(args.steps, args.warmup, repeats=5)
+    s1 = float(np.median(reps1))
     p1.free()
+    rc_s, rc_launch = read_ceiling(torch, model_bytes(n, k, 1))
     p1c = Point(n, k, 1, seed, rotate=False)
     lat1 = p1c.time_cold(100, 5)
     p1c.free()
@@ -618,11 +736,24 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 (f32 accumulate; bf16 in/out)",
+        "dtype": "bf16",
+        "dtype_by_route": {
+            "single-token (T=1)": "bf16 activations x exact bf16 (128+q) codes, f32 dot products, "
+                                  "group scale in f32, binary64 cross-wave sum",
+            "tiled (T=1024)": "f16 activations (per-token power of two) x f16 (q-8)*scale (per-row power "
+                              "of two), f32 accumulate"},
         "data": "synthetic",
         "config": {"workload": "decode_6144x5120_t1", "n": n, "k": k, "t": 1,
                    "weight_format": "Q4_G64_FP16",
-                   "cache": "cold (rotating buffer sets, >= 1 GiB between reuses)"},
+                   "cache": "cold (rotating buffer sets, >= 1 GiB between reuses)",
+                   "timing": "median of %d graph replays of exactly %d calls, each queued behind %d "
+                             "untimed calls" % (len(reps1), args.steps, max(args.warmup, 8))},
+        "replays_us_per_call": [round(v * 1e6, 3) for v in reps1],
+        # the pages' READ_% column: the op's logical GB/s against a plain
+        # streaming read of the same number of bytes on this GPU, timed alike
+        "read_ceiling": {"bytes": model_bytes(n, k, 1) // 16 * 16, "us": round(rc_s * 1e6, 3),
+                         "gbs": round(model_bytes(n, k, 1) // 16 * 16 / rc_s / 1e9, 1), "launch": rc_launch},
+        "read_pct": round(100.0 * v1 / (model_bytes(n, k, 1) // 16 * 16 / rc_s / 1e9), 2),
         # dominant kernel: the single-token kernel is the whole call at T = 1;
         # its algorithmic bytes per launch are model_bytes (W, X and Y once each)
         "roofline": {"bound": "hbm", "achieved": round(v1, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
