@@ -15,10 +15,18 @@ in the C file's header:
   FP64 matrix product as the oracle;
 * "linear-benchmark.md", section 4 table: 34 bytes per 64-weight group.
 
+The other weight formats of the same op (Q5G64_F16S, Q6G64_F16S,
+W8G32_F16S, NVFP4, BF16_CTRL; "linear-benchmark.md", sections 0 and 4) are
+``linear_fmt`` / ``linear_fmt_at`` with the format's planes; their readings
+(bit layouts and code meanings the pages leave open) are stated in the C
+file.
+
 Parity status: ``fp16_to_double``, ``bf16_to_double``, ``double_to_bf16``,
-``weight_bytes``, ``linear`` and ``linear_at`` are each pinned by the CPU
-test-suite (hand-worked examples, library special cases, invariants, exact
-rational brute force); none is "parity unpinned".
+``weight_bytes``, ``linear`` and ``linear_at``, and ``e4m3_to_double``,
+``e2m1_to_double``, ``fmt_weight_bytes``, ``linear_fmt`` and
+``linear_fmt_at`` are each pinned by the CPU test-suite (hand-worked
+examples, library special cases, invariants, relations between formats,
+exact rational brute force); none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -86,6 +94,18 @@ class Oracle:
         lib.q4o_swiglu.restype = None
         lib.q4o_max_threads.argtypes = []
         lib.q4o_max_threads.restype = ctypes.c_int
+        vp = ctypes.c_void_p
+        lib.q4o_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        lib.q4o_e4m3_to_double.restype = ctypes.c_double
+        lib.q4o_e2m1_to_double.argtypes = [ctypes.c_uint8]
+        lib.q4o_e2m1_to_double.restype = ctypes.c_double
+        lib.q4o_fmt_weight_bytes.argtypes = [ctypes.c_int, i64, i64]
+        lib.q4o_fmt_weight_bytes.restype = i64
+        lib.q4o_linear_fmt.argtypes = [ctypes.c_int, u16p, u8p, u8p, vp, u16p, f64p, i64, i64, i64, ctypes.c_int]
+        lib.q4o_linear_fmt.restype = None
+        lib.q4o_linear_fmt_at.argtypes = [ctypes.c_int, u16p, u8p, u8p, vp, i64, i64, i64, i64p, i64p, i64,
+                                          u16p, ctypes.c_int]
+        lib.q4o_linear_fmt_at.restype = None
         self.lib = lib
         self.path = lib_path
 
@@ -104,6 +124,62 @@ class Oracle:
 
     def max_threads(self) -> int:
         return int(self.lib.q4o_max_threads())
+
+    def e4m3_to_double(self, bits: int) -> float:
+        return self.lib.q4o_e4m3_to_double(int(bits) & 0xFF)
+
+    def e2m1_to_double(self, nib: int) -> float:
+        return self.lib.q4o_e2m1_to_double(int(nib) & 0xF)
+
+    def fmt_weight_bytes(self, fmt: int, n: int, k: int) -> int:
+        return int(self.lib.q4o_fmt_weight_bytes(int(fmt), int(n), int(k)))
+
+    # other weight formats ---------------------------------------------------
+    @staticmethod
+    def _prep_fmt(fmt, x, lo, hi, sc, n, k, t):
+        if k % 64 != 0 or k < 64:
+            raise ValueError("K must be a positive multiple of 64")
+        if fmt not in PLANES:
+            raise ValueError("unknown format %r" % (fmt,))
+        lo_b, hi_b, sc_b = (f(n, k) for f in PLANES[fmt])
+        x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1)
+        lo = np.ascontiguousarray(lo).reshape(-1).view(np.uint8)
+        hi = np.zeros(1, np.uint8) if hi_b == 0 else np.ascontiguousarray(hi).reshape(-1).view(np.uint8)
+        sc = np.zeros(1, np.uint8) if sc_b == 0 else np.ascontiguousarray(sc).reshape(-1).view(np.uint8)
+        if x.size != k * t or lo.size != lo_b or (hi_b and hi.size != hi_b) or (sc_b and sc.size != sc_b):
+            raise ValueError("plane sizes do not match the format and N, K, T")
+        return x, lo, hi, sc
+
+    def linear_fmt(self, fmt: int, x, lo, hi, sc, n: int, k: int, t: int, threads: int = 0,
+                   with_acc: bool = False):
+        """Y = bf16(W . X) for a weight in format ``fmt`` (FMT_*), given as
+        its planes (numpy arrays of any dtype, read as bytes; ``hi`` and
+        ``sc`` may be None where the format has none).  Returns bf16 bits
+        ``[T, N]`` (and the binary64 sums with ``with_acc``)."""
+        x, lo, hi, sc = self._prep_fmt(fmt, x, lo, hi, sc, n, k, t)
+        y = np.zeros(t * n, dtype=np.uint16)
+        acc = np.zeros(t * n, dtype=np.float64) if with_acc else None
+        self.lib.q4o_linear_fmt(int(fmt), _ptr(x, ctypes.c_uint16), _ptr(lo, ctypes.c_uint8),
+                                _ptr(hi, ctypes.c_uint8), sc.ctypes.data, _ptr(y, ctypes.c_uint16),
+                                _ptr(acc, ctypes.c_double), n, k, t, int(threads))
+        y = y.reshape(t, n)
+        if with_acc:
+            return y, acc.reshape(t, n)
+        return y
+
+    def linear_fmt_at(self, fmt: int, x, lo, hi, sc, n: int, k: int, t: int, ns, ts, threads: int = 0):
+        """Selected elements ``Y[ns[i], ts[i]]`` of the format-``fmt`` product."""
+        x, lo, hi, sc = self._prep_fmt(fmt, x, lo, hi, sc, n, k, t)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        ts = np.ascontiguousarray(ts, dtype=np.int64)
+        if ns.shape != ts.shape or (ns.size and (ns.min() < 0 or ns.max() >= n or ts.min() < 0 or ts.max() >= t)):
+            raise ValueError("bad sample indices")
+        out = np.zeros(ns.size, dtype=np.uint16)
+        self.lib.q4o_linear_fmt_at(int(fmt), _ptr(x, ctypes.c_uint16), _ptr(lo, ctypes.c_uint8),
+                                   _ptr(hi, ctypes.c_uint8), sc.ctypes.data, n, k, t,
+                                   _ptr(ns, ctypes.c_int64), _ptr(ts, ctypes.c_int64), ns.size,
+                                   _ptr(out, ctypes.c_uint16), int(threads))
+        return out
 
     # the product ------------------------------------------------------------
     @staticmethod
@@ -186,6 +262,18 @@ class Oracle:
         return out
 
 
+# Weight formats (the pages' "linear-benchmark.md" section 4 table) and the
+# byte sizes of their planes (low/code plane, high plane, scale plane).
+FMT_Q4, FMT_Q5, FMT_Q6, FMT_W8, FMT_NVFP4, FMT_BF16 = range(6)
+PLANES = {
+    FMT_Q4: (lambda n, k: n * k // 2, lambda n, k: 0, lambda n, k: n * (k // 64) * 2),
+    FMT_Q5: (lambda n, k: n * k // 2, lambda n, k: n * k // 8, lambda n, k: n * (k // 64) * 2),
+    FMT_Q6: (lambda n, k: n * k // 2, lambda n, k: n * k // 4, lambda n, k: n * (k // 64) * 2),
+    FMT_W8: (lambda n, k: n * k, lambda n, k: 0, lambda n, k: n * (k // 32) * 2),
+    FMT_NVFP4: (lambda n, k: n * k // 2, lambda n, k: 0, lambda n, k: n * (k // 16)),
+    FMT_BF16: (lambda n, k: n * k * 2, lambda n, k: 0, lambda n, k: 0),
+}
+
 _lock = threading.Lock()
 _default = None
 
@@ -241,3 +329,11 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     """bfloat16 bit patterns -> binary64 values (exact), for tolerance checks."""
     b = np.ascontiguousarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def linear_fmt(*args, **kw):
+    return default().linear_fmt(*args, **kw)
+
+
+def linear_fmt_at(*args, **kw):
+    return default().linear_fmt_at(*args, **kw)

@@ -268,6 +268,187 @@ void q4o_linear_at(const uint16_t *x, const uint8_t *codes, const uint16_t *scal
     }
 }
 
+/* ------------------------------------------------------------------------
+ * The other weight formats of the same pure Linear.
+ *
+ * "linear-benchmark.md", section 4 (theoretical traffic), weight-format
+ * table: Q5G64_F16S (64 weights per group: 32 low-code bytes + 8 high bytes +
+ * a 2-byte scale = 42 bytes), Q6G64_F16S (32 + 16 + 2 = 50 bytes per 64),
+ * W8G32_F16S (32 weights per group: 32 code bytes + 2 scale bytes = 34),
+ * NVFP4 (16 weights per group: 8 code bytes + one E4M3 scale byte = 9) and
+ * BF16_CTRL (plain bf16 weights, 2 N K bytes); section 0 lists the formats
+ * the A16 Linear takes.  The pages give byte counts only.  Readings taken
+ * (the plainest packing that matches those counts):
+ *   Q5: q = low nibble | high bit << 4 in 0..31, weight (q - 16) * scale;
+ *       low plane [N][K/2] as in Q4 (even k in the low nibble), high plane
+ *       [N][K/8]: bit i of byte b is the high bit of k = 8b + i.
+ *   Q6: q = low nibble | high pair << 4 in 0..63, weight (q - 32) * scale;
+ *       high plane [N][K/4]: bits 2i, 2i+1 of byte b are the high pair of
+ *       k = 4b + i.
+ *   W8: a two's-complement byte c per weight, plane [N][K], weight c * scale
+ *       with scales [N][K/32].
+ *   NVFP4: an E2M1 code per weight (plane [N][K/2], even k in the low
+ *       nibble), one E4M3 scale byte per 16 weights (plane [N][K/16]),
+ *       weight = E2M1 value * E4M3 value (no further tensor-wide scale: the
+ *       table counts none).
+ *   BF16_CTRL: the weights themselves, bf16 bits [N][K].
+ * Every product of a weight and an activation is exact in binary64 (at most
+ * 27 significant bits); sums are taken in binary64 in increasing k and
+ * rounded once to bf16, as for Q4.
+ * ------------------------------------------------------------------------ */
+#define Q4O_FMT_Q4 0
+#define Q4O_FMT_Q5 1
+#define Q4O_FMT_Q6 2
+#define Q4O_FMT_W8 3
+#define Q4O_FMT_NVFP4 4
+#define Q4O_FMT_BF16 5
+
+/* OCP 8-bit floating point E4M3 (the "fn" variant: exponent bias 7, three
+ * fraction bits, subnormals, no infinities, S.1111.111 is NaN), decoded by
+ * hand. */
+double q4o_e4m3_to_double(uint8_t b)
+{
+    int sign = (b >> 7) & 1;
+    int e = (b >> 3) & 0xF;
+    int m = b & 0x7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);           /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexp((double)(m + 8), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* OCP 4-bit floating point E2M1 (exponent bias 1, one fraction bit,
+ * exponent 0 is subnormal): magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double q4o_e2m1_to_double(uint8_t nib)
+{
+    int sign = (nib >> 3) & 1;
+    int e = (nib >> 1) & 3;
+    int m = nib & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+/* Weight bytes of an N x K matrix in each format, the pages' closed forms
+ * (section 4 table; K a multiple of 64, so K_pad = K wherever K % 128 == 0
+ * and the group count is N * K / group size).  -1 for an unknown format. */
+int64_t q4o_fmt_weight_bytes(int fmt, int64_t n, int64_t k)
+{
+    switch (fmt) {
+    case Q4O_FMT_Q4: return n * (k / 64) * 34;
+    case Q4O_FMT_Q5: return n * (k / 64) * 42;
+    case Q4O_FMT_Q6: return n * (k / 64) * 50;
+    case Q4O_FMT_W8: return n * (k / 32) * 34;
+    case Q4O_FMT_NVFP4: return n * (k / 16) * 9;
+    case Q4O_FMT_BF16: return 2 * n * k;
+    default: return -1;
+    }
+}
+
+static int low_nibble(const uint8_t *lo, int64_t K, int64_t n, int64_t k)
+{
+    uint8_t byte = lo[n * (K / 2) + k / 2];
+    return (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+}
+
+/* One weight value W[n,k] of format fmt, exact in binary64.  lo: the code
+ * plane (Q4/Q5/Q6/NVFP4 nibbles, W8 bytes, BF16 values); hi: the high plane
+ * (Q5, Q6; else unused); sc: the scale plane (fp16 bits, or E4M3 bytes for
+ * NVFP4; unused for BF16). */
+static double fmt_weight(int fmt, const uint8_t *lo, const uint8_t *hi, const void *sc,
+                         int64_t K, int64_t n, int64_t k)
+{
+    const uint16_t *s16 = (const uint16_t *)sc;
+    switch (fmt) {
+    case Q4O_FMT_Q4: {
+        int q = low_nibble(lo, K, n, k);
+        return (double)(q - 8) * q4o_fp16_to_double(s16[n * (K / 64) + k / 64]);
+    }
+    case Q4O_FMT_Q5: {
+        int h = (hi[n * (K / 8) + k / 8] >> (k % 8)) & 1;
+        int q = low_nibble(lo, K, n, k) | (h << 4);
+        return (double)(q - 16) * q4o_fp16_to_double(s16[n * (K / 64) + k / 64]);
+    }
+    case Q4O_FMT_Q6: {
+        int h = (hi[n * (K / 4) + k / 4] >> (2 * (k % 4))) & 3;
+        int q = low_nibble(lo, K, n, k) | (h << 4);
+        return (double)(q - 32) * q4o_fp16_to_double(s16[n * (K / 64) + k / 64]);
+    }
+    case Q4O_FMT_W8: {
+        int c = (int)(int8_t)lo[n * K + k];
+        return (double)c * q4o_fp16_to_double(s16[n * (K / 32) + k / 32]);
+    }
+    case Q4O_FMT_NVFP4: {
+        const uint8_t *s8 = (const uint8_t *)sc;
+        return q4o_e2m1_to_double((uint8_t)low_nibble(lo, K, n, k)) * q4o_e4m3_to_double(s8[n * (K / 16) + k / 16]);
+    }
+    case Q4O_FMT_BF16: {
+        const uint16_t *w = (const uint16_t *)lo;
+        return q4o_bf16_to_double(w[n * K + k]);
+    }
+    default:
+        return NAN;
+    }
+}
+
+/* Full product in format fmt (layouts above; x and y as for q4o_linear):
+ * y[t*N + n] = bf16_rne(sum_k W[n,k] X[k,t]), binary64 sum in increasing k;
+ * acc (optional) receives the unrounded sums. */
+void q4o_linear_fmt(int fmt, const uint16_t *x, const uint8_t *lo, const uint8_t *hi, const void *sc,
+                    uint16_t *y, double *acc, int64_t N, int64_t K, int64_t T, int threads)
+{
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k)
+                w[k] = fmt_weight(fmt, lo, hi, sc, K, n, k);
+            for (int64_t t = 0; t < T; ++t) {
+                double sum = 0.0;
+                const uint16_t *xt = x + t * K;
+                for (int64_t k = 0; k < K; ++k)
+                    sum += w[k] * q4o_bf16_to_double(xt[k]);
+                y[t * N + n] = q4o_double_to_bf16(sum);
+                if (acc)
+                    acc[t * N + n] = sum;
+            }
+        }
+        free(w);
+    }
+}
+
+/* Selected elements of the format-fmt product: out[i] = Y[ns[i], ts[i]]. */
+void q4o_linear_fmt_at(int fmt, const uint16_t *x, const uint8_t *lo, const uint8_t *hi, const void *sc,
+                       int64_t N, int64_t K, int64_t T, const int64_t *ns, const int64_t *ts, int64_t count,
+                       uint16_t *out, int threads)
+{
+    (void)N;
+    (void)T;
+#ifdef _OPENMP
+    if (threads > 0)
+        omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < count; ++i) {
+        double sum = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            sum += fmt_weight(fmt, lo, hi, sc, K, ns[i], k) * q4o_bf16_to_double(x[ts[i] * K + k]);
+        out[i] = q4o_double_to_bf16(sum);
+    }
+}
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int q4o_max_threads(void)
 {

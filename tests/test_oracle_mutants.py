@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import oracle_pins
+import oracle_pins_fmt
 
 MUTANTS = [
     ("sign of the code offset", "(double)(q - 8) * s", "(double)(8 - q) * s"),
@@ -46,6 +47,23 @@ MUTANTS = [
     ("swiglu gate rounded to binary32 first", "y[i] = q4o_double_to_bf16(silu * u[i]);",
      "y[i] = q4o_double_to_bf16((double)(float)silu * (double)(float)u[i]);"),
     ("residual subtracted", "s += q4o_bf16_to_double(r[t * N + n]);", "s -= q4o_bf16_to_double(r[t * N + n]);"),
+    ("Q5 code offset 15", "(double)(q - 16) * q4o_fp16_to_double", "(double)(q - 15) * q4o_fp16_to_double"),
+    ("Q5 high bits read from the top", "(hi[n * (K / 8) + k / 8] >> (k % 8)) & 1", "(hi[n * (K / 8) + k / 8] >> (7 - k % 8)) & 1"),
+    ("Q5 high plane stride", "(hi[n * (K / 8) + k / 8] >> (k % 8)) & 1", "(hi[n * (K / 16) + k / 8] >> (k % 8)) & 1"),
+    ("Q5 high bit weighted 8", "int q = low_nibble(lo, K, n, k) | (h << 4);\n        return (double)(q - 16)",
+     "int q = low_nibble(lo, K, n, k) | (h << 3);\n        return (double)(q - 16)"),
+    ("Q6 pairs packed as nibbles", "(hi[n * (K / 4) + k / 4] >> (2 * (k % 4))) & 3", "(hi[n * (K / 4) + k / 4] >> (k % 4)) & 3"),
+    ("Q6 code offset 16", "(double)(q - 32) * q4o_fp16_to_double", "(double)(q - 16) * q4o_fp16_to_double"),
+    ("W8 codes unsigned", "int c = (int)(int8_t)lo[n * K + k];", "int c = (int)lo[n * K + k];"),
+    ("W8 groups of 64", "s16[n * (K / 32) + k / 32]", "s16[n * (K / 32) + k / 64]"),
+    ("NVFP4 groups of 32", "s8[n * (K / 16) + k / 16]", "s8[n * (K / 16) + k / 32]"),
+    ("E2M1 subnormal as 1", "(e == 0) ? 0.5 * m", "(e == 0) ? 1.0 * m"),
+    ("E4M3 exponent bias 6", "ldexp((double)(m + 8), e - 10)", "ldexp((double)(m + 8), e - 9)"),
+    ("E4M3 subnormal scale", "ldexp((double)m, -9);           /* subnormal", "ldexp((double)m, -10);           /* subnormal"),
+    ("BF16 weight row stride", "return q4o_bf16_to_double(w[n * K + k]);", "return q4o_bf16_to_double(w[(n * K + k) / 2 * 2]);"),
+    ("Q5 byte count 40", "return n * (k / 64) * 42;", "return n * (k / 64) * 40;"),
+    ("sampled format path reads the wrong token", "fmt_weight(fmt, lo, hi, sc, K, ns[i], k) * q4o_bf16_to_double(x[ts[i] * K + k]);",
+     "fmt_weight(fmt, lo, hi, sc, K, ns[i], k) * q4o_bf16_to_double(x[k]);"),
     ("sampled path reads k-major",
      "acc += weight_value(codes, scales, K, n, k) * q4o_bf16_to_double(x[t * K + k]);",
      "acc += weight_value(codes, scales, K, n, k) * q4o_bf16_to_double(x[(k * 7 + t) % K]);"),
@@ -53,13 +71,13 @@ MUTANTS = [
 
 
 def _catches(o):
-    failures = []
-    for pin in oracle_pins.ALL_PINS:
+    """Name of the first pin that fails on oracle `o` (None if every pin passes)."""
+    for pin in oracle_pins.ALL_PINS + oracle_pins_fmt.ALL_PINS:
         try:
             pin(o)
         except AssertionError:
-            failures.append(pin.__name__)
-    return failures
+            return pin.__name__
+    return None
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
