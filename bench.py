@@ -213,6 +213,83 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
+def fmt_weight_bytes(fmt, n, k):
+    """The pages' weight bytes of each format ("linear-benchmark.md" section 4)."""
+    per = {0: (34, 64), 1: (42, 64), 2: (50, 64), 3: (34, 32), 4: (9, 16)}
+    if fmt == 5:
+        return 2 * n * k
+    b, g = per[fmt]
+    return n * k // g * b
+
+
+def fmt_model_bytes(fmt, n, k, t):
+    return fmt_weight_bytes(fmt, n, k) + 2 * k * t + 2 * n * t
+
+
+class FmtPoint:
+    """Rotating buffer sets for one (format, N, K, T), like Point."""
+
+    def __init__(self, fmt, n, k, t, seed):
+        import torch
+        import weight_only_bit_q4_amd as q4
+        from weight_only_bit_q4_amd import inputs
+        self.fmt, self.n, self.k, self.t, self.q4, self.torch = fmt, n, k, t, q4, torch
+        w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, seed)
+        x = inputs.gen_x(k, t, seed)
+        self.nsets = max(2, int(math.ceil(ROTATE_BYTES / fmt_model_bytes(fmt, n, k, t))) + 1)
+        self.ws_bytes = max(q4.q4lin_fmt_workspace_bytes(fmt, n, k, t), 0)
+
+        def d(a):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a).reshape(-1).view(np.uint8).copy()).cuda()
+        xd, wd, hd, sd = d(x), d(w), d(hi), d(sc)
+        self.sets = []
+        for _ in range(self.nsets):
+            self.sets.append((xd.clone(), wd.clone(), None if hd is None else hd.clone(),
+                              None if sd is None else sd.clone(), torch.empty(t * n * 2, dtype=torch.uint8, device="cuda"),
+                              torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device="cuda")))
+        torch.cuda.synchronize()
+
+    def call(self, i, h):
+        x, w, hi, sc, y, ws = self.sets[i % self.nsets]
+        st = self.q4.q4lin_linear_fmt(self.fmt, x.data_ptr(), w.data_ptr(), 0 if hi is None else hi.data_ptr(),
+                                      0 if sc is None else sc.data_ptr(), y.data_ptr(), self.n, self.k, self.t,
+                                      ws.data_ptr() if self.ws_bytes else 0, self.ws_bytes, h)
+        if st != 0:
+            raise RuntimeError("q4lin_linear_fmt: " + self.q4.q4lin_status_string(st))
+
+    def free(self):
+        self.sets = []
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def formats_table(torch, points, repeats=5):
+    """Every weight format at the given (N, K, T) points: per-call time
+    (median of `repeats` graph replays), logical GB/s with the format's own
+    weight bytes, and READ_% against a streaming read of the same bytes."""
+    from weight_only_bit_q4_amd import inputs
+    ceil = {}
+    rows = []
+    for (n, k, t) in points:
+        for fmt in range(6):
+            mb = fmt_model_bytes(fmt, n, k, t)
+            if mb not in ceil:
+                ceil[mb] = read_ceiling(torch, mb)
+            p = FmtPoint(fmt, n, k, t, inputs.workload_seed("decode_6144x5120_t1") + 100 * fmt)
+            steps = max(20, min(500, int(2e-3 / max(1e-6, mb / 4e12))))
+            sec = _graph_period(torch, p.call, steps, repeats)
+            p.free()
+            rc_s, _ = ceil[mb]
+            gb = mb / sec / 1e9
+            row = {"format": inputs.FMT_NAMES[fmt], "n": n, "k": k, "t": t, "us": round(sec * 1e6, 3),
+                   "model_bytes": mb, "gbs": round(gb, 1), "hbm_frac": round(gb / HBM_PEAK_GBS, 4),
+                   "read_ceiling_us": round(rc_s * 1e6, 3), "read_pct": round(100.0 * rc_s / sec, 2),
+                   "tflops": round(useful_flops(n, k, t) / sec / 1e12, 3)}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+    return rows
+
+
 def cpu_baseline_t1(n, k, seed, budget_s=10.0, budget_1t_s=4.0):
     """The oracle, untuned, on the host cores: whole T=1 problems repeated
     for about `budget_s` seconds with all cores (OpenMP over rows), then for
@@ -504,6 +581,9 @@ def main(argv=None):
     ap.add_argument("--csv", type=str, default=None)
     ap.add_argument("--copy-calibration", type=int, default=None, metavar="BYTES",
                     help="run a plain copy of BYTES bytes (for scaling the byte counters), then exit")
+    ap.add_argument("--formats", action="store_true",
+                    help="every weight format (Q4/Q5/Q6/W8/NVFP4/BF16_CTRL) at 6144x5120 T=1 and 16, and the "
+                         "BF16_CTRL control row 14336x5120 T=1: time, GB/s, READ_%%")
     ap.add_argument("--trace-summary", type=str, default=None, metavar="CSV",
                     help="summarize a rocprofv3 kernel_trace.csv (per kernel and population), then exit")
     args = ap.parse_args(argv)
@@ -581,6 +661,10 @@ def main(argv=None):
 
     if args.ceilings:
         ceilings()
+        return 0
+
+    if args.formats:
+        formats_table(torch, [(n, k, 1), (n, k, 16), (14336, 5120, 1)], repeats=args.repeats)
         return 0
 
     if args.suite:

@@ -69,6 +69,7 @@ extern "C" {
 #define Q4LIN_E_WORKSPACE 4 /* workspace smaller than q4lin_workspace_bytes()     */
 #define Q4LIN_E_LAUNCH 5    /* the HIP runtime refused a kernel launch (e.g. the
                                current device is not a gfx950 GPU)               */
+#define Q4LIN_E_FORMAT 6    /* unknown weight format (q4lin_linear_fmt)          */
 
 /* Bytes of workspace q4lin_linear needs for this shape (0 when none), or a
  * negative status (-Q4LIN_E_SHAPE) for a shape outside the contract.  Pure
@@ -167,6 +168,58 @@ Q4LIN_API int q4lin_linear_noalloc(const void *x, const void *codes, const void 
  * (64 MiB): the largest q4lin_workspace_bytes() it accepts.  Pure host
  * function. */
 Q4LIN_API int64_t q4lin_noalloc_scratch_bytes(void);
+
+/* The other weight formats of the same A16 Linear ("linear-benchmark.md",
+ * section 0: the Q4/Q5/Q6/W8 and BF16_CTRL formats use the A16 routes, and
+ * NVFP4 supports A16; section 4, weight-format table: bytes per group).  The
+ * table gives only byte counts; the packing read here is the plainest one
+ * that matches them:
+ *
+ *   Q4LIN_FMT_Q4G64_F16S  q4lin_linear's weight (w = codes, w_hi unused).
+ *   Q4LIN_FMT_Q5G64_F16S  w: uint8 [N][K/2] low nibbles as Q4 (even k in the
+ *           low nibble); w_hi: uint8 [N][K/8], bit i of byte b is the high
+ *           bit of k = 8b + i; scales: fp16 [N][K/64].  q = low | high << 4
+ *           in 0..31, weight (q - 16) * scale.  42 bytes per 64 weights.
+ *   Q4LIN_FMT_Q6G64_F16S  w as Q5; w_hi: uint8 [N][K/4], bits 2i and 2i+1 of
+ *           byte b are the high pair of k = 4b + i; scales fp16 [N][K/64];
+ *           q in 0..63, weight (q - 32) * scale.  50 bytes per 64 weights.
+ *   Q4LIN_FMT_W8G32_F16S  w: int8 [N][K] (two's complement); scales: fp16
+ *           [N][K/32]; weight c * scale.  34 bytes per 32 weights.
+ *   Q4LIN_FMT_NVFP4  w: uint8 [N][K/2] of E2M1 codes (even k in the low
+ *           nibble); scales: uint8 [N][K/16] of E4M3 values (bias 7, no
+ *           infinities); weight E2M1 * E4M3.  9 bytes per 16 weights.  The
+ *           A4 policy (activations quantized to FP4 in the call) is not
+ *           offered.
+ *   Q4LIN_FMT_BF16  w: bf16 [N][K], the weights themselves (BF16_CTRL, the
+ *           dense control of the pages' bench); w_hi and scales unused.
+ *
+ * Alignment: x and w 16 bytes, y 2, w_hi 2 (Q5) or 4 (Q6), scales 2 (1 for
+ * NVFP4).  x and y as for q4lin_linear.  The sum is taken in binary32 and
+ * rounded once to bf16 (an output whose binary32 sums leave the range is
+ * formed again in binary64).
+ * Routes: Q4 as q4lin_linear; the others stream their weight once per
+ * 32 tokens on one workgroup per block of rows with K split across its
+ * waves (matrix cores on exact bf16 code values, the scale applied per
+ * group in binary32); no workspace (NULL and 0 are accepted).  Errors as for
+ * q4lin_linear, plus Q4LIN_E_FORMAT for an unknown format. */
+#define Q4LIN_FMT_Q4G64_F16S 0
+#define Q4LIN_FMT_Q5G64_F16S 1
+#define Q4LIN_FMT_Q6G64_F16S 2
+#define Q4LIN_FMT_W8G32_F16S 3
+#define Q4LIN_FMT_NVFP4 4
+#define Q4LIN_FMT_BF16 5
+Q4LIN_API int q4lin_linear_fmt(int fmt, const void *x, const void *w, const void *w_hi, const void *scales,
+                 void *y, int64_t n, int64_t k, int64_t t,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Weight bytes of an N x K matrix in format fmt, the pages' closed forms
+ * ("linear-benchmark.md", section 4: groups * bytes per group; 2 N K for
+ * BF16), or a negative status.  Pure host function. */
+Q4LIN_API int64_t q4lin_fmt_weight_bytes(int fmt, int64_t n, int64_t k);
+
+/* Workspace bytes q4lin_linear_fmt needs (q4lin_workspace_bytes for Q4, 0
+ * for the others), or a negative status.  Pure host function. */
+Q4LIN_API int64_t q4lin_fmt_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t t);
 
 /* Static, human-readable text for a status code (never NULL). */
 Q4LIN_API const char *q4lin_status_string(int status);

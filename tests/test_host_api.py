@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(0, 6):
+    for st in range(0, 7):
         assert q.q4lin_status_string(st)
     assert q.q4lin_status_string(99) == "unknown status"
 
@@ -224,3 +224,32 @@ def test_noalloc_scratch_size_and_rejections():
     for (n, k, t) in [(6144, 5120, 1024), (6144, 5120, 128), (14336, 5120, 1024), (34816, 5120, 1024),
                       (5120, 17408, 1024)]:
         assert 0 <= q.q4lin_workspace_bytes(n, k, t) <= cap, (n, k, t)
+
+
+# -- the weight-format entry point: host-side checks only ---------------------
+def test_fmt_weight_bytes_and_rejections():
+    n, k = 6144, 5120
+    assert q.q4lin_fmt_weight_bytes(q.Q4LIN_FMT_Q4G64_F16S, n, k) == 16_711_680
+    assert q.q4lin_fmt_weight_bytes(q.Q4LIN_FMT_Q5G64_F16S, n, k) == n * k // 64 * 42
+    assert q.q4lin_fmt_weight_bytes(q.Q4LIN_FMT_Q6G64_F16S, n, k) == n * k // 64 * 50
+    assert q.q4lin_fmt_weight_bytes(q.Q4LIN_FMT_W8G32_F16S, n, k) == n * k // 32 * 34
+    assert q.q4lin_fmt_weight_bytes(q.Q4LIN_FMT_NVFP4, n, k) == n * k // 16 * 9
+    assert q.q4lin_fmt_weight_bytes(q.Q4LIN_FMT_BF16, n, k) == 2 * n * k
+    assert q.q4lin_fmt_weight_bytes(9, n, k) == -q.Q4LIN_E_FORMAT
+    assert q.q4lin_fmt_weight_bytes(1, n, 100) == -q.Q4LIN_E_SHAPE
+    p = 0x10000
+    assert q.q4lin_linear_fmt(9, p, p, p, p, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_FORMAT
+    assert q.q4lin_status_string(q.Q4LIN_E_FORMAT) == "unknown weight format"
+    for f in (1, 2, 3, 4, 5):
+        assert q.q4lin_fmt_workspace_bytes(f, n, k, 1024) == 0
+        assert q.q4lin_linear_fmt(f, 0, 0, 0, 0, 0, 0, 128, 4, 0, 0, 0) == q.Q4LIN_OK      # empty
+        assert q.q4lin_linear_fmt(f, p, p, p, p, p, 64, 96, 1, 0, 0, 0) == q.Q4LIN_E_SHAPE
+        assert q.q4lin_linear_fmt(f, 0, p, p, p, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_NULL
+        assert q.q4lin_linear_fmt(f, p + 8, p, p, p, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
+    # planes a format has are required; the ones it lacks may be NULL
+    assert q.q4lin_linear_fmt(q.Q4LIN_FMT_Q5G64_F16S, p, p, 0, p, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_NULL
+    assert q.q4lin_linear_fmt(q.Q4LIN_FMT_W8G32_F16S, p, p, p, 0, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_NULL
+    assert q.q4lin_linear_fmt(q.Q4LIN_FMT_Q6G64_F16S, p, p, p + 2, p, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
+    # Q4 goes through q4lin_linear's checks and workspace
+    assert q.q4lin_fmt_workspace_bytes(0, n, k, 1024) == q.q4lin_workspace_bytes(n, k, 1024)
+    assert q.q4lin_linear_fmt(0, p, p, 0, p, p, n, k, 1024, p, 16, 0) == q.Q4LIN_E_WORKSPACE

@@ -1,0 +1,165 @@
+"""The other weight formats (Q5G64_F16S, Q6G64_F16S, W8G32_F16S, NVFP4 A16,
+BF16_CTRL) on the GPU against the oracle, through the C ABI
+(q4lin_linear_fmt): hand-worked examples bit for bit, seeded problems of the
+workload's shape at T = 1 and 16 and ragged shapes element by element, the
+offset codes' exact zeros, wide-range scales, inputs preserved and writes
+confined to y."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins_fmt
+from gpu_util import announce, assert_close, dev, host_bits, sample_indices, torch
+from weight_only_bit_q4_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [inputs.FMT_Q5, inputs.FMT_Q6, inputs.FMT_W8, inputs.FMT_NVFP4, inputs.FMT_BF16]
+FMT_IDS = [inputs.FMT_NAMES[f] for f in FMTS]
+# examples whose exact sum needs more than binary32 (held to the tolerance)
+FP32_INEXACT = {"BF16_single_rounding"}
+
+
+def _bytes_dev(a):
+    a = np.ascontiguousarray(a)
+    return torch().from_numpy(a.reshape(-1).view(np.uint8).copy()).cuda()
+
+
+def run_fmt(fmt, x, w, hi, sc, n, k, t, y=None, what=""):
+    import weight_only_bit_q4_amd as q4
+    th = torch()
+    announce("%s q4lin_linear_fmt fmt=%d n=%d k=%d t=%d" % (what, fmt, n, k, t))
+    xd = dev(np.asarray(x, dtype=np.uint16).reshape(t, k))
+    wd = _bytes_dev(w).view(n, -1)
+    hd = _bytes_dev(hi) if hi is not None else None
+    sd = _bytes_dev(sc) if sc is not None else None
+    yd = q4.linear_fmt(fmt, xd, wd, hd, sd, y=y)
+    th.cuda.synchronize()
+    return host_bits(yd)
+
+
+@pytest.mark.parametrize("replicate", [1, 3, 20, 40], ids=["t1", "t3", "t20", "t40"])
+def test_fmt_worked_examples(replicate):
+    for ex in oracle_pins_fmt.load_examples():
+        fmt, x, lo, hi, sc, want = oracle_pins_fmt.materialize(ex)
+        n, k, t = ex["n"], ex["k"], ex["t"]
+        xr = np.tile(x, (replicate, 1))
+        got = run_fmt(fmt, xr, lo, hi, sc, n, k, t * replicate, what=ex["name"])
+        want_r = np.tile(want.reshape(t, n), (replicate, 1))
+        if ex["name"] in FP32_INEXACT:
+            assert_close(got, want_r, what=ex["name"])
+        else:
+            assert np.array_equal(got.reshape(-1), want_r.reshape(-1)), (
+                ex["name"], [hex(v) for v in got.reshape(-1)[:8]], [hex(v) for v in want_r.reshape(-1)[:8]])
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("t", [1, 16])
+def test_fmt_6144x5120(fmt, t):
+    n, k = 6144, 5120
+    seed = inputs.workload_seed("decode_6144x5120_t1") + 100 * fmt
+    w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, seed)
+    x = inputs.gen_x(k, t, seed)
+    got = run_fmt(fmt, x, w, hi, sc, n, k, t, what="6144x5120")
+    assert_close(got, oracle.linear_fmt(fmt, x, w, hi, sc, n, k, t), what="%s T=%d" % (inputs.FMT_NAMES[fmt], t))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("n,k,t", [(1, 64, 1), (7, 64, 3), (97, 320, 5), (300, 1088, 17), (1000, 2048, 33),
+                                   (4100, 704, 32), (20000, 256, 2)])
+def test_fmt_ragged(fmt, n, k, t):
+    w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, 300 + n + k + t)
+    x = inputs.gen_x(k, t, 300 + t)
+    got = run_fmt(fmt, x, w, hi, sc, n, k, t, what="ragged")
+    assert_close(got, oracle.linear_fmt(fmt, x, w, hi, sc, n, k, t),
+                 what="%s %dx%d T=%d" % (inputs.FMT_NAMES[fmt], n, k, t))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_fmt_prefill_t1024_sampled(fmt):
+    """T = 1024 runs the kernel once per 32 tokens; sampled outputs and the
+    token-run boundaries against the oracle."""
+    n, k, t = 6144, 5120, 1024
+    seed = inputs.workload_seed("prefill_6144x5120_t1024") + 100 * fmt
+    w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, seed)
+    x = inputs.gen_x(k, t, seed)
+    got = run_fmt(fmt, x, w, hi, sc, n, k, t, what="prefill")
+    ns, ts = sample_indices(n, t, 1500, seed, (15, 16, 255, 256, n - 1), (31, 32, 33, 511, 512, 1023))
+    ref = oracle.linear_fmt_at(fmt, x, w, hi, sc, n, k, t, ns, ts)
+    assert_close(got[ts, ns], ref, what="%s T=1024 sampled" % inputs.FMT_NAMES[fmt])
+
+
+@pytest.mark.parametrize("t", [1, 20])
+def test_fmt_offset_codes_give_exact_zeros(t):
+    n, k = 96, 640
+    x = inputs.gen_x(k, t, 77)
+    cases = {
+        inputs.FMT_Q5: (np.zeros((n, k // 2), np.uint8), np.full((n, k // 8), 0xFF, np.uint8)),
+        inputs.FMT_Q6: (np.zeros((n, k // 2), np.uint8), np.full((n, k // 4), 0xAA, np.uint8)),
+        inputs.FMT_W8: (np.zeros((n, k), np.uint8), None),
+        inputs.FMT_NVFP4: (np.full((n, k // 2), 0x88, np.uint8), None),   # E2M1 -0
+    }
+    for fmt, (w, hi) in cases.items():
+        _, _, sc = inputs.gen_fmt_weight(fmt, n, k, 78)
+        got = run_fmt(fmt, x, w, hi, sc, n, k, t, what="offset codes")
+        assert np.all((got & 0x7FFF) == 0), inputs.FMT_NAMES[fmt]
+
+
+@pytest.mark.parametrize("fmt", [inputs.FMT_Q5, inputs.FMT_Q6, inputs.FMT_W8], ids=["Q5", "Q6", "W8"])
+def test_fmt_wide_range_scales(fmt):
+    """fp16 scales over many binades (subnormal, negative, zero) and
+    activations over many binades."""
+    n, k, t = 64, 1024, 9
+    r = np.random.default_rng(5 + fmt)
+    w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, 91)
+    m = sc.size
+    sv = r.choice([-1, 1], size=m) * np.ldexp(r.uniform(1, 2, m), r.integers(-24, 12, m))
+    sv[r.random(m) < 0.05] = 0.0
+    sc = sv.astype(np.float16).view(np.uint16).reshape(sc.shape)
+    xv = (r.standard_normal((t, k)) * np.ldexp(1.0, r.integers(-20, 20, (t, k)))).astype(np.float32)
+    x = inputs.f32_to_bf16_bits(xv)
+    got = run_fmt(fmt, x, w, hi, sc, n, k, t, what="wide range")
+    assert_close(got, oracle.linear_fmt(fmt, x, w, hi, sc, n, k, t), what="wide range %s" % inputs.FMT_NAMES[fmt])
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_fmt_inputs_preserved_and_output_guarded(fmt):
+    import hashlib
+    import weight_only_bit_q4_amd as q4
+    th = torch()
+    n, k, t = 400, 768, 20
+    w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, 4242)
+    x = inputs.gen_x(k, t, 4242)
+    xd, wd = dev(x), _bytes_dev(w)
+    hd = _bytes_dev(hi) if hi is not None else None
+    sd = _bytes_dev(sc) if sc is not None else None
+    ins = [v for v in (xd, wd, hd, sd) if v is not None]
+
+    def digest(v):
+        return hashlib.sha256(v.cpu().contiguous().view(th.uint8).numpy().tobytes()).hexdigest()
+
+    before = [digest(v) for v in ins]
+    pad, canary = 4096, 0x5A5A
+    buf = th.full((t * n + 2 * pad,), canary, dtype=th.int16, device="cuda")
+    y = buf[pad:pad + t * n]
+    announce("guard q4lin_linear_fmt fmt=%d n=%d k=%d t=%d" % (fmt, n, k, t))
+    st = q4.q4lin_linear_fmt(fmt, xd.data_ptr(), wd.data_ptr(), hd.data_ptr() if hd is not None else 0,
+                             sd.data_ptr() if sd is not None else 0, y.data_ptr(), n, k, t, 0, 0,
+                             th.cuda.current_stream().cuda_stream)
+    assert st == 0, q4.q4lin_status_string(st)
+    th.cuda.synchronize()
+    assert [digest(v) for v in ins] == before
+    h = buf.cpu().numpy()
+    assert np.all(h[:pad] == canary) and np.all(h[pad + t * n:] == canary)
+    assert_close(host_bits(y).reshape(t, n), oracle.linear_fmt(fmt, x, w, hi, sc, n, k, t), what="guarded")
+
+
+def test_fmt_q4_is_q4lin_linear():
+    """Format 0 through q4lin_linear_fmt is q4lin_linear, bit for bit."""
+    import weight_only_bit_q4_amd as q4
+    n, k, t = 512, 1024, 70
+    x, c, s = inputs.gen_problem(n, k, t, 12)
+    a = run_fmt(inputs.FMT_Q4, x, c, None, s, n, k, t, what="fmt Q4")
+    xd, cd, sd = dev(x), dev(c), dev(s)
+    b = host_bits(q4.linear(xd, cd, sd))
+    assert np.array_equal(a, b)

@@ -26,6 +26,14 @@ Q4LIN_E_SHAPE = 2
 Q4LIN_E_ALIGN = 3
 Q4LIN_E_WORKSPACE = 4
 Q4LIN_E_LAUNCH = 5
+Q4LIN_E_FORMAT = 6
+
+Q4LIN_FMT_Q4G64_F16S = 0
+Q4LIN_FMT_Q5G64_F16S = 1
+Q4LIN_FMT_Q6G64_F16S = 2
+Q4LIN_FMT_W8G32_F16S = 3
+Q4LIN_FMT_NVFP4 = 4
+Q4LIN_FMT_BF16 = 5
 
 Q4LIN_ROUTE_NONE = 0
 Q4LIN_ROUTE_GEMV = 1
@@ -36,7 +44,8 @@ Q4LIN_ROUTE_DECODE = 4
 EXPORTED = ("q4lin_workspace_bytes", "q4lin_linear", "q4lin_linear_add", "q4lin_linear_pair",
             "q4lin_pair_workspace_bytes", "q4lin_linear_swiglu", "q4lin_swiglu_workspace_bytes",
             "q4lin_status_string", "q4lin_route", "q4lin_version", "q4lin_linear_noalloc",
-            "q4lin_noalloc_scratch_bytes")
+            "q4lin_noalloc_scratch_bytes", "q4lin_linear_fmt", "q4lin_fmt_weight_bytes",
+            "q4lin_fmt_workspace_bytes")
 
 
 class Q4LinError(RuntimeError):
@@ -84,6 +93,13 @@ def _load() -> ctypes.CDLL:
     lib.q4lin_linear_noalloc.restype = ctypes.c_int
     lib.q4lin_noalloc_scratch_bytes.argtypes = []
     lib.q4lin_noalloc_scratch_bytes.restype = i64
+    ci = ctypes.c_int
+    lib.q4lin_linear_fmt.argtypes = [ci, vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.q4lin_linear_fmt.restype = ci
+    lib.q4lin_fmt_weight_bytes.argtypes = [ci, i64, i64]
+    lib.q4lin_fmt_weight_bytes.restype = i64
+    lib.q4lin_fmt_workspace_bytes.argtypes = [ci, i64, i64, i64]
+    lib.q4lin_fmt_workspace_bytes.restype = i64
     return lib
 
 
@@ -151,6 +167,22 @@ def q4lin_linear_noalloc(x: int, codes: int, scales: int, y: int, n: int, k: int
 
 def q4lin_noalloc_scratch_bytes() -> int:
     return int(load().q4lin_noalloc_scratch_bytes())
+
+
+def q4lin_linear_fmt(fmt: int, x: int, w: int, w_hi: int, scales: int, y: int, n: int, k: int, t: int,
+                     workspace: int, workspace_bytes: int, stream: int) -> int:
+    """Raw call of the weight-format entry point (Q4LIN_FMT_*); returns the status."""
+    return int(load().q4lin_linear_fmt(int(fmt), x or None, w or None, w_hi or None, scales or None, y or None,
+                                       int(n), int(k), int(t), workspace or None, int(workspace_bytes),
+                                       stream or None))
+
+
+def q4lin_fmt_weight_bytes(fmt: int, n: int, k: int) -> int:
+    return int(load().q4lin_fmt_weight_bytes(int(fmt), int(n), int(k)))
+
+
+def q4lin_fmt_workspace_bytes(fmt: int, n: int, k: int, t: int) -> int:
+    return int(load().q4lin_fmt_workspace_bytes(int(fmt), int(n), int(k), int(t)))
 
 
 def q4lin_status_string(status: int) -> str:
@@ -282,6 +314,38 @@ def linear_swiglu(x, codes_gate, scales_gate, codes_up, scales_up, y=None, works
         stream = torch.cuda.current_stream(x.device).cuda_stream
     st = q4lin_linear_swiglu(x.data_ptr(), codes_gate.data_ptr(), scales_gate.data_ptr(), codes_up.data_ptr(),
                              scales_up.data_ptr(), y.data_ptr(), n, k, t, ws_ptr, ws_bytes, stream)
+    if st != Q4LIN_OK:
+        raise Q4LinError(st)
+    return y
+
+
+def linear_fmt(fmt, x, w, w_hi=None, scales=None, y=None, stream=None):
+    """Y = W x X for a weight in format ``fmt`` (Q4LIN_FMT_*) on torch device
+    tensors: ``x`` ``[T, K]`` bf16 bits; ``w``, ``w_hi``, ``scales`` the
+    format's planes as laid out in ``include/q4lin.h`` (any dtype, read as
+    bytes; ``w`` gives N as its first dimension).  Returns ``y`` ``[T, N]``."""
+    import torch
+
+    t, k = x.shape
+    n = w.shape[0]
+    if not x.is_contiguous() or x.element_size() != 2:
+        raise ValueError("x must be contiguous with 2-byte elements")
+    for name, ten in (("w", w), ("w_hi", w_hi), ("scales", scales)):
+        if ten is not None and not ten.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if y is None:
+        y = torch.empty((t, n), dtype=torch.bfloat16, device=x.device)
+    if tuple(y.shape) != (t, n) or y.element_size() != 2 or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [T, N] tensor of 2-byte elements")
+    need = q4lin_fmt_workspace_bytes(fmt, n, k, t)
+    if need < 0:
+        raise Q4LinError(-need)
+    ws = torch.empty(need, dtype=torch.uint8, device=x.device) if need > 0 else None
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = q4lin_linear_fmt(fmt, x.data_ptr(), w.data_ptr(), w_hi.data_ptr() if w_hi is not None else 0,
+                          scales.data_ptr() if scales is not None else 0, y.data_ptr(), n, k, t,
+                          ws.data_ptr() if ws is not None else 0, need, stream)
     if st != Q4LIN_OK:
         raise Q4LinError(st)
     return y

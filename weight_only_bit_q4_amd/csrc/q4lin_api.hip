@@ -41,6 +41,10 @@ constexpr int64_t kMaxT = int64_t(1) << 21;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxBytes = int64_t(1) << 40;
 constexpr size_t kGemvLdsLimit = 64 * 1024;
+static_assert(q4lin::FMT_Q5 == Q4LIN_FMT_Q5G64_F16S && q4lin::FMT_Q6 == Q4LIN_FMT_Q6G64_F16S &&
+                  q4lin::FMT_W8 == Q4LIN_FMT_W8G32_F16S && q4lin::FMT_NVFP4 == Q4LIN_FMT_NVFP4 &&
+                  q4lin::FMT_BF16 == Q4LIN_FMT_BF16,
+              "the kernels' format numbers are the header's");
 
 bool shape_ok(int64_t n, int64_t k, int64_t t) {
   if (n < 0 || t < 0 || k < 64 || (k % 64) != 0) return false;
@@ -188,6 +192,50 @@ extern "C" {
 
 int64_t q4lin_noalloc_scratch_bytes(void) { return (int64_t)kScratchBytes; }
 
+int64_t q4lin_fmt_weight_bytes(int fmt, int64_t n, int64_t k) {
+  if (n < 0 || k < 64 || (k % 64) != 0 || n > kMaxN || k > kMaxK) return -Q4LIN_E_SHAPE;
+  switch (fmt) {
+    case Q4LIN_FMT_Q4G64_F16S: return n * (k / 64) * 34;
+    case Q4LIN_FMT_Q5G64_F16S: return n * (k / 64) * 42;
+    case Q4LIN_FMT_Q6G64_F16S: return n * (k / 64) * 50;
+    case Q4LIN_FMT_W8G32_F16S: return n * (k / 32) * 34;
+    case Q4LIN_FMT_NVFP4: return n * (k / 16) * 9;
+    case Q4LIN_FMT_BF16: return 2 * n * k;
+    default: return -Q4LIN_E_FORMAT;
+  }
+}
+
+int64_t q4lin_fmt_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t t) {
+  if (fmt == Q4LIN_FMT_Q4G64_F16S) return q4lin_workspace_bytes(n, k, t);
+  if (fmt < Q4LIN_FMT_Q5G64_F16S || fmt > Q4LIN_FMT_BF16) return -Q4LIN_E_FORMAT;
+  if (!shape_ok(n, k, t) || 2 * n * k >= kMaxBytes) return -Q4LIN_E_SHAPE;
+  return 0;
+}
+
+int q4lin_linear_fmt(int fmt, const void* x, const void* w, const void* w_hi, const void* scales, void* y,
+                     int64_t n, int64_t k, int64_t t, void* workspace, size_t workspace_bytes, void* stream) {
+  if (fmt == Q4LIN_FMT_Q4G64_F16S)
+    return q4lin_linear(x, w, scales, y, n, k, t, workspace, workspace_bytes, stream);
+  if (fmt < Q4LIN_FMT_Q5G64_F16S || fmt > Q4LIN_FMT_BF16) return Q4LIN_E_FORMAT;
+  if (!shape_ok(n, k, t) || 2 * n * k >= kMaxBytes) return Q4LIN_E_SHAPE;
+  if (n == 0 || t == 0) return Q4LIN_OK;
+  const bool has_hi = fmt == Q4LIN_FMT_Q5G64_F16S || fmt == Q4LIN_FMT_Q6G64_F16S;
+  const bool has_sc = fmt != Q4LIN_FMT_BF16;
+  if (!x || !w || !y || (has_hi && !w_hi) || (has_sc && !scales)) return Q4LIN_E_NULL;
+  const uintptr_t hi_align = fmt == Q4LIN_FMT_Q5G64_F16S ? 2 : 4;
+  const uintptr_t sc_align = fmt == Q4LIN_FMT_NVFP4 ? 1 : 2;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 2) || (has_hi && !aligned(w_hi, hi_align)) ||
+      (has_sc && !aligned(scales, sc_align)))
+    return Q4LIN_E_ALIGN;
+  q4lin::FmtPlan plan;
+  if (!q4lin::fmt_plan(fmt, n, k, t, &plan)) return Q4LIN_E_SHAPE;
+  (void)workspace;
+  (void)workspace_bytes;
+  const q4lin::FmtArgs a{fmt, x, w, w_hi, scales, y, n, k, t};
+  const hipError_t e = q4lin::launch_fmt(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+}
+
 int q4lin_linear_noalloc(const void* x, const void* codes, const void* scales, void* y,
                          int64_t n, int64_t k, int64_t t, void* stream) {
   int route = Q4LIN_ROUTE_NONE;
@@ -331,6 +379,7 @@ const char* q4lin_status_string(int status) {
     case Q4LIN_E_ALIGN: return "pointer misaligned (x, codes: 16 B; scales, y, residual: 2 B; workspace: 256 B)";
     case Q4LIN_E_WORKSPACE: return "workspace smaller than q4lin_workspace_bytes()";
     case Q4LIN_E_LAUNCH: return "kernel launch failed";
+    case Q4LIN_E_FORMAT: return "unknown weight format";
     default: return "unknown status";
   }
 }

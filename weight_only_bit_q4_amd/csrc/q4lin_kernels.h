@@ -127,4 +127,25 @@ hipError_t launch_tiled_f32(const TiledArgs& a, SumSource* src, hipStream_t stre
 hipError_t launch_swiglu_combine(const SumSource& g, const SumSource& u, void* y, int64_t n, int64_t t,
                                  hipStream_t stream);
 
+// The other weight formats (few-token route, any T in runs of 32 tokens).
+// Format numbers as in the public header's Q4LIN_FMT_* values.
+enum { FMT_Q4 = 0, FMT_Q5 = 1, FMT_Q6 = 2, FMT_W8 = 3, FMT_NVFP4 = 4, FMT_BF16 = 5 };
+struct FmtArgs {
+  int fmt;
+  const void* x;
+  const void* lo;  // code plane (BF16_CTRL: the weights)
+  const void* hi;  // high plane (Q5, Q6), else unused
+  const void* sc;  // scale plane (fp16, or E4M3 bytes for NVFP4; unused for BF16_CTRL)
+  void* y;
+  int64_t n, k, t;
+};
+struct FmtPlan {
+  int bn;      // rows per workgroup
+  int ct;      // 16-row column tiles per wave
+  int blocks;  // workgroups
+  size_t lds_bytes;
+};
+bool fmt_plan(int fmt, int64_t n, int64_t k, int64_t t, FmtPlan* p);
+hipError_t launch_fmt(const FmtArgs& a, hipStream_t stream);
+
 }  // namespace q4lin

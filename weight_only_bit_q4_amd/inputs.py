@@ -67,6 +67,43 @@ def gen_x(k: int, t: int, seed: int) -> np.ndarray:
     return f32_to_bf16_bits(v)
 
 
+# The other weight formats (the weight-format table of "linear-benchmark.md"
+# section 4), numbered as the library's Q4LIN_FMT_* values; the plane layouts
+# are the ones stated in include/q4lin.h.
+FMT_Q4, FMT_Q5, FMT_Q6, FMT_W8, FMT_NVFP4, FMT_BF16 = range(6)
+FMT_NAMES = {FMT_Q4: "Q4G64_F16S", FMT_Q5: "Q5G64_F16S", FMT_Q6: "Q6G64_F16S", FMT_W8: "W8G32_F16S",
+             FMT_NVFP4: "NVFP4", FMT_BF16: "BF16_CTRL"}
+
+
+def gen_fmt_weight(fmt: int, n: int, k: int, seed: int):
+    """(w, w_hi, scales) planes of an N x K weight in format ``fmt``, seeded:
+    code bytes uniform (every code equally likely; W8 bytes uniform in
+    -128..127), high planes uniform, fp16 scales uniform in [2^-7, 2^-5]
+    (one per 64 weights, per 32 for W8), NVFP4 E4M3 scales uniform over the
+    positive encodings with exponent field 4..9 (about 2^-3..2^2); BF16
+    weights N(0, 1/16^2) rounded to bf16.  Planes that a format lacks are
+    None."""
+    r = _rng(seed, STREAM_CODES)
+    if fmt == FMT_Q4:
+        return gen_codes(n, k, seed), None, gen_scales(n, k, seed)
+    if fmt in (FMT_Q5, FMT_Q6):
+        lo = r.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        hi = r.integers(0, 256, size=(n, k // (8 if fmt == FMT_Q5 else 4)), dtype=np.uint8)
+        return lo, hi, gen_scales(n, k, seed)
+    if fmt == FMT_W8:
+        w = r.integers(0, 256, size=(n, k), dtype=np.uint8)
+        s = _rng(seed, STREAM_SCALES).uniform(2.0 ** -7, 2.0 ** -5, size=(n, k // 32))
+        return w, None, s.astype(np.float16).view(np.uint16)
+    if fmt == FMT_NVFP4:
+        w = r.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        s = _rng(seed, STREAM_SCALES).integers(0x20, 0x50, size=(n, k // 16), dtype=np.uint8)
+        return w, None, s
+    if fmt == FMT_BF16:
+        v = r.standard_normal(size=(n, k), dtype=np.float32) * np.float32(1.0 / 16)
+        return f32_to_bf16_bits(v), None, None
+    raise ValueError("unknown format %r" % (fmt,))
+
+
 @dataclass(frozen=True)
 class Problem:
     n: int
