@@ -531,8 +531,10 @@ def trace_summary(path):
     population: calls that follow another call of the op back to back
     ('back_to_back': graph replays) and calls that follow any other kernel
     ('after_other': the cold single calls behind a cache flush, and the first
-    call of each replay).  Prints one markdown table row per (kernel,
-    population) with count, median, min, p95 and mean in ns."""
+    call of each replay).  The op's kernels and the benchmark's read probe
+    are listed (torch's and the runtime's own kernels are not).  Prints one
+    markdown table row per (kernel, population) with count, median, min, p95
+    and mean in ns."""
     import csv
     rows = []
     with open(path, newline="") as f:
@@ -542,14 +544,14 @@ def trace_summary(path):
     groups = {}
     prev = None
     for (a, b, name) in rows:
-        pop = "back_to_back" if prev is not None and prev.startswith("q4lin") else "after_other"
-        short = name.split("(")[0]
+        short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0].strip()
+        pop = "back_to_back" if prev == short else "after_other"
         groups.setdefault((short, pop), []).append(b - a)
         prev = short
     print("| kernel | population | calls | median ns | min ns | p95 ns | mean ns |")
     print("|---|---|---|---|---|---|---|")
     for (name, pop), d in sorted(groups.items(), key=lambda kv: (-len(kv[1]), kv[0])):
-        if not name.startswith("q4lin"):
+        if name.startswith("at::") or "rocclr" in name:
             continue
         a = np.asarray(d, dtype=np.float64)
         print("| %s | %s | %d | %.0f | %.0f | %.0f | %.1f |" % (name, pop, a.size, np.median(a), a.min(),
