@@ -232,6 +232,7 @@ Q4LIN_API const char *q4lin_status_string(int status);
 #define Q4LIN_ROUTE_SKINNY 2 /* small T: W streamed once, matrix cores, K split */
 #define Q4LIN_ROUTE_TILED 3  /* large T: LDS-tiled matrix-core GEMM            */
 #define Q4LIN_ROUTE_DECODE 4 /* one token: one weight stream per CU, K split   */
+#define Q4LIN_ROUTE_MID 5    /* medium T: row blocks x K slices, matrix cores  */
 Q4LIN_API int q4lin_route(int64_t n, int64_t k, int64_t t);
 
 /* Library version as major*10000 + minor*100 + patch. */

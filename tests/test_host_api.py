@@ -93,14 +93,20 @@ def test_routes_and_workspace_sizes():
     assert q.q4lin_workspace_bytes(6144, 5120, 1) == 0
     for t in (1, 2, 3, 4, 5, 16, 64, 128, 512, 1024):
         r = q.q4lin_route(6144, 5120, t)
-        assert r in (q.Q4LIN_ROUTE_DECODE, q.Q4LIN_ROUTE_GEMV, q.Q4LIN_ROUTE_SKINNY, q.Q4LIN_ROUTE_TILED)
+        assert r in (q.Q4LIN_ROUTE_DECODE, q.Q4LIN_ROUTE_GEMV, q.Q4LIN_ROUTE_SKINNY, q.Q4LIN_ROUTE_TILED,
+                     q.Q4LIN_ROUTE_MID)
         ws = q.q4lin_workspace_bytes(6144, 5120, t)
         if r == q.Q4LIN_ROUTE_TILED:
             # float16 activations padded to 32 tokens plus one int32 per token
             tp = (t + 31) // 32 * 32
             assert ws >= tp * 5120 * 2 + tp * 4
+        elif r == q.Q4LIN_ROUTE_MID:
+            # binary32 partials of the K slices, [S][T][N]
+            assert ws % (t * 6144 * 4) == 0 and 0 <= ws // (t * 6144 * 4) <= 8
         else:
             assert ws == 0
+    for t in (33, 64, 65, 128):
+        assert q.q4lin_route(6144, 5120, t) == q.Q4LIN_ROUTE_MID
     assert q.q4lin_route(6144, 5120, 1024) == q.Q4LIN_ROUTE_TILED
 
 

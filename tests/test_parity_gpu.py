@@ -158,6 +158,9 @@ def test_large_shapes(shape, t):
     # ragged rows; 2 splits of 13 and 14 groups (the second starts at an odd
     # group, so its scales sit in the other halves of their dwords)
     (1000, 5120, 40), (700, 1728, 60), (4000, 1344, 100),
+    # medium-T route: row blocks of 96, odd group counts per slice, one slice,
+    # every token-tile shape, rows and tokens ragged
+    (97, 192, 33), (6100, 320, 64), (95, 5120, 65), (1, 128, 128), (20000, 640, 77), (193, 4160, 127),
 ])
 def test_ragged_shapes(n, k, t):
     x, c, s = inputs.gen_problem(n, k, t, 1000 + n + k + t)
@@ -236,9 +239,10 @@ def test_wide_range_scales_and_activations(t):
     assert_close(got, oracle_full(x, c, s, n, k, t), what="wide range T=%d" % t)
 
 
-@pytest.mark.parametrize("n,k,ts", [(32, 128, (1, 3, 17, 40)), (200, 1280, (40,))],
-                         ids=["one_split", "k_split"])
-def test_extreme_magnitudes_finite_and_infinite(n, k, ts):
+@pytest.mark.parametrize("n,k,ts,route", [(32, 128, (1, 3, 17, 40), None), (200, 1280, (200,), 3),
+                                           (200, 1280, (40, 100), 5)],
+                         ids=["one_split", "tiled_k_split", "mid_k_split"])
+def test_extreme_magnitudes_finite_and_infinite(n, k, ts, route):
     """Largest finite activations and scales: results overflow to +-Inf
     exactly where the exact sum does; nothing becomes NaN; every other output
     meets the tolerance.  T = 3 and 17 take the small-T route's rescaled
@@ -251,8 +255,11 @@ def test_extreme_magnitudes_finite_and_infinite(n, k, ts):
     the matrix cores float16 weights, whose roundings do not cancel, so those
     outputs first come out as +-Inf; the route forms every non-finite output
     again exactly, so they too must match.  The second shape splits K over
-    two workgroups per tile (about ten cancellations among its 4000 odd-row
-    outputs), so the same repair runs in the split-sum pass."""
+    two workgroups per tile (about fifty cancellations among its 20000
+    odd-row outputs), so the same repair runs in the split-sum pass; the
+    third runs the medium-T route, whose binary32 sums of 128 + q times
+    activations near the bf16 maximum overflow and are repaired the same
+    way."""
     import weight_only_bit_q4_amd as q4
     for t in ts:
         r = np.random.default_rng(9)
@@ -264,8 +271,8 @@ def test_extreme_magnitudes_finite_and_infinite(n, k, ts):
         got = run_op(x, c, s, n, k, t, what="extreme")
         want = oracle_full(x, c, s, n, k, t)
         assert not np.any(((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)), "NaN produced"
-        if k == 1280:
-            assert q4.q4lin_route(n, k, t) == q4.Q4LIN_ROUTE_TILED
+        if route is not None:
+            assert q4.q4lin_route(n, k, t) == route
         assert_close(got, want, what="extreme %dx%d T=%d" % (n, k, t))
 
 

@@ -40,6 +40,7 @@ Q4LIN_ROUTE_GEMV = 1
 Q4LIN_ROUTE_SKINNY = 2
 Q4LIN_ROUTE_TILED = 3
 Q4LIN_ROUTE_DECODE = 4
+Q4LIN_ROUTE_MID = 5
 
 EXPORTED = ("q4lin_workspace_bytes", "q4lin_linear", "q4lin_linear_add", "q4lin_linear_pair",
             "q4lin_pair_workspace_bytes", "q4lin_linear_swiglu", "q4lin_swiglu_workspace_bytes",

@@ -41,6 +41,8 @@ constexpr int64_t kMaxT = int64_t(1) << 21;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxBytes = int64_t(1) << 40;
 constexpr size_t kGemvLdsLimit = 64 * 1024;
+// the medium-T route takes T from here up to its plan's limit (128)
+constexpr int64_t kMidFirstT = 33;
 static_assert(q4lin::FMT_Q5 == Q4LIN_FMT_Q5G64_F16S && q4lin::FMT_Q6 == Q4LIN_FMT_Q6G64_F16S &&
                   q4lin::FMT_W8 == Q4LIN_FMT_W8G32_F16S && q4lin::FMT_NVFP4 == Q4LIN_FMT_NVFP4 &&
                   q4lin::FMT_BF16 == Q4LIN_FMT_BF16,
@@ -68,11 +70,15 @@ int pick_route(int64_t n, int64_t k, int64_t t) {
   if (t == 1 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
   if (q4lin::skinny_plan(n, k, t, &sp)) return Q4LIN_ROUTE_SKINNY;
   if (t <= 4 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
+  q4lin::MidPlan mp;
+  if (t >= kMidFirstT && q4lin::mid_plan(n, k, t, &mp)) return Q4LIN_ROUTE_MID;
   return Q4LIN_ROUTE_TILED;
 }
 
 size_t route_workspace(int route, int64_t n, int64_t k, int64_t t) {
-  return route == Q4LIN_ROUTE_TILED ? q4lin::tiled_workspace_bytes(n, k, t) : 0;
+  if (route == Q4LIN_ROUTE_TILED) return q4lin::tiled_workspace_bytes(n, k, t);
+  if (route == Q4LIN_ROUTE_MID) return q4lin::mid_workspace_bytes(n, k, t);
+  return 0;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -114,6 +120,8 @@ int run_linear(const void* x, const void* codes, const void* scales, const void*
     e = q4lin::launch_decode(ga, s);
   } else if (route == Q4LIN_ROUTE_SKINNY) {
     e = q4lin::launch_skinny(ga, s);
+  } else if (route == Q4LIN_ROUTE_MID) {
+    e = q4lin::launch_mid(ga, workspace, s);
   } else {
     q4lin::TiledArgs a{x, codes, scales, y, n, k, t, workspace, q4lin::tiled_pick_config(n, k, t), res};
     e = q4lin::launch_tiled(a, s);
@@ -129,7 +137,9 @@ size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 //   SPLIT: one launch per weight on the route chosen for N rows;
 //   TILED: the many-token route per weight, its raw sums left in the
 //          partials of a workspace half each.
-enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3 };
+//   MID:   the medium-T route per weight, binary32 sums, its split partials
+//          after the sums in each half.
+enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3, SW_MID = 4 };
 struct SwigluPlan {
   int mode;
   int route;
@@ -147,6 +157,8 @@ bool swiglu_plan(int64_t n, int64_t k, int64_t t, SwigluPlan* p) {
   if (r1 == Q4LIN_ROUTE_TILED && !q4lin::tiled_shape_ok(n, k, t)) return false;
   if (r1 == Q4LIN_ROUTE_TILED) {
     *p = SwigluPlan{SW_TILED, r1, al256(q4lin::tiled_workspace_bytes_f32(n, k, t))};
+  } else if (r1 == Q4LIN_ROUTE_MID) {
+    *p = SwigluPlan{SW_MID, r1, al256((size_t)(n * t * 4)) + al256(q4lin::mid_workspace_bytes(n, k, t))};
   } else {
     *p = SwigluPlan{SW_SPLIT, r1, al256((size_t)(n * t * 4))};
   }
@@ -293,6 +305,16 @@ int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scale
       q4lin::GemvArgs b{x, codes_up, scales_up, w1, n, k, t};
       b.f32 = true;
       e = launch_sums(p.route, b, s);
+    }
+  } else if (p.mode == SW_MID) {
+    const size_t sums = al256((size_t)(n * t * 4));
+    q4lin::GemvArgs a{x, codes_gate, scales_gate, w0, n, k, t};
+    a.f32 = true;
+    e = q4lin::launch_mid(a, w0 + sums, s);
+    if (e == hipSuccess) {
+      q4lin::GemvArgs b{x, codes_up, scales_up, w1, n, k, t};
+      b.f32 = true;
+      e = q4lin::launch_mid(b, w1 + sums, s);
     }
   } else {
     const q4lin::TiledConfig cfg = q4lin::tiled_pick_config(n, k, t);

@@ -53,6 +53,36 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// One output of the Q4 op formed again from its definition: per 64-group
+// the exact sum of (q - 8) x in binary64 (each product exact), times the
+// group's fp16 scale, summed over the groups in binary64 (plus the LinearAdd
+// residual), rounded to bf16.  The matrix-core routes call it, one thread per
+// output, for the rare outputs whose binary32 arithmetic came out non-finite
+// (terms near the top of the binary32 range that cancel, or a binary32 sum
+// that overflows although the exact sum does not); an output whose exact
+// value overflows bf16 comes out as the same infinity again.
+__device__ __attribute__((noinline)) inline uint16_t exact_q4_output(const uint16_t* __restrict__ x,
+                                                                     const uint8_t* __restrict__ codes,
+                                                                     const uint16_t* __restrict__ scales,
+                                                                     const uint16_t* res, int N, int K, int n,
+                                                                     int t) {
+  const int G = K >> 6;
+  const uint8_t* cr = codes + (size_t)n * (size_t)(K >> 1);
+  const uint16_t* xr = x + (size_t)t * (size_t)K;
+  double acc = 0.0;
+  for (int g = 0; g < G; ++g) {
+    double p = 0.0;
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t b = cr[32 * g + j];
+      p += (double)((int)(b & 15u) - 8) * (double)bf16_bits_to_f32(xr[64 * g + 2 * j]);
+      p += (double)((int)(b >> 4) - 8) * (double)bf16_bits_to_f32(xr[64 * g + 2 * j + 1]);
+    }
+    acc += (double)f16_bits_to_f32(scales[(size_t)n * (size_t)G + g]) * p;
+  }
+  if (res != nullptr) acc += (double)bf16_bits_to_f32(res[(size_t)t * (size_t)N + n]);
+  return f32_to_bf16_rne((float)acc);
+}
+
 template <int V>
 using Slot = std::integral_constant<int, V>;
 

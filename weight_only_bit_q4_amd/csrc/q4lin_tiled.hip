@@ -216,42 +216,6 @@ prep_act_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __re
   if (wave == 0 && sub == 0) texp[t] = e;
 }
 
-// ---------------------------------------------------------------------------
-// exact recomputation of one output
-// ---------------------------------------------------------------------------
-// The matrix cores see each weight rounded once to float16.  Where that
-// rounding matters beyond the stated accuracy, the result comes out of range:
-// terms near the top of the binary32 range that cancel exactly (their float16
-// roundings do not), or a running FP32 sum that overflows although the exact
-// sum does not.  Every output that rounds to a non-finite bf16 value is
-// therefore formed again from the inputs, one thread per output: per 64-group
-// the exact sum of (q - 8) x in binary64 (each product exact), times the
-// group's scale, summed over the groups in binary64 (with the residual of
-// LinearAdd), then rounded to bf16 -- the plain definition of the op.  An
-// output whose exact value overflows bf16 comes out as the same infinity
-// again.  Finite outputs never take this path, so it costs one bit test per
-// 16-byte store.
-__device__ __attribute__((noinline)) uint16_t exact_output(const uint16_t* __restrict__ x,
-                                                           const uint8_t* __restrict__ codes,
-                                                           const uint16_t* __restrict__ scales,
-                                                           const uint16_t* res, int N, int K, int n, int t) {
-  const int G = K >> 6;
-  const uint8_t* cr = codes + (size_t)n * (size_t)(K >> 1);
-  const uint16_t* xr = x + (size_t)t * (size_t)K;
-  double acc = 0.0;
-  for (int g = 0; g < G; ++g) {
-    double p = 0.0;
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t b = cr[32 * g + j];
-      p += (double)((int)(b & 15u) - 8) * (double)bf16_bits_to_f32(xr[64 * g + 2 * j]);
-      p += (double)((int)(b >> 4) - 8) * (double)bf16_bits_to_f32(xr[64 * g + 2 * j + 1]);
-    }
-    acc += (double)f16_bits_to_f32(scales[(size_t)n * (size_t)G + g]) * p;
-  }
-  if (res != nullptr) acc += (double)bf16_bits_to_f32(res[(size_t)t * (size_t)N + n]);
-  return f32_to_bf16_rne((float)acc);
-}
-
 // bit i of the result: bf16 value i of the 8 in v is Inf or NaN
 __device__ __forceinline__ uint32_t nonfinite8(u32x4_t v) {
   uint32_t m = 0;
@@ -872,10 +836,10 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
       if (t0 + tl < T) {
         u32x4_t v = *reinterpret_cast<const u32x4_t*>(otile + tl * BN + cn * 8);
         uint32_t bad = nonfinite8(v);
-        while (bad != 0u) {  // rare: recompute exactly (see exact_output)
+        while (bad != 0u) {  // rare: recompute exactly (exact_q4_output)
           const int i = __builtin_ctz(bad);
           bad &= bad - 1u;
-          const uint32_t h = exact_output(xraw, codes, scales, ADD ? res : nullptr, N, K, n0 + cn * 8 + i, t0 + tl);
+          const uint32_t h = exact_q4_output(xraw, codes, scales, ADD ? res : nullptr, N, K, n0 + cn * 8 + i, t0 + tl);
           v[i >> 1] = (i & 1) ? ((v[i >> 1] & 0xFFFFu) | (h << 16)) : ((v[i >> 1] & 0xFFFF0000u) | h);
         }
         *reinterpret_cast<u32x4_t*>(y + (size_t)(t0 + tl) * N + n0 + cn * 8) = v;
@@ -886,7 +850,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
       const int tl = c / BN, nl = c - tl * BN;
       if (t0 + tl < T && n0 + nl < N) {
         uint16_t v = otile[c];
-        if ((v & 0x7F80u) == 0x7F80u) v = exact_output(xraw, codes, scales, ADD ? res : nullptr, N, K, n0 + nl, t0 + tl);
+        if ((v & 0x7F80u) == 0x7F80u) v = exact_q4_output(xraw, codes, scales, ADD ? res : nullptr, N, K, n0 + nl, t0 + tl);
         y[(size_t)(t0 + tl) * N + n0 + nl] = v;
       }
     }
@@ -914,7 +878,7 @@ tiled_reduce_kernel(const float* __restrict__ part, const int* __restrict__ texp
   v = __builtin_ldexpf(v, texp[t] - rexp[n]);
   if (res != nullptr) v += bf16_bits_to_f32(res[i]);  // LinearAdd
   uint16_t h = f32_to_bf16_rne(v);
-  if ((h & 0x7F80u) == 0x7F80u) h = exact_output(xraw, codes, scales, res, N, K, n, t);  // rare
+  if ((h & 0x7F80u) == 0x7F80u) h = exact_q4_output(xraw, codes, scales, res, N, K, n, t);  // rare
   y[i] = h;
 }
 
