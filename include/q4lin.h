@@ -193,8 +193,8 @@ Q4LIN_API int64_t q4lin_noalloc_scratch_bytes(void);
  *   Q4LIN_FMT_BF16  w: bf16 [N][K], the weights themselves (BF16_CTRL, the
  *           dense control of the pages' bench); w_hi and scales unused.
  *
- * Alignment: x and w 16 bytes, y 2, w_hi 2 (Q5) or 4 (Q6), scales 2 (1 for
- * NVFP4).  x and y as for q4lin_linear.  The sum is taken in binary32 and
+ * Alignment: x and w 16 bytes, y 2, w_hi 4 (Q5) or 8 (Q6), scales 2 (NVFP4
+ * included).  x and y as for q4lin_linear.  The sum is taken in binary32 and
  * rounded once to bf16 (an output whose binary32 sums leave the range is
  * formed again in binary64).
  * Routes: Q4 as q4lin_linear; the others stream their weight once per

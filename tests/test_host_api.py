@@ -256,6 +256,9 @@ def test_fmt_weight_bytes_and_rejections():
     assert q.q4lin_linear_fmt(q.Q4LIN_FMT_Q5G64_F16S, p, p, 0, p, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_NULL
     assert q.q4lin_linear_fmt(q.Q4LIN_FMT_W8G32_F16S, p, p, p, 0, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_NULL
     assert q.q4lin_linear_fmt(q.Q4LIN_FMT_Q6G64_F16S, p, p, p + 2, p, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
+    assert q.q4lin_linear_fmt(q.Q4LIN_FMT_Q6G64_F16S, p, p, p + 4, p, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
+    assert q.q4lin_linear_fmt(q.Q4LIN_FMT_Q5G64_F16S, p, p, p + 2, p, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
+    assert q.q4lin_linear_fmt(q.Q4LIN_FMT_NVFP4, p, p, p, p + 1, p, 64, 128, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
     # Q4 goes through q4lin_linear's checks and workspace
     assert q.q4lin_fmt_workspace_bytes(0, n, k, 1024) == q.q4lin_workspace_bytes(n, k, 1024)
     assert q.q4lin_linear_fmt(0, p, p, 0, p, p, n, k, 1024, p, 16, 0) == q.Q4LIN_E_WORKSPACE

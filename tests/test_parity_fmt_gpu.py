@@ -66,13 +66,23 @@ def test_fmt_6144x5120(fmt, t):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("n,k,t", [(1, 64, 1), (7, 64, 3), (97, 320, 5), (300, 1088, 17), (1000, 2048, 33),
-                                   (4100, 704, 32), (20000, 256, 2)])
+                                   (4100, 704, 32), (20000, 256, 2), (4100, 8192, 3)])
 def test_fmt_ragged(fmt, n, k, t):
     w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, 300 + n + k + t)
     x = inputs.gen_x(k, t, 300 + t)
     got = run_fmt(fmt, x, w, hi, sc, n, k, t, what="ragged")
     assert_close(got, oracle.linear_fmt(fmt, x, w, hi, sc, n, k, t),
                  what="%s %dx%d T=%d" % (inputs.FMT_NAMES[fmt], n, k, t))
+
+
+def test_fmt_long_k_scale_table():
+    """K = 131072 in W8: a row's scales take 8 KiB, so a block holds 12 rows
+    instead of 13 (the LDS scale table is capped); every output compared."""
+    fmt, n, k, t = inputs.FMT_W8, 3100, 131072, 2
+    w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, 77)
+    x = inputs.gen_x(k, t, 78)
+    got = run_fmt(fmt, x, w, hi, sc, n, k, t, what="long K")
+    assert_close(got, oracle.linear_fmt(fmt, x, w, hi, sc, n, k, t), what="W8 3100x131072 T=2")
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)

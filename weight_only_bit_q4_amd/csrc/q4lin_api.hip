@@ -234,10 +234,9 @@ int q4lin_linear_fmt(int fmt, const void* x, const void* w, const void* w_hi, co
   const bool has_hi = fmt == Q4LIN_FMT_Q5G64_F16S || fmt == Q4LIN_FMT_Q6G64_F16S;
   const bool has_sc = fmt != Q4LIN_FMT_BF16;
   if (!x || !w || !y || (has_hi && !w_hi) || (has_sc && !scales)) return Q4LIN_E_NULL;
-  const uintptr_t hi_align = fmt == Q4LIN_FMT_Q5G64_F16S ? 2 : 4;
-  const uintptr_t sc_align = fmt == Q4LIN_FMT_NVFP4 ? 1 : 2;
+  const uintptr_t hi_align = fmt == Q4LIN_FMT_Q5G64_F16S ? 4 : 8;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 2) || (has_hi && !aligned(w_hi, hi_align)) ||
-      (has_sc && !aligned(scales, sc_align)))
+      (has_sc && !aligned(scales, 2)))
     return Q4LIN_E_ALIGN;
   q4lin::FmtPlan plan;
   if (!q4lin::fmt_plan(fmt, n, k, t, &plan)) return Q4LIN_E_SHAPE;

@@ -18,13 +18,16 @@
 //   BF16_CTRL  the bf16 weights [N][K].
 //
 // Work mapping.  One workgroup of eight waves per block of BN <= 16 CT rows;
-// the waves split K into eight contiguous runs of "units" (one scale group
-// of Q5/Q6/W8, 64 weights of NVFP4, 32 of BF16), so every weight byte is
-// read once for all T <= 32 tokens.  Lane l serves row 16 ct + l % 16 and
-// the (l / 16)-th quarter of each unit: its loads are 8 (16 for BF16)
-// contiguous code bytes per row and unit, plus the matching high bits, and
-// 16 or 32 contiguous bytes of activations per token.  Longer T runs the
-// kernel once per 32 tokens.
+// the waves split K into eight contiguous runs of pairs of "units" (a unit
+// is one scale group of Q5/Q6/W8, 64 weights of NVFP4, 32 of BF16), so
+// every weight byte is read once for all T <= 32 tokens.  Lane l serves row
+// 16 ct + l % 16.  Its code loads are 16 contiguous bytes per row and pair:
+// quarter q = l / 16 reads half q % 2 of unit q / 2 (BF16: quarter q of
+// each unit), with the matching high bits; lanes l and l + 32 then swap
+// half of them, so every matrix-core instruction still reduces within one
+// unit.  The block's scales are copied into LDS once.  Activations: 16 or
+// 32 contiguous bytes per token and unit.  Longer T runs the kernel once
+// per 32 tokens.
 //
 // Arithmetic (v_mfma_f32_16x16x32_bf16, A = activations, B = weights, every
 // instruction reduces over one unit):
@@ -42,8 +45,8 @@
 //   * NVFP4: E2M1 times E4M3 has at most 6 significant bits and lies in
 //     [2^-10, 2688], so each weight is formed exactly as bf16 (hardware FP4
 //     conversion with a unit scale, an FP32 product with the decoded E4M3
-//     scale, a conversion that is exact) and fed straight to the matrix
-//     cores.
+//     scale, whose upper half is already the bf16 value) and fed straight
+//     to the matrix cores.
 //   * BF16_CTRL: the weights as they are.
 //   * The eight wave partials are summed in binary64 and rounded to bf16
 //     once; an output that comes out non-finite (binary32 partials that left
@@ -60,13 +63,24 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kUnroll = 2;  // units per pipeline step (the next step's loads fly during this one's products)
+constexpr int kTableBytes = 88 * 1024;  // LDS for the block's scales (with the 64 KiB sum area: 152 KiB)
+constexpr uint32_t kNowhere = 0x80000000u;  // a buffer offset past every range: reads zeros, no access
 
-// weights per unit (a lane holds a quarter of a row's unit: 8 code bytes,
-// 16 for BF16_CTRL)
+// Buffer loads: offsets at or past the resource's byte count return zeros
+// without a memory access, so loads past a wave's run need no branch (and
+// the wait counts stay fixed).
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// A unit is one scale group (Q5, Q6, W8), 64 weights (NVFP4) or 32 (BF16):
+// weights, code bytes per row, scale bytes per row
 template <int F>
 struct Unit {
   static constexpr int K = (F == FMT_W8 || F == FMT_BF16) ? 32 : 64;
+  static constexpr int CB = F == FMT_BF16 ? 64 : 32;
+  static constexpr int SB = F == FMT_NVFP4 ? 4 : F == FMT_BF16 ? 0 : 2;
 };
 
 // (a & m) | c and (a & m) ^ c in one instruction each (gfx950 three-input
@@ -137,9 +151,12 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 }
 
 // NVFP4: code dword w (E2M1 nibbles of k0..k7, even k low) times scale s ->
-// the eight exact bf16 weights in natural order
+// the eight exact bf16 weights in natural order.  E2M1 has at most 2
+// significant bits and E4M3 at most 4, so the binary32 product is exact
+// and fits bf16: its upper half is the weight, no rounding.
 __device__ __forceinline__ uint32_t nvfp4_pair(f32x2_t v, float s) {
-  return (uint32_t)f32_to_bf16_rne(v.x * s) | ((uint32_t)f32_to_bf16_rne(v.y * s) << 16);
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, v.y * s), __builtin_bit_cast(uint32_t, v.x * s),
+                               0x07060302u);
 }
 __device__ __forceinline__ bf16x8_t nvfp4_operand(uint32_t w, float s) {
   u32x4_t r;
@@ -198,14 +215,17 @@ __device__ __attribute__((noinline)) uint16_t exact_output(const uint16_t* __res
   return f32_to_bf16_rne((float)acc);
 }
 
-// One lane's loads for one unit: code bytes (and high bits, scale) of CT
-// rows, activations of TT tokens.
+// One lane's loads for one pair of units: 16 code bytes per row (two loads
+// of 16 for BF16_CTRL), the high bits that go with them, and the
+// activations of both units for TT token tiles.
 template <int F, int CT, int TT>
 struct Loads {
-  u32x4_t c[CT];      // code bytes (.x .y for 8-byte formats)
-  uint32_t h[CT];     // high bits (Q5: 16, Q6: 32) or the E4M3 scale byte (NVFP4)
-  uint16_t s[CT];     // fp16 scale (Q5, Q6, W8)
-  u32x4_t a[TT][2];   // activations: [tt][16-byte half]
+  static constexpr int NC = F == FMT_BF16 ? 2 : 1;       // 16-byte code loads per row
+  static constexpr int NH = F == FMT_Q6 ? 2 : 1;         // high-bit dwords per row
+  static constexpr int XH = Unit<F>::K == 64 ? 2 : 1;    // 16-byte activation pieces per unit and token
+  u32x4_t c[CT][NC];
+  uint32_t h[CT][NH];
+  u32x4_t a[2][TT][XH];
 };
 
 template <int F, int CT, int TT>
@@ -213,60 +233,101 @@ __global__ void __launch_bounds__(kThreads, 1)
 fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const uint8_t* __restrict__ hi,
            const uint8_t* __restrict__ sc, uint16_t* __restrict__ y, int N, int K, int T, int BN) {
   using U = Unit<F>;
+  using L_t = Loads<F, CT, TT>;
+  constexpr int XH = L_t::XH;
   constexpr bool NIB = (F == FMT_Q5 || F == FMT_Q6);     // nibble codes with an offset
-  constexpr bool SCALED = (F == FMT_Q5 || F == FMT_Q6 || F == FMT_W8);
-  constexpr int XH = U::K == 64 ? 2 : 1;                 // 16-byte activation pieces per unit and token
+  constexpr bool PAIRED = F != FMT_BF16;                 // one 16-byte load spans a pair of units
+  constexpr int NB = 2;                                  // pairs in flight (register sets)
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lq = lane >> 4;
+  // the quarter of each unit this lane multiplies: after the exchange of
+  // the paired loads, quarter lq holds code bytes 8 xq .. 8 xq + 7 of a unit
+  const int xq = PAIRED ? (((lq & 1) << 1) | (lq >> 1)) : lq;
   const int n0 = blockIdx.x * BN;
   const int rows = min(BN, N - n0);
   const int units = K / U::K;
-  const int ub = (int)(((int64_t)units * wave) / kWaves), ue = (int)(((int64_t)units * (wave + 1)) / kWaves);
+  const int pairs = (units + 1) >> 1;
+  const int pb = (int)(((int64_t)pairs * wave) / kWaves), pe = (int)(((int64_t)pairs * (wave + 1)) / kWaves);
+  const int ts = units * U::SB;  // bytes of one row's scales
+  uint8_t* tab = lds + (size_t)kWaves * 32 * BN * 4;
 
-  // per column tile: this lane's row (rows past the block repeat the last
-  // one; their sums are never stored)
-  const uint8_t* lo_row[CT];
-  const uint8_t* hi_row[CT];
-  const uint8_t* sc_row[CT];
+  // Byte offsets of this lane's loads, per column tile (rows past the
+  // block repeat the last one; their sums are never stored), relative to
+  // buffers over the block's rows of each plane.
+  const int row_bytes = units * U::CB;
+  constexpr int HB = F == FMT_Q5 ? 8 : F == FMT_Q6 ? 16 : 0;  // high-plane bytes per unit and row
+  const rsrc_t rlo = make_rsrc(lo + (size_t)n0 * row_bytes, (uint32_t)(rows * row_bytes));
+  const rsrc_t rhi = make_rsrc(HB ? hi + (size_t)n0 * units * HB : lo, (uint32_t)(rows * units * HB));
+  const rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)T * K * 2));
+  uint32_t lo_off[CT], hi_off[CT];
+  int tab_row[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    const size_t r = (size_t)(n0 + min(16 * ct + li, rows - 1));
-    if constexpr (F == FMT_BF16) lo_row[ct] = lo + r * (size_t)K * 2 + (size_t)lq * 16;
-    else if constexpr (F == FMT_W8) lo_row[ct] = lo + r * (size_t)K + (size_t)lq * 8;
-    else lo_row[ct] = lo + r * (size_t)(K / 2) + (size_t)lq * 8;
-    if constexpr (F == FMT_Q5) hi_row[ct] = hi + r * (size_t)(K / 8) + (size_t)lq * 2;
-    else if constexpr (F == FMT_Q6) hi_row[ct] = hi + r * (size_t)(K / 4) + (size_t)lq * 4;
-    else hi_row[ct] = nullptr;
-    if constexpr (F == FMT_NVFP4) sc_row[ct] = sc + r * (size_t)(K / 16) + (size_t)lq;
-    else if constexpr (F == FMT_W8) sc_row[ct] = sc + r * (size_t)(K / 32) * 2;
-    else if constexpr (SCALED) sc_row[ct] = sc + r * (size_t)(K / 64) * 2;
-    else sc_row[ct] = nullptr;
+    const int rl = min(16 * ct + li, rows - 1);
+    // paired formats: quarter lq reads half lq % 2 of the pair's unit lq / 2
+    if constexpr (F == FMT_BF16) lo_off[ct] = (uint32_t)(rl * row_bytes + lq * 16);
+    else lo_off[ct] = (uint32_t)(rl * row_bytes + (lq >> 1) * U::CB + (lq & 1) * 16);
+    hi_off[ct] = (uint32_t)(rl * units * HB + (lq >> 1) * HB + (lq & 1) * (HB / 2));
+    tab_row[ct] = rl * ts;
   }
-  const uint16_t* x_row[TT];
+  uint32_t x_off[TT];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) x_row[tt] = x + (size_t)min(16 * tt + li, T - 1) * (size_t)K + lq * (8 * XH);
+  for (int tt = 0; tt < TT; ++tt) x_off[tt] = (uint32_t)(min(16 * tt + li, T - 1) * K * 2 + xq * 16 * XH);
 
-  auto load = [&](int u, Loads<F, CT, TT>& L) __device__ {
+  // Pair p covers units 2p and 2p + 1.  A pair past the wave's run reads
+  // nothing; the second unit of the last pair of an odd count reads the
+  // next row's bytes or nothing, and its products are skipped.
+  auto load = [&](int p, L_t& L) __device__ {
+    const bool live = p < pe;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       if constexpr (F == FMT_BF16) {
-        L.c[ct] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(lo_row[ct] + (size_t)u * 64));
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+          L.c[ct][v] = __builtin_amdgcn_raw_buffer_load_b128(
+              rlo, live ? lo_off[ct] + (uint32_t)((2 * p + v) * U::CB) : kNowhere, 0, 2);
       } else {
-        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(lo_row[ct] + (size_t)u * 32));
-        L.c[ct] = u32x4_t{v.x, v.y, 0u, 0u};
+        L.c[ct][0] = __builtin_amdgcn_raw_buffer_load_b128(rlo, live ? lo_off[ct] + (uint32_t)(2 * p * U::CB) : kNowhere,
+                                                           0, 2);
       }
-      if constexpr (F == FMT_Q5) L.h[ct] = *reinterpret_cast<const uint16_t*>(hi_row[ct] + (size_t)u * 8);
-      if constexpr (F == FMT_Q6) L.h[ct] = *reinterpret_cast<const uint32_t*>(hi_row[ct] + (size_t)u * 16);
-      if constexpr (F == FMT_NVFP4) L.h[ct] = sc_row[ct][(size_t)u * 4];
-      if constexpr (SCALED) L.s[ct] = reinterpret_cast<const uint16_t*>(sc_row[ct])[u];
+      const uint32_t ho = live ? hi_off[ct] + (uint32_t)(2 * p * HB) : kNowhere;
+      if constexpr (F == FMT_Q5) L.h[ct][0] = __builtin_amdgcn_raw_buffer_load_b32(rhi, ho, 0, 0);
+      if constexpr (F == FMT_Q6) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rhi, ho, 0, 0);
+        L.h[ct][0] = v.x;
+        L.h[ct][1] = v.y;
+      }
     }
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+    for (int v = 0; v < 2; ++v)
 #pragma unroll
-      for (int p = 0; p < XH; ++p)
-        L.a[tt][p] = *reinterpret_cast<const u32x4_t*>(x_row[tt] + (size_t)u * U::K + 8 * p);
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int p2 = 0; p2 < XH; ++p2)
+          L.a[v][tt][p2] = __builtin_amdgcn_raw_buffer_load_b128(
+              rx, live ? x_off[tt] + (uint32_t)(((2 * p + v) * U::K + 8 * p2) * 2) : kNowhere, 0, 0);
+  };
+
+  // The block's scales go to LDS once (their rows are contiguous in the
+  // plane): eight 2-byte elements per thread and batch.
+  const int elems = rows * ts / 2;
+  const rsrc_t rsc = make_rsrc(U::SB ? sc + (size_t)n0 * ts : lo, (uint32_t)(rows * ts));
+  uint16_t* sdst = reinterpret_cast<uint16_t*>(tab);
+  auto stage_load = [&](int i0, uint16_t (&v)[8]) __device__ {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * kThreads + tid;
+      v[j] = __builtin_amdgcn_raw_buffer_load_b16(rsc, i < elems ? (uint32_t)(2 * i) : kNowhere, 0, 0);
+    }
+  };
+  auto stage_store = [&](int i0, const uint16_t (&v)[8]) __device__ {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * kThreads + tid;
+      if (i < elems) sdst[i] = v[j];
+    }
   };
 
   // constant operands of the offset codes (q = 16 for Q5, 32 for Q6; c = 0 for W8)
@@ -274,6 +335,7 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   const bf16x8_t bconst = __builtin_bit_cast(bf16x8_t, u32x4_t{kc, kc, kc, kc});
   const bf16x8_t bconst_hi = __builtin_bit_cast(bf16x8_t, u32x4_t{0x43C043C0u, 0x43C043C0u, 0x43C043C0u, 0x43C043C0u});
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const int hsh = (lane >> 5) << 4;  // Q5: the half of a high dword that belongs to this lane
 
   f32x4_t acc[CT][TT];
 #pragma unroll
@@ -281,15 +343,17 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[ct][tt] = zero4;
 
-  // the products of one unit
-  auto unit_products = [&](const Loads<F, CT, TT>& L) __device__ {
+  // the products of unit u: a = its activations, c = this lane's 8 code
+  // bytes per row (two dwords), h = their high bits
+  auto unit_products = [&](int u, const u32x4_t (&a)[TT][XH], const u32x2_t (&c)[CT], const uint32_t (&h)[CT])
+      __device__ {
     if constexpr (NIB) {
       bf16x8_t av[TT][2];
       f32x4_t cr[TT];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        av[tt][0] = pair_order(L.a[tt][0]);
-        av[tt][1] = pair_order(L.a[tt][1]);
+        av[tt][0] = pair_order(a[tt][0]);
+        av[tt][1] = pair_order(a[tt][1]);
         cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][0], bconst, zero4, 0, 0, 0);
         cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][1], bconst, cr[tt], 0, 0, 0);
       }
@@ -297,13 +361,13 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
       for (int ct = 0; ct < CT; ++ct) {
         bf16x8_t b0, b1;
         if constexpr (F == FMT_Q5) {
-          b0 = q5_operand(L.c[ct].x, L.h[ct] & 0xFFu);
-          b1 = q5_operand(L.c[ct].y, L.h[ct] >> 8);
+          b0 = q5_operand(c[ct].x, h[ct]);
+          b1 = q5_operand(c[ct].y, h[ct] >> 8);
         } else {
-          b0 = q6_operand(L.c[ct].x, L.h[ct] & 0xFFFFu);
-          b1 = q6_operand(L.c[ct].y, L.h[ct] >> 16);
+          b0 = q6_operand(c[ct].x, h[ct]);
+          b1 = q6_operand(c[ct].y, h[ct] >> 16);
         }
-        const float s = f16_bits_to_f32(L.s[ct]);
+        const float s = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(tab + tab_row[ct] + 2 * u));
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
           f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][0], b0, zero4, 0, 0, 0);
@@ -317,15 +381,15 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
       f32x4_t cr[TT];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        av[tt] = __builtin_bit_cast(bf16x8_t, L.a[tt][0]);
+        av[tt] = __builtin_bit_cast(bf16x8_t, a[tt][0]);
         cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bconst, zero4, 0, 0, 0);
         cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bconst_hi, cr[tt], 0, 0, 0);
       }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         bf16x8_t bl, bh;
-        w8_operands(L.c[ct].x, L.c[ct].y, bl, bh);
-        const float s = f16_bits_to_f32(L.s[ct]);
+        w8_operands(c[ct].x, c[ct].y, bl, bh);
+        const float s = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(tab + tab_row[ct] + 2 * u));
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
           f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bl, zero4, 0, 0, 0);
@@ -334,45 +398,92 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
           for (int r = 0; r < 4; ++r) acc[ct][tt][r] = __builtin_fmaf(s, p[r] - cr[tt][r], acc[ct][tt][r]);
         }
       }
-    } else if constexpr (F == FMT_NVFP4) {
+    } else {  // NVFP4: the lane's 16 weights are one E4M3 scale group
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const float s = e4m3_to_f32(L.h[ct]);
-        const bf16x8_t b0 = nvfp4_operand(L.c[ct].x, s), b1 = nvfp4_operand(L.c[ct].y, s);
+        const float s = e4m3_to_f32(tab[tab_row[ct] + 4 * u + xq]);
+        const bf16x8_t b0 = nvfp4_operand(c[ct].x, s), b1 = nvfp4_operand(c[ct].y, s);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
-          acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, L.a[tt][0]), b0,
+          acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[tt][0]), b0,
                                                                 acc[ct][tt], 0, 0, 0);
-          acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, L.a[tt][1]), b1,
+          acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[tt][1]), b1,
                                                                 acc[ct][tt], 0, 0, 0);
         }
       }
-    } else {  // BF16_CTRL
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-          acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, L.a[tt][0]),
-                                                                __builtin_bit_cast(bf16x8_t, L.c[ct]), acc[ct][tt],
-                                                                0, 0, 0);
     }
   };
 
-  // the wave's units, kUnroll per step, the next step's loads in flight
-  // during this step's products (indexes past the run repeat its last unit,
-  // so every load stays inside the planes; those units are skipped)
-  if (ub < ue) {
-    Loads<F, CT, TT> cur[kUnroll], nxt[kUnroll];
+  // the products of pair p (its second unit is skipped past the row's end)
+  auto pair_products = [&](int p, const L_t& L) __device__ {
+    const bool second = 2 * p + 1 < units;
+    if constexpr (F == FMT_BF16) {
 #pragma unroll
-    for (int v = 0; v < kUnroll; ++v) load(min(ub + v, ue - 1), cur[v]);
-    for (int u = ub; u < ue; u += kUnroll) {
+      for (int v = 0; v < 2; ++v) {
+        if (v == 1 && !second) break;
 #pragma unroll
-      for (int v = 0; v < kUnroll; ++v) load(min(u + kUnroll + v, ue - 1), nxt[v]);
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int v = 0; v < kUnroll; ++v)
-        if (u + v < ue) unit_products(cur[v]);
+          for (int tt = 0; tt < TT; ++tt)
+            acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, L.a[v][tt][0]),
+                                                                  __builtin_bit_cast(bf16x8_t, L.c[ct][v]),
+                                                                  acc[ct][tt], 0, 0, 0);
+      }
+    } else {
+      // Lanes l and l + 32 (quarters q and q + 2) exchange half of their
+      // 16 bytes: afterwards every lane holds 8 code bytes of each unit,
+      // bytes 8 xq .. 8 xq + 7 (and their high bits).
+      u32x2_t ca[CT], cb[CT];
+      uint32_t ha[CT], hb[CT];
 #pragma unroll
-      for (int v = 0; v < kUnroll; ++v) cur[v] = nxt[v];
+      for (int ct = 0; ct < CT; ++ct) {
+        const auto sx = __builtin_amdgcn_permlane32_swap(L.c[ct][0].x, L.c[ct][0].z, false, false);
+        const auto sy = __builtin_amdgcn_permlane32_swap(L.c[ct][0].y, L.c[ct][0].w, false, false);
+        ca[ct] = u32x2_t{sx[0], sy[0]};
+        cb[ct] = u32x2_t{sx[1], sy[1]};
+        ha[ct] = hb[ct] = 0u;
+        if constexpr (F == FMT_Q5) {
+          // both lanes get both dwords: [0] the lower lane's, [1] the upper lane's
+          const auto hs = __builtin_amdgcn_permlane32_swap(L.h[ct][0], L.h[ct][0], false, false);
+          ha[ct] = hs[0] >> hsh;
+          hb[ct] = hs[1] >> hsh;
+        }
+        if constexpr (F == FMT_Q6) {
+          const auto hs = __builtin_amdgcn_permlane32_swap(L.h[ct][0], L.h[ct][1], false, false);
+          ha[ct] = hs[0];
+          hb[ct] = hs[1];
+        }
+      }
+      unit_products(2 * p, L.a[0], ca, ha);
+      if (second) unit_products(2 * p + 1, L.a[1], cb, hb);
+    }
+  };
+
+  // Scales of the block (first batch) in flight with the first NB pairs'
+  // loads; NB register sets take turns, so while one pair's products run
+  // the next NB - 1 pairs' loads are in flight.  (A table larger than one
+  // batch is copied first, on its own.)
+  L_t b[NB];
+  uint16_t sv[8];
+  const bool one_batch = elems <= 8 * kThreads;
+  if constexpr (U::SB > 0) {
+    if (!one_batch) {
+      for (int i0 = 0; i0 < elems; i0 += 8 * kThreads) {
+        stage_load(i0, sv);
+        stage_store(i0, sv);
+      }
+    }
+    stage_load(0, sv);  // a repeat of the first batch when already copied
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) load(pb + i, b[i]);
+  if constexpr (U::SB > 0) stage_store(0, sv);
+  __syncthreads();
+  for (int p = pb; p < pe; p += NB) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (i == 0 || p + i < pe) pair_products(p + i, b[i]);
+      load(p + i + NB, b[i]);
     }
   }
 
@@ -447,13 +558,17 @@ bool fmt_plan(int fmt, int64_t n, int64_t k, int64_t t, FmtPlan* p) {
   if (fmt < FMT_Q5 || fmt > FMT_BF16 || n < 1 || t < 1 || k < 64 || (k % 64) != 0) return false;
   // per-row offsets are 64-bit; the kernel's int arithmetic needs N, K, T below 2^31
   if (n >= (int64_t(1) << 31) || k >= (int64_t(1) << 30) || t >= (int64_t(1) << 31)) return false;
+  // bytes of one row's scales in the LDS table
+  const int64_t ts = fmt == FMT_BF16 ? 0 : fmt == FMT_W8 || fmt == FMT_NVFP4 ? k / 16 : k / 32;
   int64_t bn = (n + 255) / 256;  // about one workgroup per CU
   if (bn > 64) bn = 64;          // at most four 16-row column tiles per wave
+  if (ts > 0 && bn * ts > kTableBytes) bn = kTableBytes / ts;
+  if (bn < 1) return false;
   const int64_t ct = (bn + 15) / 16;
   p->bn = (int)bn;
   p->ct = (int)ct;
   p->blocks = (int)((n + bn - 1) / bn);
-  p->lds_bytes = (size_t)kWaves * 32 * (size_t)bn * 4;
+  p->lds_bytes = (size_t)kWaves * 32 * (size_t)bn * 4 + (size_t)((bn * ts + 15) / 16 * 16);
   return true;
 }
 
