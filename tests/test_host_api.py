@@ -44,7 +44,7 @@ def test_shape_rejected(n, k, t):
 
 @pytest.mark.parametrize("n,k,t", [
     (64, 1 << 20, 1024),        # float16 activation copy 2 GiB: past the tiled kernels' 32-bit offsets
-    (1 << 24, 4096, 64),        # scale plane n * k / 32 = 2 GiB
+    (1 << 24, 4096, 160),       # scale plane n * k / 32 = 2 GiB
 ])
 def test_tiled_route_rejects_shapes_past_32bit_offsets(n, k, t):
     # the shapes pass the general limits and would take the many-token route
@@ -101,8 +101,9 @@ def test_routes_and_workspace_sizes():
             tp = (t + 31) // 32 * 32
             assert ws >= tp * 5120 * 2 + tp * 4
         elif r == q.Q4LIN_ROUTE_MID:
-            # binary32 partials of the K slices, [S][T][N]
-            assert ws % (t * 6144 * 4) == 0 and 0 <= ws // (t * 6144 * 4) <= 8
+            # none up to 64 tokens; above, binary32 partials of the K slices [S][T][N]
+            assert (ws == 0) == (t <= 64)
+            assert ws % (t * 6144 * 4) == 0 and ws // (t * 6144 * 4) <= 8
         else:
             assert ws == 0
     for t in (33, 64, 65, 128):
@@ -173,7 +174,7 @@ def test_linear_pair_shapes_and_workspace():
     # fused routes need none; the many-token route needs the larger weight's
     assert q.q4lin_pair_workspace_bytes(3072, 3072, 5120, 1) == 0
     assert q.q4lin_pair_workspace_bytes(1000, 700, 2048, 20) == 0
-    n1, n2, k, t = 768, 256, 1024, 100
+    n1, n2, k, t = 768, 256, 1024, 200
     need = q.q4lin_pair_workspace_bytes(n1, n2, k, t)
     assert need == max(q.q4lin_workspace_bytes(n1, k, t), q.q4lin_workspace_bytes(n2, k, t)) > 0
     assert q.q4lin_linear_pair(p, p, p, p, n1, p, p, p, n2, k, t, p, need - 1, 0) == q.Q4LIN_E_WORKSPACE

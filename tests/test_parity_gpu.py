@@ -241,7 +241,7 @@ def test_wide_range_scales_and_activations(t):
 
 @pytest.mark.parametrize("n,k,ts,route", [(32, 128, (1, 3, 17, 40), None), (200, 1280, (200,), 3),
                                            (200, 1280, (40, 100), 5)],
-                         ids=["one_split", "tiled_k_split", "mid_k_split"])
+                         ids=["one_split", "tiled_k_split", "medium_t"])
 def test_extreme_magnitudes_finite_and_infinite(n, k, ts, route):
     """Largest finite activations and scales: results overflow to +-Inf
     exactly where the exact sum does; nothing becomes NaN; every other output

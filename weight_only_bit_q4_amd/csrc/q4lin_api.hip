@@ -41,8 +41,19 @@ constexpr int64_t kMaxT = int64_t(1) << 21;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxBytes = int64_t(1) << 40;
 constexpr size_t kGemvLdsLimit = 64 * 1024;
-// the medium-T route takes T from here up to its plan's limit (128)
+// The medium-T route takes T from kMidFirstT to the split-K plan's limit
+// (128): up to kMidFmtLastT tokens it runs the few-token kernel of the
+// weight formats on the Q4 codes (one pass, no workspace; 21-23 us against
+// 23.5-24.6 at T = 33..57 on 6144 x 5120), above that the split-K kernel
+// (30.6-33.8 against 34-41 us at T = 65..121).
 constexpr int64_t kMidFirstT = 33;
+constexpr int64_t kMidFmtLastT = 64;
+
+// whether a medium-T call runs the few-token kernel (else the split-K one)
+bool mid_uses_fmt(int64_t n, int64_t k, int64_t t) {
+  q4lin::FmtPlan fp;
+  return t <= kMidFmtLastT && q4lin::fmt_plan(q4lin::FMT_Q4, n, k, t, &fp);
+}
 static_assert(q4lin::FMT_Q5 == Q4LIN_FMT_Q5G64_F16S && q4lin::FMT_Q6 == Q4LIN_FMT_Q6G64_F16S &&
                   q4lin::FMT_W8 == Q4LIN_FMT_W8G32_F16S && q4lin::FMT_NVFP4 == Q4LIN_FMT_NVFP4 &&
                   q4lin::FMT_BF16 == Q4LIN_FMT_BF16,
@@ -70,6 +81,7 @@ int pick_route(int64_t n, int64_t k, int64_t t) {
   if (t == 1 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
   if (q4lin::skinny_plan(n, k, t, &sp)) return Q4LIN_ROUTE_SKINNY;
   if (t <= 4 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
+  if (t >= kMidFirstT && mid_uses_fmt(n, k, t)) return Q4LIN_ROUTE_MID;
   q4lin::MidPlan mp;
   if (t >= kMidFirstT && q4lin::mid_plan(n, k, t, &mp)) return Q4LIN_ROUTE_MID;
   return Q4LIN_ROUTE_TILED;
@@ -77,8 +89,17 @@ int pick_route(int64_t n, int64_t k, int64_t t) {
 
 size_t route_workspace(int route, int64_t n, int64_t k, int64_t t) {
   if (route == Q4LIN_ROUTE_TILED) return q4lin::tiled_workspace_bytes(n, k, t);
-  if (route == Q4LIN_ROUTE_MID) return q4lin::mid_workspace_bytes(n, k, t);
+  if (route == Q4LIN_ROUTE_MID && !mid_uses_fmt(n, k, t)) return q4lin::mid_workspace_bytes(n, k, t);
   return 0;
+}
+
+// The medium-T route runs the Q4 weight through the few-token kernel of
+// the weight formats (up to 128 tokens per weight read).
+q4lin::FmtArgs q4_fmt_args(const q4lin::GemvArgs& g) {
+  q4lin::FmtArgs a{q4lin::FMT_Q4, g.x, g.codes, nullptr, g.scales, g.y, g.n, g.k, g.t};
+  a.res = g.res;
+  a.f32 = g.f32;
+  return a;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -121,7 +142,7 @@ int run_linear(const void* x, const void* codes, const void* scales, const void*
   } else if (route == Q4LIN_ROUTE_SKINNY) {
     e = q4lin::launch_skinny(ga, s);
   } else if (route == Q4LIN_ROUTE_MID) {
-    e = q4lin::launch_mid(ga, workspace, s);
+    e = mid_uses_fmt(n, k, t) ? q4lin::launch_fmt(q4_fmt_args(ga), s) : q4lin::launch_mid(ga, workspace, s);
   } else {
     q4lin::TiledArgs a{x, codes, scales, y, n, k, t, workspace, q4lin::tiled_pick_config(n, k, t), res};
     e = q4lin::launch_tiled(a, s);
@@ -137,8 +158,8 @@ size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 //   SPLIT: one launch per weight on the route chosen for N rows;
 //   TILED: the many-token route per weight, its raw sums left in the
 //          partials of a workspace half each.
-//   MID:   the medium-T route per weight, binary32 sums, its split partials
-//          after the sums in each half.
+//   MID:   the medium-T route per weight, binary32 sums (the split-K
+//          kernel's partials after the sums in each half).
 enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3, SW_MID = 4 };
 struct SwigluPlan {
   int mode;
@@ -158,7 +179,8 @@ bool swiglu_plan(int64_t n, int64_t k, int64_t t, SwigluPlan* p) {
   if (r1 == Q4LIN_ROUTE_TILED) {
     *p = SwigluPlan{SW_TILED, r1, al256(q4lin::tiled_workspace_bytes_f32(n, k, t))};
   } else if (r1 == Q4LIN_ROUTE_MID) {
-    *p = SwigluPlan{SW_MID, r1, al256((size_t)(n * t * 4)) + al256(q4lin::mid_workspace_bytes(n, k, t))};
+    *p = SwigluPlan{SW_MID, r1,
+                    al256((size_t)(n * t * 4)) + (mid_uses_fmt(n, k, t) ? 0 : al256(q4lin::mid_workspace_bytes(n, k, t)))};
   } else {
     *p = SwigluPlan{SW_SPLIT, r1, al256((size_t)(n * t * 4))};
   }
@@ -309,11 +331,11 @@ int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scale
     const size_t sums = al256((size_t)(n * t * 4));
     q4lin::GemvArgs a{x, codes_gate, scales_gate, w0, n, k, t};
     a.f32 = true;
-    e = q4lin::launch_mid(a, w0 + sums, s);
+    e = mid_uses_fmt(n, k, t) ? q4lin::launch_fmt(q4_fmt_args(a), s) : q4lin::launch_mid(a, w0 + sums, s);
     if (e == hipSuccess) {
       q4lin::GemvArgs b{x, codes_up, scales_up, w1, n, k, t};
       b.f32 = true;
-      e = q4lin::launch_mid(b, w1 + sums, s);
+      e = mid_uses_fmt(n, k, t) ? q4lin::launch_fmt(q4_fmt_args(b), s) : q4lin::launch_mid(b, w1 + sums, s);
     }
   } else {
     const q4lin::TiledConfig cfg = q4lin::tiled_pick_config(n, k, t);

@@ -63,7 +63,8 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTableBytes = 88 * 1024;  // LDS for the block's scales (with the 64 KiB sum area: 152 KiB)
+constexpr int kTableBytes = 88 * 1024;   // LDS for the block's scales (with the 64 KiB sum area: 152 KiB)
+constexpr int kLdsBytes = 160 * 1024;    // LDS of one workgroup
 constexpr uint32_t kNowhere = 0x80000000u;  // a buffer offset past every range: reads zeros, no access
 
 // Buffer loads: offsets at or past the resource's byte count return zeros
@@ -73,6 +74,22 @@ using rsrc_t = __amdgpu_buffer_rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+// 16-byte direct-to-LDS buffer load: each lane sends 16 bytes from base +
+// voffset to lds_base + 16 * lane (lds_base wave-uniform)
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voffset, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voffset, 0,
+                                           0, 0);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4
+// and lgkmcnt 11:8 left at "no wait")
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt holds 0..63");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4)); }
 
 // A unit is one scale group (Q5, Q6, W8), 64 weights (NVFP4) or 32 (BF16):
 // weights, code bytes per row, scale bytes per row
@@ -122,6 +139,17 @@ __device__ __forceinline__ bf16x8_t q6_operand(uint32_t w, uint32_t h) {
   r.y = and_or(hs >> 2, 0x00300030u, and_or(w >> 4, 0x000F000Fu, 0x43004300u));
   r.z = and_or(hs >> 4, 0x00300030u, and_or(w >> 8, 0x000F000Fu, 0x43004300u));
   r.w = and_or(hs >> 6, 0x00300030u, and_or(w >> 12, 0x000F000Fu, 0x43004300u));
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// Q4: code dword w (nibbles of k0..k7) -> the eight exact bf16 values
+// 128 + q in pair order
+__device__ __forceinline__ bf16x8_t q4_operand(uint32_t w) {
+  u32x4_t r;
+  r.x = and_or(w, 0x000F000Fu, 0x43004300u);
+  r.y = and_or(w >> 4, 0x000F000Fu, 0x43004300u);
+  r.z = and_or(w >> 8, 0x000F000Fu, 0x43004300u);
+  r.w = and_or(w >> 12, 0x000F000Fu, 0x43004300u);
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
@@ -188,7 +216,9 @@ __device__ double weight_exact(const uint8_t* __restrict__ lo, const uint8_t* __
       return v * (double)e4m3_to_f32(sc[r * (K / 16) + k / 16]);
     } else {
       const double s = (double)f16_bits_to_f32(reinterpret_cast<const uint16_t*>(sc)[r * (K / 64) + k / 64]);
-      if constexpr (F == FMT_Q5) {
+      if constexpr (F == FMT_Q4) {
+        return (double)(nib - 8) * s;
+      } else if constexpr (F == FMT_Q5) {
         const int q = nib | ((int)((hi[r * (K / 8) + k / 8] >> (k & 7)) & 1u) << 4);
         return (double)(q - 16) * s;
       } else {
@@ -202,16 +232,19 @@ __device__ double weight_exact(const uint8_t* __restrict__ lo, const uint8_t* __
 // An output whose binary32 partial sums left the range (activations near
 // the top of the bf16 range make the products of the offset codes overflow
 // although the exact sum may not) is formed again from the inputs: the sum
-// over k in binary64 of exact products, rounded once.  Finite outputs never
-// come here.
+// over k in binary64 of exact products (plus the residual), rounded once.
+// Finite outputs never come here.
 template <int F>
 __device__ __attribute__((noinline)) uint16_t exact_output(const uint16_t* __restrict__ x,
                                                            const uint8_t* __restrict__ lo,
                                                            const uint8_t* __restrict__ hi,
-                                                           const uint8_t* __restrict__ sc, int K, int n, int t) {
+                                                           const uint8_t* __restrict__ sc,
+                                                           const uint16_t* __restrict__ res, int N, int K, int n,
+                                                           int t) {
   double acc = 0.0;
   for (int k = 0; k < K; ++k)
     acc += weight_exact<F>(lo, hi, sc, K, n, k) * (double)bf16_bits_to_f32(x[(size_t)t * K + k]);
+  if (res != nullptr) acc += (double)bf16_bits_to_f32(res[(size_t)t * N + n]);
   return f32_to_bf16_rne((float)acc);
 }
 
@@ -228,19 +261,32 @@ struct Loads {
   u32x4_t a[2][TT][XH];
 };
 
-template <int F, int CT, int TT>
+template <int F, int CT, int TT, int WT>
 __global__ void __launch_bounds__(kThreads, 1)
 fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const uint8_t* __restrict__ hi,
-           const uint8_t* __restrict__ sc, uint16_t* __restrict__ y, int N, int K, int T, int BN) {
+           const uint8_t* __restrict__ sc, uint16_t* __restrict__ y, const uint16_t* __restrict__ res, int f32out,
+           int N, int K, int T, int BN) {
   using U = Unit<F>;
   using L_t = Loads<F, CT, TT>;
   constexpr int XH = L_t::XH;
-  constexpr bool NIB = (F == FMT_Q5 || F == FMT_Q6);     // nibble codes with an offset
+  constexpr bool NIB = (F == FMT_Q4 || F == FMT_Q5 || F == FMT_Q6);  // nibble codes with an offset
+  constexpr int WK = kWaves / WT;  // waves per token range: each takes a K run
+  constexpr int BT = 32 * WT;      // tokens per launch
   constexpr bool PAIRED = F != FMT_BF16;                 // one 16-byte load spans a pair of units
   constexpr int NB = 2;                                  // pairs in flight (register sets)
+  // Above 16 tokens the activations go through a ring in LDS: each wave
+  // copies its pairs' activations with direct-to-LDS loads in memory order
+  // (consecutive lanes read consecutive 16-byte pieces of a token, so the
+  // loads coalesce) and reads them back in matrix-core operand order.
+  constexpr bool XL = TT == 2;
+  constexpr int TTK = 16 * TT;                // tokens per wave
+  constexpr int PPT = U::K * 2 / 16;          // 16-byte pieces per token and unit
+  constexpr int SLOT = 2 * TTK * PPT * 16;    // one pair's activations [unit][token][piece]
+  constexpr int NI = 2 * TTK * PPT / 64;      // direct-to-LDS loads per pair
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wk = wave % WK, wt = wave / WK;  // K run, 32-token range
   const int li = lane & 15, lq = lane >> 4;
   // the quarter of each unit this lane multiplies: after the exchange of
   // the paired loads, quarter lq holds code bytes 8 xq .. 8 xq + 7 of a unit
@@ -249,9 +295,11 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   const int rows = min(BN, N - n0);
   const int units = K / U::K;
   const int pairs = (units + 1) >> 1;
-  const int pb = (int)(((int64_t)pairs * wave) / kWaves), pe = (int)(((int64_t)pairs * (wave + 1)) / kWaves);
+  const int pb = (int)(((int64_t)pairs * wk) / WK), pe = (int)(((int64_t)pairs * (wk + 1)) / WK);
   const int ts = units * U::SB;  // bytes of one row's scales
-  uint8_t* tab = lds + (size_t)kWaves * 32 * BN * 4;
+  // LDS: [activation rings of the 8 waves (XL)] or [partials], then the
+  // scale table; the partials of the final sum reuse the start
+  uint8_t* tab = lds + (XL ? (size_t)kWaves * 2 * SLOT : (size_t)kWaves * 32 * BN * 4);
 
   // Byte offsets of this lane's loads, per column tile (rows past the
   // block repeat the last one; their sums are never stored), relative to
@@ -274,7 +322,47 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   }
   uint32_t x_off[TT];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) x_off[tt] = (uint32_t)(min(16 * tt + li, T - 1) * K * 2 + xq * 16 * XH);
+  for (int tt = 0; tt < TT; ++tt)
+    x_off[tt] = (uint32_t)(min(32 * wt + 16 * tt + li, T - 1) * K * 2 + xq * 16 * XH);
+
+  // The ring: slot p % 2 holds pair p's activations, piece (v, tl, pc) at
+  // position (v TTK + tl) PPT + (pc ^ (tl % PPT)) (the XOR spreads the
+  // operand reads of 16 tokens over the banks).  Load j of a pair moves
+  // positions 64 j .. 64 j + 63, lane l the one at 64 j + l.
+  uint8_t* const ring = lds + (size_t)wave * 2 * SLOT;
+  uint32_t xdma[XL ? NI : 1];
+  if constexpr (XL) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int q = j * 64 + lane;
+      const int v = q / (TTK * PPT), tl = (q / PPT) % TTK, pc = (q % PPT) ^ (tl % PPT);
+      xdma[j] = (uint32_t)(min(32 * wt + tl, T - 1) * K * 2 + v * U::K * 2 + pc * 16);
+    }
+  }
+  // a pair past the wave's run reads nothing (zeros land in the slot)
+  auto issue_x = [&](int p) __device__ {
+    if constexpr (XL) {
+      uint8_t* slot = ring + (p & 1) * SLOT;
+      const uint32_t base = (uint32_t)(2 * p * U::K * 2);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) dma16(rx, p < pe ? xdma[j] + base : kNowhere, slot + j * 1024);
+    }
+  };
+  // pair p's operands: lane (li, lq) takes pieces XH xq .. XH xq + XH - 1 of
+  // token 16 tt + li in each unit
+  auto read_x = [&](int p, u32x4_t (&A)[2][TT][XH]) __device__ {
+    const uint8_t* slot = ring + (p & 1) * SLOT;
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int h = 0; h < XH; ++h) {
+          const int tl = 16 * tt + li;
+          A[v][tt][h] = *reinterpret_cast<const u32x4_t*>(
+              slot + ((v * TTK + tl) * PPT + ((XH * xq + h) ^ (tl % PPT))) * 16);
+        }
+  };
 
   // Pair p covers units 2p and 2p + 1.  A pair past the wave's run reads
   // nothing; the second unit of the last pair of an odd count reads the
@@ -300,14 +388,16 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
         L.h[ct][1] = v.y;
       }
     }
+    if constexpr (!XL) {
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
+      for (int v = 0; v < 2; ++v)
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int p2 = 0; p2 < XH; ++p2)
-          L.a[v][tt][p2] = __builtin_amdgcn_raw_buffer_load_b128(
-              rx, live ? x_off[tt] + (uint32_t)(((2 * p + v) * U::K + 8 * p2) * 2) : kNowhere, 0, 0);
+          for (int p2 = 0; p2 < XH; ++p2)
+            L.a[v][tt][p2] = __builtin_amdgcn_raw_buffer_load_b128(
+                rx, live ? x_off[tt] + (uint32_t)(((2 * p + v) * U::K + 8 * p2) * 2) : kNowhere, 0, 0);
+    }
   };
 
   // The block's scales go to LDS once (their rows are contiguous in the
@@ -330,8 +420,11 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
     }
   };
 
-  // constant operands of the offset codes (q = 16 for Q5, 32 for Q6; c = 0 for W8)
-  const uint32_t kc = F == FMT_Q5 ? 0x43104310u : F == FMT_Q6 ? 0x43204320u : 0x43004300u;
+  // constant operands of the offset codes (q = 8 for Q4, 16 for Q5, 32 for Q6; c = 0 for W8)
+  const uint32_t kc = F == FMT_Q4   ? 0x43084308u
+                      : F == FMT_Q5 ? 0x43104310u
+                      : F == FMT_Q6 ? 0x43204320u
+                                    : 0x43004300u;
   const bf16x8_t bconst = __builtin_bit_cast(bf16x8_t, u32x4_t{kc, kc, kc, kc});
   const bf16x8_t bconst_hi = __builtin_bit_cast(bf16x8_t, u32x4_t{0x43C043C0u, 0x43C043C0u, 0x43C043C0u, 0x43C043C0u});
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -360,7 +453,10 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         bf16x8_t b0, b1;
-        if constexpr (F == FMT_Q5) {
+        if constexpr (F == FMT_Q4) {
+          b0 = q4_operand(c[ct].x);
+          b1 = q4_operand(c[ct].y);
+        } else if constexpr (F == FMT_Q5) {
           b0 = q5_operand(c[ct].x, h[ct]);
           b1 = q5_operand(c[ct].y, h[ct] >> 8);
         } else {
@@ -415,7 +511,7 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   };
 
   // the products of pair p (its second unit is skipped past the row's end)
-  auto pair_products = [&](int p, const L_t& L) __device__ {
+  auto pair_products = [&](int p, const L_t& L, const u32x4_t (&A)[2][TT][XH]) __device__ {
     const bool second = 2 * p + 1 < units;
     if constexpr (F == FMT_BF16) {
 #pragma unroll
@@ -425,7 +521,7 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt)
-            acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, L.a[v][tt][0]),
+            acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[v][tt][0]),
                                                                   __builtin_bit_cast(bf16x8_t, L.c[ct][v]),
                                                                   acc[ct][tt], 0, 0, 0);
       }
@@ -454,15 +550,15 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
           hb[ct] = hs[1];
         }
       }
-      unit_products(2 * p, L.a[0], ca, ha);
-      if (second) unit_products(2 * p + 1, L.a[1], cb, hb);
+      unit_products(2 * p, A[0], ca, ha);
+      if (second) unit_products(2 * p + 1, A[1], cb, hb);
     }
   };
 
-  // Scales of the block (first batch) in flight with the first NB pairs'
-  // loads; NB register sets take turns, so while one pair's products run
-  // the next NB - 1 pairs' loads are in flight.  (A table larger than one
-  // batch is copied first, on its own.)
+  // Scales of the block (first batch) in flight with the first two pairs'
+  // loads; two register sets (and ring slots) take turns, so while one
+  // pair's products run the next pair's loads are in flight.  (A table
+  // larger than one batch is copied first, on its own.)
   L_t b[NB];
   uint16_t sv[8];
   const bool one_batch = elems <= 8 * kThreads;
@@ -475,19 +571,56 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
     }
     stage_load(0, sv);  // a repeat of the first batch when already copied
   }
+  // per pair, in this order: its activations to LDS (XL), then its codes
 #pragma unroll
-  for (int i = 0; i < NB; ++i) load(pb + i, b[i]);
+  for (int i = 0; i < NB; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_x(pb + i);
+    __builtin_amdgcn_sched_barrier(0);
+    load(pb + i, b[i]);
+  }
   if constexpr (U::SB > 0) stage_store(0, sv);
-  __syncthreads();
+  // the table's writes are visible after this; the loads stay in flight
+  // (a fence here would also wait for the copies into the rings)
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  // loads per pair: LC code-plane loads after NI activation loads
+  constexpr int LC = CT * (Loads<F, CT, TT>::NC + ((F == FMT_Q5 || F == FMT_Q6) ? 1 : 0));
+  // (Every load is issued outside the branches, so the compiler's count of
+  // the loads in flight stays exact.)
   for (int p = pb; p < pe; p += NB) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      if (i == 0 || p + i < pe) pair_products(p + i, b[i]);
+      u32x4_t A[2][TT][XH];
+      if constexpr (XL) {
+        // pair p + i's activations have landed once only the loads issued
+        // after them (its codes, the next pair's activations and codes) may
+        // be outstanding
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<2 * LC + NI>();
+        read_x(p + i, A);
+        wait_lgkm0();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_x(p + i + NB);  // into the slot just read
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int h = 0; h < XH; ++h) A[v][tt][h] = b[i].a[v][tt][h];
+      }
+      if (i == 0 || p + i < pe) pair_products(p + i, b[i], A);
       load(p + i + NB, b[i]);
     }
   }
+  if constexpr (XL) {
+    wait_vm<0>();  // every copy into the rings has landed before they are reused
+    __syncthreads();
+  }
 
-  // eight-way sum in binary64: red[wave][t < 32][col < BN] binary32 partials
+  // sum over the WK runs in binary64: red[wk][t < BT][col < BN] binary32 partials
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
@@ -496,8 +629,8 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tt + 4 * lq + r;
-        if (col < BN && t < T) red[(wave * 32 + t) * BN + col] = acc[ct][tt][r];
+        const int t = 32 * wt + 16 * tt + 4 * lq + r;
+        if (col < BN && t < T) red[(wk * BT + t) * BN + col] = acc[ct][tt][r];
       }
   }
   __syncthreads();
@@ -505,48 +638,57 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
     const int t = i / rows, col = i - t * rows;
     double v = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += (double)red[(w * 32 + t) * BN + col];
+    for (int w = 0; w < WK; ++w) v += (double)red[(w * BT + t) * BN + col];
+    const size_t o = (size_t)t * N + n0 + col;
+    if (f32out) {
+      reinterpret_cast<float*>(y)[o] = (float)v;  // binary32 sums (the gate and up of LinearSwiGLU)
+      continue;
+    }
+    if (res != nullptr) v += (double)bf16_bits_to_f32(res[o]);  // LinearAdd
     uint16_t h = f32_to_bf16_rne((float)v);
-    if ((h & 0x7F80u) == 0x7F80u) h = exact_output<F>(x, lo, hi, sc, K, n0 + col, t);  // rare
-    y[(size_t)t * N + n0 + col] = h;
+    if ((h & 0x7F80u) == 0x7F80u) h = exact_output<F>(x, lo, hi, sc, res, N, K, n0 + col, t);  // rare
+    y[o] = h;
   }
 }
 
-template <int F, int CT, int TT>
-hipError_t launch_one(const FmtArgs& a, const FmtPlan& p, const uint16_t* x, uint16_t* y, int t, hipStream_t s) {
-  auto kern = fmt_kernel<F, CT, TT>;
+template <int F, int CT, int TT, int WT>
+hipError_t launch_one(const FmtArgs& a, const FmtPlan& p, const uint16_t* x, uint16_t* y, const uint16_t* res,
+                      int t, hipStream_t s) {
+  auto kern = fmt_kernel<F, CT, TT, WT>;
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)p.blocks), dim3(kThreads), p.lds_bytes, s>>>(
       x, static_cast<const uint8_t*>(a.lo), static_cast<const uint8_t*>(a.hi), static_cast<const uint8_t*>(a.sc), y,
-      (int)a.n, (int)a.k, t, p.bn);
+      res, a.f32 ? 1 : 0, (int)a.n, (int)a.k, t, p.bn);
   return hipGetLastError();
+}
+
+template <int F, int TT, int WT>
+hipError_t launch_ct(const FmtArgs& a, const FmtPlan& p, const uint16_t* x, uint16_t* y, const uint16_t* res, int t,
+                     hipStream_t s) {
+  switch (p.ct) {
+    case 1: return launch_one<F, 1, TT, WT>(a, p, x, y, res, t, s);
+    case 2: return launch_one<F, 2, TT, WT>(a, p, x, y, res, t, s);
+    case 3: return launch_one<F, 3, TT, WT>(a, p, x, y, res, t, s);
+    default: return launch_one<F, 4, TT, WT>(a, p, x, y, res, t, s);
+  }
 }
 
 template <int F>
 hipError_t launch_fmt_t(const FmtArgs& a, const FmtPlan& p, hipStream_t s) {
-  // 32 tokens per launch (a weight read per launch)
-  for (int64_t t0 = 0; t0 < a.t; t0 += 32) {
-    const int t = (int)(a.t - t0 < 32 ? a.t - t0 : 32);
+  // up to 128 tokens per launch (a weight read per launch): 32 per token
+  // range of waves, 16 per tile
+  const size_t osz = a.f32 ? 4 : 2;
+  for (int64_t t0 = 0; t0 < a.t; t0 += 128) {
+    const int t = (int)(a.t - t0 < 128 ? a.t - t0 : 128);
     const uint16_t* x = static_cast<const uint16_t*>(a.x) + t0 * a.k;
-    uint16_t* y = static_cast<uint16_t*>(a.y) + t0 * a.n;
+    uint16_t* y = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.y) + (size_t)t0 * a.n * osz);
+    const uint16_t* res = a.res ? static_cast<const uint16_t*>(a.res) + t0 * a.n : nullptr;
     hipError_t e;
-    const int tt = t > 16 ? 2 : 1;
-    if (tt == 1) {
-      switch (p.ct) {
-        case 1: e = launch_one<F, 1, 1>(a, p, x, y, t, s); break;
-        case 2: e = launch_one<F, 2, 1>(a, p, x, y, t, s); break;
-        case 3: e = launch_one<F, 3, 1>(a, p, x, y, t, s); break;
-        default: e = launch_one<F, 4, 1>(a, p, x, y, t, s); break;
-      }
-    } else {
-      switch (p.ct) {
-        case 1: e = launch_one<F, 1, 2>(a, p, x, y, t, s); break;
-        case 2: e = launch_one<F, 2, 2>(a, p, x, y, t, s); break;
-        case 3: e = launch_one<F, 3, 2>(a, p, x, y, t, s); break;
-        default: e = launch_one<F, 4, 2>(a, p, x, y, t, s); break;
-      }
-    }
+    if (t <= 16) e = launch_ct<F, 1, 1>(a, p, x, y, res, t, s);
+    else if (t <= 32) e = launch_ct<F, 2, 1>(a, p, x, y, res, t, s);
+    else if (t <= 64) e = launch_ct<F, 2, 2>(a, p, x, y, res, t, s);
+    else e = launch_ct<F, 2, 4>(a, p, x, y, res, t, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -555,20 +697,28 @@ hipError_t launch_fmt_t(const FmtArgs& a, const FmtPlan& p, hipStream_t s) {
 }  // namespace
 
 bool fmt_plan(int fmt, int64_t n, int64_t k, int64_t t, FmtPlan* p) {
-  if (fmt < FMT_Q5 || fmt > FMT_BF16 || n < 1 || t < 1 || k < 64 || (k % 64) != 0) return false;
+  if (fmt < FMT_Q4 || fmt > FMT_BF16 || n < 1 || t < 1 || k < 64 || (k % 64) != 0) return false;
   // per-row offsets are 64-bit; the kernel's int arithmetic needs N, K, T below 2^31
   if (n >= (int64_t(1) << 31) || k >= (int64_t(1) << 30) || t >= (int64_t(1) << 31)) return false;
   // bytes of one row's scales in the LDS table
   const int64_t ts = fmt == FMT_BF16 ? 0 : fmt == FMT_W8 || fmt == FMT_NVFP4 ? k / 16 : k / 32;
+  // launches of more than 16 tokens keep the waves' activation rings in LDS
+  // (two slots of 2 units x 32 tokens per wave)
+  const int64_t ppt = (fmt == FMT_W8 || fmt == FMT_BF16) ? 4 : 8;
+  const int64_t ring = t > 16 ? (int64_t)kWaves * 2 * (2 * 32 * ppt * 16) : 0;
+  const int64_t table_cap = ring + kTableBytes <= kLdsBytes ? kTableBytes : kLdsBytes - ring;
   int64_t bn = (n + 255) / 256;  // about one workgroup per CU
   if (bn > 64) bn = 64;          // at most four 16-row column tiles per wave
-  if (ts > 0 && bn * ts > kTableBytes) bn = kTableBytes / ts;
+  if (ts > 0 && bn * ts > table_cap) bn = table_cap / ts;
   if (bn < 1) return false;
   const int64_t ct = (bn + 15) / 16;
   p->bn = (int)bn;
   p->ct = (int)ct;
   p->blocks = (int)((n + bn - 1) / bn);
-  p->lds_bytes = (size_t)kWaves * 32 * (size_t)bn * 4 + (size_t)((bn * ts + 15) / 16 * 16);
+  // binary32 partials [8 waves][32 tokens][bn] (the same for every split of
+  // the waves into token ranges; they reuse the rings), then the scale table
+  const int64_t red = (int64_t)kWaves * 32 * bn * 4;
+  p->lds_bytes = (size_t)((red > ring ? red : ring) + (bn * ts + 15) / 16 * 16);
   return true;
 }
 
@@ -576,6 +726,7 @@ hipError_t launch_fmt(const FmtArgs& a, hipStream_t stream) {
   FmtPlan p;
   if (!fmt_plan(a.fmt, a.n, a.k, a.t, &p)) return hipErrorInvalidValue;
   switch (a.fmt) {
+    case FMT_Q4: return launch_fmt_t<FMT_Q4>(a, p, stream);
     case FMT_Q5: return launch_fmt_t<FMT_Q5>(a, p, stream);
     case FMT_Q6: return launch_fmt_t<FMT_Q6>(a, p, stream);
     case FMT_W8: return launch_fmt_t<FMT_W8>(a, p, stream);

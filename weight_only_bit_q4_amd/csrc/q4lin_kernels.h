@@ -152,6 +152,8 @@ struct FmtArgs {
   const void* sc;  // scale plane (fp16, or E4M3 bytes for NVFP4; unused for BF16_CTRL)
   void* y;
   int64_t n, k, t;
+  const void* res = nullptr;  // LinearAdd residual, bf16 [T][N] (nullptr: plain Linear)
+  bool f32 = false;           // outputs as binary32 [T][N] (LinearSwiGLU's sums), not bf16
 };
 struct FmtPlan {
   int bn;      // rows per workgroup
