@@ -64,7 +64,7 @@ def test_add_all_code8_returns_residual(n, k, t):
 
 @pytest.mark.parametrize("n,k,t", [(6144, 5120, 1), (512, 1024, 4), (1536, 5120, 9), (1000, 2048, 20),
                                    (2048, 1024, 64), (700, 1280, 70), (1024, 1024, 300), (97, 320, 40),
-                                   (6144, 256, 1024), (6100, 320, 1000)])
+                                   (6144, 256, 1024), (6100, 320, 1000), (2600, 17408, 1)])
 def test_add_matches_oracle(n, k, t):
     x, codes, scales = inputs.gen_problem(n, k, t, 47)
     # a residual of the size of the product, so both terms matter

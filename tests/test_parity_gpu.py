@@ -154,6 +154,9 @@ def test_large_shapes(shape, t):
 @pytest.mark.parametrize("n,k,t", [
     (1, 64, 1), (1, 64, 2), (7, 64, 3), (33, 128, 4), (97, 192, 5), (1, 64, 33), (17, 320, 31),
     (200, 576, 129), (5, 1088, 257), (130, 4160, 70), (300, 2048, 1), (16, 64, 1000),
+    # one token on long rows: twelve waves per workgroup, wave slices of
+    # unequal length (257 and 320 groups over 12 waves), ragged blocks
+    (1, 16448, 1), (100, 17408, 1), (5100, 20480, 1),
     # K split over several workgroups per tile: 8 splits of 10 groups with
     # ragged rows; 2 splits of 13 and 14 groups (the second starts at an odd
     # group, so its scales sit in the other halves of their dwords)
@@ -240,8 +243,8 @@ def test_wide_range_scales_and_activations(t):
 
 
 @pytest.mark.parametrize("n,k,ts,route", [(32, 128, (1, 3, 17, 40), None), (200, 1280, (200,), 3),
-                                           (200, 1280, (40, 100), 5)],
-                         ids=["one_split", "tiled_k_split", "medium_t"])
+                                           (200, 1280, (40, 100), 5), (32, 17408, (1,), 4)],
+                         ids=["one_split", "tiled_k_split", "medium_t", "long_row_one_token"])
 def test_extreme_magnitudes_finite_and_infinite(n, k, ts, route):
     """Largest finite activations and scales: results overflow to +-Inf
     exactly where the exact sum does; nothing becomes NaN; every other output

@@ -70,7 +70,8 @@ def test_pair_worked_examples(replicate):
 # wide K (few-token vector route)
 @pytest.mark.parametrize("n1,n2,k,t", [(3072, 3072, 5120, 1), (1000, 333, 2048, 1), (2048, 2048, 1024, 4),
                                        (6144, 1024, 5120, 2), (1000, 700, 2048, 20), (517, 1531, 1280, 9),
-                                       (768, 256, 1024, 100), (97, 160, 320, 40), (128, 256, 20480, 3)])
+                                       (768, 256, 1024, 100), (97, 160, 320, 40), (128, 256, 20480, 3),
+                                       (2560, 1000, 17408, 1)])
 def test_pair_matches_oracle(n1, n2, k, t):
     x, c1, s1 = inputs.gen_problem(n1, k, t, 71)
     _, c2, s2 = inputs.gen_problem(n2, k, t, 73)

@@ -60,7 +60,7 @@ def _pair(n, k, t, seed):
 
 @pytest.mark.parametrize("n,k,t", [(3072, 5120, 1), (1000, 2048, 1), (2048, 1024, 4), (1000, 2048, 20),
                                    (517, 1280, 9), (128, 20480, 3), (768, 1024, 100), (1024, 1024, 300),
-                                   (97, 320, 40), (6144, 5120, 64), (6144, 256, 1024)])
+                                   (97, 320, 40), (6144, 5120, 64), (6144, 256, 1024), (2560, 17408, 1)])
 def test_swiglu_matches_oracle(n, k, t):
     x, cg, sg, cu, su = _pair(n, k, t, 101)
     got = run_swiglu(x, cg, sg, cu, su, n, k, t, what="seeded")

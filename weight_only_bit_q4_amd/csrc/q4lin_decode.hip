@@ -162,8 +162,8 @@ __device__ __forceinline__ float piece_dot_pre(const uint32_t (&c)[16], const u3
 // piece of X, converts each code piece once and runs one dot chain per token
 // (vector-ALU work grows with NT, the weight stream does not: a few tokens
 // cost little more than one).
-template <int PL, int MAXR, int NT>
-__global__ void __launch_bounds__(kThreads)
+template <int PL, int MAXR, int NT, int WV>
+__global__ void __launch_bounds__(64 * WV)
 decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
               uint16_t* y, int N, int K, int BN, const uint16_t* res, SecondPlane p2) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -183,7 +183,7 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   const int rows = min(BN, N - n0);
 
   // wave slice, slots and row groups (all wave-uniform but the lane's own)
-  const int gl = (G * wave) / kWaves, gh = (G * (wave + 1)) / kWaves;
+  const int gl = (G * wave) / WV, gh = (G * (wave + 1)) / WV;
   const int ng = gh - gl;
   const int P = 2 * ng;                          // pieces per row in the slice
   const int S = max((P + PL - 1) / PL, 1);       // slots per row
@@ -199,7 +199,7 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   // more than that apart, so that the eight threads of a row, which read the
   // eight regions at the same offset, hit different banks), then the waves'
   // per-token exponents.
-  int* wexp = reinterpret_cast<int*>(lds + kWaves * NT * kRegion<MAXR>);
+  int* wexp = reinterpret_cast<int*>(lds + WV * NT * kRegion<MAXR>);
 
   // 1. the lane's activations (first: waiting for them waits for nothing else)
   u32x4_t xv[NT][PL][4];
@@ -303,8 +303,17 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 #pragma unroll
   for (int t = 0; t < NT; ++t) ew[t] = 0;
   if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+    // (rare: the activations and codes are read again, so that their
+    // registers need not live through the products above)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const u32x4_t* xp =
+            reinterpret_cast<const u32x4_t*>(x + (size_t)t * K + 64 * gl + 32 * min(pc0 + i, max(P - 1, 0)));
+#pragma unroll
+        for (int d = 0; d < 4; ++d) xv[t][i][d] = xp[d];
+      }
       uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < PL; ++i)
@@ -323,9 +332,13 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
       for (int i = 0; i < PL; ++i) s8[i] = piece_dot(k8, xf[i]);
 #pragma unroll
       for (int j = 0; j < MAXR; ++j) {
+        const uint8_t* rp = codes + (size_t)(n0 + min(grp + R * j, rows - 1)) * (size_t)(K >> 1) + (size_t)gl * 32;
         float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < PL; ++i) a = __builtin_fmaf(sc[j][i], piece_dot(w[j][i], xf[i]) - s8[i], a);
+        for (int i = 0; i < PL; ++i) {
+          const u32x4_t wj = *reinterpret_cast<const u32x4_t*>(rp + 16 * min(pc0 + i, max(P - 1, 0)));
+          a = __builtin_fmaf(sc[j][i], piece_dot(wj, xf[i]) - s8[i], a);
+        }
         acc[t][j] = a;
       }
       ew[t] = e + 24;
@@ -352,10 +365,13 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 #pragma unroll
     for (int t = 0; t < NT; ++t) wexp[wave * NT + t] = ew[t];
   __syncthreads();
-  for (int idx = tid; idx < NT * rows * kWaves; idx += kThreads) {
-    const int wv = idx % kWaves, rt = idx / kWaves;
+  // (twelve waves: each thread leaves its wave's sum in LDS and one thread
+  // per (row, token) adds the twelve in wave order)
+  double* dsum = reinterpret_cast<double*>(lds + (((size_t)WV * NT * kRegion<MAXR> + (size_t)WV * NT * 4 + 7) & ~(size_t)7));
+  for (int idx = tid; idx < NT * rows * WV; idx += 64 * WV) {
+    const int wv = idx % WV, rt = idx / WV;
     const int t = NT == 1 ? 0 : rt / rows, r = rt - t * rows;
-    const int glw = (G * wv) / kWaves, ngw = (G * (wv + 1)) / kWaves - glw;
+    const int glw = (G * wv) / WV, ngw = (G * (wv + 1)) / WV - glw;
     const int Sw = max((2 * ngw + PL - 1) / PL, 1), Rw = 64 / Sw;
     const int g = r % Rw, j = r / Rw;
     const float* sp = reinterpret_cast<const float*>(lds + (wv * NT + t) * kRegion<MAXR>) + j * 64 + g * Sw;
@@ -385,11 +401,27 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
       for (; sl < Sw; ++sl) v0 += sp[sl];
     }
     double v = __builtin_ldexp((double)((v0 + v1) + (v2 + v3)), wexp[wv * NT + t]);
-    // the eight threads of a (row, token) are eight consecutive lanes of one wave
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    if (wv == 0) {
+    if constexpr (WV == 8) {
+      // the eight threads of a (row, token) are eight consecutive lanes of one wave
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      if (wv == 0) {
+        if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + n0 + r]);  // LinearAdd
+        if (p2.f32) reinterpret_cast<float*>(y)[(size_t)t * N + n0 + r] = (float)v;  // LinearSwiGLU sums
+        else y[(size_t)t * N + n0 + r] = f32_to_bf16_rne((float)v);
+      }
+    } else {
+      dsum[idx] = v;
+    }
+  }
+  if constexpr (WV != 8) {
+    __syncthreads();
+    for (int rt = tid; rt < NT * rows; rt += 64 * WV) {
+      const int t = NT == 1 ? 0 : rt / rows, r = rt - t * rows;
+      double v = 0.0;
+#pragma unroll
+      for (int wv = 0; wv < WV; ++wv) v += dsum[rt * WV + wv];
       if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + n0 + r]);  // LinearAdd
       if (p2.f32) reinterpret_cast<float*>(y)[(size_t)t * N + n0 + r] = (float)v;  // LinearSwiGLU sums
       else y[(size_t)t * N + n0 + r] = f32_to_bf16_rne((float)v);
@@ -397,18 +429,21 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   }
 }
 
-size_t decode_lds(int maxr, int nt) {
-  return (size_t)kWaves * (size_t)nt * (size_t)(64 * maxr * 4 + 16) + (size_t)kWaves * (size_t)nt * 4;
+// LDS bytes: per wave and token the scratch region, the waves' exponents,
+// and for twelve waves the per-wave sums of the bn rows (binary64)
+size_t decode_lds(int maxr, int nt, int wv, int64_t bn) {
+  const size_t base = (size_t)wv * (size_t)nt * (size_t)(64 * maxr * 4 + 16) + (size_t)wv * (size_t)nt * 4;
+  return wv == 8 ? base : ((base + 7) & ~(size_t)7) + (size_t)nt * (size_t)bn * (size_t)wv * 8;
 }
 
-template <int PL, int MAXR, int NT>
+template <int PL, int MAXR, int NT, int WV = 8>
 hipError_t launch_pm(const DecodePlan& p, const GemvArgs& a, hipStream_t stream) {
-  auto kern = decode_kernel<PL, MAXR, NT>;
-  const size_t lds = decode_lds(MAXR, NT);
+  auto kern = decode_kernel<PL, MAXR, NT, WV>;
+  const size_t lds = decode_lds(MAXR, NT, WV, p.bn);
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
   const int blocks1 = (int)((a.n + p.bn - 1) / p.bn), blocks2 = (int)((a.n2 + p.bn - 1) / p.bn);
-  kern<<<dim3((unsigned)(blocks1 + blocks2)), dim3(kThreads), lds, stream>>>(
+  kern<<<dim3((unsigned)(blocks1 + blocks2)), dim3(64 * WV), lds, stream>>>(
       static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
       static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, p.bn, static_cast<const uint16_t*>(a.res),
       second_plane(a, blocks1));
@@ -423,6 +458,34 @@ constexpr int kShapes[][2] = {{1, 8}, {2, 8}, {4, 4}, {1, 16}};
 
 }  // namespace
 
+// One lane shape (pl pieces per lane, at most maxr rows per lane) for wv
+// waves: the fewest workgroups per CU (up to cmax) whose blocks it covers.
+static bool plan_shape(int64_t n, int64_t G, int64_t t, int wv, int64_t pl, int64_t maxr, int64_t cmax,
+                       DecodePlan* p) {
+  const int64_t pmax = 2 * ((G + wv - 1) / wv);
+  const int64_t pmin = 2 * (G / wv);
+  const int64_t s = (pmax + pl - 1) / pl;
+  if (s > 64) return false;
+  // every wave, also one with the smaller slice, must cover bn rows
+  const int64_t smin = pmin > 0 ? (pmin + pl - 1) / pl : 1;
+  const int64_t rmin = 64 / (s > smin ? s : smin);
+  for (int64_t c = 1; c <= cmax; ++c) {  // workgroups per CU
+    const int64_t bn = (n + 256 * c - 1) / (256 * c);
+    if ((bn + rmin - 1) / rmin > maxr) continue;
+    // fewer than half the lanes busy: leave the shape to the other route
+    if (2 * rmin * s < 64 && bn > rmin) continue;
+    // c workgroups of this size must fit one CU's 160 KB of LDS
+    if (decode_lds((int)maxr, (int)t, wv, bn) * (size_t)c > 160 * 1024) continue;
+    p->bn = (int)bn;
+    p->pl = (int)pl;
+    p->maxr = (int)maxr;
+    p->waves = wv;
+    p->blocks = (int)((n + bn - 1) / bn);
+    return true;
+  }
+  return false;
+}
+
 // For each shape in turn, the fewest workgroups per CU (1..6, so blocks of
 // about N / (256 c) rows) whose rows the shape covers.  Measured on
 // 6144/14336/34816 x 5120 and 5120 x 17408: more, smaller blocks beat
@@ -433,34 +496,26 @@ bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p) {
   if (t < 1 || t > kMaxDecodeTokens || n < 1 || k < 64) return false;
   if (n * (k / 2) >= (int64_t(1) << 31)) return false;  // 32-bit buffer offsets
   const int64_t G = k / 64;
-  const int64_t pmax = 2 * ((G + kWaves - 1) / kWaves);
-  const int64_t pmin = 2 * (G / kWaves);
+  bool found = false;
   for (const auto& sh : kShapes) {
     const int64_t pl = sh[0], maxr = sh[1];
     if (t > 1 && !(pl == 1 && maxr == 8)) continue;
-    const int64_t s = (pmax + pl - 1) / pl;
-    if (s > 64) continue;
-    // every wave, also one with the smaller slice, must cover bn rows
-    const int64_t smin = pmin > 0 ? (pmin + pl - 1) / pl : 1;
-    const int64_t rmin = 64 / (s > smin ? s : smin);
-    // (with several tokens a workgroup takes every register a CU's SIMDs
-    // hold for two waves each: one workgroup per CU, c = 1 only; measured, a
-    // second round of workgroups costs more than the small-T route)
-    for (int64_t c = 1; c <= (t > 1 ? 1 : 6); ++c) {  // workgroups per CU
-      const int64_t bn = (n + 256 * c - 1) / (256 * c);
-      if ((bn + rmin - 1) / rmin > maxr) continue;
-      // fewer than half the lanes busy: leave the shape to the other route
-      if (2 * rmin * s < 64 && bn > rmin) continue;
-      // c workgroups of this size must fit one CU's 160 KB of LDS
-      if (decode_lds((int)maxr, (int)t) * (size_t)c > 160 * 1024) continue;
-      p->bn = (int)bn;
-      p->pl = (int)pl;
-      p->maxr = (int)maxr;
-      p->blocks = (int)((n + bn - 1) / bn);
+    if (plan_shape(n, G, t, kWaves, pl, maxr, t > 1 ? 1 : 6, p)) {
+      found = true;
+      break;
+    }
+  }
+  // A long row (K > 16384) needs two pieces per lane with eight waves; twelve
+  // waves keep one piece per lane, twenty rows each (3 waves per SIMD, one
+  // workgroup per CU).
+  if (t == 1 && (!found || p->pl > 1)) {
+    DecodePlan q;
+    if (plan_shape(n, G, t, 12, 1, 20, 1, &q)) {
+      *p = q;
       return true;
     }
   }
-  return false;
+  return found;
 }
 
 hipError_t launch_decode(const GemvArgs& a, hipStream_t stream) {
@@ -474,10 +529,10 @@ hipError_t launch_decode(const GemvArgs& a, hipStream_t stream) {
     const int64_t b = (a.n + p.bn - 1) / p.bn + (a.n2 + p.bn - 1) / p.bn;
     DecodePlan q;
     if (b <= p.blocks || !decode_plan(a.n + a.n2 + extra, a.k, a.t, &q)) break;
-    if (q.pl != p.pl || q.maxr != p.maxr) break;  // keep the kernel shape
+    if (q.pl != p.pl || q.maxr != p.maxr || q.waves != p.waves) break;  // keep the kernel shape
     p = q;
   }
-  if (p.pl == 1 && p.maxr == 8) {
+  if (p.waves == 8 && p.pl == 1 && p.maxr == 8) {
     switch (a.t) {
       case 1: return launch_pm<1, 8, 1>(p, a, stream);
       case 2: return launch_pm<1, 8, 2>(p, a, stream);
@@ -486,6 +541,7 @@ hipError_t launch_decode(const GemvArgs& a, hipStream_t stream) {
     }
   }
   if (a.t != 1) return hipErrorInvalidValue;
+  if (p.waves == 12) return p.pl == 1 && p.maxr == 20 ? launch_pm<1, 20, 1, 12>(p, a, stream) : hipErrorInvalidValue;
   if (p.pl == 1 && p.maxr == 16) return launch_pm<1, 16, 1>(p, a, stream);
   if (p.pl == 2 && p.maxr == 8) return launch_pm<2, 8, 1>(p, a, stream);
   if (p.pl == 4 && p.maxr == 4) return launch_pm<4, 4, 1>(p, a, stream);

@@ -57,6 +57,7 @@ struct DecodePlan {
   int pl;      // consecutive 16-byte pieces per lane and row
   int maxr;    // rows per lane, at most
   int blocks;  // workgroups
+  int waves;   // waves per workgroup (8, or 12 for long rows)
 };
 bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p);
 hipError_t launch_decode(const GemvArgs& a, hipStream_t stream);
