@@ -66,12 +66,15 @@ def test_pair_worked_examples(replicate):
 
 # (n1, n2, k, t): gate/up-like equal halves, uneven halves with ragged blocks,
 # one to four tokens (single-launch single-token route), small T (single
-# launch, matrix cores), many tokens (one launch sequence per weight) and a
-# wide K (few-token vector route)
+# launch, matrix cores), medium T (one launch sequence per weight), many
+# tokens (one activation preparation and one launch for both weights' tiles:
+# whole tiles, ragged tiles with a K split over three workgroups, tiny
+# weights) and a wide K (few-token vector route)
 @pytest.mark.parametrize("n1,n2,k,t", [(3072, 3072, 5120, 1), (1000, 333, 2048, 1), (2048, 2048, 1024, 4),
                                        (6144, 1024, 5120, 2), (1000, 700, 2048, 20), (517, 1531, 1280, 9),
                                        (768, 256, 1024, 100), (97, 160, 320, 40), (128, 256, 20480, 3),
-                                       (2560, 1000, 17408, 1)])
+                                       (2560, 1000, 17408, 1), (3072, 3072, 1024, 300), (1000, 700, 2048, 200),
+                                       (97, 33, 320, 1000)])
 def test_pair_matches_oracle(n1, n2, k, t):
     x, c1, s1 = inputs.gen_problem(n1, k, t, 71)
     _, c2, s2 = inputs.gen_problem(n2, k, t, 73)

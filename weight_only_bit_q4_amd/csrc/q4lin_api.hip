@@ -120,6 +120,12 @@ int check_linear(const void* x, const void* codes, const void* scales, const voi
   return Q4LIN_OK;
 }
 
+// Two weights over one X take the many-token route together when the route
+// for their rows is that one (shared activation preparation, one launch).
+bool pair_on_tiled(int route, int64_t n1, int64_t n2, int64_t k, int64_t t) {
+  return route == Q4LIN_ROUTE_TILED && q4lin::tiled_shape_ok(n1, k, t) && q4lin::tiled_shape_ok(n2, k, t);
+}
+
 // The op, with an optional residual (LinearAdd when res is not null).
 int run_linear(const void* x, const void* codes, const void* scales, const void* res, void* y,
                int64_t n, int64_t k, int64_t t, void* workspace, size_t workspace_bytes, void* stream) {
@@ -164,25 +170,27 @@ enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3, SW_MID = 4 };
 struct SwigluPlan {
   int mode;
   int route;
-  size_t half;  // bytes of each weight's half of the workspace
+  size_t half;   // bytes of each weight's half of the workspace (TILED: unused)
+  size_t total;  // workspace bytes
 };
 
 bool swiglu_plan(int64_t n, int64_t k, int64_t t, SwigluPlan* p) {
   if (!shape_ok(n, k, t) || !shape_ok(2 * n, k, t) || !shape_ok(n, k, 2 * t)) return false;
   const int r2 = pick_route(2 * n, k, t);
   if (r2 == Q4LIN_ROUTE_DECODE || r2 == Q4LIN_ROUTE_SKINNY) {
-    *p = SwigluPlan{SW_FUSED, r2, al256((size_t)(n * t * 4))};
+    *p = SwigluPlan{SW_FUSED, r2, al256((size_t)(n * t * 4)), 2 * al256((size_t)(n * t * 4))};
     return true;
   }
   const int r1 = pick_route(n, k, t);
   if (r1 == Q4LIN_ROUTE_TILED && !q4lin::tiled_shape_ok(n, k, t)) return false;
   if (r1 == Q4LIN_ROUTE_TILED) {
-    *p = SwigluPlan{SW_TILED, r1, al256(q4lin::tiled_workspace_bytes_f32(n, k, t))};
+    *p = SwigluPlan{SW_TILED, r1, 0, q4lin::tiled_pair_workspace_bytes(n, n, k, t, true)};
   } else if (r1 == Q4LIN_ROUTE_MID) {
-    *p = SwigluPlan{SW_MID, r1,
-                    al256((size_t)(n * t * 4)) + (mid_uses_fmt(n, k, t) ? 0 : al256(q4lin::mid_workspace_bytes(n, k, t)))};
+    const size_t half =
+        al256((size_t)(n * t * 4)) + (mid_uses_fmt(n, k, t) ? 0 : al256(q4lin::mid_workspace_bytes(n, k, t)));
+    *p = SwigluPlan{SW_MID, r1, half, 2 * half};
   } else {
-    *p = SwigluPlan{SW_SPLIT, r1, al256((size_t)(n * t * 4))};
+    *p = SwigluPlan{SW_SPLIT, r1, al256((size_t)(n * t * 4)), 2 * al256((size_t)(n * t * 4))};
   }
   return true;
 }
@@ -288,7 +296,7 @@ int64_t q4lin_swiglu_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   SwigluPlan p;
   if (!swiglu_plan(n, k, t, &p)) return -Q4LIN_E_SHAPE;
   if (n == 0 || t == 0) return 0;
-  return (int64_t)(2 * p.half);
+  return (int64_t)p.total;
 }
 
 int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scales_gate, const void* codes_up,
@@ -301,7 +309,7 @@ int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scale
   if (!aligned(x, 16) || !aligned(codes_gate, 16) || !aligned(scales_gate, 2) || !aligned(codes_up, 16) ||
       !aligned(scales_up, 2) || !aligned(y, 2))
     return Q4LIN_E_ALIGN;
-  if (workspace_bytes < 2 * p.half) return Q4LIN_E_WORKSPACE;
+  if (workspace_bytes < p.total) return Q4LIN_E_WORKSPACE;
   if (!workspace) return Q4LIN_E_NULL;
   if (!aligned(workspace, 256)) return Q4LIN_E_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -338,13 +346,12 @@ int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scale
       e = mid_uses_fmt(n, k, t) ? q4lin::launch_fmt(q4_fmt_args(b), s) : q4lin::launch_mid(b, w1 + sums, s);
     }
   } else {
-    const q4lin::TiledConfig cfg = q4lin::tiled_pick_config(n, k, t);
-    q4lin::TiledArgs a{x, codes_gate, scales_gate, y, n, k, t, w0, cfg};
-    e = q4lin::launch_tiled_f32(a, &sg, s);
-    if (e == hipSuccess) {
-      q4lin::TiledArgs b{x, codes_up, scales_up, y, n, k, t, w1, cfg};
-      e = q4lin::launch_tiled_f32(b, &su, s);
-    }
+    // both weights' tiles in one launch after one activation preparation;
+    // their raw binary32 sums stay in the workspace for the combine
+    q4lin::TiledArgs a{x, codes_gate, scales_gate, y, n, k, t, w0, q4lin::tiled_pick_config(2 * n, k, t)};
+    a.f32 = true;
+    const q4lin::TiledPairArgs pa{a, codes_up, scales_up, y, n};
+    e = q4lin::launch_tiled_pair(pa, &sg, &su, s);
   }
   if (e == hipSuccess) e = q4lin::launch_swiglu_combine(sg, su, y, n, t, s);
   return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
@@ -378,8 +385,26 @@ int q4lin_linear_pair(const void* x, const void* codes1, const void* scales1, vo
                    : run_linear(x, codes2, scales2, nullptr, y2, n2, k, t, workspace, workspace_bytes, stream);
   }
   const int route = pick_route(n1 + n2, k, t);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pair_on_tiled(route, n1, n2, k, t)) {
+    // the many-token route: one activation preparation, one launch for both
+    // weights' tiles
+    if (!x || !codes1 || !scales1 || !y1 || !codes2 || !scales2 || !y2) return Q4LIN_E_NULL;
+    if (!aligned(x, 16) || !aligned(codes1, 16) || !aligned(scales1, 2) || !aligned(y1, 2) ||
+        !aligned(codes2, 16) || !aligned(scales2, 2) || !aligned(y2, 2))
+      return Q4LIN_E_ALIGN;
+    const size_t need = q4lin::tiled_pair_workspace_bytes(n1, n2, k, t, false);
+    if (workspace_bytes < need) return Q4LIN_E_WORKSPACE;
+    if (!workspace) return Q4LIN_E_NULL;
+    if (!aligned(workspace, 256)) return Q4LIN_E_ALIGN;
+    q4lin::TiledPairArgs pa{q4lin::TiledArgs{x, codes1, scales1, y1, n1, k, t, workspace,
+                                              q4lin::tiled_pick_config(n1 + n2, k, t)},
+                            codes2, scales2, y2, n2};
+    const hipError_t e = q4lin::launch_tiled_pair(pa, nullptr, nullptr, s);
+    return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+  }
   if (route != Q4LIN_ROUTE_DECODE && route != Q4LIN_ROUTE_SKINNY) {
-    // the many-token and wide-K routes: one launch sequence per weight
+    // the medium-T and wide-K routes: one launch sequence per weight
     const int s1 = run_linear(x, codes1, scales1, nullptr, y1, n1, k, t, workspace, workspace_bytes, stream);
     if (s1 != Q4LIN_OK) return s1;
     return run_linear(x, codes2, scales2, nullptr, y2, n2, k, t, workspace, workspace_bytes, stream);
@@ -393,7 +418,6 @@ int q4lin_linear_pair(const void* x, const void* codes1, const void* scales1, vo
   ga.scales2 = scales2;
   ga.y2 = y2;
   ga.n2 = n2;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = route == Q4LIN_ROUTE_DECODE ? q4lin::launch_decode(ga, s) : q4lin::launch_skinny(ga, s);
   return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
 }
@@ -402,6 +426,8 @@ int64_t q4lin_pair_workspace_bytes(int64_t n1, int64_t n2, int64_t k, int64_t t)
   if (!shape_ok(n1, k, t) || !shape_ok(n2, k, t) || !shape_ok(n1 + n2, k, t)) return -Q4LIN_E_SHAPE;
   const int route = pick_route(n1 + n2, k, t);
   if (n1 > 0 && n2 > 0 && (route == Q4LIN_ROUTE_DECODE || route == Q4LIN_ROUTE_SKINNY)) return 0;
+  if (n1 > 0 && n2 > 0 && t > 0 && pair_on_tiled(route, n1, n2, k, t))
+    return (int64_t)q4lin::tiled_pair_workspace_bytes(n1, n2, k, t, false);
   const size_t w1 = route_workspace(pick_route(n1, k, t), n1, k, t);
   const size_t w2 = route_workspace(pick_route(n2, k, t), n2, k, t);
   return (int64_t)(w1 > w2 ? w1 : w2);

@@ -111,6 +111,35 @@ struct SumSource {
   size_t stride;
 };
 
+// The second weight of a LinearPair / LinearSwiGLU on the many-token route,
+// as the tiled kernel sees it: the workgroups from `first` on serve it.
+struct TiledPlane2 {
+  const uint8_t* codes = nullptr;
+  const uint16_t* scales = nullptr;
+  uint16_t* y = nullptr;
+  float* part = nullptr;     // its partial sums (K split or binary32 sums)
+  const int* rexp = nullptr;  // its row exponents
+  int n = 0;                 // rows (0: no second weight)
+  int tiles_n = 0;           // its row tiles
+  int first = 0;             // its first workgroup
+};
+
+// Two weights over one X on the many-token route: one activation
+// preparation (it also takes both weights' row exponents) and one launch
+// whose workgroups cover both weights' tiles (the second's after the
+// first's); the K-split sums, if any, are added per weight.  Workspace: the
+// activations once, then each weight's row exponents and partials.
+struct TiledPairArgs {
+  TiledArgs a;  // x, the first weight, y, n, k, t, workspace, cfg (for n + n2 rows), f32
+  const void* codes2;
+  const void* scales2;
+  void* y2;
+  int64_t n2;
+};
+size_t tiled_pair_workspace_bytes(int64_t n1, int64_t n2, int64_t k, int64_t t, bool f32);
+// src1/src2 (binary32 sums only) receive where each weight's sums are
+hipError_t launch_tiled_pair(const TiledPairArgs& p, SumSource* src1, SumSource* src2, hipStream_t stream);
+
 int64_t tiled_tpad(int64_t t);
 // Whether the tiled kernels can address (n, k, t): their buffer offsets are
 // 32-bit, so the float16 activation copy (tpad * k * 2 bytes) and the scale
@@ -119,11 +148,6 @@ bool tiled_shape_ok(int64_t n, int64_t k, int64_t t);
 size_t tiled_workspace_bytes(int64_t n, int64_t k, int64_t t);
 TiledConfig tiled_pick_config(int64_t n, int64_t k, int64_t t);
 hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream);
-// LinearSwiGLU's many-token leg: the tiled kernel with its raw FP32 sums left
-// in the workspace's partials (no bf16 pass); *src then describes them.  The
-// workspace must hold tiled_workspace_bytes_f32(n, k, t).
-size_t tiled_workspace_bytes_f32(int64_t n, int64_t k, int64_t t);
-hipError_t launch_tiled_f32(const TiledArgs& a, SumSource* src, hipStream_t stream);
 // y[t][n] = bf16(silu(G) * U), G and U from the two sources ([T][N] each).
 hipError_t launch_swiglu_combine(const SumSource& g, const SumSource& u, void* y, int64_t n, int64_t t,
                                  hipStream_t stream);

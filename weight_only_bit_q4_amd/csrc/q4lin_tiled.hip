@@ -154,9 +154,13 @@ template <int MAXJ, int TOK>
 __global__ void __launch_bounds__(kPrepThreads)
 prep_act_kernel(const u32x4_t* __restrict__ x, int K, int T, int Tpad, int* __restrict__ texp,
                 u32x4_t* __restrict__ x16, const uint16_t* __restrict__ scales, int N, int* __restrict__ rexp,
-                int tok_blocks) {
+                int tok_blocks, int row_blocks1, const uint16_t* __restrict__ scales2, int N2,
+                int* __restrict__ rexp2) {
   if ((int)blockIdx.x >= tok_blocks) {
-    row_exponents(scales, N, K >> 6, ((int)blockIdx.x - tok_blocks) * kRowsPerBlock, rexp);
+    // the row exponents of the weight (and of a second weight after it)
+    const int rb = (int)blockIdx.x - tok_blocks;
+    if (rb < row_blocks1) row_exponents(scales, N, K >> 6, rb * kRowsPerBlock, rexp);
+    else row_exponents(scales2, N2, K >> 6, (rb - row_blocks1) * kRowsPerBlock, rexp2);
     return;
   }
   constexpr int SUBS = 64 / TOK;                         // lanes per token in a wave
@@ -386,7 +390,7 @@ __global__ void __launch_bounds__(64 * WN * WT)
 tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, const int* __restrict__ rexp,
              const uint16_t* __restrict__ xraw, const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
              uint16_t* y, float* __restrict__ part, int N, int K, int T, int Tpad, int tiles_n,
-             int tiles_t, int KS, const uint16_t* res) {
+             int tiles_t, int KS, const uint16_t* res, TiledPlane2 p2) {
   using Sh = TiledShape<NS, TS, WN, WT>;
   constexpr int NT = Sh::NT, BN = Sh::BN, BT = Sh::BT, CD = Sh::CD, CQ = Sh::CQ, CP = Sh::CP, AI = Sh::AI, SQ = Sh::SQ;
   constexpr int NW = WN * WT;
@@ -395,8 +399,20 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   const int G = K >> 6;
   // K split: the workgroup's share is the Gs groups from g0 (all of K when KS
   // is 1); inside the kernel groups are counted from g0
+  // two weights: the workgroups from p2.first on serve the second
+  int wgi = (int)blockIdx.x;
+  if (p2.n > 0 && wgi >= p2.first) {
+    codes = p2.codes;
+    scales = p2.scales;
+    y = p2.y;
+    part = p2.part;
+    rexp = p2.rexp;
+    N = p2.n;
+    tiles_n = p2.tiles_n;
+    wgi -= p2.first;
+  }
   const int nblk = tiles_n * tiles_t;
-  const int ks = blockIdx.x / nblk, bidx = blockIdx.x - ks * nblk;
+  const int ks = wgi / nblk, bidx = wgi - ks * nblk;
   const int g0 = (int)(((int64_t)G * ks) / KS);
   const int Gs = (int)(((int64_t)G * (ks + 1)) / KS) - g0;
   const int tid = threadIdx.x;
@@ -882,9 +898,19 @@ tiled_reduce_kernel(const float* __restrict__ part, const int* __restrict__ texp
   y[i] = h;
 }
 
+// The weight's tiles (and a second weight's after them); the K-split sums
+// of each weight, if any, added by a pass per weight.
+struct Plane2Host {
+  const void* codes = nullptr;
+  const void* scales = nullptr;
+  void* y = nullptr;
+  float* part = nullptr;
+  const int* rexp = nullptr;
+  int64_t n = 0;
+};
 template <int NS, int TS, int WN, int WT>
 hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, const int* rexp, float* part,
-                      int tpad, hipStream_t stream) {
+                      int tpad, hipStream_t stream, const Plane2Host& h2 = Plane2Host{}) {
   using Sh = TiledShape<NS, TS, WN, WT>;
   const int tiles_n = (int)((a.n + Sh::BN - 1) / Sh::BN);
   const int tiles_t = (int)((a.t + Sh::BT - 1) / Sh::BT);
@@ -893,16 +919,36 @@ hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, c
   if (e != hipSuccess) return e;
   const int ks = a.cfg.ks;
   if (ks < 1 || ks > kMaxSplits) return hipErrorInvalidValue;
-  kern<<<dim3((unsigned)(tiles_n * tiles_t * ks)), dim3(Sh::NT), Sh::LDS_B, stream>>>(
+  const bool keep_part = ks > 1 || a.f32;
+  TiledPlane2 p2;
+  int blocks = tiles_n * tiles_t * ks;
+  if (h2.n > 0) {
+    p2.codes = static_cast<const uint8_t*>(h2.codes);
+    p2.scales = static_cast<const uint16_t*>(h2.scales);
+    p2.y = static_cast<uint16_t*>(h2.y);
+    p2.part = keep_part ? h2.part : nullptr;
+    p2.rexp = h2.rexp;
+    p2.n = (int)h2.n;
+    p2.tiles_n = (int)((h2.n + Sh::BN - 1) / Sh::BN);
+    p2.first = blocks;
+    blocks += p2.tiles_n * tiles_t * ks;
+  }
+  kern<<<dim3((unsigned)blocks), dim3(Sh::NT), Sh::LDS_B, stream>>>(
       x16, texp, rexp, static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes),
       static_cast<const uint16_t*>(a.scales),
-      static_cast<uint16_t*>(a.y), (ks > 1 || a.f32) ? part : nullptr, (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t, ks,
-      static_cast<const uint16_t*>(a.res));
+      static_cast<uint16_t*>(a.y), keep_part ? part : nullptr, (int)a.n, (int)a.k, (int)a.t, tpad, tiles_n, tiles_t, ks,
+      static_cast<const uint16_t*>(a.res), p2);
   e = hipGetLastError();
   if (e != hipSuccess || ks == 1 || a.f32) return e;
   tiled_reduce_kernel<<<dim3((unsigned)((a.n + 255) / 256), (unsigned)a.t), dim3(256), 0, stream>>>(
       part, texp, rexp, static_cast<uint16_t*>(a.y), (int)a.n, tpad, ks, static_cast<const uint16_t*>(a.res),
       static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
+      (int)a.k);
+  e = hipGetLastError();
+  if (e != hipSuccess || h2.n == 0) return e;
+  tiled_reduce_kernel<<<dim3((unsigned)((h2.n + 255) / 256), (unsigned)a.t), dim3(256), 0, stream>>>(
+      h2.part, texp, h2.rexp, static_cast<uint16_t*>(h2.y), (int)h2.n, tpad, ks, nullptr,
+      static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(h2.codes), static_cast<const uint16_t*>(h2.scales),
       (int)a.k);
   return hipGetLastError();
 }
@@ -954,25 +1000,54 @@ size_t tiled_workspace_bytes(int64_t n, int64_t k, int64_t t) {
   return align256((size_t)(tp * k * 2)) + align256((size_t)(tp * 4)) + align256((size_t)(n * 4)) + part;
 }
 
-size_t tiled_workspace_bytes_f32(int64_t n, int64_t k, int64_t t) {
-  const int64_t tp = tiled_tpad(t);
-  const TiledConfig c = tiled_pick_config(n, k, t);
-  return align256((size_t)(tp * k * 2)) + align256((size_t)(tp * 4)) + align256((size_t)(n * 4)) +
-         align256((size_t)c.ks * (size_t)tp * (size_t)n * 4);
+namespace {
+
+// The activation preparation: X into float16 tiles with the token exponents,
+// and the row exponents of the weight (and of a second weight).
+hipError_t launch_prep(const TiledArgs& a, u32x4_t* x16, int* texp, int* rexp, const void* scales2, int64_t n2,
+                       int* rexp2, hipStream_t stream) {
+  const int64_t tp = tiled_tpad(a.t);
+  const u32x4_t* x = static_cast<const u32x4_t*>(a.x);
+  int k = (int)a.k, t = (int)a.t, n = (int)a.n, tpad = (int)tp;
+  const int tok = prep_tokens(a.t);
+  const int tok_blocks = (int)(tp / tok);
+  const int row_blocks = (int)((a.n + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int row_blocks2 = (int)((n2 + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int nwv = kPrepThreads / 64;
+  const int nj = (int)(((a.k / 8 + nwv - 1) / nwv + 64 / tok - 1) / (64 / tok));  // pieces per lane
+  const dim3 grid((unsigned)(tok_blocks + row_blocks + row_blocks2)), block(kPrepThreads);
+  const uint16_t* sc = static_cast<const uint16_t*>(a.scales);
+  const uint16_t* sc2 = static_cast<const uint16_t*>(scales2);
+  const int n2i = (int)n2;
+  // longer rows (nj > 10) take the chunked two-pass form of the kernel
+  const int mj = nj <= 2 ? 2 : nj <= 5 ? 5 : 10;
+  auto launch = [&](auto kern) {
+    kern<<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks, row_blocks, sc2, n2i, rexp2);
+  };
+  if (tok == 2) {
+    if (mj == 2) launch(prep_act_kernel<2, 2>);
+    else if (mj == 5) launch(prep_act_kernel<5, 2>);
+    else launch(prep_act_kernel<10, 2>);
+  } else {
+    if (mj == 2) launch(prep_act_kernel<2, 4>);
+    else if (mj == 5) launch(prep_act_kernel<5, 4>);
+    else launch(prep_act_kernel<10, 4>);
+  }
+  return hipGetLastError();
 }
 
-hipError_t launch_tiled_f32(const TiledArgs& a, SumSource* src, hipStream_t stream) {
-  TiledArgs b = a;
-  b.f32 = true;
-  b.res = nullptr;
-  const int64_t tp = tiled_tpad(a.t);
-  uint8_t* w = static_cast<uint8_t*>(a.workspace);
-  const int* texp = reinterpret_cast<const int*>(w + align256((size_t)(tp * a.k * 2)));
-  const int* rexp = reinterpret_cast<const int*>(reinterpret_cast<const uint8_t*>(texp) + align256((size_t)(tp * 4)));
-  const float* part = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(rexp) + align256((size_t)(a.n * 4)));
-  *src = SumSource{part, texp, rexp, a.cfg.ks, (size_t)tp * (size_t)a.n};
-  return launch_tiled(b, stream);
+hipError_t launch_shape(const TiledArgs& a, const u32x4_t* x16, const int* texp, const int* rexp, float* part,
+                        int tpad, hipStream_t stream, const Plane2Host& h2) {
+  const TiledConfig c = a.cfg;
+  if (c.ns == 3 && c.ts == 2 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 2, 2, 2>(a, x16, texp, rexp, part, tpad, stream, h2);
+  if (c.ns == 3 && c.ts == 1 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 1, 2, 2>(a, x16, texp, rexp, part, tpad, stream, h2);
+  if (c.ns == 3 && c.ts == 2 && c.wn == 1 && c.wt == 4) return launch_cfg<3, 2, 1, 4>(a, x16, texp, rexp, part, tpad, stream, h2);
+  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 4) return launch_cfg<1, 1, 1, 4>(a, x16, texp, rexp, part, tpad, stream, h2);
+  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 1) return launch_cfg<1, 1, 1, 1>(a, x16, texp, rexp, part, tpad, stream, h2);
+  return hipErrorInvalidValue;
 }
+
+}  // namespace
 
 hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   const int64_t tp = tiled_tpad(a.t);
@@ -980,39 +1055,51 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream) {
   int* texp = reinterpret_cast<int*>(static_cast<uint8_t*>(a.workspace) + align256((size_t)(tp * a.k * 2)));
   int* rexp = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(texp) + align256((size_t)(tp * 4)));
   float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(rexp) + align256((size_t)(a.n * 4)));
-  {
-    const u32x4_t* x = static_cast<const u32x4_t*>(a.x);
-    int k = (int)a.k, t = (int)a.t, n = (int)a.n, tpad = (int)tp;
-    const int tok = prep_tokens(a.t);
-    const int tok_blocks = (int)(tp / tok);
-    const int row_blocks = (int)((a.n + kRowsPerBlock - 1) / kRowsPerBlock);
-    const int nwv = kPrepThreads / 64;
-    const int nj = (int)(((a.k / 8 + nwv - 1) / nwv + 64 / tok - 1) / (64 / tok));  // pieces per lane
-    const dim3 grid((unsigned)(tok_blocks + row_blocks)), block(kPrepThreads);
-    const uint16_t* sc = static_cast<const uint16_t*>(a.scales);
-    // longer rows (nj > 10) take the chunked two-pass form of the kernel
-    const int mj = nj <= 2 ? 2 : nj <= 5 ? 5 : 10;
-    auto launch = [&](auto kern) { kern<<<grid, block, 0, stream>>>(x, k, t, tpad, texp, x16, sc, n, rexp, tok_blocks); };
-    if (tok == 2) {
-      if (mj == 2) launch(prep_act_kernel<2, 2>);
-      else if (mj == 5) launch(prep_act_kernel<5, 2>);
-      else launch(prep_act_kernel<10, 2>);
-    } else {
-      if (mj == 2) launch(prep_act_kernel<2, 4>);
-      else if (mj == 5) launch(prep_act_kernel<5, 4>);
-      else launch(prep_act_kernel<10, 4>);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int tpad = (int)tp;
-  const TiledConfig c = a.cfg;
-  if (c.ns == 3 && c.ts == 2 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 2, 2, 2>(a, x16, texp, rexp, part, tpad, stream);
-  if (c.ns == 3 && c.ts == 1 && c.wn == 2 && c.wt == 2) return launch_cfg<3, 1, 2, 2>(a, x16, texp, rexp, part, tpad, stream);
-  if (c.ns == 3 && c.ts == 2 && c.wn == 1 && c.wt == 4) return launch_cfg<3, 2, 1, 4>(a, x16, texp, rexp, part, tpad, stream);
-  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 4) return launch_cfg<1, 1, 1, 4>(a, x16, texp, rexp, part, tpad, stream);
-  if (c.ns == 1 && c.ts == 1 && c.wn == 1 && c.wt == 1) return launch_cfg<1, 1, 1, 1>(a, x16, texp, rexp, part, tpad, stream);
-  return hipErrorInvalidValue;
+  hipError_t e = launch_prep(a, x16, texp, rexp, nullptr, 0, nullptr, stream);
+  if (e != hipSuccess) return e;
+  return launch_shape(a, x16, texp, rexp, part, (int)tp, stream, Plane2Host{});
+}
+
+// Pair workspace: activations, token exponents, row exponents of each
+// weight, then (K split or binary32 sums) each weight's partials
+// [split][Tpad][N].
+size_t tiled_pair_workspace_bytes(int64_t n1, int64_t n2, int64_t k, int64_t t, bool f32) {
+  const int64_t tp = tiled_tpad(t);
+  const TiledConfig c = tiled_pick_config(n1 + n2, k, t);
+  const bool keep = c.ks > 1 || f32;
+  return align256((size_t)(tp * k * 2)) + align256((size_t)(tp * 4)) + align256((size_t)(n1 * 4)) +
+         align256((size_t)(n2 * 4)) + (keep ? align256((size_t)c.ks * (size_t)tp * (size_t)n1 * 4) : 0) +
+         (keep ? align256((size_t)c.ks * (size_t)tp * (size_t)n2 * 4) : 0);
+}
+
+hipError_t launch_tiled_pair(const TiledPairArgs& p, SumSource* src1, SumSource* src2, hipStream_t stream) {
+  const TiledArgs& a = p.a;
+  const int64_t tp = tiled_tpad(a.t);
+  uint8_t* w = static_cast<uint8_t*>(a.workspace);
+  u32x4_t* x16 = reinterpret_cast<u32x4_t*>(w);
+  w += align256((size_t)(tp * a.k * 2));
+  int* texp = reinterpret_cast<int*>(w);
+  w += align256((size_t)(tp * 4));
+  int* rexp1 = reinterpret_cast<int*>(w);
+  w += align256((size_t)(a.n * 4));
+  int* rexp2 = reinterpret_cast<int*>(w);
+  w += align256((size_t)(p.n2 * 4));
+  const bool keep = a.cfg.ks > 1 || a.f32;
+  float* part1 = reinterpret_cast<float*>(w);
+  w += keep ? align256((size_t)a.cfg.ks * (size_t)tp * (size_t)a.n * 4) : 0;
+  float* part2 = reinterpret_cast<float*>(w);
+  hipError_t e = launch_prep(a, x16, texp, rexp1, p.scales2, p.n2, rexp2, stream);
+  if (e != hipSuccess) return e;
+  Plane2Host h2;
+  h2.codes = p.codes2;
+  h2.scales = p.scales2;
+  h2.y = p.y2;
+  h2.part = part2;
+  h2.rexp = rexp2;
+  h2.n = p.n2;
+  if (src1 != nullptr) *src1 = SumSource{part1, texp, rexp1, a.cfg.ks, (size_t)tp * (size_t)a.n};
+  if (src2 != nullptr) *src2 = SumSource{part2, texp, rexp2, a.cfg.ks, (size_t)tp * (size_t)p.n2};
+  return launch_shape(a, x16, texp, rexp1, part1, (int)tp, stream, h2);
 }
 
 }  // namespace q4lin
