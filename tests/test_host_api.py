@@ -193,7 +193,12 @@ def test_linear_swiglu_checks():
     assert q.q4lin_swiglu_workspace_bytes(0, 128, 5) == 0
     assert q.q4lin_linear_swiglu(p, p, p, p, p, p, 8, 96, 1, 0, 0, 0) == q.Q4LIN_E_SHAPE
     assert q.q4lin_swiglu_workspace_bytes(8, 96, 1) == -q.Q4LIN_E_SHAPE
-    for n, k, t in [(6144, 5120, 1), (1000, 2048, 20), (768, 1024, 100), (128, 20480, 3)]:
+    # one to four tokens on the single-token route: one pass, no workspace
+    # (a null workspace is accepted)
+    assert q.q4lin_swiglu_workspace_bytes(6144, 5120, 1) == 0
+    assert q.q4lin_swiglu_workspace_bytes(2048, 1024, 4) == 0
+    assert q.q4lin_linear_swiglu(p, p, p, p, p, p + 1, 6144, 5120, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
+    for n, k, t in [(1000, 2048, 20), (768, 1024, 100), (128, 20480, 3)]:
         need = q.q4lin_swiglu_workspace_bytes(n, k, t)
         assert need >= 2 * n * t * 4 and need % 256 == 0
         assert q.q4lin_linear_swiglu(p, p, p, p, p, p, n, k, t, p, need - 1, 0) == q.Q4LIN_E_WORKSPACE

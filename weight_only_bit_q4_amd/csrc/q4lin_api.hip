@@ -166,7 +166,7 @@ size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 //          partials of a workspace half each.
 //   MID:   the medium-T route per weight, binary32 sums (the split-K
 //          kernel's partials after the sums in each half).
-enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3, SW_MID = 4 };
+enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3, SW_MID = 4, SW_GLU = 5 };
 struct SwigluPlan {
   int mode;
   int route;
@@ -177,6 +177,10 @@ struct SwigluPlan {
 bool swiglu_plan(int64_t n, int64_t k, int64_t t, SwigluPlan* p) {
   if (!shape_ok(n, k, t) || !shape_ok(2 * n, k, t) || !shape_ok(n, k, 2 * t)) return false;
   const int r2 = pick_route(2 * n, k, t);
+  if (r2 == Q4LIN_ROUTE_DECODE && q4lin::decode_glu_ok(n, k, t)) {
+    *p = SwigluPlan{SW_GLU, r2, 0, 0};
+    return true;
+  }
   if (r2 == Q4LIN_ROUTE_DECODE || r2 == Q4LIN_ROUTE_SKINNY) {
     *p = SwigluPlan{SW_FUSED, r2, al256((size_t)(n * t * 4)), 2 * al256((size_t)(n * t * 4))};
     return true;
@@ -310,14 +314,27 @@ int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scale
       !aligned(scales_up, 2) || !aligned(y, 2))
     return Q4LIN_E_ALIGN;
   if (workspace_bytes < p.total) return Q4LIN_E_WORKSPACE;
-  if (!workspace) return Q4LIN_E_NULL;
-  if (!aligned(workspace, 256)) return Q4LIN_E_ALIGN;
+  if (p.total > 0) {
+    if (!workspace) return Q4LIN_E_NULL;
+    if (!aligned(workspace, 256)) return Q4LIN_E_ALIGN;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* w0 = static_cast<uint8_t*>(workspace);
   uint8_t* w1 = w0 + p.half;
   q4lin::SumSource sg{reinterpret_cast<const float*>(w0), nullptr, nullptr, 1, 0};
   q4lin::SumSource su{reinterpret_cast<const float*>(w1), nullptr, nullptr, 1, 0};
   hipError_t e = hipSuccess;
+  if (p.mode == SW_GLU) {
+    // one pass: every workgroup takes the same rows of both weights and
+    // stores bf16(silu(G) U) itself
+    q4lin::GemvArgs a{x, codes_gate, scales_gate, y, n, k, t};
+    a.codes2 = codes_up;
+    a.scales2 = scales_up;
+    a.n2 = n;
+    a.glu = true;
+    e = q4lin::launch_decode(a, s);
+    return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+  }
   if (p.mode == SW_FUSED) {
     q4lin::GemvArgs a{x, codes_gate, scales_gate, w0, n, k, t};
     a.codes2 = codes_up;

@@ -162,7 +162,9 @@ __device__ __forceinline__ float piece_dot_pre(const uint32_t (&c)[16], const u3
 // piece of X, converts each code piece once and runs one dot chain per token
 // (vector-ALU work grows with NT, the weight stream does not: a few tokens
 // cost little more than one).
-template <int PL, int MAXR, int NT, int WV>
+// WV: waves per workgroup (8, or 12 for long rows); GLU: LinearSwiGLU in one
+// pass (each workgroup takes the same rows of the gate and the up weight).
+template <int PL, int MAXR, int NT, int WV, bool GLU>
 __global__ void __launch_bounds__(64 * WV)
 decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
               uint16_t* y, int N, int K, int BN, const uint16_t* res, SecondPlane p2) {
@@ -171,7 +173,8 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bid = blockIdx.x;
-  if (p2.n > 0 && bid >= p2.first) {  // LinearPair: the second weight
+  constexpr bool glu = GLU;
+  if (!glu && p2.n > 0 && bid >= p2.first) {  // LinearPair: the second weight
     codes = p2.codes;
     scales = p2.scales;
     y = p2.y;
@@ -179,8 +182,24 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     res = nullptr;  // a pair carries no residual
     bid -= p2.first;
   }
-  const int n0 = bid * BN;
-  const int rows = min(BN, N - n0);
+  // LinearSwiGLU: the block's rows are hrows gate rows from n0, then the
+  // same rows of the up weight
+  const int n0 = glu ? bid * (BN >> 1) : bid * BN;
+  const int hrows = glu ? min(BN >> 1, N - n0) : 0;
+  const int rows = glu ? 2 * hrows : min(BN, N - n0);
+  // local row lr of the block (clamped to its rows): the planes it reads and
+  // its row there
+  auto plane_row = [&](int lr, const uint8_t*& cp, const uint16_t*& sp) __device__ {
+    lr = min(lr, rows - 1);
+    if (glu && lr >= hrows) {
+      cp = p2.codes;
+      sp = p2.scales;
+      return n0 + lr - hrows;
+    }
+    cp = codes;
+    sp = scales;
+    return n0 + lr;
+  };
 
   // wave slice, slots and row groups (all wave-uniform but the lane's own)
   const int gl = (G * wave) / WV, gh = (G * (wave + 1)) / WV;
@@ -218,8 +237,10 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   u32x4_t w[MAXR][PL];
 #pragma unroll
   for (int j = 0; j < MAXR; ++j) {
-    const int row = n0 + min(grp + R * j, rows - 1);
-    const uint8_t* rp = codes + (size_t)row * (size_t)(K >> 1) + (size_t)gl * 32;
+    const uint8_t* cp;
+    const uint16_t* sp;
+    const int row = plane_row(grp + R * j, cp, sp);
+    const uint8_t* rp = cp + (size_t)row * (size_t)(K >> 1) + (size_t)gl * 32;
 #pragma unroll
     for (int i = 0; i < PL; ++i)
       w[j][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(rp + 16 * min(pc0 + i, max(P - 1, 0))));
@@ -230,7 +251,10 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   uint16_t sbits[MAXR][PL];
 #pragma unroll
   for (int j = 0; j < MAXR; ++j) {
-    const uint16_t* sr = scales + (size_t)(n0 + min(grp + R * j, rows - 1)) * (size_t)G + gl;
+    const uint8_t* cp;
+    const uint16_t* sp;
+    const int row = plane_row(grp + R * j, cp, sp);
+    const uint16_t* sr = sp + (size_t)row * (size_t)G + gl;
 #pragma unroll
     for (int i = 0; i < PL; ++i) sbits[j][i] = sr[min(pc0 + i, max(P - 1, 0)) >> 1];
   }
@@ -303,16 +327,18 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 #pragma unroll
   for (int t = 0; t < NT; ++t) ew[t] = 0;
   if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-    // (rare: the activations and codes are read again, so that their
-    // registers need not live through the products above)
+    // (rare; twelve waves read the activations and codes again, so that
+    // their registers need not live through the products above)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      if constexpr (WV != 8) {
 #pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        const u32x4_t* xp =
-            reinterpret_cast<const u32x4_t*>(x + (size_t)t * K + 64 * gl + 32 * min(pc0 + i, max(P - 1, 0)));
+        for (int i = 0; i < PL; ++i) {
+          const u32x4_t* xp =
+              reinterpret_cast<const u32x4_t*>(x + (size_t)t * K + 64 * gl + 32 * min(pc0 + i, max(P - 1, 0)));
 #pragma unroll
-        for (int d = 0; d < 4; ++d) xv[t][i][d] = xp[d];
+          for (int d = 0; d < 4; ++d) xv[t][i][d] = xp[d];
+        }
       }
       uint32_t m = 0;
 #pragma unroll
@@ -332,11 +358,16 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
       for (int i = 0; i < PL; ++i) s8[i] = piece_dot(k8, xf[i]);
 #pragma unroll
       for (int j = 0; j < MAXR; ++j) {
-        const uint8_t* rp = codes + (size_t)(n0 + min(grp + R * j, rows - 1)) * (size_t)(K >> 1) + (size_t)gl * 32;
+        const uint8_t* cp;
+        const uint16_t* sp;
+        const int row = plane_row(grp + R * j, cp, sp);
+        const uint8_t* rp = cp + (size_t)row * (size_t)(K >> 1) + (size_t)gl * 32;
         float a = 0.0f;
 #pragma unroll
         for (int i = 0; i < PL; ++i) {
-          const u32x4_t wj = *reinterpret_cast<const u32x4_t*>(rp + 16 * min(pc0 + i, max(P - 1, 0)));
+          u32x4_t wj;
+          if constexpr (WV != 8) wj = *reinterpret_cast<const u32x4_t*>(rp + 16 * min(pc0 + i, max(P - 1, 0)));
+          else wj = w[j][i];
           a = __builtin_fmaf(sc[j][i], piece_dot(wj, xf[i]) - s8[i], a);
         }
         acc[t][j] = a;
@@ -368,6 +399,8 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
   // (twelve waves: each thread leaves its wave's sum in LDS and one thread
   // per (row, token) adds the twelve in wave order)
   double* dsum = reinterpret_cast<double*>(lds + (((size_t)WV * NT * kRegion<MAXR> + (size_t)WV * NT * 4 + 7) & ~(size_t)7));
+  // (LinearSwiGLU: the (row, token) sums in binary64, after the wave sums)
+  double* dres = dsum + (WV == 8 ? 0 : (size_t)NT * BN * WV);
   for (int idx = tid; idx < NT * rows * WV; idx += 64 * WV) {
     const int wv = idx % WV, rt = idx / WV;
     const int t = NT == 1 ? 0 : rt / rows, r = rt - t * rows;
@@ -407,9 +440,13 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
       v += __shfl_xor(v, 2);
       v += __shfl_xor(v, 4);
       if (wv == 0) {
-        if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + n0 + r]);  // LinearAdd
-        if (p2.f32) reinterpret_cast<float*>(y)[(size_t)t * N + n0 + r] = (float)v;  // LinearSwiGLU sums
-        else y[(size_t)t * N + n0 + r] = f32_to_bf16_rne((float)v);
+        if (glu) {
+          dres[t * rows + r] = v;
+        } else {
+          if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + n0 + r]);  // LinearAdd
+          if (p2.f32) reinterpret_cast<float*>(y)[(size_t)t * N + n0 + r] = (float)v;  // LinearSwiGLU sums
+          else y[(size_t)t * N + n0 + r] = f32_to_bf16_rne((float)v);
+        }
       }
     } else {
       dsum[idx] = v;
@@ -422,9 +459,27 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
       double v = 0.0;
 #pragma unroll
       for (int wv = 0; wv < WV; ++wv) v += dsum[rt * WV + wv];
+      if (glu) {
+        dres[t * rows + r] = v;
+        continue;
+      }
       if (res != nullptr) v += (double)bf16_bits_to_f32(res[(size_t)t * N + n0 + r]);  // LinearAdd
       if (p2.f32) reinterpret_cast<float*>(y)[(size_t)t * N + n0 + r] = (float)v;  // LinearSwiGLU sums
       else y[(size_t)t * N + n0 + r] = f32_to_bf16_rne((float)v);
+    }
+  }
+  if (glu) {
+    // y = bf16(silu(G) U): each sum rounded to binary32 first (the sums a
+    // LinearSwiGLU leaves between passes), the gate in binary64, one
+    // rounding of the product
+    __syncthreads();
+    for (int i = tid; i < NT * hrows; i += 64 * WV) {
+      const int t = NT == 1 ? 0 : i / hrows, r = i - t * hrows;
+      // (+0 maps a -0 sum to +0, as a sum of zero products starts at +0)
+      const double g = (double)(float)dres[t * rows + r] + 0.0;
+      const double u = (double)(float)dres[t * rows + hrows + r] + 0.0;
+      const double silu = g / (1.0 + exp(-g));
+      y[(size_t)t * N + n0 + r] = f32_to_bf16_rne((float)(silu * u));
     }
   }
 }
@@ -433,16 +488,19 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
 // and for twelve waves the per-wave sums of the bn rows (binary64)
 size_t decode_lds(int maxr, int nt, int wv, int64_t bn) {
   const size_t base = (size_t)wv * (size_t)nt * (size_t)(64 * maxr * 4 + 16) + (size_t)wv * (size_t)nt * 4;
-  return wv == 8 ? base : ((base + 7) & ~(size_t)7) + (size_t)nt * (size_t)bn * (size_t)wv * 8;
+  const size_t sums = (size_t)nt * (size_t)bn * 8;  // LinearSwiGLU's (row, token) sums
+  return ((base + 7) & ~(size_t)7) + (wv == 8 ? 0 : (size_t)nt * (size_t)bn * (size_t)wv * 8) + sums;
 }
 
 template <int PL, int MAXR, int NT, int WV = 8>
 hipError_t launch_pm(const DecodePlan& p, const GemvArgs& a, hipStream_t stream) {
-  auto kern = decode_kernel<PL, MAXR, NT, WV>;
+  auto kern = a.glu ? decode_kernel<PL, MAXR, NT, WV, WV == 8> : decode_kernel<PL, MAXR, NT, WV, false>;
   const size_t lds = decode_lds(MAXR, NT, WV, p.bn);
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
-  const int blocks1 = (int)((a.n + p.bn - 1) / p.bn), blocks2 = (int)((a.n2 + p.bn - 1) / p.bn);
+  // (LinearSwiGLU: bn / 2 rows of each weight per workgroup)
+  const int blocks1 = a.glu ? (int)((a.n + p.bn / 2 - 1) / (p.bn / 2)) : (int)((a.n + p.bn - 1) / p.bn);
+  const int blocks2 = a.glu ? 0 : (int)((a.n2 + p.bn - 1) / p.bn);
   kern<<<dim3((unsigned)(blocks1 + blocks2)), dim3(64 * WV), lds, stream>>>(
       static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
       static_cast<uint16_t*>(a.y), (int)a.n, (int)a.k, p.bn, static_cast<const uint16_t*>(a.res),
@@ -518,14 +576,25 @@ bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p) {
   return found;
 }
 
+bool decode_glu_ok(int64_t n, int64_t k, int64_t t) {
+  DecodePlan p;
+  return decode_plan(2 * n, k, t, &p) && p.waves == 8;
+}
+
 hipError_t launch_decode(const GemvArgs& a, hipStream_t stream) {
   DecodePlan p;
   if (!decode_plan(a.n + a.n2, a.k, a.t, &p)) return hipErrorInvalidValue;
+  if (a.glu) {
+    // the plan for both weights' rows, an even count per workgroup (the same
+    // rows of each weight); odd counts give up a row
+    if (a.n2 != a.n || p.waves != 8) return hipErrorInvalidValue;
+    p.bn = p.bn >= 2 ? p.bn & ~1 : 2;
+  }
   // Two weights: each ends in its own partial workgroup, which can push the
   // grid one past a round of the CUs (6144 + 1024 rows: 220 + 37 of 28 rows
   // against 256).  Plan for a few more rows (bn grows by one) until the two
   // grids together fit what the plan sized for one.
-  for (int64_t extra = p.bn, i = 0; a.n2 > 0 && i < 4; extra += p.bn, ++i) {
+  for (int64_t extra = p.bn, i = 0; a.n2 > 0 && !a.glu && i < 4; extra += p.bn, ++i) {
     const int64_t b = (a.n + p.bn - 1) / p.bn + (a.n2 + p.bn - 1) / p.bn;
     DecodePlan q;
     if (b <= p.blocks || !decode_plan(a.n + a.n2 + extra, a.k, a.t, &q)) break;

@@ -25,6 +25,10 @@ struct GemvArgs {
   void* y2 = nullptr;
   int64_t n2 = 0;
   bool f32 = false;  // outputs as binary32 [T][N] (LinearSwiGLU's gate and up sums), not bf16
+  // LinearSwiGLU in one pass (single-token route): codes/scales are the gate,
+  // codes2/scales2 the up weight (n2 == n); every workgroup takes the same
+  // rows of both and stores bf16(silu(G) * U) into y
+  bool glu = false;
 };
 
 // The second plane of a LinearPair as the kernels see it: the workgroups from
@@ -36,10 +40,11 @@ struct SecondPlane {
   int n;      // rows (0: no second plane)
   int first;  // its first workgroup
   int f32;    // every output stored as binary32 [T][N] instead of bf16
+  int glu;    // LinearSwiGLU: a workgroup's rows are H gate rows, then the same H up rows
 };
 inline SecondPlane second_plane(const GemvArgs& a, int first) {
   return SecondPlane{static_cast<const uint8_t*>(a.codes2), static_cast<const uint16_t*>(a.scales2),
-                     static_cast<uint16_t*>(a.y2), (int)a.n2, first, a.f32 ? 1 : 0};
+                     static_cast<uint16_t*>(a.y2), (int)a.n2, first, a.f32 ? 1 : 0, a.glu ? 1 : 0};
 }
 
 // Few-token route.  Each of the 4 waves of a workgroup owns a quarter of the
@@ -60,6 +65,8 @@ struct DecodePlan {
   int waves;   // waves per workgroup (8, or 12 for long rows)
 };
 bool decode_plan(int64_t n, int64_t k, int64_t t, DecodePlan* p);
+// whether LinearSwiGLU of n rows per weight runs in one pass on this route
+bool decode_glu_ok(int64_t n, int64_t k, int64_t t);
 hipError_t launch_decode(const GemvArgs& a, hipStream_t stream);
 
 // Small-T route: one workgroup of eight waves per block of bn rows, K split
