@@ -54,6 +54,17 @@ bool mid_uses_fmt(int64_t n, int64_t k, int64_t t) {
   q4lin::FmtPlan fp;
   return t <= kMidFmtLastT && q4lin::fmt_plan(q4lin::FMT_Q4, n, k, t, &fp);
 }
+
+// The small-T route's single weight from kSmallFmtFirstT tokens on runs the
+// few-token kernel of the weight formats on the Q4 codes (6144 x 5120:
+// T = 5 9.9 against 11.2 us, T = 17 13.7 / 16.2, T = 32 15.2 / 20.4 on the
+// small-T kernel, which keeps two weights in one launch: LinearPair and
+// LinearSwiGLU).
+constexpr int64_t kSmallFmtFirstT = 5;
+bool small_uses_fmt(int64_t n, int64_t k, int64_t t) {
+  q4lin::FmtPlan fp;
+  return t >= kSmallFmtFirstT && q4lin::fmt_plan(q4lin::FMT_Q4, n, k, t, &fp);
+}
 static_assert(q4lin::FMT_Q5 == Q4LIN_FMT_Q5G64_F16S && q4lin::FMT_Q6 == Q4LIN_FMT_Q6G64_F16S &&
                   q4lin::FMT_W8 == Q4LIN_FMT_W8G32_F16S && q4lin::FMT_NVFP4 == Q4LIN_FMT_NVFP4 &&
                   q4lin::FMT_BF16 == Q4LIN_FMT_BF16,
@@ -146,7 +157,7 @@ int run_linear(const void* x, const void* codes, const void* scales, const void*
   } else if (route == Q4LIN_ROUTE_DECODE) {
     e = q4lin::launch_decode(ga, s);
   } else if (route == Q4LIN_ROUTE_SKINNY) {
-    e = q4lin::launch_skinny(ga, s);
+    e = small_uses_fmt(n, k, t) ? q4lin::launch_fmt(q4_fmt_args(ga), s) : q4lin::launch_skinny(ga, s);
   } else if (route == Q4LIN_ROUTE_MID) {
     e = mid_uses_fmt(n, k, t) ? q4lin::launch_fmt(q4_fmt_args(ga), s) : q4lin::launch_mid(ga, workspace, s);
   } else {
