@@ -874,16 +874,57 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
 }
 
 // The K-split outputs: y[t][n] = bf16(2^(e[t] - c[n]) * sum over splits of
-// the partials), the splits added in order.  One thread per output; its (at
-// most kMaxSplits) partial loads are all issued before the sum.
+// the partials), the splits added in order.  A thread takes four consecutive
+// outputs (16-byte partial loads, all issued before the sums) when N is a
+// multiple of 4, else one.
 constexpr int kMaxSplits = 8;
+__device__ __forceinline__ uint16_t reduce_out(float v, int e, const uint16_t* res, size_t i,
+                                               const uint16_t* __restrict__ xraw, const uint8_t* __restrict__ codes,
+                                               const uint16_t* __restrict__ scales, int N, int K, int n, int t) {
+  v = __builtin_ldexpf(v, e);
+  if (res != nullptr) v += bf16_bits_to_f32(res[i]);  // LinearAdd
+  uint16_t h = f32_to_bf16_rne(v);
+  if ((h & 0x7F80u) == 0x7F80u) h = exact_q4_output(xraw, codes, scales, res, N, K, n, t);  // rare
+  return h;
+}
 __global__ void __launch_bounds__(256)
 tiled_reduce_kernel(const float* __restrict__ part, const int* __restrict__ texp, const int* __restrict__ rexp,
                     uint16_t* y, int N, int Tpad, int KS, const uint16_t* res, const uint16_t* __restrict__ xraw,
                     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int K) {
-  const int n = blockIdx.x * 256 + threadIdx.x, t = blockIdx.y;
+  const int t = blockIdx.y;
+  const size_t stride = (size_t)Tpad * N;
+  if ((N & 3) == 0) {
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (n >= N) return;
+    const size_t i = (size_t)t * N + n;
+    f32x4_t p[kMaxSplits];
+#pragma unroll
+    for (int k = 0; k < kMaxSplits; ++k)
+      p[k] = k < KS ? *reinterpret_cast<const f32x4_t*>(part + k * stride + i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const u32x4_t ce = *reinterpret_cast<const u32x4_t*>(rexp + n);
+    const int et = texp[t];
+    uint16_t h[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kMaxSplits; ++k)
+        if (k < KS) v += p[k][j];
+      h[j] = reduce_out(v, et - (int)ce[j], res, i + j, xraw, codes, scales, N, K, n + j, t);
+    }
+    uint16_t* yo = y + i;
+    if ((reinterpret_cast<uintptr_t>(yo) & 7) == 0) {
+      *reinterpret_cast<u32x2_t*>(yo) = u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yo[j] = h[j];
+    }
+    return;
+  }
+  const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= N) return;
-  const size_t i = (size_t)t * N + n, stride = (size_t)Tpad * N;
+  const size_t i = (size_t)t * N + n;
   float p[kMaxSplits];
 #pragma unroll
   for (int k = 0; k < kMaxSplits; ++k) p[k] = k < KS ? part[k * stride + i] : 0.0f;
@@ -891,11 +932,13 @@ tiled_reduce_kernel(const float* __restrict__ part, const int* __restrict__ texp
 #pragma unroll
   for (int k = 0; k < kMaxSplits; ++k)
     if (k < KS) v += p[k];
-  v = __builtin_ldexpf(v, texp[t] - rexp[n]);
-  if (res != nullptr) v += bf16_bits_to_f32(res[i]);  // LinearAdd
-  uint16_t h = f32_to_bf16_rne(v);
-  if ((h & 0x7F80u) == 0x7F80u) h = exact_q4_output(xraw, codes, scales, res, N, K, n, t);  // rare
-  y[i] = h;
+  y[i] = reduce_out(v, texp[t] - rexp[n], res, i, xraw, codes, scales, N, K, n, t);
+}
+
+// grid of the split sums for n outputs per token
+inline dim3 reduce_grid(int64_t n, int64_t t) {
+  const int64_t per_block = (n % 4 == 0) ? 1024 : 256;
+  return dim3((unsigned)((n + per_block - 1) / per_block), (unsigned)t);
 }
 
 // The weight's tiles (and a second weight's after them); the K-split sums
@@ -940,13 +983,13 @@ hipError_t launch_cfg(const TiledArgs& a, const u32x4_t* x16, const int* texp, c
       static_cast<const uint16_t*>(a.res), p2);
   e = hipGetLastError();
   if (e != hipSuccess || ks == 1 || a.f32) return e;
-  tiled_reduce_kernel<<<dim3((unsigned)((a.n + 255) / 256), (unsigned)a.t), dim3(256), 0, stream>>>(
+  tiled_reduce_kernel<<<reduce_grid(a.n, a.t), dim3(256), 0, stream>>>(
       part, texp, rexp, static_cast<uint16_t*>(a.y), (int)a.n, tpad, ks, static_cast<const uint16_t*>(a.res),
       static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes), static_cast<const uint16_t*>(a.scales),
       (int)a.k);
   e = hipGetLastError();
   if (e != hipSuccess || h2.n == 0) return e;
-  tiled_reduce_kernel<<<dim3((unsigned)((h2.n + 255) / 256), (unsigned)a.t), dim3(256), 0, stream>>>(
+  tiled_reduce_kernel<<<reduce_grid(h2.n, a.t), dim3(256), 0, stream>>>(
       h2.part, texp, h2.rexp, static_cast<uint16_t*>(h2.y), (int)h2.n, tpad, ks, nullptr,
       static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(h2.codes), static_cast<const uint16_t*>(h2.scales),
       (int)a.k);
