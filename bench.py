@@ -355,6 +355,7 @@ KERNEL_SOURCES = {
     "decode": "weight_only_bit_q4_amd/csrc/q4lin_decode.hip",
     "tiled": "weight_only_bit_q4_amd/csrc/q4lin_tiled.hip",
     "mid": "weight_only_bit_q4_amd/csrc/q4lin_mid.hip",
+    "fmt": "weight_only_bit_q4_amd/csrc/q4lin_fmt.hip",
 }
 
 
