@@ -354,7 +354,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
     "decode": "weight_only_bit_q4_amd/csrc/q4lin_decode.hip",
     "tiled": "weight_only_bit_q4_amd/csrc/q4lin_tiled.hip",
-    "mid": "weight_only_bit_q4_amd/csrc/q4lin_mid.hip",
     "fmt": "weight_only_bit_q4_amd/csrc/q4lin_fmt.hip",
 }
 

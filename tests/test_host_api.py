@@ -101,9 +101,8 @@ def test_routes_and_workspace_sizes():
             tp = (t + 31) // 32 * 32
             assert ws >= tp * 5120 * 2 + tp * 4
         elif r == q.Q4LIN_ROUTE_MID:
-            # none up to 64 tokens; above, binary32 partials of the K slices [S][T][N]
-            assert (ws == 0) == (t <= 64)
-            assert ws % (t * 6144 * 4) == 0 and ws // (t * 6144 * 4) <= 8
+            # one pass of the weight formats' kernel: no workspace
+            assert ws == 0
         else:
             assert ws == 0
     for t in (33, 64, 65, 128):

@@ -75,6 +75,26 @@ def test_fmt_ragged(fmt, n, k, t):
                  what="%s %dx%d T=%d" % (inputs.FMT_NAMES[fmt], n, k, t))
 
 
+# (n, k, t): the many-token kernel's token tiles (2, 3, 4, 6, 8 per wave)
+# with one to four column tiles, one or two token ranges per row block (two
+# from 65 tokens up to 8192 rows; a ragged second range; a grid whose last
+# row of eight has row blocks past N), a run of pairs longer than one chunk
+# of codes (K = 16384), a single unit (K = 64), and T past 128
+TOKEN_TILE_SHAPES = [(2048, 2048, 24), (2048, 2048, 40), (6144, 1024, 64), (6144, 1024, 80), (6144, 1024, 128),
+                     (6144, 2048, 128), (2000, 1024, 77), (4096, 1024, 200), (4096, 1024, 60), (10240, 640, 48), (16384, 640, 64),
+                     (16384, 640, 100), (500, 16384, 97), (300, 1088, 130), (100, 64, 33)]
+
+
+@pytest.mark.parametrize("fmt", [inputs.FMT_Q4] + FMTS, ids=["Q4G64_F16S"] + FMT_IDS)
+@pytest.mark.parametrize("n,k,t", TOKEN_TILE_SHAPES)
+def test_fmt_token_tiles(fmt, n, k, t):
+    w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, 500 + n + t)
+    x = inputs.gen_x(k, t, 501 + t)
+    got = run_fmt(fmt, x, w, hi, sc, n, k, t, what="token tiles")
+    assert_close(got, oracle.linear_fmt(fmt, x, w, hi, sc, n, k, t),
+                 what="%s %dx%d T=%d" % (inputs.FMT_NAMES[fmt], n, k, t))
+
+
 def test_fmt_long_k_scale_table():
     """K = 131072 in W8: a row's scales take 8 KiB, so a block holds 12 rows
     instead of 13 (the LDS scale table is capped); every output compared."""
@@ -87,14 +107,14 @@ def test_fmt_long_k_scale_table():
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 def test_fmt_prefill_t1024_sampled(fmt):
-    """T = 1024 runs the kernel once per 32 tokens; sampled outputs and the
+    """T = 1024 runs the kernel once per 128 tokens; sampled outputs and the
     token-run boundaries against the oracle."""
     n, k, t = 6144, 5120, 1024
     seed = inputs.workload_seed("prefill_6144x5120_t1024") + 100 * fmt
     w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, seed)
     x = inputs.gen_x(k, t, seed)
     got = run_fmt(fmt, x, w, hi, sc, n, k, t, what="prefill")
-    ns, ts = sample_indices(n, t, 1500, seed, (15, 16, 255, 256, n - 1), (31, 32, 33, 511, 512, 1023))
+    ns, ts = sample_indices(n, t, 1500, seed, (15, 16, 255, 256, n - 1), (31, 32, 33, 127, 128, 511, 512, 1023))
     ref = oracle.linear_fmt_at(fmt, x, w, hi, sc, n, k, t, ns, ts)
     assert_close(got[ts, ns], ref, what="%s T=1024 sampled" % inputs.FMT_NAMES[fmt])
 

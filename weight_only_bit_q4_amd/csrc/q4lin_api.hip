@@ -41,18 +41,16 @@ constexpr int64_t kMaxT = int64_t(1) << 21;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxBytes = int64_t(1) << 40;
 constexpr size_t kGemvLdsLimit = 64 * 1024;
-// The medium-T route takes T from kMidFirstT to the split-K plan's limit
-// (128): up to kMidFmtLastT tokens it runs the few-token kernel of the
-// weight formats on the Q4 codes (one pass, no workspace; 21-23 us against
-// 23.5-24.6 at T = 33..57 on 6144 x 5120), above that the split-K kernel
-// (30.6-33.8 against 34-41 us at T = 65..121).
+// The medium-T route takes T from kMidFirstT to kMidLastT: the weight
+// formats' kernel on the Q4 codes, every wave on all the tokens of its run
+// (one weight pass, no workspace).
 constexpr int64_t kMidFirstT = 33;
-constexpr int64_t kMidFmtLastT = 64;
+constexpr int64_t kMidLastT = 128;
 
-// whether a medium-T call runs the few-token kernel (else the split-K one)
-bool mid_uses_fmt(int64_t n, int64_t k, int64_t t) {
+// whether the medium-T route takes (n, k, t)
+bool mid_ok(int64_t n, int64_t k, int64_t t) {
   q4lin::FmtPlan fp;
-  return t <= kMidFmtLastT && q4lin::fmt_plan(q4lin::FMT_Q4, n, k, t, &fp);
+  return t >= kMidFirstT && t <= kMidLastT && q4lin::fmt_plan(q4lin::FMT_Q4, n, k, t, &fp);
 }
 
 // The small-T route's single weight from kSmallFmtFirstT tokens on runs the
@@ -92,20 +90,17 @@ int pick_route(int64_t n, int64_t k, int64_t t) {
   if (t == 1 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
   if (q4lin::skinny_plan(n, k, t, &sp)) return Q4LIN_ROUTE_SKINNY;
   if (t <= 4 && q4lin::gemv_lds_bytes(k, t) <= kGemvLdsLimit) return Q4LIN_ROUTE_GEMV;
-  if (t >= kMidFirstT && mid_uses_fmt(n, k, t)) return Q4LIN_ROUTE_MID;
-  q4lin::MidPlan mp;
-  if (t >= kMidFirstT && q4lin::mid_plan(n, k, t, &mp)) return Q4LIN_ROUTE_MID;
+  if (mid_ok(n, k, t)) return Q4LIN_ROUTE_MID;
   return Q4LIN_ROUTE_TILED;
 }
 
 size_t route_workspace(int route, int64_t n, int64_t k, int64_t t) {
   if (route == Q4LIN_ROUTE_TILED) return q4lin::tiled_workspace_bytes(n, k, t);
-  if (route == Q4LIN_ROUTE_MID && !mid_uses_fmt(n, k, t)) return q4lin::mid_workspace_bytes(n, k, t);
   return 0;
 }
 
-// The medium-T route runs the Q4 weight through the few-token kernel of
-// the weight formats (up to 128 tokens per weight read).
+// The small-T and medium-T routes run the Q4 weight through the weight
+// formats' kernel (up to 128 tokens per weight read).
 q4lin::FmtArgs q4_fmt_args(const q4lin::GemvArgs& g) {
   q4lin::FmtArgs a{q4lin::FMT_Q4, g.x, g.codes, nullptr, g.scales, g.y, g.n, g.k, g.t};
   a.res = g.res;
@@ -159,7 +154,7 @@ int run_linear(const void* x, const void* codes, const void* scales, const void*
   } else if (route == Q4LIN_ROUTE_SKINNY) {
     e = small_uses_fmt(n, k, t) ? q4lin::launch_fmt(q4_fmt_args(ga), s) : q4lin::launch_skinny(ga, s);
   } else if (route == Q4LIN_ROUTE_MID) {
-    e = mid_uses_fmt(n, k, t) ? q4lin::launch_fmt(q4_fmt_args(ga), s) : q4lin::launch_mid(ga, workspace, s);
+    e = q4lin::launch_fmt(q4_fmt_args(ga), s);
   } else {
     q4lin::TiledArgs a{x, codes, scales, y, n, k, t, workspace, q4lin::tiled_pick_config(n, k, t), res};
     e = q4lin::launch_tiled(a, s);
@@ -175,8 +170,7 @@ size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 //   SPLIT: one launch per weight on the route chosen for N rows;
 //   TILED: the many-token route per weight, its raw sums left in the
 //          partials of a workspace half each.
-//   MID:   the medium-T route per weight, binary32 sums (the split-K
-//          kernel's partials after the sums in each half).
+//   MID:   the medium-T route per weight, binary32 sums in each half.
 enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3, SW_MID = 4, SW_GLU = 5 };
 struct SwigluPlan {
   int mode;
@@ -201,8 +195,7 @@ bool swiglu_plan(int64_t n, int64_t k, int64_t t, SwigluPlan* p) {
   if (r1 == Q4LIN_ROUTE_TILED) {
     *p = SwigluPlan{SW_TILED, r1, 0, q4lin::tiled_pair_workspace_bytes(n, n, k, t, true)};
   } else if (r1 == Q4LIN_ROUTE_MID) {
-    const size_t half =
-        al256((size_t)(n * t * 4)) + (mid_uses_fmt(n, k, t) ? 0 : al256(q4lin::mid_workspace_bytes(n, k, t)));
+    const size_t half = al256((size_t)(n * t * 4));
     *p = SwigluPlan{SW_MID, r1, half, 2 * half};
   } else {
     *p = SwigluPlan{SW_SPLIT, r1, al256((size_t)(n * t * 4)), 2 * al256((size_t)(n * t * 4))};
@@ -364,14 +357,13 @@ int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scale
       e = launch_sums(p.route, b, s);
     }
   } else if (p.mode == SW_MID) {
-    const size_t sums = al256((size_t)(n * t * 4));
     q4lin::GemvArgs a{x, codes_gate, scales_gate, w0, n, k, t};
     a.f32 = true;
-    e = mid_uses_fmt(n, k, t) ? q4lin::launch_fmt(q4_fmt_args(a), s) : q4lin::launch_mid(a, w0 + sums, s);
+    e = q4lin::launch_fmt(q4_fmt_args(a), s);
     if (e == hipSuccess) {
       q4lin::GemvArgs b{x, codes_up, scales_up, w1, n, k, t};
       b.f32 = true;
-      e = mid_uses_fmt(n, k, t) ? q4lin::launch_fmt(q4_fmt_args(b), s) : q4lin::launch_mid(b, w1 + sums, s);
+      e = q4lin::launch_fmt(q4_fmt_args(b), s);
     }
   } else {
     // both weights' tiles in one launch after one activation preparation;

@@ -20,17 +20,30 @@
 // Work mapping.  One workgroup of eight waves per block of BN <= 16 CT rows;
 // the waves split K into eight contiguous runs of pairs of "units" (a unit
 // is one scale group of Q5/Q6/W8, 64 weights of NVFP4, 32 of BF16), so
-// every weight byte is read once for all T <= 32 tokens.  Lane l serves row
+// every weight byte is read once per launch.  Lane l serves row
 // 16 ct + l % 16.  Its code loads are 16 contiguous bytes per row and pair:
 // quarter q = l / 16 reads half q % 2 of unit q / 2 (BF16: quarter q of
 // each unit), with the matching high bits; lanes l and l + 32 then swap
 // half of them, so every matrix-core instruction still reduces within one
-// unit.  The block's scales are copied into LDS once.  Activations: 16 or
-// 32 contiguous bytes per token and unit.  Longer T runs the kernel once
-// per 32 tokens.
+// unit.  The block's scales are copied into LDS once.
+//   * Up to 16 tokens (fmt_kernel): the activations of a pair go straight
+//     to registers with its codes (16 or 32 contiguous bytes per token and
+//     unit).
+//   * 17 to 128 tokens (fmt_tok_kernel, up to 64 with 3 or 4 column tiles):
+//     every wave takes all the launch's tokens for its run, so each code
+//     operand is built once for all of them; the activations pass through a
+//     per-wave ring in LDS (direct copies in memory order, read back in
+//     operand order); a wave's codes are loaded several pairs at a time.
+//   Longer T runs the kernel once per 128 (64) tokens.
 //
 // Arithmetic (v_mfma_f32_16x16x32_bf16, A = activations, B = weights, every
 // instruction reduces over one unit):
+//   * Q4: one three-input bitwise operation per pair of weights builds the
+//     exact bf16 value 128 + q (q < 128 has unit spacing there); up to 16
+//     tokens in the pair order of a code dword as below, from 17 tokens in
+//     the activations' own order (k0,k1) (k2,k3) ... (one byte permute per
+//     pair), so the activation pieces need no permute; the correction is as
+//     for Q5/Q6 with offset 8;
 //   * Q5/Q6: two three-input bitwise operations per pair of weights build
 //     the exact bf16 value 128 + q (q < 128 has unit spacing there), in the
 //     pair order (k0,k4) (k1,k5) (k2,k6) (k3,k7) of a code dword; the
@@ -66,6 +79,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTableBytes = 88 * 1024;   // LDS for the block's scales (with the 64 KiB sum area: 152 KiB)
 constexpr int kLdsBytes = 160 * 1024;    // LDS of one workgroup
 constexpr uint32_t kNowhere = 0x80000000u;  // a buffer offset past every range: reads zeros, no access
+constexpr int kRingWave = 16 * 1024;      // LDS of one wave's activation ring (17 to 128 tokens)
 
 // Buffer loads: offsets at or past the resource's byte count return zeros
 // without a memory access, so loads past a wave's run need no branch (and
@@ -76,10 +90,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // 16-byte direct-to-LDS buffer load: each lane sends 16 bytes from base +
-// voffset to lds_base + 16 * lane (lds_base wave-uniform)
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voffset, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voffset, 0,
-                                           0, 0);
+// voffset + soffset to lds_base + 16 * lane (soffset and lds_base
+// wave-uniform)
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voffset, uint32_t soffset, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voffset,
+                                           soffset, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4
@@ -150,6 +165,20 @@ __device__ __forceinline__ bf16x8_t q4_operand(uint32_t w) {
   r.y = and_or(w >> 4, 0x000F000Fu, 0x43004300u);
   r.z = and_or(w >> 8, 0x000F000Fu, 0x43004300u);
   r.w = and_or(w >> 12, 0x000F000Fu, 0x43004300u);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// Q4: code dword w (nibbles of k0..k7) -> the eight exact bf16 values
+// 128 + q in natural order (k0,k1) (k2,k3) (k4,k5) (k6,k7): byte b of w
+// gives its low nibble to the pair's low half and, through w >> 4, its high
+// nibble to the high half
+__device__ __forceinline__ bf16x8_t q4_natural(uint32_t w) {
+  const uint32_t u = w >> 4;
+  u32x4_t r;
+  r.x = and_or(__builtin_amdgcn_perm(u, w, 0x04040000u), 0x000F000Fu, 0x43004300u);
+  r.y = and_or(__builtin_amdgcn_perm(u, w, 0x05050101u), 0x000F000Fu, 0x43004300u);
+  r.z = and_or(__builtin_amdgcn_perm(u, w, 0x06060202u), 0x000F000Fu, 0x43004300u);
+  r.w = and_or(__builtin_amdgcn_perm(u, w, 0x07070303u), 0x000F000Fu, 0x43004300u);
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
@@ -248,379 +277,230 @@ __device__ __attribute__((noinline)) uint16_t exact_output(const uint16_t* __res
   return f32_to_bf16_rne((float)acc);
 }
 
-// One lane's loads for one pair of units: 16 code bytes per row (two loads
-// of 16 for BF16_CTRL), the high bits that go with them, and the
-// activations of both units for TT token tiles.
-template <int F, int CT, int TT>
-struct Loads {
-  static constexpr int NC = F == FMT_BF16 ? 2 : 1;       // 16-byte code loads per row
-  static constexpr int NH = F == FMT_Q6 ? 2 : 1;         // high-bit dwords per row
-  static constexpr int XH = Unit<F>::K == 64 ? 2 : 1;    // 16-byte activation pieces per unit and token
-  u32x4_t c[CT][NC];
-  uint32_t h[CT][NH];
-  u32x4_t a[2][TT][XH];
+// Per-format load shape: 16-byte code loads per row and pair, high-bit
+// dwords per row, 16-byte activation pieces per unit and token, high-plane
+// bytes per unit and row, loads per column tile and pair.
+template <int F>
+struct Fmt {
+  static constexpr int NC = F == FMT_BF16 ? 2 : 1;
+  static constexpr int NH = F == FMT_Q6 ? 2 : 1;
+  static constexpr int XH = Unit<F>::K == 64 ? 2 : 1;
+  static constexpr int HB = F == FMT_Q5 ? 8 : F == FMT_Q6 ? 16 : 0;
+  static constexpr int LPT = NC + ((F == FMT_Q5 || F == FMT_Q6) ? 1 : 0);
+  static constexpr bool NIB = F == FMT_Q4 || F == FMT_Q5 || F == FMT_Q6;  // nibble codes with an offset
+  static constexpr bool PAIRED = F != FMT_BF16;                            // one 16-byte load spans two units
 };
 
-template <int F, int CT, int TT, int WT>
-__global__ void __launch_bounds__(kThreads, 1)
-fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const uint8_t* __restrict__ hi,
-           const uint8_t* __restrict__ sc, uint16_t* __restrict__ y, const uint16_t* __restrict__ res, int f32out,
-           int N, int K, int T, int BN) {
-  using U = Unit<F>;
-  using L_t = Loads<F, CT, TT>;
-  constexpr int XH = L_t::XH;
-  constexpr bool NIB = (F == FMT_Q4 || F == FMT_Q5 || F == FMT_Q6);  // nibble codes with an offset
-  constexpr int WK = kWaves / WT;  // waves per token range: each takes a K run
-  constexpr int BT = 32 * WT;      // tokens per launch
-  constexpr bool PAIRED = F != FMT_BF16;                 // one 16-byte load spans a pair of units
-  constexpr int NB = 2;                                  // pairs in flight (register sets)
-  // Above 16 tokens the activations go through a ring in LDS: each wave
-  // copies its pairs' activations with direct-to-LDS loads in memory order
-  // (consecutive lanes read consecutive 16-byte pieces of a token, so the
-  // loads coalesce) and reads them back in matrix-core operand order.
-  constexpr bool XL = TT == 2;
-  constexpr int TTK = 16 * TT;                // tokens per wave
-  constexpr int PPT = U::K * 2 / 16;          // 16-byte pieces per token and unit
-  constexpr int SLOT = 2 * TTK * PPT * 16;    // one pair's activations [unit][token][piece]
-  constexpr int NI = 2 * TTK * PPT / 64;      // direct-to-LDS loads per pair
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wk = wave % WK, wt = wave / WK;  // K run, 32-token range
-  const int li = lane & 15, lq = lane >> 4;
-  // the quarter of each unit this lane multiplies: after the exchange of
-  // the paired loads, quarter lq holds code bytes 8 xq .. 8 xq + 7 of a unit
-  const int xq = PAIRED ? (((lq & 1) << 1) | (lq >> 1)) : lq;
-  const int n0 = blockIdx.x * BN;
-  const int rows = min(BN, N - n0);
-  const int units = K / U::K;
-  const int pairs = (units + 1) >> 1;
-  const int pb = (int)(((int64_t)pairs * wk) / WK), pe = (int)(((int64_t)pairs * (wk + 1)) / WK);
-  const int ts = units * U::SB;  // bytes of one row's scales
-  // LDS: [activation rings of the 8 waves (XL)] or [partials], then the
-  // scale table; the partials of the final sum reuse the start
-  uint8_t* tab = lds + (XL ? (size_t)kWaves * 2 * SLOT : (size_t)kWaves * 32 * BN * 4);
+// The codes of one pair of units for CT column tiles (and their high bits)
+template <int F, int CT>
+struct PairCodes {
+  u32x4_t c[CT][Fmt<F>::NC];
+  uint32_t h[CT][Fmt<F>::NH];
+};
 
-  // Byte offsets of this lane's loads, per column tile (rows past the
-  // block repeat the last one; their sums are never stored), relative to
-  // buffers over the block's rows of each plane.
-  const int row_bytes = units * U::CB;
-  constexpr int HB = F == FMT_Q5 ? 8 : F == FMT_Q6 ? 16 : 0;  // high-plane bytes per unit and row
-  const rsrc_t rlo = make_rsrc(lo + (size_t)n0 * row_bytes, (uint32_t)(rows * row_bytes));
-  const rsrc_t rhi = make_rsrc(HB ? hi + (size_t)n0 * units * HB : lo, (uint32_t)(rows * units * HB));
-  const rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)T * K * 2));
-  uint32_t lo_off[CT], hi_off[CT];
-  int tab_row[CT];
+// Byte offsets of this lane's code loads per column tile (rows past the
+// block repeat the last one; their sums are never stored), relative to
+// buffers over the block's rows of each plane, and the lane's row in the
+// scale table.  Paired formats: quarter lq reads half lq % 2 of the pair's
+// unit lq / 2; BF16_CTRL: quarter lq of each unit.
+template <int F, int CT>
+__device__ __forceinline__ void lane_offsets(int rows, int units, int ts, int li, int lq, uint32_t (&lo_off)[CT],
+                                             uint32_t (&hi_off)[CT], int (&tab_row)[CT]) {
+  constexpr int HB = Fmt<F>::HB;
+  const int row_bytes = units * Unit<F>::CB;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int rl = min(16 * ct + li, rows - 1);
-    // paired formats: quarter lq reads half lq % 2 of the pair's unit lq / 2
     if constexpr (F == FMT_BF16) lo_off[ct] = (uint32_t)(rl * row_bytes + lq * 16);
-    else lo_off[ct] = (uint32_t)(rl * row_bytes + (lq >> 1) * U::CB + (lq & 1) * 16);
+    else lo_off[ct] = (uint32_t)(rl * row_bytes + (lq >> 1) * Unit<F>::CB + (lq & 1) * 16);
     hi_off[ct] = (uint32_t)(rl * units * HB + (lq >> 1) * HB + (lq & 1) * (HB / 2));
     tab_row[ct] = rl * ts;
   }
-  uint32_t x_off[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
-    x_off[tt] = (uint32_t)(min(32 * wt + 16 * tt + li, T - 1) * K * 2 + xq * 16 * XH);
+}
 
-  // The ring: slot p % 2 holds pair p's activations, piece (v, tl, pc) at
-  // position (v TTK + tl) PPT + (pc ^ (tl % PPT)) (the XOR spreads the
-  // operand reads of 16 tokens over the banks).  Load j of a pair moves
-  // positions 64 j .. 64 j + 63, lane l the one at 64 j + l.
-  uint8_t* const ring = lds + (size_t)wave * 2 * SLOT;
-  uint32_t xdma[XL ? NI : 1];
-  if constexpr (XL) {
+// The code loads of pair p: the pair's offset is the wave-uniform buffer
+// offset; a pair past the wave's run reads through the empty resource rnull
+// (nothing, zeros)
+template <int F, int CT>
+__device__ __forceinline__ void load_codes(rsrc_t rlo, rsrc_t rhi, rsrc_t rnull, const uint32_t (&lo_off)[CT],
+                                           const uint32_t (&hi_off)[CT], int p, bool live, PairCodes<F, CT>& L) {
+  constexpr int CB = Unit<F>::CB, HB = Fmt<F>::HB;
+  const rsrc_t rl = live ? rlo : rnull, rh = live ? rhi : rnull;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int q = j * 64 + lane;
-      const int v = q / (TTK * PPT), tl = (q / PPT) % TTK, pc = (q % PPT) ^ (tl % PPT);
-      xdma[j] = (uint32_t)(min(32 * wt + tl, T - 1) * K * 2 + v * U::K * 2 + pc * 16);
+  for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+    for (int v = 0; v < Fmt<F>::NC; ++v)
+      L.c[ct][v] = __builtin_amdgcn_raw_buffer_load_b128(rl, lo_off[ct], (uint32_t)((2 * p + v) * CB), 2);
+    if constexpr (F == FMT_Q5) L.h[ct][0] = __builtin_amdgcn_raw_buffer_load_b32(rh, hi_off[ct], (uint32_t)(2 * p * HB), 0);
+    if constexpr (F == FMT_Q6) {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rh, hi_off[ct], (uint32_t)(2 * p * HB), 0);
+      L.h[ct][0] = v.x;
+      L.h[ct][1] = v.y;
     }
   }
-  // a pair past the wave's run reads nothing (zeros land in the slot)
-  auto issue_x = [&](int p) __device__ {
-    if constexpr (XL) {
-      uint8_t* slot = ring + (p & 1) * SLOT;
-      const uint32_t base = (uint32_t)(2 * p * U::K * 2);
-#pragma unroll
-      for (int j = 0; j < NI; ++j) dma16(rx, p < pe ? xdma[j] + base : kNowhere, slot + j * 1024);
-    }
-  };
-  // pair p's operands: lane (li, lq) takes pieces XH xq .. XH xq + XH - 1 of
-  // token 16 tt + li in each unit
-  auto read_x = [&](int p, u32x4_t (&A)[2][TT][XH]) __device__ {
-    const uint8_t* slot = ring + (p & 1) * SLOT;
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int h = 0; h < XH; ++h) {
-          const int tl = 16 * tt + li;
-          A[v][tt][h] = *reinterpret_cast<const u32x4_t*>(
-              slot + ((v * TTK + tl) * PPT + ((XH * xq + h) ^ (tl % PPT))) * 16);
-        }
-  };
+}
 
-  // Pair p covers units 2p and 2p + 1.  A pair past the wave's run reads
-  // nothing; the second unit of the last pair of an odd count reads the
-  // next row's bytes or nothing, and its products are skipped.
-  auto load = [&](int p, L_t& L) __device__ {
-    const bool live = p < pe;
+// Lanes l and l + 32 (quarters q and q + 2) exchange half of their 16 code
+// bytes: afterwards every lane holds 8 code bytes of each unit of the pair,
+// bytes 8 xq .. 8 xq + 7, and their high bits (ca, ha: the first unit).
+template <int F, int CT>
+__device__ __forceinline__ void split_pair(const PairCodes<F, CT>& L, int hsh, u32x2_t (&ca)[CT], u32x2_t (&cb)[CT],
+                                           uint32_t (&ha)[CT], uint32_t (&hb)[CT]) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      if constexpr (F == FMT_BF16) {
-#pragma unroll
-        for (int v = 0; v < 2; ++v)
-          L.c[ct][v] = __builtin_amdgcn_raw_buffer_load_b128(
-              rlo, live ? lo_off[ct] + (uint32_t)((2 * p + v) * U::CB) : kNowhere, 0, 2);
-      } else {
-        L.c[ct][0] = __builtin_amdgcn_raw_buffer_load_b128(rlo, live ? lo_off[ct] + (uint32_t)(2 * p * U::CB) : kNowhere,
-                                                           0, 2);
-      }
-      const uint32_t ho = live ? hi_off[ct] + (uint32_t)(2 * p * HB) : kNowhere;
-      if constexpr (F == FMT_Q5) L.h[ct][0] = __builtin_amdgcn_raw_buffer_load_b32(rhi, ho, 0, 0);
-      if constexpr (F == FMT_Q6) {
-        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rhi, ho, 0, 0);
-        L.h[ct][0] = v.x;
-        L.h[ct][1] = v.y;
-      }
+  for (int ct = 0; ct < CT; ++ct) {
+    const auto sx = __builtin_amdgcn_permlane32_swap(L.c[ct][0].x, L.c[ct][0].z, false, false);
+    const auto sy = __builtin_amdgcn_permlane32_swap(L.c[ct][0].y, L.c[ct][0].w, false, false);
+    ca[ct] = u32x2_t{sx[0], sy[0]};
+    cb[ct] = u32x2_t{sx[1], sy[1]};
+    ha[ct] = hb[ct] = 0u;
+    if constexpr (F == FMT_Q5) {
+      // both lanes get both dwords: [0] the lower lane's, [1] the upper lane's
+      const auto hs = __builtin_amdgcn_permlane32_swap(L.h[ct][0], L.h[ct][0], false, false);
+      ha[ct] = hs[0] >> hsh;
+      hb[ct] = hs[1] >> hsh;
     }
-    if constexpr (!XL) {
-#pragma unroll
-      for (int v = 0; v < 2; ++v)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int p2 = 0; p2 < XH; ++p2)
-            L.a[v][tt][p2] = __builtin_amdgcn_raw_buffer_load_b128(
-                rx, live ? x_off[tt] + (uint32_t)(((2 * p + v) * U::K + 8 * p2) * 2) : kNowhere, 0, 0);
+    if constexpr (F == FMT_Q6) {
+      const auto hs = __builtin_amdgcn_permlane32_swap(L.h[ct][0], L.h[ct][1], false, false);
+      ha[ct] = hs[0];
+      hb[ct] = hs[1];
     }
-  };
+  }
+}
 
-  // The block's scales go to LDS once (their rows are contiguous in the
-  // plane): eight 2-byte elements per thread and batch.
-  const int elems = rows * ts / 2;
-  const rsrc_t rsc = make_rsrc(U::SB ? sc + (size_t)n0 * ts : lo, (uint32_t)(rows * ts));
-  uint16_t* sdst = reinterpret_cast<uint16_t*>(tab);
-  auto stage_load = [&](int i0, uint16_t (&v)[8]) __device__ {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = i0 + j * kThreads + tid;
-      v[j] = __builtin_amdgcn_raw_buffer_load_b16(rsc, i < elems ? (uint32_t)(2 * i) : kNowhere, 0, 0);
-    }
-  };
-  auto stage_store = [&](int i0, const uint16_t (&v)[8]) __device__ {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = i0 + j * kThreads + tid;
-      if (i < elems) sdst[i] = v[j];
-    }
-  };
-
+// The products of unit u of a paired format for TT token tiles: a = its
+// activations (XH 16-byte pieces per tile), c = this lane's 8 code bytes per
+// row (two dwords), h = their high bits.  NAT: the Q4 operands are built in
+// the activations' own order (k0,k1) (k2,k3) ..., so the activation pieces
+// go to the matrix cores as loaded; otherwise the code order (k0,k4) (k1,k5)
+// ... and the activations are permuted to it.
+template <int F, int CT, int TT, bool NAT>
+__device__ __forceinline__ void unit_products(int u, const u32x4_t (&a)[TT][Fmt<F>::XH], const u32x2_t (&c)[CT],
+                                              const uint32_t (&h)[CT], const uint8_t* tab, const int (&tab_row)[CT],
+                                              int xq, f32x4_t (&acc)[CT][TT]) {
   // constant operands of the offset codes (q = 8 for Q4, 16 for Q5, 32 for Q6; c = 0 for W8)
-  const uint32_t kc = F == FMT_Q4   ? 0x43084308u
-                      : F == FMT_Q5 ? 0x43104310u
-                      : F == FMT_Q6 ? 0x43204320u
-                                    : 0x43004300u;
+  constexpr uint32_t kc = F == FMT_Q4 ? 0x43084308u : F == FMT_Q5 ? 0x43104310u : F == FMT_Q6 ? 0x43204320u
+                                                                                              : 0x43004300u;
   const bf16x8_t bconst = __builtin_bit_cast(bf16x8_t, u32x4_t{kc, kc, kc, kc});
   const bf16x8_t bconst_hi = __builtin_bit_cast(bf16x8_t, u32x4_t{0x43C043C0u, 0x43C043C0u, 0x43C043C0u, 0x43C043C0u});
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const int hsh = (lane >> 5) << 4;  // Q5: the half of a high dword that belongs to this lane
+  if constexpr (Fmt<F>::NIB) {
+    bf16x8_t av[TT][2];
+    f32x4_t cr[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if constexpr (NAT) {
+        av[tt][0] = __builtin_bit_cast(bf16x8_t, a[tt][0]);
+        av[tt][1] = __builtin_bit_cast(bf16x8_t, a[tt][1]);
+      } else {
+        av[tt][0] = pair_order(a[tt][0]);
+        av[tt][1] = pair_order(a[tt][1]);
+      }
+      cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][0], bconst, zero4, 0, 0, 0);
+      cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][1], bconst, cr[tt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      bf16x8_t b0, b1;
+      if constexpr (F == FMT_Q4 && NAT) {
+        b0 = q4_natural(c[ct].x);
+        b1 = q4_natural(c[ct].y);
+      } else if constexpr (F == FMT_Q4) {
+        b0 = q4_operand(c[ct].x);
+        b1 = q4_operand(c[ct].y);
+      } else if constexpr (F == FMT_Q5) {
+        b0 = q5_operand(c[ct].x, h[ct]);
+        b1 = q5_operand(c[ct].y, h[ct] >> 8);
+      } else {
+        b0 = q6_operand(c[ct].x, h[ct]);
+        b1 = q6_operand(c[ct].y, h[ct] >> 16);
+      }
+      const float s = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(tab + tab_row[ct] + 2 * u));
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][0], b0, zero4, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][1], b1, p, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ct][tt][r] = __builtin_fmaf(s, p[r] - cr[tt][r], acc[ct][tt][r]);
+      }
+    }
+  } else if constexpr (F == FMT_W8) {
+    bf16x8_t av[TT];
+    f32x4_t cr[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      av[tt] = __builtin_bit_cast(bf16x8_t, a[tt][0]);
+      cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bconst, zero4, 0, 0, 0);
+      cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bconst_hi, cr[tt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      bf16x8_t bl, bh;
+      w8_operands(c[ct].x, c[ct].y, bl, bh);
+      const float s = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(tab + tab_row[ct] + 2 * u));
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bl, zero4, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bh, p, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ct][tt][r] = __builtin_fmaf(s, p[r] - cr[tt][r], acc[ct][tt][r]);
+      }
+    }
+  } else {  // NVFP4: the lane's 16 weights are one E4M3 scale group
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const float s = e4m3_to_f32(tab[tab_row[ct] + 4 * u + xq]);
+      const bf16x8_t b0 = nvfp4_operand(c[ct].x, s), b1 = nvfp4_operand(c[ct].y, s);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[tt][0]), b0,
+                                                              acc[ct][tt], 0, 0, 0);
+        acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[tt][1]), b1,
+                                                              acc[ct][tt], 0, 0, 0);
+      }
+    }
+  }
+}
 
-  f32x4_t acc[CT][TT];
+// BF16_CTRL: one unit (32 weights) of bf16 weights, c = this lane's 16 bytes per row
+template <int CT, int TT>
+__device__ __forceinline__ void bf16_unit(const u32x4_t (&a)[TT][1], const u32x4_t (&c)[CT],
+                                          f32x4_t (&acc)[CT][TT]) {
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[ct][tt] = zero4;
+    for (int tt = 0; tt < TT; ++tt)
+      acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[tt][0]),
+                                                            __builtin_bit_cast(bf16x8_t, c[ct]), acc[ct][tt], 0, 0, 0);
+}
 
-  // the products of unit u: a = its activations, c = this lane's 8 code
-  // bytes per row (two dwords), h = their high bits
-  auto unit_products = [&](int u, const u32x4_t (&a)[TT][XH], const u32x2_t (&c)[CT], const uint32_t (&h)[CT])
-      __device__ {
-    if constexpr (NIB) {
-      bf16x8_t av[TT][2];
-      f32x4_t cr[TT];
+// The block's scales go to LDS once (their rows are contiguous in the plane):
+// eight 2-byte elements per thread and batch.
+__device__ __forceinline__ void stage_load(rsrc_t rsc, int elems, int i0, int tid, uint16_t (&v)[8]) {
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        av[tt][0] = pair_order(a[tt][0]);
-        av[tt][1] = pair_order(a[tt][1]);
-        cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][0], bconst, zero4, 0, 0, 0);
-        cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][1], bconst, cr[tt], 0, 0, 0);
-      }
+  for (int j = 0; j < 8; ++j) {
+    const int i = i0 + j * kThreads + tid;
+    v[j] = __builtin_amdgcn_raw_buffer_load_b16(rsc, i < elems ? (uint32_t)(2 * i) : kNowhere, 0, 0);
+  }
+}
+__device__ __forceinline__ void stage_store(uint16_t* dst, int elems, int i0, int tid, const uint16_t (&v)[8]) {
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        bf16x8_t b0, b1;
-        if constexpr (F == FMT_Q4) {
-          b0 = q4_operand(c[ct].x);
-          b1 = q4_operand(c[ct].y);
-        } else if constexpr (F == FMT_Q5) {
-          b0 = q5_operand(c[ct].x, h[ct]);
-          b1 = q5_operand(c[ct].y, h[ct] >> 8);
-        } else {
-          b0 = q6_operand(c[ct].x, h[ct]);
-          b1 = q6_operand(c[ct].y, h[ct] >> 16);
-        }
-        const float s = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(tab + tab_row[ct] + 2 * u));
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][0], b0, zero4, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt][1], b1, p, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ct][tt][r] = __builtin_fmaf(s, p[r] - cr[tt][r], acc[ct][tt][r]);
-        }
-      }
-    } else if constexpr (F == FMT_W8) {
-      bf16x8_t av[TT];
-      f32x4_t cr[TT];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        av[tt] = __builtin_bit_cast(bf16x8_t, a[tt][0]);
-        cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bconst, zero4, 0, 0, 0);
-        cr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bconst_hi, cr[tt], 0, 0, 0);
-      }
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        bf16x8_t bl, bh;
-        w8_operands(c[ct].x, c[ct].y, bl, bh);
-        const float s = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(tab + tab_row[ct] + 2 * u));
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bl, zero4, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[tt], bh, p, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ct][tt][r] = __builtin_fmaf(s, p[r] - cr[tt][r], acc[ct][tt][r]);
-        }
-      }
-    } else {  // NVFP4: the lane's 16 weights are one E4M3 scale group
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const float s = e4m3_to_f32(tab[tab_row[ct] + 4 * u + xq]);
-        const bf16x8_t b0 = nvfp4_operand(c[ct].x, s), b1 = nvfp4_operand(c[ct].y, s);
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[tt][0]), b0,
-                                                                acc[ct][tt], 0, 0, 0);
-          acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[tt][1]), b1,
-                                                                acc[ct][tt], 0, 0, 0);
-        }
-      }
-    }
-  };
+  for (int j = 0; j < 8; ++j) {
+    const int i = i0 + j * kThreads + tid;
+    if (i < elems) dst[i] = v[j];
+  }
+}
 
-  // the products of pair p (its second unit is skipped past the row's end)
-  auto pair_products = [&](int p, const L_t& L, const u32x4_t (&A)[2][TT][XH]) __device__ {
-    const bool second = 2 * p + 1 < units;
-    if constexpr (F == FMT_BF16) {
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        if (v == 1 && !second) break;
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-            acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[v][tt][0]),
-                                                                  __builtin_bit_cast(bf16x8_t, L.c[ct][v]),
-                                                                  acc[ct][tt], 0, 0, 0);
-      }
-    } else {
-      // Lanes l and l + 32 (quarters q and q + 2) exchange half of their
-      // 16 bytes: afterwards every lane holds 8 code bytes of each unit,
-      // bytes 8 xq .. 8 xq + 7 (and their high bits).
-      u32x2_t ca[CT], cb[CT];
-      uint32_t ha[CT], hb[CT];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const auto sx = __builtin_amdgcn_permlane32_swap(L.c[ct][0].x, L.c[ct][0].z, false, false);
-        const auto sy = __builtin_amdgcn_permlane32_swap(L.c[ct][0].y, L.c[ct][0].w, false, false);
-        ca[ct] = u32x2_t{sx[0], sy[0]};
-        cb[ct] = u32x2_t{sx[1], sy[1]};
-        ha[ct] = hb[ct] = 0u;
-        if constexpr (F == FMT_Q5) {
-          // both lanes get both dwords: [0] the lower lane's, [1] the upper lane's
-          const auto hs = __builtin_amdgcn_permlane32_swap(L.h[ct][0], L.h[ct][0], false, false);
-          ha[ct] = hs[0] >> hsh;
-          hb[ct] = hs[1] >> hsh;
-        }
-        if constexpr (F == FMT_Q6) {
-          const auto hs = __builtin_amdgcn_permlane32_swap(L.h[ct][0], L.h[ct][1], false, false);
-          ha[ct] = hs[0];
-          hb[ct] = hs[1];
-        }
-      }
-      unit_products(2 * p, A[0], ca, ha);
-      if (second) unit_products(2 * p + 1, A[1], cb, hb);
-    }
-  };
-
-  // Scales of the block (first batch) in flight with the first two pairs'
-  // loads; two register sets (and ring slots) take turns, so while one
-  // pair's products run the next pair's loads are in flight.  (A table
-  // larger than one batch is copied first, on its own.)
-  L_t b[NB];
-  uint16_t sv[8];
-  const bool one_batch = elems <= 8 * kThreads;
-  if constexpr (U::SB > 0) {
-    if (!one_batch) {
-      for (int i0 = 0; i0 < elems; i0 += 8 * kThreads) {
-        stage_load(i0, sv);
-        stage_store(i0, sv);
-      }
-    }
-    stage_load(0, sv);  // a repeat of the first batch when already copied
-  }
-  // per pair, in this order: its activations to LDS (XL), then its codes
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    __builtin_amdgcn_sched_barrier(0);
-    issue_x(pb + i);
-    __builtin_amdgcn_sched_barrier(0);
-    load(pb + i, b[i]);
-  }
-  if constexpr (U::SB > 0) stage_store(0, sv);
-  // the table's writes are visible after this; the loads stay in flight
-  // (a fence here would also wait for the copies into the rings)
-  wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
-  // loads per pair: LC code-plane loads after NI activation loads
-  constexpr int LC = CT * (Loads<F, CT, TT>::NC + ((F == FMT_Q5 || F == FMT_Q6) ? 1 : 0));
-  // (Every load is issued outside the branches, so the compiler's count of
-  // the loads in flight stays exact.)
-  for (int p = pb; p < pe; p += NB) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      u32x4_t A[2][TT][XH];
-      if constexpr (XL) {
-        // pair p + i's activations have landed once only the loads issued
-        // after them (its codes, the next pair's activations and codes) may
-        // be outstanding
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm<2 * LC + NI>();
-        read_x(p + i, A);
-        wait_lgkm0();
-        __builtin_amdgcn_sched_barrier(0);
-        issue_x(p + i + NB);  // into the slot just read
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-#pragma unroll
-        for (int v = 0; v < 2; ++v)
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-            for (int h = 0; h < XH; ++h) A[v][tt][h] = b[i].a[v][tt][h];
-      }
-      if (i == 0 || p + i < pe) pair_products(p + i, b[i], A);
-      load(p + i + NB, b[i]);
-    }
-  }
-  if constexpr (XL) {
-    wait_vm<0>();  // every copy into the rings has landed before they are reused
-    __syncthreads();
-  }
-
-  // sum over the WK runs in binary64: red[wk][t < BT][col < BN] binary32 partials
+// The sum over the eight waves' K runs in binary64: red[w][t < 16 TT][col <
+// BN] binary32 partials (lane (li, lq) of wave w holds row 16 ct + li,
+// tokens 16 tt + 4 lq + r), then one output per thread and step, rounded
+// once; an output that comes out non-finite is formed again exactly.
+template <int F, int CT, int TT>
+__device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t* lds, int wave, int li, int lq,
+                                          int tid, const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo,
+                                          const uint8_t* __restrict__ hi, const uint8_t* __restrict__ sc,
+                                          uint16_t* __restrict__ y, const uint16_t* __restrict__ res, int f32out,
+                                          int N, int K, int T, int BN, int n0, int rows) {
+  constexpr int BT = 16 * TT;
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
@@ -629,8 +509,8 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 32 * wt + 16 * tt + 4 * lq + r;
-        if (col < BN && t < T) red[(wk * BT + t) * BN + col] = acc[ct][tt][r];
+        const int t = 16 * tt + 4 * lq + r;
+        if (col < BN && t < T) red[(wave * BT + t) * BN + col] = acc[ct][tt][r];
       }
   }
   __syncthreads();
@@ -638,57 +518,466 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
     const int t = i / rows, col = i - t * rows;
     double v = 0.0;
 #pragma unroll
-    for (int w = 0; w < WK; ++w) v += (double)red[(w * BT + t) * BN + col];
+    for (int w = 0; w < kWaves; ++w) v += (double)red[(w * BT + t) * BN + col];
     const size_t o = (size_t)t * N + n0 + col;
     if (f32out) {
       reinterpret_cast<float*>(y)[o] = (float)v;  // binary32 sums (the gate and up of LinearSwiGLU)
       continue;
     }
     if (res != nullptr) v += (double)bf16_bits_to_f32(res[o]);  // LinearAdd
-    uint16_t h = f32_to_bf16_rne((float)v);
-    if ((h & 0x7F80u) == 0x7F80u) h = exact_output<F>(x, lo, hi, sc, res, N, K, n0 + col, t);  // rare
-    y[o] = h;
+    uint16_t hv = f32_to_bf16_rne((float)v);
+    if ((hv & 0x7F80u) == 0x7F80u) hv = exact_output<F>(x, lo, hi, sc, res, N, K, n0 + col, t);  // rare
+    y[o] = hv;
   }
 }
 
-template <int F, int CT, int TT, int WT>
-hipError_t launch_one(const FmtArgs& a, const FmtPlan& p, const uint16_t* x, uint16_t* y, const uint16_t* res,
+// ---------------------------------------------------------------------------
+// Up to 16 tokens: the eight waves split the block's pairs of units; each
+// pair's codes and activations go straight to registers, two register sets
+// taking turns (the next pair's loads in flight during a pair's products).
+// ---------------------------------------------------------------------------
+template <int F, int CT>
+__global__ void __launch_bounds__(kThreads, 1)
+fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const uint8_t* __restrict__ hi,
+           const uint8_t* __restrict__ sc, uint16_t* __restrict__ y, const uint16_t* __restrict__ res, int f32out,
+           int N, int K, int T, int BN) {
+  using U = Unit<F>;
+  constexpr int XH = Fmt<F>::XH, HB = Fmt<F>::HB;
+  constexpr int NB = 2;  // pairs in flight (register sets)
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lq = lane >> 4;
+  // the quarter of each unit this lane multiplies: after the exchange of
+  // the paired loads, quarter lq holds code bytes 8 xq .. 8 xq + 7 of a unit
+  const int xq = Fmt<F>::PAIRED ? (((lq & 1) << 1) | (lq >> 1)) : lq;
+  const int n0 = blockIdx.x * BN;
+  const int rows = min(BN, N - n0);
+  const int units = K / U::K;
+  const int pairs = (units + 1) >> 1;
+  const int pb = (int)(((int64_t)pairs * wave) / kWaves), pe = (int)(((int64_t)pairs * (wave + 1)) / kWaves);
+  const int ts = units * U::SB;  // bytes of one row's scales
+  // LDS: the partials of the final sum, then the scale table
+  uint8_t* tab = lds + (size_t)kWaves * 16 * BN * 4;
+
+  const rsrc_t rlo = make_rsrc(lo + (size_t)n0 * units * U::CB, (uint32_t)(rows * units * U::CB));
+  const rsrc_t rhi = make_rsrc(HB ? hi + (size_t)n0 * units * HB : lo, (uint32_t)(rows * units * HB));
+  const rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)T * K * 2));
+  const rsrc_t rnull = make_rsrc(x, 0u);  // every access out of range
+  uint32_t lo_off[CT], hi_off[CT];
+  int tab_row[CT];
+  lane_offsets<F, CT>(rows, units, ts, li, lq, lo_off, hi_off, tab_row);
+  const uint32_t x_off = (uint32_t)(min(li, T - 1) * K * 2 + xq * 16 * XH);
+
+  struct Loads {
+    PairCodes<F, CT> c;
+    u32x4_t a[2][1][XH];
+  };
+  auto load = [&](int p, Loads& L) __device__ {
+    const bool live = p < pe;
+    load_codes<F, CT>(rlo, rhi, rnull, lo_off, hi_off, p, live, L.c);
+    const rsrc_t r = live ? rx : rnull;
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int p2 = 0; p2 < XH; ++p2)
+        L.a[v][0][p2] = __builtin_amdgcn_raw_buffer_load_b128(r, x_off, (uint32_t)(((2 * p + v) * U::K + 8 * p2) * 2), 0);
+  };
+
+  const int elems = rows * ts / 2;
+  const rsrc_t rsc = make_rsrc(U::SB ? sc + (size_t)n0 * ts : lo, (uint32_t)(rows * ts));
+  uint16_t* sdst = reinterpret_cast<uint16_t*>(tab);
+  const int hsh = (lane >> 5) << 4;  // Q5: the half of a high dword that belongs to this lane
+
+  f32x4_t acc[CT][1];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) acc[ct][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // the products of pair p (its second unit is skipped past the row's end)
+  auto pair_products = [&](int p, const Loads& L) __device__ {
+    const bool second = 2 * p + 1 < units;
+    if constexpr (F == FMT_BF16) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        if (v == 1 && !second) break;
+        u32x4_t cv[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) cv[ct] = L.c.c[ct][v];
+        bf16_unit<CT, 1>(L.a[v], cv, acc);
+      }
+    } else {
+      u32x2_t ca[CT], cb[CT];
+      uint32_t ha[CT], hb[CT];
+      split_pair<F, CT>(L.c, hsh, ca, cb, ha, hb);
+      unit_products<F, CT, 1, false>(2 * p, L.a[0], ca, ha, tab, tab_row, xq, acc);
+      if (second) unit_products<F, CT, 1, false>(2 * p + 1, L.a[1], cb, hb, tab, tab_row, xq, acc);
+    }
+  };
+
+  // Scales of the block (first batch) in flight with the first two pairs'
+  // loads.  (A table larger than one batch is copied first, on its own.)
+  Loads b[NB];
+  uint16_t sv[8];
+  if constexpr (U::SB > 0) {
+    if (elems > 8 * kThreads) {
+      for (int i0 = 0; i0 < elems; i0 += 8 * kThreads) {
+        stage_load(rsc, elems, i0, tid, sv);
+        stage_store(sdst, elems, i0, tid, sv);
+      }
+    }
+    stage_load(rsc, elems, 0, tid, sv);  // a repeat of the first batch when already copied
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) load(pb + i, b[i]);
+  if constexpr (U::SB > 0) stage_store(sdst, elems, 0, tid, sv);
+  // the table's writes are visible after this; the loads stay in flight
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  // (Every load is issued outside the branches, so the compiler's count of
+  // the loads in flight stays exact.)
+  for (int p = pb; p < pe; p += NB) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (i == 0 || p + i < pe) pair_products(p + i, b[i]);
+      load(p + i + NB, b[i]);
+    }
+  }
+  // (the partials area lies before the scale table: no wait for its readers)
+  final_sum<F, CT, 1>(acc, lds, wave, li, lq, tid, x, lo, hi, sc, y, res, f32out, N, K, T, BN, n0, rows);
+}
+
+// ---------------------------------------------------------------------------
+// 17 to 128 tokens: every wave takes all 16 TT tokens of the launch for its
+// run of pairs, so each code operand is built once for all of them.  The
+// activations go through a ring of NS unit slots per wave in LDS (direct
+// copies in memory order, read back in operand order).  A wave loads the
+// codes of a chunk of up to six pairs at once (four or two for Q5/Q6),
+// right after the copies of the chunk's first NS units: a unit's copies
+// complete in issue order with the codes, so the wait for a unit's
+// activations has a fixed count and the codes have the chunk's first units
+// to arrive.
+// ---------------------------------------------------------------------------
+template <int F, int TT>
+struct TokShape {
+  static constexpr int PPT = Unit<F>::K * 2 / 16;   // 16-byte pieces per token and unit
+  static constexpr int TTK = 16 * TT;               // tokens per launch
+  static constexpr int SLOT = TTK * PPT * 16;       // one unit's activations [token][piece]
+  static constexpr int NS = SLOT * 4 <= kRingWave ? 4 : SLOT * 2 <= kRingWave ? 2 : 1;  // slots per wave
+  static constexpr int NI = TTK * PPT / 64;         // direct-to-LDS loads per unit and lane
+  static constexpr int RING = kWaves * NS * SLOT;   // all waves' rings
+};
+// code pairs held in registers at once (fewer with the high bits of Q5/Q6)
+template <int F, int CT>
+constexpr int tok_pairs() {
+  return (F == FMT_Q5 || F == FMT_Q6) ? (CT <= 2 ? 4 : 2) : (CT <= 2 ? 6 : 4);
+}
+
+template <int F, int CT, int TT>
+__global__ void __launch_bounds__(kThreads, 1)
+fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const uint8_t* __restrict__ hi,
+               const uint8_t* __restrict__ sc, uint16_t* __restrict__ y, const uint16_t* __restrict__ res,
+               int f32out, int N, int K, int T, int BN, int TS) {
+  using U = Unit<F>;
+  using S = TokShape<F, TT>;
+  constexpr int XH = Fmt<F>::XH, HB = Fmt<F>::HB;
+  constexpr int PPT = S::PPT, NS = S::NS, NI = S::NI, SLOT = S::SLOT;
+  constexpr int MP = tok_pairs<F, CT>();
+  constexpr int LC = CT * Fmt<F>::LPT;  // code-plane loads per pair
+  constexpr bool NAT = F == FMT_Q4;
+  static_assert((2 * MP) % NS == 0, "a chunk of pairs keeps the ring's slot order");
+  static_assert((NS - 1) * NI + MP * LC <= 63, "the load counter holds 63");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lq = lane >> 4;
+  const int xq = Fmt<F>::PAIRED ? (((lq & 1) << 1) | (lq >> 1)) : lq;
+  // Workgroup -> (row block, token range of 16 TT tokens).  With TS ranges
+  // the TS workgroups of a row block have the same number mod 8, so they run
+  // on one XCD (workgroups are dealt to the eight XCDs in turn) and its
+  // codes come from HBM once.
+  int rb = blockIdx.x, tr = 0;
+  if (TS > 1) {
+    const int g = blockIdx.x >> 3;
+    tr = g % TS;
+    rb = (g / TS) * 8 + (blockIdx.x & 7);
+  }
+  const int n0 = rb * BN, t0 = tr * 16 * TT;
+  if (n0 >= N || t0 >= T) return;  // (the grid's last row of eight)
+  x += (size_t)t0 * K;
+  if (res != nullptr) res += (size_t)t0 * N;
+  y = f32out ? reinterpret_cast<uint16_t*>(reinterpret_cast<float*>(y) + (size_t)t0 * N) : y + (size_t)t0 * N;
+  T = min(16 * TT, T - t0);
+  const int rows = min(BN, N - n0);
+  const int units = K / U::K;
+  const int pairs = (units + 1) >> 1;
+  const int pb = (int)(((int64_t)pairs * wave) / kWaves), pe = (int)(((int64_t)pairs * (wave + 1)) / kWaves);
+  const int ue = min(2 * pe, units);  // past this wave's last unit
+  const int ts = units * U::SB;
+  // LDS: the rings, then the scale table; the final sum's partials reuse
+  // the start once both are no longer read
+  uint8_t* const ring = lds + (size_t)wave * NS * SLOT;
+  uint8_t* tab = lds + S::RING;
+
+  const rsrc_t rlo = make_rsrc(lo + (size_t)n0 * units * U::CB, (uint32_t)(rows * units * U::CB));
+  const rsrc_t rhi = make_rsrc(HB ? hi + (size_t)n0 * units * HB : lo, (uint32_t)(rows * units * HB));
+  const rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)T * K * 2));
+  const rsrc_t rnull = make_rsrc(x, 0u);  // every access out of range
+  uint32_t lo_off[CT], hi_off[CT];
+  int tab_row[CT];
+  lane_offsets<F, CT>(rows, units, ts, li, lq, lo_off, hi_off, tab_row);
+
+  // A slot holds one unit's activations, piece (tl, pc) of token tl at
+  // position tl PPT + (pc ^ swz(tl)), swz(tl) = (tl / (16 / PPT)) % PPT: the
+  // sixteen lanes of an operand read (16 consecutive tokens, one piece
+  // each) then meet every 16-byte bank group of a 256-byte LDS row once.
+  // Copy j of a unit moves positions 64 j .. 64 j + 63, lane l the one at
+  // 64 j + l: 16 contiguous bytes of memory per lane, consecutive lanes on
+  // consecutive pieces.  Tokens past T repeat the last one (their sums are
+  // never stored).
+  auto swz = [](int tl) { return (tl / (16 / PPT)) % PPT; };
+  uint32_t xdma[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int q = j * 64 + lane;
+    const int tl = q / PPT, pc = (q % PPT) ^ swz(tl);
+    xdma[j] = (uint32_t)(min(tl, T - 1) * K * 2 + pc * 16);
+  }
+  // the unit's offset is the wave-uniform buffer offset; a unit past the
+  // run reads through rnull (nothing lands but zeros)
+  auto issue_x = [&](int u, int slot) __device__ {
+    uint8_t* dst = ring + slot * SLOT;
+    const rsrc_t r = u < ue ? rx : rnull;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) dma16(r, xdma[j], (uint32_t)(u * U::K * 2), dst + j * 1024);
+  };
+  // unit operands: lane (li, lq) takes pieces XH xq .. XH xq + XH - 1 of
+  // token 16 tt + li (swz(16 tt + li) = swz(li), so only the slot and the
+  // token tile move the address, by constants)
+  const uint8_t* xrd[XH];
+#pragma unroll
+  for (int h = 0; h < XH; ++h) xrd[h] = ring + (li * PPT + ((XH * xq + h) ^ swz(li))) * 16;
+  auto read_x = [&](int slot, u32x4_t (&A)[TT][XH]) __device__ {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int h = 0; h < XH; ++h)
+        A[tt][h] = *reinterpret_cast<const u32x4_t*>(xrd[h] + slot * SLOT + tt * (16 * PPT * 16));
+  };
+
+  const int elems = rows * ts / 2;
+  const rsrc_t rsc = make_rsrc(U::SB ? sc + (size_t)n0 * ts : lo, (uint32_t)(rows * ts));
+  uint16_t* sdst = reinterpret_cast<uint16_t*>(tab);
+  const int hsh = (lane >> 5) << 4;
+
+  f32x4_t acc[CT][TT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[ct][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Prologue: the scales' first batch, the first NS units' activations, then
+  // the first chunk's codes.
+  PairCodes<F, CT> cc[MP];
+  uint16_t sv[8];
+  if constexpr (U::SB > 0) {
+    if (elems > 8 * kThreads) {
+      for (int i0 = 0; i0 < elems; i0 += 8 * kThreads) {
+        stage_load(rsc, elems, i0, tid, sv);
+        stage_store(sdst, elems, i0, tid, sv);
+      }
+    }
+    stage_load(rsc, elems, 0, tid, sv);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) issue_x(2 * pb + s, s);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < MP; ++i) load_codes<F, CT>(rlo, rhi, rnull, lo_off, hi_off, pb + i, pb + i < pe, cc[i]);
+  if constexpr (U::SB > 0) stage_store(sdst, elems, 0, tid, sv);
+  // the table's writes are visible after this; the loads stay in flight
+  // (a fence here would also wait for the copies into the rings)
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+
+  // Chunks of MP pairs.  Unit j of a chunk reads slot j % NS.  Before it,
+  // the loads issued after its activations are: for j < NS the later
+  // slots' copies and the chunk's codes (issued after the copies of the
+  // chunk's first NS units), else the NS - 1 copies issued after it.
+  // (Every load is issued outside the branches, so these counts and the
+  // compiler's own stay exact.)
+  for (int p0 = pb; p0 < pe; p0 += MP) {
+#pragma unroll
+    for (int i = 0; i < MP; ++i) {
+      u32x2_t ca[CT], cb[CT];
+      uint32_t ha[CT], hb[CT];
+      if constexpr (Fmt<F>::PAIRED) split_pair<F, CT>(cc[i], hsh, ca, cb, ha, hb);
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const int j = 2 * i + v, u = 2 * p0 + j;
+        u32x4_t A[TT][XH];
+        __builtin_amdgcn_sched_barrier(0);
+        if (j < NS) wait_vm<(NS - 1) * NI + MP * LC>();
+        else wait_vm<(NS - 1) * NI>();
+        read_x(j % NS, A);
+        wait_lgkm0();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_x(u + NS, j % NS);  // into the slot just read
+        __builtin_amdgcn_sched_barrier(0);
+        if (u < ue) {
+          if constexpr (F == FMT_BF16) {
+            u32x4_t cv[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) cv[ct] = cc[i].c[ct][v];
+            bf16_unit<CT, TT>(A, cv, acc);
+          } else {
+            unit_products<F, CT, TT, NAT>(u, A, v ? cb : ca, v ? hb : ha, tab, tab_row, xq, acc);
+          }
+        }
+      }
+    }
+    // the next chunk's codes, after the copies of its first NS units (as in
+    // the prologue; past the run they read nothing)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < MP; ++i)
+      load_codes<F, CT>(rlo, rhi, rnull, lo_off, hi_off, p0 + MP + i, p0 + MP + i < pe, cc[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vm<0>();  // every copy into the rings has landed before the space is reused
+  __syncthreads();
+  final_sum<F, CT, TT>(acc, lds, wave, li, lq, tid, x, lo, hi, sc, y, res, f32out, N, K, T, BN, n0, rows);
+}
+
+// LDS of a launch: the few-token kernel's partials and scale table, or the
+// many-token kernel's rings and table (the partials reuse them)
+size_t fmt_lds(int ppt, int tt, int64_t bn, int64_t ts) {
+  const int64_t table = (bn * ts + 15) / 16 * 16;
+  const int64_t red = (int64_t)kWaves * 16 * tt * bn * 4;
+  if (tt == 1) return (size_t)(red + table);
+  const int64_t slot = 16 * tt * ppt * 16;
+  const int64_t ns = slot * 4 <= kRingWave ? 4 : slot * 2 <= kRingWave ? 2 : 1;
+  const int64_t ring = kWaves * ns * slot;
+  return (size_t)(ring + table > red ? ring + table : red);
+}
+
+// token tiles per many-token launch: 2, 3, 4, 6 or 8 (at most 4 with 3 or 4
+// column tiles, for the registers)
+int tok_tiles(int64_t t, int ct) {
+  const int cap = ct <= 2 ? 8 : 4;
+  const int need = (int)((t + 15) / 16);
+  static const int kTiles[] = {2, 3, 4, 6, 8};
+  for (int v : kTiles)
+    if (v >= need && v <= cap) return v;
+  return cap;
+}
+
+// One launch's shape on 17 or more tokens: row blocks of bn rows (ct column
+// tiles), ts token ranges of 16 tt tokens each.  Above 64 tokens (when the
+// rows allow) a row block twice as tall serves half the tokens: every
+// workgroup still does the same work, but the activation bytes it copies
+// (its tokens' whole rows) halve (6144 x 5120: T = 65..128 24.4-30.2 us
+// against 24.8-32.9); below that the taller block's extra code loads cost
+// more than the copies saved (T = 33..64 21-22 against 17-20.5 us).
+struct TokLaunch {
+  int64_t bn;
+  int ct, ts, tt;
+  int64_t grid;
+};
+TokLaunch tok_launch(int64_t n, int64_t t, int64_t bn1, int64_t ts_bytes, int64_t table_cap) {
+  TokLaunch L;
+  L.ts = 1;
+  L.bn = bn1;
+  if (t > 64 && (n + 255) / 256 <= 32) {
+    const int64_t bn2 = (2 * n + 255) / 256;
+    if (ts_bytes == 0 || bn2 * ts_bytes <= table_cap) {
+      L.ts = 2;
+      L.bn = bn2;
+    }
+  }
+  L.ct = (int)((L.bn + 15) / 16);
+  L.tt = tok_tiles((t + L.ts - 1) / L.ts, L.ct);
+  const int64_t nrb = (n + L.bn - 1) / L.bn;
+  L.grid = L.ts == 1 ? nrb : (nrb + 7) / 8 * 8 * L.ts;
+  return L;
+}
+
+template <int F, int CT, int TT>
+hipError_t launch_tok(const FmtArgs& a, const TokLaunch& L, const uint16_t* x, uint16_t* y, const uint16_t* res,
                       int t, hipStream_t s) {
-  auto kern = fmt_kernel<F, CT, TT, WT>;
+  auto kern = fmt_tok_kernel<F, CT, TT>;
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)p.blocks), dim3(kThreads), p.lds_bytes, s>>>(
+  const size_t lds = fmt_lds(TokShape<F, TT>::PPT, TT, L.bn, (a.k / Unit<F>::K) * Unit<F>::SB);
+  kern<<<dim3((unsigned)L.grid), dim3(kThreads), lds, s>>>(
+      x, static_cast<const uint8_t*>(a.lo), static_cast<const uint8_t*>(a.hi), static_cast<const uint8_t*>(a.sc), y,
+      res, a.f32 ? 1 : 0, (int)a.n, (int)a.k, t, (int)L.bn, L.ts);
+  return hipGetLastError();
+}
+
+template <int F, int CT>
+hipError_t launch_tok_ct(const FmtArgs& a, const TokLaunch& L, const uint16_t* x, uint16_t* y, const uint16_t* res,
+                         int t, hipStream_t s) {
+  switch (L.tt) {
+    case 2: return launch_tok<F, CT, 2>(a, L, x, y, res, t, s);
+    case 3: return launch_tok<F, CT, 3>(a, L, x, y, res, t, s);
+    case 4: return launch_tok<F, CT, 4>(a, L, x, y, res, t, s);
+    default:
+      if constexpr (CT <= 2) {
+        if (L.tt == 6) return launch_tok<F, CT, 6>(a, L, x, y, res, t, s);
+        return launch_tok<F, CT, 8>(a, L, x, y, res, t, s);
+      }
+      return hipErrorInvalidValue;
+  }
+}
+
+template <int F, int CT>
+hipError_t launch_few(const FmtArgs& a, const FmtPlan& p, const uint16_t* x, uint16_t* y, const uint16_t* res, int t,
+                      hipStream_t s) {
+  auto kern = fmt_kernel<F, CT>;
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(kern));
+  if (e != hipSuccess) return e;
+  const size_t lds = fmt_lds(0, 1, p.bn, (a.k / Unit<F>::K) * Unit<F>::SB);
+  kern<<<dim3((unsigned)p.blocks), dim3(kThreads), lds, s>>>(
       x, static_cast<const uint8_t*>(a.lo), static_cast<const uint8_t*>(a.hi), static_cast<const uint8_t*>(a.sc), y,
       res, a.f32 ? 1 : 0, (int)a.n, (int)a.k, t, p.bn);
   return hipGetLastError();
 }
 
-template <int F, int TT, int WT>
-hipError_t launch_ct(const FmtArgs& a, const FmtPlan& p, const uint16_t* x, uint16_t* y, const uint16_t* res, int t,
-                     hipStream_t s) {
-  switch (p.ct) {
-    case 1: return launch_one<F, 1, TT, WT>(a, p, x, y, res, t, s);
-    case 2: return launch_one<F, 2, TT, WT>(a, p, x, y, res, t, s);
-    case 3: return launch_one<F, 3, TT, WT>(a, p, x, y, res, t, s);
-    default: return launch_one<F, 4, TT, WT>(a, p, x, y, res, t, s);
-  }
-}
-
 template <int F>
 hipError_t launch_fmt_t(const FmtArgs& a, const FmtPlan& p, hipStream_t s) {
-  // up to 128 tokens per launch (a weight read per launch): 32 per token
-  // range of waves, 16 per tile
+  // one weight pass per launch of up to 128 tokens (64 with 3 or 4 column
+  // tiles and one token range)
   const size_t osz = a.f32 ? 4 : 2;
-  for (int64_t t0 = 0; t0 < a.t; t0 += 128) {
-    const int t = (int)(a.t - t0 < 128 ? a.t - t0 : 128);
+  const int64_t tsb = (a.k / Unit<F>::K) * Unit<F>::SB;
+  const int64_t table_cap = kLdsBytes - (int64_t)kWaves * kRingWave;
+  int64_t per = 128;
+  if (a.t > 16) {
+    const TokLaunch L = tok_launch(a.n, a.t > 128 ? 128 : a.t, p.bn, tsb, table_cap);
+    per = (int64_t)L.ts * 16 * (L.ct <= 2 ? 8 : 4);
+  }
+  for (int64_t t0 = 0; t0 < a.t; t0 += per) {
+    const int t = (int)(a.t - t0 < per ? a.t - t0 : per);
     const uint16_t* x = static_cast<const uint16_t*>(a.x) + t0 * a.k;
     uint16_t* y = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.y) + (size_t)t0 * a.n * osz);
     const uint16_t* res = a.res ? static_cast<const uint16_t*>(a.res) + t0 * a.n : nullptr;
     hipError_t e;
-    if (t <= 16) e = launch_ct<F, 1, 1>(a, p, x, y, res, t, s);
-    else if (t <= 32) e = launch_ct<F, 2, 1>(a, p, x, y, res, t, s);
-    else if (t <= 64) e = launch_ct<F, 2, 2>(a, p, x, y, res, t, s);
-    else e = launch_ct<F, 2, 4>(a, p, x, y, res, t, s);
+    if (t <= 16) {
+      switch (p.ct) {
+        case 1: e = launch_few<F, 1>(a, p, x, y, res, t, s); break;
+        case 2: e = launch_few<F, 2>(a, p, x, y, res, t, s); break;
+        case 3: e = launch_few<F, 3>(a, p, x, y, res, t, s); break;
+        default: e = launch_few<F, 4>(a, p, x, y, res, t, s); break;
+      }
+    } else {
+      const TokLaunch L = tok_launch(a.n, t, p.bn, tsb, table_cap);
+      switch (L.ct) {
+        case 1: e = launch_tok_ct<F, 1>(a, L, x, y, res, t, s); break;
+        case 2: e = launch_tok_ct<F, 2>(a, L, x, y, res, t, s); break;
+        case 3: e = launch_tok_ct<F, 3>(a, L, x, y, res, t, s); break;
+        default: e = launch_tok_ct<F, 4>(a, L, x, y, res, t, s); break;
+      }
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -703,9 +992,8 @@ bool fmt_plan(int fmt, int64_t n, int64_t k, int64_t t, FmtPlan* p) {
   // bytes of one row's scales in the LDS table
   const int64_t ts = fmt == FMT_BF16 ? 0 : fmt == FMT_W8 || fmt == FMT_NVFP4 ? k / 16 : k / 32;
   // launches of more than 16 tokens keep the waves' activation rings in LDS
-  // (two slots of 2 units x 32 tokens per wave)
-  const int64_t ppt = (fmt == FMT_W8 || fmt == FMT_BF16) ? 4 : 8;
-  const int64_t ring = t > 16 ? (int64_t)kWaves * 2 * (2 * 32 * ppt * 16) : 0;
+  // (at most kRingWave bytes per wave)
+  const int64_t ring = t > 16 ? (int64_t)kWaves * kRingWave : 0;
   const int64_t table_cap = ring + kTableBytes <= kLdsBytes ? kTableBytes : kLdsBytes - ring;
   int64_t bn = (n + 255) / 256;  // about one workgroup per CU
   if (bn > 64) bn = 64;          // at most four 16-row column tiles per wave
@@ -715,11 +1003,11 @@ bool fmt_plan(int fmt, int64_t n, int64_t k, int64_t t, FmtPlan* p) {
   p->bn = (int)bn;
   p->ct = (int)ct;
   p->blocks = (int)((n + bn - 1) / bn);
-  // binary32 partials [8 waves][32 tokens][bn] (the same for every split of
-  // the waves into token ranges; they reuse the rings), then the scale table
-  const int64_t red = (int64_t)kWaves * 32 * bn * 4;
-  p->lds_bytes = (size_t)((red > ring ? red : ring) + (bn * ts + 15) / 16 * 16);
-  return true;
+  // the largest launch's LDS (the partials of 16 tokens per tile)
+  const int ppt = (fmt == FMT_W8 || fmt == FMT_BF16) ? 4 : 8;
+  const int tt = t <= 16 ? 1 : tok_tiles(t > 128 ? 128 : t, (int)ct);
+  p->lds_bytes = fmt_lds(ppt, tt, bn, ts);
+  return p->lds_bytes <= (size_t)kLdsBytes;
 }
 
 hipError_t launch_fmt(const FmtArgs& a, hipStream_t stream) {

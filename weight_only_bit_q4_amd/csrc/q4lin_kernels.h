@@ -159,19 +159,6 @@ hipError_t launch_tiled(const TiledArgs& a, hipStream_t stream);
 hipError_t launch_swiglu_combine(const SumSource& g, const SumSource& u, void* y, int64_t n, int64_t t,
                                  hipStream_t stream);
 
-// Medium-T route: row blocks x K slices, about one workgroup per CU, the
-// slices' binary32 partials [S][T][N] in the workspace (none when S = 1).
-struct MidPlan {
-  int shape;       // 0: 128 x 32 tiles, 1: 96 x 64, 2: 96 x 128
-  int bn;          // rows per workgroup
-  int row_blocks;  // workgroups along the rows
-  int splits;      // K slices S
-  int gsp;         // scale-table row length (groups per slice, rounded up to even)
-  size_t lds_bytes;
-};
-bool mid_plan(int64_t n, int64_t k, int64_t t, MidPlan* p);
-size_t mid_workspace_bytes(int64_t n, int64_t k, int64_t t);
-hipError_t launch_mid(const GemvArgs& a, void* workspace, hipStream_t stream);
 
 // The other weight formats (few-token route, any T in runs of 32 tokens).
 // Format numbers as in the public header's Q4LIN_FMT_* values.
