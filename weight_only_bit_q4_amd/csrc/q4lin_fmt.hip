@@ -490,10 +490,15 @@ __device__ __forceinline__ void stage_store(uint16_t* dst, int elems, int i0, in
   }
 }
 
+// Row stride of the final sum's partials: BN rounded up to 4 mod 16 floats,
+// so the four token quads (4 lq rows apart) of a write land 16 banks apart
+__host__ __device__ constexpr int red_stride(int bn) { return (bn + 11) / 16 * 16 + 4; }
+
 // The sum over the eight waves' K runs in binary64: red[w][t < 16 TT][col <
-// BN] binary32 partials (lane (li, lq) of wave w holds row 16 ct + li,
-// tokens 16 tt + 4 lq + r), then one output per thread and step, rounded
-// once; an output that comes out non-finite is formed again exactly.
+// BN] binary32 partials, rows red_stride(BN) floats apart (lane (li, lq) of
+// wave w holds row 16 ct + li, tokens 16 tt + 4 lq + r), then one output per
+// thread and step, rounded once; an output that comes out non-finite is
+// formed again exactly.
 template <int F, int CT, int TT>
 __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t* lds, int wave, int li, int lq,
                                           int tid, const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo,
@@ -501,6 +506,7 @@ __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t*
                                           uint16_t* __restrict__ y, const uint16_t* __restrict__ res, int f32out,
                                           int N, int K, int T, int BN, int n0, int rows) {
   constexpr int BT = 16 * TT;
+  const int RS = red_stride(BN);
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
@@ -510,7 +516,7 @@ __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t*
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tt + 4 * lq + r;
-        if (col < BN && t < T) red[(wave * BT + t) * BN + col] = acc[ct][tt][r];
+        if (col < BN && t < T) red[(wave * BT + t) * RS + col] = acc[ct][tt][r];
       }
   }
   __syncthreads();
@@ -518,7 +524,7 @@ __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t*
     const int t = i / rows, col = i - t * rows;
     double v = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += (double)red[(w * BT + t) * BN + col];
+    for (int w = 0; w < kWaves; ++w) v += (double)red[(w * BT + t) * RS + col];
     const size_t o = (size_t)t * N + n0 + col;
     if (f32out) {
       reinterpret_cast<float*>(y)[o] = (float)v;  // binary32 sums (the gate and up of LinearSwiGLU)
@@ -558,7 +564,7 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   const int pb = (int)(((int64_t)pairs * wave) / kWaves), pe = (int)(((int64_t)pairs * (wave + 1)) / kWaves);
   const int ts = units * U::SB;  // bytes of one row's scales
   // LDS: the partials of the final sum, then the scale table
-  uint8_t* tab = lds + (size_t)kWaves * 16 * BN * 4;
+  uint8_t* tab = lds + (size_t)kWaves * 16 * red_stride(BN) * 4;
 
   const rsrc_t rlo = make_rsrc(lo + (size_t)n0 * units * U::CB, (uint32_t)(rows * units * U::CB));
   const rsrc_t rhi = make_rsrc(HB ? hi + (size_t)n0 * units * HB : lo, (uint32_t)(rows * units * HB));
@@ -853,7 +859,7 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
 // many-token kernel's rings and table (the partials reuse them)
 size_t fmt_lds(int ppt, int tt, int64_t bn, int64_t ts) {
   const int64_t table = (bn * ts + 15) / 16 * 16;
-  const int64_t red = (int64_t)kWaves * 16 * tt * bn * 4;
+  const int64_t red = (int64_t)kWaves * 16 * tt * red_stride((int)bn) * 4;
   if (tt == 1) return (size_t)(red + table);
   const int64_t slot = 16 * tt * ppt * 16;
   const int64_t ns = slot * 4 <= kRingWave ? 4 : slot * 2 <= kRingWave ? 2 : 1;
