@@ -318,6 +318,14 @@ __device__ __forceinline__ void lane_offsets(int rows, int units, int ts, int li
   }
 }
 
+// A lane exchange: every lane takes the 16 bytes lane src4 / 4 holds
+__device__ __forceinline__ u32x4_t lane_piece(u32x4_t v, int src4) {
+  return u32x4_t{(uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.x),
+                 (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.y),
+                 (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.z),
+                 (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.w)};
+}
+
 // The code loads of pair p: the pair's offset is the wave-uniform buffer
 // offset; a pair past the wave's run reads through the empty resource rnull
 // (nothing, zeros)
@@ -573,7 +581,13 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   uint32_t lo_off[CT], hi_off[CT];
   int tab_row[CT];
   lane_offsets<F, CT>(rows, units, ts, li, lq, lo_off, hi_off, tab_row);
-  const uint32_t x_off = (uint32_t)(min(li, T - 1) * K * 2 + xq * 16 * XH);
+  // Activations: lane (li, lq) multiplies pieces XH xq .. XH xq + XH - 1 of
+  // token li in each unit, but lane l loads those of token l / 4 and
+  // quarter l % 4, so that a quarter-wave reads four token rows (sixteen
+  // rows of 16 bytes each take the address unit about three times as
+  // long); a lane exchange then hands every lane its own pieces.
+  const uint32_t x_off = (uint32_t)(min(lane >> 2, T - 1) * K * 2 + (lane & 3) * 16 * XH);
+  const int xsrc4 = (4 * li + xq) * 4;  // the lane holding this lane's pieces (byte address)
 
   struct Loads {
     PairCodes<F, CT> c;
@@ -602,6 +616,11 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   // the products of pair p (its second unit is skipped past the row's end)
   auto pair_products = [&](int p, const Loads& L) __device__ {
     const bool second = 2 * p + 1 < units;
+    u32x4_t A[2][1][XH];
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int h = 0; h < XH; ++h) A[v][0][h] = lane_piece(L.a[v][0][h], xsrc4);
     if constexpr (F == FMT_BF16) {
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
@@ -609,14 +628,14 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
         u32x4_t cv[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) cv[ct] = L.c.c[ct][v];
-        bf16_unit<CT, 1>(L.a[v], cv, acc);
+        bf16_unit<CT, 1>(A[v], cv, acc);
       }
     } else {
       u32x2_t ca[CT], cb[CT];
       uint32_t ha[CT], hb[CT];
       split_pair<F, CT>(L.c, hsh, ca, cb, ha, hb);
-      unit_products<F, CT, 1, false>(2 * p, L.a[0], ca, ha, tab, tab_row, xq, acc);
-      if (second) unit_products<F, CT, 1, false>(2 * p + 1, L.a[1], cb, hb, tab, tab_row, xq, acc);
+      unit_products<F, CT, 1, false>(2 * p, A[0], ca, ha, tab, tab_row, xq, acc);
+      if (second) unit_products<F, CT, 1, false>(2 * p + 1, A[1], cb, hb, tab, tab_row, xq, acc);
     }
   };
 
