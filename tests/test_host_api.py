@@ -170,9 +170,11 @@ def test_linear_pair_shapes_and_workspace():
     assert q.q4lin_linear_pair(p, p, p, p, 8, p, p, p, 8, 96, 1, 0, 0, 0) == q.Q4LIN_E_SHAPE
     assert q.q4lin_linear_pair(p, p, p, p, -1, p, p, p, 8, 128, 1, 0, 0, 0) == q.Q4LIN_E_SHAPE
     assert q.q4lin_pair_workspace_bytes(8, 8, 96, 1) == -q.Q4LIN_E_SHAPE
-    # the fused one-to-32-token routes need none
+    # the fused one-to-128-token routes need none
     assert q.q4lin_pair_workspace_bytes(3072, 3072, 5120, 1) == 0
     assert q.q4lin_pair_workspace_bytes(1000, 700, 2048, 20) == 0
+    assert q.q4lin_pair_workspace_bytes(3072, 3072, 5120, 64) == 0
+    assert q.q4lin_pair_workspace_bytes(1000, 333, 2048, 128) == 0
     # many tokens: the activations once, then each weight's row exponents
     # (and partial sums under a K split)
     n1, n2, k, t = 768, 256, 1024, 200
@@ -197,7 +199,13 @@ def test_linear_swiglu_checks():
     assert q.q4lin_swiglu_workspace_bytes(6144, 5120, 1) == 0
     assert q.q4lin_swiglu_workspace_bytes(2048, 1024, 4) == 0
     assert q.q4lin_linear_swiglu(p, p, p, p, p, p + 1, 6144, 5120, 1, 0, 0, 0) == q.Q4LIN_E_ALIGN
-    for n, k, t in [(1000, 2048, 20), (768, 1024, 100), (128, 20480, 3)]:
+    # 5 to 128 tokens on the weight formats' kernel: one pass, no workspace
+    for n, k, t in [(1000, 2048, 20), (768, 1024, 100), (3072, 5120, 5), (3072, 5120, 128)]:
+        assert q.q4lin_swiglu_workspace_bytes(n, k, t) == 0
+    # its scale table of both weights' rows does not fit for K = 2^20 beyond
+    # 16 tokens: one medium-T launch per weight and the combine
+    assert q.q4lin_swiglu_workspace_bytes(16, 1 << 20, 40) == 2 * ((16 * 40 * 4 + 255) // 256 * 256)
+    for n, k, t in [(128, 20480, 3), (1024, 1024, 300), (16, 1 << 20, 40)]:
         need = q.q4lin_swiglu_workspace_bytes(n, k, t)
         assert need >= 2 * n * t * 4 and need % 256 == 0
         assert q.q4lin_linear_swiglu(p, p, p, p, p, p, n, k, t, p, need - 1, 0) == q.Q4LIN_E_WORKSPACE

@@ -1,7 +1,8 @@
 """LinearPair (two weights over one X, two outputs) on the GPU against the
 oracle, through the C ABI (q4lin_linear_pair): each output must match the
 oracle's product of its own weight, on the fused routes (one to four tokens,
-small T) and on the routes that run the weights one after the other; worked
+5 to 128 tokens, many tokens) and on the wide-K route that runs the weights
+one after the other; worked
 examples bit for bit, seeded problems within the tolerance, uneven row
 counts (ragged blocks in both planes) and the one-plane degenerate forms."""
 import numpy as np
@@ -65,14 +66,18 @@ def test_pair_worked_examples(replicate):
 
 
 # (n1, n2, k, t): gate/up-like equal halves, uneven halves with ragged blocks,
-# one to four tokens (single-launch single-token route), small T (single
-# launch, matrix cores), medium T (one launch sequence per weight), many
-# tokens (one activation preparation and one launch for both weights' tiles:
-# whole tiles, ragged tiles with a K split over three workgroups, tiny
-# weights) and a wide K (few-token vector route)
+# one to four tokens (single-launch single-token route), 5 to 128 tokens (one
+# launch of the weight formats' kernel, the second weight's rows as further
+# row blocks: few-token and many-token kernels, one and two token ranges,
+# one to four column tiles), many tokens (one activation preparation and one
+# launch for both weights' tiles: whole tiles, ragged tiles with a K split
+# over three workgroups, tiny weights) and a wide K (few-token vector route)
 @pytest.mark.parametrize("n1,n2,k,t", [(3072, 3072, 5120, 1), (1000, 333, 2048, 1), (2048, 2048, 1024, 4),
                                        (6144, 1024, 5120, 2), (1000, 700, 2048, 20), (517, 1531, 1280, 9),
                                        (768, 256, 1024, 100), (97, 160, 320, 40), (128, 256, 20480, 3),
+                                       (3072, 3072, 5120, 16), (3072, 3072, 5120, 64), (2000, 1500, 1024, 128),
+                                       (1000, 333, 2048, 77), (4096, 4096, 1024, 65), (700, 64, 1280, 5),
+                                       (64, 9000, 640, 33), (8000, 8000, 640, 48),
                                        (2560, 1000, 17408, 1), (3072, 3072, 1024, 300), (1000, 700, 2048, 200),
                                        (97, 33, 320, 1000)])
 def test_pair_matches_oracle(n1, n2, k, t):

@@ -1,8 +1,9 @@
 """LinearSwiGLU (Y = bf16(silu(Wg x X) * (Wu x X))) on the GPU against the
 oracle, through the C ABI (q4lin_linear_swiglu), on every way the two sums
-are made (both weights in one launch for one to four tokens and small T, one
-launch per weight on the wide-K few-token route, the many-token route with
-and without a K split): seeded problems within the tolerance, the closed
+are made (one pass with the gate applied in the final sum for one to four
+tokens and for 5 to 128, both weights' sums in one launch, one launch per
+weight on the wide-K routes, the many-token route with and without a K
+split): seeded problems within the tolerance, the closed
 forms (an all-eight gate gives zeros signed like U, an all-eight up weight
 zeros), the single-rounding worked example, and sampled outputs at the
 6144 x 5120 shape.  The tolerance is the plain op's, carried through the
@@ -58,9 +59,17 @@ def _pair(n, k, t, seed):
     return x, cg, sg, cu, su
 
 
+# 5 to 128 tokens run one launch of the weight formats' kernel, each
+# workgroup on the same rows of both weights: 16 or 32 rows of each (two or
+# four column tiles), few-token and many-token kernels, one and two token
+# ranges, ragged row blocks; K = 2^20 beyond 16 tokens takes one medium-T
+# launch per weight and the combine
 @pytest.mark.parametrize("n,k,t", [(3072, 5120, 1), (1000, 2048, 1), (2048, 1024, 4), (1000, 2048, 20),
                                    (517, 1280, 9), (128, 20480, 3), (768, 1024, 100), (1024, 1024, 300),
-                                   (97, 320, 40), (6144, 5120, 64), (6144, 256, 1024), (2560, 17408, 1)])
+                                   (97, 320, 40), (6144, 5120, 64), (6144, 256, 1024), (2560, 17408, 1),
+                                   (3072, 5120, 5), (3072, 5120, 16), (6000, 1024, 12), (6000, 1024, 17),
+                                   (3072, 1024, 100), (1000, 2048, 128), (333, 640, 65), (4100, 640, 33),
+                                   (16, 1 << 20, 40)])
 def test_swiglu_matches_oracle(n, k, t):
     x, cg, sg, cu, su = _pair(n, k, t, 101)
     got = run_swiglu(x, cg, sg, cu, su, n, k, t, what="seeded")

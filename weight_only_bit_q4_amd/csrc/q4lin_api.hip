@@ -132,6 +132,14 @@ bool pair_on_tiled(int route, int64_t n1, int64_t n2, int64_t k, int64_t t) {
   return route == Q4LIN_ROUTE_TILED && q4lin::tiled_shape_ok(n1, k, t) && q4lin::tiled_shape_ok(n2, k, t);
 }
 
+// ... and one launch of the weight formats' kernel where the route for their
+// rows runs a single weight there (the small-T route from kSmallFmtFirstT
+// tokens, the medium-T route): the second weight's rows are further row
+// blocks of the same launch.
+bool pair_on_fmt(int route, int64_t n1, int64_t n2, int64_t k, int64_t t) {
+  return (route == Q4LIN_ROUTE_SKINNY && small_uses_fmt(n1 + n2, k, t)) || route == Q4LIN_ROUTE_MID;
+}
+
 // The op, with an optional residual (LinearAdd when res is not null).
 int run_linear(const void* x, const void* codes, const void* scales, const void* res, void* y,
                int64_t n, int64_t k, int64_t t, void* workspace, size_t workspace_bytes, void* stream) {
@@ -170,8 +178,12 @@ size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 //   SPLIT: one launch per weight on the route chosen for N rows;
 //   TILED: the many-token route per weight, its raw sums left in the
 //          partials of a workspace half each.
-//   MID:   the medium-T route per weight, binary32 sums in each half.
-enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3, SW_MID = 4, SW_GLU = 5 };
+//   MID:   the medium-T route per weight, binary32 sums in each half;
+//   GLU:   the single-token route, each workgroup on the same rows of both
+//          weights, the gate applied in its final sum (no workspace);
+//   FMT:   the same on the weight formats' kernel, kSmallFmtFirstT to
+//          kMidLastT tokens (no workspace).
+enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3, SW_MID = 4, SW_GLU = 5, SW_FMT = 6 };
 struct SwigluPlan {
   int mode;
   int route;
@@ -184,6 +196,12 @@ bool swiglu_plan(int64_t n, int64_t k, int64_t t, SwigluPlan* p) {
   const int r2 = pick_route(2 * n, k, t);
   if (r2 == Q4LIN_ROUTE_DECODE && q4lin::decode_glu_ok(n, k, t)) {
     *p = SwigluPlan{SW_GLU, r2, 0, 0};
+    return true;
+  }
+  q4lin::FmtPlan fp;
+  if (t >= kSmallFmtFirstT && t <= kMidLastT && (r2 == Q4LIN_ROUTE_SKINNY || r2 == Q4LIN_ROUTE_MID) &&
+      q4lin::fmt_plan(q4lin::FMT_Q4, n, k, t, &fp, true)) {
+    *p = SwigluPlan{SW_FMT, r2, 0, 0};
     return true;
   }
   if (r2 == Q4LIN_ROUTE_DECODE || r2 == Q4LIN_ROUTE_SKINNY) {
@@ -339,6 +357,15 @@ int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scale
     e = q4lin::launch_decode(a, s);
     return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
   }
+  if (p.mode == SW_FMT) {
+    q4lin::FmtArgs a{q4lin::FMT_Q4, x, codes_gate, nullptr, scales_gate, y, n, k, t};
+    a.lo2 = codes_up;
+    a.sc2 = scales_up;
+    a.n2 = n;
+    a.glu = true;
+    e = q4lin::launch_fmt(a, s);
+    return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+  }
   if (p.mode == SW_FUSED) {
     q4lin::GemvArgs a{x, codes_gate, scales_gate, w0, n, k, t};
     a.codes2 = codes_up;
@@ -423,8 +450,21 @@ int q4lin_linear_pair(const void* x, const void* codes1, const void* scales1, vo
     const hipError_t e = q4lin::launch_tiled_pair(pa, nullptr, nullptr, s);
     return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
   }
+  if (pair_on_fmt(route, n1, n2, k, t)) {
+    if (!x || !codes1 || !scales1 || !y1 || !codes2 || !scales2 || !y2) return Q4LIN_E_NULL;
+    if (!aligned(x, 16) || !aligned(codes1, 16) || !aligned(scales1, 2) || !aligned(y1, 2) ||
+        !aligned(codes2, 16) || !aligned(scales2, 2) || !aligned(y2, 2))
+      return Q4LIN_E_ALIGN;
+    q4lin::FmtArgs a{q4lin::FMT_Q4, x, codes1, nullptr, scales1, y1, n1, k, t};
+    a.lo2 = codes2;
+    a.sc2 = scales2;
+    a.y2 = y2;
+    a.n2 = n2;
+    const hipError_t e = q4lin::launch_fmt(a, s);
+    return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+  }
   if (route != Q4LIN_ROUTE_DECODE && route != Q4LIN_ROUTE_SKINNY) {
-    // the medium-T and wide-K routes: one launch sequence per weight
+    // the wide-K routes: one launch sequence per weight
     const int s1 = run_linear(x, codes1, scales1, nullptr, y1, n1, k, t, workspace, workspace_bytes, stream);
     if (s1 != Q4LIN_OK) return s1;
     return run_linear(x, codes2, scales2, nullptr, y2, n2, k, t, workspace, workspace_bytes, stream);
@@ -445,7 +485,8 @@ int q4lin_linear_pair(const void* x, const void* codes1, const void* scales1, vo
 int64_t q4lin_pair_workspace_bytes(int64_t n1, int64_t n2, int64_t k, int64_t t) {
   if (!shape_ok(n1, k, t) || !shape_ok(n2, k, t) || !shape_ok(n1 + n2, k, t)) return -Q4LIN_E_SHAPE;
   const int route = pick_route(n1 + n2, k, t);
-  if (n1 > 0 && n2 > 0 && (route == Q4LIN_ROUTE_DECODE || route == Q4LIN_ROUTE_SKINNY)) return 0;
+  if (n1 > 0 && n2 > 0 && (route == Q4LIN_ROUTE_DECODE || route == Q4LIN_ROUTE_SKINNY || route == Q4LIN_ROUTE_MID))
+    return 0;
   if (n1 > 0 && n2 > 0 && t > 0 && pair_on_tiled(route, n1, n2, k, t))
     return (int64_t)q4lin::tiled_pair_workspace_bytes(n1, n2, k, t, false);
   const size_t w1 = route_workspace(pick_route(n1, k, t), n1, k, t);

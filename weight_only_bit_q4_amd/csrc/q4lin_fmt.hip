@@ -302,19 +302,23 @@ struct PairCodes {
 // block repeat the last one; their sums are never stored), relative to
 // buffers over the block's rows of each plane, and the lane's row in the
 // scale table.  Paired formats: quarter lq reads half lq % 2 of the pair's
-// unit lq / 2; BF16_CTRL: quarter lq of each unit.
-template <int F, int CT>
+// unit lq / 2; BF16_CTRL: quarter lq of each unit.  GLU: the first CT / 2
+// tiles are the gate weight's rows, the others the same rows of the up
+// weight, whose scales follow the gate's in the table.
+template <int F, int CT, bool GLU = false>
 __device__ __forceinline__ void lane_offsets(int rows, int units, int ts, int li, int lq, uint32_t (&lo_off)[CT],
                                              uint32_t (&hi_off)[CT], int (&tab_row)[CT]) {
   constexpr int HB = Fmt<F>::HB;
+  constexpr int CTH = GLU ? CT / 2 : CT;  // column tiles per weight
   const int row_bytes = units * Unit<F>::CB;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    const int rl = min(16 * ct + li, rows - 1);
+    const int pl = ct / CTH;
+    const int rl = min(16 * (ct - pl * CTH) + li, rows - 1);
     if constexpr (F == FMT_BF16) lo_off[ct] = (uint32_t)(rl * row_bytes + lq * 16);
     else lo_off[ct] = (uint32_t)(rl * row_bytes + (lq >> 1) * Unit<F>::CB + (lq & 1) * 16);
     hi_off[ct] = (uint32_t)(rl * units * HB + (lq >> 1) * HB + (lq & 1) * (HB / 2));
-    tab_row[ct] = rl * ts;
+    tab_row[ct] = (pl * rows + rl) * ts;
   }
 }
 
@@ -328,14 +332,17 @@ __device__ __forceinline__ u32x4_t lane_piece(u32x4_t v, int src4) {
 
 // The code loads of pair p: the pair's offset is the wave-uniform buffer
 // offset; a pair past the wave's run reads through the empty resource rnull
-// (nothing, zeros)
-template <int F, int CT>
-__device__ __forceinline__ void load_codes(rsrc_t rlo, rsrc_t rhi, rsrc_t rnull, const uint32_t (&lo_off)[CT],
-                                           const uint32_t (&hi_off)[CT], int p, bool live, PairCodes<F, CT>& L) {
+// (nothing, zeros).  GLU: the last CT / 2 tiles read the up weight (rlo2).
+template <int F, int CT, bool GLU = false>
+__device__ __forceinline__ void load_codes(rsrc_t rlo, rsrc_t rlo2, rsrc_t rhi, rsrc_t rnull,
+                                           const uint32_t (&lo_off)[CT], const uint32_t (&hi_off)[CT], int p,
+                                           bool live, PairCodes<F, CT>& L) {
+  static_assert(!GLU || Fmt<F>::HB == 0, "the gated pair has no high planes");
   constexpr int CB = Unit<F>::CB, HB = Fmt<F>::HB;
-  const rsrc_t rl = live ? rlo : rnull, rh = live ? rhi : rnull;
+  const rsrc_t ra = live ? rlo : rnull, rb = live ? rlo2 : rnull, rh = live ? rhi : rnull;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
+    const rsrc_t rl = (GLU && ct >= CT / 2) ? rb : ra;
 #pragma unroll
     for (int v = 0; v < Fmt<F>::NC; ++v)
       L.c[ct][v] = __builtin_amdgcn_raw_buffer_load_b128(rl, lo_off[ct], (uint32_t)((2 * p + v) * CB), 2);
@@ -506,25 +513,27 @@ __host__ __device__ constexpr int red_stride(int bn) { return (bn + 11) / 16 * 1
 // BN] binary32 partials, rows red_stride(BN) floats apart (lane (li, lq) of
 // wave w holds row 16 ct + li, tokens 16 tt + 4 lq + r), then one output per
 // thread and step, rounded once; an output that comes out non-finite is
-// formed again exactly.
-template <int F, int CT, int TT>
+// formed again exactly.  GLU: columns BN .. 2 BN - 1 hold the up weight's
+// rows, and the output is bf16(silu(G) U) of the two sums.
+template <int F, int CT, int TT, bool GLU = false>
 __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t* lds, int wave, int li, int lq,
                                           int tid, const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo,
                                           const uint8_t* __restrict__ hi, const uint8_t* __restrict__ sc,
                                           uint16_t* __restrict__ y, const uint16_t* __restrict__ res, int f32out,
                                           int N, int K, int T, int BN, int n0, int rows) {
   constexpr int BT = 16 * TT;
-  const int RS = red_stride(BN);
+  constexpr int CTH = GLU ? CT / 2 : CT;
+  const int RS = red_stride(GLU ? 2 * BN : BN);
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    const int col = 16 * ct + li;
+    const int pl = ct / CTH, c = 16 * (ct - pl * CTH) + li, col = pl * BN + c;
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tt + 4 * lq + r;
-        if (col < BN && t < T) red[(wave * BT + t) * RS + col] = acc[ct][tt][r];
+        if (c < BN && t < T) red[(wave * BT + t) * RS + col] = acc[ct][tt][r];
       }
   }
   __syncthreads();
@@ -534,6 +543,18 @@ __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t*
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) v += (double)red[(w * BT + t) * RS + col];
     const size_t o = (size_t)t * N + n0 + col;
+    if constexpr (GLU) {
+      double u = 0.0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) u += (double)red[(w * BT + t) * RS + BN + col];
+      // each sum rounded to binary32 as where the two sums are stored
+      // between passes (+0 maps a -0 sum to +0, as a sum of zero products
+      // starts at +0), the gate in binary64, one rounding of the product
+      const double g = (double)(float)v + 0.0, uv = (double)(float)u + 0.0;
+      const double silu = g / (1.0 + exp(-g));
+      y[o] = f32_to_bf16_rne((float)(silu * uv));
+      continue;
+    }
     if (f32out) {
       reinterpret_cast<float*>(y)[o] = (float)v;  // binary32 sums (the gate and up of LinearSwiGLU)
       continue;
@@ -545,16 +566,29 @@ __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t*
   }
 }
 
+// A launch's second weight.  LinearPair (the kernels' GLU false, n > 0):
+// workgroups from row block `first` on take its rows and write y (no
+// residual).  LinearSwiGLU (GLU true): every workgroup takes the same rows
+// of the gate (the first weight) and of this up weight.
+struct Plane2 {
+  const uint8_t* lo;
+  const uint8_t* hi;
+  const uint8_t* sc;
+  uint16_t* y;
+  int n;
+  int first;
+};
+
 // ---------------------------------------------------------------------------
 // Up to 16 tokens: the eight waves split the block's pairs of units; each
 // pair's codes and activations go straight to registers, two register sets
 // taking turns (the next pair's loads in flight during a pair's products).
 // ---------------------------------------------------------------------------
-template <int F, int CT>
+template <int F, int CT, bool GLU>
 __global__ void __launch_bounds__(kThreads, 1)
 fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const uint8_t* __restrict__ hi,
            const uint8_t* __restrict__ sc, uint16_t* __restrict__ y, const uint16_t* __restrict__ res, int f32out,
-           int N, int K, int T, int BN) {
+           int N, int K, int T, int BN, Plane2 p2) {
   using U = Unit<F>;
   constexpr int XH = Fmt<F>::XH, HB = Fmt<F>::HB;
   constexpr int NB = 2;  // pairs in flight (register sets)
@@ -565,22 +599,33 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   // the quarter of each unit this lane multiplies: after the exchange of
   // the paired loads, quarter lq holds code bytes 8 xq .. 8 xq + 7 of a unit
   const int xq = Fmt<F>::PAIRED ? (((lq & 1) << 1) | (lq >> 1)) : lq;
-  const int n0 = blockIdx.x * BN;
+  int bid = blockIdx.x;
+  if (!GLU && p2.n > 0 && bid >= p2.first) {  // LinearPair: the second weight's row blocks
+    lo = p2.lo;
+    hi = p2.hi;
+    sc = p2.sc;
+    y = p2.y;
+    N = p2.n;
+    res = nullptr;
+    bid -= p2.first;
+  }
+  const int n0 = bid * BN;
   const int rows = min(BN, N - n0);
   const int units = K / U::K;
   const int pairs = (units + 1) >> 1;
   const int pb = (int)(((int64_t)pairs * wave) / kWaves), pe = (int)(((int64_t)pairs * (wave + 1)) / kWaves);
   const int ts = units * U::SB;  // bytes of one row's scales
   // LDS: the partials of the final sum, then the scale table
-  uint8_t* tab = lds + (size_t)kWaves * 16 * red_stride(BN) * 4;
+  uint8_t* tab = lds + (size_t)kWaves * 16 * red_stride(GLU ? 2 * BN : BN) * 4;
 
   const rsrc_t rlo = make_rsrc(lo + (size_t)n0 * units * U::CB, (uint32_t)(rows * units * U::CB));
+  const rsrc_t rlo2 = GLU ? make_rsrc(p2.lo + (size_t)n0 * units * U::CB, (uint32_t)(rows * units * U::CB)) : rlo;
   const rsrc_t rhi = make_rsrc(HB ? hi + (size_t)n0 * units * HB : lo, (uint32_t)(rows * units * HB));
   const rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)T * K * 2));
   const rsrc_t rnull = make_rsrc(x, 0u);  // every access out of range
   uint32_t lo_off[CT], hi_off[CT];
   int tab_row[CT];
-  lane_offsets<F, CT>(rows, units, ts, li, lq, lo_off, hi_off, tab_row);
+  lane_offsets<F, CT, GLU>(rows, units, ts, li, lq, lo_off, hi_off, tab_row);
   // Activations: lane (li, lq) multiplies pieces XH xq .. XH xq + XH - 1 of
   // token li in each unit, but lane l loads those of token l / 4 and
   // quarter l % 4, so that a quarter-wave reads four token rows (sixteen
@@ -595,7 +640,7 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   };
   auto load = [&](int p, Loads& L) __device__ {
     const bool live = p < pe;
-    load_codes<F, CT>(rlo, rhi, rnull, lo_off, hi_off, p, live, L.c);
+    load_codes<F, CT, GLU>(rlo, rlo2, rhi, rnull, lo_off, hi_off, p, live, L.c);
     const rsrc_t r = live ? rx : rnull;
 #pragma unroll
     for (int v = 0; v < 2; ++v)
@@ -606,6 +651,7 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
 
   const int elems = rows * ts / 2;
   const rsrc_t rsc = make_rsrc(U::SB ? sc + (size_t)n0 * ts : lo, (uint32_t)(rows * ts));
+  const rsrc_t rsc2 = GLU ? make_rsrc(p2.sc + (size_t)n0 * ts, (uint32_t)(rows * ts)) : rsc;
   uint16_t* sdst = reinterpret_cast<uint16_t*>(tab);
   const int hsh = (lane >> 5) << 4;  // Q5: the half of a high dword that belongs to this lane
 
@@ -642,19 +688,27 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   // Scales of the block (first batch) in flight with the first two pairs'
   // loads.  (A table larger than one batch is copied first, on its own.)
   Loads b[NB];
-  uint16_t sv[8];
+  uint16_t sv[8], sv2[8];
   if constexpr (U::SB > 0) {
     if (elems > 8 * kThreads) {
       for (int i0 = 0; i0 < elems; i0 += 8 * kThreads) {
         stage_load(rsc, elems, i0, tid, sv);
         stage_store(sdst, elems, i0, tid, sv);
+        if constexpr (GLU) {
+          stage_load(rsc2, elems, i0, tid, sv2);
+          stage_store(sdst + elems, elems, i0, tid, sv2);
+        }
       }
     }
     stage_load(rsc, elems, 0, tid, sv);  // a repeat of the first batch when already copied
+    if constexpr (GLU) stage_load(rsc2, elems, 0, tid, sv2);
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) load(pb + i, b[i]);
-  if constexpr (U::SB > 0) stage_store(sdst, elems, 0, tid, sv);
+  if constexpr (U::SB > 0) {
+    stage_store(sdst, elems, 0, tid, sv);
+    if constexpr (GLU) stage_store(sdst + elems, elems, 0, tid, sv2);
+  }
   // the table's writes are visible after this; the loads stay in flight
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
@@ -668,7 +722,7 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
     }
   }
   // (the partials area lies before the scale table: no wait for its readers)
-  final_sum<F, CT, 1>(acc, lds, wave, li, lq, tid, x, lo, hi, sc, y, res, f32out, N, K, T, BN, n0, rows);
+  final_sum<F, CT, 1, GLU>(acc, lds, wave, li, lq, tid, x, lo, hi, sc, y, res, f32out, N, K, T, BN, n0, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -697,11 +751,11 @@ constexpr int tok_pairs() {
   return (F == FMT_Q5 || F == FMT_Q6) ? (CT <= 2 ? 4 : 2) : (CT <= 2 ? 6 : 4);
 }
 
-template <int F, int CT, int TT>
+template <int F, int CT, int TT, bool GLU>
 __global__ void __launch_bounds__(kThreads, 1)
 fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const uint8_t* __restrict__ hi,
                const uint8_t* __restrict__ sc, uint16_t* __restrict__ y, const uint16_t* __restrict__ res,
-               int f32out, int N, int K, int T, int BN, int TS) {
+               int f32out, int N, int K, int T, int BN, int TS, Plane2 p2) {
   using U = Unit<F>;
   using S = TokShape<F, TT>;
   constexpr int XH = Fmt<F>::XH, HB = Fmt<F>::HB;
@@ -726,6 +780,15 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
     tr = g % TS;
     rb = (g / TS) * 8 + (blockIdx.x & 7);
   }
+  if (!GLU && p2.n > 0 && rb >= p2.first) {  // LinearPair: the second weight's row blocks
+    lo = p2.lo;
+    hi = p2.hi;
+    sc = p2.sc;
+    y = p2.y;
+    N = p2.n;
+    res = nullptr;
+    rb -= p2.first;
+  }
   const int n0 = rb * BN, t0 = tr * 16 * TT;
   if (n0 >= N || t0 >= T) return;  // (the grid's last row of eight)
   x += (size_t)t0 * K;
@@ -744,12 +807,13 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
   uint8_t* tab = lds + S::RING;
 
   const rsrc_t rlo = make_rsrc(lo + (size_t)n0 * units * U::CB, (uint32_t)(rows * units * U::CB));
+  const rsrc_t rlo2 = GLU ? make_rsrc(p2.lo + (size_t)n0 * units * U::CB, (uint32_t)(rows * units * U::CB)) : rlo;
   const rsrc_t rhi = make_rsrc(HB ? hi + (size_t)n0 * units * HB : lo, (uint32_t)(rows * units * HB));
   const rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)T * K * 2));
   const rsrc_t rnull = make_rsrc(x, 0u);  // every access out of range
   uint32_t lo_off[CT], hi_off[CT];
   int tab_row[CT];
-  lane_offsets<F, CT>(rows, units, ts, li, lq, lo_off, hi_off, tab_row);
+  lane_offsets<F, CT, GLU>(rows, units, ts, li, lq, lo_off, hi_off, tab_row);
 
   // A slot holds one unit's activations, piece (tl, pc) of token tl at
   // position tl PPT + (pc ^ swz(tl)), swz(tl) = (tl / (16 / PPT)) % PPT: the
@@ -791,6 +855,7 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
 
   const int elems = rows * ts / 2;
   const rsrc_t rsc = make_rsrc(U::SB ? sc + (size_t)n0 * ts : lo, (uint32_t)(rows * ts));
+  const rsrc_t rsc2 = GLU ? make_rsrc(p2.sc + (size_t)n0 * ts, (uint32_t)(rows * ts)) : rsc;
   uint16_t* sdst = reinterpret_cast<uint16_t*>(tab);
   const int hsh = (lane >> 5) << 4;
 
@@ -803,23 +868,32 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
   // Prologue: the scales' first batch, the first NS units' activations, then
   // the first chunk's codes.
   PairCodes<F, CT> cc[MP];
-  uint16_t sv[8];
+  uint16_t sv[8], sv2[8];
   if constexpr (U::SB > 0) {
     if (elems > 8 * kThreads) {
       for (int i0 = 0; i0 < elems; i0 += 8 * kThreads) {
         stage_load(rsc, elems, i0, tid, sv);
         stage_store(sdst, elems, i0, tid, sv);
+        if constexpr (GLU) {
+          stage_load(rsc2, elems, i0, tid, sv2);
+          stage_store(sdst + elems, elems, i0, tid, sv2);
+        }
       }
     }
     stage_load(rsc, elems, 0, tid, sv);
+    if constexpr (GLU) stage_load(rsc2, elems, 0, tid, sv2);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < NS; ++s) issue_x(2 * pb + s, s);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < MP; ++i) load_codes<F, CT>(rlo, rhi, rnull, lo_off, hi_off, pb + i, pb + i < pe, cc[i]);
-  if constexpr (U::SB > 0) stage_store(sdst, elems, 0, tid, sv);
+  for (int i = 0; i < MP; ++i)
+    load_codes<F, CT, GLU>(rlo, rlo2, rhi, rnull, lo_off, hi_off, pb + i, pb + i < pe, cc[i]);
+  if constexpr (U::SB > 0) {
+    stage_store(sdst, elems, 0, tid, sv);
+    if constexpr (GLU) stage_store(sdst + elems, elems, 0, tid, sv2);
+  }
   // the table's writes are visible after this; the loads stay in flight
   // (a fence here would also wait for the copies into the rings)
   wait_lgkm0();
@@ -866,19 +940,20 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < MP; ++i)
-      load_codes<F, CT>(rlo, rhi, rnull, lo_off, hi_off, p0 + MP + i, p0 + MP + i < pe, cc[i]);
+      load_codes<F, CT, GLU>(rlo, rlo2, rhi, rnull, lo_off, hi_off, p0 + MP + i, p0 + MP + i < pe, cc[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vm<0>();  // every copy into the rings has landed before the space is reused
   __syncthreads();
-  final_sum<F, CT, TT>(acc, lds, wave, li, lq, tid, x, lo, hi, sc, y, res, f32out, N, K, T, BN, n0, rows);
+  final_sum<F, CT, TT, GLU>(acc, lds, wave, li, lq, tid, x, lo, hi, sc, y, res, f32out, N, K, T, BN, n0, rows);
 }
 
 // LDS of a launch: the few-token kernel's partials and scale table, or the
-// many-token kernel's rings and table (the partials reuse them)
-size_t fmt_lds(int ppt, int tt, int64_t bn, int64_t ts) {
-  const int64_t table = (bn * ts + 15) / 16 * 16;
-  const int64_t red = (int64_t)kWaves * 16 * tt * red_stride((int)bn) * 4;
+// many-token kernel's rings and table (the partials reuse them).  w: the
+// weights whose rows a workgroup takes (2 for the gated pair).
+size_t fmt_lds(int ppt, int tt, int64_t bn, int64_t ts, int w) {
+  const int64_t table = (w * bn * ts + 15) / 16 * 16;
+  const int64_t red = (int64_t)kWaves * 16 * tt * red_stride((int)(w * bn)) * 4;
   if (tt == 1) return (size_t)(red + table);
   const int64_t slot = 16 * tt * ppt * 16;
   const int64_t ns = slot * 4 <= kRingWave ? 4 : slot * 2 <= kRingWave ? 2 : 1;
@@ -897,76 +972,123 @@ int tok_tiles(int64_t t, int ct) {
   return cap;
 }
 
+// Column tiles of a workgroup of bn rows (per weight for the gated pair)
+int fmt_col_tiles(int64_t bn, bool glu) { return (int)((glu ? 2 : 1) * ((bn + 15) / 16)); }
+
 // One launch's shape on 17 or more tokens: row blocks of bn rows (ct column
 // tiles), ts token ranges of 16 tt tokens each.  Above 64 tokens (when the
 // rows allow) a row block twice as tall serves half the tokens: every
 // workgroup still does the same work, but the activation bytes it copies
 // (its tokens' whole rows) halve (6144 x 5120: T = 65..128 24.4-30.2 us
 // against 24.8-32.9); below that the taller block's extra code loads cost
-// more than the copies saved (T = 33..64 21-22 against 17-20.5 us).
+// more than the copies saved (T = 33..64 21-22 against 17-20.5 us).  The
+// rows of both weights count: a pair's second weight adds row blocks from
+// `first` on; the gated pair's workgroups take bn rows of each.
 struct TokLaunch {
   int64_t bn;
   int ct, ts, tt;
+  int64_t first;  // row blocks of the first weight
   int64_t grid;
 };
-TokLaunch tok_launch(int64_t n, int64_t t, int64_t bn1, int64_t ts_bytes, int64_t table_cap) {
+TokLaunch tok_launch(const FmtArgs& a, int64_t t, int64_t bn1, int64_t ts_bytes, int64_t table_cap) {
+  const int64_t rows = a.glu ? 2 * a.n : a.n + a.n2;
   TokLaunch L;
   L.ts = 1;
   L.bn = bn1;
-  if (t > 64 && (n + 255) / 256 <= 32) {
-    const int64_t bn2 = (2 * n + 255) / 256;
-    if (ts_bytes == 0 || bn2 * ts_bytes <= table_cap) {
+  if (t > 64 && (rows + 255) / 256 <= 32) {
+    const int64_t bn2 = a.glu ? (a.n + 127) / 128 : (2 * rows + 255) / 256;
+    if ((a.glu ? 2 : 1) * bn2 * ts_bytes <= table_cap) {
       L.ts = 2;
       L.bn = bn2;
     }
   }
-  L.ct = (int)((L.bn + 15) / 16);
+  L.ct = fmt_col_tiles(L.bn, a.glu);
   L.tt = tok_tiles((t + L.ts - 1) / L.ts, L.ct);
-  const int64_t nrb = (n + L.bn - 1) / L.bn;
+  L.first = (a.n + L.bn - 1) / L.bn;
+  const int64_t nrb = a.glu ? L.first : L.first + (a.n2 + L.bn - 1) / L.bn;
   L.grid = L.ts == 1 ? nrb : (nrb + 7) / 8 * 8 * L.ts;
   return L;
 }
 
-template <int F, int CT, int TT>
-hipError_t launch_tok(const FmtArgs& a, const TokLaunch& L, const uint16_t* x, uint16_t* y, const uint16_t* res,
-                      int t, hipStream_t s) {
-  auto kern = fmt_tok_kernel<F, CT, TT>;
+// One launch's pointers: the token range's activations, outputs, residual
+// and second weight
+struct Chunk {
+  const uint16_t* x;
+  uint16_t* y;
+  const uint16_t* res;
+  Plane2 p2;
+  int t;
+};
+
+template <int F, int CT, int TT, bool GLU>
+hipError_t launch_tok(const FmtArgs& a, const TokLaunch& L, const Chunk& c, hipStream_t s) {
+  auto kern = fmt_tok_kernel<F, CT, TT, GLU>;
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
-  const size_t lds = fmt_lds(TokShape<F, TT>::PPT, TT, L.bn, (a.k / Unit<F>::K) * Unit<F>::SB);
+  const size_t lds = fmt_lds(TokShape<F, TT>::PPT, TT, L.bn, (a.k / Unit<F>::K) * Unit<F>::SB, GLU ? 2 : 1);
+  Plane2 p2 = c.p2;
+  p2.first = (int)L.first;
   kern<<<dim3((unsigned)L.grid), dim3(kThreads), lds, s>>>(
-      x, static_cast<const uint8_t*>(a.lo), static_cast<const uint8_t*>(a.hi), static_cast<const uint8_t*>(a.sc), y,
-      res, a.f32 ? 1 : 0, (int)a.n, (int)a.k, t, (int)L.bn, L.ts);
+      c.x, static_cast<const uint8_t*>(a.lo), static_cast<const uint8_t*>(a.hi), static_cast<const uint8_t*>(a.sc),
+      c.y, c.res, a.f32 ? 1 : 0, (int)a.n, (int)a.k, c.t, (int)L.bn, L.ts, p2);
   return hipGetLastError();
 }
 
-template <int F, int CT>
-hipError_t launch_tok_ct(const FmtArgs& a, const TokLaunch& L, const uint16_t* x, uint16_t* y, const uint16_t* res,
-                         int t, hipStream_t s) {
+template <int F, int CT, bool GLU>
+hipError_t launch_tok_ct(const FmtArgs& a, const TokLaunch& L, const Chunk& c, hipStream_t s) {
   switch (L.tt) {
-    case 2: return launch_tok<F, CT, 2>(a, L, x, y, res, t, s);
-    case 3: return launch_tok<F, CT, 3>(a, L, x, y, res, t, s);
-    case 4: return launch_tok<F, CT, 4>(a, L, x, y, res, t, s);
+    case 2: return launch_tok<F, CT, 2, GLU>(a, L, c, s);
+    case 3: return launch_tok<F, CT, 3, GLU>(a, L, c, s);
+    case 4: return launch_tok<F, CT, 4, GLU>(a, L, c, s);
     default:
       if constexpr (CT <= 2) {
-        if (L.tt == 6) return launch_tok<F, CT, 6>(a, L, x, y, res, t, s);
-        return launch_tok<F, CT, 8>(a, L, x, y, res, t, s);
+        if (L.tt == 6) return launch_tok<F, CT, 6, GLU>(a, L, c, s);
+        return launch_tok<F, CT, 8, GLU>(a, L, c, s);
       }
       return hipErrorInvalidValue;
   }
 }
 
-template <int F, int CT>
-hipError_t launch_few(const FmtArgs& a, const FmtPlan& p, const uint16_t* x, uint16_t* y, const uint16_t* res, int t,
-                      hipStream_t s) {
-  auto kern = fmt_kernel<F, CT>;
+template <int F, int CT, bool GLU>
+hipError_t launch_few(const FmtArgs& a, const FmtPlan& p, const Chunk& c, hipStream_t s) {
+  auto kern = fmt_kernel<F, CT, GLU>;
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(kern));
   if (e != hipSuccess) return e;
-  const size_t lds = fmt_lds(0, 1, p.bn, (a.k / Unit<F>::K) * Unit<F>::SB);
+  const size_t lds = fmt_lds(0, 1, p.bn, (a.k / Unit<F>::K) * Unit<F>::SB, GLU ? 2 : 1);
+  Plane2 p2 = c.p2;
+  p2.first = (int)((a.n + p.bn - 1) / p.bn);
   kern<<<dim3((unsigned)p.blocks), dim3(kThreads), lds, s>>>(
-      x, static_cast<const uint8_t*>(a.lo), static_cast<const uint8_t*>(a.hi), static_cast<const uint8_t*>(a.sc), y,
-      res, a.f32 ? 1 : 0, (int)a.n, (int)a.k, t, p.bn);
+      c.x, static_cast<const uint8_t*>(a.lo), static_cast<const uint8_t*>(a.hi), static_cast<const uint8_t*>(a.sc),
+      c.y, c.res, a.f32 ? 1 : 0, (int)a.n, (int)a.k, c.t, p.bn, p2);
   return hipGetLastError();
+}
+
+template <int F, bool GLU>
+hipError_t launch_chunk(const FmtArgs& a, const FmtPlan& p, const Chunk& c, int64_t tsb, int64_t table_cap,
+                        hipStream_t s) {
+  if (c.t <= 16) {
+    if constexpr (GLU) {  // 2 or 4 column tiles: 16 or 32 rows of each weight
+      return p.ct == 2 ? launch_few<F, 2, true>(a, p, c, s) : launch_few<F, 4, true>(a, p, c, s);
+    } else {
+      switch (p.ct) {
+        case 1: return launch_few<F, 1, false>(a, p, c, s);
+        case 2: return launch_few<F, 2, false>(a, p, c, s);
+        case 3: return launch_few<F, 3, false>(a, p, c, s);
+        default: return launch_few<F, 4, false>(a, p, c, s);
+      }
+    }
+  }
+  const TokLaunch L = tok_launch(a, c.t, p.bn, tsb, table_cap);
+  if constexpr (GLU) {
+    return L.ct == 2 ? launch_tok_ct<F, 2, true>(a, L, c, s) : launch_tok_ct<F, 4, true>(a, L, c, s);
+  } else {
+    switch (L.ct) {
+      case 1: return launch_tok_ct<F, 1, false>(a, L, c, s);
+      case 2: return launch_tok_ct<F, 2, false>(a, L, c, s);
+      case 3: return launch_tok_ct<F, 3, false>(a, L, c, s);
+      default: return launch_tok_ct<F, 4, false>(a, L, c, s);
+    }
+  }
 }
 
 template <int F>
@@ -978,30 +1100,23 @@ hipError_t launch_fmt_t(const FmtArgs& a, const FmtPlan& p, hipStream_t s) {
   const int64_t table_cap = kLdsBytes - (int64_t)kWaves * kRingWave;
   int64_t per = 128;
   if (a.t > 16) {
-    const TokLaunch L = tok_launch(a.n, a.t > 128 ? 128 : a.t, p.bn, tsb, table_cap);
+    const TokLaunch L = tok_launch(a, a.t > 128 ? 128 : a.t, p.bn, tsb, table_cap);
     per = (int64_t)L.ts * 16 * (L.ct <= 2 ? 8 : 4);
   }
   for (int64_t t0 = 0; t0 < a.t; t0 += per) {
-    const int t = (int)(a.t - t0 < per ? a.t - t0 : per);
-    const uint16_t* x = static_cast<const uint16_t*>(a.x) + t0 * a.k;
-    uint16_t* y = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.y) + (size_t)t0 * a.n * osz);
-    const uint16_t* res = a.res ? static_cast<const uint16_t*>(a.res) + t0 * a.n : nullptr;
+    Chunk c;
+    c.t = (int)(a.t - t0 < per ? a.t - t0 : per);
+    c.x = static_cast<const uint16_t*>(a.x) + t0 * a.k;
+    c.y = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(a.y) + (size_t)t0 * a.n * osz);
+    c.res = a.res ? static_cast<const uint16_t*>(a.res) + t0 * a.n : nullptr;
+    c.p2 = Plane2{static_cast<const uint8_t*>(a.lo2), static_cast<const uint8_t*>(a.hi2),
+                  static_cast<const uint8_t*>(a.sc2),
+                  a.y2 && !a.glu ? static_cast<uint16_t*>(a.y2) + t0 * a.n2 : nullptr, (int)a.n2, 0};
     hipError_t e;
-    if (t <= 16) {
-      switch (p.ct) {
-        case 1: e = launch_few<F, 1>(a, p, x, y, res, t, s); break;
-        case 2: e = launch_few<F, 2>(a, p, x, y, res, t, s); break;
-        case 3: e = launch_few<F, 3>(a, p, x, y, res, t, s); break;
-        default: e = launch_few<F, 4>(a, p, x, y, res, t, s); break;
-      }
+    if constexpr (F == FMT_Q4) {
+      e = a.glu ? launch_chunk<F, true>(a, p, c, tsb, table_cap, s) : launch_chunk<F, false>(a, p, c, tsb, table_cap, s);
     } else {
-      const TokLaunch L = tok_launch(a.n, t, p.bn, tsb, table_cap);
-      switch (L.ct) {
-        case 1: e = launch_tok_ct<F, 1>(a, L, x, y, res, t, s); break;
-        case 2: e = launch_tok_ct<F, 2>(a, L, x, y, res, t, s); break;
-        case 3: e = launch_tok_ct<F, 3>(a, L, x, y, res, t, s); break;
-        default: e = launch_tok_ct<F, 4>(a, L, x, y, res, t, s); break;
-      }
+      e = launch_chunk<F, false>(a, p, c, tsb, table_cap, s);
     }
     if (e != hipSuccess) return e;
   }
@@ -1010,8 +1125,9 @@ hipError_t launch_fmt_t(const FmtArgs& a, const FmtPlan& p, hipStream_t s) {
 
 }  // namespace
 
-bool fmt_plan(int fmt, int64_t n, int64_t k, int64_t t, FmtPlan* p) {
+bool fmt_plan(int fmt, int64_t n, int64_t k, int64_t t, FmtPlan* p, bool glu) {
   if (fmt < FMT_Q4 || fmt > FMT_BF16 || n < 1 || t < 1 || k < 64 || (k % 64) != 0) return false;
+  if (glu && fmt != FMT_Q4) return false;
   // per-row offsets are 64-bit; the kernel's int arithmetic needs N, K, T below 2^31
   if (n >= (int64_t(1) << 31) || k >= (int64_t(1) << 30) || t >= (int64_t(1) << 31)) return false;
   // bytes of one row's scales in the LDS table
@@ -1020,24 +1136,28 @@ bool fmt_plan(int fmt, int64_t n, int64_t k, int64_t t, FmtPlan* p) {
   // (at most kRingWave bytes per wave)
   const int64_t ring = t > 16 ? (int64_t)kWaves * kRingWave : 0;
   const int64_t table_cap = ring + kTableBytes <= kLdsBytes ? kTableBytes : kLdsBytes - ring;
-  int64_t bn = (n + 255) / 256;  // about one workgroup per CU
-  if (bn > 64) bn = 64;          // at most four 16-row column tiles per wave
-  if (ts > 0 && bn * ts > table_cap) bn = table_cap / ts;
+  const int w = glu ? 2 : 1;
+  int64_t bn = (n + 255) / 256;  // about one workgroup per CU (the gated pair: 2 bn rows per workgroup)
+  if (bn > 64 / w) bn = 64 / w;  // at most four 16-row column tiles per wave
+  if (ts > 0 && w * bn * ts > table_cap) bn = table_cap / (w * ts);
   if (bn < 1) return false;
-  const int64_t ct = (bn + 15) / 16;
+  const int ct = fmt_col_tiles(bn, glu);
   p->bn = (int)bn;
-  p->ct = (int)ct;
+  p->ct = ct;
   p->blocks = (int)((n + bn - 1) / bn);
   // the largest launch's LDS (the partials of 16 tokens per tile)
   const int ppt = (fmt == FMT_W8 || fmt == FMT_BF16) ? 4 : 8;
-  const int tt = t <= 16 ? 1 : tok_tiles(t > 128 ? 128 : t, (int)ct);
-  p->lds_bytes = fmt_lds(ppt, tt, bn, ts);
+  const int tt = t <= 16 ? 1 : tok_tiles(t > 128 ? 128 : t, ct);
+  p->lds_bytes = fmt_lds(ppt, tt, bn, ts, w);
   return p->lds_bytes <= (size_t)kLdsBytes;
 }
 
 hipError_t launch_fmt(const FmtArgs& a, hipStream_t stream) {
   FmtPlan p;
-  if (!fmt_plan(a.fmt, a.n, a.k, a.t, &p)) return hipErrorInvalidValue;
+  const bool two = !a.glu && a.n2 > 0;
+  if (!fmt_plan(a.fmt, two ? a.n + a.n2 : a.n, a.k, a.t, &p, a.glu)) return hipErrorInvalidValue;
+  if (two) p.blocks = (int)((a.n + p.bn - 1) / p.bn + (a.n2 + p.bn - 1) / p.bn);
+  if (a.glu && a.fmt != FMT_Q4) return hipErrorInvalidValue;
   switch (a.fmt) {
     case FMT_Q4: return launch_fmt_t<FMT_Q4>(a, p, stream);
     case FMT_Q5: return launch_fmt_t<FMT_Q5>(a, p, stream);

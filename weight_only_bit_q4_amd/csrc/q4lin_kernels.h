@@ -173,6 +173,16 @@ struct FmtArgs {
   int64_t n, k, t;
   const void* res = nullptr;  // LinearAdd residual, bf16 [T][N] (nullptr: plain Linear)
   bool f32 = false;           // outputs as binary32 [T][N] (LinearSwiGLU's sums), not bf16
+  // A second weight of the same format and K over the same X in the same
+  // launch.  LinearPair (glu false): n2 rows of its own, output y2 (bf16
+  // [T][n2], no residual).  LinearSwiGLU (glu true, Q4 only): the up weight
+  // of the gate's N rows (lo/sc: the gate); y = bf16(silu(G) U), y2 unused.
+  const void* lo2 = nullptr;
+  const void* hi2 = nullptr;
+  const void* sc2 = nullptr;
+  void* y2 = nullptr;
+  int64_t n2 = 0;
+  bool glu = false;
 };
 struct FmtPlan {
   int bn;      // rows per workgroup
@@ -180,7 +190,8 @@ struct FmtPlan {
   int blocks;  // workgroups
   size_t lds_bytes;
 };
-bool fmt_plan(int fmt, int64_t n, int64_t k, int64_t t, FmtPlan* p);
+// glu: rows per workgroup of each of the gate and up weights (N rows each)
+bool fmt_plan(int fmt, int64_t n, int64_t k, int64_t t, FmtPlan* p, bool glu = false);
 hipError_t launch_fmt(const FmtArgs& a, hipStream_t stream);
 
 }  // namespace q4lin
