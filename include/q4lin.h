@@ -109,9 +109,11 @@ Q4LIN_API int q4lin_linear_add(const void *x, const void *codes, const void *sca
  *
  * each element equal to what q4lin_linear gives for that weight alone.  Each
  * (codes, scales, y) triple follows q4lin_linear's layout and alignment with
- * its own row count.  The one- to four-token and small-T routes (chosen for
- * N1 + N2 rows) run both weights in a single launch; the other routes run one
- * launch sequence per weight, one after the other on `stream`.  workspace
+ * its own row count.  Up to 128 tokens the route chosen for N1 + N2 rows runs
+ * both weights in a single launch, the second weight's rows as further row
+ * blocks; beyond that the many-token route runs both weights' tiles in one
+ * launch after one activation preparation; the wide-K routes run one launch
+ * sequence per weight, one after the other on `stream`.  workspace
  * must hold q4lin_pair_workspace_bytes(n1, n2, k, t) bytes.  N1 or N2 = 0
  * reduces to q4lin_linear on the other weight (whose pointers alone are then
  * checked).  y1 and y2 must not overlap each other or any input. */
@@ -135,9 +137,12 @@ Q4LIN_API int64_t q4lin_pair_workspace_bytes(int64_t n1, int64_t n2, int64_t k, 
  * bfloat16.  The gate weight (codes_gate, scales_gate) and the up weight
  * (codes_up, scales_up) both have N rows and q4lin_linear's layout and
  * alignment; y is bf16 [T][N] like q4lin_linear's.  workspace must hold
- * q4lin_swiglu_workspace_bytes(n, k, t) bytes (never 0 for a non-empty
- * product: the two sums pass through it), 256-byte aligned.  y must not
- * overlap any input or the workspace.  Errors as for q4lin_linear. */
+ * q4lin_swiglu_workspace_bytes(n, k, t) bytes, 256-byte aligned: 0 where one
+ * pass takes the same rows of both weights and applies the gate before its
+ * store (1 to 128 tokens, where the rows' scales fit the kernel's tables),
+ * else room for the two binary32 sums (or the many-token route's
+ * activation copy and partials).  y must not overlap any input or the
+ * workspace.  Errors as for q4lin_linear. */
 Q4LIN_API int q4lin_linear_swiglu(const void *x, const void *codes_gate, const void *scales_gate,
                       const void *codes_up, const void *scales_up, void *y, int64_t n, int64_t k, int64_t t,
                       void *workspace, size_t workspace_bytes, void *stream);

@@ -68,7 +68,7 @@ def _pair(n, k, t, seed):
                                    (517, 1280, 9), (128, 20480, 3), (768, 1024, 100), (1024, 1024, 300),
                                    (97, 320, 40), (6144, 5120, 64), (6144, 256, 1024), (2560, 17408, 1),
                                    (3072, 5120, 5), (3072, 5120, 16), (6000, 1024, 12), (6000, 1024, 17),
-                                   (3072, 1024, 100), (1000, 2048, 128), (333, 640, 65), (4100, 640, 33),
+                                   (6000, 640, 100), (1000, 2048, 128), (333, 640, 65), (4100, 640, 33),
                                    (16, 1 << 20, 40)])
 def test_swiglu_matches_oracle(n, k, t):
     x, cg, sg, cu, su = _pair(n, k, t, 101)

@@ -488,33 +488,60 @@ __device__ __forceinline__ void bf16_unit(const u32x4_t (&a)[TT][1], const u32x4
                                                             __builtin_bit_cast(bf16x8_t, c[ct]), acc[ct][tt], 0, 0, 0);
 }
 
-// The block's scales go to LDS once (their rows are contiguous in the plane):
-// eight 2-byte elements per thread and batch.
-__device__ __forceinline__ void stage_load(rsrc_t rsc, int elems, int i0, int tid, uint16_t (&v)[8]) {
+// Each wave copies the scale bytes of its own units [u0, u1) of the block's
+// rows into the LDS table ([row][unit], ts bytes a row, the plane's own
+// layout).  No other wave reads them, so the copy needs no workgroup
+// barrier: a wave starts on its units as soon as its own loads are in.
+// 2-byte elements, eight per lane and batch.
+struct WaveTable {
+  int ts, boff, ner, ne;  // row bytes, byte offset of u0 in a row, elements per row, elements
+  __device__ WaveTable(int rows, int ts_, int u0, int u1, int sb)
+      : ts(ts_), boff(u0 * sb), ner((u1 - u0) * sb / 2), ne(rows * ((u1 - u0) * sb / 2)) {}
+  // byte offsets (in the plane's rows from the block's first and in the
+  // table alike) of batch e0's elements; past the end: kNowhere
+  __device__ __forceinline__ void offsets(int e0, int lane, uint32_t (&o)[8]) const {
+    const int d = ner > 0 ? ner : 1;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = i0 + j * kThreads + tid;
-    v[j] = __builtin_amdgcn_raw_buffer_load_b16(rsc, i < elems ? (uint32_t)(2 * i) : kNowhere, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + 64 * j + lane, r = e / d;
+      o[j] = e < ne ? (uint32_t)(r * ts + boff + 2 * (e - r * d)) : kNowhere;
+    }
   }
-}
-__device__ __forceinline__ void stage_store(uint16_t* dst, int elems, int i0, int tid, const uint16_t (&v)[8]) {
+  __device__ __forceinline__ void load(rsrc_t rsc, const uint32_t (&o)[8], uint16_t (&v)[8]) const {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = i0 + j * kThreads + tid;
-    if (i < elems) dst[i] = v[j];
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b16(rsc, o[j], 0, 0);
   }
-}
+  __device__ __forceinline__ void store(uint8_t* tab, const uint32_t (&o)[8], const uint16_t (&v)[8]) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (o[j] != kNowhere) *reinterpret_cast<uint16_t*>(tab + o[j]) = v[j];
+  }
+  // every batch after the first, copied at once (long rows only)
+  __device__ __forceinline__ void copy_rest(rsrc_t rsc, uint8_t* tab, int lane) const {
+    for (int e0 = 8 * 64; e0 < ne; e0 += 8 * 64) {
+      uint32_t o[8];
+      uint16_t v[8];
+      offsets(e0, lane, o);
+      load(rsc, o, v);
+      store(tab, o, v);
+    }
+  }
+};
 
 // Row stride of the final sum's partials: BN rounded up to 4 mod 16 floats,
 // so the four token quads (4 lq rows apart) of a write land 16 banks apart
 __host__ __device__ constexpr int red_stride(int bn) { return (bn + 11) / 16 * 16 + 4; }
+// Columns of the partials: the block's rows, or for the gated pair both
+// weights' rows, the second from BN rounded up to a multiple of 4
+__host__ __device__ constexpr int red_cols(int bn, bool glu) { return glu ? 2 * ((bn + 3) & ~3) : bn; }
 
-// The sum over the eight waves' K runs in binary64: red[w][t < 16 TT][col <
-// BN] binary32 partials, rows red_stride(BN) floats apart (lane (li, lq) of
-// wave w holds row 16 ct + li, tokens 16 tt + 4 lq + r), then one output per
-// thread and step, rounded once; an output that comes out non-finite is
-// formed again exactly.  GLU: columns BN .. 2 BN - 1 hold the up weight's
-// rows, and the output is bf16(silu(G) U) of the two sums.
+// The sum over the eight waves' K runs in binary64: red[w][t < 16 TT][col]
+// binary32 partials, rows red_stride() floats apart (lane (li, lq) of wave w
+// holds row 16 ct + li, tokens 16 tt + 4 lq + r), then four adjacent
+// outputs of one token per thread and step (16-byte partial reads), each
+// rounded once; an output that comes out non-finite is formed again
+// exactly.  GLU: the up weight's rows are columns BNP.. (BN rounded up to a
+// multiple of 4), and the output is bf16(silu(G) U) of the two sums.
 template <int F, int CT, int TT, bool GLU = false>
 __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t* lds, int wave, int li, int lq,
                                           int tid, const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo,
@@ -523,11 +550,12 @@ __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t*
                                           int N, int K, int T, int BN, int n0, int rows) {
   constexpr int BT = 16 * TT;
   constexpr int CTH = GLU ? CT / 2 : CT;
-  const int RS = red_stride(GLU ? 2 * BN : BN);
+  const int BNP = GLU ? (BN + 3) & ~3 : BN;
+  const int RS = red_stride(red_cols(BN, GLU));
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    const int pl = ct / CTH, c = 16 * (ct - pl * CTH) + li, col = pl * BN + c;
+    const int pl = ct / CTH, c = 16 * (ct - pl * CTH) + li, col = pl * BNP + c;
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
@@ -537,32 +565,69 @@ __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t*
       }
   }
   __syncthreads();
-  for (int i = tid; i < T * rows; i += kThreads) {
-    const int t = i / rows, col = i - t * rows;
-    double v = 0.0;
+  // (columns rows .. 4 G4 - 1 of a row lie within its stride; their sums
+  // are never used)
+  const int G4 = (rows + 3) >> 2;
+  for (int i = tid; i < T * G4; i += kThreads) {
+    const int t = i / G4, c0 = 4 * (i - t * G4);
+    const int nv = min(4, rows - c0);
+    double v[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += (double)red[(w * BT + t) * RS + col];
-    const size_t o = (size_t)t * N + n0 + col;
+    for (int w = 0; w < kWaves; ++w) {
+      const f32x4_t p = *reinterpret_cast<const f32x4_t*>(red + (w * BT + t) * RS + c0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] += (double)p[j];
+    }
+    const size_t o = (size_t)t * N + n0 + c0;
+    uint16_t h[4] = {0, 0, 0, 0};
     if constexpr (GLU) {
-      double u = 0.0;
+      double u[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) u += (double)red[(w * BT + t) * RS + BN + col];
-      // each sum rounded to binary32 as where the two sums are stored
-      // between passes (+0 maps a -0 sum to +0, as a sum of zero products
-      // starts at +0), the gate in binary64, one rounding of the product
-      const double g = (double)(float)v + 0.0, uv = (double)(float)u + 0.0;
-      const double silu = g / (1.0 + exp(-g));
-      y[o] = f32_to_bf16_rne((float)(silu * uv));
+      for (int w = 0; w < kWaves; ++w) {
+        const f32x4_t p = *reinterpret_cast<const f32x4_t*>(red + (w * BT + t) * RS + BNP + c0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] += (double)p[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j >= nv) break;
+        // each sum rounded to binary32 as where the two sums are stored
+        // between passes (+0 maps a -0 sum to +0, as a sum of zero products
+        // starts at +0), the gate in binary64, one rounding of the product
+        const double g = (double)(float)v[j] + 0.0, uv = (double)(float)u[j] + 0.0;
+        const double silu = g / (1.0 + exp(-g));
+        h[j] = f32_to_bf16_rne((float)(silu * uv));
+      }
+    } else if (f32out) {
+      // binary32 sums (the gate and up of LinearSwiGLU)
+      float* yf = reinterpret_cast<float*>(y) + o;
+      if (nv == 4 && (reinterpret_cast<uintptr_t>(yf) & 15) == 0) {
+        *reinterpret_cast<f32x4_t*>(yf) = f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j < nv) yf[j] = (float)v[j];
+      }
       continue;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j >= nv) break;
+        double a = v[j];
+        if (res != nullptr) a += (double)bf16_bits_to_f32(res[o + j]);  // LinearAdd
+        h[j] = f32_to_bf16_rne((float)a);
+        if ((h[j] & 0x7F80u) == 0x7F80u) h[j] = exact_output<F>(x, lo, hi, sc, res, N, K, n0 + c0 + j, t);  // rare
+      }
     }
-    if (f32out) {
-      reinterpret_cast<float*>(y)[o] = (float)v;  // binary32 sums (the gate and up of LinearSwiGLU)
-      continue;
+    uint16_t* yo = y + o;
+    if (nv == 4 && (reinterpret_cast<uintptr_t>(yo) & 7) == 0) {
+      *reinterpret_cast<u32x2_t*>(yo) = u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < nv) yo[j] = h[j];
     }
-    if (res != nullptr) v += (double)bf16_bits_to_f32(res[o]);  // LinearAdd
-    uint16_t hv = f32_to_bf16_rne((float)v);
-    if ((hv & 0x7F80u) == 0x7F80u) hv = exact_output<F>(x, lo, hi, sc, res, N, K, n0 + col, t);  // rare
-    y[o] = hv;
   }
 }
 
@@ -616,7 +681,7 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   const int pb = (int)(((int64_t)pairs * wave) / kWaves), pe = (int)(((int64_t)pairs * (wave + 1)) / kWaves);
   const int ts = units * U::SB;  // bytes of one row's scales
   // LDS: the partials of the final sum, then the scale table
-  uint8_t* tab = lds + (size_t)kWaves * 16 * red_stride(GLU ? 2 * BN : BN) * 4;
+  uint8_t* tab = lds + (size_t)kWaves * 16 * red_stride(red_cols(BN, GLU)) * 4;
 
   const rsrc_t rlo = make_rsrc(lo + (size_t)n0 * units * U::CB, (uint32_t)(rows * units * U::CB));
   const rsrc_t rlo2 = GLU ? make_rsrc(p2.lo + (size_t)n0 * units * U::CB, (uint32_t)(rows * units * U::CB)) : rlo;
@@ -649,10 +714,10 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
         L.a[v][0][p2] = __builtin_amdgcn_raw_buffer_load_b128(r, x_off, (uint32_t)(((2 * p + v) * U::K + 8 * p2) * 2), 0);
   };
 
-  const int elems = rows * ts / 2;
   const rsrc_t rsc = make_rsrc(U::SB ? sc + (size_t)n0 * ts : lo, (uint32_t)(rows * ts));
   const rsrc_t rsc2 = GLU ? make_rsrc(p2.sc + (size_t)n0 * ts, (uint32_t)(rows * ts)) : rsc;
-  uint16_t* sdst = reinterpret_cast<uint16_t*>(tab);
+  uint8_t* const tab2 = tab + rows * ts;  // GLU: the up weight's scales
+  const WaveTable wt(rows, ts, 2 * pb, min(2 * pe, units), U::SB);
   const int hsh = (lane >> 5) << 4;  // Q5: the half of a high dword that belongs to this lane
 
   f32x4_t acc[CT][1];
@@ -685,33 +750,26 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
     }
   };
 
-  // Scales of the block (first batch) in flight with the first two pairs'
-  // loads.  (A table larger than one batch is copied first, on its own.)
+  // The wave's scales (first batch) in flight with the first two pairs'
+  // loads.  (Batches past the first are copied before, on their own.)
   Loads b[NB];
+  uint32_t so[8];
   uint16_t sv[8], sv2[8];
   if constexpr (U::SB > 0) {
-    if (elems > 8 * kThreads) {
-      for (int i0 = 0; i0 < elems; i0 += 8 * kThreads) {
-        stage_load(rsc, elems, i0, tid, sv);
-        stage_store(sdst, elems, i0, tid, sv);
-        if constexpr (GLU) {
-          stage_load(rsc2, elems, i0, tid, sv2);
-          stage_store(sdst + elems, elems, i0, tid, sv2);
-        }
-      }
-    }
-    stage_load(rsc, elems, 0, tid, sv);  // a repeat of the first batch when already copied
-    if constexpr (GLU) stage_load(rsc2, elems, 0, tid, sv2);
+    wt.copy_rest(rsc, tab, lane);
+    if constexpr (GLU) wt.copy_rest(rsc2, tab2, lane);
+    wt.offsets(0, lane, so);
+    wt.load(rsc, so, sv);
+    if constexpr (GLU) wt.load(rsc2, so, sv2);
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) load(pb + i, b[i]);
   if constexpr (U::SB > 0) {
-    stage_store(sdst, elems, 0, tid, sv);
-    if constexpr (GLU) stage_store(sdst + elems, elems, 0, tid, sv2);
+    wt.store(tab, so, sv);
+    if constexpr (GLU) wt.store(tab2, so, sv2);
   }
-  // the table's writes are visible after this; the loads stay in flight
+  // (a wave reads only the table entries it wrote itself: no barrier)
   wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
   // (Every load is issued outside the branches, so the compiler's count of
   // the loads in flight stays exact.)
   for (int p = pb; p < pe; p += NB) {
@@ -853,10 +911,10 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
         A[tt][h] = *reinterpret_cast<const u32x4_t*>(xrd[h] + slot * SLOT + tt * (16 * PPT * 16));
   };
 
-  const int elems = rows * ts / 2;
   const rsrc_t rsc = make_rsrc(U::SB ? sc + (size_t)n0 * ts : lo, (uint32_t)(rows * ts));
   const rsrc_t rsc2 = GLU ? make_rsrc(p2.sc + (size_t)n0 * ts, (uint32_t)(rows * ts)) : rsc;
-  uint16_t* sdst = reinterpret_cast<uint16_t*>(tab);
+  uint8_t* const tab2 = tab + rows * ts;  // GLU: the up weight's scales
+  const WaveTable wt(rows, ts, 2 * pb, ue, U::SB);
   const int hsh = (lane >> 5) << 4;
 
   f32x4_t acc[CT][TT];
@@ -868,20 +926,14 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
   // Prologue: the scales' first batch, the first NS units' activations, then
   // the first chunk's codes.
   PairCodes<F, CT> cc[MP];
+  uint32_t so[8];
   uint16_t sv[8], sv2[8];
   if constexpr (U::SB > 0) {
-    if (elems > 8 * kThreads) {
-      for (int i0 = 0; i0 < elems; i0 += 8 * kThreads) {
-        stage_load(rsc, elems, i0, tid, sv);
-        stage_store(sdst, elems, i0, tid, sv);
-        if constexpr (GLU) {
-          stage_load(rsc2, elems, i0, tid, sv2);
-          stage_store(sdst + elems, elems, i0, tid, sv2);
-        }
-      }
-    }
-    stage_load(rsc, elems, 0, tid, sv);
-    if constexpr (GLU) stage_load(rsc2, elems, 0, tid, sv2);
+    wt.copy_rest(rsc, tab, lane);
+    if constexpr (GLU) wt.copy_rest(rsc2, tab2, lane);
+    wt.offsets(0, lane, so);
+    wt.load(rsc, so, sv);
+    if constexpr (GLU) wt.load(rsc2, so, sv2);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -891,13 +943,12 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
   for (int i = 0; i < MP; ++i)
     load_codes<F, CT, GLU>(rlo, rlo2, rhi, rnull, lo_off, hi_off, pb + i, pb + i < pe, cc[i]);
   if constexpr (U::SB > 0) {
-    stage_store(sdst, elems, 0, tid, sv);
-    if constexpr (GLU) stage_store(sdst + elems, elems, 0, tid, sv2);
+    wt.store(tab, so, sv);
+    if constexpr (GLU) wt.store(tab2, so, sv2);
   }
-  // the table's writes are visible after this; the loads stay in flight
-  // (a fence here would also wait for the copies into the rings)
+  // (a wave reads only the table entries it wrote itself: no barrier; the
+  // loads stay in flight)
   wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
 
   // Chunks of MP pairs.  Unit j of a chunk reads slot j % NS.  Before it,
   // the loads issued after its activations are: for j < NS the later
@@ -953,7 +1004,7 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
 // weights whose rows a workgroup takes (2 for the gated pair).
 size_t fmt_lds(int ppt, int tt, int64_t bn, int64_t ts, int w) {
   const int64_t table = (w * bn * ts + 15) / 16 * 16;
-  const int64_t red = (int64_t)kWaves * 16 * tt * red_stride((int)(w * bn)) * 4;
+  const int64_t red = (int64_t)kWaves * 16 * tt * red_stride(red_cols((int)bn, w == 2)) * 4;
   if (tt == 1) return (size_t)(red + table);
   const int64_t slot = 16 * tt * ppt * 16;
   const int64_t ns = slot * 4 <= kRingWave ? 4 : slot * 2 <= kRingWave ? 2 : 1;
@@ -983,7 +1034,10 @@ int fmt_col_tiles(int64_t bn, bool glu) { return (int)((glu ? 2 : 1) * ((bn + 15
 // against 24.8-32.9); below that the taller block's extra code loads cost
 // more than the copies saved (T = 33..64 21-22 against 17-20.5 us).  The
 // rows of both weights count: a pair's second weight adds row blocks from
-// `first` on; the gated pair's workgroups take bn rows of each.
+// `first` on.  The gated pair's workgroups take bn rows of each weight and
+// keep one token range (3072 x 5120 each: T = 72 24.3 against 26.8 us,
+// T = 100 29.8 / 30.9, T = 128 32.0 / 31.5: its taller block has four
+// column tiles for 2 x 24 rows).
 struct TokLaunch {
   int64_t bn;
   int ct, ts, tt;
@@ -995,9 +1049,9 @@ TokLaunch tok_launch(const FmtArgs& a, int64_t t, int64_t bn1, int64_t ts_bytes,
   TokLaunch L;
   L.ts = 1;
   L.bn = bn1;
-  if (t > 64 && (rows + 255) / 256 <= 32) {
-    const int64_t bn2 = a.glu ? (a.n + 127) / 128 : (2 * rows + 255) / 256;
-    if ((a.glu ? 2 : 1) * bn2 * ts_bytes <= table_cap) {
+  if (!a.glu && t > 64 && (rows + 255) / 256 <= 32) {
+    const int64_t bn2 = (2 * rows + 255) / 256;
+    if (bn2 * ts_bytes <= table_cap) {
       L.ts = 2;
       L.bn = bn2;
     }
