@@ -637,8 +637,12 @@ def main(argv=None):
               % (weight_bytes(n, k), rc_s * 1e6, rc_gbs), flush=True)
         for t in range(lo, hi + 1, step):
             p = Point(n, k, t, wl_seed, data=(xall[:t], codes, scales))
-            steps = max(20, min(200, int(2e-3 / max(1e-6, 1e-6 * t))))
-            secs = p.time(steps, 5, repeats=args.repeats)
+            # about 10 ms of timed calls behind a quarter as many untimed
+            # ones, as for the single points (shorter replays run at lower
+            # clocks: 6144x5120 T=128 27.3 us with 20 calls behind 8,
+            # 23.8 us with 1000 behind 50)
+            steps = max(200, min(2000, int(10e-3 / max(6e-6, 0.2e-6 * t))))
+            secs = p.time(steps, max(50, steps // 4), repeats=args.repeats)
             p.free()
             med = float(np.median(secs))
             row = {"t": t, "us": med * 1e6, "min_us": min(secs) * 1e6, "gbs": gbs(n, k, t, med),

@@ -301,22 +301,30 @@ struct PairCodes {
 // Byte offsets of this lane's code loads per column tile (rows past the
 // block repeat the last one; their sums are never stored), relative to
 // buffers over the block's rows of each plane, and the lane's row in the
-// scale table.  Paired formats: quarter lq reads half lq % 2 of the pair's
-// unit lq / 2; BF16_CTRL: quarter lq of each unit.  GLU: the first CT / 2
-// tiles are the gate weight's rows, the others the same rows of the up
-// weight, whose scales follow the gate's in the table.
-template <int F, int CT, bool GLU = false>
+// scale table.  A tile's pair of units is 64 bytes of each of its 16 rows
+// (paired formats: piece q is half q % 2 of unit q / 2; BF16_CTRL: piece q
+// of each unit); lane (li, lq) multiplies piece lq of row li.  Direct: it
+// loads that piece itself (a quarter-wave reads 16 rows).  COAL: lane l
+// loads piece l % 4 of row l / 4 (a quarter-wave reads four rows, about
+// three times faster through the address unit) and a lane exchange hands
+// the pieces over.  GLU: the first CT / 2 tiles are the gate weight's rows,
+// the others the same rows of the up weight, whose scales follow the
+// gate's in the table.
+template <int F, int CT, bool GLU = false, bool COAL = false>
 __device__ __forceinline__ void lane_offsets(int rows, int units, int ts, int li, int lq, uint32_t (&lo_off)[CT],
                                              uint32_t (&hi_off)[CT], int (&tab_row)[CT]) {
   constexpr int HB = Fmt<F>::HB;
   constexpr int CTH = GLU ? CT / 2 : CT;  // column tiles per weight
   const int row_bytes = units * Unit<F>::CB;
+  const int lane = 16 * lq + li;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int pl = ct / CTH;
     const int rl = min(16 * (ct - pl * CTH) + li, rows - 1);
-    if constexpr (F == FMT_BF16) lo_off[ct] = (uint32_t)(rl * row_bytes + lq * 16);
-    else lo_off[ct] = (uint32_t)(rl * row_bytes + (lq >> 1) * Unit<F>::CB + (lq & 1) * 16);
+    const int rc = COAL ? min(16 * (ct - pl * CTH) + (lane >> 2), rows - 1) : rl;  // the row this lane loads
+    const int qc = COAL ? (lane & 3) : lq;                                          // and its piece
+    if constexpr (F == FMT_BF16) lo_off[ct] = (uint32_t)(rc * row_bytes + qc * 16);
+    else lo_off[ct] = (uint32_t)(rc * row_bytes + (qc >> 1) * Unit<F>::CB + (qc & 1) * 16);
     hi_off[ct] = (uint32_t)(rl * units * HB + (lq >> 1) * HB + (lq & 1) * (HB / 2));
     tab_row[ct] = (pl * rows + rl) * ts;
   }
@@ -500,11 +508,21 @@ struct WaveTable {
   // byte offsets (in the plane's rows from the block's first and in the
   // table alike) of batch e0's elements; past the end: kNowhere
   __device__ __forceinline__ void offsets(int e0, int lane, uint32_t (&o)[8]) const {
+    // one division per lane; each next element (64 further) steps the row
+    // by q and the column by m (carrying into the row)
     const int d = ner > 0 ? ner : 1;
+    const int q = 64 / d, m = 64 - q * d;
+    int e = e0 + lane, r = e / d, c = e - r * d;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int e = e0 + 64 * j + lane, r = e / d;
-      o[j] = e < ne ? (uint32_t)(r * ts + boff + 2 * (e - r * d)) : kNowhere;
+      o[j] = e < ne ? (uint32_t)(r * ts + boff + 2 * c) : kNowhere;
+      e += 64;
+      r += q;
+      c += m;
+      if (c >= d) {
+        c -= d;
+        ++r;
+      }
     }
   }
   __device__ __forceinline__ void load(rsrc_t rsc, const uint32_t (&o)[8], uint16_t (&v)[8]) const {
@@ -537,10 +555,10 @@ __host__ __device__ constexpr int red_cols(int bn, bool glu) { return glu ? 2 * 
 
 // The sum over the eight waves' K runs in binary64: red[w][t < 16 TT][col]
 // binary32 partials, rows red_stride() floats apart (lane (li, lq) of wave w
-// holds row 16 ct + li, tokens 16 tt + 4 lq + r), then four adjacent
-// outputs of one token per thread and step (16-byte partial reads), each
-// rounded once; an output that comes out non-finite is formed again
-// exactly.  GLU: the up weight's rows are columns BNP.. (BN rounded up to a
+// holds row 16 ct + li, tokens 16 tt + 4 lq + r), then one output per
+// thread and step (up to 1024 outputs) or four adjacent ones (16-byte
+// partial reads; more outputs), each rounded once; an output that comes out
+// non-finite is formed again exactly.  GLU: the up weight's rows are columns BNP.. (BN rounded up to a
 // multiple of 4), and the output is bf16(silu(G) U) of the two sums.
 template <int F, int CT, int TT, bool GLU = false>
 __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t* lds, int wave, int li, int lq,
@@ -565,40 +583,62 @@ __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t*
       }
   }
   __syncthreads();
-  // (columns rows .. 4 G4 - 1 of a row lie within its stride; their sums
-  // are never used)
+  // one output from its sums (the gate and up sums for GLU)
+  auto finish = [&](double v, double u, size_t o, int t, int col) __device__ -> uint16_t {
+    if constexpr (GLU) {
+      // each sum rounded to binary32 as where the two sums are stored
+      // between passes (+0 maps a -0 sum to +0, as a sum of zero products
+      // starts at +0), the gate in binary64, one rounding of the product
+      const double g = (double)(float)v + 0.0, uv = (double)(float)u + 0.0;
+      const double silu = g / (1.0 + exp(-g));
+      return f32_to_bf16_rne((float)(silu * uv));
+    } else {
+      if (res != nullptr) v += (double)bf16_bits_to_f32(res[o]);  // LinearAdd
+      uint16_t h = f32_to_bf16_rne((float)v);
+      if ((h & 0x7F80u) == 0x7F80u) h = exact_output<F>(x, lo, hi, sc, res, N, K, n0 + col, t);  // rare
+      return h;
+    }
+  };
+  if (T * rows <= 2 * kThreads) {
+    // up to two outputs per thread: one per step (the shortest chains)
+    for (int i = tid; i < T * rows; i += kThreads) {
+      const int t = i / rows, col = i - t * rows;
+      double v = 0.0, u = 0.0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        v += (double)red[(w * BT + t) * RS + col];
+        if constexpr (GLU) u += (double)red[(w * BT + t) * RS + BNP + col];
+      }
+      const size_t o = (size_t)t * N + n0 + col;
+      if (!GLU && f32out) {
+        reinterpret_cast<float*>(y)[o] = (float)v;  // binary32 sums (the gate and up of LinearSwiGLU)
+        continue;
+      }
+      y[o] = finish(v, u, o, t, col);
+    }
+    return;
+  }
+  // more: four adjacent outputs of one token per step (16-byte partial
+  // reads; columns rows .. 4 G4 - 1 of a row lie within its stride and
+  // their sums are never used)
   const int G4 = (rows + 3) >> 2;
   for (int i = tid; i < T * G4; i += kThreads) {
     const int t = i / G4, c0 = 4 * (i - t * G4);
     const int nv = min(4, rows - c0);
-    double v[4] = {0.0, 0.0, 0.0, 0.0};
+    double v[4] = {0.0, 0.0, 0.0, 0.0}, u[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const f32x4_t p = *reinterpret_cast<const f32x4_t*>(red + (w * BT + t) * RS + c0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] += (double)p[j];
+      if constexpr (GLU) {
+        const f32x4_t q = *reinterpret_cast<const f32x4_t*>(red + (w * BT + t) * RS + BNP + c0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] += (double)q[j];
+      }
     }
     const size_t o = (size_t)t * N + n0 + c0;
-    uint16_t h[4] = {0, 0, 0, 0};
-    if constexpr (GLU) {
-      double u[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const f32x4_t p = *reinterpret_cast<const f32x4_t*>(red + (w * BT + t) * RS + BNP + c0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) u[j] += (double)p[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j >= nv) break;
-        // each sum rounded to binary32 as where the two sums are stored
-        // between passes (+0 maps a -0 sum to +0, as a sum of zero products
-        // starts at +0), the gate in binary64, one rounding of the product
-        const double g = (double)(float)v[j] + 0.0, uv = (double)(float)u[j] + 0.0;
-        const double silu = g / (1.0 + exp(-g));
-        h[j] = f32_to_bf16_rne((float)(silu * uv));
-      }
-    } else if (f32out) {
+    if (!GLU && f32out) {
       // binary32 sums (the gate and up of LinearSwiGLU)
       float* yf = reinterpret_cast<float*>(y) + o;
       if (nv == 4 && (reinterpret_cast<uintptr_t>(yf) & 15) == 0) {
@@ -609,16 +649,11 @@ __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t*
           if (j < nv) yf[j] = (float)v[j];
       }
       continue;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j >= nv) break;
-        double a = v[j];
-        if (res != nullptr) a += (double)bf16_bits_to_f32(res[o + j]);  // LinearAdd
-        h[j] = f32_to_bf16_rne((float)a);
-        if ((h[j] & 0x7F80u) == 0x7F80u) h[j] = exact_output<F>(x, lo, hi, sc, res, N, K, n0 + c0 + j, t);  // rare
-      }
     }
+    uint16_t h[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < nv) h[j] = finish(v[j], u[j], o + j, t, c0 + j);
     uint16_t* yo = y + o;
     if (nv == 4 && (reinterpret_cast<uintptr_t>(yo) & 7) == 0) {
       *reinterpret_cast<u32x2_t*>(yo) = u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
@@ -628,6 +663,21 @@ __device__ __forceinline__ void final_sum(const f32x4_t (&acc)[CT][TT], uint8_t*
       for (int j = 0; j < 4; ++j)
         if (j < nv) yo[j] = h[j];
     }
+  }
+}
+
+// Compile-time step numbers: nested_steps<0, M>(n, fn) runs fn(IC<0>),
+// then fn(IC<1>) inside a branch taken when 1 < n, and so on up to M - 1,
+// so that the code of step s is reached only through steps 0 .. s - 1.
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+template <int I, int M, class Fn>
+__device__ __forceinline__ void nested_steps(int n, Fn& fn) {
+  fn(IC<I>{});
+  if constexpr (I + 1 < M) {
+    if (I + 1 < n) nested_steps<I + 1, M>(n, fn);
   }
 }
 
@@ -692,11 +742,15 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
   int tab_row[CT];
   lane_offsets<F, CT, GLU>(rows, units, ts, li, lq, lo_off, hi_off, tab_row);
   // Activations: lane (li, lq) multiplies pieces XH xq .. XH xq + XH - 1 of
-  // token li in each unit, but lane l loads those of token l / 4 and
-  // quarter l % 4, so that a quarter-wave reads four token rows (sixteen
-  // rows of 16 bytes each take the address unit about three times as
-  // long); a lane exchange then hands every lane its own pieces.
-  const uint32_t x_off = (uint32_t)(min(lane >> 2, T - 1) * K * 2 + (lane & 3) * 16 * XH);
+  // token li in each unit.  From five tokens on lane l loads those of token
+  // l / 4 and quarter l % 4, so that a quarter-wave reads four token rows
+  // (sixteen rows of 16 bytes each take the address unit about three times
+  // as long), and a lane exchange then hands every lane its own pieces; up
+  // to four tokens a quarter-wave reads at most four rows anyway (tokens
+  // past T repeat the last) and each lane loads its own pieces.
+  const bool xchg = T > 4;
+  const uint32_t x_off = xchg ? (uint32_t)(min(lane >> 2, T - 1) * K * 2 + (lane & 3) * 16 * XH)
+                              : (uint32_t)(min(li, T - 1) * K * 2 + xq * 16 * XH);
   const int xsrc4 = (4 * li + xq) * 4;  // the lane holding this lane's pieces (byte address)
 
   struct Loads {
@@ -731,7 +785,7 @@ fmt_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const
 #pragma unroll
     for (int v = 0; v < 2; ++v)
 #pragma unroll
-      for (int h = 0; h < XH; ++h) A[v][0][h] = lane_piece(L.a[v][0][h], xsrc4);
+      for (int h = 0; h < XH; ++h) A[v][0][h] = xchg ? lane_piece(L.a[v][0][h], xsrc4) : L.a[v][0][h];
     if constexpr (F == FMT_BF16) {
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
@@ -803,10 +857,12 @@ struct TokShape {
   static constexpr int NI = TTK * PPT / 64;         // direct-to-LDS loads per unit and lane
   static constexpr int RING = kWaves * NS * SLOT;   // all waves' rings
 };
-// code pairs held in registers at once (fewer with the high bits of Q5/Q6)
-template <int F, int CT>
+// code pairs held in registers at once (fewer with the high bits of Q5/Q6
+// and beside the accumulators of eight token tiles)
+template <int F, int CT, int TT>
 constexpr int tok_pairs() {
-  return (F == FMT_Q5 || F == FMT_Q6) ? (CT <= 2 ? 4 : 2) : (CT <= 2 ? 6 : 4);
+  constexpr int m = (F == FMT_Q5 || F == FMT_Q6) ? (CT <= 2 ? 4 : 2) : (CT <= 2 ? 6 : 4);
+  return TT >= 8 ? m - 2 : m;
 }
 
 template <int F, int CT, int TT, bool GLU>
@@ -818,7 +874,7 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
   using S = TokShape<F, TT>;
   constexpr int XH = Fmt<F>::XH, HB = Fmt<F>::HB;
   constexpr int PPT = S::PPT, NS = S::NS, NI = S::NI, SLOT = S::SLOT;
-  constexpr int MP = tok_pairs<F, CT>();
+  constexpr int MP = tok_pairs<F, CT, TT>();
   constexpr int LC = CT * Fmt<F>::LPT;  // code-plane loads per pair
   constexpr bool NAT = F == FMT_Q4;
   static_assert((2 * MP) % NS == 0, "a chunk of pairs keeps the ring's slot order");
@@ -871,7 +927,8 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
   const rsrc_t rnull = make_rsrc(x, 0u);  // every access out of range
   uint32_t lo_off[CT], hi_off[CT];
   int tab_row[CT];
-  lane_offsets<F, CT, GLU>(rows, units, ts, li, lq, lo_off, hi_off, tab_row);
+  lane_offsets<F, CT, GLU, true>(rows, units, ts, li, lq, lo_off, hi_off, tab_row);
+  const int csrc4 = (4 * li + lq) * 4;  // the lane that loaded this lane's code pieces (byte address)
 
   // A slot holds one unit's activations, piece (tl, pc) of token tl at
   // position tl PPT + (pc ^ swz(tl)), swz(tl) = (tl / (16 / PPT)) % PPT: the
@@ -926,6 +983,7 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
   // Prologue: the scales' first batch, the first NS units' activations, then
   // the first chunk's codes.
   PairCodes<F, CT> cc[MP];
+  int pchunk = pb;  // the chunk's first pair
   uint32_t so[8];
   uint16_t sv[8], sv2[8];
   if constexpr (U::SB > 0) {
@@ -953,14 +1011,21 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
   // Chunks of MP pairs.  Unit j of a chunk reads slot j % NS.  Before it,
   // the loads issued after its activations are: for j < NS the later
   // slots' copies and the chunk's codes (issued after the copies of the
-  // chunk's first NS units), else the NS - 1 copies issued after it.
-  // (Every load is issued outside the branches, so these counts and the
-  // compiler's own stay exact.)
-  for (int p0 = pb; p0 < pe; p0 += MP) {
-#pragma unroll
-    for (int i = 0; i < MP; ++i) {
+  // chunk's first NS units), else the NS - 1 copies issued after it.  The
+  // pairs of a chunk run nested (pair i + 1 inside pair i's branch), so
+  // pairs past the run issue nothing and every path to a pair has issued
+  // the same loads before it: these counts and the compiler's own stay
+  // exact.  The next chunk's codes are loaded only when it exists.
+  auto pair_step = [&](auto ic) __device__ {
+    constexpr int i = decltype(ic)::value;
+    const int p0 = pchunk;
+    {
       u32x2_t ca[CT], cb[CT];
       uint32_t ha[CT], hb[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int v = 0; v < Fmt<F>::NC; ++v) cc[i].c[ct][v] = lane_piece(cc[i].c[ct][v], csrc4);
       if constexpr (Fmt<F>::PAIRED) split_pair<F, CT>(cc[i], hsh, ca, cb, ha, hb);
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
@@ -986,12 +1051,17 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
         }
       }
     }
+  };
+  for (pchunk = pb; pchunk < pe; pchunk += MP) {
+    nested_steps<0, MP>(pe - pchunk, pair_step);
     // the next chunk's codes, after the copies of its first NS units (as in
-    // the prologue; past the run they read nothing)
+    // the prologue; pairs past the run read nothing)
     __builtin_amdgcn_sched_barrier(0);
+    if (pchunk + MP < pe) {
 #pragma unroll
-    for (int i = 0; i < MP; ++i)
-      load_codes<F, CT, GLU>(rlo, rlo2, rhi, rnull, lo_off, hi_off, p0 + MP + i, p0 + MP + i < pe, cc[i]);
+      for (int i = 0; i < MP; ++i)
+        load_codes<F, CT, GLU>(rlo, rlo2, rhi, rnull, lo_off, hi_off, pchunk + MP + i, pchunk + MP + i < pe, cc[i]);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vm<0>();  // every copy into the rings has landed before the space is reused
