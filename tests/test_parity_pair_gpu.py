@@ -78,6 +78,8 @@ def test_pair_worked_examples(replicate):
                                        (3072, 3072, 5120, 16), (3072, 3072, 5120, 64), (2000, 1500, 1024, 128),
                                        (1000, 333, 2048, 77), (4096, 4096, 1024, 65), (700, 64, 1280, 5),
                                        (64, 9000, 640, 33), (8000, 8000, 640, 48),
+                                       (1, 1, 640, 64), (777, 1234, 640, 100), (3, 5, 64, 17),
+                                       (1, 2000, 1024, 5), (2000, 1, 1024, 128),
                                        (2560, 1000, 17408, 1), (3072, 3072, 1024, 300), (1000, 700, 2048, 200),
                                        (97, 33, 320, 1000)])
 def test_pair_matches_oracle(n1, n2, k, t):

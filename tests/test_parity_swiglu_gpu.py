@@ -69,7 +69,8 @@ def _pair(n, k, t, seed):
                                    (97, 320, 40), (6144, 5120, 64), (6144, 256, 1024), (2560, 17408, 1),
                                    (3072, 5120, 5), (3072, 5120, 16), (6000, 1024, 12), (6000, 1024, 17),
                                    (6000, 640, 100), (1000, 2048, 128), (333, 640, 65), (4100, 640, 33),
-                                   (16, 1 << 20, 40)])
+                                   (16, 1 << 20, 40), (1, 640, 100), (5, 64, 17), (2, 128, 5), (1000, 64, 128),
+                                   (257, 2048, 33)])
 def test_swiglu_matches_oracle(n, k, t):
     x, cg, sg, cu, su = _pair(n, k, t, 101)
     got = run_swiglu(x, cg, sg, cu, su, n, k, t, what="seeded")
