@@ -1069,6 +1069,97 @@ fmt_tok_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, c
   final_sum<F, CT, TT, GLU>(acc, lds, wave, li, lq, tid, x, lo, hi, sc, y, res, f32out, N, K, T, BN, n0, rows);
 }
 
+// ---------------------------------------------------------------------------
+// BF16_CTRL at one token (K <= 8192): the dense control needs no operand
+// work, so it runs as a plain streaming GEMV.  Each wave takes whole rows,
+// two at a time (grid-stride over the rows); lane l multiplies pieces
+// l, l + 64, ... (8 weights, 16 bytes each) with the same pieces of X, which
+// it loads once.  v_dot2_f32_bf16 chains per lane (the bf16 products are
+// exact in FP32), the 64 lane partials summed in binary64, one rounding; a
+// non-finite result is formed again exactly.
+// ---------------------------------------------------------------------------
+constexpr int kGemvWaves = 4;
+template <int CH>
+__global__ void __launch_bounds__(64 * kGemvWaves)
+bf16_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, uint16_t* __restrict__ y,
+                 const uint16_t* __restrict__ res, int f32out, int N, int K) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kGemvWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = gridDim.x * kGemvWaves;
+  const uint32_t row_bytes = (uint32_t)K * 2;
+  // pieces past the row read through the resource's end: zeros, no access
+  const rsrc_t rx = make_rsrc(x, row_bytes);
+  u32x4_t xp[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) xp[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((lane + 64 * i) * 16), 0, 0);
+  // (each dword goes through a scalar: a bit cast of a vector element takes
+  // the vector's first bytes)
+  auto dot2 = [](uint32_t wv, uint32_t xv, float c) __device__ {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wv), __builtin_bit_cast(bf16x2_t, xv), c, false);
+  };
+  auto dot = [&](const u32x4_t (&a)[CH]) __device__ {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t w0 = a[i].x, w1 = a[i].y, w2 = a[i].z, w3 = a[i].w;
+      const uint32_t x0 = xp[i].x, x1 = xp[i].y, x2 = xp[i].z, x3 = xp[i].w;
+      s = dot2(w0, x0, s);
+      s = dot2(w1, x1, s);
+      s = dot2(w2, x2, s);
+      s = dot2(w3, x3, s);
+    }
+    double d = (double)s;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
+    return d;
+  };
+  auto finish = [&](int n, double v) __device__ {
+    if (f32out) {
+      reinterpret_cast<float*>(y)[n] = (float)v;
+      return;
+    }
+    if (res != nullptr) v += (double)bf16_bits_to_f32(res[n]);  // LinearAdd
+    uint16_t h = f32_to_bf16_rne((float)v);
+    if ((h & 0x7F80u) == 0x7F80u) h = exact_output<FMT_BF16>(x, w, nullptr, nullptr, res, N, K, n, 0);  // rare
+    y[n] = h;
+  };
+  for (int r = gw; r < N; r += 2 * nw) {
+    const int r2 = min(r + nw, N - 1);  // (past the rows: the last row again, not stored)
+    const rsrc_t ra = make_rsrc(w + (size_t)r * row_bytes, row_bytes);
+    const rsrc_t rb = make_rsrc(w + (size_t)r2 * row_bytes, row_bytes);
+    u32x4_t a[CH], b[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)((lane + 64 * i) * 16), 0, 2);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)((lane + 64 * i) * 16), 0, 2);
+    const double va = dot(a), vb = dot(b);
+    if (lane == 0) {
+      finish(r, va);
+      if (r + nw < N) finish(r + nw, vb);
+    }
+  }
+}
+
+template <int CH>
+hipError_t launch_bf16_gemv_ch(const FmtArgs& a, hipStream_t s) {
+  const int64_t blocks = (a.n + 2 * kGemvWaves - 1) / (2 * kGemvWaves);  // two rows per wave
+  bf16_gemv_kernel<CH><<<dim3((unsigned)blocks), dim3(64 * kGemvWaves), 0, s>>>(
+      static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.lo), static_cast<uint16_t*>(a.y),
+      static_cast<const uint16_t*>(a.res), a.f32 ? 1 : 0, (int)a.n, (int)a.k);
+  return hipGetLastError();
+}
+// pieces per lane: the smallest of these that covers K / 512
+hipError_t launch_bf16_gemv(const FmtArgs& a, hipStream_t s) {
+  const int64_t need = (a.k / 8 + 63) / 64;
+  if (need <= 2) return launch_bf16_gemv_ch<2>(a, s);
+  if (need <= 4) return launch_bf16_gemv_ch<4>(a, s);
+  if (need <= 6) return launch_bf16_gemv_ch<6>(a, s);
+  if (need <= 8) return launch_bf16_gemv_ch<8>(a, s);
+  if (need <= 10) return launch_bf16_gemv_ch<10>(a, s);
+  if (need <= 12) return launch_bf16_gemv_ch<12>(a, s);
+  return launch_bf16_gemv_ch<16>(a, s);
+}
+
 // LDS of a launch: the few-token kernel's partials and scale table, or the
 // many-token kernel's rings and table (the partials reuse them).  w: the
 // weights whose rows a workgroup takes (2 for the gated pair).
@@ -1282,6 +1373,7 @@ hipError_t launch_fmt(const FmtArgs& a, hipStream_t stream) {
   if (!fmt_plan(a.fmt, two ? a.n + a.n2 : a.n, a.k, a.t, &p, a.glu)) return hipErrorInvalidValue;
   if (two) p.blocks = (int)((a.n + p.bn - 1) / p.bn + (a.n2 + p.bn - 1) / p.bn);
   if (a.glu && a.fmt != FMT_Q4) return hipErrorInvalidValue;
+  if (a.fmt == FMT_BF16 && a.t == 1 && !two && a.k <= 8192) return launch_bf16_gemv(a, stream);
   switch (a.fmt) {
     case FMT_Q4: return launch_fmt_t<FMT_Q4>(a, p, stream);
     case FMT_Q5: return launch_fmt_t<FMT_Q5>(a, p, stream);
