@@ -1140,6 +1140,200 @@ bf16_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Q5, Q6, W8 and NVFP4 at one token (K <= 8192): the same streaming GEMV.
+// A piece is 16 bytes of the code plane (32 weights; W8: 16) with its high
+// bits and scale; lane l takes pieces l, l + 64, ... of each of the wave's
+// two rows.  The exact bf16 operands of the matrix-core kernels go through
+// v_dot2_f32_bf16 chains (Q5/Q6 in pair order, with the activations
+// permuted once per wave); the products of the all-offset codes run through
+// the same chain on the same activations (once per wave), so P - C is
+// exactly 0 for a piece of offset codes; the scale is applied in FP32 per
+// piece; binary64 lane sum, one rounding, exact repair when non-finite.
+// ---------------------------------------------------------------------------
+template <int F>
+struct GemvPiece {
+  static constexpr int KW = F == FMT_W8 ? 16 : 32;   // weights per piece
+  static constexpr int XV = KW / 8;                  // 16-byte activation vectors per piece
+  static constexpr int HB = F == FMT_Q5 ? 4 : F == FMT_Q6 ? 8 : 0;  // high-plane bytes per piece
+};
+__device__ __forceinline__ float dot2_bf(uint32_t w, uint32_t x, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, x), c, false);
+}
+// The sum over a piece (code dwords c, high bits hbits, NVFP4 scales s0 and
+// s1 of its two sixteens) of operand . activation, in one fixed chain order
+// for the code operands and the constant ones alike
+template <int F>
+__device__ __forceinline__ float piece_chain(u32x4_t c, uint64_t hbits, float s0, float s1,
+                                             const u32x4_t (&xa)[GemvPiece<F>::XV], bool constant) {
+  float d = 0.0f;
+  if constexpr (F == FMT_Q5 || F == FMT_Q6) {
+    constexpr uint32_t kc = F == FMT_Q5 ? 0x43104310u : 0x43204320u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // code dword j: weights 8 j .. 8 j + 7 of the piece
+      u32x4_t b = u32x4_t{kc, kc, kc, kc};
+      if (!constant) {
+        const uint32_t cw = c[j];
+        b = F == FMT_Q5 ? __builtin_bit_cast(u32x4_t, q5_operand(cw, (uint32_t)(hbits >> (8 * j)) & 0xFFu))
+                        : __builtin_bit_cast(u32x4_t, q6_operand(cw, (uint32_t)(hbits >> (16 * j)) & 0xFFFFu));
+      }
+      const uint32_t b0 = b.x, b1 = b.y, b2 = b.z, b3 = b.w;
+      const uint32_t x0 = xa[j].x, x1 = xa[j].y, x2 = xa[j].z, x3 = xa[j].w;
+      d = dot2_bf(b0, x0, d);
+      d = dot2_bf(b1, x1, d);
+      d = dot2_bf(b2, x2, d);
+      d = dot2_bf(b3, x3, d);
+    }
+  } else if constexpr (F == FMT_W8) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // weights 8 h .. 8 h + 7 of the piece
+      u32x4_t lo4, hi4;
+      if (constant) {
+        lo4 = u32x4_t{0x43004300u, 0x43004300u, 0x43004300u, 0x43004300u};
+        hi4 = u32x4_t{0x43C043C0u, 0x43C043C0u, 0x43C043C0u, 0x43C043C0u};
+      } else {
+        bf16x8_t lo8, hi8;
+        const uint32_t c0 = c[2 * h], c1 = c[2 * h + 1];
+        w8_operands(c0, c1, lo8, hi8);
+        lo4 = __builtin_bit_cast(u32x4_t, lo8);
+        hi4 = __builtin_bit_cast(u32x4_t, hi8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t l = lo4[i], hh = hi4[i], xx = xa[h][i];
+        d = dot2_bf(l, xx, d);
+        d = dot2_bf(hh, xx, d);
+      }
+    }
+  } else {  // NVFP4: exact weights, the E4M3 scale of each 16 inside
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t cw = c[j];
+      const u32x4_t b = __builtin_bit_cast(u32x4_t, nvfp4_operand(cw, j < 2 ? s0 : s1));
+      const uint32_t b0 = b.x, b1 = b.y, b2 = b.z, b3 = b.w;
+      const uint32_t x0 = xa[j].x, x1 = xa[j].y, x2 = xa[j].z, x3 = xa[j].w;
+      d = dot2_bf(b0, x0, d);
+      d = dot2_bf(b1, x1, d);
+      d = dot2_bf(b2, x2, d);
+      d = dot2_bf(b3, x3, d);
+    }
+  }
+  return d;
+}
+
+template <int F, int CH>
+__global__ void __launch_bounds__(64 * kGemvWaves)
+fmt_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, const uint8_t* __restrict__ hi,
+                const uint8_t* __restrict__ sc, uint16_t* __restrict__ y, const uint16_t* __restrict__ res,
+                int f32out, int N, int K) {
+  using P = GemvPiece<F>;
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kGemvWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = gridDim.x * kGemvWaves;
+  const uint32_t row_lo = F == FMT_W8 ? (uint32_t)K : (uint32_t)K / 2;
+  const uint32_t row_hi = (uint32_t)(K / P::KW) * P::HB;
+  const uint32_t row_sc = F == FMT_NVFP4 ? (uint32_t)K / 16 : F == FMT_W8 ? (uint32_t)K / 16 : (uint32_t)K / 32;
+  // the activations of this lane's pieces (permuted to pair order for
+  // Q5/Q6), and their correction chains; pieces past the row read zeros
+  const rsrc_t rx = make_rsrc(x, (uint32_t)K * 2);
+  u32x4_t xa[CH][P::XV];
+  float corr[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+#pragma unroll
+    for (int v = 0; v < P::XV; ++v)
+      xa[i][v] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(((lane + 64 * i) * P::KW + 8 * v) * 2), 0, 0);
+  struct Row {
+    u32x4_t c[CH];
+    uint64_t h[CH];
+    uint32_t sv[CH];
+  };
+  auto load_row = [&](int r, Row& w) __device__ {
+    const rsrc_t rl = make_rsrc(lo + (size_t)r * row_lo, row_lo);
+    const rsrc_t rh = make_rsrc(P::HB ? hi + (size_t)r * row_hi : lo, row_hi);
+    const rsrc_t rs = make_rsrc(sc + (size_t)r * row_sc, row_sc);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t p = (uint32_t)(lane + 64 * i);
+      w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rl, p * 16, 0, 2);
+      if constexpr (F == FMT_Q5) {
+        w.h[i] = __builtin_amdgcn_raw_buffer_load_b32(rh, p * 4, 0, 0);
+      } else if constexpr (F == FMT_Q6) {
+        const u32x2_t hv = __builtin_amdgcn_raw_buffer_load_b64(rh, p * 8, 0, 0);
+        w.h[i] = (uint64_t)hv.x | ((uint64_t)hv.y << 32);
+      } else {
+        w.h[i] = 0;
+      }
+      // the piece's scale bytes: Q5/Q6 and W8 one fp16 per two pieces, NVFP4 two E4M3 bytes per piece
+      w.sv[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, F == FMT_NVFP4 ? p * 2 : (p >> 1) * 2, 0, 0);
+    }
+  };
+  auto row_sum = [&](const Row& w) __device__ {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if constexpr (F == FMT_NVFP4) {
+        acc += piece_chain<F>(w.c[i], 0, e4m3_to_f32(w.sv[i] & 0xFFu), e4m3_to_f32(w.sv[i] >> 8), xa[i], false);
+      } else {
+        const float d = piece_chain<F>(w.c[i], w.h[i], 0.f, 0.f, xa[i], false);
+        acc = __builtin_fmaf(f16_bits_to_f32(w.sv[i]), d - corr[i], acc);
+      }
+    }
+    double v = (double)acc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+  };
+  auto finish = [&](int n, double v) __device__ {
+    if (f32out) {
+      reinterpret_cast<float*>(y)[n] = (float)v;
+      return;
+    }
+    if (res != nullptr) v += (double)bf16_bits_to_f32(res[n]);  // LinearAdd
+    uint16_t hv = f32_to_bf16_rne((float)v);
+    if ((hv & 0x7F80u) == 0x7F80u) hv = exact_output<F>(x, lo, hi, sc, res, N, K, n, 0);  // rare
+    y[n] = hv;
+  };
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    if constexpr (F == FMT_Q5 || F == FMT_Q6) {
+#pragma unroll
+      for (int v = 0; v < P::XV; ++v) xa[i][v] = __builtin_bit_cast(u32x4_t, pair_order(xa[i][v]));
+    }
+    corr[i] = F == FMT_NVFP4 ? 0.0f : piece_chain<F>(u32x4_t{0u, 0u, 0u, 0u}, 0, 0.f, 0.f, xa[i], true);
+  }
+  for (int r = gw; r < N; r += 2 * nw) {
+    Row wa, wb;
+    load_row(r, wa);
+    load_row(min(r + nw, N - 1), wb);  // (past the rows: the last row again, not stored)
+    const double va = row_sum(wa), vb = row_sum(wb);
+    if (lane == 0) {
+      finish(r, va);
+      if (r + nw < N) finish(r + nw, vb);
+    }
+  }
+}
+
+template <int F, int CH>
+hipError_t launch_fmt_gemv_ch(const FmtArgs& a, hipStream_t s) {
+  const int64_t blocks = (a.n + 2 * kGemvWaves - 1) / (2 * kGemvWaves);  // two rows per wave
+  fmt_gemv_kernel<F, CH><<<dim3((unsigned)blocks), dim3(64 * kGemvWaves), 0, s>>>(
+      static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.lo), static_cast<const uint8_t*>(a.hi),
+      static_cast<const uint8_t*>(a.sc), static_cast<uint16_t*>(a.y), static_cast<const uint16_t*>(a.res),
+      a.f32 ? 1 : 0, (int)a.n, (int)a.k);
+  return hipGetLastError();
+}
+template <int F>
+hipError_t launch_fmt_gemv(const FmtArgs& a, hipStream_t s) {
+  const int64_t need = (a.k / GemvPiece<F>::KW + 63) / 64;  // pieces per lane
+  if (need <= 1) return launch_fmt_gemv_ch<F, 1>(a, s);
+  if (need <= 2) return launch_fmt_gemv_ch<F, 2>(a, s);
+  if (need <= 3) return launch_fmt_gemv_ch<F, 3>(a, s);
+  if (need <= 4) return launch_fmt_gemv_ch<F, 4>(a, s);
+  if (need <= 6) return launch_fmt_gemv_ch<F, 6>(a, s);
+  return launch_fmt_gemv_ch<F, 8>(a, s);
+}
+
 template <int CH>
 hipError_t launch_bf16_gemv_ch(const FmtArgs& a, hipStream_t s) {
   const int64_t blocks = (a.n + 2 * kGemvWaves - 1) / (2 * kGemvWaves);  // two rows per wave
@@ -1373,7 +1567,16 @@ hipError_t launch_fmt(const FmtArgs& a, hipStream_t stream) {
   if (!fmt_plan(a.fmt, two ? a.n + a.n2 : a.n, a.k, a.t, &p, a.glu)) return hipErrorInvalidValue;
   if (two) p.blocks = (int)((a.n + p.bn - 1) / p.bn + (a.n2 + p.bn - 1) / p.bn);
   if (a.glu && a.fmt != FMT_Q4) return hipErrorInvalidValue;
-  if (a.fmt == FMT_BF16 && a.t == 1 && !two && a.k <= 8192) return launch_bf16_gemv(a, stream);
+  if (a.t == 1 && !two && a.k <= 8192) {  // one token: the streaming GEMVs
+    switch (a.fmt) {
+      case FMT_BF16: return launch_bf16_gemv(a, stream);
+      case FMT_Q5: return launch_fmt_gemv<FMT_Q5>(a, stream);
+      case FMT_Q6: return launch_fmt_gemv<FMT_Q6>(a, stream);
+      case FMT_W8: return launch_fmt_gemv<FMT_W8>(a, stream);
+      case FMT_NVFP4: return launch_fmt_gemv<FMT_NVFP4>(a, stream);
+      default: break;
+    }
+  }
   switch (a.fmt) {
     case FMT_Q4: return launch_fmt_t<FMT_Q4>(a, p, stream);
     case FMT_Q5: return launch_fmt_t<FMT_Q5>(a, p, stream);
