@@ -203,9 +203,12 @@ Q4LIN_API int64_t q4lin_noalloc_scratch_bytes(void);
  * rounded once to bf16 (an output whose binary32 sums leave the range is
  * formed again in binary64).
  * Routes: Q4 as q4lin_linear; the others stream their weight once per
- * 32 tokens on one workgroup per block of rows with K split across its
- * waves (matrix cores on exact bf16 code values, the scale applied per
- * group in binary32); no workspace (NULL and 0 are accepted).  Errors as for
+ * 128 tokens (64 where a block of rows needs three or four 16-row column
+ * tiles) on one workgroup per block of rows with K split across its waves
+ * (matrix cores on exact bf16 code values, the scale applied per group in
+ * binary32); at one token with K up to 8192 a streaming GEMV (whole rows per
+ * wave, bf16 dot products on the same exact values); no workspace (NULL and
+ * 0 are accepted).  Errors as for
  * q4lin_linear, plus Q4LIN_E_FORMAT for an unknown format. */
 #define Q4LIN_FMT_Q4G64_F16S 0
 #define Q4LIN_FMT_Q5G64_F16S 1
