@@ -75,6 +75,31 @@ def test_fmt_ragged(fmt, n, k, t):
                  what="%s %dx%d T=%d" % (inputs.FMT_NAMES[fmt], n, k, t))
 
 
+# One token, K up to 8192: the streaming GEMV, one instantiation per number
+# of 16-byte pieces a lane takes along a row (Q5/Q6/NVFP4: 32 weights a piece,
+# 1..4 pieces; W8: 16, 1..8; BF16_CTRL: 8, 2..16), each at the smallest and
+# the largest K it serves, on an odd row count (the grid's last wave takes
+# one real row); K = 8256 is past the GEMV (the matrix-core kernel at T = 1).
+GEMV_KS = {
+    inputs.FMT_Q5: [64, 2048, 2112, 4096, 4160, 6144, 6208, 8192, 8256],
+    inputs.FMT_Q6: [64, 2048, 2112, 4096, 4160, 6144, 6208, 8192, 8256],
+    inputs.FMT_NVFP4: [64, 2048, 2112, 4096, 4160, 6144, 6208, 8192, 8256],
+    inputs.FMT_W8: [64, 1024, 1088, 2048, 2112, 3072, 3136, 4096, 4160, 6144, 6208, 8192, 8256],
+    inputs.FMT_BF16: [64, 1024, 1088, 2048, 2112, 3072, 3136, 4096, 4160, 5120, 5184, 6144, 6208, 8192, 8256],
+}
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_fmt_one_token_lane_shapes(fmt):
+    n = 37
+    for k in GEMV_KS[fmt]:
+        w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, 900 + k)
+        x = inputs.gen_x(k, 1, 901 + k)
+        got = run_fmt(fmt, x, w, hi, sc, n, k, 1, what="one token")
+        assert_close(got, oracle.linear_fmt(fmt, x, w, hi, sc, n, k, 1),
+                     what="%s %dx%d T=1" % (inputs.FMT_NAMES[fmt], n, k))
+
+
 # (n, k, t): the many-token kernel's token tiles (2, 3, 4, 6, 8 per wave)
 # with one to four column tiles, one or two token ranges per row block (two
 # from 65 tokens up to 8192 rows; a ragged second range; a grid whose last
