@@ -436,9 +436,7 @@ decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     double v = __builtin_ldexp((double)((v0 + v1) + (v2 + v3)), wexp[wv * NT + t]);
     if constexpr (WV == 8) {
       // the eight threads of a (row, token) are eight consecutive lanes of one wave
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 4);
+      v = sum8_lanes(v);
       if (wv == 0) {
         if (glu) {
           dres[t * rows + r] = v;

@@ -83,6 +83,48 @@ __device__ __attribute__((noinline)) inline uint16_t exact_q4_output(const uint1
   return f32_to_bf16_rne((float)acc);
 }
 
+// Lane sums of a binary64 value without LDS round trips.  Each step adds
+// the value of a partner lane from the other half of the group being merged
+// (a pairing that is its own inverse), so every lane of the group ends with
+// the same bits (a + b == b + a).  DPP moves inside a row of 16 lanes
+// (quad_perm [1,0,3,2] and [2,3,0,1], then the mirror of each half-row and
+// of the row), the gfx950 lane swaps across rows (v_permlane16_swap: rows 0
+// and 1, 2 and 3; v_permlane32_swap: the two halves of the wave).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// sum over each aligned group of 8 lanes
+__device__ __forceinline__ double sum8_lanes(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]: lane pairs
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]: the quads
+  v += dpp_f64<0x141>(v);  // row_half_mirror: the other quad of the eight
+  return v;
+}
+// sum over all 64 lanes (every lane active)
+__device__ __forceinline__ double sum64_lanes(double v) {
+  v = sum8_lanes(v);
+  v += dpp_f64<0x140>(v);  // row_mirror: the other eight of the row
+  {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    v = __builtin_bit_cast(double, ((uint64_t)h[0] << 32) | l[0]) +
+        __builtin_bit_cast(double, ((uint64_t)h[1] << 32) | l[1]);
+  }
+  {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    v = __builtin_bit_cast(double, ((uint64_t)h[0] << 32) | l[0]) +
+        __builtin_bit_cast(double, ((uint64_t)h[1] << 32) | l[1]);
+  }
+  return v;
+}
+
 template <int V>
 using Slot = std::integral_constant<int, V>;
 

@@ -1108,10 +1108,7 @@ bf16_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, 
       s = dot2(w2, x2, s);
       s = dot2(w3, x3, s);
     }
-    double d = (double)s;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
-    return d;
+    return sum64_lanes((double)s);
   };
   auto finish = [&](int n, double v) __device__ {
     if (f32out) {
@@ -1132,6 +1129,10 @@ bf16_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, 
     for (int i = 0; i < CH; ++i) a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)((lane + 64 * i) * 16), 0, 2);
 #pragma unroll
     for (int i = 0; i < CH; ++i) b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)((lane + 64 * i) * 16), 0, 2);
+    // every load of both rows in flight before the first product (left to
+    // itself the scheduler moves each load down to its use, one or two
+    // loads in flight at a time)
+    __builtin_amdgcn_sched_barrier(0);
     const double va = dot(a), vb = dot(b);
     if (lane == 0) {
       finish(r, va);
@@ -1279,10 +1280,7 @@ fmt_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, 
         acc = __builtin_fmaf(f16_bits_to_f32(w.sv[i]), d - corr[i], acc);
       }
     }
-    double v = (double)acc;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return sum64_lanes((double)acc);
   };
   auto finish = [&](int n, double v) __device__ {
     if (f32out) {
@@ -1294,6 +1292,16 @@ fmt_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, 
     if ((hv & 0x7F80u) == 0x7F80u) hv = exact_output<F>(x, lo, hi, sc, res, N, K, n, 0);  // rare
     y[n] = hv;
   };
+  // The grid gives every wave its two rows gw and gw + nw (2 nw >= N).  All
+  // their loads go out before anything waits (left to itself the scheduler
+  // moves each load down to its use); the activations' permutation and
+  // correction chains run while the rows are in flight.
+  const int r = gw;
+  if (r >= N) return;
+  Row wa, wb;
+  load_row(r, wa);
+  load_row(min(r + nw, N - 1), wb);  // (past the rows: the last row again, not stored)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     if constexpr (F == FMT_Q5 || F == FMT_Q6) {
@@ -1302,15 +1310,10 @@ fmt_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ lo, 
     }
     corr[i] = F == FMT_NVFP4 ? 0.0f : piece_chain<F>(u32x4_t{0u, 0u, 0u, 0u}, 0, 0.f, 0.f, xa[i], true);
   }
-  for (int r = gw; r < N; r += 2 * nw) {
-    Row wa, wb;
-    load_row(r, wa);
-    load_row(min(r + nw, N - 1), wb);  // (past the rows: the last row again, not stored)
-    const double va = row_sum(wa), vb = row_sum(wb);
-    if (lane == 0) {
-      finish(r, va);
-      if (r + nw < N) finish(r + nw, vb);
-    }
+  const double va = row_sum(wa), vb = row_sum(wb);
+  if (lane == 0) {
+    finish(r, va);
+    if (r + nw < N) finish(r + nw, vb);
   }
 }
 
