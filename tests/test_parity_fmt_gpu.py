@@ -77,14 +77,14 @@ def test_fmt_ragged(fmt, n, k, t):
 
 # One token, K up to 8192: the streaming GEMV, one instantiation per number
 # of 16-byte pieces a lane takes along a row (Q5/Q6/NVFP4: 32 weights a piece,
-# 1..4 pieces; W8: 16, 1..8; BF16_CTRL: 8, 2..16), each at the smallest and
+# 1..4 pieces; W8: 16, 1..6 and 8; BF16_CTRL: 8, 2..16), each at the smallest and
 # the largest K it serves, on an odd row count (the grid's last wave takes
 # one real row); K = 8256 is past the GEMV (the matrix-core kernel at T = 1).
 GEMV_KS = {
     inputs.FMT_Q5: [64, 2048, 2112, 4096, 4160, 6144, 6208, 8192, 8256],
     inputs.FMT_Q6: [64, 2048, 2112, 4096, 4160, 6144, 6208, 8192, 8256],
     inputs.FMT_NVFP4: [64, 2048, 2112, 4096, 4160, 6144, 6208, 8192, 8256],
-    inputs.FMT_W8: [64, 1024, 1088, 2048, 2112, 3072, 3136, 4096, 4160, 6144, 6208, 8192, 8256],
+    inputs.FMT_W8: [64, 1024, 1088, 2048, 2112, 3072, 3136, 4096, 4160, 5120, 5184, 6144, 6208, 8192, 8256],
     inputs.FMT_BF16: [64, 1024, 1088, 2048, 2112, 3072, 3136, 4096, 4160, 5120, 5184, 6144, 6208, 8192, 8256],
 }
 

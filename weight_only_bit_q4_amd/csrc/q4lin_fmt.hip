@@ -1333,8 +1333,12 @@ hipError_t launch_fmt_gemv(const FmtArgs& a, hipStream_t s) {
   if (need <= 2) return launch_fmt_gemv_ch<F, 2>(a, s);
   if (need <= 3) return launch_fmt_gemv_ch<F, 3>(a, s);
   if (need <= 4) return launch_fmt_gemv_ch<F, 4>(a, s);
-  if (need <= 6) return launch_fmt_gemv_ch<F, 6>(a, s);
-  return launch_fmt_gemv_ch<F, 8>(a, s);
+  if constexpr (F == FMT_W8) {  // (W8 alone has more than 4: 16 weights a piece)
+    if (need <= 5) return launch_fmt_gemv_ch<F, 5>(a, s);
+    if (need <= 6) return launch_fmt_gemv_ch<F, 6>(a, s);
+    return launch_fmt_gemv_ch<F, 8>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int CH>
