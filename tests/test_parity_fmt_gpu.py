@@ -218,3 +218,46 @@ def test_fmt_q4_is_q4lin_linear():
     xd, cd, sd = dev(x), dev(c), dev(s)
     b = host_bits(q4.linear(xd, cd, sd))
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("fmt", [inputs.FMT_Q5, inputs.FMT_W8, inputs.FMT_NVFP4, inputs.FMT_BF16],
+                         ids=["Q5", "W8", "NVFP4", "BF16_CTRL"])
+@pytest.mark.parametrize("t", [1, 16, 40])
+def test_fmt_graph_replay_with_changed_inputs(fmt, t):
+    """One format call captured in a HIP graph (the one-token GEMV, the
+    few-token and the many-token kernels); the activations and every weight
+    plane are then overwritten in place before each replay, with unrelated
+    eager work between replays: every replay matches the oracle for the
+    inputs of that moment (no workspace, no state kept between calls)."""
+    import weight_only_bit_q4_amd as q4
+    th = torch()
+    n, k = 300, 2048
+    w0, h0, s0 = inputs.gen_fmt_weight(fmt, n, k, 700 + t)
+    x0 = inputs.gen_x(k, t, 701 + t)
+    xd = dev(np.asarray(x0, dtype=np.uint16).reshape(t, k))
+    wd = _bytes_dev(w0).view(n, -1)
+    hd = _bytes_dev(h0) if h0 is not None else None
+    sd = _bytes_dev(s0) if s0 is not None else None
+    y = th.empty((t, n), dtype=th.bfloat16, device="cuda")
+    q4.linear_fmt(fmt, xd, wd, hd, sd, y=y)   # warm-up outside capture
+    th.cuda.synchronize()
+    g = th.cuda.CUDAGraph()
+    announce("format graph capture fmt=%d n=%d k=%d t=%d" % (fmt, n, k, t))
+    with th.cuda.graph(g):
+        q4.linear_fmt(fmt, xd, wd, hd, sd, y=y)
+    for rep in range(3):
+        w, hi, sc = inputs.gen_fmt_weight(fmt, n, k, 710 + 10 * rep + t)
+        x = inputs.gen_x(k, t, 711 + 10 * rep + t)
+        xd.copy_(dev(np.asarray(x, dtype=np.uint16).reshape(t, k)))
+        wd.copy_(_bytes_dev(w).view(n, -1))
+        if hd is not None:
+            hd.copy_(_bytes_dev(hi))
+        if sd is not None:
+            sd.copy_(_bytes_dev(sc))
+        th.cuda.synchronize()
+        g.replay()
+        th.cuda.synchronize()
+        assert_close(host_bits(y), oracle.linear_fmt(fmt, x, w, hi, sc, n, k, t),
+                     what="%s replay %d T=%d" % (inputs.FMT_NAMES[fmt], rep, t))
+        junk = th.randn(1 << 20, device="cuda")
+        junk.sum().item()

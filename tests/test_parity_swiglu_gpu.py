@@ -128,3 +128,41 @@ def test_swiglu_prefill_6144x5120_t1024_sampled():
     _, g = oracle.linear_at(x, cg, sg, n, k, t, ns, ts, with_acc=True)
     _, u = oracle.linear_at(x, cu, su, n, k, t, ns, ts, with_acc=True)
     swiglu_close(got[ts, ns], g, u, what="LinearSwiGLU 6144x5120 T=1024 sampled")
+
+
+@pytest.mark.parametrize("t", [1, 16, 64, 300])
+def test_swiglu_graph_replay_with_changed_inputs(t):
+    """One LinearSwiGLU call captured in a HIP graph (one pass with the gate in
+    the final sum at 1, 16 and 64 tokens; the tiled sums and the combine pass
+    at 300), the activations and both weights overwritten in place before each
+    replay, eager work between replays: every replay matches the oracle."""
+    import weight_only_bit_q4_amd as q4
+    th = torch()
+    n, k = 200, 1024
+    x0, cg0, sg0, cu0, su0 = _pair(n, k, t, 800 + t)
+    xd = dev(np.asarray(x0, dtype=np.uint16).reshape(t, k))
+    planes = [dev(np.asarray(a, dtype=dt).reshape(n, -1)) for a, dt in
+              ((cg0, np.uint8), (sg0, np.uint16), (cu0, np.uint8), (su0, np.uint16))]
+    y = th.empty((t, n), dtype=th.bfloat16, device="cuda")
+    need = q4.q4lin_swiglu_workspace_bytes(n, k, t)
+    ws = th.empty(max(need, 1), dtype=th.uint8, device="cuda")
+    wsv = ws[:need] if need else None
+    q4.linear_swiglu(xd, *planes, y=y, workspace=wsv)   # warm-up outside capture
+    th.cuda.synchronize()
+    g = th.cuda.CUDAGraph()
+    announce("swiglu graph capture n=%d k=%d t=%d" % (n, k, t))
+    with th.cuda.graph(g):
+        q4.linear_swiglu(xd, *planes, y=y, workspace=wsv)
+    for rep in range(3):
+        x, cg, sg, cu, su = _pair(n, k, t, 810 + 10 * rep + t)
+        xd.copy_(dev(np.asarray(x, dtype=np.uint16).reshape(t, k)))
+        for p, (a, dt) in zip(planes, ((cg, np.uint8), (sg, np.uint16), (cu, np.uint8), (su, np.uint16))):
+            p.copy_(dev(np.asarray(a, dtype=dt).reshape(n, -1)))
+        th.cuda.synchronize()
+        g.replay()
+        th.cuda.synchronize()
+        _, gs = oracle.linear(x, cg, sg, n, k, t, with_acc=True)
+        _, us = oracle.linear(x, cu, su, n, k, t, with_acc=True)
+        swiglu_close(host_bits(y), gs, us, what="LinearSwiGLU replay %d T=%d" % (rep, t))
+        junk = th.randn(1 << 20, device="cuda")
+        junk.sum().item()
