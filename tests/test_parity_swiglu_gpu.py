@@ -59,6 +59,10 @@ def _pair(n, k, t, seed):
     return x, cg, sg, cu, su
 
 
+# From 129 tokens, where the 2N-row problem takes 96 x 256 tiles without a
+# K split, one tiled launch applies the gate in its epilogue (tiles of 48
+# rows of each weight; ragged rows and tokens, five groups); with a K split
+# (3072 x 5120 at T = 512) the sums go through the workspace and the combine.
 # 5 to 128 tokens run one launch of the weight formats' kernel, each
 # workgroup on the same rows of both weights: 16 or 32 rows of each (two or
 # four column tiles), few-token and many-token kernels, one and two token
@@ -70,7 +74,8 @@ def _pair(n, k, t, seed):
                                    (3072, 5120, 5), (3072, 5120, 16), (6000, 1024, 12), (6000, 1024, 17),
                                    (6000, 640, 100), (1000, 2048, 128), (333, 640, 65), (4100, 640, 33),
                                    (16, 1 << 20, 40), (1, 640, 100), (5, 64, 17), (2, 128, 5), (1000, 64, 128),
-                                   (257, 2048, 33)])
+                                   (257, 2048, 33), (3000, 320, 1000), (1001, 640, 700), (200, 1024, 300),
+                                   (3072, 5120, 512), (4800, 192, 257)])
 def test_swiglu_matches_oracle(n, k, t):
     x, cg, sg, cu, su = _pair(n, k, t, 101)
     got = run_swiglu(x, cg, sg, cu, su, n, k, t, what="seeded")

@@ -182,8 +182,12 @@ size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 //   GLU:   the single-token route, each workgroup on the same rows of both
 //          weights, the gate applied in its final sum (no workspace);
 //   FMT:   the same on the weight formats' kernel, kSmallFmtFirstT to
-//          kMidLastT tokens (no workspace).
-enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3, SW_MID = 4, SW_GLU = 5, SW_FMT = 6 };
+//          kMidLastT tokens (no workspace);
+//   TGLU:  the many-token route in one tiled launch whose tiles take the
+//          same rows of both weights (96 x 256 tiles for 2N rows, no K
+//          split), the gate applied in the epilogue (workspace: the
+//          activation preparation only).
+enum { SW_FUSED = 1, SW_SPLIT = 2, SW_TILED = 3, SW_MID = 4, SW_GLU = 5, SW_FMT = 6, SW_TGLU = 7 };
 struct SwigluPlan {
   int mode;
   int route;
@@ -210,6 +214,10 @@ bool swiglu_plan(int64_t n, int64_t k, int64_t t, SwigluPlan* p) {
   }
   const int r1 = pick_route(n, k, t);
   if (r1 == Q4LIN_ROUTE_TILED && !q4lin::tiled_shape_ok(n, k, t)) return false;
+  if (r1 == Q4LIN_ROUTE_TILED && q4lin::tiled_glu_ok(n, k, t)) {
+    *p = SwigluPlan{SW_TGLU, r1, 0, q4lin::tiled_glu_workspace_bytes(n, k, t)};
+    return true;
+  }
   if (r1 == Q4LIN_ROUTE_TILED) {
     *p = SwigluPlan{SW_TILED, r1, 0, q4lin::tiled_pair_workspace_bytes(n, n, k, t, true)};
   } else if (r1 == Q4LIN_ROUTE_MID) {
@@ -364,6 +372,13 @@ int q4lin_linear_swiglu(const void* x, const void* codes_gate, const void* scale
     a.n2 = n;
     a.glu = true;
     e = q4lin::launch_fmt(a, s);
+    return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
+  }
+  if (p.mode == SW_TGLU) {
+    // one activation preparation and one tiled launch whose tiles take the
+    // same rows of both weights and store bf16(silu(G) U) themselves
+    const q4lin::TiledArgs a{x, codes_gate, scales_gate, y, n, k, t, workspace, q4lin::tiled_pick_config(2 * n, k, t)};
+    e = q4lin::launch_tiled_glu(a, codes_up, scales_up, s);
     return e == hipSuccess ? Q4LIN_OK : Q4LIN_E_LAUNCH;
   }
   if (p.mode == SW_FUSED) {

@@ -146,6 +146,13 @@ struct TiledPairArgs {
 size_t tiled_pair_workspace_bytes(int64_t n1, int64_t n2, int64_t k, int64_t t, bool f32);
 // src1/src2 (binary32 sums only) receive where each weight's sums are
 hipError_t launch_tiled_pair(const TiledPairArgs& p, SumSource* src1, SumSource* src2, hipStream_t stream);
+// LinearSwiGLU in one tiled launch (after the activation preparation):
+// tiles of 48 gate rows and the same 48 up rows, bf16(silu(G) U) formed in
+// the epilogue.  a: x, the gate's planes, y, n, k, t, workspace; where
+// tiled_glu_ok (the 2N-row problem on 96 x 256 tiles without a K split).
+bool tiled_glu_ok(int64_t n, int64_t k, int64_t t);
+size_t tiled_glu_workspace_bytes(int64_t n, int64_t k, int64_t t);
+hipError_t launch_tiled_glu(const TiledArgs& a, const void* codes_up, const void* scales_up, hipStream_t stream);
 
 int64_t tiled_tpad(int64_t t);
 // Whether the tiled kernels can address (n, k, t): their buffer offsets are

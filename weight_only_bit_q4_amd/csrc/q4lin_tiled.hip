@@ -384,8 +384,10 @@ struct TiledShape {
 };
 
 // ADD: the LinearAdd form (a residual joins the results); the plain form
-// carries none of its code.
-template <int NS, int TS, int WN, int WT, bool ADD>
+// carries none of its code.  GLU: the gated LinearSwiGLU tile (rows 0 ..
+// BN/2 - 1 of a tile are rows n0 .. of the gate, rows BN/2 .. the same rows
+// of the up weight, p2's planes; the epilogue forms bf16(silu(G) U)).
+template <int NS, int TS, int WN, int WT, bool ADD, bool GLU = false>
 __global__ void __launch_bounds__(64 * WN * WT)
 tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, const int* __restrict__ rexp,
              const uint16_t* __restrict__ xraw, const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
@@ -401,7 +403,7 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // is 1); inside the kernel groups are counted from g0
   // two weights: the workgroups from p2.first on serve the second
   int wgi = (int)blockIdx.x;
-  if (p2.n > 0 && wgi >= p2.first) {
+  if (!GLU && p2.n > 0 && wgi >= p2.first) {
     codes = p2.codes;
     scales = p2.scales;
     y = p2.y;
@@ -442,7 +444,11 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
       tile_n = lin - tile_t * tiles_n;
     }
   }
-  const int n0 = tile_n * BN;
+  // GLU: BH rows of each weight per tile; tile row r < BH is row n0 + r of
+  // the gate, r >= BH row n0 + r - BH of the up weight
+  constexpr int BH = GLU ? BN / 2 : BN;
+  auto prow = [](int r) { return GLU && r >= BH ? r - BH : r; };
+  const int n0 = tile_n * BH;
   const int tb0 = tile_t * (BT / 32);                 // first 32-token block
   const int tb_last = Tpad / 32 - 1;
 
@@ -453,13 +459,18 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // of the pair slot, so the slot holds [row][64 bytes].  Pieces past the
   // tile (when 4 BN is not a multiple of NT) repeat the last one into the
   // slot's slack; rows past N repeat row N-1 (their outputs are dropped).
+  // (GLU: load i of a wave reads 16 rows, 16 (i NW + wave) .. + 15, all of
+  // one weight since BH is a multiple of 16; the up weight's from rc2)
   const uint8_t* codes_tile = codes + (size_t)n0 * (K >> 1);
-  const rsrc_t rc = make_rsrc(codes_tile, (uint32_t)min((int64_t)(N - n0) * (K >> 1), (int64_t)0x7FFFFFFF));
+  const uint32_t tile_code_bytes = (uint32_t)min((int64_t)(N - n0) * (K >> 1), (int64_t)0x7FFFFFFF);
+  const rsrc_t rc = make_rsrc(codes_tile, tile_code_bytes);
+  const rsrc_t rc2 = GLU ? make_rsrc(p2.codes + (size_t)n0 * (K >> 1), tile_code_bytes) : rc;
+  static_assert(BH % 16 == 0, "a code load's 16 rows belong to one weight");
   uint32_t coff[CQ];
 #pragma unroll
   for (int i = 0; i < CQ; ++i) {
     const int j = min((i * NW + wave) * 64 + lane, 4 * BN - 1);
-    coff[i] = (uint32_t)(min(j >> 2, N - 1 - n0) * (K >> 1) + (j & 3) * 16);
+    coff[i] = (uint32_t)(min(prow(j >> 2), N - 1 - n0) * (K >> 1) + (j & 3) * 16);
   }
   // Scales move in strips of P groups (one strip per block of unrolled
   // steps): strip b holds, for every row of the tile, the 48 bytes (three
@@ -477,17 +488,39 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   // scale of group g0 + P b, its scale of group g0 + P b + j sits at byte
   // 48 r + (o & 15) + 2 j of the strip.
   static_assert(2 * P + 14 <= 48, "a row's strip must fit three pieces");
+  // GLU: each weight's rows take whole 1-KiB chunks of a strip (chunk c =
+  // i NW + wave: the gate's rows in chunks 0 .. SCH - 1, the up weight's from
+  // chunk SCH, its row r' at byte 1024 SCH + 48 r'), so that every load
+  // reads one weight's scale plane.
+  constexpr int SCH = (3 * BH + 63) / 64;  // chunks of one weight's rows (GLU)
+  static_assert(!GLU || 2 * SCH <= SQ * NW, "both weights' strip chunks fit the strip");
+  auto strip_rs = [&](const uint16_t* sc, int n) __device__ {
+    const uintptr_t pl = reinterpret_cast<uintptr_t>(sc), base = pl & ~(uintptr_t)15;
+    return make_rsrc(reinterpret_cast<const void*>(base),
+                     (uint32_t)min(((int64_t)(pl - base) + (int64_t)n * ((int64_t)G * 2) + 15) & ~(int64_t)15,
+                                   (int64_t)0x7FFFFFF0));
+  };
   const uintptr_t s_plane = reinterpret_cast<uintptr_t>(scales);
   const uintptr_t s_base = s_plane & ~(uintptr_t)15;
-  const rsrc_t rs = make_rsrc(reinterpret_cast<const void*>(s_base),
-                              (uint32_t)min(((int64_t)(s_plane - s_base) + (int64_t)N * G * 2 + 15) & ~(int64_t)15,
-                                            (int64_t)0x7FFFFFF0));
+  const rsrc_t rs = strip_rs(scales, N);
+  const uintptr_t s_plane2 = GLU ? reinterpret_cast<uintptr_t>(p2.scales) : s_plane;
+  const uintptr_t s_base2 = s_plane2 & ~(uintptr_t)15;
+  const rsrc_t rs2 = GLU ? strip_rs(p2.scales, N) : rs;
   uint32_t so_p[SQ];  // strip 0 offset o of the row of piece i, plus 16 (p % 3)
 #pragma unroll
   for (int i = 0; i < SQ; ++i) {
-    const int p = min(i * NT + tid, 3 * BN - 1);
-    const int r = min(p / 3, N - 1 - n0);
-    so_p[i] = (uint32_t)(s_plane - s_base) + (uint32_t)((n0 + r) * G + g0) * 2u + (uint32_t)(p % 3) * 16u;
+    if constexpr (GLU) {
+      const int c = i * NW + wave;
+      const bool up = c >= SCH;
+      const int p = min((up ? c - SCH : c) * 64 + lane, 3 * BH - 1);
+      const int r = min(p / 3, N - 1 - n0);
+      so_p[i] = (uint32_t)(up ? s_plane2 - s_base2 : s_plane - s_base) + (uint32_t)((n0 + r) * G + g0) * 2u +
+                (uint32_t)(p % 3) * 16u;
+    } else {
+      const int p = min(i * NT + tid, 3 * BN - 1);
+      const int r = min(p / 3, N - 1 - n0);
+      so_p[i] = (uint32_t)(s_plane - s_base) + (uint32_t)((n0 + r) * G + g0) * 2u + (uint32_t)(p % 3) * 16u;
+    }
   }
   // Code dword c of this thread belongs to tile row (c * NT + tid) / 8;
   // s_r48[c] = 48 r and s_o[c] the strip 0 offset o of that row.  s_mul[c] is
@@ -499,10 +532,11 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
 #pragma unroll
   for (int c = 0; c < CD; ++c) {
     const int r = min((c * NT + tid) >> 3, BN - 1);
-    const int rr = min(r, N - 1 - n0);
-    s_o[c] = (uint32_t)(s_plane - s_base) + (uint32_t)((n0 + rr) * G + g0) * 2u;
-    s_r48[c] = (uint32_t)r * 48u;
-    rx_c[c] = rexp[n0 + rr];
+    const bool up = GLU && r >= BH;
+    const int rr = min(prow(r), N - 1 - n0);
+    s_o[c] = (uint32_t)(up ? s_plane2 - s_base2 : s_plane - s_base) + (uint32_t)((n0 + rr) * G + g0) * 2u;
+    s_r48[c] = up ? (uint32_t)(1024 * SCH + 48 * (r - BH)) : (uint32_t)r * 48u;
+    rx_c[c] = up ? p2.rexp[n0 + rr] : rexp[n0 + rr];
   }
   // The epilogue's exponents, also loaded now: c[n] of the lane's rows and
   // e[t] of its tokens (16 per 32-token block: t = tl + 8 (r / 4) + r % 4,
@@ -550,7 +584,8 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
   auto issue_one = [&](int q, auto qs, int ga, f16x8_t (&a)[TS][4], auto vi) __device__ {
     constexpr int v = decltype(vi)::value;
     if constexpr (v < CQ) {
-      dma16(rc, coff[v], (uint32_t)(g0 + 2 * q) * 32, code_slot(qs) + (v * NW + wave) * 1024);
+      dma16((GLU && (v * NW + wave) * 16 >= BH) ? rc2 : rc, coff[v], (uint32_t)(g0 + 2 * q) * 32,
+            code_slot(qs) + (v * NW + wave) * 1024);
     } else {
       constexpr int i = v - CQ, ts = i / 4, m = i % 4;
       buf_read_agpr<m * 1024>(a[ts][m], rx, aoff[ts], (uint32_t)(g0 + ga) * 4096);
@@ -564,7 +599,8 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
 #pragma unroll
     for (int i = 0; i < SQ; ++i) {
       // (o + 16 k) & ~15 = (o & ~15) + 16 k, with o the row's strip offset
-      dma16(rs, (so_p[i] + (uint32_t)b * (2u * P)) & ~15u, 0u, dst + (i * NW + wave) * 1024);
+      dma16((GLU && i * NW + wave >= SCH) ? rs2 : rs, (so_p[i] + (uint32_t)b * (2u * P)) & ~15u, 0u,
+            dst + (i * NW + wave) * 1024);
     }
   };
   const int qlast = (Gs - 1) >> 1;
@@ -802,6 +838,45 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
           if (t < T && n < N) pk[(size_t)t * N + n] = acc[ts][ns][r];
         }
       }
+    return;
+  }
+  if constexpr (GLU) {
+    // LinearSwiGLU: the tile's raw FP32 sums ([token][row]: the gate's rows,
+    // then the up weight's) and the exponents go through LDS; each output
+    // then takes its two sums as the two-pass form does: scaled by
+    // 2^(e[t] - c[n]) in binary64 (+0 maps a -0 sum to +0), the gate
+    // silu(g) = g / (1 + e^-g) in binary64, one rounding of the product.
+    static_assert(BT * BN * 4 + (BT + BN) * 4 <= 160 * 1024, "the gated tile's sums fit the LDS");
+    __syncthreads();
+    float* ft = reinterpret_cast<float*>(lds);
+    int* el = reinterpret_cast<int*>(lds + BT * BN * 4);
+    int* cl = el + BT;
+#pragma unroll
+    for (int ts = 0; ts < TS; ++ts) {
+      const int tl = (wt * TS + ts) * 32 + 4 * lh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+          ft[(tl + 8 * (r >> 2) + (r & 3)) * BN + (wn * NS + ns) * 32 + li] = acc[ts][ns][r];
+    }
+    for (int i = tid; i < BT; i += NT) el[i] = texp[min(32 * tb0 + i, Tpad - 1)];
+    for (int i = tid; i < BN; i += NT) cl[i] = (i >= BH ? p2.rexp : rexp)[min(n0 + prow(i), N - 1)];
+    __syncthreads();
+    // (the binary64 gate costs about 7 us per round of tiles with 3072 rows of
+    // each weight and K = 5120:
+    // the epilogue is bound by the binary64 rate of the CU, four outputs per
+    // thread and round gained nothing)
+    const int tg0 = 32 * tb0;
+    for (int c = tid; c < BT * BH; c += NT) {
+      const int tl = c / BH, r = c - tl * BH;
+      if (tg0 + tl < T && n0 + r < N) {
+        const double gv = __builtin_ldexp((double)ft[tl * BN + r], el[tl] - cl[r]) + 0.0;
+        const double uv = __builtin_ldexp((double)ft[tl * BN + BH + r], el[tl] - cl[BH + r]) + 0.0;
+        const double silu = gv / (1.0 + exp(-gv));
+        y[(size_t)(tg0 + tl) * N + n0 + r] = f32_to_bf16_rne((float)(silu * uv));
+      }
+    }
     return;
   }
   // LinearAdd: the tile's residual values, all loaded before the first use
@@ -1150,6 +1225,56 @@ hipError_t launch_tiled_pair(const TiledPairArgs& p, SumSource* src1, SumSource*
   if (src1 != nullptr) *src1 = SumSource{part1, texp, rexp1, a.cfg.ks, (size_t)tp * (size_t)a.n};
   if (src2 != nullptr) *src2 = SumSource{part2, texp, rexp2, a.cfg.ks, (size_t)tp * (size_t)p.n2};
   return launch_shape(a, x16, texp, rexp1, part1, (int)tp, stream, h2);
+}
+
+// LinearSwiGLU in one tiled launch after the activation preparation: every
+// 96-row tile takes 48 rows of the gate and the same 48 rows of the up
+// weight and forms bf16(silu(G) U) in its epilogue from the same binary32
+// sums, scaled and combined as the two-pass form does (no partials, no
+// combine pass).  Only where the 2N-row problem takes the 96 x 256 tiles
+// without a K split.
+bool tiled_glu_ok(int64_t n, int64_t k, int64_t t) {
+  const TiledConfig c = tiled_pick_config(2 * n, k, t);
+  return c.ns == 3 && c.ts == 2 && c.wn == 1 && c.wt == 4 && c.ks == 1 && tiled_shape_ok(n, k, t);
+}
+
+// Workspace: the activations, the token exponents, each weight's row exponents.
+size_t tiled_glu_workspace_bytes(int64_t n, int64_t k, int64_t t) {
+  const int64_t tp = tiled_tpad(t);
+  return align256((size_t)(tp * k * 2)) + align256((size_t)(tp * 4)) + 2 * align256((size_t)(n * 4));
+}
+
+hipError_t launch_tiled_glu(const TiledArgs& a, const void* codes_up, const void* scales_up, hipStream_t stream) {
+  using Sh = TiledShape<3, 2, 1, 4>;
+  constexpr int BH = Sh::BN / 2;
+  constexpr size_t kGluLds = (size_t)Sh::BT * Sh::BN * 4 + (size_t)(Sh::BT + Sh::BN) * 4;
+  const int64_t tp = tiled_tpad(a.t);
+  uint8_t* w = static_cast<uint8_t*>(a.workspace);
+  u32x4_t* x16 = reinterpret_cast<u32x4_t*>(w);
+  w += align256((size_t)(tp * a.k * 2));
+  int* texp = reinterpret_cast<int*>(w);
+  w += align256((size_t)(tp * 4));
+  int* rexp_g = reinterpret_cast<int*>(w);
+  w += align256((size_t)(a.n * 4));
+  int* rexp_u = reinterpret_cast<int*>(w);
+  hipError_t e = launch_prep(a, x16, texp, rexp_g, scales_up, a.n, rexp_u, stream);
+  if (e != hipSuccess) return e;
+  auto kern = tiled_kernel<3, 2, 1, 4, false, true>;
+  e = allow_full_lds(reinterpret_cast<const void*>(kern));
+  if (e != hipSuccess) return e;
+  const int tiles_n = (int)((a.n + BH - 1) / BH);
+  const int tiles_t = (int)((a.t + Sh::BT - 1) / Sh::BT);
+  TiledPlane2 p2;
+  p2.codes = static_cast<const uint8_t*>(codes_up);
+  p2.scales = static_cast<const uint16_t*>(scales_up);
+  p2.rexp = rexp_u;
+  p2.n = (int)a.n;
+  const size_t lds = (size_t)Sh::LDS_B > kGluLds ? (size_t)Sh::LDS_B : kGluLds;
+  kern<<<dim3((unsigned)(tiles_n * tiles_t)), dim3(Sh::NT), lds, stream>>>(
+      x16, texp, rexp_g, static_cast<const uint16_t*>(a.x), static_cast<const uint8_t*>(a.codes),
+      static_cast<const uint16_t*>(a.scales), static_cast<uint16_t*>(a.y), nullptr, (int)a.n, (int)a.k, (int)a.t,
+      (int)tp, tiles_n, tiles_t, 1, nullptr, p2);
+  return hipGetLastError();
 }
 
 }  // namespace q4lin
