@@ -139,10 +139,15 @@ Q4LIN_API int64_t q4lin_pair_workspace_bytes(int64_t n1, int64_t n2, int64_t k, 
  * alignment; y is bf16 [T][N] like q4lin_linear's.  workspace must hold
  * q4lin_swiglu_workspace_bytes(n, k, t) bytes, 256-byte aligned: 0 where one
  * pass takes the same rows of both weights and applies the gate before its
- * store (1 to 128 tokens, where the rows' scales fit the kernel's tables),
- * else room for the two binary32 sums (or the many-token route's
- * activation copy and partials).  y must not overlap any input or the
- * workspace.  Errors as for q4lin_linear. */
+ * store (1 to 128 tokens, where the rows' scales fit the kernel's tables);
+ * from 129 tokens, where the 2N-row problem takes the many-token route's
+ * 96 x 256 tiles without a K split, one tiled launch whose tiles take 48
+ * rows of each weight applies the gate in its epilogue and the workspace
+ * holds only the activation preparation (q4lin_workspace_bytes' layout with
+ * both weights' row exponents); else room for the two binary32 sums (or the
+ * many-token route's activation copy and partials) and a combine pass.  y
+ * must not overlap any input or the workspace.  Errors as for
+ * q4lin_linear. */
 Q4LIN_API int q4lin_linear_swiglu(const void *x, const void *codes_gate, const void *scales_gate,
                       const void *codes_up, const void *scales_up, void *y, int64_t n, int64_t k, int64_t t,
                       void *workspace, size_t workspace_bytes, void *stream);

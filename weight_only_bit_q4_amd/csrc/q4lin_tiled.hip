@@ -863,10 +863,9 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     for (int i = tid; i < BT; i += NT) el[i] = texp[min(32 * tb0 + i, Tpad - 1)];
     for (int i = tid; i < BN; i += NT) cl[i] = (i >= BH ? p2.rexp : rexp)[min(n0 + prow(i), N - 1)];
     __syncthreads();
-    // (the binary64 gate costs about 7 us per round of tiles with 3072 rows of
-    // each weight and K = 5120:
-    // the epilogue is bound by the binary64 rate of the CU, four outputs per
-    // thread and round gained nothing)
+    // (the binary64 gate costs about 7 us per round of tiles with 3072 rows
+    // of each weight and K = 5120: the epilogue is bound by the CU's binary64
+    // rate; four outputs per thread and round gained nothing)
     const int tg0 = 32 * tb0;
     for (int c = tid; c < BT * BH; c += NT) {
       const int tl = c / BH, r = c - tl * BH;
