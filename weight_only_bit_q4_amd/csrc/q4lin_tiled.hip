@@ -863,17 +863,44 @@ tiled_kernel(const u32x4_t* __restrict__ x16, const int* __restrict__ texp, cons
     for (int i = tid; i < BT; i += NT) el[i] = texp[min(32 * tb0 + i, Tpad - 1)];
     for (int i = tid; i < BN; i += NT) cl[i] = (i >= BH ? p2.rexp : rexp)[min(n0 + prow(i), N - 1)];
     __syncthreads();
-    // (the binary64 gate costs about 7 us per round of tiles with 3072 rows
-    // of each weight and K = 5120: the epilogue is bound by the CU's binary64
-    // rate; four outputs per thread and round gained nothing)
+    // Eight adjacent rows of one token per thread and step: 16-byte LDS
+    // reads of their sums and exponents and one 16-byte store where the rows
+    // allow (one LDS read and one 2-byte store per output took about 6 us
+    // more than the pair's epilogue at 3072 rows of each weight, T = 1024).
     const int tg0 = 32 * tb0;
-    for (int c = tid; c < BT * BH; c += NT) {
-      const int tl = c / BH, r = c - tl * BH;
-      if (tg0 + tl < T && n0 + r < N) {
-        const double gv = __builtin_ldexp((double)ft[tl * BN + r], el[tl] - cl[r]) + 0.0;
-        const double uv = __builtin_ldexp((double)ft[tl * BN + BH + r], el[tl] - cl[BH + r]) + 0.0;
+    constexpr int G8 = BH / 8;
+    static_assert(BH % 8 == 0 && BT % 4 == 0, "16-byte groups of rows and exponents");
+    const bool vec = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+    for (int gi = tid; gi < BT * G8; gi += NT) {
+      const int tl = gi / G8, r0 = (gi - tl * G8) * 8;
+      if (tg0 + tl >= T || n0 + r0 >= N) continue;
+      const f32x4_t* fg = reinterpret_cast<const f32x4_t*>(ft + tl * BN + r0);
+      const f32x4_t* fu = reinterpret_cast<const f32x4_t*>(ft + tl * BN + BH + r0);
+      const int4* cg = reinterpret_cast<const int4*>(cl + r0);
+      const int4* cu = reinterpret_cast<const int4*>(cl + BH + r0);
+      const f32x4_t g4[2] = {fg[0], fg[1]}, u4[2] = {fu[0], fu[1]};
+      const int4 cg4[2] = {cg[0], cg[1]}, cu4[2] = {cu[0], cu[1]};
+      const int e = el[tl];
+      uint16_t h[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int cgj = j & 2 ? (j & 1 ? cg4[j >> 2].w : cg4[j >> 2].z) : (j & 1 ? cg4[j >> 2].y : cg4[j >> 2].x);
+        const int cuj = j & 2 ? (j & 1 ? cu4[j >> 2].w : cu4[j >> 2].z) : (j & 1 ? cu4[j >> 2].y : cu4[j >> 2].x);
+        const float gj = g4[j >> 2][j & 3], uj = u4[j >> 2][j & 3];
+        const double gv = __builtin_ldexp((double)gj, e - cgj) + 0.0;
+        const double uv = __builtin_ldexp((double)uj, e - cuj) + 0.0;
         const double silu = gv / (1.0 + exp(-gv));
-        y[(size_t)(tg0 + tl) * N + n0 + r] = f32_to_bf16_rne((float)(silu * uv));
+        h[j] = f32_to_bf16_rne((float)(silu * uv));
+      }
+      uint16_t* yo = y + (size_t)(tg0 + tl) * N + n0 + r0;
+      if (vec && n0 + r0 + 8 <= N) {
+        *reinterpret_cast<u32x4_t*>(yo) =
+            u32x4_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16),
+                    (uint32_t)h[4] | ((uint32_t)h[5] << 16), (uint32_t)h[6] | ((uint32_t)h[7] << 16)};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (n0 + r0 + j < N) yo[j] = h[j];
       }
     }
     return;
