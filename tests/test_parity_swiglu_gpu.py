@@ -85,7 +85,7 @@ def test_swiglu_matches_oracle(n, k, t):
     swiglu_close(got, g, u, what="LinearSwiGLU %dx%d T=%d" % (n, k, t))
 
 
-@pytest.mark.parametrize("n,k,t", [(512, 1024, 1), (1000, 2048, 20), (700, 1280, 70)])
+@pytest.mark.parametrize("n,k,t", [(512, 1024, 1), (1000, 2048, 20), (700, 1280, 70), (3000, 320, 1000)])
 def test_swiglu_zero_gate_and_zero_up(n, k, t):
     x, cg, sg, cu, su = _pair(n, k, t, 103)
     eights = np.full_like(cg, 0x88)
